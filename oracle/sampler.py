@@ -1,0 +1,106 @@
+"""Token choice: greedy argmax and temperature sampling by Gumbel-max.
+
+Greedy follows the walkthrough's Step 8 (temperature 0 -> argmax of the
+logits); ties go to the lowest index, and NaN ranks above every number (numpy's
+argmax rule).  Temperature T > 0 draws from softmax(logits / T) (Step 8).  The
+draw is taken as argmax_v(logits_v / T + G_v) with Gumbel noise
+G_v = -ln(-ln u_v), which samples exactly that distribution and needs no
+ordered prefix sum.  The uniforms come from Philox4x64-10 (Salmon, Moraes, Dror,
+Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC'11), a counter-based
+generator:
+
+  counter = (v // 4, step, seq, 0), key = (seed, 0), word = v % 4
+  u_v = ((r >> 40) + 0.5) * 2^-24        (top 24 bits, exact in float32)
+
+Philox4x64-10: ten rounds of
+  (hi0, lo0) = M0 * c0,  (hi1, lo1) = M1 * c2          (128-bit products)
+  c = (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0)
+with the key bumped by the Weyl constants (W0, W1) between rounds; M0, M1, W0,
+W1 are the paper's 64-bit multipliers and Weyl increments.
+"""
+import numpy as np
+
+U64 = np.uint64
+M32 = U64(0xFFFFFFFF)
+PHILOX_M0 = U64(0xD2E7470EE14C6C93)
+PHILOX_M1 = U64(0xCA5A826395121157)
+PHILOX_W0 = U64(0x9E3779B97F4A7C15)
+PHILOX_W1 = U64(0xBB67AE8584CAA73B)
+
+
+def _mulhilo(a, b):
+    """128-bit product of uint64 arrays: (high 64 bits, low 64 bits)."""
+    a = np.asarray(a, U64)
+    b = np.asarray(b, U64)
+    alo, ahi = a & M32, a >> U64(32)
+    blo, bhi = b & M32, b >> U64(32)
+    p0 = alo * blo
+    p1 = alo * bhi
+    p2 = ahi * blo
+    p3 = ahi * bhi
+    mid = (p0 >> U64(32)) + (p1 & M32) + (p2 & M32)
+    hi = p3 + (p1 >> U64(32)) + (p2 >> U64(32)) + (mid >> U64(32))
+    lo = a * b
+    return hi, lo
+
+
+def philox4x64_10(ctr, key):
+    """ctr: 4 uint64 arrays (broadcastable), key: 2 uint64 values -> 4 uint64 arrays."""
+    with np.errstate(over="ignore"):
+        c0, c1, c2, c3 = (np.asarray(c, U64) for c in ctr)
+        k0, k1 = U64(key[0]), U64(key[1])
+        for r in range(10):
+            if r:
+                k0 = U64(k0 + PHILOX_W0)
+                k1 = U64(k1 + PHILOX_W1)
+            hi0, lo0 = _mulhilo(PHILOX_M0, c0)
+            hi1, lo1 = _mulhilo(PHILOX_M1, c2)
+            c0, c1, c2, c3 = hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0
+    return c0, c1, c2, c3
+
+
+def uniforms(vocab, seed, step, seq):
+    """u_v for v in [0, vocab) as float32, per the counter layout above."""
+    v = np.arange(vocab, dtype=np.uint64)
+    words = philox4x64_10((v >> U64(2), U64(step), U64(seq), U64(0)), (seed & 0xFFFFFFFFFFFFFFFF, 0))
+    w = np.stack(words, axis=0)
+    r = w[(v & U64(3)).astype(np.int64), np.arange(vocab)]
+    return (((r >> U64(40)).astype(np.float64) + 0.5) * 2.0 ** -24).astype(np.float32)
+
+
+def gumbel(vocab, seed, step, seq):
+    """G_v = -ln(-ln u_v), float64 from the float32 uniform."""
+    u = uniforms(vocab, seed, step, seq).astype(np.float64)
+    return -np.log(-np.log(u))
+
+
+def greedy(logits):
+    """argmax with the lowest index on ties (NaN ranks above every number)."""
+    return int(np.argmax(np.asarray(logits)))
+
+
+def sample(logits, temperature, seed, step, seq):
+    """Greedy for temperature 0, else argmax(logits / T + Gumbel)."""
+    if temperature == 0:
+        return greedy(logits)
+    lg = np.asarray(logits, dtype=np.float64)
+    return int(np.argmax(lg / temperature + gumbel(lg.size, seed, step, seq)))
+
+
+def scores(logits, temperature, seed, step, seq):
+    """The perturbed scores the sampler takes the argmax of."""
+    lg = np.asarray(logits, dtype=np.float64)
+    if temperature == 0:
+        return lg
+    return lg / temperature + gumbel(lg.size, seed, step, seq)
+
+
+def uniforms_batch(vocab, seed, steps, seq):
+    """u[step][v] for many steps at once (same layout as ``uniforms``)."""
+    steps = np.asarray(steps, dtype=np.uint64)[:, None]
+    v = np.arange(vocab, dtype=np.uint64)[None, :]
+    words = philox4x64_10((v >> U64(2), steps, U64(seq), U64(0)), (seed & 0xFFFFFFFFFFFFFFFF, 0))
+    w = np.stack(np.broadcast_arrays(*words), axis=0)
+    sel = np.broadcast_to((v & U64(3)).astype(np.int64), w.shape[1:])
+    r = np.take_along_axis(w, sel[None], axis=0)[0]
+    return (((r >> U64(40)).astype(np.float64) + 0.5) * 2.0 ** -24).astype(np.float32)

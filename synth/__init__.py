@@ -1,0 +1,256 @@
+"""Seeded synthetic inputs: model tensors in GGUF block layout, prompts, preset KV.
+
+This module produces inputs only.  It holds none of the forward pass: it draws
+normal weights, encodes them into Q8_0 / Q4_0 blocks (the encoder is how a GGUF
+file is made offline; the decoder path only ever decodes), and draws token ids.
+Both the CPU oracle and the GPU library are fed from here and from nowhere else.
+
+Recipe (per tensor): numpy ``Generator(PCG64(SeedSequence([seed, tag_lo, tag_hi,
+chunk])))`` where tag is the first 8 bytes of sha256(tensor name) and chunk
+indexes fixed row ranges of about 4M values, so large tensors are drawn in
+parallel with a result independent of the thread count.
+  * 2-D matrices: N(0, 0.02), then block-encoded in the config's type
+  * 1-D gains: 1 + N(0, 0.02), float32
+  * prompts: uniform ids in [0, vocab)
+  * preset K/V (batched long-context workload): N(0, 1) float32
+
+Block layouts (GGUF's public layout; 32 values per block, blocks run along the
+input dimension of each output row, a row padded with zeros to whole blocks):
+  Q8_0: little-endian fp16 scale d, then 32 int8 q            -> 34 bytes
+  Q4_0: little-endian fp16 scale d, then 16 bytes; byte j holds element j in
+        its low nibble and element j+16 in its high nibble, value = d*(n-8)
+                                                              -> 18 bytes
+"""
+import hashlib
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass
+
+import numpy as np
+
+from . import configs
+from .configs import CONFIGS, get, layer_is_global  # noqa: F401
+
+# ggml type ids (the numbering a GGUF file uses)
+T_F32 = 0
+T_Q4_0 = 2
+T_Q8_0 = 8
+TYPE_IDS = {"f32": T_F32, "q4_0": T_Q4_0, "q8_0": T_Q8_0}
+BLOCK = 32
+BLOCK_BYTES = {T_Q8_0: 34, T_Q4_0: 18}
+
+Q8_DTYPE = np.dtype([("d", "<f2"), ("qs", "i1", (32,))])
+Q4_DTYPE = np.dtype([("d", "<f2"), ("qs", "u1", (16,))])
+assert Q8_DTYPE.itemsize == 34 and Q4_DTYPE.itemsize == 18
+
+
+@dataclass
+class SynthTensor:
+    name: str
+    type: int          # ggml type id
+    rows: int          # output dimension (1 for gains)
+    cols: int          # logical input dimension
+    data: np.ndarray   # raw bytes, uint8, GGUF block layout
+
+    @property
+    def nbytes(self):
+        return int(self.data.nbytes)
+
+    def sha256(self):
+        return hashlib.sha256(self.data.tobytes()).hexdigest()
+
+
+def n_blocks(cols):
+    return (cols + BLOCK - 1) // BLOCK
+
+
+def tensor_nbytes(ttype, rows, cols):
+    if ttype == T_F32:
+        return rows * cols * 4
+    return rows * n_blocks(cols) * BLOCK_BYTES[ttype]
+
+
+def _threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _tag(name):
+    h = hashlib.sha256(name.encode()).digest()[:8]
+    v = int.from_bytes(h, "little")
+    return [v & 0xFFFFFFFF, v >> 32]
+
+
+def _rng(seed, name, chunk):
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed] + _tag(name) + [chunk])))
+
+
+# ---------------------------------------------------------------- encoders
+def encode_q8_0(x):
+    """f32 [rows][cols] -> Q8_0 blocks [rows][nblk] (structured, 34 B each).
+
+    Per block: amax = max|x|, d = fp16(amax/127), q = clamp(rint(x/d), -127, 127),
+    with x/d taken in f32 against the fp16-rounded d; an all-zero block stores
+    d = 0, q = 0.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    rows, cols = x.shape
+    nb = n_blocks(cols)
+    if nb * BLOCK != cols:
+        x = np.concatenate([x, np.zeros((rows, nb * BLOCK - cols), np.float32)], axis=1)
+    xb = x.reshape(rows, nb, BLOCK)
+    amax = np.max(np.abs(xb), axis=2)
+    d16 = (amax / np.float32(127.0)).astype(np.float16)
+    d32 = d16.astype(np.float32)
+    safe = np.where(d32 == 0, np.float32(1.0), d32)
+    q = np.rint(xb / safe[..., None])
+    np.clip(q, -127, 127, out=q)
+    q[d32 == 0] = 0
+    out = np.empty((rows, nb), dtype=Q8_DTYPE)
+    out["d"] = d16
+    out["qs"] = q.astype(np.int8)
+    return out
+
+
+def encode_q4_0(x):
+    """f32 [rows][cols] -> Q4_0 blocks [rows][nblk] (structured, 18 B each).
+
+    Per block: amax = max|x|, d = fp16(amax/8), n = clamp(rint(x/d), -8, 7) + 8;
+    byte j = n[j] | n[j+16] << 4.  An all-zero block stores d = 0, n = 8.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    rows, cols = x.shape
+    nb = n_blocks(cols)
+    if nb * BLOCK != cols:
+        x = np.concatenate([x, np.zeros((rows, nb * BLOCK - cols), np.float32)], axis=1)
+    xb = x.reshape(rows, nb, BLOCK)
+    amax = np.max(np.abs(xb), axis=2)
+    d16 = (amax / np.float32(8.0)).astype(np.float16)
+    d32 = d16.astype(np.float32)
+    safe = np.where(d32 == 0, np.float32(1.0), d32)
+    n = np.rint(xb / safe[..., None])
+    np.clip(n, -8, 7, out=n)
+    n[d32 == 0] = 0
+    n = (n + 8).astype(np.uint8)
+    out = np.empty((rows, nb), dtype=Q4_DTYPE)
+    out["d"] = d16
+    out["qs"] = n[..., :16] | (n[..., 16:] << 4)
+    return out
+
+
+def encode(ttype, x):
+    """Encode an f32 matrix into raw GGUF bytes (uint8, flat)."""
+    x = np.asarray(x, dtype=np.float32)
+    if ttype == T_F32:
+        return np.ascontiguousarray(x).view(np.uint8).reshape(-1).copy()
+    blocks = encode_q8_0(x) if ttype == T_Q8_0 else encode_q4_0(x)
+    return blocks.view(np.uint8).reshape(-1)
+
+
+# ---------------------------------------------------------------- tensors
+def tensor_specs(cfg):
+    """List of (name, type id, rows, cols, kind) for a config, kind in {matrix, gain}."""
+    H, hd = cfg["hidden"], cfg["head_dim"]
+    qd, kd, F, V = cfg["n_head"] * hd, cfg["n_head_kv"] * hd, cfg["ffn"], cfg["vocab"]
+    wt = TYPE_IDS[cfg["wtype"]]
+    specs = [("token_embd.weight", TYPE_IDS[cfg["embd_type"]], V, H, "matrix")]
+    for i in range(cfg["n_layer"]):
+        p = f"blk.{i}."
+        specs += [
+            (p + "attn_norm.weight", T_F32, 1, H, "gain"),
+            (p + "attn_q.weight", wt, qd, H, "matrix"),
+            (p + "attn_k.weight", wt, kd, H, "matrix"),
+            (p + "attn_v.weight", wt, kd, H, "matrix"),
+        ]
+        if cfg["qk_norm"]:
+            specs += [(p + "attn_q_norm.weight", T_F32, 1, hd, "gain"),
+                      (p + "attn_k_norm.weight", T_F32, 1, hd, "gain")]
+        specs += [(p + "attn_output.weight", wt, H, qd, "matrix")]
+        if cfg["sandwich_norm"]:
+            specs += [(p + "post_attention_norm.weight", T_F32, 1, H, "gain")]
+        specs += [
+            (p + "ffn_norm.weight", T_F32, 1, H, "gain"),
+            (p + "ffn_gate.weight", wt, F, H, "matrix"),
+            (p + "ffn_up.weight", wt, F, H, "matrix"),
+            (p + "ffn_down.weight", wt, H, F, "matrix"),
+        ]
+        if cfg["sandwich_norm"]:
+            specs += [(p + "post_ffw_norm.weight", T_F32, 1, H, "gain")]
+    specs += [("output_norm.weight", T_F32, 1, H, "gain")]
+    if not cfg["tied"]:
+        specs += [("output.weight", TYPE_IDS[cfg["wtype"]], V, H, "matrix")]
+    return specs
+
+
+def _chunk_rows(cols):
+    return max(1, (1 << 22) // max(1, cols))
+
+
+def _gen_tensor(seed, name, ttype, rows, cols, kind, pool):
+    if kind == "gain":
+        x = 1.0 + 0.02 * _rng(seed, name, 0).standard_normal(cols, dtype=np.float32)
+        return SynthTensor(name, T_F32, 1, cols, x.astype(np.float32).view(np.uint8).copy())
+    cr = _chunk_rows(cols)
+    starts = list(range(0, rows, cr))
+    row_bytes = tensor_nbytes(ttype, 1, cols)
+    out = np.empty(rows * row_bytes, dtype=np.uint8)
+
+    def work(ci):
+        r0 = starts[ci]
+        r1 = min(rows, r0 + cr)
+        x = _rng(seed, name, ci).standard_normal((r1 - r0, cols), dtype=np.float32)
+        x *= np.float32(0.02)
+        out[r0 * row_bytes:r1 * row_bytes] = encode(ttype, x)
+
+    if pool is None or len(starts) == 1:
+        for ci in range(len(starts)):
+            work(ci)
+    else:
+        list(pool.map(work, range(len(starts))))
+    return SynthTensor(name, ttype, rows, cols, out)
+
+
+def generate(cfg, threads=None):
+    """Draw every tensor of a config.  Returns {name: SynthTensor}."""
+    seed = cfg["seed"]
+    specs = tensor_specs(cfg)
+    nt = threads or _threads()
+    with ThreadPoolExecutor(nt) as pool:
+        tensors = {}
+        for name, ttype, rows, cols, kind in specs:
+            tensors[name] = _gen_tensor(seed, name, ttype, rows, cols, kind, pool)
+    return tensors
+
+
+def prompt(cfg, length=None, tag="prompt"):
+    """Prompt token ids, int32, uniform in [0, vocab)."""
+    n = cfg["prompt_len"] if length is None else length
+    return _rng(cfg["seed"], tag, 0).integers(0, cfg["vocab"], size=n).astype(np.int32)
+
+
+def first_tokens(cfg):
+    """First decode input per sequence of the batched preset-KV workload."""
+    return _rng(cfg["seed"], "first", 0).integers(0, cfg["vocab"], size=cfg["batch"]).astype(np.int32)
+
+
+def preset_kv(cfg, seq, layer, n_pos=None):
+    """Preset post-RoPE K and V for one (sequence, layer): two f32 [n_kv][n_pos][head_dim]."""
+    n = cfg["preset_kv"] if n_pos is None else n_pos
+    shape = (cfg["n_head_kv"], n, cfg["head_dim"])
+    r = _rng(cfg["seed"], f"kv.{seq}.{layer}", 0)
+    k = r.standard_normal(shape, dtype=np.float32)
+    v = r.standard_normal(shape, dtype=np.float32)
+    return k, v
+
+
+def manifest(tensors):
+    """{name: sha256} of every tensor's bytes, for reports."""
+    return {n: t.sha256() for n, t in tensors.items()}
+
+
+def weight_bytes(cfg):
+    """Bytes of every block-encoded matrix (algorithmic weight traffic of one decode step)."""
+    return sum(tensor_nbytes(t, r, c) for _, t, r, c, k in tensor_specs(cfg) if k == "matrix")

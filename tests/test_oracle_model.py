@@ -1,0 +1,190 @@
+"""Pins for oracle.model: closed forms on hand-built models and invariants on
+seeded ones (CPU only)."""
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import OracleModel, ops
+
+TINY = dict(name="pin", n_layer=2, hidden=16, n_head=4, n_head_kv=2, head_dim=4, ffn=12, vocab=10,
+            rms_eps=1e-6, rope_theta=1e4, rope_theta_local=1e4, window=0, window_period=0,
+            qk_norm=False, sandwich_norm=False, act="silu", wtype="f32", embd_type="f32", tied=True,
+            seed=7, prompt_len=6, decode_steps=3, batch=1, temperature=0.0, preset_kv=0)
+
+
+def f32_model(cfg, fill):
+    """Tensors of ``cfg`` as f32 records; fill(name, rows, cols) -> array."""
+    out = {}
+    for name, _t, rows, cols, _k in synth.tensor_specs(cfg):
+        a = np.asarray(fill(name, rows, cols), dtype=np.float32).reshape(rows, cols)
+        out[name] = synth.SynthTensor(name, synth.T_F32, rows, cols, a.view(np.uint8).reshape(-1).copy())
+    return out
+
+
+def rand_embed_zero_rest(seed):
+    r = np.random.default_rng(seed)
+
+    def fill(name, rows, cols):
+        if name == "token_embd.weight":
+            return r.standard_normal((rows, cols))
+        if rows == 1:
+            return 1 + 0.1 * r.standard_normal(cols)
+        return np.zeros((rows, cols))
+    return fill
+
+
+def test_zero_layers_pass_residual_through():
+    m_t = f32_model(TINY, rand_embed_zero_rest(1))
+    m = OracleModel(TINY, m_t, max_ctx=8)
+    toks = [3, 0, 9, 3]
+    logits = m.forward(0, toks, all_logits=True)
+    E = np.frombuffer(m_t["token_embd.weight"].data.tobytes(), np.float32).reshape(10, 16).astype(np.float64)
+    g = np.frombuffer(m_t["output_norm.weight"].data.tobytes(), np.float32).astype(np.float64)
+    for i, t in enumerate(toks):
+        e = E[t]
+        xn = e / math.sqrt(np.mean(e * e) + 1e-6) * g
+        assert np.allclose(logits[i], E @ xn, rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("rv,head", [(5, 0), (5, 2), (5, 3), (2, 1), (2, 3)])
+def test_one_hot_v_and_o_with_uniform_attention(rv, head):
+    """Q = K = 0 makes attention uniform over the prefix.  attn_v one-hot at
+    (rv, cv) and attn_output one-hot at (ro, co) give, per position t,
+    x_t[ro] += wo * mean_{j<=t}(wv * h_j[cv]) iff column co reads a query head of
+    the KV head that owns rv (GQA by repeat).  Pins the orientation of attn_v
+    (8 x 16) and of the square attn_output (16 x 16), and the head mapping."""
+    cfg = dict(TINY, n_layer=1)
+    hd, group = 4, 2
+    g_kv = rv // hd
+    co = head * hd + rv % hd
+    reads = head // group == g_kv
+    cv, ro, wv, wo = 11, 6, 0.75, -1.25
+    base = rand_embed_zero_rest(2)
+
+    def fill(name, rows, cols):
+        if name.endswith("attn_v.weight"):
+            a = np.zeros((rows, cols)); a[rv, cv] = wv; return a
+        if name.endswith("attn_output.weight"):
+            a = np.zeros((rows, cols)); a[ro, co] = wo; return a
+        return base(name, rows, cols)
+    t = f32_model(cfg, fill)
+    m = OracleModel(cfg, t, max_ctx=8)
+    toks = [1, 4, 4, 7, 2]
+    x = m.hidden(0, toks)
+    E = np.frombuffer(t["token_embd.weight"].data.tobytes(), np.float32).reshape(10, 16).astype(np.float64)
+    ga = np.frombuffer(t["blk.0.attn_norm.weight"].data.tobytes(), np.float32).astype(np.float64)
+    h = np.array([E[k] / math.sqrt(np.mean(E[k] ** 2) + 1e-6) * ga for k in toks])
+    for i in range(len(toks)):
+        want = E[toks[i]].copy()
+        if reads:
+            want[ro] += wo * np.mean(wv * h[:i + 1, cv])
+        assert np.allclose(x[i], want, rtol=1e-13, atol=1e-14)
+
+
+def test_window_one_makes_every_position_independent():
+    """Window 1 on every layer: each position attends only to itself, so the
+    logits of a token do not depend on its position or neighbours, except through
+    RoPE, which cancels for a query against its own key."""
+    cfg = dict(TINY, window=1, window_period=100, qk_norm=True)
+    t = synth.generate(dict(cfg, wtype="q8_0"), threads=1)
+    m = OracleModel(cfg, t, max_ctx=16)
+    a = m.forward(0, [5, 2, 7, 2, 9, 5], all_logits=True)
+    assert np.allclose(a[1], a[3], rtol=1e-12)
+    assert np.allclose(a[0], a[5], rtol=1e-12)
+    m.reset()
+    b = m.forward(0, [2], all_logits=True)
+    assert np.allclose(a[1], b[0], rtol=1e-12)
+
+
+VARIANTS = {
+    "llama": dict(TINY, wtype="q8_0"),
+    "qwen3": dict(TINY, wtype="q8_0", qk_norm=True, rope_theta=1e6, rope_theta_local=1e6),
+    "gemma3": dict(TINY, wtype="q8_0", qk_norm=True, sandwich_norm=True, act="gelu_tanh",
+                   window=3, window_period=2, rope_theta=1e6, rope_theta_local=1e4, n_head_kv=1),
+    "q4": dict(TINY, wtype="q4_0", embd_type="q4_0", tied=False, ffn=40),
+}
+
+
+@pytest.mark.parametrize("variant", sorted(VARIANTS))
+def test_kv_cached_decode_equals_full_recompute(variant):
+    cfg = VARIANTS[variant]
+    t = synth.generate(cfg, threads=1)
+    toks = list(synth.prompt(cfg, 9))
+    full = OracleModel(cfg, t, max_ctx=16).forward(0, toks, all_logits=True)
+    m = OracleModel(cfg, t, max_ctx=16)
+    rows = [m.forward(0, toks[:4], all_logits=True)]
+    for tok in toks[4:]:
+        rows.append(m.forward(0, [tok]))
+    inc = np.concatenate(rows, axis=0)
+    assert np.allclose(inc, full, rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("variant", sorted(VARIANTS))
+def test_causality(variant):
+    cfg = VARIANTS[variant]
+    t = synth.generate(cfg, threads=1)
+    toks = list(synth.prompt(cfg, 8))
+    a = OracleModel(cfg, t, max_ctx=16).forward(0, toks, all_logits=True)
+    toks2 = toks[:5] + [(x + 1) % cfg["vocab"] for x in toks[5:]]
+    b = OracleModel(cfg, t, max_ctx=16).forward(0, toks2, all_logits=True)
+    assert np.array_equal(a[:5], b[:5])
+    assert not np.allclose(a[5:], b[5:])
+
+
+def test_split_prefill_equals_single_prefill():
+    cfg = VARIANTS["qwen3"]
+    t = synth.generate(cfg, threads=1)
+    toks = list(synth.prompt(cfg, 10))
+    one = OracleModel(cfg, t, max_ctx=16).forward(0, toks)
+    m = OracleModel(cfg, t, max_ctx=16)
+    m.forward(0, toks[:6])
+    two = m.forward(0, toks[6:])
+    assert np.allclose(one, two, rtol=1e-11, atol=1e-13)
+
+
+def test_sequences_are_independent_and_reset_reproduces():
+    cfg = VARIANTS["llama"]
+    t = synth.generate(cfg, threads=1)
+    m = OracleModel(cfg, t, max_ctx=16, n_seqs=2)
+    a = m.forward(0, [1, 2, 3])
+    m.forward(1, [4, 4, 4, 4])
+    b = m.forward(0, [5])
+    m.reset(0)
+    assert np.array_equal(m.forward(0, [1, 2, 3]), a)
+    assert np.array_equal(m.forward(0, [5]), b)
+
+
+def test_untied_head_uses_output_weight():
+    cfg = VARIANTS["q4"]
+    t = synth.generate(cfg, threads=1)
+    m = OracleModel(cfg, t, max_ctx=8)
+    assert m.lm_head_name() == "output.weight"
+    tied = OracleModel(VARIANTS["llama"], synth.generate(VARIANTS["llama"], threads=1), max_ctx=8)
+    assert tied.lm_head_name() == "token_embd.weight"
+
+
+def test_quantized_embedding_rows_match_full_decode():
+    cfg = VARIANTS["q4"]
+    t = synth.generate(cfg, threads=1)
+    m = OracleModel(cfg, t, max_ctx=8)
+    from oracle import blocks
+    te = t["token_embd.weight"]
+    full = blocks.dequant(te.type, te.data, te.rows, te.cols)
+    assert np.array_equal(m.embed([3, 0, 3]), full[[3, 0, 3]].astype(np.float64))
+
+
+def test_rmsnorm_and_rope_order_in_block():
+    """Per-head norm happens before RoPE: with an all-equal gain the order does
+    not matter (RoPE keeps the head's norm), with a non-uniform gain it does."""
+    x = np.random.default_rng(3).standard_normal((1, 1, 8))
+    ang = ops.rope_angles([3], ops.rope_inv_freq(1e4, 8))
+    w1 = np.full(8, 1.3)
+    a = ops.apply_rope(ops.rmsnorm(x, w1, 1e-6), ang)
+    b = ops.rmsnorm(ops.apply_rope(x, ang), w1, 1e-6)
+    assert np.allclose(a, b, rtol=1e-12)
+    w2 = np.linspace(0.5, 2.0, 8)
+    a = ops.apply_rope(ops.rmsnorm(x, w2, 1e-6), ang)
+    b = ops.rmsnorm(ops.apply_rope(x, ang), w2, 1e-6)
+    assert not np.allclose(a, b)

@@ -1,0 +1,84 @@
+"""Pins for oracle.sampler (CPU only).
+
+Philox4x64-10 is checked against numpy's own implementation of the same
+generator (numpy.random.Philox, which advances its counter by one before each
+block of four words).  The Gumbel-max sampler is checked against the target
+distribution softmax(logits / T) with a chi-square test.
+"""
+import numpy as np
+import pytest
+from scipy import stats
+
+from oracle import sampler
+
+KEYS = [(0, 0), (5, 0), (0x1234567890ABCDEF, 0x0FEDCBA987654321), (2 ** 64 - 1, 2 ** 64 - 1)]
+CTRS = [(1, 0, 0, 0), (5, 7, 11, 13), (2 ** 64 - 1, 3, 2 ** 63, 1), (99, 0, 15, 0)]
+
+
+@pytest.mark.parametrize("key", KEYS)
+@pytest.mark.parametrize("ctr", CTRS)
+def test_philox_matches_numpy(key, ctr):
+    c = list(ctr)
+    # numpy increments the 256-bit counter before generating; start one below
+    if c[0] == 0:
+        pytest.skip("needs a borrow")
+    prev = np.array([c[0] - 1, c[1], c[2], c[3]], dtype=np.uint64)
+    bg = np.random.Philox(counter=prev, key=np.array(key, dtype=np.uint64))
+    want = [int(x) for x in bg.random_raw(4)]
+    got = [int(x) for x in sampler.philox4x64_10([np.uint64(x) for x in c], key)]
+    assert got == want
+
+
+def test_philox_vectorised_equals_scalar():
+    ctr0 = np.arange(10, dtype=np.uint64)
+    vec = sampler.philox4x64_10((ctr0, np.uint64(3), np.uint64(4), np.uint64(0)), (9, 0))
+    for i in range(10):
+        sc = sampler.philox4x64_10((np.uint64(i), np.uint64(3), np.uint64(4), np.uint64(0)), (9, 0))
+        assert [int(v[i]) for v in vec] == [int(s) for s in sc]
+
+
+def test_uniforms_layout_and_range():
+    u = sampler.uniforms(37, seed=5, step=2, seq=3)
+    assert u.dtype == np.float32 and u.shape == (37,)
+    assert (u > 0).all() and (u < 1).all()
+    # element v takes word v % 4 of counter (v // 4, step, seq, 0)
+    w = sampler.philox4x64_10((np.uint64(6), np.uint64(2), np.uint64(3), np.uint64(0)), (5, 0))
+    r = int(w[1])
+    assert u[25] == np.float32(((r >> 40) + 0.5) * 2.0 ** -24)
+    ub = sampler.uniforms_batch(37, 5, [0, 2], 3)
+    assert np.array_equal(ub[1], u)
+
+
+def test_uniforms_are_uniform():
+    u = sampler.uniforms_batch(64, 5, np.arange(2000), 0).reshape(-1).astype(np.float64)
+    assert stats.kstest(u, "uniform").pvalue > 1e-3
+
+
+@pytest.mark.parametrize("temperature", [1.0, 0.5])
+def test_gumbel_max_samples_softmax(temperature):
+    logits = np.array([0.3, -1.0, 2.0, 0.0, 1.1, -0.4, 0.9, 1.6])
+    n = 100_000
+    u = sampler.uniforms_batch(8, 5, np.arange(n), 1).astype(np.float64)
+    draws = np.argmax(logits / temperature - np.log(-np.log(u)), axis=1)
+    p = np.exp(logits / temperature - np.max(logits / temperature))
+    p /= p.sum()
+    obs = np.bincount(draws, minlength=8)
+    chi2 = stats.chisquare(obs, p * n)
+    assert chi2.pvalue > 1e-4
+    # the scalar path takes the same decision as the batched one
+    for s in range(5):
+        assert sampler.sample(logits, temperature, 5, s, 1) == draws[s]
+
+
+def test_low_temperature_is_greedy_and_reproducible():
+    logits = np.array([0.1, 3.0, 2.0, -1.0, 2.9])
+    for s in range(20):
+        assert sampler.sample(logits, 1e-3, 5, s, 0) == 1
+    assert sampler.sample(logits, 1.0, 5, 7, 2) == sampler.sample(logits, 1.0, 5, 7, 2)
+    draws = {sampler.sample(np.zeros(16), 1.0, 5, s, 0) for s in range(60)}
+    assert len(draws) > 8  # flat logits: many different tokens over steps
+
+
+def test_greedy_ties_lowest_index():
+    assert sampler.greedy([2.0, 5.0, 5.0]) == 1
+    assert sampler.sample([2.0, 5.0, 5.0], 0.0, 1, 1, 1) == 1
