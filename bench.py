@@ -1,0 +1,199 @@
+"""Throughput of the quantized decoder forward pass on one MI355X.
+
+One step = kv_reset, prefill of the prompt, then the decode steps (greedy, the
+token chained on the device), all on seeded synthetic weights of the workload's
+shape.  Prints one JSON line:
+  value        decode tokens/s (whole job, one GPU)
+  prefill_*    prefill tokens/s and FP32-MFMA utilisation
+  hbm_frac     decode algorithmic bytes per step / decode time / 8 TB/s
+  roofline     the dominant kernel's algorithmic bytes / its average launch time
+               (HIP events on the launch stream, over a second pass of the timed steps)
+  cpu_baseline the CPU oracle timed on a bounded sample of the same workload
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
+FP32_MFMA_PEAK = 157.3e12  # FLOP/s, MI355X dense FP32 matrix
+
+
+def step_bytes_decode(cfg, pos):
+    """Algorithmic HBM bytes of one decode step at KV length ``pos`` (before the step)."""
+    import synth
+    B = cfg["batch"]
+    specs = synth.tensor_specs(cfg)
+    layer_w = sum(synth.tensor_nbytes(t, r, c) for n, t, r, c, k in specs if k == "matrix" and n.startswith("blk."))
+    embd = [s for s in specs if s[0] == "token_embd.weight"][0]
+    embd_bytes = synth.tensor_nbytes(embd[1], embd[2], embd[3])
+    head = [s for s in specs if s[0] == "output.weight"]
+    head_bytes = synth.tensor_nbytes(head[0][1], head[0][2], head[0][3]) if head else embd_bytes
+    row = embd_bytes / embd[2]
+    kv = 0
+    for l in range(cfg["n_layer"]):
+        n_keys = pos + 1
+        if not synth.layer_is_global(cfg, l):
+            n_keys = min(n_keys, cfg["window"])
+        kv += cfg["n_head_kv"] * cfg["head_dim"] * 8 * (n_keys + 1)  # read keys + write the new one
+    return layer_w + head_bytes + B * (kv + row + cfg["vocab"] * 4)
+
+
+def prefill_flops(cfg, T):
+    H, hd, nq, nkv, F, V = (cfg[k] for k in ("hidden", "head_dim", "n_head", "n_head_kv", "ffn", "vocab"))
+    lin = 2 * T * (H * (nq + 2 * nkv) * hd + nq * hd * H + 3 * H * F)
+    attn = 0
+    for l in range(cfg["n_layer"]):
+        import synth
+        w = 0 if synth.layer_is_global(cfg, l) else cfg["window"]
+        keys = sum(min(i + 1, w) if w else i + 1 for i in range(T))
+        attn += 4 * hd * nq * keys
+    return cfg["n_layer"] * lin + attn + 2 * V * H
+
+
+def cpu_baseline(cfg, tensors, budget_s=20.0):
+    """The oracle as it stands, timed on the host: a short prefill, then decode
+    steps until the budget is spent.  Returns decode tokens/s and the sample."""
+    from oracle import OracleModel
+    import synth
+    cores = len(os.sched_getaffinity(0))
+    T0 = min(32, cfg["prompt_len"])
+    om = OracleModel(cfg, tensors, max_ctx=T0 + 64)
+    prompt = synth.prompt(cfg, T0)
+    t0 = time.perf_counter()
+    logits = om.forward(0, prompt)
+    t_pre = time.perf_counter() - t0
+    tok = int(np.argmax(logits[-1]))
+    n, t_dec = 0, 0.0
+    while n < 48 and (t_dec < budget_s or n < 2):
+        t0 = time.perf_counter()
+        logits = om.forward(0, [tok])
+        t_dec += time.perf_counter() - t0
+        tok = int(np.argmax(logits[-1]))
+        n += 1
+    return dict(value=n / t_dec, unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"{cfg['name']}: {T0}-token prefill ({t_pre:.1f} s, {T0 / t_pre:.1f} tokens/s), then {n} "
+                       f"greedy decode steps timed ({t_dec:.1f} s), float64 numpy, {cores} host threads")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", default="c2")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path has no multi-GPU mode",
+              file=sys.stderr)
+        sys.exit(2)
+
+    cores = len(os.sched_getaffinity(0))
+    os.environ.setdefault("OMP_NUM_THREADS", str(cores))
+    os.environ.setdefault("OPENBLAS_NUM_THREADS", str(cores))
+    import torch
+
+    import decoder_gguf_quantized_amd as qdec
+    import synth
+
+    cfg = synth.get(args.config)
+    if cfg["preset_kv"]:
+        print("bench.py: the batched preset-KV workload is measured by its own mode (not yet built)", file=sys.stderr)
+        sys.exit(2)
+    t_gen = time.perf_counter()
+    tensors = synth.generate(cfg)
+    t_gen = time.perf_counter() - t_gen
+    dev = torch.device("cuda:0")
+    T, N, V = cfg["prompt_len"], cfg["decode_steps"], cfg["vocab"]
+    prompt = synth.prompt(cfg)
+    model = qdec.Model(cfg, tensors, max_seqs=1, max_ctx=T + N + 1)
+    pl = torch.empty(V, dtype=torch.float32, device=dev)
+    dl = torch.empty((N, V), dtype=torch.float32, device=dev)
+    toks = torch.empty((N + 1, 1), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def one_step(ev):
+        model.kv_reset()
+        ev[0].record(stream)
+        model.prefill(0, prompt, pl, toks[0])
+        ev[1].record(stream)
+        for s in range(N):
+            model.decode_step(toks[s], dl[s:s + 1], toks[s + 1])
+        ev[2].record(stream)
+
+    def run(k):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(k)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(k):
+            one_step(evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        pre = [e[0].elapsed_time(e[1]) for e in evs]
+        dec = [e[1].elapsed_time(e[2]) for e in evs]
+        return wall, pre, dec
+
+    for _ in range(args.warmup):
+        run(1)
+    wall, pre_ms, dec_ms = run(args.steps)
+    # second pass of the same steps with per-kernel events for the roofline figure
+    model.kernel_timing(True)
+    run(args.steps)
+    kst = model.kernel_timing(False)
+    model.close()
+
+    dec_tok_s = args.steps * N / (sum(dec_ms) / 1e3)
+    pre_tok_s = args.steps * T / (sum(pre_ms) / 1e3)
+    bytes_dec = sum(step_bytes_decode(cfg, T + s) for s in range(N))
+    hbm_frac = bytes_dec / (np.mean(dec_ms) / 1e3) / HBM_PEAK
+    mfma_util = prefill_flops(cfg, T) / (np.mean(pre_ms) / 1e3) / FP32_MFMA_PEAK
+    dom = max(kst.items(), key=lambda kv: kv[1]["ms"])
+    dname, d = dom
+    if d["flops"] and d["bytes"] and dname.startswith("gemm"):
+        achieved = d["flops"] / (d["ms"] / 1e3) / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=157.3, unit="TFLOP/s",
+                    frac=round(achieved / 157.3, 4), traffic=None)
+    else:
+        achieved = d["bytes"] / (d["ms"] / 1e3) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=8000.0, unit="GB/s",
+                    frac=round(achieved / 8000.0, 4), traffic=None)
+    roof.update(kernel=dname, launches=d["launches"], avg_launch_us=round(d["ms"] * 1e3 / d["launches"], 2),
+                bytes_per_launch=round(d["bytes"] / d["launches"]))
+    line = {
+        "metric": "decode tokens/sec + HBM GB/s fraction; prefill tokens/sec + MFMA util",
+        "value": round(dec_tok_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg['name']}, {cfg['wtype'].upper()} weights, prompt {T}, decode {N} greedy, batch 1",
+                   "prompt": T, "decode_steps": N, "batch": 1, "weights": cfg["wtype"]},
+        "prefill_tokens_per_s": round(pre_tok_s, 1),
+        "prefill_mfma_util": round(float(mfma_util), 4),
+        "decode_hbm_frac": round(float(hbm_frac), 4),
+        "decode_ms_per_token": round(float(np.mean(dec_ms)) / N, 4),
+        "roofline": roof,
+        "kernels": {k: dict(launches=v["launches"], ms=round(v["ms"], 3)) for k, v in sorted(kst.items())},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, tensors)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

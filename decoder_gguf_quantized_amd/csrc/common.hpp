@@ -1,0 +1,110 @@
+// Device helpers shared by the gfx950 kernels: wave64 reductions over DPP,
+// fp16 scale loads, the argmax ordering and the Philox4x64-10 generator.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define QD_DEV __device__ __forceinline__
+
+namespace qd {
+
+constexpr int kWave = 64;
+
+// ggml type ids
+constexpr int kF32 = 0;
+constexpr int kQ4_0 = 2;
+constexpr int kQ8_0 = 8;
+
+template <int CTRL, int ROW_MASK = 0xf>
+QD_DEV float dpp_add(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, true));
+}
+
+// Sum over lane groups of G consecutive lanes (G in {8, 16, 32, 64}); every
+// lane of a group receives its group's sum.
+template <int G>
+QD_DEV float group_sum(float v) {
+  v = dpp_add<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_add<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = dpp_add<0x141>(v);  // row_half_mirror: 8-lane sums
+  if constexpr (G >= 16) v = dpp_add<0x140>(v);  // row_mirror: 16-lane sums
+  if constexpr (G >= 32) v += __shfl_xor(v, 16);
+  if constexpr (G >= 64) v += __shfl_xor(v, 32);
+  return v;
+}
+
+// Full-wave sum, returned uniformly to every lane.
+QD_DEV float wave_sum(float v) {
+  v = dpp_add<0xB1>(v);
+  v = dpp_add<0x4E>(v);
+  v = dpp_add<0x141>(v);
+  v = dpp_add<0x140>(v);
+  v = dpp_add<0x142, 0xa>(v);  // row_bcast:15 into rows 1, 3
+  v = dpp_add<0x143, 0xc>(v);  // row_bcast:31 into rows 2, 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+QD_DEV float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+QD_DEV float half_bits_to_float(uint16_t h) {
+  _Float16 f = __builtin_bit_cast(_Float16, h);
+  return (float)f;
+}
+
+QD_DEV float load_half(const uint16_t* p) { return half_bits_to_float(*p); }
+
+// v & m through an opaque instruction, so that the byte-wise conversions of the
+// masked word stay v_cvt_f32_ubyteN instead of being folded into bit-field
+// extracts (one extra op per element).
+QD_DEV uint32_t opaque_and(uint32_t v, uint32_t m) {
+  uint32_t r;
+  asm volatile("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(v), "v"(m));
+  return r;
+}
+
+// Argmax ordering: (a, ia) ranks before (b, ib).  NaN ranks above every number,
+// equal values go to the lower index.
+QD_DEV bool ranks_before(float a, int ia, float b, int ib) {
+  bool an = a != a, bn = b != b;
+  if (an || bn) return an && bn ? ia < ib : an;
+  return a > b || (a == b && ia < ib);
+}
+
+// Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two 64x64->128
+// multiplies with the paper's multipliers, key bumped by its Weyl constants.
+struct u64x4 {
+  uint64_t v[4];
+};
+
+QD_DEV u64x4 philox4x64_10(u64x4 c, uint64_t k0, uint64_t k1) {
+  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += W0;
+      k1 += W1;
+    }
+    uint64_t hi0 = __umul64hi(M0, c.v[0]), lo0 = M0 * c.v[0];
+    uint64_t hi1 = __umul64hi(M1, c.v[2]), lo1 = M1 * c.v[2];
+    u64x4 n;
+    n.v[0] = hi1 ^ c.v[1] ^ k0;
+    n.v[1] = lo1;
+    n.v[2] = hi0 ^ c.v[3] ^ k1;
+    n.v[3] = lo0;
+    c = n;
+  }
+  return c;
+}
+
+// Uniform in (0, 1) from the top 23 bits: ((r >> 41) + 0.5) * 2^-23, computed as
+// the exact integer 2*(r>>41)+1 < 2^24 times 2^-24 (exact in f32).
+QD_DEV float philox_uniform(uint64_t r) {
+  uint32_t k = (uint32_t)(r >> 41) * 2u + 1u;
+  return (float)k * 5.9604644775390625e-08f;  // 2^-24
+}
+
+}  // namespace qd

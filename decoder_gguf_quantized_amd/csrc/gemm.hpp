@@ -1,0 +1,167 @@
+// Prefill projection: Y[t][n] = sum_k X[t][k] * W[n][k] for a whole prompt,
+// W block-quantized in HBM -- a dense contraction, so it runs on the matrix
+// cores (V_MFMA_F32_32X32X2_F32, f32 operands, f32 accumulation).
+//
+// Qwen3 walkthrough, "Overview" (prefill handles all prompt tokens at once) and
+// Steps 5-6 (`x @ W.T` projections); Synsema "Choose the engine": weights stay
+// quantized and are multiplied in f32.  Each weight tile is decoded exactly
+// (d * q) into LDS as f32 once per workgroup and reused by all 64 token rows
+// of the tile.
+//
+// Tiling: workgroup tile 64 tokens x 128 weight rows, BK = 32 (one quant block),
+// double-buffered LDS (k-major, so each MFMA operand read is 32 consecutive
+// floats).  Four waves in a 2 x 2 arrangement, each owning 32 tokens x 64 rows as
+// two 32x32 accumulators.  MFMA lane layout (32x32x2 f32): A[i][k] from lane
+// i + 32k, B[k][j] from lane j + 32k, D[i][j] in lane j + 32*((i/4)%2), register
+// (i%4) + 4*(i/8).
+#pragma once
+#include "common.hpp"
+#include "gemv.hpp"
+
+namespace qd {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+struct GemmArgs {
+  const uint8_t* qs;    // weights, same layout as GemvArgs
+  const uint16_t* d;
+  int rows;
+  int nblk;
+  const float* x;       // [T][ldx]
+  int ldx;
+  int T;
+  float* y;             // [T][ldy]
+  int ldy;
+};
+
+template <int QT, int MODE>
+__global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
+  constexpr int BM = 64, BN = 128, BK = 32;
+  constexpr int AP = BM + 4, BP = BN + 4;
+  __shared__ float As[2][BK][AP];
+  __shared__ float Bs[2][BK][BP];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int n0 = blockIdx.x * BN, t0 = blockIdx.y * BM;
+  const int kp = a.nblk * 32;
+
+  // staging registers
+  float4 xa[2];
+  uint4 wq;        // Q8_0: 16 int8; F32 uses wf[4]; Q4_0 uses the low 8 bytes
+  float4 wf[4];
+  float wd = 0.f;
+  const int brow = tid >> 1, bhalf = tid & 1;
+  const bool brow_ok = n0 + brow < a.rows;
+
+  auto load = [&](int kb) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      int idx = tid + 256 * i, row = idx >> 3, kq = idx & 7;
+      int t = t0 + row;
+      xa[i] = t < a.T ? *reinterpret_cast<const float4*>(a.x + (size_t)t * a.ldx + kb * BK + 4 * kq)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (brow_ok) {
+      size_t r = n0 + brow;
+      if constexpr (QT == kQ8_0) {
+        wq = *reinterpret_cast<const uint4*>(a.qs + r * kp + kb * BK + 16 * bhalf);
+        wd = load_half(a.d + r * a.nblk + kb);
+      } else if constexpr (QT == kQ4_0) {
+        uint2 v = *reinterpret_cast<const uint2*>(a.qs + (r * a.nblk + kb) * 16 + 8 * bhalf);
+        wq.x = v.x;
+        wq.y = v.y;
+        wd = load_half(a.d + r * a.nblk + kb);
+      } else {
+        const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.qs) + r * kp + kb * BK + 16 * bhalf);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wf[i] = p[i];
+      }
+    }
+  };
+
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      int idx = tid + 256 * i, row = idx >> 3, kq = idx & 7;
+      As[buf][4 * kq + 0][row] = xa[i].x;
+      As[buf][4 * kq + 1][row] = xa[i].y;
+      As[buf][4 * kq + 2][row] = xa[i].z;
+      As[buf][4 * kq + 3][row] = xa[i].w;
+    }
+    if constexpr (QT == kQ8_0) {
+      uint32_t w4[4] = {wq.x, wq.y, wq.z, wq.w};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float v = brow_ok ? wd * (float)(int8_t)(w4[i >> 2] >> (8 * (i & 3))) : 0.f;
+        Bs[buf][16 * bhalf + i][brow] = v;
+      }
+    } else if constexpr (QT == kQ4_0) {
+      uint32_t w2[2] = {wq.x, wq.y};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint32_t byte = (w2[i >> 2] >> (8 * (i & 3))) & 0xffu;
+        float lo = brow_ok ? wd * (float)((int)(byte & 15u) - 8) : 0.f;
+        float hi = brow_ok ? wd * (float)((int)(byte >> 4) - 8) : 0.f;
+        Bs[buf][8 * bhalf + i][brow] = lo;
+        Bs[buf][16 + 8 * bhalf + i][brow] = hi;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        Bs[buf][16 * bhalf + 4 * i + 0][brow] = brow_ok ? wf[i].x : 0.f;
+        Bs[buf][16 * bhalf + 4 * i + 1][brow] = brow_ok ? wf[i].y : 0.f;
+        Bs[buf][16 * bhalf + 4 * i + 2][brow] = brow_ok ? wf[i].z : 0.f;
+        Bs[buf][16 * bhalf + 4 * i + 3][brow] = brow_ok ? wf[i].w : 0.f;
+      }
+    }
+  };
+
+  f32x16 acc0, acc1;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0.f;
+
+  load(0);
+  store(0);
+  __syncthreads();
+  const int li = lane & 31, lk = lane >> 5;
+  for (int kb = 0; kb < a.nblk; ++kb) {
+    const int buf = kb & 1;
+    if (kb + 1 < a.nblk) load(kb + 1);
+#pragma unroll
+    for (int p = 0; p < BK / 2; ++p) {
+      float av = As[buf][2 * p + lk][wm * 32 + li];
+      float b0 = Bs[buf][2 * p + lk][wn * 64 + li];
+      float b1 = Bs[buf][2 * p + lk][wn * 64 + 32 + li];
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b0, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b1, acc1, 0, 0, 0);
+    }
+    if (kb + 1 < a.nblk) store(buf ^ 1);
+    __syncthreads();
+  }
+
+  constexpr bool kPair = MODE == kModePairSilu || MODE == kModePairGelu;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    int i = 8 * (r >> 2) + 4 * lk + (r & 3);
+    int t = t0 + wm * 32 + i;
+    if (t >= a.T) continue;
+    float* yr = a.y + (size_t)t * a.ldy;
+    int n = n0 + wn * 64 + li;
+    if constexpr (kPair) {
+      int nn = (n0 + wn * 64) / 2 + li;
+      if (n + 32 < a.rows) {
+        float g = acc0[r], u = acc1[r];
+        yr[nn] = (MODE == kModePairSilu ? act_silu(g) : act_gelu_tanh(g)) * u;
+      }
+    } else if constexpr (MODE == kModeAdd) {
+      if (n < a.rows) yr[n] += acc0[r];
+      if (n + 32 < a.rows) yr[n + 32] += acc1[r];
+    } else {
+      if (n < a.rows) yr[n] = acc0[r];
+      if (n + 32 < a.rows) yr[n + 32] = acc1[r];
+    }
+  }
+}
+
+}  // namespace qd

@@ -1,0 +1,252 @@
+// Decode projection: y[m][n] = sum_k W[n][k] * x[m][k] for a handful of input
+// rows (decode batch, 1..16), W block-quantized in HBM.
+//
+// Qwen3 walkthrough, Step 5 (Q/K/V/O projections `x @ W.T`) and Step 6 (SwiGLU);
+// Synsema "Choose the engine": the weights stay quantized and are multiplied in
+// f32 -- each block is decoded in registers (int8 / nibble -> f32, fp16 scale
+// applied once per block) and every product and sum is f32.
+//
+// Bandwidth design (decode is a weight stream, ~1 byte per weight):
+//   * scales and quants are split (SoA) so a lane issues one 16-byte load per
+//     unit (Q8_0: 16 weights, Q4_0: a whole 32-weight block, F32: 4 weights);
+//     64 lanes read 1 KB contiguous per row: fully coalesced.
+//   * each wave streams two rows at once; the input rows sit in LDS (RMSNorm
+//     prologue fused), so a unit's activations are read once for both rows.
+//   * the reduction over the 64 lanes is a DPP tree; lane 0 writes the result
+//     with the mode's epilogue (store, residual add, or gate/up pair with the
+//     activation: act(gate) * up).
+//   * Q8_0: int8 -> f32 is one SDWA conversion per weight.  Q4_0: nibbles are
+//     masked a word at a time and converted with v_cvt_f32_ubyteN; the offset 8
+//     is folded into the block as -8 * sum(x over the block), so the per-weight
+//     cost is one conversion and one FMA.
+#pragma once
+#include "common.hpp"
+
+namespace qd {
+
+enum { kModeStore = 0, kModeAdd = 1, kModePairSilu = 2, kModePairGelu = 3 };
+
+struct GemvArgs {
+  const uint8_t* qs;     // Q8_0: int8 [rows][kp]; Q4_0: u8 [rows][nblk][16]; F32: f32 [rows][kp]
+  const uint16_t* d;     // fp16 scales [rows][nblk] (quantized types)
+  int rows;              // weight rows
+  int nblk;              // 32-value blocks per row, kp = 32 * nblk
+  const float* x;        // input rows [m][ldx]; columns [0, kp) are read
+  int ldx;
+  const float* norm_w;   // RMSNorm gain [kp], or null for no prologue norm
+  float eps;
+  float* y;              // output rows [m][ldy]
+  int ldy;
+  int m;                 // input rows in this launch (<= template M)
+};
+
+QD_DEV float act_silu(float g) { return g / (1.0f + expf(-g)); }
+QD_DEV float act_gelu_tanh(float x) {
+  const float c = 0.7978845608028654f;  // sqrt(2/pi)
+  return 0.5f * x * (1.0f + tanhf(c * (x + 0.044715f * x * x * x)));
+}
+
+// Gate/up interleave used by the pair modes: weight rows [64b, 64b+32) hold gate
+// rows [32b, 32b+32) and [64b+32, 64b+64) the matching up rows.
+QD_DEV int pair_gate_row(int n) { return (n >> 5) * 64 + (n & 31); }
+
+QD_DEV float dot16_q8(uint4 w, const float4& a, const float4& b, const float4& c, const float4& e) {
+  float s = 0.f;
+  s += (float)(int8_t)(w.x) * a.x;
+  s += (float)(int8_t)(w.x >> 8) * a.y;
+  s += (float)(int8_t)(w.x >> 16) * a.z;
+  s += (float)(int8_t)(w.x >> 24) * a.w;
+  s += (float)(int8_t)(w.y) * b.x;
+  s += (float)(int8_t)(w.y >> 8) * b.y;
+  s += (float)(int8_t)(w.y >> 16) * b.z;
+  s += (float)(int8_t)(w.y >> 24) * b.w;
+  s += (float)(int8_t)(w.z) * c.x;
+  s += (float)(int8_t)(w.z >> 8) * c.y;
+  s += (float)(int8_t)(w.z >> 16) * c.z;
+  s += (float)(int8_t)(w.z >> 24) * c.w;
+  s += (float)(int8_t)(w.w) * e.x;
+  s += (float)(int8_t)(w.w >> 8) * e.y;
+  s += (float)(int8_t)(w.w >> 16) * e.z;
+  s += (float)(int8_t)(w.w >> 24) * e.w;
+  return s;
+}
+
+// One Q4_0 block: returns sum_j n_j * x_j (n = raw nibble, no offset) where the
+// low nibbles of the 16 payload bytes are elements 0..15 and the high nibbles
+// elements 16..31.  High nibbles are converted in place (value 16 n) and scaled
+// by 1/16 at the end (exact).
+QD_DEV float dot32_q4_raw(uint4 w, const float* x) {
+  const float4* xv = reinterpret_cast<const float4*>(x);
+  float lo = 0.f, hi = 0.f;
+  uint32_t words[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t l = opaque_and(words[i], 0x0F0F0F0Fu);
+    uint32_t h = opaque_and(words[i], 0xF0F0F0F0u);
+    float4 xl = xv[i], xh = xv[4 + i];
+    lo += (float)(l & 0xffu) * xl.x;
+    lo += (float)((l >> 8) & 0xffu) * xl.y;
+    lo += (float)((l >> 16) & 0xffu) * xl.z;
+    lo += (float)(l >> 24) * xl.w;
+    hi += (float)(h & 0xffu) * xh.x;
+    hi += (float)((h >> 8) & 0xffu) * xh.y;
+    hi += (float)((h >> 16) & 0xffu) * xh.z;
+    hi += (float)(h >> 24) * xh.w;
+  }
+  return lo + 0.0625f * hi;
+}
+
+// Load the input rows into LDS, optionally RMSNorm-ed with gain norm_w:
+// xs[mi][k] = x[mi][k] * rsqrt(mean_k x^2 + eps) * w[k].  Rows mi >= a.m are zero.
+template <int M>
+QD_DEV void gemv_stage_x(const GemvArgs& a, float* xs, int kp) {
+  __shared__ float red[4][M];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float scale[M];
+#pragma unroll
+  for (int mi = 0; mi < M; ++mi) scale[mi] = 1.f;
+  if (a.norm_w) {
+#pragma unroll
+    for (int mi = 0; mi < M; ++mi) {
+      float ss = 0.f;
+      if (mi < a.m)
+        for (int k = tid; k < kp; k += 256) {
+          float v = a.x[(size_t)mi * a.ldx + k];
+          ss += v * v;
+        }
+      ss = wave_sum(ss);
+      if (lane == 0) red[wave][mi] = ss;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int mi = 0; mi < M; ++mi) {
+      float ss = red[0][mi] + red[1][mi] + red[2][mi] + red[3][mi];
+      scale[mi] = 1.0f / sqrtf(ss / (float)kp + a.eps);
+    }
+  }
+#pragma unroll
+  for (int mi = 0; mi < M; ++mi) {
+    for (int k = tid; k < kp; k += 256) {
+      float v = 0.f;
+      if (mi < a.m) {
+        v = a.x[(size_t)mi * a.ldx + k];
+        if (a.norm_w) v = v * scale[mi] * a.norm_w[k];
+      }
+      xs[mi * kp + k] = v;
+    }
+  }
+}
+
+template <int QT, int M, int MODE>
+__global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
+  extern __shared__ float4 smem4[];
+  float* xs = reinterpret_cast<float*>(smem4);
+  const int kp = a.nblk * 32;
+  float* xsum = xs + M * kp;  // Q4_0 only: [M][nblk] block sums of x
+  gemv_stage_x<M>(a, xs, kp);
+  __syncthreads();
+  if constexpr (QT == kQ4_0) {
+    for (int i = threadIdx.x; i < M * a.nblk; i += 256) {
+      const float* p = xs + (i / a.nblk) * kp + (i % a.nblk) * 32;
+      float s = 0.f;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) s += p[j];
+      xsum[i] = s;
+    }
+    __syncthreads();
+  }
+
+  constexpr bool kPair = MODE == kModePairSilu || MODE == kModePairGelu;
+  const int lane = threadIdx.x & 63;
+  const int gwave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nwaves = gridDim.x * 4;
+  const int ngroups = kPair ? a.rows / 2 : (a.rows + 1) / 2;
+
+  for (int grp = gwave; grp < ngroups; grp += nwaves) {
+    int r0, r1;
+    if constexpr (kPair) {
+      r0 = pair_gate_row(grp);
+      r1 = r0 + 32;
+    } else {
+      r0 = 2 * grp;
+      r1 = min(2 * grp + 1, a.rows - 1);
+    }
+    float acc0[M], acc1[M];
+#pragma unroll
+    for (int mi = 0; mi < M; ++mi) acc0[mi] = acc1[mi] = 0.f;
+
+    if constexpr (QT == kQ8_0) {
+      const int nunits = 2 * a.nblk;
+      const int8_t* q0 = reinterpret_cast<const int8_t*>(a.qs) + (size_t)r0 * kp;
+      const int8_t* q1 = reinterpret_cast<const int8_t*>(a.qs) + (size_t)r1 * kp;
+      const uint16_t* d0p = a.d + (size_t)r0 * a.nblk;
+      const uint16_t* d1p = a.d + (size_t)r1 * a.nblk;
+      for (int u = lane; u < nunits; u += 64) {
+        uint4 w0 = *reinterpret_cast<const uint4*>(q0 + 16 * u);
+        uint4 w1 = *reinterpret_cast<const uint4*>(q1 + 16 * u);
+        float d0 = load_half(d0p + (u >> 1));
+        float d1 = load_half(d1p + (u >> 1));
+#pragma unroll
+        for (int mi = 0; mi < M; ++mi) {
+          const float4* xv = reinterpret_cast<const float4*>(xs + mi * kp + 16 * u);
+          float4 xa = xv[0], xb = xv[1], xc = xv[2], xd = xv[3];
+          acc0[mi] += d0 * dot16_q8(w0, xa, xb, xc, xd);
+          acc1[mi] += d1 * dot16_q8(w1, xa, xb, xc, xd);
+        }
+      }
+    } else if constexpr (QT == kQ4_0) {
+      const uint4* q0 = reinterpret_cast<const uint4*>(a.qs) + (size_t)r0 * a.nblk;
+      const uint4* q1 = reinterpret_cast<const uint4*>(a.qs) + (size_t)r1 * a.nblk;
+      const uint16_t* d0p = a.d + (size_t)r0 * a.nblk;
+      const uint16_t* d1p = a.d + (size_t)r1 * a.nblk;
+      for (int u = lane; u < a.nblk; u += 64) {
+        uint4 w0 = q0[u];
+        uint4 w1 = q1[u];
+        float d0 = load_half(d0p + u);
+        float d1 = load_half(d1p + u);
+#pragma unroll
+        for (int mi = 0; mi < M; ++mi) {
+          const float* xp = xs + mi * kp + 32 * u;
+          float bs = 8.0f * xsum[mi * a.nblk + u];
+          acc0[mi] += d0 * (dot32_q4_raw(w0, xp) - bs);
+          acc1[mi] += d1 * (dot32_q4_raw(w1, xp) - bs);
+        }
+      }
+    } else {  // F32 rows
+      const int nunits = kp / 4;
+      const float4* w0p = reinterpret_cast<const float4*>(a.qs) + (size_t)r0 * (kp / 4);
+      const float4* w1p = reinterpret_cast<const float4*>(a.qs) + (size_t)r1 * (kp / 4);
+      for (int u = lane; u < nunits; u += 64) {
+        float4 w0 = w0p[u], w1 = w1p[u];
+#pragma unroll
+        for (int mi = 0; mi < M; ++mi) {
+          float4 xv = reinterpret_cast<const float4*>(xs + mi * kp)[u];
+          acc0[mi] += w0.x * xv.x + w0.y * xv.y + w0.z * xv.z + w0.w * xv.w;
+          acc1[mi] += w1.x * xv.x + w1.y * xv.y + w1.z * xv.z + w1.w * xv.w;
+        }
+      }
+    }
+
+#pragma unroll
+    for (int mi = 0; mi < M; ++mi) {
+      float s0 = wave_sum(acc0[mi]);
+      float s1 = wave_sum(acc1[mi]);
+      if (lane == 0 && mi < a.m) {
+        float* yr = a.y + (size_t)mi * a.ldy;
+        if constexpr (MODE == kModeStore) {
+          yr[r0] = s0;
+          if (2 * grp + 1 < a.rows) yr[r1] = s1;
+        } else if constexpr (MODE == kModeAdd) {
+          yr[r0] += s0;
+          if (2 * grp + 1 < a.rows) yr[r1] += s1;
+        } else if constexpr (MODE == kModePairSilu) {
+          yr[grp] = act_silu(s0) * s1;
+        } else {
+          yr[grp] = act_gelu_tanh(s0) * s1;
+        }
+      }
+    }
+  }
+}
+
+}  // namespace qd

@@ -1,0 +1,1049 @@
+// libqdec: runtime and C ABI of the MI355X quantized decoder.
+//
+// The model struct owns repacked weights, the f32 KV cache and the workspace;
+// each ABI call validates its arguments on the host, then enqueues the step's
+// kernels on the caller's stream and returns.  Handle / status / poison rules
+// follow tessl `python/README.md` ("Handle ownership, closing and errors", "How
+// the buffers cross"); the forward pass follows the Qwen3 walkthrough Steps 2-9
+// and the qwen3 architecture file on Synsema "Local inference and architectures".
+#include "../../include/qdec.h"
+
+#include <algorithm>
+#include <chrono>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <thread>
+#include <unordered_map>
+#include <vector>
+
+#include "attention.hpp"
+#include "common.hpp"
+#include "gemm.hpp"
+#include "gemv.hpp"
+#include "misc.hpp"
+
+using namespace qd;
+
+namespace {
+
+thread_local std::string g_err;
+
+void set_err(const char* fmt, ...) {
+  char buf[1024];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+}
+
+struct Mat {
+  int type = -1;
+  int rows = 0, cols = 0, nblk = 0;
+  uint8_t* qs = nullptr;   // quants (or f32 values for F32)
+  uint16_t* d = nullptr;   // fp16 scales
+  double gguf_bytes = 0;   // bytes of the tensor in GGUF layout (what a step streams)
+};
+
+struct Layer {
+  float* attn_norm = nullptr;
+  float* q_norm = nullptr;
+  float* k_norm = nullptr;
+  float* post_attn = nullptr;
+  float* ffn_norm = nullptr;
+  float* post_ffw = nullptr;
+  Mat qkv, o, gu, down;
+  bool global = true;
+};
+
+struct NameRef {
+  const Mat* mat = nullptr;
+  int row_off = 0, rows = 0, cols = 0, pair = 0;
+  const float* vec = nullptr;
+};
+
+struct KRec {
+  const char* cls;
+  hipEvent_t a, b;
+  double bytes, flops;
+};
+
+bool is_quant(int t) { return t == kQ8_0 || t == kQ4_0; }
+int64_t blk_bytes(int t) { return t == kQ8_0 ? 34 : 18; }
+int64_t nblocks(int64_t cols) { return (cols + 31) / 32; }
+int64_t tensor_bytes(int t, int64_t rows, int64_t cols) {
+  return t == kF32 ? rows * cols * 4 : rows * nblocks(cols) * blk_bytes(t);
+}
+
+struct HipError {
+  std::string msg;
+};
+
+void hipck(hipError_t e, const char* what) {
+  if (e != hipSuccess) throw HipError{std::string(what) + ": " + hipGetErrorString(e)};
+}
+
+}  // namespace
+
+struct qdec_model {
+  qdec_config cfg{};
+  int max_seqs = 0, max_ctx = 0;
+  int qd = 0, kd = 0, nqkv = 0, Fp = 0;
+  std::vector<Layer> layers;
+  Mat embd, out_w;
+  bool tied = true;
+  float* output_norm = nullptr;
+  float* inv_freq_g = nullptr;
+  float* inv_freq_l = nullptr;
+  float* kc = nullptr;
+  float* vc = nullptr;
+  size_t kv_layer = 0;  // floats per layer of one cache
+  int ws_T = 0;
+  float *x = nullptr, *h = nullptr, *qkv = nullptr, *q = nullptr, *a = nullptr, *m = nullptr, *y = nullptr;
+  float* part_o = nullptr;
+  float* part_ml = nullptr;
+  int chunk = 0, nchunk = 0;
+  float* s_v = nullptr;
+  int* s_i = nullptr;
+  int nvchunk = 0;
+  int* d_pos = nullptr;
+  int* d_tok = nullptr;
+  int* d_prompt = nullptr;
+  int* err_host = nullptr;
+  int* err_dev = nullptr;
+  std::vector<int> kvlen;
+  bool poisoned = false;
+  std::vector<void*> allocs;
+  std::unordered_map<std::string, NameRef> names;
+  bool timing = false;
+  std::vector<KRec> krecs;
+  hipStream_t last_stream = nullptr;
+
+  const Mat& lm() const { return tied ? embd : out_w; }
+
+  template <typename T>
+  T* dalloc(size_t count) {
+    void* p = nullptr;
+    size_t bytes = std::max<size_t>(count * sizeof(T), 256);
+    hipck(hipMalloc(&p, bytes), "hipMalloc");
+    allocs.push_back(p);
+    return reinterpret_cast<T*>(p);
+  }
+};
+
+namespace {
+
+// ------------------------------------------------------------ launch helpers
+struct Timed {
+  qdec_model* m;
+  hipStream_t st;
+  const char* cls;
+  double bytes, flops;
+  hipEvent_t a = nullptr, b = nullptr;
+  Timed(qdec_model* mm, hipStream_t s, const char* c, double by, double fl) : m(mm), st(s), cls(c), bytes(by), flops(fl) {
+    if (m && m->timing) {
+      hipck(hipEventCreate(&a), "hipEventCreate");
+      hipck(hipEventCreate(&b), "hipEventCreate");
+      hipck(hipEventRecord(a, st), "hipEventRecord");
+    }
+  }
+  ~Timed() noexcept(false) {
+    hipck(hipGetLastError(), cls);
+    if (m && m->timing) {
+      hipck(hipEventRecord(b, st), "hipEventRecord");
+      m->krecs.push_back(KRec{cls, a, b, bytes, flops});
+    }
+  }
+};
+
+const char* gemv_class(int type) { return type == kQ4_0 ? "gemv_q4_0" : type == kQ8_0 ? "gemv_q8_0" : "gemv_f32"; }
+const char* gemm_class(int type) { return type == kQ4_0 ? "gemm_q4_0" : type == kQ8_0 ? "gemm_q8_0" : "gemm_f32"; }
+
+template <int QT, int M>
+void gemv_dispatch_mode(int mode, dim3 grid, size_t lds, hipStream_t st, const GemvArgs& a) {
+  switch (mode) {
+    case kModeStore: gemv_kernel<QT, M, kModeStore><<<grid, 256, lds, st>>>(a); break;
+    case kModeAdd: gemv_kernel<QT, M, kModeAdd><<<grid, 256, lds, st>>>(a); break;
+    case kModePairSilu: gemv_kernel<QT, M, kModePairSilu><<<grid, 256, lds, st>>>(a); break;
+    default: gemv_kernel<QT, M, kModePairGelu><<<grid, 256, lds, st>>>(a); break;
+  }
+}
+
+template <int QT>
+void gemv_dispatch_m(int M, int mode, dim3 grid, size_t lds, hipStream_t st, const GemvArgs& a) {
+  switch (M) {
+    case 1: gemv_dispatch_mode<QT, 1>(mode, grid, lds, st, a); break;
+    case 2: gemv_dispatch_mode<QT, 2>(mode, grid, lds, st, a); break;
+    case 4: gemv_dispatch_mode<QT, 4>(mode, grid, lds, st, a); break;
+    case 8: gemv_dispatch_mode<QT, 8>(mode, grid, lds, st, a); break;
+    default: gemv_dispatch_mode<QT, 16>(mode, grid, lds, st, a); break;
+  }
+}
+
+constexpr size_t kGemvLdsMax = 64 * 1024;
+
+// y[r][*] (op)= W x[r] for rows r < nrows, in launches of up to 16 rows that fit
+// the LDS budget.
+void gemv(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, const float* norm_w, float eps,
+          float* y, int ldy, int nrows, int mode) {
+  const int kp = w.nblk * 32;
+  const size_t per_row = (size_t)kp * 4 + (w.type == kQ4_0 ? (size_t)w.nblk * 4 : 0);
+  // rows per launch: a power of two (the kernel's M) whose staged inputs fit the LDS budget
+  int cap = 16;
+  while (cap > 1 && per_row * cap > kGemvLdsMax) cap /= 2;
+  if (per_row > kGemvLdsMax) throw HipError{"gemv: input row too long for LDS"};
+  const bool pair = mode == kModePairSilu || mode == kModePairGelu;
+  const int ngroups = pair ? w.rows / 2 : (w.rows + 1) / 2;
+  dim3 grid(std::min((ngroups + 3) / 4, 2048));
+  for (int r0 = 0; r0 < nrows; r0 += cap) {
+    const int mr = std::min(cap, nrows - r0);
+    int M = 1;
+    while (M < mr) M *= 2;
+    GemvArgs a{w.qs, w.d, w.rows, w.nblk, x + (size_t)r0 * ldx, ldx, norm_w, eps, y + (size_t)r0 * ldy, ldy, mr};
+    const size_t lds = per_row * M;
+    const double bytes = w.gguf_bytes + (double)mr * kp * 4 + (double)mr * (pair ? w.rows / 2 : w.rows) * 4;
+    Timed tm(m, st, gemv_class(w.type), bytes, 2.0 * mr * w.rows * (double)w.cols);
+    if (w.type == kQ8_0) gemv_dispatch_m<kQ8_0>(M, mode, grid, lds, st, a);
+    else if (w.type == kQ4_0) gemv_dispatch_m<kQ4_0>(M, mode, grid, lds, st, a);
+    else gemv_dispatch_m<kF32>(M, mode, grid, lds, st, a);
+  }
+}
+
+template <int QT>
+void gemm_dispatch(int mode, dim3 grid, hipStream_t st, const GemmArgs& a) {
+  switch (mode) {
+    case kModeStore: gemm_kernel<QT, kModeStore><<<grid, 256, 0, st>>>(a); break;
+    case kModeAdd: gemm_kernel<QT, kModeAdd><<<grid, 256, 0, st>>>(a); break;
+    case kModePairSilu: gemm_kernel<QT, kModePairSilu><<<grid, 256, 0, st>>>(a); break;
+    default: gemm_kernel<QT, kModePairGelu><<<grid, 256, 0, st>>>(a); break;
+  }
+}
+
+void gemm(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, int T, float* y, int ldy, int mode) {
+  GemmArgs a{w.qs, w.d, w.rows, w.nblk, x, ldx, T, y, ldy};
+  dim3 grid((w.rows + 127) / 128, (T + 63) / 64);
+  const bool pair = mode == kModePairSilu || mode == kModePairGelu;
+  const double bytes = w.gguf_bytes + (double)T * w.nblk * 32 * 4 + (double)T * (pair ? w.rows / 2 : w.rows) * 4;
+  Timed tm(m, st, gemm_class(w.type), bytes, 2.0 * T * (double)w.rows * w.cols);
+  if (w.type == kQ8_0) gemm_dispatch<kQ8_0>(mode, grid, st, a);
+  else if (w.type == kQ4_0) gemm_dispatch<kQ4_0>(mode, grid, st, a);
+  else gemm_dispatch<kF32>(mode, grid, st, a);
+}
+
+void rmsnorm_rows(qdec_model* m, hipStream_t st, const float* x, int ldx, const float* w, int n, float* out, int ldo,
+                  int rows, int add) {
+  NormArgs a{x, ldx, w, m ? m->cfg.rms_eps : 0.f, n, out, ldo, add};
+  Timed tm(m, st, "rmsnorm", (double)rows * n * (add ? 12 : 8), 0);
+  rmsnorm_kernel<<<rows, 256, 0, st>>>(a);
+}
+
+template <int HD>
+void attn_decode_hd(int G, dim3 grid, hipStream_t st, const AttnDecodeArgs& a) {
+  switch (G) {
+    case 1: attn_decode_kernel<HD, 1><<<grid, 256, 0, st>>>(a); break;
+    case 2: attn_decode_kernel<HD, 2><<<grid, 256, 0, st>>>(a); break;
+    case 4: attn_decode_kernel<HD, 4><<<grid, 256, 0, st>>>(a); break;
+    default:
+      if constexpr (HD == 128) attn_decode_kernel<HD, 8><<<grid, 256, 0, st>>>(a);
+      break;
+  }
+}
+
+size_t l_off(const qdec_model* m, int layer, int seq, int g) {
+  return (size_t)layer * m->kv_layer + ((size_t)seq * m->cfg.n_head_kv + g) * m->max_ctx * m->cfg.head_dim;
+}
+
+int layer_window(const qdec_model* m, int l) { return m->layers[l].global ? 0 : m->cfg.window; }
+
+void attention_decode(qdec_model* m, hipStream_t st, int l, int B) {
+  const qdec_config& c = m->cfg;
+  const int hd = c.head_dim, G = c.n_head / c.n_head_kv;
+  const float scale_log2 = (float)(1.0 / std::sqrt((double)hd) * 1.4426950408889634);
+  AttnDecodeArgs a{m->q, m->kc + l * m->kv_layer, m->vc + l * m->kv_layer, m->max_ctx, m->d_pos, c.n_head,
+                   c.n_head_kv, layer_window(m, l), m->chunk, scale_log2, m->part_o, m->part_ml, m->nchunk};
+  double kvbytes = 0;
+  for (int s = 0; s < B; ++s) {
+    int p = m->kvlen[s];
+    int lo = a.window > 0 ? std::max(0, p - a.window + 1) : 0;
+    kvbytes += (double)(p - lo + 1) * c.n_head_kv * hd * 8;
+  }
+  {
+    Timed tm(m, st, "attn_decode", kvbytes + (double)B * c.n_head * hd * 4, 4.0 * kvbytes / 8 * G);
+    dim3 grid(m->nchunk, c.n_head_kv, B);
+    if (hd == 64) attn_decode_hd<64>(G, grid, st, a);
+    else if (hd == 128) attn_decode_hd<128>(G, grid, st, a);
+    else attn_decode_hd<256>(G, grid, st, a);
+  }
+  AttnCombineArgs cb{m->part_o, m->part_ml, m->d_pos, c.n_head, hd, a.window, m->chunk, m->nchunk, m->a};
+  Timed tm(m, st, "attn_combine", (double)B * c.n_head * hd * 4 * 2, 0);
+  attn_combine_kernel<<<dim3(c.n_head, B), hd, 0, st>>>(cb);
+}
+
+void attention_prefill(qdec_model* m, hipStream_t st, int l, int seq, int T, int pos0) {
+  const qdec_config& c = m->cfg;
+  const int hd = c.head_dim;
+  const size_t seq_off = (size_t)seq * c.n_head_kv * m->max_ctx * hd;
+  AttnPrefillArgs a{m->q, m->kc + l * m->kv_layer + seq_off, m->vc + l * m->kv_layer + seq_off, m->max_ctx, T, pos0,
+                    c.n_head, c.n_head_kv, layer_window(m, l),
+                    (float)(1.0 / std::sqrt((double)hd) * 1.4426950408889634), m->a};
+  double pairs = 0;
+  for (int t = 0; t < T; ++t) {
+    int p = pos0 + t, lo = a.window > 0 ? std::max(0, p - a.window + 1) : 0;
+    pairs += p - lo + 1;
+  }
+  Timed tm(m, st, "attn_prefill", (double)T * c.n_head * hd * 8 + (double)(pos0 + T) * c.n_head_kv * hd * 8,
+           4.0 * hd * c.n_head * pairs);
+  const int QT = 256 / (hd / 8);
+  dim3 grid((T + QT - 1) / QT, c.n_head);
+  if (hd == 64) attn_prefill_kernel<64, 64><<<grid, 256, 0, st>>>(a);
+  else if (hd == 128) attn_prefill_kernel<128, 32><<<grid, 256, 0, st>>>(a);
+  else attn_prefill_kernel<256, 16><<<grid, 256, 0, st>>>(a);
+}
+
+void rope_kv(qdec_model* m, hipStream_t st, int l, int n, int seq0, int pos0, const int* dpos) {
+  const qdec_config& c = m->cfg;
+  const Layer& L = m->layers[l];
+  RopeArgs a{m->qkv, m->nqkv, m->q, m->kc + l * m->kv_layer, m->vc + l * m->kv_layer, m->max_ctx, c.n_head,
+             c.n_head_kv, c.head_dim, L.q_norm, L.k_norm, c.rms_eps, L.global ? m->inv_freq_g : m->inv_freq_l,
+             seq0, pos0, dpos};
+  Timed tm(m, st, "rope_kv", (double)n * m->nqkv * 8, 0);
+  rope_kv_kernel<<<n, 256, 0, st>>>(a);
+}
+
+void embed(qdec_model* m, hipStream_t st, const int* d_tokens, int n, float* out) {
+  const qdec_config& c = m->cfg;
+  EmbedArgs a{WView{m->embd.qs, m->embd.d, m->embd.type, m->embd.nblk}, c.hidden, c.vocab, n, d_tokens, out,
+              c.hidden, m->err_dev};
+  Timed tm(m, st, "embed", (double)n * (m->embd.gguf_bytes / m->embd.rows + c.hidden * 4), 0);
+  embed_kernel<<<n, 256, 0, st>>>(a);
+}
+
+void sample(qdec_model* m, hipStream_t st, const float* logits, int ld, int rows, float temp, uint64_t seed,
+            uint64_t step, int* out, int* out2) {
+  const int V = m->cfg.vocab;
+  SampleArgs a{logits, ld, V, rows, temp, seed, step, m->s_v, m->s_i, m->nvchunk, out, out2};
+  {
+    Timed tm(m, st, "sample", (double)rows * V * 4, 0);
+    sample_stage1_kernel<<<dim3(m->nvchunk, rows), 256, 0, st>>>(a);
+  }
+  Timed tm(m, st, "sample_final", (double)rows * m->nvchunk * 8, 0);
+  sample_stage2_kernel<<<rows, 64, 0, st>>>(a);
+}
+
+// The blocks over n tokens of one sequence (prefill) or one token of each of n
+// sequences (decode, dpos != null); the residual stream is m->x.
+void blocks(qdec_model* m, hipStream_t st, int n, int seq, int pos0, const int* dpos) {
+  const qdec_config& c = m->cfg;
+  const int H = c.hidden;
+  const bool dec = dpos != nullptr;
+  const int act_mode = c.act == QDEC_ACT_GELU_TANH ? kModePairGelu : kModePairSilu;
+  for (int l = 0; l < c.n_layer; ++l) {
+    const Layer& L = m->layers[l];
+    // attention sublayer
+    if (dec) {
+      gemv(m, st, L.qkv, m->x, H, L.attn_norm, c.rms_eps, m->qkv, m->nqkv, n, kModeStore);
+    } else {
+      rmsnorm_rows(m, st, m->x, H, L.attn_norm, H, m->h, H, n, 0);
+      gemm(m, st, L.qkv, m->h, H, n, m->qkv, m->nqkv, kModeStore);
+    }
+    rope_kv(m, st, l, n, seq, pos0, dpos);
+    if (dec) attention_decode(m, st, l, n);
+    else attention_prefill(m, st, l, seq, n, pos0);
+    if (c.sandwich_norm) {
+      if (dec) gemv(m, st, L.o, m->a, m->qd, nullptr, 0.f, m->y, H, n, kModeStore);
+      else gemm(m, st, L.o, m->a, m->qd, n, m->y, H, kModeStore);
+      rmsnorm_rows(m, st, m->y, H, L.post_attn, H, m->x, H, n, 1);
+    } else {
+      if (dec) gemv(m, st, L.o, m->a, m->qd, nullptr, 0.f, m->x, H, n, kModeAdd);
+      else gemm(m, st, L.o, m->a, m->qd, n, m->x, H, kModeAdd);
+    }
+    // feed-forward sublayer
+    if (dec) {
+      gemv(m, st, L.gu, m->x, H, L.ffn_norm, c.rms_eps, m->m, m->Fp, n, act_mode);
+    } else {
+      rmsnorm_rows(m, st, m->x, H, L.ffn_norm, H, m->h, H, n, 0);
+      gemm(m, st, L.gu, m->h, H, n, m->m, m->Fp, act_mode);
+    }
+    if (c.sandwich_norm) {
+      if (dec) gemv(m, st, L.down, m->m, m->Fp, nullptr, 0.f, m->y, H, n, kModeStore);
+      else gemm(m, st, L.down, m->m, m->Fp, n, m->y, H, kModeStore);
+      rmsnorm_rows(m, st, m->y, H, L.post_ffw, H, m->x, H, n, 1);
+    } else {
+      if (dec) gemv(m, st, L.down, m->m, m->Fp, nullptr, 0.f, m->x, H, n, kModeAdd);
+      else gemm(m, st, L.down, m->m, m->Fp, n, m->x, H, kModeAdd);
+    }
+  }
+}
+
+// ------------------------------------------------------------ error handling
+void drain(hipStream_t st) {
+  hipEvent_t ev;
+  if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) return;
+  if (hipEventRecord(ev, st) == hipSuccess) {
+    auto t0 = std::chrono::steady_clock::now();
+    while (hipEventQuery(ev) == hipErrorNotReady) {
+      if (std::chrono::steady_clock::now() - t0 > std::chrono::seconds(30)) {
+        g_err += " (stream still busy after the 30 s wait)";
+        break;
+      }
+      std::this_thread::sleep_for(std::chrono::microseconds(200));
+    }
+  }
+  (void)hipEventDestroy(ev);
+}
+
+int fail_internal(qdec_model* m, hipStream_t st, const std::string& msg) {
+  set_err("internal: %s", msg.c_str());
+  (void)hipGetLastError();
+  drain(st);
+  if (m) m->poisoned = true;
+  return QDEC_INTERNAL;
+}
+
+int check_usable(qdec_model* m) {
+  if (!m) {
+    set_err("model handle is NULL");
+    return QDEC_REFUSED;
+  }
+  if (m->poisoned) {
+    set_err("poisoned: an earlier GPU failure latched this handle; free it and load again");
+    return QDEC_REFUSED;
+  }
+  if (m->err_host && __atomic_load_n(m->err_host, __ATOMIC_ACQUIRE)) {
+    m->poisoned = true;
+    set_err("internal: a device-resident token id was outside [0, vocab) (clamped); handle poisoned");
+    return QDEC_INTERNAL;
+  }
+  return QDEC_OK;
+}
+
+// ------------------------------------------------------------ loading
+struct Expect {
+  std::string name;
+  int64_t rows, cols;
+  bool matrix;  // quantized allowed
+  bool required;
+};
+
+std::vector<Expect> expected_tensors(const qdec_config& c) {
+  std::vector<Expect> e;
+  const int64_t H = c.hidden, hd = c.head_dim, qd = (int64_t)c.n_head * hd, kd = (int64_t)c.n_head_kv * hd;
+  e.push_back({"token_embd.weight", c.vocab, H, true, true});
+  for (int i = 0; i < c.n_layer; ++i) {
+    std::string p = "blk." + std::to_string(i) + ".";
+    e.push_back({p + "attn_norm.weight", 1, H, false, true});
+    e.push_back({p + "attn_q.weight", qd, H, true, true});
+    e.push_back({p + "attn_k.weight", kd, H, true, true});
+    e.push_back({p + "attn_v.weight", kd, H, true, true});
+    if (c.qk_norm) {
+      e.push_back({p + "attn_q_norm.weight", 1, hd, false, true});
+      e.push_back({p + "attn_k_norm.weight", 1, hd, false, true});
+    }
+    e.push_back({p + "attn_output.weight", H, qd, true, true});
+    if (c.sandwich_norm) e.push_back({p + "post_attention_norm.weight", 1, H, false, true});
+    e.push_back({p + "ffn_norm.weight", 1, H, false, true});
+    e.push_back({p + "ffn_gate.weight", c.ffn, H, true, true});
+    e.push_back({p + "ffn_up.weight", c.ffn, H, true, true});
+    e.push_back({p + "ffn_down.weight", H, c.ffn, true, true});
+    if (c.sandwich_norm) e.push_back({p + "post_ffw_norm.weight", 1, H, false, true});
+  }
+  e.push_back({"output_norm.weight", 1, H, false, true});
+  e.push_back({"output.weight", c.vocab, H, true, false});
+  return e;
+}
+
+bool scales_finite(const qdec_tensor& t) {
+  if (!is_quant(t.type)) return true;
+  const uint8_t* b = static_cast<const uint8_t*>(t.host_data);
+  const int64_t nb = t.rows * nblocks(t.cols), bb = blk_bytes(t.type);
+  for (int64_t i = 0; i < nb; ++i) {
+    uint16_t h = (uint16_t)b[i * bb] | ((uint16_t)b[i * bb + 1] << 8);
+    if (((h >> 10) & 0x1f) == 0x1f) return false;
+  }
+  return true;
+}
+
+// Repack GGUF rows [src_rows][blocks] into (quants, scales) at device row dst_row
+// of a host staging buffer of the fused matrix.
+struct Stage {
+  int type;
+  int64_t rows, nblk;
+  std::vector<uint8_t> qs;
+  std::vector<uint16_t> d;
+  Stage(int t, int64_t r, int64_t nb) : type(t), rows(r), nblk(nb) {
+    qs.assign((size_t)(t == kQ4_0 ? r * nb * 16 : t == kQ8_0 ? r * nb * 32 : r * nb * 32 * 4), 0);
+    if (is_quant(t)) d.assign((size_t)(r * nb), 0);
+  }
+  void put_row(int64_t dst_row, const qdec_tensor& t, int64_t src_row) {
+    const uint8_t* src = static_cast<const uint8_t*>(t.host_data);
+    const int64_t nb = nblocks(t.cols);
+    if (type == kF32) {
+      std::memcpy(&qs[(size_t)dst_row * nblk * 32 * 4], src + src_row * t.cols * 4, (size_t)t.cols * 4);
+      return;
+    }
+    const int64_t bb = blk_bytes(type), payload = bb - 2;
+    for (int64_t b = 0; b < nb; ++b) {
+      const uint8_t* blk = src + (src_row * nb + b) * bb;
+      d[(size_t)(dst_row * nblk + b)] = (uint16_t)blk[0] | ((uint16_t)blk[1] << 8);
+      std::memcpy(&qs[(size_t)((dst_row * nblk + b) * payload)], blk + 2, (size_t)payload);
+    }
+  }
+};
+
+Mat upload(qdec_model* m, const Stage& s, int rows, int cols, double gguf_bytes, hipStream_t st) {
+  Mat w;
+  w.type = s.type;
+  w.rows = rows;
+  w.cols = cols;
+  w.nblk = (int)s.nblk;
+  w.gguf_bytes = gguf_bytes;
+  w.qs = m->dalloc<uint8_t>(s.qs.size());
+  hipck(hipMemcpyAsync(w.qs, s.qs.data(), s.qs.size(), hipMemcpyHostToDevice, st), "upload");
+  if (is_quant(s.type)) {
+    w.d = m->dalloc<uint16_t>(s.d.size());
+    hipck(hipMemcpyAsync(w.d, s.d.data(), s.d.size() * 2, hipMemcpyHostToDevice, st), "upload");
+  }
+  hipck(hipStreamSynchronize(st), "upload sync");
+  return w;
+}
+
+float* upload_vec(qdec_model* m, const qdec_tensor& t, hipStream_t st) {
+  float* p = m->dalloc<float>((size_t)t.cols);
+  hipck(hipMemcpyAsync(p, t.host_data, (size_t)t.cols * 4, hipMemcpyHostToDevice, st), "upload");
+  return p;
+}
+
+void free_model(qdec_model* m) {
+  for (void* p : m->allocs) (void)hipFree(p);
+  m->allocs.clear();
+  for (auto& r : m->krecs) {
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  if (m->err_host) (void)hipHostFree(m->err_host);
+  delete m;
+}
+
+int load(const qdec_config* cfgp, const qdec_tensor* ts, int32_t n, int32_t max_seqs, int32_t max_ctx,
+         hipStream_t st, qdec_model** out) {
+  if (!cfgp || !out) {
+    set_err("cfg and out must not be NULL");
+    return QDEC_REFUSED;
+  }
+  *out = nullptr;
+  const qdec_config c = *cfgp;
+  if (c.n_layer <= 0 || c.hidden <= 0 || c.n_head <= 0 || c.n_head_kv <= 0 || c.head_dim <= 0 || c.ffn <= 0 ||
+      c.vocab <= 0) {
+    set_err("config: every dimension must be positive");
+    return QDEC_REFUSED;
+  }
+  if (c.hidden % 32) { set_err("config: hidden (%d) must be a multiple of 32", c.hidden); return QDEC_REFUSED; }
+  if (c.head_dim != 64 && c.head_dim != 128 && c.head_dim != 256) {
+    set_err("config: head_dim %d unsupported (64, 128 or 256)", c.head_dim);
+    return QDEC_REFUSED;
+  }
+  if (c.n_head % c.n_head_kv) { set_err("config: n_head must be a multiple of n_head_kv"); return QDEC_REFUSED; }
+  const int G = c.n_head / c.n_head_kv;
+  if (!(G == 1 || G == 2 || G == 4 || (G == 8 && c.head_dim == 128))) {
+    set_err("config: query heads per KV head = %d unsupported (1, 2, 4; 8 with head_dim 128)", G);
+    return QDEC_REFUSED;
+  }
+  if (c.act != QDEC_ACT_SILU && c.act != QDEC_ACT_GELU_TANH) { set_err("config: act must be 0 or 1"); return QDEC_REFUSED; }
+  if (c.window < 0 || (c.window > 0 && c.window_period <= 0)) {
+    set_err("config: window >= 0, and window_period >= 1 when window > 0");
+    return QDEC_REFUSED;
+  }
+  if (!(c.rms_eps >= 0.f) || !std::isfinite(c.rms_eps) || !(c.rope_theta > 0.f) ||
+      (c.window > 0 && !(c.rope_theta_local > 0.f))) {
+    set_err("config: rms_eps must be finite and >= 0, rope thetas > 0");
+    return QDEC_REFUSED;
+  }
+  if (max_seqs < 1 || max_seqs > 64) { set_err("max_seqs must be in [1, 64], got %d", max_seqs); return QDEC_REFUSED; }
+  if (max_ctx < 1) { set_err("max_ctx must be >= 1"); return QDEC_REFUSED; }
+  if (n < 0 || (n > 0 && !ts)) { set_err("tensors: NULL array or negative count"); return QDEC_REFUSED; }
+
+  // validate every tensor before allocating anything
+  std::vector<Expect> exp = expected_tensors(c);
+  std::unordered_map<std::string, const Expect*> byname;
+  for (auto& e : exp) byname[e.name] = &e;
+  std::unordered_map<std::string, const qdec_tensor*> got;
+  for (int i = 0; i < n; ++i) {
+    const qdec_tensor& t = ts[i];
+    if (!t.name) { set_err("tensor %d: NULL name", i); return QDEC_REFUSED; }
+    auto it = byname.find(t.name);
+    if (it == byname.end()) { set_err("tensor '%s': not a tensor of this configuration", t.name); return QDEC_REFUSED; }
+    if (got.count(t.name)) { set_err("tensor '%s': given twice", t.name); return QDEC_REFUSED; }
+    const Expect& e = *it->second;
+    if (t.type != kF32 && t.type != kQ8_0 && t.type != kQ4_0) {
+      set_err("tensor '%s': type %d unsupported (F32 = 0, Q4_0 = 2, Q8_0 = 8)", t.name, t.type);
+      return QDEC_REFUSED;
+    }
+    if (!e.matrix && t.type != kF32) { set_err("tensor '%s': norm gains must be F32", t.name); return QDEC_REFUSED; }
+    if (t.rows != e.rows || t.cols != e.cols) {
+      set_err("tensor '%s': dims [%lld][%lld], expected [%lld][%lld]", t.name, (long long)t.rows, (long long)t.cols,
+              (long long)e.rows, (long long)e.cols);
+      return QDEC_REFUSED;
+    }
+    if (t.n_bytes != tensor_bytes(t.type, t.rows, t.cols)) {
+      set_err("tensor '%s': %lld bytes, expected %lld", t.name, (long long)t.n_bytes,
+              (long long)tensor_bytes(t.type, t.rows, t.cols));
+      return QDEC_REFUSED;
+    }
+    if (!t.host_data) { set_err("tensor '%s': NULL data", t.name); return QDEC_REFUSED; }
+    if (!scales_finite(t)) { set_err("tensor '%s': a block scale is not finite", t.name); return QDEC_REFUSED; }
+    got[t.name] = &t;
+  }
+  for (auto& e : exp)
+    if (e.required && !got.count(e.name)) { set_err("tensor '%s' is missing", e.name.c_str()); return QDEC_REFUSED; }
+  for (int i = 0; i < c.n_layer; ++i) {
+    std::string p = "blk." + std::to_string(i) + ".";
+    int tq = got[p + "attn_q.weight"]->type;
+    if (got[p + "attn_k.weight"]->type != tq || got[p + "attn_v.weight"]->type != tq) {
+      set_err("layer %d: attn_q, attn_k and attn_v must share one type", i);
+      return QDEC_REFUSED;
+    }
+    if (got[p + "ffn_gate.weight"]->type != got[p + "ffn_up.weight"]->type) {
+      set_err("layer %d: ffn_gate and ffn_up must share one type", i);
+      return QDEC_REFUSED;
+    }
+  }
+
+  qdec_model* m = new qdec_model();
+  try {
+    m->cfg = c;
+    m->max_seqs = max_seqs;
+    m->max_ctx = max_ctx;
+    m->qd = c.n_head * c.head_dim;
+    m->kd = c.n_head_kv * c.head_dim;
+    m->nqkv = m->qd + 2 * m->kd;
+    m->Fp = (int)(nblocks(c.ffn) * 32);
+    const int H = c.hidden;
+    auto TN = [&](const std::string& s) -> const qdec_tensor& { return *got.at(s); };
+
+    {  // embedding / LM head
+      const qdec_tensor& e = TN("token_embd.weight");
+      Stage s(e.type, e.rows, nblocks(e.cols));
+      for (int64_t r = 0; r < e.rows; ++r) s.put_row(r, e, r);
+      m->embd = upload(m, s, (int)e.rows, (int)e.cols, (double)e.n_bytes, st);
+      m->names[e.name] = NameRef{&m->embd, 0, (int)e.rows, (int)e.cols, 0, nullptr};
+      m->tied = !got.count("output.weight");
+      if (!m->tied) {
+        const qdec_tensor& o = TN("output.weight");
+        Stage so(o.type, o.rows, nblocks(o.cols));
+        for (int64_t r = 0; r < o.rows; ++r) so.put_row(r, o, r);
+        m->out_w = upload(m, so, (int)o.rows, (int)o.cols, (double)o.n_bytes, st);
+        m->names[o.name] = NameRef{&m->out_w, 0, (int)o.rows, (int)o.cols, 0, nullptr};
+      }
+      m->output_norm = upload_vec(m, TN("output_norm.weight"), st);
+    }
+    m->layers.resize(c.n_layer);
+    for (int i = 0; i < c.n_layer; ++i) {
+      Layer& L = m->layers[i];
+      std::string p = "blk." + std::to_string(i) + ".";
+      L.global = c.window <= 0 || (i % c.window_period == c.window_period - 1);
+      L.attn_norm = upload_vec(m, TN(p + "attn_norm.weight"), st);
+      L.ffn_norm = upload_vec(m, TN(p + "ffn_norm.weight"), st);
+      if (c.qk_norm) {
+        L.q_norm = upload_vec(m, TN(p + "attn_q_norm.weight"), st);
+        L.k_norm = upload_vec(m, TN(p + "attn_k_norm.weight"), st);
+      }
+      if (c.sandwich_norm) {
+        L.post_attn = upload_vec(m, TN(p + "post_attention_norm.weight"), st);
+        L.post_ffw = upload_vec(m, TN(p + "post_ffw_norm.weight"), st);
+      }
+      {  // fused q|k|v rows
+        const qdec_tensor &tq = TN(p + "attn_q.weight"), &tk = TN(p + "attn_k.weight"), &tv = TN(p + "attn_v.weight");
+        Stage s(tq.type, m->nqkv, nblocks(H));
+        for (int64_t r = 0; r < tq.rows; ++r) s.put_row(r, tq, r);
+        for (int64_t r = 0; r < tk.rows; ++r) s.put_row(m->qd + r, tk, r);
+        for (int64_t r = 0; r < tv.rows; ++r) s.put_row(m->qd + m->kd + r, tv, r);
+        L.qkv = upload(m, s, m->nqkv, H, (double)(tq.n_bytes + tk.n_bytes + tv.n_bytes), st);
+        m->names[tq.name] = NameRef{&L.qkv, 0, m->qd, H, 0, nullptr};
+        m->names[tk.name] = NameRef{&L.qkv, m->qd, m->kd, H, 0, nullptr};
+        m->names[tv.name] = NameRef{&L.qkv, m->qd + m->kd, m->kd, H, 0, nullptr};
+      }
+      {
+        const qdec_tensor& to = TN(p + "attn_output.weight");
+        Stage s(to.type, to.rows, nblocks(to.cols));
+        for (int64_t r = 0; r < to.rows; ++r) s.put_row(r, to, r);
+        L.o = upload(m, s, (int)to.rows, (int)to.cols, (double)to.n_bytes, st);
+        m->names[to.name] = NameRef{&L.o, 0, (int)to.rows, (int)to.cols, 0, nullptr};
+      }
+      {  // gate/up interleaved in 32-row groups, zero rows up to Fp
+        const qdec_tensor &tg = TN(p + "ffn_gate.weight"), &tu = TN(p + "ffn_up.weight");
+        Stage s(tg.type, 2 * (int64_t)m->Fp, nblocks(H));
+        for (int64_t r = 0; r < tg.rows; ++r) {
+          int64_t gr = (r / 32) * 64 + (r % 32);
+          s.put_row(gr, tg, r);
+          s.put_row(gr + 32, tu, r);
+        }
+        L.gu = upload(m, s, 2 * m->Fp, H, (double)(tg.n_bytes + tu.n_bytes), st);
+        m->names[tg.name] = NameRef{&L.gu, 0, c.ffn, H, 1, nullptr};
+        m->names[tu.name] = NameRef{&L.gu, 0, c.ffn, H, 2, nullptr};
+      }
+      {
+        const qdec_tensor& td = TN(p + "ffn_down.weight");
+        Stage s(td.type, td.rows, nblocks(td.cols));
+        for (int64_t r = 0; r < td.rows; ++r) s.put_row(r, td, r);
+        L.down = upload(m, s, (int)td.rows, (int)td.cols, (double)td.n_bytes, st);
+        m->names[td.name] = NameRef{&L.down, 0, (int)td.rows, (int)td.cols, 0, nullptr};
+      }
+    }
+    {  // RoPE inverse frequencies: 1 / theta^(i / half) in double, rounded once to f32
+      const int half = c.head_dim / 2;
+      std::vector<float> fg(half), fl(half);
+      for (int i = 0; i < half; ++i) {
+        fg[i] = (float)(1.0 / std::pow((double)c.rope_theta, (double)i / half));
+        fl[i] = (float)(1.0 / std::pow((double)(c.window > 0 ? c.rope_theta_local : c.rope_theta), (double)i / half));
+      }
+      m->inv_freq_g = m->dalloc<float>(half);
+      m->inv_freq_l = m->dalloc<float>(half);
+      hipck(hipMemcpy(m->inv_freq_g, fg.data(), half * 4, hipMemcpyHostToDevice), "upload");
+      hipck(hipMemcpy(m->inv_freq_l, fl.data(), half * 4, hipMemcpyHostToDevice), "upload");
+    }
+    // KV cache [L][B][nkv][ctx][hd] f32
+    m->kv_layer = (size_t)max_seqs * c.n_head_kv * max_ctx * c.head_dim;
+    m->kc = m->dalloc<float>(m->kv_layer * c.n_layer);
+    m->vc = m->dalloc<float>(m->kv_layer * c.n_layer);
+    // workspace
+    m->ws_T = std::max(std::min(max_ctx, 4096), max_seqs);
+    const size_t T = m->ws_T;
+    m->x = m->dalloc<float>(T * H);
+    m->h = m->dalloc<float>(T * H);
+    m->y = m->dalloc<float>(T * H);
+    m->qkv = m->dalloc<float>(T * m->nqkv);
+    m->q = m->dalloc<float>(T * m->qd);
+    m->a = m->dalloc<float>(T * m->qd);
+    m->m = m->dalloc<float>(T * m->Fp);
+    hipck(hipMemsetAsync(m->m, 0, T * m->Fp * 4, st), "memset");
+    {  // decode split over positions: enough chunks to fill the GPU at max length
+      const double want = (double)max_ctx * c.n_head_kv * max_seqs / 2048.0;
+      int ch = 32;
+      while (ch < want && ch < 1024) ch *= 2;
+      m->chunk = ch;
+      m->nchunk = (max_ctx + ch - 1) / ch;
+    }
+    m->part_o = m->dalloc<float>((size_t)max_seqs * c.n_head * m->nchunk * c.head_dim);
+    m->part_ml = m->dalloc<float>((size_t)max_seqs * c.n_head * m->nchunk * 2);
+    m->nvchunk = (c.vocab + kSampleChunk - 1) / kSampleChunk;
+    m->s_v = m->dalloc<float>((size_t)max_seqs * m->nvchunk);
+    m->s_i = m->dalloc<int>((size_t)max_seqs * m->nvchunk);
+    m->d_pos = m->dalloc<int>(64);
+    m->d_tok = m->dalloc<int>(64);
+    m->d_prompt = m->dalloc<int>(T);
+    hipck(hipHostMalloc((void**)&m->err_host, sizeof(int), hipHostMallocMapped), "hipHostMalloc");
+    *m->err_host = 0;
+    hipck(hipHostGetDevicePointer((void**)&m->err_dev, m->err_host, 0), "hipHostGetDevicePointer");
+    m->kvlen.assign(max_seqs, 0);
+    hipck(hipStreamSynchronize(st), "load sync");
+  } catch (const HipError& e) {
+    set_err("internal: %s", e.msg.c_str());
+    drain(st);
+    free_model(m);
+    return QDEC_INTERNAL;
+  } catch (const std::bad_alloc&) {
+    set_err("host out of memory while loading");
+    free_model(m);
+    return QDEC_INTERNAL;
+  }
+  *out = m;
+  return QDEC_OK;
+}
+
+}  // namespace
+
+// ================================================================= C ABI
+extern "C" {
+
+int32_t qdec_abi_version(void) { return QDEC_ABI_VERSION; }
+
+const char* qdec_last_error(void) { return g_err.c_str(); }
+
+int qdec_load_weights(const qdec_config* cfg, const qdec_tensor* tensors, int32_t n_tensors, int32_t max_seqs,
+                      int32_t max_ctx, void* stream, qdec_model** out) {
+  g_err.clear();
+  try {
+    return load(cfg, tensors, n_tensors, max_seqs, max_ctx, (hipStream_t)stream, out);
+  } catch (...) {
+    set_err("internal: unexpected exception while loading");
+    return QDEC_INTERNAL;
+  }
+}
+
+int qdec_prefill(qdec_model* m, int32_t seq, const int32_t* tokens, int32_t n_tokens, float* d_logits,
+                 int32_t* d_token_out, uint32_t flags, void* stream) {
+  g_err.clear();
+  if (int rc = check_usable(m)) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  const qdec_config& c = m->cfg;
+  if (seq < 0 || seq >= m->max_seqs) { set_err("seq %d outside [0, %d)", seq, m->max_seqs); return QDEC_REFUSED; }
+  if (n_tokens <= 0) { set_err("n_tokens must be > 0"); return QDEC_REFUSED; }
+  if (!tokens || !d_logits) { set_err("tokens and d_logits must not be NULL"); return QDEC_REFUSED; }
+  if (flags & ~(uint32_t)QDEC_ALL_LOGITS) { set_err("prefill: unknown flag bits 0x%x", flags); return QDEC_REFUSED; }
+  if ((int64_t)m->kvlen[seq] + n_tokens > m->max_ctx) {
+    set_err("seq %d: kv_len %d + %d tokens exceeds max_ctx %d", seq, m->kvlen[seq], n_tokens, m->max_ctx);
+    return QDEC_REFUSED;
+  }
+  for (int i = 0; i < n_tokens; ++i)
+    if (tokens[i] < 0 || tokens[i] >= c.vocab) {
+      set_err("tokens[%d] = %d outside [0, %d)", i, tokens[i], c.vocab);
+      return QDEC_REFUSED;
+    }
+  const bool all = flags & QDEC_ALL_LOGITS;
+  try {
+    m->last_stream = st;
+    const int H = c.hidden, V = c.vocab;
+    const int pos_start = m->kvlen[seq];
+    for (int c0 = 0; c0 < n_tokens; c0 += m->ws_T) {
+      const int T = std::min(m->ws_T, n_tokens - c0);
+      const int pos0 = pos_start + c0;
+      const bool last = c0 + T == n_tokens;
+      hipck(hipMemcpyAsync(m->d_prompt, tokens + c0, (size_t)T * 4, hipMemcpyHostToDevice, st), "token upload");
+      embed(m, st, m->d_prompt, T, m->x);
+      blocks(m, st, T, seq, pos0, nullptr);
+      if (all) {
+        rmsnorm_rows(m, st, m->x, H, m->output_norm, H, m->h, H, T, 0);
+        gemm(m, st, m->lm(), m->h, H, T, d_logits + (size_t)c0 * V, V, kModeStore);
+      } else if (last) {
+        gemv(m, st, m->lm(), m->x + (size_t)(T - 1) * H, H, m->output_norm, c.rms_eps, d_logits, V, 1, kModeStore);
+      }
+      if (last && d_token_out) {
+        const float* row = all ? d_logits + (size_t)(n_tokens - 1) * V : d_logits;
+        sample(m, st, row, V, 1, 0.f, 0, 0, d_token_out, nullptr);
+      }
+    }
+    m->kvlen[seq] += n_tokens;
+  } catch (const HipError& e) {
+    return fail_internal(m, st, e.msg);
+  }
+  return QDEC_OK;
+}
+
+int qdec_decode_step(qdec_model* m, const int32_t* tokens, int32_t n_seqs, float* d_logits, int32_t* d_token_out,
+                     float temperature, uint64_t seed, uint64_t step, uint32_t flags, void* stream) {
+  g_err.clear();
+  if (int rc = check_usable(m)) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  const qdec_config& c = m->cfg;
+  if (n_seqs < 1 || n_seqs > m->max_seqs) { set_err("n_seqs %d outside [1, %d]", n_seqs, m->max_seqs); return QDEC_REFUSED; }
+  if (!tokens || !d_logits || !d_token_out) { set_err("tokens, d_logits and d_token_out must not be NULL"); return QDEC_REFUSED; }
+  if (!(temperature >= 0.f) || !std::isfinite(temperature)) { set_err("temperature must be finite and >= 0"); return QDEC_REFUSED; }
+  if (flags & ~(uint32_t)QDEC_TOKENS_ON_DEVICE) { set_err("decode: unknown flag bits 0x%x", flags); return QDEC_REFUSED; }
+  const bool on_dev = flags & QDEC_TOKENS_ON_DEVICE;
+  for (int s = 0; s < n_seqs; ++s) {
+    if (m->kvlen[s] >= m->max_ctx) { set_err("seq %d: KV cache full (max_ctx %d)", s, m->max_ctx); return QDEC_REFUSED; }
+    if (!on_dev && (tokens[s] < 0 || tokens[s] >= c.vocab)) {
+      set_err("tokens[%d] = %d outside [0, %d)", s, tokens[s], c.vocab);
+      return QDEC_REFUSED;
+    }
+  }
+  try {
+    m->last_stream = st;
+    StepArgs sa{};
+    sa.n = n_seqs;
+    for (int s = 0; s < n_seqs; ++s) {
+      sa.pos[s] = m->kvlen[s];
+      sa.host_tok[s] = on_dev ? 0 : tokens[s];
+    }
+    sa.dev_tok = on_dev ? tokens : nullptr;
+    sa.vocab = c.vocab;
+    sa.d_pos = m->d_pos;
+    sa.d_tok = m->d_tok;
+    sa.err = m->err_dev;
+    {
+      Timed tm(m, st, "step_begin", 0, 0);
+      step_begin_kernel<<<1, 64, 0, st>>>(sa);
+    }
+    embed(m, st, m->d_tok, n_seqs, m->x);
+    blocks(m, st, n_seqs, 0, 0, m->d_pos);
+    gemv(m, st, m->lm(), m->x, c.hidden, m->output_norm, c.rms_eps, d_logits, c.vocab, n_seqs, kModeStore);
+    sample(m, st, d_logits, c.vocab, n_seqs, temperature, seed, step, d_token_out, nullptr);
+    for (int s = 0; s < n_seqs; ++s) m->kvlen[s] += 1;
+  } catch (const HipError& e) {
+    return fail_internal(m, st, e.msg);
+  }
+  return QDEC_OK;
+}
+
+int qdec_kv_reset(qdec_model* m, int32_t seq) {
+  g_err.clear();
+  if (int rc = check_usable(m)) return rc;
+  if (seq < -1 || seq >= m->max_seqs) { set_err("seq %d outside [-1, %d)", seq, m->max_seqs); return QDEC_REFUSED; }
+  if (seq < 0) std::fill(m->kvlen.begin(), m->kvlen.end(), 0);
+  else m->kvlen[seq] = 0;
+  return QDEC_OK;
+}
+
+int qdec_kv_write(qdec_model* m, int32_t seq, int32_t layer, const float* d_k, const float* d_v, int32_t n_pos,
+                  void* stream) {
+  g_err.clear();
+  if (int rc = check_usable(m)) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  const qdec_config& c = m->cfg;
+  if (seq < 0 || seq >= m->max_seqs) { set_err("seq %d outside [0, %d)", seq, m->max_seqs); return QDEC_REFUSED; }
+  if (layer < 0 || layer >= c.n_layer) { set_err("layer %d outside [0, %d)", layer, c.n_layer); return QDEC_REFUSED; }
+  if (n_pos < 0 || n_pos > m->max_ctx) { set_err("n_pos %d outside [0, %d]", n_pos, m->max_ctx); return QDEC_REFUSED; }
+  if (n_pos > 0 && (!d_k || !d_v)) { set_err("d_k and d_v must not be NULL"); return QDEC_REFUSED; }
+  try {
+    const size_t row = (size_t)c.head_dim * 4;
+    for (int g = 0; g < c.n_head_kv; ++g) {
+      const size_t dst = l_off(m, layer, seq, g);
+      if (n_pos) {
+        hipck(hipMemcpyAsync(m->kc + dst, d_k + (size_t)g * n_pos * c.head_dim, n_pos * row, hipMemcpyDeviceToDevice, st), "kv copy");
+        hipck(hipMemcpyAsync(m->vc + dst, d_v + (size_t)g * n_pos * c.head_dim, n_pos * row, hipMemcpyDeviceToDevice, st), "kv copy");
+      }
+    }
+    m->kvlen[seq] = n_pos;
+  } catch (const HipError& e) {
+    return fail_internal(m, st, e.msg);
+  }
+  return QDEC_OK;
+}
+
+int qdec_kv_len(const qdec_model* m, int32_t seq, int32_t* out) {
+  g_err.clear();
+  if (!m || !out) { set_err("model and out must not be NULL"); return QDEC_REFUSED; }
+  if (seq < 0 || seq >= m->max_seqs) { set_err("seq %d outside [0, %d)", seq, m->max_seqs); return QDEC_REFUSED; }
+  *out = m->kvlen[seq];
+  return QDEC_OK;
+}
+
+int qdec_poisoned(const qdec_model* m) { return m ? (m->poisoned ? 1 : 0) : -1; }
+
+int qdec_free(qdec_model* m) {
+  g_err.clear();
+  if (!m) { set_err("model handle is NULL"); return QDEC_REFUSED; }
+  drain(m->last_stream);
+  (void)hipDeviceSynchronize();
+  free_model(m);
+  return QDEC_OK;
+}
+
+int qdec_debug_dequant(qdec_model* m, const char* name, float* d_out, void* stream) {
+  g_err.clear();
+  if (int rc = check_usable(m)) return rc;
+  if (!name || !d_out) { set_err("name and d_out must not be NULL"); return QDEC_REFUSED; }
+  auto it = m->names.find(name);
+  if (it == m->names.end()) { set_err("no loaded matrix named '%s'", name); return QDEC_REFUSED; }
+  const NameRef& r = it->second;
+  hipStream_t st = (hipStream_t)stream;
+  try {
+    DequantArgs a{WView{r.mat->qs, r.mat->d, r.mat->type, r.mat->nblk}, nullptr, r.row_off, r.rows, r.cols, r.pair, d_out};
+    Timed tm(m, st, "dequant", 0, 0);
+    dequant_kernel<<<r.rows, 256, 0, st>>>(a);
+  } catch (const HipError& e) {
+    return fail_internal(m, st, e.msg);
+  }
+  return QDEC_OK;
+}
+
+int qdec_debug_embed(qdec_model* m, const int32_t* d_tokens, int32_t n, float* d_out, void* stream) {
+  g_err.clear();
+  if (int rc = check_usable(m)) return rc;
+  if (!d_tokens || !d_out || n <= 0) { set_err("d_tokens, d_out must not be NULL and n > 0"); return QDEC_REFUSED; }
+  hipStream_t st = (hipStream_t)stream;
+  try {
+    embed(m, st, d_tokens, n, d_out);
+  } catch (const HipError& e) {
+    return fail_internal(m, st, e.msg);
+  }
+  return QDEC_OK;
+}
+
+int qdec_debug_sample(const float* d_logits, int32_t rows, int32_t vocab, float temperature, uint64_t seed,
+                      uint64_t step, int32_t* d_out, void* stream) {
+  g_err.clear();
+  if (!d_logits || !d_out || rows <= 0 || vocab <= 0) { set_err("bad arguments"); return QDEC_REFUSED; }
+  if (!(temperature >= 0.f) || !std::isfinite(temperature)) { set_err("temperature must be finite and >= 0"); return QDEC_REFUSED; }
+  hipStream_t st = (hipStream_t)stream;
+  const int nch = (vocab + kSampleChunk - 1) / kSampleChunk;
+  float* pv = nullptr;
+  int* pi = nullptr;
+  if (hipMalloc(&pv, (size_t)rows * nch * 4) != hipSuccess || hipMalloc(&pi, (size_t)rows * nch * 4) != hipSuccess) {
+    (void)hipFree(pv);
+    set_err("internal: hipMalloc failed");
+    return QDEC_INTERNAL;
+  }
+  SampleArgs a{d_logits, vocab, vocab, rows, temperature, seed, step, pv, pi, nch, d_out, nullptr};
+  sample_stage1_kernel<<<dim3(nch, rows), 256, 0, st>>>(a);
+  sample_stage2_kernel<<<rows, 64, 0, st>>>(a);
+  hipError_t e = hipStreamSynchronize(st);
+  (void)hipFree(pv);
+  (void)hipFree(pi);
+  if (e != hipSuccess) { set_err("internal: %s", hipGetErrorString(e)); return QDEC_INTERNAL; }
+  return QDEC_OK;
+}
+
+int qdec_debug_matmul(int32_t type, int64_t rows, int64_t cols, const void* host_data, int64_t n_bytes,
+                      const float* d_x, int32_t n_x, float* d_y, void* stream) {
+  g_err.clear();
+  if (type != kF32 && type != kQ8_0 && type != kQ4_0) { set_err("type %d unsupported", type); return QDEC_REFUSED; }
+  if (rows <= 0 || cols <= 0 || rows > (1 << 24) || cols > (1 << 20) || !host_data || !d_x || !d_y || n_x <= 0) {
+    set_err("bad arguments");
+    return QDEC_REFUSED;
+  }
+  if (n_bytes != tensor_bytes(type, rows, cols)) { set_err("n_bytes %lld, expected %lld", (long long)n_bytes, (long long)tensor_bytes(type, rows, cols)); return QDEC_REFUSED; }
+  hipStream_t st = (hipStream_t)stream;
+  qdec_model tmp;  // holds the allocations only
+  int rc = QDEC_OK;
+  try {
+    qdec_tensor t{"w", type, rows, cols, host_data, n_bytes};
+    Stage s(type, rows, nblocks(cols));
+    for (int64_t r = 0; r < rows; ++r) s.put_row(r, t, r);
+    Mat w = upload(&tmp, s, (int)rows, (int)cols, (double)n_bytes, st);
+    const int kp = w.nblk * 32;
+    if (n_x <= 16) gemv(nullptr, st, w, d_x, kp, nullptr, 0.f, d_y, (int)rows, n_x, kModeStore);
+    else gemm(nullptr, st, w, d_x, kp, n_x, d_y, (int)rows, kModeStore);
+    hipck(hipStreamSynchronize(st), "matmul sync");
+  } catch (const HipError& e) {
+    set_err("internal: %s", e.msg.c_str());
+    rc = QDEC_INTERNAL;
+  }
+  for (void* p : tmp.allocs) (void)hipFree(p);
+  tmp.allocs.clear();
+  return rc;
+}
+
+int qdec_kernel_timing(qdec_model* m, int32_t enable, qdec_kstat* out, int32_t max_out, int32_t* n_out) {
+  g_err.clear();
+  if (int rc = check_usable(m)) return rc;
+  if (enable) {
+    m->timing = true;
+    return QDEC_OK;
+  }
+  m->timing = false;
+  try {
+    if (m->last_stream || !m->krecs.empty()) hipck(hipDeviceSynchronize(), "timing sync");
+    std::vector<qdec_kstat> agg;
+    for (auto& r : m->krecs) {
+      float ms = 0.f;
+      hipck(hipEventElapsedTime(&ms, r.a, r.b), "hipEventElapsedTime");
+      auto it = std::find_if(agg.begin(), agg.end(), [&](const qdec_kstat& k) { return std::strcmp(k.name, r.cls) == 0; });
+      if (it == agg.end()) {
+        qdec_kstat k{};
+        std::snprintf(k.name, sizeof(k.name), "%s", r.cls);
+        agg.push_back(k);
+        it = agg.end() - 1;
+      }
+      it->launches += 1;
+      it->total_ms += ms;
+      it->bytes += r.bytes;
+      it->flops += r.flops;
+      (void)hipEventDestroy(r.a);
+      (void)hipEventDestroy(r.b);
+    }
+    m->krecs.clear();
+    int k = 0;
+    for (; k < (int)agg.size() && k < max_out && out; ++k) out[k] = agg[k];
+    if (n_out) *n_out = k;
+  } catch (const HipError& e) {
+    return fail_internal(m, m->last_stream, e.msg);
+  }
+  return QDEC_OK;
+}
+
+}  // extern "C"

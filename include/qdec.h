@@ -1,0 +1,187 @@
+/*
+ * qdec.h -- C ABI of the MI355X decoder library (libqdec.so).
+ *
+ * The library runs the forward pass of a Llama / Qwen3 / Gemma-3-style decoder
+ * over GGUF block-quantized weights on one gfx950 GPU: prefill of a prompt and
+ * token-by-token decode over a KV cache, with greedy or temperature sampling.
+ *
+ * What each call computes is defined on these pages:
+ *   [W]  "How Modern LLMs Actually Generate Text: A Pure Python Walkthrough"
+ *        (Qwen3-0.6B in MLX), Steps 2-9: embedding, RMSNorm, RoPE, grouped-query
+ *        attention with a KV cache, SwiGLU, the block, LM head, sampling, the
+ *        generation loop.
+ *   [S]  Synsema "Local inference and architectures": the qwen3 architecture
+ *        file (op order, per-head Q/K norm before RoPE, tied head
+ *        `output.weight | token_embd.weight`), gelu_tanh for Gemma 3, and the
+ *        rule that weights stay block-quantized and are multiplied in f32.
+ *   [T]  tessl `python/README.md`, sections "Handle ownership, closing and
+ *        errors" and "How the buffers cross": opaque handle freed exactly once,
+ *        status 1 = refusal / status 2 = bug caught at the boundary, a poisoned
+ *        latch after GPU failure, waiting for in-flight work on failure.
+ *
+ * Conventions for every call:
+ *   - `d_*` arguments are device pointers on the current HIP device; other
+ *     pointers are host pointers.  The library never frees caller memory.
+ *   - `stream` is a hipStream_t (may be NULL for the null stream).  Work is
+ *     enqueued on it and the call returns without a host wait, except where a
+ *     call says otherwise.  Caller buffers must stay alive until the stream has
+ *     passed the call.
+ *   - Return value: QDEC_OK, QDEC_REFUSED (caller error found before anything
+ *     was enqueued; the handle stays usable; qdec_last_error() says which
+ *     argument and why), or QDEC_INTERNAL (a HIP error or a broken internal
+ *     invariant; the library drained the stream with a bounded wait and
+ *     latched the handle as poisoned: every later call on it is refused until
+ *     it is freed).
+ *   - A handle is used from one thread at a time; error text is thread-local.
+ */
+#ifndef QDEC_H
+#define QDEC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QDEC_ABI_VERSION 1
+
+enum { QDEC_OK = 0, QDEC_REFUSED = 1, QDEC_INTERNAL = 2 };
+
+/* Tensor types, numbered as a GGUF file numbers them (ggml type ids).
+ * Q8_0: 34-byte blocks = fp16 scale d + 32 int8 q, w = d*q.
+ * Q4_0: 18-byte blocks = fp16 scale d + 16 bytes; byte j holds element j in its
+ *       low nibble and element j+16 in its high nibble, w = d*(n-8).
+ * Blocks run along a row's input dimension; a row holds ceil(cols/32) blocks. */
+enum { QDEC_T_F32 = 0, QDEC_T_Q4_0 = 2, QDEC_T_Q8_0 = 8 };
+
+enum { QDEC_ACT_SILU = 0, QDEC_ACT_GELU_TANH = 1 };
+
+enum {
+  QDEC_ALL_LOGITS = 1u << 0,       /* prefill: logits of every position, not only the last */
+  QDEC_TOKENS_ON_DEVICE = 1u << 1  /* decode: `tokens` is a device pointer (e.g. last d_token_out) */
+};
+
+typedef struct qdec_model qdec_model; /* opaque; owned by the caller; freed exactly once */
+
+/* Model shape.  [W] Steps 3-7 and [S] "The format" define the block; window /
+ * window_period / rope_theta_local / sandwich_norm / act cover the Gemma-3
+ * variant: layer i uses full attention and rope_theta iff
+ * window == 0 or i % window_period == window_period - 1, otherwise keys with
+ * p - window < j <= p and rope_theta_local. */
+typedef struct {
+  int32_t n_layer, hidden, n_head, n_head_kv, head_dim, ffn, vocab;
+  float rms_eps, rope_theta, rope_theta_local;
+  int32_t window, window_period;
+  int32_t qk_norm;       /* per-head RMSNorm of q and k (gain [head_dim]) before RoPE */
+  int32_t sandwich_norm; /* RMSNorm of each sublayer output before its residual add */
+  int32_t act;           /* QDEC_ACT_* */
+} qdec_config;
+
+/* One tensor in GGUF naming ("token_embd.weight", "blk.3.attn_q.weight",
+ * "blk.3.attn_q_norm.weight", "blk.3.post_attention_norm.weight",
+ * "blk.3.post_ffw_norm.weight", "output_norm.weight", "output.weight", ...).
+ * Matrices are [rows = output dim][cols = input dim]; 1-D gains have rows = 1,
+ * type QDEC_T_F32.  host_data is borrowed for the duration of the call. */
+typedef struct {
+  const char* name;
+  int32_t type;
+  int64_t rows, cols;
+  const void* host_data;
+  int64_t n_bytes; /* rows*ceil(cols/32)*{34|18}, or rows*cols*4 for F32 */
+} qdec_tensor;
+
+int32_t qdec_abi_version(void);
+const char* qdec_last_error(void); /* valid until the next call on this thread */
+
+/* Validate every tensor (names required by cfg, types, dims, byte counts,
+ * finite fp16 scales) before allocating anything; then copy the weights into
+ * library-owned device memory, repacked to an aligned scale/quant split with the
+ * same byte count, and allocate an f32 KV cache of max_seqs x max_ctx
+ * positions.  `output.weight` is optional (absent: the head reuses
+ * token_embd.weight, [S] `a | b`).  Synchronizes `stream` before returning.
+ * Limits: 1 <= max_seqs <= 64; hidden and head_dim multiples of 32 and head_dim
+ * in {64, 128, 256}; n_head a multiple of n_head_kv. */
+int qdec_load_weights(const qdec_config* cfg, const qdec_tensor* tensors, int32_t n_tensors,
+                      int32_t max_seqs, int32_t max_ctx, void* stream, qdec_model** out);
+
+/* Prefill ([W] Step 9, phase 1): append n_tokens host token ids at positions
+ * kv_len(seq).. and advance kv_len(seq) by n_tokens.  Writes logits f32 [vocab]
+ * of the last position (or [n_tokens][vocab] with QDEC_ALL_LOGITS) to d_logits,
+ * and the greedy token of the last position to d_token_out if non-NULL.
+ * Refused: seq out of range, n_tokens <= 0, kv_len + n_tokens > max_ctx, a token
+ * outside [0, vocab), NULL d_logits. */
+int qdec_prefill(qdec_model* m, int32_t seq, const int32_t* tokens, int32_t n_tokens,
+                 float* d_logits, int32_t* d_token_out, uint32_t flags, void* stream);
+
+/* Decode step ([W] Step 9, phase 2): sequences 0..n_seqs-1 each consume
+ * tokens[s] at position kv_len(s), which then advances by one.  Writes logits
+ * f32 [n_seqs][vocab] and the chosen tokens int32 [n_seqs].  temperature == 0:
+ * greedy argmax (lowest index on ties); temperature > 0: argmax of
+ * logits/temperature + Gumbel noise from Philox4x64-10 with key (seed, 0) and
+ * counter (v/4, step, s, 0), word v%4, u = ((r>>41)+0.5)*2^-23.
+ * With QDEC_TOKENS_ON_DEVICE, tokens is a device pointer; ids outside [0, vocab)
+ * are clamped and latch an error reported as QDEC_INTERNAL by the next call.
+ * Refused: n_seqs outside [1, max_seqs], any kv_len(s) == max_ctx, a host token
+ * out of range, temperature < 0 or NaN, NULL outputs. */
+int qdec_decode_step(qdec_model* m, const int32_t* tokens, int32_t n_seqs, float* d_logits,
+                     int32_t* d_token_out, float temperature, uint64_t seed, uint64_t step,
+                     uint32_t flags, void* stream);
+
+/* Forget the cached positions of one sequence (seq = -1: all).  Host-side only;
+ * stale KV rows are never read past kv_len. */
+int qdec_kv_reset(qdec_model* m, int32_t seq);
+
+/* Install preset post-RoPE K and V, each f32 [n_head_kv][n_pos][head_dim]
+ * (device), for one (sequence, layer) at positions 0..n_pos-1, and set
+ * kv_len(seq) = n_pos. */
+int qdec_kv_write(qdec_model* m, int32_t seq, int32_t layer, const float* d_k, const float* d_v,
+                  int32_t n_pos, void* stream);
+
+int qdec_kv_len(const qdec_model* m, int32_t seq, int32_t* out);
+int qdec_poisoned(const qdec_model* m); /* 1 if latched, 0 if not, -1 for NULL */
+
+/* Release everything the handle owns, after draining its last stream (bounded
+ * wait, 30 s).  Call exactly once per handle. */
+int qdec_free(qdec_model* m);
+
+/* ---------------------------------------------------------------- tests and measurement */
+
+/* Decode the named tensor (as loaded) to f32 [rows][cols] in d_out with the same
+ * in-kernel dequantization the forward pass uses.  Bit-exact by construction. */
+int qdec_debug_dequant(qdec_model* m, const char* name, float* d_out, void* stream);
+
+/* Embedding gather of n device token ids into d_out f32 [n][hidden]. */
+int qdec_debug_embed(qdec_model* m, const int32_t* d_tokens, int32_t n, float* d_out, void* stream);
+
+/* Row-wise token choice over d_logits [rows][vocab] with the decode step's rule
+ * (temperature 0: argmax with the lowest index on ties, NaN ranking above every
+ * number; else Gumbel-max with counter (v/4, step, row, 0)).  d_out int32 [rows]. */
+int qdec_debug_sample(const float* d_logits, int32_t rows, int32_t vocab, float temperature,
+                      uint64_t seed, uint64_t step, int32_t* d_out, void* stream);
+
+/* One projection y[r][n] = sum_k W[n][k] x[r][k] with the forward pass's kernels:
+ * the decode GEMV for n_x <= 16, the prefill MFMA GEMM above.  W is given in GGUF
+ * bytes on the host (uploaded and repacked per call; synchronous).  d_x f32
+ * [n_x][ceil(cols/32)*32] (zero padded), d_y f32 [n_x][rows]. */
+int qdec_debug_matmul(int32_t type, int64_t rows, int64_t cols, const void* host_data,
+                      int64_t n_bytes, const float* d_x, int32_t n_x, float* d_y, void* stream);
+
+/* Per-kernel timing with HIP events on the launch stream.  enable = 1 starts
+ * recording every launch; enable = 0 synchronizes, writes up to max_out records
+ * (one per kernel class) and stops.  Records carry the algorithmic bytes and
+ * flops of each launch as the library counts them. */
+typedef struct {
+  char name[32];
+  int64_t launches;
+  double total_ms;
+  double bytes; /* algorithmic HBM bytes summed over launches */
+  double flops; /* algorithmic flops summed over launches */
+} qdec_kstat;
+
+int qdec_kernel_timing(qdec_model* m, int32_t enable, qdec_kstat* out, int32_t max_out, int32_t* n_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QDEC_H */

@@ -10,7 +10,8 @@ Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC'11), a counter-based
 generator:
 
   counter = (v // 4, step, seq, 0), key = (seed, 0), word = v % 4
-  u_v = ((r >> 40) + 0.5) * 2^-24        (top 24 bits, exact in float32)
+  u_v = ((r >> 41) + 0.5) * 2^-23        (top 23 bits; exact in float32 and
+                                          strictly inside (0, 1), so G is finite)
 
 Philox4x64-10: ten rounds of
   (hi0, lo0) = M0 * c0,  (hi1, lo1) = M1 * c2          (128-bit products)
@@ -65,7 +66,7 @@ def uniforms(vocab, seed, step, seq):
     words = philox4x64_10((v >> U64(2), U64(step), U64(seq), U64(0)), (seed & 0xFFFFFFFFFFFFFFFF, 0))
     w = np.stack(words, axis=0)
     r = w[(v & U64(3)).astype(np.int64), np.arange(vocab)]
-    return (((r >> U64(40)).astype(np.float64) + 0.5) * 2.0 ** -24).astype(np.float32)
+    return (((r >> U64(41)).astype(np.float64) + 0.5) * 2.0 ** -23).astype(np.float32)
 
 
 def gumbel(vocab, seed, step, seq):
@@ -103,4 +104,4 @@ def uniforms_batch(vocab, seed, steps, seq):
     w = np.stack(np.broadcast_arrays(*words), axis=0)
     sel = np.broadcast_to((v & U64(3)).astype(np.int64), w.shape[1:])
     r = np.take_along_axis(w, sel[None], axis=0)[0]
-    return (((r >> U64(40)).astype(np.float64) + 0.5) * 2.0 ** -24).astype(np.float32)
+    return (((r >> U64(41)).astype(np.float64) + 0.5) * 2.0 ** -23).astype(np.float32)

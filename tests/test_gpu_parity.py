@@ -1,0 +1,246 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bit-exact: dequantization, embedding gather, argmax token choice.
+Within 2e-3 (max |gpu - oracle| / max |oracle| per row): projections, every
+logits row of prefill and decode.  Tokens: identical wherever the oracle's
+top-2 margin exceeds twice that tolerance; decode continues by teacher forcing
+(the oracle consumes the GPU's tokens).
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import OracleModel, blocks, sampler
+from tests.gpu_helpers import SMALL, TOL, as_np, check_row, rel_err, token_agrees
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import decoder_gguf_quantized_amd as qdec  # noqa: E402
+
+
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+_MODELS = {}
+
+
+def model_for(key, max_ctx=256, max_seqs=2):
+    """(cfg, tensors, GPU Model) cached per key."""
+    if key not in _MODELS:
+        cfg = synth.get(key) if key.startswith("c") else dict(SMALL[key])
+        t = synth.generate(cfg)
+        dev()
+        _MODELS[key] = (cfg, t, qdec.Model(cfg, t, max_seqs=max_seqs, max_ctx=max_ctx))
+    return _MODELS[key]
+
+
+# ---------------------------------------------------------------- bit-exact pieces
+@pytest.mark.parametrize("key", ["c1"] + sorted(SMALL))
+def test_dequant_bit_exact(key):
+    cfg, t, m = model_for(key)
+    for name, tt in t.items():
+        if tt.rows == 1:
+            continue
+        out = torch.empty((tt.rows, tt.cols), dtype=torch.float32, device=dev())
+        m.debug_dequant(name, out)
+        torch.cuda.synchronize()
+        want = blocks.dequant(tt.type, tt.data, tt.rows, tt.cols)
+        got = as_np(out)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), name
+
+
+@pytest.mark.parametrize("key", ["c1", "llama_q4_hd64_g4", "qwen3_hd128_g2"])
+def test_embedding_gather_bit_exact(key):
+    cfg, t, m = model_for(key)
+    ids = np.array([0, cfg["vocab"] - 1, 7, 7, 123 % cfg["vocab"]], dtype=np.int32)
+    out = torch.empty((len(ids), cfg["hidden"]), dtype=torch.float32, device=dev())
+    m.debug_embed(torch.from_numpy(ids).to(dev()), out)
+    torch.cuda.synchronize()
+    te = t["token_embd.weight"]
+    want = blocks.dequant(te.type, te.data, te.rows, te.cols)[ids]
+    assert np.array_equal(as_np(out).view(np.uint32), want.view(np.uint32))
+
+
+def test_argmax_bit_exact_with_ties_and_nan():
+    rng = np.random.default_rng(5)
+    V = 9000  # three 4096-entry chunks, ragged tail
+    L = rng.standard_normal((8, V)).astype(np.float32)
+    L[1, :] = 1.0                       # all equal -> 0
+    L[2, 4095] = L[2, 5000] = 50.0      # tie across chunks -> 4095
+    L[3, 8999] = 60.0                   # last element
+    L[4, 17] = np.nan; L[4, 9] = np.nan  # first NaN wins (numpy's rule)
+    L[5, :] = -np.inf; L[5, 300] = -1e30
+    L[6, 4096] = np.float32(3e38)
+    L[7, 0] = -0.0; L[7, 1:] = -1.0; L[7, 5] = 0.0   # -0 == +0 -> lower index
+    out = torch.empty(8, dtype=torch.int32, device=dev())
+    qdec.debug_sample(torch.from_numpy(L).to(dev()), 0.0, 0, 0, out)
+    torch.cuda.synchronize()
+    want = [sampler.greedy(r) for r in L]
+    assert as_np(out).tolist() == want
+
+
+@pytest.mark.parametrize("temperature", [1.0, 0.7])
+def test_gumbel_sampling_matches_oracle(temperature):
+    rng = np.random.default_rng(6)
+    rows, V = 16, 151936
+    L = (rng.standard_normal((rows, V)) * 3).astype(np.float32)
+    out = torch.empty(rows, dtype=torch.int32, device=dev())
+    agree = 0
+    for step in range(4):
+        qdec.debug_sample(torch.from_numpy(L).to(dev()), temperature, 5, step, out)
+        torch.cuda.synchronize()
+        got = as_np(out)
+        for r in range(rows):
+            s = sampler.scores(L[r], temperature, 5, step, r)
+            top2 = np.partition(s, -2)[-2:]
+            if top2[1] - top2[0] > 1e-4:
+                assert got[r] == int(np.argmax(s)), (step, r)
+                agree += 1
+    assert agree >= 60
+
+
+# ---------------------------------------------------------------- projections
+MATMUL_CASES = [
+    # (type, rows, cols, n_x)
+    (synth.T_Q8_0, 4096, 1024, 1), (synth.T_Q8_0, 1000, 688, 3), (synth.T_Q8_0, 257, 1152, 16),
+    (synth.T_Q8_0, 300, 256, 17), (synth.T_Q8_0, 1024, 3072, 130),
+    (synth.T_Q4_0, 6144, 4096, 1), (synth.T_Q4_0, 130, 14336, 2), (synth.T_Q4_0, 512, 1408, 9),
+    (synth.T_Q4_0, 333, 512, 70),
+    (synth.T_F32, 1024, 256, 1), (synth.T_F32, 200, 352, 5), (synth.T_F32, 129, 96, 65),
+]
+
+
+@pytest.mark.parametrize("ttype,rows,cols,n_x", MATMUL_CASES)
+def test_projection_matches_oracle(ttype, rows, cols, n_x):
+    rng = np.random.default_rng(rows * 7 + cols + n_x)
+    w = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
+    raw = synth.encode(ttype, w)
+    kp = ((cols + 31) // 32) * 32
+    x = np.zeros((n_x, kp), np.float32)
+    x[:, :cols] = rng.standard_normal((n_x, cols))
+    y = torch.empty((n_x, rows), dtype=torch.float32, device=dev())
+    qdec.debug_matmul(ttype, rows, cols, raw, torch.from_numpy(x).to(dev()), y)
+    W = blocks.dequant(ttype, raw, rows, cols).astype(np.float64)
+    want = x[:, :cols].astype(np.float64) @ W.T
+    got = as_np(y)
+    for r in range(n_x):
+        check_row(got[r], want[r])
+
+
+# ---------------------------------------------------------------- whole model
+def run_gpu(m, cfg, prompt, n_steps, seq=0):
+    """Prefill (all logits) then n_steps greedy decode steps chained on device.
+    Returns prefill logits [T][V], decode logits [n][V], decode tokens [n]."""
+    V = cfg["vocab"]
+    T = len(prompt)
+    pl = torch.empty((T, V), dtype=torch.float32, device=dev())
+    tok = torch.empty(1, dtype=torch.int32, device=dev())
+    m.kv_reset()
+    m.prefill(seq, prompt, pl, tok, all_logits=True)
+    dl = torch.empty((n_steps, V), dtype=torch.float32, device=dev())
+    toks = torch.empty((n_steps, 1), dtype=torch.int32, device=dev())
+    cur = tok
+    for s in range(n_steps):
+        m.decode_step(cur, dl[s:s + 1], toks[s])
+        cur = toks[s]
+    torch.cuda.synchronize()
+    first = int(as_np(tok)[0])
+    return as_np(pl), as_np(dl), [first] + as_np(toks).reshape(-1).tolist()
+
+
+def oracle_run(cfg, t, prompt, gpu_tokens, n_steps):
+    om = OracleModel(cfg, t, max_ctx=len(prompt) + n_steps + 1)
+    pl = om.forward(0, prompt, all_logits=True)
+    dl = [om.forward(0, [gpu_tokens[s]])[0] for s in range(n_steps)]
+    return pl, np.array(dl)
+
+
+@pytest.mark.parametrize("key", ["c1"] + sorted(SMALL))
+def test_prefill_and_decode_match_oracle(key):
+    cfg, t, m = model_for(key)
+    T, n = 70, 12
+    prompt = synth.prompt(cfg, T)
+    g_pl, g_dl, g_tok = run_gpu(m, cfg, prompt, n)
+    o_pl, o_dl = oracle_run(cfg, t, prompt, g_tok, n)
+    errs = [check_row(g_pl[i], o_pl[i]) for i in range(T)]
+    errs += [check_row(g_dl[s], o_dl[s]) for s in range(n)]
+    assert token_agrees(g_tok[0], o_pl[-1])
+    for s in range(n):
+        assert token_agrees(g_tok[s + 1], o_dl[s])
+    print(f"{key}: max rel err {max(errs):.2e}")
+
+
+@pytest.mark.parametrize("key", ["c1", "gemma_hd256_g4"])
+def test_gpu_decode_equals_gpu_prefill_recompute(key):
+    cfg, t, m = model_for(key)
+    prompt = synth.prompt(cfg, 20)
+    g_pl, g_dl, g_tok = run_gpu(m, cfg, prompt, 6)
+    full = list(prompt) + g_tok[:6]
+    V = cfg["vocab"]
+    pl = torch.empty((len(full), V), dtype=torch.float32, device=dev())
+    m.kv_reset()
+    m.prefill(0, full, pl, None, all_logits=True)
+    torch.cuda.synchronize()
+    rec = as_np(pl)
+    for s in range(6):
+        check_row(g_dl[s], rec[20 + s])
+
+
+def test_split_prefill_and_reset_are_consistent():
+    cfg, t, m = model_for("qwen3_hd128_g2")
+    V = cfg["vocab"]
+    prompt = synth.prompt(cfg, 90)
+    a = torch.empty(V, dtype=torch.float32, device=dev())
+    b = torch.empty(V, dtype=torch.float32, device=dev())
+    c = torch.empty(V, dtype=torch.float32, device=dev())
+    m.kv_reset()
+    m.prefill(0, prompt, a)
+    m.kv_reset()
+    m.prefill(0, prompt[:37], b)
+    m.prefill(0, prompt[37:], b)
+    m.kv_reset()
+    m.prefill(0, prompt, c)
+    torch.cuda.synchronize()
+    check_row(as_np(b), as_np(a))
+    assert np.array_equal(as_np(a), as_np(c))  # reset then rerun: bit-identical
+    assert m.kv_len(0) == 90
+
+
+def test_two_sequences_are_independent():
+    cfg, t, m = model_for("qwen3_hd128_g2")
+    V = cfg["vocab"]
+    p0, p1 = synth.prompt(cfg, 30), synth.prompt(cfg, 45, tag="other")
+    l0 = torch.empty(V, dtype=torch.float32, device=dev())
+    l1 = torch.empty(V, dtype=torch.float32, device=dev())
+    m.kv_reset()
+    m.prefill(0, p0, l0)
+    m.prefill(1, p1, l1)
+    dl = torch.empty((2, V), dtype=torch.float32, device=dev())
+    tk = torch.empty(2, dtype=torch.int32, device=dev())
+    m.decode_step([5, 9], dl, tk)
+    torch.cuda.synchronize()
+    om = OracleModel(cfg, t, max_ctx=64, n_seqs=2)
+    om.forward(0, p0)
+    om.forward(1, p1)
+    o = om.decode([5, 9])
+    check_row(as_np(dl)[0], o[0])
+    check_row(as_np(dl)[1], o[1])
+    assert m.kv_len(0) == 31 and m.kv_len(1) == 46
+
+
+def test_refusals_leave_handle_usable():
+    cfg, t, m = model_for("c1")
+    V = cfg["vocab"]
+    lg = torch.empty(V, dtype=torch.float32, device=dev())
+    with pytest.raises(qdec.QdecError):
+        m.prefill(0, [V], lg)
+    with pytest.raises(qdec.QdecError):
+        m.prefill(5, [1], lg)
+    with pytest.raises(qdec.QdecError):
+        m.decode_step([1], lg, torch.empty(1, dtype=torch.int32, device=dev()), temperature=-1.0)
+    m.kv_reset()
+    m.prefill(0, [1, 2, 3], lg)
+    assert not m.poisoned and m.kv_len(0) == 3

@@ -41,10 +41,13 @@ def test_uniforms_layout_and_range():
     u = sampler.uniforms(37, seed=5, step=2, seq=3)
     assert u.dtype == np.float32 and u.shape == (37,)
     assert (u > 0).all() and (u < 1).all()
+    # the extreme words map strictly inside (0, 1) in float32
+    lo, hi = np.float32(0.5 * 2.0 ** -23), np.float32((2 ** 23 - 0.5) * 2.0 ** -23)
+    assert 0 < lo and hi < 1
     # element v takes word v % 4 of counter (v // 4, step, seq, 0)
     w = sampler.philox4x64_10((np.uint64(6), np.uint64(2), np.uint64(3), np.uint64(0)), (5, 0))
     r = int(w[1])
-    assert u[25] == np.float32(((r >> 40) + 0.5) * 2.0 ** -24)
+    assert u[25] == np.float32(((r >> 41) + 0.5) * 2.0 ** -23)
     ub = sampler.uniforms_batch(37, 5, [0, 2], 3)
     assert np.array_equal(ub[1], u)
 
