@@ -20,18 +20,23 @@
 namespace qd {
 
 struct AttnDecodeArgs {
-  const float* q;       // [B][nq*hd], after QK-norm and RoPE
-  const float* kc;      // layer base of the cache: [B][nkv][ctx][hd]
-  const float* vc;
+  const float* qkv;     // [B][ldqkv] raw projections q | k | v (before QK-norm and RoPE)
+  int ldqkv;
+  float* kc;            // layer base of the cache: [B][nkv][ctx][hd]
+  float* vc;
   int ctx;
-  const int* pos;       // [B] position of the newest token (already in the cache)
+  const int* pos;       // [B] position of the new token
   int nq, nkv;
   int window;           // 0 = full causal
   int chunk;            // positions per workgroup
-  float scale_log2;     // hd^-1/2 * log2(e)
-  float* part_o;        // [B][nq][nchunk][hd], unnormalised
-  float* part_ml;       // [B][nq][nchunk][2]: running max (log2 domain), sum
   int nchunk;
+  const float* q_norm;  // [hd] or null (no QK-norm)
+  const float* k_norm;
+  float eps;
+  const float2* rope;   // [ctx][hd/2] (cos, sin) of f32(pos) * inv_freq[i]
+  float scale_log2;     // hd^-1/2 * log2(e)
+  float* part_o;        // [B][nq][nchunk][hd], unnormalised partial outputs
+  float* part_ml;       // [B][nq][nchunk][2]: running max (log2 domain), sum
 };
 
 QD_DEV void attn_key_range(int p, int window, int& lo, int& hi) {
@@ -39,6 +44,34 @@ QD_DEV void attn_key_range(int p, int window, int& lo, int& hi) {
   lo = window > 0 ? max(0, p - window + 1) : 0;
 }
 
+// Per-head RMSNorm (gain nw, or none) and the half-split rotation of one head
+// held as 8 dims per lane over a group of LG = hd/8 lanes.  Dim d pairs with
+// d + hd/2, which lives in lane li ^ (LG/2) at the same slot.
+template <int LG>
+QD_DEV void norm_rope_group(float (&v)[8], const float* nw, float eps, int hd, int li, const float (&c)[8],
+                            const float (&sn)[8]) {
+  if (nw) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+    ss = group_sum<LG>(ss);
+    const float scale = 1.0f / sqrtf(ss / (float)hd + eps);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = v[e] * scale * nw[8 * li + e];
+  }
+  const bool first_half = li < LG / 2;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float other = __shfl_xor(v[e], LG / 2);
+    v[e] = first_half ? v[e] * c[e] - other * sn[e] : v[e] * c[e] + other * sn[e];
+  }
+}
+
+// Workgroup = (chunk of positions, KV head, sequence); it serves the KV head's
+// whole group of query heads.  Prologue: QK-norm + RoPE of the group's queries,
+// and, in the chunk that holds the new position, of the new key, which it also
+// appends (with the new value) to the cache.  Each workgroup writes one partial
+// (m, l, o) per query head; attn_combine_kernel merges the chunks.
 template <int HD, int G>
 __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
   constexpr int LG = HD / 8;      // lanes per position
@@ -55,40 +88,80 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
   const int start = max(lo, c * a.chunk), end = min(hi + 1, (c + 1) * a.chunk);
 
   const int tid = threadIdx.x, gi = tid / LG, li = tid % LG;
-  const int group = a.nq / a.nkv;
+  const float* row = a.qkv + (size_t)s * a.ldqkv;
+  float cs[8], sn[8];
+  {
+    const float2* rt = a.rope + (size_t)p * (HD / 2) + (8 * li) % (HD / 2);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float2 t = rt[e];
+      cs[e] = t.x;
+      sn[e] = t.y;
+    }
+  }
   float q[G][8], o[G][8], m[G], l[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float4* qp = reinterpret_cast<const float4*>(a.q + (size_t)s * a.nq * HD + (size_t)(g * group + h) * HD + li * 8);
+    const float4* qp = reinterpret_cast<const float4*>(row + (size_t)(g * G + h) * HD + li * 8);
     float4 q0 = qp[0], q1 = qp[1];
-    q[h][0] = q0.x * a.scale_log2; q[h][1] = q0.y * a.scale_log2;
-    q[h][2] = q0.z * a.scale_log2; q[h][3] = q0.w * a.scale_log2;
-    q[h][4] = q1.x * a.scale_log2; q[h][5] = q1.y * a.scale_log2;
-    q[h][6] = q1.z * a.scale_log2; q[h][7] = q1.w * a.scale_log2;
+    float v[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+    norm_rope_group<LG>(v, a.q_norm, a.eps, HD, li, cs, sn);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[h][e] = v[e] * a.scale_log2;
     m[h] = -INFINITY;
     l[h] = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
   }
   const size_t head_base = ((size_t)s * a.nkv + g) * a.ctx;
+  float kn[8], vn[8];
+  const bool has_new = c == c_hi;
+  if (has_new) {
+    const float4* kp = reinterpret_cast<const float4*>(row + (size_t)(a.nq + g) * HD + li * 8);
+    const float4* vp = reinterpret_cast<const float4*>(row + (size_t)(a.nq + a.nkv + g) * HD + li * 8);
+    float4 k0 = kp[0], k1 = kp[1], v0 = vp[0], v1 = vp[1];
+    float kv8[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+    norm_rope_group<LG>(kv8, a.k_norm, a.eps, HD, li, cs, sn);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kn[e] = kv8[e];
+    vn[0] = v0.x; vn[1] = v0.y; vn[2] = v0.z; vn[3] = v0.w;
+    vn[4] = v1.x; vn[5] = v1.y; vn[6] = v1.z; vn[7] = v1.w;
+    if (gi == 0) {
+      float4* kd = reinterpret_cast<float4*>(a.kc + (head_base + p) * HD + li * 8);
+      float4* vd = reinterpret_cast<float4*>(a.vc + (head_base + p) * HD + li * 8);
+      kd[0] = make_float4(kn[0], kn[1], kn[2], kn[3]);
+      kd[1] = make_float4(kn[4], kn[5], kn[6], kn[7]);
+      vd[0] = v0;
+      vd[1] = v1;
+    }
+  }
   for (int j = start + gi; j < end; j += NG) {
-    const float4* kp = reinterpret_cast<const float4*>(a.kc + (head_base + j) * HD + li * 8);
-    const float4* vp = reinterpret_cast<const float4*>(a.vc + (head_base + j) * HD + li * 8);
-    float4 k0 = kp[0], k1 = kp[1];
-    float4 v0 = vp[0], v1 = vp[1];
+    float k[8], v[8];
+    if (has_new && j == p) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        k[e] = kn[e];
+        v[e] = vn[e];
+      }
+    } else {
+      const float4* kp = reinterpret_cast<const float4*>(a.kc + (head_base + j) * HD + li * 8);
+      const float4* vp = reinterpret_cast<const float4*>(a.vc + (head_base + j) * HD + li * 8);
+      float4 k0 = kp[0], k1 = kp[1], v0 = vp[0], v1 = vp[1];
+      k[0] = k0.x; k[1] = k0.y; k[2] = k0.z; k[3] = k0.w; k[4] = k1.x; k[5] = k1.y; k[6] = k1.z; k[7] = k1.w;
+      v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w; v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+    }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float dot = q[h][0] * k0.x + q[h][1] * k0.y + q[h][2] * k0.z + q[h][3] * k0.w +
-                  q[h][4] * k1.x + q[h][5] * k1.y + q[h][6] * k1.z + q[h][7] * k1.w;
-      float sc = group_sum<LG>(dot);
-      float mn = fmaxf(m[h], sc);
-      float corr = exp2f(m[h] - mn);
-      float pr = exp2f(sc - mn);
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dot += q[h][e] * k[e];
+      const float sc = group_sum<LG>(dot);
+      const float mn = fmaxf(m[h], sc);
+      const float corr = exp2f(m[h] - mn);
+      const float pr = exp2f(sc - mn);
       l[h] = l[h] * corr + pr;
-      o[h][0] = o[h][0] * corr + pr * v0.x; o[h][1] = o[h][1] * corr + pr * v0.y;
-      o[h][2] = o[h][2] * corr + pr * v0.z; o[h][3] = o[h][3] * corr + pr * v0.w;
-      o[h][4] = o[h][4] * corr + pr * v1.x; o[h][5] = o[h][5] * corr + pr * v1.y;
-      o[h][6] = o[h][6] * corr + pr * v1.z; o[h][7] = o[h][7] * corr + pr * v1.w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[h][e] = o[h][e] * corr + pr * v[e];
       m[h] = mn;
     }
   }
@@ -109,12 +182,12 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
     float L = 0.f, O = 0.f;
     if (M != -INFINITY) {
       for (int k = 0; k < NG; ++k) {
-        float w = sm_m[k][h] == -INFINITY ? 0.f : exp2f(sm_m[k][h] - M);
+        const float w = sm_m[k][h] == -INFINITY ? 0.f : exp2f(sm_m[k][h] - M);
         L += sm_l[k][h] * w;
         O += sm_o[k][h][dd] * w;
       }
     }
-    const size_t pi = ((size_t)s * a.nq + g * group + h) * a.nchunk + c;
+    const size_t pi = ((size_t)s * a.nq + g * G + h) * a.nchunk + c;
     a.part_o[pi * HD + dd] = O;
     if (dd == 0) {
       a.part_ml[pi * 2 + 0] = M;
@@ -127,30 +200,45 @@ struct AttnCombineArgs {
   const float* part_o;
   const float* part_ml;
   const int* pos;
-  int nq, hd, window, chunk, nchunk;
+  int nq, window, chunk, nchunk;
   float* out;           // [B][nq*hd]
 };
 
-// One workgroup per (query head, sequence); thread dd merges dimension dd over
-// the chunks that hold keys: O = sum_c o_c 2^(m_c - M) / sum_c l_c 2^(m_c - M).
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnCombineArgs a) {
-  const int h = blockIdx.x, s = blockIdx.y, dd = threadIdx.x;
-  if (dd >= a.hd) return;
+// Merge of the chunks that hold keys for (query head, sequence): one wave per
+// head; lane k takes chunks k, k+64, ... and the lanes merge their running
+// (m, l) pairs; then each lane rescales and sums its dims over the chunks.
+template <int HD>
+__global__ __launch_bounds__(64) void attn_combine_kernel(AttnCombineArgs a) {
+  const int h = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
   int lo, hi;
   attn_key_range(a.pos[s], a.window, lo, hi);
   const int c_lo = lo / a.chunk, c_hi = hi / a.chunk;
   const size_t base = ((size_t)s * a.nq + h) * a.nchunk;
   float M = -INFINITY;
-  for (int c = c_lo; c <= c_hi; ++c) M = fmaxf(M, a.part_ml[(base + c) * 2]);
-  float L = 0.f, O = 0.f;
-  for (int c = c_lo; c <= c_hi; ++c) {
-    float mc = a.part_ml[(base + c) * 2];
-    float w = mc == -INFINITY ? 0.f : exp2f(mc - M);
-    L += a.part_ml[(base + c) * 2 + 1] * w;
-    O += a.part_o[(base + c) * a.hd + dd] * w;
+  for (int c = c_lo + lane; c <= c_hi; c += 64) M = fmaxf(M, a.part_ml[(base + c) * 2]);
+  M = wave_max(M);
+  float L = 0.f;
+  for (int c = c_lo + lane; c <= c_hi; c += 64) {
+    const float mc = a.part_ml[(base + c) * 2];
+    L += mc == -INFINITY ? 0.f : a.part_ml[(base + c) * 2 + 1] * exp2f(mc - M);
   }
-  a.out[(size_t)s * a.nq * a.hd + (size_t)h * a.hd + dd] = O / L;
+  L = wave_sum(L);
+  const float inv = 1.0f / L;
+  constexpr int DPL = HD / 64;  // dims per lane
+  float o[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) o[e] = 0.f;
+  for (int c = c_lo; c <= c_hi; ++c) {
+    const float mc = a.part_ml[(base + c) * 2];
+    const float w = mc == -INFINITY ? 0.f : exp2f(mc - M);
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) o[e] += a.part_o[(base + c) * HD + lane + 64 * e] * w;
+  }
+  float* dst = a.out + (size_t)s * a.nq * HD + (size_t)h * HD;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) dst[lane + 64 * e] = o[e] * inv;
 }
+
 
 struct AttnPrefillArgs {
   const float* q;       // [T][nq*hd]

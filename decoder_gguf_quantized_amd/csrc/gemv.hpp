@@ -10,8 +10,11 @@
 //   * scales and quants are split (SoA) so a lane issues one 16-byte load per
 //     unit (Q8_0: 16 weights, Q4_0: a whole 32-weight block, F32: 4 weights);
 //     64 lanes read 1 KB contiguous per row: fully coalesced.
-//   * each wave streams two rows at once; the input rows sit in LDS (RMSNorm
-//     prologue fused), so a unit's activations are read once for both rows.
+//   * each wave streams R rows at once with U units per lane in flight per row
+//     (R*U 16-byte loads per lane before the first use); the input rows sit in
+//     LDS (RMSNorm prologue fused), so a unit's activations are read once for
+//     all R rows.  The first row group's weights are requested before the
+//     prologue, so the input staging overlaps the first weight fetch.
 //   * the reduction over the 64 lanes is a DPP tree; lane 0 writes the result
 //     with the mode's epilogue (store, residual add, or gate/up pair with the
 //     activation: act(gate) * up).
@@ -38,6 +41,8 @@ struct GemvArgs {
   float* y;              // output rows [m][ldy]
   int ldy;
   int m;                 // input rows in this launch (<= template M)
+  float* const* y_ind;   // if non-null, the output base is *y_ind + y_off (graph replays)
+  long y_off;
 };
 
 QD_DEV float act_silu(float g) { return g / (1.0f + expf(-g)); }
@@ -137,12 +142,107 @@ QD_DEV void gemv_stage_x(const GemvArgs& a, float* xs, int kp) {
   }
 }
 
-template <int QT, int M, int MODE>
+// Weights of one row group held in registers between load and use.
+template <int QT, int R, int U>
+struct WRegs {
+  uint4 w[R][U];
+  float d[R][U];
+};
+
+// Rows of group `grp`: R consecutive rows, or for the pair modes R/2 outputs,
+// each a (gate, up) row pair of the interleaved layout.
+template <int R, bool PAIR>
+QD_DEV void group_rows(int grp, int rows, int (&r)[R]) {
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    if constexpr (PAIR) {
+      const int n = grp * (R / 2) + i / 2;
+      r[i] = pair_gate_row(n) + (i & 1) * 32;
+    } else {
+      r[i] = min(grp * R + i, rows - 1);
+    }
+  }
+}
+
+// Issue the loads of U units per lane for R rows: unit u = base + lane + 64 k.
+template <int QT, int R, int U>
+QD_DEV void gemv_load(const GemvArgs& a, const int (&r)[R], int base, int lane, int nunits, WRegs<QT, R, U>& W) {
+  const int kp = a.nblk * 32;
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    const int u = base + lane + 64 * k;
+    const bool ok = u < nunits;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      if constexpr (QT == kQ8_0) {
+        W.w[i][k] = ok ? *reinterpret_cast<const uint4*>(a.qs + (size_t)r[i] * kp + 16 * u) : make_uint4(0, 0, 0, 0);
+        W.d[i][k] = ok ? load_half(a.d + (size_t)r[i] * a.nblk + (u >> 1)) : 0.f;
+      } else if constexpr (QT == kQ4_0) {
+        W.w[i][k] = ok ? reinterpret_cast<const uint4*>(a.qs)[(size_t)r[i] * a.nblk + u] : make_uint4(0, 0, 0, 0);
+        W.d[i][k] = ok ? load_half(a.d + (size_t)r[i] * a.nblk + u) : 0.f;
+      } else {
+        W.w[i][k] = ok ? reinterpret_cast<const uint4*>(a.qs)[(size_t)r[i] * (kp / 4) + u] : make_uint4(0, 0, 0, 0);
+        W.d[i][k] = 1.f;
+      }
+    }
+  }
+}
+
+template <int QT, int R, int U, int M>
+QD_DEV void gemv_compute(const float* xs, const float* xsum, int kp, int nblk, int base, int lane, int nunits,
+                         const WRegs<QT, R, U>& W, float (&acc)[R][M]) {
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    const int u = base + lane + 64 * k;
+    if (u >= nunits) continue;
+#pragma unroll
+    for (int mi = 0; mi < M; ++mi) {
+      if constexpr (QT == kQ8_0) {
+        const float4* xv = reinterpret_cast<const float4*>(xs + mi * kp + 16 * u);
+        float4 xa = xv[0], xb = xv[1], xc = xv[2], xd = xv[3];
+#pragma unroll
+        for (int i = 0; i < R; ++i) acc[i][mi] += W.d[i][k] * dot16_q8(W.w[i][k], xa, xb, xc, xd);
+      } else if constexpr (QT == kQ4_0) {
+        const float* xp = xs + mi * kp + 32 * u;
+        const float bs = 8.0f * xsum[mi * nblk + u];
+#pragma unroll
+        for (int i = 0; i < R; ++i) acc[i][mi] += W.d[i][k] * (dot32_q4_raw(W.w[i][k], xp) - bs);
+      } else {
+        const float4 xv = reinterpret_cast<const float4*>(xs + mi * kp)[u];
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          const uint4 w = W.w[i][k];
+          acc[i][mi] += __uint_as_float(w.x) * xv.x + __uint_as_float(w.y) * xv.y + __uint_as_float(w.z) * xv.z +
+                        __uint_as_float(w.w) * xv.w;
+        }
+      }
+    }
+  }
+}
+
+// R rows per wave, U 16-byte units per lane in flight per row, M input rows.
+// The first group's weights are requested before the input rows are staged, so
+// the prologue (x load, RMSNorm, LDS) overlaps the first weight fetch.
+template <int QT, int M, int MODE, int R, int U>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   extern __shared__ float4 smem4[];
   float* xs = reinterpret_cast<float*>(smem4);
   const int kp = a.nblk * 32;
   float* xsum = xs + M * kp;  // Q4_0 only: [M][nblk] block sums of x
+  constexpr bool kPair = MODE == kModePairSilu || MODE == kModePairGelu;
+  const int lane = threadIdx.x & 63;
+  const int gwave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nwaves = gridDim.x * 4;
+  const int nunits = QT == kQ8_0 ? 2 * a.nblk : (QT == kQ4_0 ? a.nblk : kp / 4);
+  const int ngroups = kPair ? a.rows / R : (a.rows + R - 1) / R;
+
+  WRegs<QT, R, U> W;
+  int r[R];
+  if (gwave < ngroups) {
+    group_rows<R, kPair>(gwave, a.rows, r);
+    gemv_load<QT, R, U>(a, r, 0, lane, nunits, W);
+  }
+
   gemv_stage_x<M>(a, xs, kp);
   __syncthreads();
   if constexpr (QT == kQ4_0) {
@@ -156,93 +256,40 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
     __syncthreads();
   }
 
-  constexpr bool kPair = MODE == kModePairSilu || MODE == kModePairGelu;
-  const int lane = threadIdx.x & 63;
-  const int gwave = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int nwaves = gridDim.x * 4;
-  const int ngroups = kPair ? a.rows / 2 : (a.rows + 1) / 2;
-
+  bool first = true;
   for (int grp = gwave; grp < ngroups; grp += nwaves) {
-    int r0, r1;
-    if constexpr (kPair) {
-      r0 = pair_gate_row(grp);
-      r1 = r0 + 32;
-    } else {
-      r0 = 2 * grp;
-      r1 = min(2 * grp + 1, a.rows - 1);
+    if (!first) group_rows<R, kPair>(grp, a.rows, r);
+    float acc[R][M];
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int mi = 0; mi < M; ++mi) acc[i][mi] = 0.f;
+    for (int base = 0; base < nunits; base += 64 * U) {
+      if (!first) gemv_load<QT, R, U>(a, r, base, lane, nunits, W);
+      first = false;
+      gemv_compute<QT, R, U, M>(xs, xsum, kp, a.nblk, base, lane, nunits, W, acc);
     }
-    float acc0[M], acc1[M];
-#pragma unroll
-    for (int mi = 0; mi < M; ++mi) acc0[mi] = acc1[mi] = 0.f;
-
-    if constexpr (QT == kQ8_0) {
-      const int nunits = 2 * a.nblk;
-      const int8_t* q0 = reinterpret_cast<const int8_t*>(a.qs) + (size_t)r0 * kp;
-      const int8_t* q1 = reinterpret_cast<const int8_t*>(a.qs) + (size_t)r1 * kp;
-      const uint16_t* d0p = a.d + (size_t)r0 * a.nblk;
-      const uint16_t* d1p = a.d + (size_t)r1 * a.nblk;
-      for (int u = lane; u < nunits; u += 64) {
-        uint4 w0 = *reinterpret_cast<const uint4*>(q0 + 16 * u);
-        uint4 w1 = *reinterpret_cast<const uint4*>(q1 + 16 * u);
-        float d0 = load_half(d0p + (u >> 1));
-        float d1 = load_half(d1p + (u >> 1));
-#pragma unroll
-        for (int mi = 0; mi < M; ++mi) {
-          const float4* xv = reinterpret_cast<const float4*>(xs + mi * kp + 16 * u);
-          float4 xa = xv[0], xb = xv[1], xc = xv[2], xd = xv[3];
-          acc0[mi] += d0 * dot16_q8(w0, xa, xb, xc, xd);
-          acc1[mi] += d1 * dot16_q8(w1, xa, xb, xc, xd);
-        }
-      }
-    } else if constexpr (QT == kQ4_0) {
-      const uint4* q0 = reinterpret_cast<const uint4*>(a.qs) + (size_t)r0 * a.nblk;
-      const uint4* q1 = reinterpret_cast<const uint4*>(a.qs) + (size_t)r1 * a.nblk;
-      const uint16_t* d0p = a.d + (size_t)r0 * a.nblk;
-      const uint16_t* d1p = a.d + (size_t)r1 * a.nblk;
-      for (int u = lane; u < a.nblk; u += 64) {
-        uint4 w0 = q0[u];
-        uint4 w1 = q1[u];
-        float d0 = load_half(d0p + u);
-        float d1 = load_half(d1p + u);
-#pragma unroll
-        for (int mi = 0; mi < M; ++mi) {
-          const float* xp = xs + mi * kp + 32 * u;
-          float bs = 8.0f * xsum[mi * a.nblk + u];
-          acc0[mi] += d0 * (dot32_q4_raw(w0, xp) - bs);
-          acc1[mi] += d1 * (dot32_q4_raw(w1, xp) - bs);
-        }
-      }
-    } else {  // F32 rows
-      const int nunits = kp / 4;
-      const float4* w0p = reinterpret_cast<const float4*>(a.qs) + (size_t)r0 * (kp / 4);
-      const float4* w1p = reinterpret_cast<const float4*>(a.qs) + (size_t)r1 * (kp / 4);
-      for (int u = lane; u < nunits; u += 64) {
-        float4 w0 = w0p[u], w1 = w1p[u];
-#pragma unroll
-        for (int mi = 0; mi < M; ++mi) {
-          float4 xv = reinterpret_cast<const float4*>(xs + mi * kp)[u];
-          acc0[mi] += w0.x * xv.x + w0.y * xv.y + w0.z * xv.z + w0.w * xv.w;
-          acc1[mi] += w1.x * xv.x + w1.y * xv.y + w1.z * xv.z + w1.w * xv.w;
-        }
-      }
-    }
-
 #pragma unroll
     for (int mi = 0; mi < M; ++mi) {
-      float s0 = wave_sum(acc0[mi]);
-      float s1 = wave_sum(acc1[mi]);
+      float s[R];
+#pragma unroll
+      for (int i = 0; i < R; ++i) s[i] = wave_sum(acc[i][mi]);
       if (lane == 0 && mi < a.m) {
-        float* yr = a.y + (size_t)mi * a.ldy;
-        if constexpr (MODE == kModeStore) {
-          yr[r0] = s0;
-          if (2 * grp + 1 < a.rows) yr[r1] = s1;
-        } else if constexpr (MODE == kModeAdd) {
-          yr[r0] += s0;
-          if (2 * grp + 1 < a.rows) yr[r1] += s1;
-        } else if constexpr (MODE == kModePairSilu) {
-          yr[grp] = act_silu(s0) * s1;
-        } else {
-          yr[grp] = act_gelu_tanh(s0) * s1;
+        float* yr = (a.y_ind ? *a.y_ind + a.y_off : a.y) + (size_t)mi * a.ldy;
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          if constexpr (kPair) {
+            if (i & 1) {
+              const int n = grp * (R / 2) + i / 2;
+              yr[n] = (MODE == kModePairSilu ? act_silu(s[i - 1]) : act_gelu_tanh(s[i - 1])) * s[i];
+            }
+          } else {
+            const int row = grp * R + i;
+            if (row < a.rows) {
+              if constexpr (MODE == kModeAdd) yr[row] += s[i];
+              else yr[row] = s[i];
+            }
+          }
         }
       }
     }

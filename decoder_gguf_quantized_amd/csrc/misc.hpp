@@ -89,8 +89,9 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(NormArgs a) {
 // Qwen3 walkthrough, Steps 4-5: per-head RMSNorm of q and k (Qwen3), then the
 // half-split rotation of pairs (d, d + hd/2) by angle = f32(pos) * inv_freq[d]
 // (a single f32 product), then k and v are appended to the cache.  Synsema's
-// qwen3 file orders the norm before the rotation.  cos/sin are the accurate
-// library functions (angles reach thousands of radians).
+// qwen3 file orders the norm before the rotation.  cos/sin come from a table
+// built at load time: the double-precision cos/sin of that f32 angle, rounded
+// once to f32 (angles reach thousands of radians).
 struct RopeArgs {
   const float* qkv;     // [n][(nq + 2 nkv) hd]
   int ldqkv;
@@ -101,7 +102,7 @@ struct RopeArgs {
   const float* q_norm;  // [hd] or null
   const float* k_norm;
   float eps;
-  const float* inv_freq;  // [hd/2]
+  const float2* rope;   // [ctx][hd/2] (cos, sin) of f32(pos) * inv_freq[i]
   int seq0, pos0;       // prefill: token t -> (seq0, pos0 + t)
   const int* dpos;      // decode (non-null): token t -> (seq t, dpos[t])
 };
@@ -112,7 +113,7 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(RopeArgs a) {
   const int pos = a.dpos ? a.dpos[t] : a.pos0 + t;
   const int half = a.hd / 2;
   const int nheads = a.nq + 2 * a.nkv;
-  const float fpos = (float)pos;
+  const float2* rt = a.rope + (size_t)pos * half;
   for (int hh = wave; hh < nheads; hh += 4) {
     const float* src = a.qkv + (size_t)t * a.ldqkv + (size_t)hh * a.hd;
     const bool is_q = hh < a.nq, is_k = !is_q && hh < a.nq + a.nkv;
@@ -152,10 +153,9 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(RopeArgs a) {
       if (i >= half) continue;
       float y1 = x1[r], y2 = x2[r];
       if (is_q || is_k) {
-        float ang = fpos * a.inv_freq[i];
-        float c = cosf(ang), s = sinf(ang);
-        y1 = x1[r] * c - x2[r] * s;
-        y2 = x1[r] * s + x2[r] * c;
+        const float2 cs = rt[i];
+        y1 = x1[r] * cs.x - x2[r] * cs.y;
+        y2 = x1[r] * cs.y + x2[r] * cs.x;
       }
       dst[i] = y1;
       dst[i + half] = y2;
@@ -170,6 +170,16 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(RopeArgs a) {
 // word v % 4.  Stage 1: one workgroup per (4096-entry vocab chunk, row).
 constexpr int kSampleChunk = 4096;
 
+// Per-step values that a replayed decode graph reads from device memory.
+struct StepParams {
+  float temperature;
+  int n;
+  uint64_t seed;
+  uint64_t step;
+  float* logits;   // caller's logits buffer for this step
+  int* tok_out;    // caller's token buffer for this step
+};
+
 struct SampleArgs {
   const float* logits;
   int ld, vocab, rows;
@@ -180,7 +190,18 @@ struct SampleArgs {
   int nchunk;
   int* out;        // [rows]
   int* out2;       // optional second copy
+  const StepParams* sp;  // if non-null: logits, out, temperature, seed, step come from here
 };
+
+QD_DEV void sample_resolve(SampleArgs& a) {
+  if (a.sp) {
+    a.logits = a.sp->logits;
+    a.out = a.sp->tok_out;
+    a.temperature = a.sp->temperature;
+    a.seed = a.sp->seed;
+    a.step = a.sp->step;
+  }
+}
 
 QD_DEV void argmax_pair_wave(float& v, int& i) {
   for (int o = 32; o > 0; o >>= 1) {
@@ -194,6 +215,7 @@ QD_DEV void argmax_pair_wave(float& v, int& i) {
 }
 
 __global__ __launch_bounds__(256) void sample_stage1_kernel(SampleArgs a) {
+  sample_resolve(a);
   __shared__ float sv[4];
   __shared__ int si[4];
   const int c = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
@@ -249,6 +271,7 @@ __global__ __launch_bounds__(256) void sample_stage1_kernel(SampleArgs a) {
 }
 
 __global__ __launch_bounds__(64) void sample_stage2_kernel(SampleArgs a) {
+  sample_resolve(a);
   const int row = blockIdx.x, lane = threadIdx.x;
   float best = -INFINITY;
   int bi = 0x7fffffff;
@@ -298,10 +321,13 @@ struct StepArgs {
   int* d_pos;
   int* d_tok;
   int* err;
+  StepParams params;
+  StepParams* d_params;
 };
 
 __global__ __launch_bounds__(64) void step_begin_kernel(StepArgs a) {
   const int i = threadIdx.x;
+  if (i == 0) *a.d_params = a.params;
   if (i >= a.n) return;
   a.d_pos[i] = a.pos[i];
   int t = a.dev_tok ? a.dev_tok[i] : a.host_tok[i];

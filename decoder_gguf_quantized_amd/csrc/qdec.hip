@@ -97,8 +97,8 @@ struct qdec_model {
   Mat embd, out_w;
   bool tied = true;
   float* output_norm = nullptr;
-  float* inv_freq_g = nullptr;
-  float* inv_freq_l = nullptr;
+  float2* rope_g = nullptr;  // [max_ctx][hd/2] (cos, sin), full-attention layers
+  float2* rope_l = nullptr;  // same for sliding-window layers
   float* kc = nullptr;
   float* vc = nullptr;
   size_t kv_layer = 0;  // floats per layer of one cache
@@ -112,6 +112,9 @@ struct qdec_model {
   int nvchunk = 0;
   int* d_pos = nullptr;
   int* d_tok = nullptr;
+  StepParams* d_params = nullptr;   // per-step values read by replayed graphs
+  hipStream_t cap_stream = nullptr; // capture stream for the decode graphs
+  std::unordered_map<int, hipGraphExec_t> graphs;  // decode graph per batch size
   int* d_prompt = nullptr;
   int* err_host = nullptr;
   int* err_dev = nullptr;
@@ -163,33 +166,44 @@ struct Timed {
 const char* gemv_class(int type) { return type == kQ4_0 ? "gemv_q4_0" : type == kQ8_0 ? "gemv_q8_0" : "gemv_f32"; }
 const char* gemm_class(int type) { return type == kQ4_0 ? "gemm_q4_0" : type == kQ8_0 ? "gemm_q8_0" : "gemm_f32"; }
 
-template <int QT, int M>
+template <int QT, int M, int R, int U>
 void gemv_dispatch_mode(int mode, dim3 grid, size_t lds, hipStream_t st, const GemvArgs& a) {
   switch (mode) {
-    case kModeStore: gemv_kernel<QT, M, kModeStore><<<grid, 256, lds, st>>>(a); break;
-    case kModeAdd: gemv_kernel<QT, M, kModeAdd><<<grid, 256, lds, st>>>(a); break;
-    case kModePairSilu: gemv_kernel<QT, M, kModePairSilu><<<grid, 256, lds, st>>>(a); break;
-    default: gemv_kernel<QT, M, kModePairGelu><<<grid, 256, lds, st>>>(a); break;
+    case kModeStore: gemv_kernel<QT, M, kModeStore, R, U><<<grid, 256, lds, st>>>(a); break;
+    case kModeAdd: gemv_kernel<QT, M, kModeAdd, R, U><<<grid, 256, lds, st>>>(a); break;
+    case kModePairSilu: gemv_kernel<QT, M, kModePairSilu, R, U><<<grid, 256, lds, st>>>(a); break;
+    default: gemv_kernel<QT, M, kModePairGelu, R, U><<<grid, 256, lds, st>>>(a); break;
+  }
+}
+
+// (R rows per wave, U units per lane per row): R = 4, U = 1 for rows of at most
+// 64 units (one unit per lane); R = 2 with U = 2 or 4 for longer rows.
+template <int QT, int M>
+void gemv_dispatch_ru(int ru, int mode, dim3 grid, size_t lds, hipStream_t st, const GemvArgs& a) {
+  switch (ru) {
+    case 0: gemv_dispatch_mode<QT, M, 4, 1>(mode, grid, lds, st, a); break;
+    case 1: gemv_dispatch_mode<QT, M, 2, 2>(mode, grid, lds, st, a); break;
+    default: gemv_dispatch_mode<QT, M, 2, 4>(mode, grid, lds, st, a); break;
   }
 }
 
 template <int QT>
-void gemv_dispatch_m(int M, int mode, dim3 grid, size_t lds, hipStream_t st, const GemvArgs& a) {
+void gemv_dispatch_m(int M, int ru, int mode, dim3 grid, size_t lds, hipStream_t st, const GemvArgs& a) {
   switch (M) {
-    case 1: gemv_dispatch_mode<QT, 1>(mode, grid, lds, st, a); break;
-    case 2: gemv_dispatch_mode<QT, 2>(mode, grid, lds, st, a); break;
-    case 4: gemv_dispatch_mode<QT, 4>(mode, grid, lds, st, a); break;
-    case 8: gemv_dispatch_mode<QT, 8>(mode, grid, lds, st, a); break;
-    default: gemv_dispatch_mode<QT, 16>(mode, grid, lds, st, a); break;
+    case 1: gemv_dispatch_ru<QT, 1>(ru, mode, grid, lds, st, a); break;
+    case 2: gemv_dispatch_ru<QT, 2>(ru, mode, grid, lds, st, a); break;
+    case 4: gemv_dispatch_ru<QT, 4>(ru, mode, grid, lds, st, a); break;
+    case 8: gemv_dispatch_ru<QT, 8>(ru, mode, grid, lds, st, a); break;
+    default: gemv_dispatch_ru<QT, 16>(ru, mode, grid, lds, st, a); break;
   }
 }
 
 constexpr size_t kGemvLdsMax = 64 * 1024;
 
 // y[r][*] (op)= W x[r] for rows r < nrows, in launches of up to 16 rows that fit
-// the LDS budget.
+// the LDS budget.  y_ind: read the output base from device memory instead.
 void gemv(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, const float* norm_w, float eps,
-          float* y, int ldy, int nrows, int mode) {
+          float* y, int ldy, int nrows, int mode, float* const* y_ind = nullptr) {
   const int kp = w.nblk * 32;
   const size_t per_row = (size_t)kp * 4 + (w.type == kQ4_0 ? (size_t)w.nblk * 4 : 0);
   // rows per launch: a power of two (the kernel's M) whose staged inputs fit the LDS budget
@@ -197,19 +211,23 @@ void gemv(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, 
   while (cap > 1 && per_row * cap > kGemvLdsMax) cap /= 2;
   if (per_row > kGemvLdsMax) throw HipError{"gemv: input row too long for LDS"};
   const bool pair = mode == kModePairSilu || mode == kModePairGelu;
-  const int ngroups = pair ? w.rows / 2 : (w.rows + 1) / 2;
-  dim3 grid(std::min((ngroups + 3) / 4, 2048));
+  const int nunits = w.type == kQ8_0 ? 2 * w.nblk : (w.type == kQ4_0 ? w.nblk : kp / 4);
+  const int ru = nunits <= 64 ? 0 : (nunits <= 128 ? 1 : 2);
+  const int R = ru == 0 ? 4 : 2;
+  const int ngroups = pair ? w.rows / R : (w.rows + R - 1) / R;
+  dim3 grid(std::max(1, std::min((ngroups + 3) / 4, 2048)));
   for (int r0 = 0; r0 < nrows; r0 += cap) {
     const int mr = std::min(cap, nrows - r0);
     int M = 1;
     while (M < mr) M *= 2;
-    GemvArgs a{w.qs, w.d, w.rows, w.nblk, x + (size_t)r0 * ldx, ldx, norm_w, eps, y + (size_t)r0 * ldy, ldy, mr};
+    GemvArgs a{w.qs, w.d, w.rows, w.nblk, x + (size_t)r0 * ldx, ldx, norm_w, eps,
+               y ? y + (size_t)r0 * ldy : nullptr, ldy, mr, y_ind, (long)r0 * ldy};
     const size_t lds = per_row * M;
     const double bytes = w.gguf_bytes + (double)mr * kp * 4 + (double)mr * (pair ? w.rows / 2 : w.rows) * 4;
     Timed tm(m, st, gemv_class(w.type), bytes, 2.0 * mr * w.rows * (double)w.cols);
-    if (w.type == kQ8_0) gemv_dispatch_m<kQ8_0>(M, mode, grid, lds, st, a);
-    else if (w.type == kQ4_0) gemv_dispatch_m<kQ4_0>(M, mode, grid, lds, st, a);
-    else gemv_dispatch_m<kF32>(M, mode, grid, lds, st, a);
+    if (w.type == kQ8_0) gemv_dispatch_m<kQ8_0>(M, ru, mode, grid, lds, st, a);
+    else if (w.type == kQ4_0) gemv_dispatch_m<kQ4_0>(M, ru, mode, grid, lds, st, a);
+    else gemv_dispatch_m<kF32>(M, ru, mode, grid, lds, st, a);
   }
 }
 
@@ -261,10 +279,12 @@ int layer_window(const qdec_model* m, int l) { return m->layers[l].global ? 0 : 
 
 void attention_decode(qdec_model* m, hipStream_t st, int l, int B) {
   const qdec_config& c = m->cfg;
+  const Layer& L = m->layers[l];
   const int hd = c.head_dim, G = c.n_head / c.n_head_kv;
   const float scale_log2 = (float)(1.0 / std::sqrt((double)hd) * 1.4426950408889634);
-  AttnDecodeArgs a{m->q, m->kc + l * m->kv_layer, m->vc + l * m->kv_layer, m->max_ctx, m->d_pos, c.n_head,
-                   c.n_head_kv, layer_window(m, l), m->chunk, scale_log2, m->part_o, m->part_ml, m->nchunk};
+  AttnDecodeArgs a{m->qkv, m->nqkv, m->kc + l * m->kv_layer, m->vc + l * m->kv_layer, m->max_ctx, m->d_pos,
+                   c.n_head, c.n_head_kv, layer_window(m, l), m->chunk, m->nchunk, L.q_norm, L.k_norm, c.rms_eps,
+                   L.global ? m->rope_g : m->rope_l, scale_log2, m->part_o, m->part_ml};
   double kvbytes = 0;
   for (int s = 0; s < B; ++s) {
     int p = m->kvlen[s];
@@ -272,15 +292,18 @@ void attention_decode(qdec_model* m, hipStream_t st, int l, int B) {
     kvbytes += (double)(p - lo + 1) * c.n_head_kv * hd * 8;
   }
   {
-    Timed tm(m, st, "attn_decode", kvbytes + (double)B * c.n_head * hd * 4, 4.0 * kvbytes / 8 * G);
+    Timed tm(m, st, "attn_decode", kvbytes + (double)B * m->nqkv * 4, 4.0 * kvbytes / 8 * G);
     dim3 grid(m->nchunk, c.n_head_kv, B);
     if (hd == 64) attn_decode_hd<64>(G, grid, st, a);
     else if (hd == 128) attn_decode_hd<128>(G, grid, st, a);
     else attn_decode_hd<256>(G, grid, st, a);
   }
-  AttnCombineArgs cb{m->part_o, m->part_ml, m->d_pos, c.n_head, hd, a.window, m->chunk, m->nchunk, m->a};
+  AttnCombineArgs cb{m->part_o, m->part_ml, m->d_pos, c.n_head, a.window, m->chunk, m->nchunk, m->a};
   Timed tm(m, st, "attn_combine", (double)B * c.n_head * hd * 4 * 2, 0);
-  attn_combine_kernel<<<dim3(c.n_head, B), hd, 0, st>>>(cb);
+  dim3 cgrid(c.n_head, B);
+  if (hd == 64) attn_combine_kernel<64><<<cgrid, 64, 0, st>>>(cb);
+  else if (hd == 128) attn_combine_kernel<128><<<cgrid, 64, 0, st>>>(cb);
+  else attn_combine_kernel<256><<<cgrid, 64, 0, st>>>(cb);
 }
 
 void attention_prefill(qdec_model* m, hipStream_t st, int l, int seq, int T, int pos0) {
@@ -308,7 +331,7 @@ void rope_kv(qdec_model* m, hipStream_t st, int l, int n, int seq0, int pos0, co
   const qdec_config& c = m->cfg;
   const Layer& L = m->layers[l];
   RopeArgs a{m->qkv, m->nqkv, m->q, m->kc + l * m->kv_layer, m->vc + l * m->kv_layer, m->max_ctx, c.n_head,
-             c.n_head_kv, c.head_dim, L.q_norm, L.k_norm, c.rms_eps, L.global ? m->inv_freq_g : m->inv_freq_l,
+             c.n_head_kv, c.head_dim, L.q_norm, L.k_norm, c.rms_eps, L.global ? m->rope_g : m->rope_l,
              seq0, pos0, dpos};
   Timed tm(m, st, "rope_kv", (double)n * m->nqkv * 8, 0);
   rope_kv_kernel<<<n, 256, 0, st>>>(a);
@@ -323,9 +346,9 @@ void embed(qdec_model* m, hipStream_t st, const int* d_tokens, int n, float* out
 }
 
 void sample(qdec_model* m, hipStream_t st, const float* logits, int ld, int rows, float temp, uint64_t seed,
-            uint64_t step, int* out, int* out2) {
+            uint64_t step, int* out, int* out2, const StepParams* sp = nullptr) {
   const int V = m->cfg.vocab;
-  SampleArgs a{logits, ld, V, rows, temp, seed, step, m->s_v, m->s_i, m->nvchunk, out, out2};
+  SampleArgs a{logits, ld, V, rows, temp, seed, step, m->s_v, m->s_i, m->nvchunk, out, out2, sp};
   {
     Timed tm(m, st, "sample", (double)rows * V * 4, 0);
     sample_stage1_kernel<<<dim3(m->nvchunk, rows), 256, 0, st>>>(a);
@@ -350,9 +373,12 @@ void blocks(qdec_model* m, hipStream_t st, int n, int seq, int pos0, const int* 
       rmsnorm_rows(m, st, m->x, H, L.attn_norm, H, m->h, H, n, 0);
       gemm(m, st, L.qkv, m->h, H, n, m->qkv, m->nqkv, kModeStore);
     }
-    rope_kv(m, st, l, n, seq, pos0, dpos);
-    if (dec) attention_decode(m, st, l, n);
-    else attention_prefill(m, st, l, seq, n, pos0);
+    if (dec) {
+      attention_decode(m, st, l, n);  // QK-norm, RoPE and the KV append run inside
+    } else {
+      rope_kv(m, st, l, n, seq, pos0, nullptr);
+      attention_prefill(m, st, l, seq, n, pos0);
+    }
     if (c.sandwich_norm) {
       if (dec) gemv(m, st, L.o, m->a, m->qd, nullptr, 0.f, m->y, H, n, kModeStore);
       else gemm(m, st, L.o, m->a, m->qd, n, m->y, H, kModeStore);
@@ -377,6 +403,17 @@ void blocks(qdec_model* m, hipStream_t st, int n, int seq, int pos0, const int* 
       else gemm(m, st, L.down, m->m, m->Fp, n, m->x, H, kModeAdd);
     }
   }
+}
+
+// One decode step for sequences 0..n-1 reading tokens, positions and the
+// step's parameters from device memory (so it can be captured and replayed).
+void decode_body(qdec_model* m, hipStream_t st, int n) {
+  const qdec_config& c = m->cfg;
+  embed(m, st, m->d_tok, n, m->x);
+  blocks(m, st, n, 0, 0, m->d_pos);
+  gemv(m, st, m->lm(), m->x, c.hidden, m->output_norm, c.rms_eps, nullptr, c.vocab, n, kModeStore,
+       &m->d_params->logits);
+  sample(m, st, nullptr, c.vocab, n, 0.f, 0, 0, nullptr, nullptr, m->d_params);
 }
 
 // ------------------------------------------------------------ error handling
@@ -518,6 +555,10 @@ float* upload_vec(qdec_model* m, const qdec_tensor& t, hipStream_t st) {
 }
 
 void free_model(qdec_model* m) {
+  for (auto& g : m->graphs)
+    if (g.second) (void)hipGraphExecDestroy(g.second);
+  m->graphs.clear();
+  if (m->cap_stream) (void)hipStreamDestroy(m->cap_stream);
   for (void* p : m->allocs) (void)hipFree(p);
   m->allocs.clear();
   for (auto& r : m->krecs) {
@@ -693,17 +734,26 @@ int load(const qdec_config* cfgp, const qdec_tensor* ts, int32_t n, int32_t max_
         m->names[td.name] = NameRef{&L.down, 0, (int)td.rows, (int)td.cols, 0, nullptr};
       }
     }
-    {  // RoPE inverse frequencies: 1 / theta^(i / half) in double, rounded once to f32
+    {  // RoPE tables.  inv_freq[i] = 1 / theta^(i / half) in double, rounded once
+       // to f32; angle = f32(pos) * inv_freq[i] as one f32 product; cos and sin
+       // of that f32 angle in double, rounded once to f32.
       const int half = c.head_dim / 2;
-      std::vector<float> fg(half), fl(half);
-      for (int i = 0; i < half; ++i) {
-        fg[i] = (float)(1.0 / std::pow((double)c.rope_theta, (double)i / half));
-        fl[i] = (float)(1.0 / std::pow((double)(c.window > 0 ? c.rope_theta_local : c.rope_theta), (double)i / half));
-      }
-      m->inv_freq_g = m->dalloc<float>(half);
-      m->inv_freq_l = m->dalloc<float>(half);
-      hipck(hipMemcpy(m->inv_freq_g, fg.data(), half * 4, hipMemcpyHostToDevice), "upload");
-      hipck(hipMemcpy(m->inv_freq_l, fl.data(), half * 4, hipMemcpyHostToDevice), "upload");
+      auto table = [&](double theta) {
+        std::vector<float> inv(half);
+        for (int i = 0; i < half; ++i) inv[i] = (float)(1.0 / std::pow(theta, (double)i / half));
+        std::vector<float> t((size_t)max_ctx * half * 2);
+        for (int p = 0; p < max_ctx; ++p)
+          for (int i = 0; i < half; ++i) {
+            const volatile float ang = (float)p * inv[i];
+            t[((size_t)p * half + i) * 2] = (float)std::cos((double)ang);
+            t[((size_t)p * half + i) * 2 + 1] = (float)std::sin((double)ang);
+          }
+        float2* d = m->dalloc<float2>((size_t)max_ctx * half);
+        hipck(hipMemcpy(d, t.data(), t.size() * 4, hipMemcpyHostToDevice), "upload");
+        return d;
+      };
+      m->rope_g = table(c.rope_theta);
+      m->rope_l = c.window > 0 && c.rope_theta_local != c.rope_theta ? table(c.rope_theta_local) : m->rope_g;
     }
     // KV cache [L][B][nkv][ctx][hd] f32
     m->kv_layer = (size_t)max_seqs * c.n_head_kv * max_ctx * c.head_dim;
@@ -734,6 +784,8 @@ int load(const qdec_config* cfgp, const qdec_tensor* ts, int32_t n, int32_t max_
     m->s_i = m->dalloc<int>((size_t)max_seqs * m->nvchunk);
     m->d_pos = m->dalloc<int>(64);
     m->d_tok = m->dalloc<int>(64);
+    m->d_params = m->dalloc<StepParams>(1);
+    hipck(hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking), "hipStreamCreate");
     m->d_prompt = m->dalloc<int>(T);
     hipck(hipHostMalloc((void**)&m->err_host, sizeof(int), hipHostMallocMapped), "hipHostMalloc");
     *m->err_host = 0;
@@ -854,14 +906,33 @@ int qdec_decode_step(qdec_model* m, const int32_t* tokens, int32_t n_seqs, float
     sa.d_pos = m->d_pos;
     sa.d_tok = m->d_tok;
     sa.err = m->err_dev;
+    sa.params = StepParams{temperature, n_seqs, seed, step, d_logits, d_token_out};
+    sa.d_params = m->d_params;
     {
       Timed tm(m, st, "step_begin", 0, 0);
       step_begin_kernel<<<1, 64, 0, st>>>(sa);
     }
-    embed(m, st, m->d_tok, n_seqs, m->x);
-    blocks(m, st, n_seqs, 0, 0, m->d_pos);
-    gemv(m, st, m->lm(), m->x, c.hidden, m->output_norm, c.rms_eps, d_logits, c.vocab, n_seqs, kModeStore);
-    sample(m, st, d_logits, c.vocab, n_seqs, temperature, seed, step, d_token_out, nullptr);
+    if (m->timing) {
+      decode_body(m, st, n_seqs);
+    } else {
+      hipGraphExec_t& ge = m->graphs[n_seqs];
+      if (!ge) {
+        hipGraph_t graph = nullptr;
+        hipck(hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeThreadLocal), "hipStreamBeginCapture");
+        try {
+          decode_body(m, m->cap_stream, n_seqs);
+        } catch (...) {
+          (void)hipStreamEndCapture(m->cap_stream, &graph);
+          if (graph) (void)hipGraphDestroy(graph);
+          throw;
+        }
+        hipck(hipStreamEndCapture(m->cap_stream, &graph), "hipStreamEndCapture");
+        hipError_t e = hipGraphInstantiate(&ge, graph, nullptr, nullptr, 0);
+        (void)hipGraphDestroy(graph);
+        hipck(e, "hipGraphInstantiate");
+      }
+      hipck(hipGraphLaunch(ge, st), "hipGraphLaunch");
+    }
     for (int s = 0; s < n_seqs; ++s) m->kvlen[s] += 1;
   } catch (const HipError& e) {
     return fail_internal(m, st, e.msg);
@@ -968,7 +1039,7 @@ int qdec_debug_sample(const float* d_logits, int32_t rows, int32_t vocab, float 
     set_err("internal: hipMalloc failed");
     return QDEC_INTERNAL;
   }
-  SampleArgs a{d_logits, vocab, vocab, rows, temperature, seed, step, pv, pi, nch, d_out, nullptr};
+  SampleArgs a{d_logits, vocab, vocab, rows, temperature, seed, step, pv, pi, nch, d_out, nullptr, nullptr};
   sample_stage1_kernel<<<dim3(nch, rows), 256, 0, st>>>(a);
   sample_stage2_kernel<<<rows, 64, 0, st>>>(a);
   hipError_t e = hipStreamSynchronize(st);
