@@ -91,6 +91,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="c2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=None, help="override the workload's decode steps (profiling runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 256 MiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path has no multi-GPU mode",
@@ -113,6 +116,8 @@ def main():
     tensors = synth.generate(cfg)
     t_gen = time.perf_counter() - t_gen
     dev = torch.device("cuda:0")
+    if args.decode_steps is not None:
+        cfg["decode_steps"] = args.decode_steps
     T, N, V = cfg["prompt_len"], cfg["decode_steps"], cfg["vocab"]
     prompt = synth.prompt(cfg)
     model = qdec.Model(cfg, tensors, max_seqs=1, max_ctx=T + N + 1)
@@ -142,6 +147,12 @@ def main():
         dec = [e[1].elapsed_time(e[2]) for e in evs]
         return wall, pre, dec
 
+    if args.copy_calibration:
+        a = torch.empty(64 << 20, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
     for _ in range(args.warmup):
         run(1)
     wall, pre_ms, dec_ms = run(args.steps)

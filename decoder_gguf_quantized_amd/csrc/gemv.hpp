@@ -76,35 +76,21 @@ QD_DEV float dot16_q8(uint4 w, const float4& a, const float4& b, const float4& c
   return s;
 }
 
-// One Q4_0 block: returns sum_j n_j * x_j (n = raw nibble, no offset) where the
-// low nibbles of the 16 payload bytes are elements 0..15 and the high nibbles
-// elements 16..31.  High nibbles are converted in place (value 16 n) and scaled
-// by 1/16 at the end (exact).
-QD_DEV float dot32_q4_raw(uint4 w, const float* x) {
-  const float4* xv = reinterpret_cast<const float4*>(x);
-  float lo = 0.f, hi = 0.f;
-  uint32_t words[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t l = opaque_and(words[i], 0x0F0F0F0Fu);
-    uint32_t h = opaque_and(words[i], 0xF0F0F0F0u);
-    float4 xl = xv[i], xh = xv[4 + i];
-    lo += (float)(l & 0xffu) * xl.x;
-    lo += (float)((l >> 8) & 0xffu) * xl.y;
-    lo += (float)((l >> 16) & 0xffu) * xl.z;
-    lo += (float)(l >> 24) * xl.w;
-    hi += (float)(h & 0xffu) * xh.x;
-    hi += (float)((h >> 8) & 0xffu) * xh.y;
-    hi += (float)((h >> 16) & 0xffu) * xh.z;
-    hi += (float)(h >> 24) * xh.w;
-  }
-  return lo + 0.0625f * hi;
-}
+// Activations per lane unit: Q8_0 16, Q4_0 32, F32 4.
+template <int QT>
+constexpr int unit_floats() { return QT == kQ8_0 ? 16 : (QT == kQ4_0 ? 32 : 4); }
 
 // Load the input rows into LDS, optionally RMSNorm-ed with gain norm_w:
-// xs[mi][k] = x[mi][k] * rsqrt(mean_k x^2 + eps) * w[k].  Rows mi >= a.m are zero.
-template <int M>
-QD_DEV void gemv_stage_x(const GemvArgs& a, float* xs, int kp) {
+// x'[mi][k] = x[mi][k] * rsqrt(mean_k x^2 + eps) * w[k].  Rows mi >= a.m are zero.
+// Layout: unit-transposed float4s, xs4[(mi * NV + i) * NU + u] holds floats
+// 4i..4i+3 of unit u (NV float4 per unit, NU units per row).  A lane owns one
+// unit, so for each slot i consecutive lanes read consecutive float4s: no bank
+// conflicts (the natural layout puts every lane's unit 64 or 128 bytes apart,
+// which lands all lanes on a handful of banks).
+template <int QT, int M>
+QD_DEV void gemv_stage_x(const GemvArgs& a, float4* xs4, int kp) {
+  constexpr int US = unit_floats<QT>(), NV = US / 4;
+  const int NU = kp / US;
   __shared__ float red[4][M];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   float scale[M];
@@ -115,9 +101,9 @@ QD_DEV void gemv_stage_x(const GemvArgs& a, float* xs, int kp) {
     for (int mi = 0; mi < M; ++mi) {
       float ss = 0.f;
       if (mi < a.m)
-        for (int k = tid; k < kp; k += 256) {
-          float v = a.x[(size_t)mi * a.ldx + k];
-          ss += v * v;
+        for (int k = 4 * tid; k < kp; k += 1024) {
+          const float4 v = *reinterpret_cast<const float4*>(a.x + (size_t)mi * a.ldx + k);
+          ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
         }
       ss = wave_sum(ss);
       if (lane == 0) red[wave][mi] = ss;
@@ -131,13 +117,20 @@ QD_DEV void gemv_stage_x(const GemvArgs& a, float* xs, int kp) {
   }
 #pragma unroll
   for (int mi = 0; mi < M; ++mi) {
-    for (int k = tid; k < kp; k += 256) {
-      float v = 0.f;
+    for (int k = 4 * tid; k < kp; k += 1024) {
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
       if (mi < a.m) {
-        v = a.x[(size_t)mi * a.ldx + k];
-        if (a.norm_w) v = v * scale[mi] * a.norm_w[k];
+        v = *reinterpret_cast<const float4*>(a.x + (size_t)mi * a.ldx + k);
+        if (a.norm_w) {
+          const float4 w = *reinterpret_cast<const float4*>(a.norm_w + k);
+          v.x = v.x * scale[mi] * w.x;
+          v.y = v.y * scale[mi] * w.y;
+          v.z = v.z * scale[mi] * w.z;
+          v.w = v.w * scale[mi] * w.w;
+        }
       }
-      xs[mi * kp + k] = v;
+      const int u = k / US, i = (k % US) / 4;
+      xs4[(mi * NV + i) * NU + u] = v;
     }
   }
 }
@@ -188,32 +181,54 @@ QD_DEV void gemv_load(const GemvArgs& a, const int (&r)[R], int base, int lane, 
   }
 }
 
+// One Q4_0 block given its 32 activations as 8 float4 (elements 0..15 in
+// xv[0..3], 16..31 in xv[4..7]): sum_j n_j x_j with the raw nibbles n (no offset).
+QD_DEV float dot32_q4_raw4(uint4 w, const float4 (&xv)[8]) {
+  float lo = 0.f, hi = 0.f;
+  uint32_t words[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t l = opaque_and(words[i], 0x0F0F0F0Fu);
+    uint32_t h = opaque_and(words[i], 0xF0F0F0F0u);
+    const float4 xl = xv[i], xh = xv[4 + i];
+    lo += (float)(l & 0xffu) * xl.x;
+    lo += (float)((l >> 8) & 0xffu) * xl.y;
+    lo += (float)((l >> 16) & 0xffu) * xl.z;
+    lo += (float)(l >> 24) * xl.w;
+    hi += (float)(h & 0xffu) * xh.x;
+    hi += (float)((h >> 8) & 0xffu) * xh.y;
+    hi += (float)((h >> 16) & 0xffu) * xh.z;
+    hi += (float)(h >> 24) * xh.w;
+  }
+  return lo + 0.0625f * hi;
+}
+
 template <int QT, int R, int U, int M>
-QD_DEV void gemv_compute(const float* xs, const float* xsum, int kp, int nblk, int base, int lane, int nunits,
+QD_DEV void gemv_compute(const float4* xs4, const float* xsum, int kp, int nblk, int base, int lane, int nunits,
                          const WRegs<QT, R, U>& W, float (&acc)[R][M]) {
+  constexpr int NV = unit_floats<QT>() / 4;
 #pragma unroll
   for (int k = 0; k < U; ++k) {
     const int u = base + lane + 64 * k;
     if (u >= nunits) continue;
 #pragma unroll
     for (int mi = 0; mi < M; ++mi) {
-      if constexpr (QT == kQ8_0) {
-        const float4* xv = reinterpret_cast<const float4*>(xs + mi * kp + 16 * u);
-        float4 xa = xv[0], xb = xv[1], xc = xv[2], xd = xv[3];
+      float4 xv[NV];
 #pragma unroll
-        for (int i = 0; i < R; ++i) acc[i][mi] += W.d[i][k] * dot16_q8(W.w[i][k], xa, xb, xc, xd);
+      for (int i = 0; i < NV; ++i) xv[i] = xs4[(mi * NV + i) * nunits + u];
+      if constexpr (QT == kQ8_0) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) acc[i][mi] += W.d[i][k] * dot16_q8(W.w[i][k], xv[0], xv[1], xv[2], xv[3]);
       } else if constexpr (QT == kQ4_0) {
-        const float* xp = xs + mi * kp + 32 * u;
         const float bs = 8.0f * xsum[mi * nblk + u];
 #pragma unroll
-        for (int i = 0; i < R; ++i) acc[i][mi] += W.d[i][k] * (dot32_q4_raw(W.w[i][k], xp) - bs);
+        for (int i = 0; i < R; ++i) acc[i][mi] += W.d[i][k] * (dot32_q4_raw4(W.w[i][k], xv) - bs);
       } else {
-        const float4 xv = reinterpret_cast<const float4*>(xs + mi * kp)[u];
 #pragma unroll
         for (int i = 0; i < R; ++i) {
           const uint4 w = W.w[i][k];
-          acc[i][mi] += __uint_as_float(w.x) * xv.x + __uint_as_float(w.y) * xv.y + __uint_as_float(w.z) * xv.z +
-                        __uint_as_float(w.w) * xv.w;
+          acc[i][mi] += __uint_as_float(w.x) * xv[0].x + __uint_as_float(w.y) * xv[0].y +
+                        __uint_as_float(w.z) * xv[0].z + __uint_as_float(w.w) * xv[0].w;
         }
       }
     }
@@ -221,78 +236,104 @@ QD_DEV void gemv_compute(const float* xs, const float* xsum, int kp, int nblk, i
 }
 
 // R rows per wave, U 16-byte units per lane in flight per row, M input rows.
-// The first group's weights are requested before the input rows are staged, so
-// the prologue (x load, RMSNorm, LDS) overlaps the first weight fetch.
+// Each wave walks its (row group, unit block) tiles with a two-deep register
+// pipeline: the loads of tile t+1 are issued before tile t is computed, so the
+// memory pipe stays busy through the arithmetic, the lane reduction and the
+// store.  The first tile is requested before the input rows are staged.
 template <int QT, int M, int MODE, int R, int U>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
-  extern __shared__ float4 smem4[];
-  float* xs = reinterpret_cast<float*>(smem4);
+  extern __shared__ float4 xs4[];
   const int kp = a.nblk * 32;
-  float* xsum = xs + M * kp;  // Q4_0 only: [M][nblk] block sums of x
+  float* xsum = reinterpret_cast<float*>(xs4 + M * kp / 4);  // Q4_0 only: [M][nblk] block sums of x
   constexpr bool kPair = MODE == kModePairSilu || MODE == kModePairGelu;
   const int lane = threadIdx.x & 63;
   const int gwave = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nwaves = gridDim.x * 4;
   const int nunits = QT == kQ8_0 ? 2 * a.nblk : (QT == kQ4_0 ? a.nblk : kp / 4);
   const int ngroups = kPair ? a.rows / R : (a.rows + R - 1) / R;
+  const int tpg = (nunits + 64 * U - 1) / (64 * U);  // tiles per row group
 
-  WRegs<QT, R, U> W;
-  int r[R];
-  if (gwave < ngroups) {
-    group_rows<R, kPair>(gwave, a.rows, r);
-    gemv_load<QT, R, U>(a, r, 0, lane, nunits, W);
+  WRegs<QT, R, U> cur, nxt;
+  int r[R], rn[R];
+  int grp = gwave, tb = 0;
+  if (grp < ngroups) {
+    group_rows<R, kPair>(grp, a.rows, r);
+    gemv_load<QT, R, U>(a, r, 0, lane, nunits, cur);
   }
 
-  gemv_stage_x<M>(a, xs, kp);
+  gemv_stage_x<QT, M>(a, xs4, kp);
   __syncthreads();
   if constexpr (QT == kQ4_0) {
     for (int i = threadIdx.x; i < M * a.nblk; i += 256) {
-      const float* p = xs + (i / a.nblk) * kp + (i % a.nblk) * 32;
+      const int mi = i / a.nblk, u = i % a.nblk;
       float s = 0.f;
 #pragma unroll
-      for (int j = 0; j < 32; ++j) s += p[j];
+      for (int j = 0; j < 8; ++j) {
+        const float4 v = xs4[(mi * 8 + j) * a.nblk + u];
+        s += (v.x + v.y) + (v.z + v.w);
+      }
       xsum[i] = s;
     }
     __syncthreads();
   }
 
-  bool first = true;
-  for (int grp = gwave; grp < ngroups; grp += nwaves) {
-    if (!first) group_rows<R, kPair>(grp, a.rows, r);
-    float acc[R][M];
+  float acc[R][M];
 #pragma unroll
-    for (int i = 0; i < R; ++i)
+  for (int i = 0; i < R; ++i)
 #pragma unroll
-      for (int mi = 0; mi < M; ++mi) acc[i][mi] = 0.f;
-    for (int base = 0; base < nunits; base += 64 * U) {
-      if (!first) gemv_load<QT, R, U>(a, r, base, lane, nunits, W);
-      first = false;
-      gemv_compute<QT, R, U, M>(xs, xsum, kp, a.nblk, base, lane, nunits, W, acc);
+    for (int mi = 0; mi < M; ++mi) acc[i][mi] = 0.f;
+
+  while (grp < ngroups) {
+    // request the next tile of this wave
+    int ngrp = grp, ntb = tb + 1;
+    if (ntb == tpg) {
+      ntb = 0;
+      ngrp = grp + nwaves;
     }
+    const bool more = ngrp < ngroups;
+    if (more) {
+      if (ngrp != grp) group_rows<R, kPair>(ngrp, a.rows, rn);
+      else
 #pragma unroll
-    for (int mi = 0; mi < M; ++mi) {
-      float s[R];
+        for (int i = 0; i < R; ++i) rn[i] = r[i];
+      gemv_load<QT, R, U>(a, rn, ntb * 64 * U, lane, nunits, nxt);
+    }
+    gemv_compute<QT, R, U, M>(xs4, xsum, kp, a.nblk, tb * 64 * U, lane, nunits, cur, acc);
+    if (tb == tpg - 1) {
 #pragma unroll
-      for (int i = 0; i < R; ++i) s[i] = wave_sum(acc[i][mi]);
-      if (lane == 0 && mi < a.m) {
-        float* yr = (a.y_ind ? *a.y_ind + a.y_off : a.y) + (size_t)mi * a.ldy;
+      for (int mi = 0; mi < M; ++mi) {
+        float sv[R];
 #pragma unroll
-        for (int i = 0; i < R; ++i) {
-          if constexpr (kPair) {
-            if (i & 1) {
-              const int n = grp * (R / 2) + i / 2;
-              yr[n] = (MODE == kModePairSilu ? act_silu(s[i - 1]) : act_gelu_tanh(s[i - 1])) * s[i];
-            }
-          } else {
-            const int row = grp * R + i;
-            if (row < a.rows) {
-              if constexpr (MODE == kModeAdd) yr[row] += s[i];
-              else yr[row] = s[i];
+        for (int i = 0; i < R; ++i) sv[i] = wave_sum(acc[i][mi]);
+        if (lane == 0 && mi < a.m) {
+          float* yr = (a.y_ind ? *a.y_ind + a.y_off : a.y) + (size_t)mi * a.ldy;
+#pragma unroll
+          for (int i = 0; i < R; ++i) {
+            if constexpr (kPair) {
+              if (i & 1) {
+                const int n = grp * (R / 2) + i / 2;
+                yr[n] = (MODE == kModePairSilu ? act_silu(sv[i - 1]) : act_gelu_tanh(sv[i - 1])) * sv[i];
+              }
+            } else {
+              const int row = grp * R + i;
+              if (row < a.rows) {
+                if constexpr (MODE == kModeAdd) yr[row] += sv[i];
+                else yr[row] = sv[i];
+              }
             }
           }
         }
       }
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int mi = 0; mi < M; ++mi) acc[i][mi] = 0.f;
     }
+    cur = nxt;
+#pragma unroll
+    for (int i = 0; i < R; ++i) r[i] = rn[i];
+    grp = ngrp;
+    tb = ntb;
   }
 }
 

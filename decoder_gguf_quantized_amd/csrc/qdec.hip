@@ -215,7 +215,9 @@ void gemv(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, 
   const int ru = nunits <= 64 ? 0 : (nunits <= 128 ? 1 : 2);
   const int R = ru == 0 ? 4 : 2;
   const int ngroups = pair ? w.rows / R : (w.rows + R - 1) / R;
-  dim3 grid(std::max(1, std::min((ngroups + 3) / 4, 2048)));
+  // waves stay resident and loop: about four workgroups per CU, so the input
+  // staging of each workgroup is amortised over many row groups
+  dim3 grid(std::max(1, std::min((ngroups + 3) / 4, 1024)));
   for (int r0 = 0; r0 < nrows; r0 += cap) {
     const int mr = std::min(cap, nrows - r0);
     int M = 1;
