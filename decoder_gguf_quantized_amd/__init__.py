@@ -81,6 +81,7 @@ def lib():
                 "qdec_prefill": (ctypes.c_int, [P, I32, P, I32, P, P, U32, P]),
                 "qdec_decode_step": (ctypes.c_int, [P, P, I32, P, P, F, U64, U64, U32, P]),
                 "qdec_kv_reset": (ctypes.c_int, [P, I32]),
+                "qdec_kv_truncate": (ctypes.c_int, [P, I32, I32]),
                 "qdec_kv_write": (ctypes.c_int, [P, I32, I32, P, P, I32, P]),
                 "qdec_kv_len": (ctypes.c_int, [P, I32, ctypes.POINTER(I32)]),
                 "qdec_poisoned": (ctypes.c_int, [P]),
@@ -297,6 +298,10 @@ class Model:
 
     def kv_reset(self, seq=-1):
         self._check(lib().qdec_kv_reset(self._handle(), _int("seq", seq)))
+
+    def kv_truncate(self, seq, n):
+        """Roll sequence ``seq`` back to its first ``n`` positions."""
+        self._check(lib().qdec_kv_truncate(self._handle(), _int("seq", seq), _int("n", n)))
 
     def kv_write(self, seq, layer, k, v):
         """Install preset post-RoPE K, V (f32 GPU tensors [n_kv][n_pos][head_dim])."""

@@ -8,6 +8,8 @@
 // and the qwen3 architecture file on Synsema "Local inference and architectures".
 #include "../../include/qdec.h"
 
+#include <hip/hip_ext.h>
+
 #include <algorithm>
 #include <chrono>
 #include <cmath>
@@ -141,25 +143,38 @@ struct qdec_model {
 namespace {
 
 // ------------------------------------------------------------ launch helpers
+// Per-kernel timing: while a Timed scope is open with timing on, the next launch
+// goes through hipExtLaunchKernelGGL with the scope's start/stop events, which
+// take their timestamps from the dispatch itself.
+thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
+
+template <typename... KArgs, typename... Args>
+void qlaunch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStream_t st, Args... args) {
+  if (g_ev_start) {
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, st, g_ev_start, g_ev_stop, 0, args...);
+    g_ev_start = g_ev_stop = nullptr;
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
+  }
+}
+
 struct Timed {
   qdec_model* m;
-  hipStream_t st;
   const char* cls;
   double bytes, flops;
   hipEvent_t a = nullptr, b = nullptr;
-  Timed(qdec_model* mm, hipStream_t s, const char* c, double by, double fl) : m(mm), st(s), cls(c), bytes(by), flops(fl) {
+  Timed(qdec_model* mm, hipStream_t, const char* c, double by, double fl) : m(mm), cls(c), bytes(by), flops(fl) {
     if (m && m->timing) {
       hipck(hipEventCreate(&a), "hipEventCreate");
       hipck(hipEventCreate(&b), "hipEventCreate");
-      hipck(hipEventRecord(a, st), "hipEventRecord");
+      g_ev_start = a;
+      g_ev_stop = b;
     }
   }
   ~Timed() noexcept(false) {
+    g_ev_start = g_ev_stop = nullptr;
     hipck(hipGetLastError(), cls);
-    if (m && m->timing) {
-      hipck(hipEventRecord(b, st), "hipEventRecord");
-      m->krecs.push_back(KRec{cls, a, b, bytes, flops});
-    }
+    if (a) m->krecs.push_back(KRec{cls, a, b, bytes, flops});
   }
 };
 
@@ -169,10 +184,10 @@ const char* gemm_class(int type) { return type == kQ4_0 ? "gemm_q4_0" : type == 
 template <int QT, int M, int R, int U>
 void gemv_dispatch_mode(int mode, dim3 grid, size_t lds, hipStream_t st, const GemvArgs& a) {
   switch (mode) {
-    case kModeStore: gemv_kernel<QT, M, kModeStore, R, U><<<grid, 256, lds, st>>>(a); break;
-    case kModeAdd: gemv_kernel<QT, M, kModeAdd, R, U><<<grid, 256, lds, st>>>(a); break;
-    case kModePairSilu: gemv_kernel<QT, M, kModePairSilu, R, U><<<grid, 256, lds, st>>>(a); break;
-    default: gemv_kernel<QT, M, kModePairGelu, R, U><<<grid, 256, lds, st>>>(a); break;
+    case kModeStore: qlaunch(gemv_kernel<QT, M, kModeStore, R, U>, grid, 256, lds, st, a); break;
+    case kModeAdd: qlaunch(gemv_kernel<QT, M, kModeAdd, R, U>, grid, 256, lds, st, a); break;
+    case kModePairSilu: qlaunch(gemv_kernel<QT, M, kModePairSilu, R, U>, grid, 256, lds, st, a); break;
+    default: qlaunch(gemv_kernel<QT, M, kModePairGelu, R, U>, grid, 256, lds, st, a); break;
   }
 }
 
@@ -236,10 +251,10 @@ void gemv(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, 
 template <int QT>
 void gemm_dispatch(int mode, dim3 grid, hipStream_t st, const GemmArgs& a) {
   switch (mode) {
-    case kModeStore: gemm_kernel<QT, kModeStore><<<grid, 256, 0, st>>>(a); break;
-    case kModeAdd: gemm_kernel<QT, kModeAdd><<<grid, 256, 0, st>>>(a); break;
-    case kModePairSilu: gemm_kernel<QT, kModePairSilu><<<grid, 256, 0, st>>>(a); break;
-    default: gemm_kernel<QT, kModePairGelu><<<grid, 256, 0, st>>>(a); break;
+    case kModeStore: qlaunch(gemm_kernel<QT, kModeStore>, grid, 256, 0, st, a); break;
+    case kModeAdd: qlaunch(gemm_kernel<QT, kModeAdd>, grid, 256, 0, st, a); break;
+    case kModePairSilu: qlaunch(gemm_kernel<QT, kModePairSilu>, grid, 256, 0, st, a); break;
+    default: qlaunch(gemm_kernel<QT, kModePairGelu>, grid, 256, 0, st, a); break;
   }
 }
 
@@ -258,17 +273,17 @@ void rmsnorm_rows(qdec_model* m, hipStream_t st, const float* x, int ldx, const 
                   int rows, int add) {
   NormArgs a{x, ldx, w, m ? m->cfg.rms_eps : 0.f, n, out, ldo, add};
   Timed tm(m, st, "rmsnorm", (double)rows * n * (add ? 12 : 8), 0);
-  rmsnorm_kernel<<<rows, 256, 0, st>>>(a);
+  qlaunch(rmsnorm_kernel, rows, 256, 0, st, a);
 }
 
 template <int HD>
 void attn_decode_hd(int G, dim3 grid, hipStream_t st, const AttnDecodeArgs& a) {
   switch (G) {
-    case 1: attn_decode_kernel<HD, 1><<<grid, 256, 0, st>>>(a); break;
-    case 2: attn_decode_kernel<HD, 2><<<grid, 256, 0, st>>>(a); break;
-    case 4: attn_decode_kernel<HD, 4><<<grid, 256, 0, st>>>(a); break;
+    case 1: qlaunch(attn_decode_kernel<HD, 1>, grid, 256, 0, st, a); break;
+    case 2: qlaunch(attn_decode_kernel<HD, 2>, grid, 256, 0, st, a); break;
+    case 4: qlaunch(attn_decode_kernel<HD, 4>, grid, 256, 0, st, a); break;
     default:
-      if constexpr (HD == 128) attn_decode_kernel<HD, 8><<<grid, 256, 0, st>>>(a);
+      if constexpr (HD == 128) qlaunch(attn_decode_kernel<HD, 8>, grid, 256, 0, st, a);
       break;
   }
 }
@@ -303,9 +318,9 @@ void attention_decode(qdec_model* m, hipStream_t st, int l, int B) {
   AttnCombineArgs cb{m->part_o, m->part_ml, m->d_pos, c.n_head, a.window, m->chunk, m->nchunk, m->a};
   Timed tm(m, st, "attn_combine", (double)B * c.n_head * hd * 4 * 2, 0);
   dim3 cgrid(c.n_head, B);
-  if (hd == 64) attn_combine_kernel<64><<<cgrid, 64, 0, st>>>(cb);
-  else if (hd == 128) attn_combine_kernel<128><<<cgrid, 64, 0, st>>>(cb);
-  else attn_combine_kernel<256><<<cgrid, 64, 0, st>>>(cb);
+  if (hd == 64) qlaunch(attn_combine_kernel<64>, cgrid, 64, 0, st, cb);
+  else if (hd == 128) qlaunch(attn_combine_kernel<128>, cgrid, 64, 0, st, cb);
+  else qlaunch(attn_combine_kernel<256>, cgrid, 64, 0, st, cb);
 }
 
 void attention_prefill(qdec_model* m, hipStream_t st, int l, int seq, int T, int pos0) {
@@ -324,9 +339,9 @@ void attention_prefill(qdec_model* m, hipStream_t st, int l, int seq, int T, int
            4.0 * hd * c.n_head * pairs);
   const int QT = 256 / (hd / 8);
   dim3 grid((T + QT - 1) / QT, c.n_head);
-  if (hd == 64) attn_prefill_kernel<64, 64><<<grid, 256, 0, st>>>(a);
-  else if (hd == 128) attn_prefill_kernel<128, 32><<<grid, 256, 0, st>>>(a);
-  else attn_prefill_kernel<256, 16><<<grid, 256, 0, st>>>(a);
+  if (hd == 64) qlaunch(attn_prefill_kernel<64, 64>, grid, 256, 0, st, a);
+  else if (hd == 128) qlaunch(attn_prefill_kernel<128, 32>, grid, 256, 0, st, a);
+  else qlaunch(attn_prefill_kernel<256, 16>, grid, 256, 0, st, a);
 }
 
 void rope_kv(qdec_model* m, hipStream_t st, int l, int n, int seq0, int pos0, const int* dpos) {
@@ -336,7 +351,7 @@ void rope_kv(qdec_model* m, hipStream_t st, int l, int n, int seq0, int pos0, co
              c.n_head_kv, c.head_dim, L.q_norm, L.k_norm, c.rms_eps, L.global ? m->rope_g : m->rope_l,
              seq0, pos0, dpos};
   Timed tm(m, st, "rope_kv", (double)n * m->nqkv * 8, 0);
-  rope_kv_kernel<<<n, 256, 0, st>>>(a);
+  qlaunch(rope_kv_kernel, n, 256, 0, st, a);
 }
 
 void embed(qdec_model* m, hipStream_t st, const int* d_tokens, int n, float* out) {
@@ -344,7 +359,7 @@ void embed(qdec_model* m, hipStream_t st, const int* d_tokens, int n, float* out
   EmbedArgs a{WView{m->embd.qs, m->embd.d, m->embd.type, m->embd.nblk}, c.hidden, c.vocab, n, d_tokens, out,
               c.hidden, m->err_dev};
   Timed tm(m, st, "embed", (double)n * (m->embd.gguf_bytes / m->embd.rows + c.hidden * 4), 0);
-  embed_kernel<<<n, 256, 0, st>>>(a);
+  qlaunch(embed_kernel, n, 256, 0, st, a);
 }
 
 void sample(qdec_model* m, hipStream_t st, const float* logits, int ld, int rows, float temp, uint64_t seed,
@@ -353,10 +368,10 @@ void sample(qdec_model* m, hipStream_t st, const float* logits, int ld, int rows
   SampleArgs a{logits, ld, V, rows, temp, seed, step, m->s_v, m->s_i, m->nvchunk, out, out2, sp};
   {
     Timed tm(m, st, "sample", (double)rows * V * 4, 0);
-    sample_stage1_kernel<<<dim3(m->nvchunk, rows), 256, 0, st>>>(a);
+    qlaunch(sample_stage1_kernel, dim3(m->nvchunk, rows), 256, 0, st, a);
   }
   Timed tm(m, st, "sample_final", (double)rows * m->nvchunk * 8, 0);
-  sample_stage2_kernel<<<rows, 64, 0, st>>>(a);
+  qlaunch(sample_stage2_kernel, rows, 64, 0, st, a);
 }
 
 // The blocks over n tokens of one sequence (prefill) or one token of each of n
@@ -912,7 +927,7 @@ int qdec_decode_step(qdec_model* m, const int32_t* tokens, int32_t n_seqs, float
     sa.d_params = m->d_params;
     {
       Timed tm(m, st, "step_begin", 0, 0);
-      step_begin_kernel<<<1, 64, 0, st>>>(sa);
+      qlaunch(step_begin_kernel, 1, 64, 0, st, sa);
     }
     if (m->timing) {
       decode_body(m, st, n_seqs);
@@ -948,6 +963,15 @@ int qdec_kv_reset(qdec_model* m, int32_t seq) {
   if (seq < -1 || seq >= m->max_seqs) { set_err("seq %d outside [-1, %d)", seq, m->max_seqs); return QDEC_REFUSED; }
   if (seq < 0) std::fill(m->kvlen.begin(), m->kvlen.end(), 0);
   else m->kvlen[seq] = 0;
+  return QDEC_OK;
+}
+
+int qdec_kv_truncate(qdec_model* m, int32_t seq, int32_t n) {
+  g_err.clear();
+  if (int rc = check_usable(m)) return rc;
+  if (seq < 0 || seq >= m->max_seqs) { set_err("seq %d outside [0, %d)", seq, m->max_seqs); return QDEC_REFUSED; }
+  if (n < 0 || n > m->kvlen[seq]) { set_err("n %d outside [0, kv_len %d]", n, m->kvlen[seq]); return QDEC_REFUSED; }
+  m->kvlen[seq] = n;
   return QDEC_OK;
 }
 
@@ -1007,7 +1031,7 @@ int qdec_debug_dequant(qdec_model* m, const char* name, float* d_out, void* stre
   try {
     DequantArgs a{WView{r.mat->qs, r.mat->d, r.mat->type, r.mat->nblk}, nullptr, r.row_off, r.rows, r.cols, r.pair, d_out};
     Timed tm(m, st, "dequant", 0, 0);
-    dequant_kernel<<<r.rows, 256, 0, st>>>(a);
+    qlaunch(dequant_kernel, r.rows, 256, 0, st, a);
   } catch (const HipError& e) {
     return fail_internal(m, st, e.msg);
   }
@@ -1042,8 +1066,8 @@ int qdec_debug_sample(const float* d_logits, int32_t rows, int32_t vocab, float 
     return QDEC_INTERNAL;
   }
   SampleArgs a{d_logits, vocab, vocab, rows, temperature, seed, step, pv, pi, nch, d_out, nullptr, nullptr};
-  sample_stage1_kernel<<<dim3(nch, rows), 256, 0, st>>>(a);
-  sample_stage2_kernel<<<rows, 64, 0, st>>>(a);
+  qlaunch(sample_stage1_kernel, dim3(nch, rows), 256, 0, st, a);
+  qlaunch(sample_stage2_kernel, rows, 64, 0, st, a);
   hipError_t e = hipStreamSynchronize(st);
   (void)hipFree(pv);
   (void)hipFree(pi);

@@ -131,6 +131,10 @@ int qdec_decode_step(qdec_model* m, const int32_t* tokens, int32_t n_seqs, float
  * stale KV rows are never read past kv_len. */
 int qdec_kv_reset(qdec_model* m, int32_t seq);
 
+/* Roll sequence seq back to its first n positions (0 <= n <= kv_len(seq)), for
+ * instance to rerun decode steps over a preset cache.  Host-side only. */
+int qdec_kv_truncate(qdec_model* m, int32_t seq, int32_t n);
+
 /* Install preset post-RoPE K and V, each f32 [n_head_kv][n_pos][head_dim]
  * (device), for one (sequence, layer) at positions 0..n_pos-1, and set
  * kv_len(seq) = n_pos. */

@@ -246,6 +246,23 @@ def preset_kv(cfg, seq, layer, n_pos=None):
     return k, v
 
 
+def preset_kv_all(cfg, seqs=None, threads=None):
+    """Yield (seq, layer, k, v) for every preset cache block, drawn in a thread
+    pool a few blocks ahead of the consumer (bounded memory)."""
+    seqs = range(cfg["batch"]) if seqs is None else seqs
+    jobs = [(s, l) for s in seqs for l in range(cfg["n_layer"])]
+    nt = threads or _threads()
+    with ThreadPoolExecutor(nt) as pool:
+        futs = {}
+        ahead = 2 * nt
+        for i, (s, l) in enumerate(jobs):
+            for j in range(i, min(len(jobs), i + ahead)):
+                if j not in futs:
+                    futs[j] = pool.submit(preset_kv, cfg, *jobs[j])
+            k, v = futs.pop(i).result()
+            yield s, l, k, v
+
+
 def manifest(tensors):
     """{name: sha256} of every tensor's bytes, for reports."""
     return {n: t.sha256() for n, t in tensors.items()}
