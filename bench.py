@@ -84,7 +84,36 @@ def cpu_baseline(cfg, tensors, budget_s=20.0):
                        f"greedy decode steps timed ({t_dec:.1f} s), float64 numpy, {cores} host threads")
 
 
-def roofline_entry(kst):
+def kernel_sources_hash():
+    """sha256 (first 16 hex) of the HIP sources, to tell whether stored counter
+    readings still describe the kernels being timed."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "decoder_gguf_quantized_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config, kernel):
+    """HBM bytes per dispatch of ``kernel`` from the committed rocprofv3 --pmc
+    summary (profiles/traffic_<config>.txt), or None when there is none or the
+    kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{config}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel") != kernel or kv.get("sources") != kernel_sources_hash():
+        return None
+    return round(float(kv["fetch_bytes"]) + float(kv["write_bytes"]))
+
+
+def roofline_entry(kst, config=None):
     """Roofline object for the kernel class with the most measured time."""
     dname, d = max(kst.items(), key=lambda kv: kv[1]["ms"])
     if d["flops"] and d["bytes"] and dname.startswith("gemm"):
@@ -97,6 +126,8 @@ def roofline_entry(kst):
                     frac=round(achieved / 8000.0, 4), traffic=None)
     roof.update(kernel=dname, launches=d["launches"], avg_launch_us=round(d["ms"] * 1e3 / d["launches"], 2),
                 bytes_per_launch=round(d["bytes"] / d["launches"]))
+    if config:
+        roof["traffic"] = measured_traffic(config, dname)
     return roof
 
 
@@ -160,7 +191,7 @@ def bench_batched(cfg, args):
                                f"temperature {temp} (Gumbel-max over Philox4x64-10)",
                    "batch": B, "preset_kv": P, "decode_steps": N, "weights": cfg["wtype"]},
         "decode_hbm_frac": round(bytes_dec / (ms / 1e3) / HBM_PEAK, 4),
-        "roofline": roofline_entry(kst),
+        "roofline": roofline_entry(kst, cfg.get("key")),
         "kernels": {k: dict(launches=v["launches"], ms=round(v["ms"], 3)) for k, v in sorted(kst.items())},
     }
     if not args.no_cpu_baseline:
@@ -217,11 +248,16 @@ def main():
     import synth
 
     cfg = synth.get(args.config)
+    cfg["key"] = args.config
+    if args.copy_calibration:
+        a = torch.empty(64 << 20, dtype=torch.float32, device="cuda:0")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
     if cfg["preset_kv"]:
         return bench_batched(cfg, args)
-    t_gen = time.perf_counter()
     tensors = synth.generate(cfg)
-    t_gen = time.perf_counter() - t_gen
     dev = torch.device("cuda:0")
     if args.decode_steps is not None:
         cfg["decode_steps"] = args.decode_steps
@@ -254,16 +290,10 @@ def main():
         dec = [e[1].elapsed_time(e[2]) for e in evs]
         return wall, pre, dec
 
-    if args.copy_calibration:
-        a = torch.empty(64 << 20, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
-        b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
     for _ in range(args.warmup):
         run(1)
     wall, pre_ms, dec_ms = run(args.steps)
-    # second pass of the same steps with per-kernel events for the roofline figure
+    # second pass of the same steps with per-dispatch events for the roofline figure
     model.kernel_timing(True)
     run(args.steps)
     kst = model.kernel_timing(False)
@@ -274,142 +304,6 @@ def main():
     bytes_dec = sum(step_bytes_decode(cfg, T + s) for s in range(N))
     hbm_frac = bytes_dec / (np.mean(dec_ms) / 1e3) / HBM_PEAK
     mfma_util = prefill_flops(cfg, T) / (np.mean(pre_ms) / 1e3) / FP32_MFMA_PEAK
-    roof = roofline_entry(kst)
-    line = {
-        "metric": "decode tokens/sec + HBM GB/s fraction; prefill tokens/sec + MFMA util",
-        "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(wall * 1e3 / args.steps, 3), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": f"{cfg['name']}: {B} sequences x {P} preset KV positions, {N} decode steps, "
-                               f"temperature {temp} (Gumbel-max over Philox4x64-10)",
-                   "batch": B, "preset_kv": P, "decode_steps": N, "weights": cfg["wtype"]},
-        "decode_hbm_frac": round(bytes_dec / (ms / 1e3) / HBM_PEAK, 4),
-        "roofline": roofline_entry(kst),
-        "kernels": {k: dict(launches=v["launches"], ms=round(v["ms"], 3)) for k, v in sorted(kst.items())},
-    }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline_batched(cfg, tensors)
-    print(json.dumps(line), flush=True)
-
-
-def cpu_baseline_batched(cfg, tensors, budget_s=20.0):
-    """The oracle on sequence 0 of the batched workload: its preset cache, then
-    sampled decode steps until the budget is spent."""
-    from oracle import OracleModel, sampler
-    import synth
-    cores = len(os.sched_getaffinity(0))
-    P = cfg["preset_kv"]
-    om = OracleModel(cfg, tensors, max_ctx=P + 16)
-    for s, l, k, v in synth.preset_kv_all(cfg, seqs=[0]):
-        om.kv_write(0, l, k, v)
-    om.set_kv_len(0, P)
-    tok = int(synth.first_tokens(cfg)[0])
-    n, t = 0, 0.0
-    while n < 8 and (t < budget_s or n < 2):
-        t0 = time.perf_counter()
-        lg = om.forward(0, [tok])[0]
-        tok = sampler.sample(lg, cfg["temperature"], cfg["seed"], n, 0)
-        t += time.perf_counter() - t0
-        n += 1
-    return dict(value=n / t, unit="tokens/s", cores=cores, kind="oracle",
-                sample=f"{cfg['name']}: sequence 0 of {cfg['batch']}, {P} preset KV positions, {n} sampled decode "
-                       f"steps timed ({t:.1f} s), float64 numpy, {cores} host threads")
-
-
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=3)
-    ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--config", default="c2")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--decode-steps", type=int, default=None, help="override the workload's decode steps (profiling runs)")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a 256 MiB device-to-device copy (reference for HBM byte counters)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path has no multi-GPU mode",
-              file=sys.stderr)
-        sys.exit(2)
-
-    cores = len(os.sched_getaffinity(0))
-    os.environ.setdefault("OMP_NUM_THREADS", str(cores))
-    os.environ.setdefault("OPENBLAS_NUM_THREADS", str(cores))
-    import torch
-
-    import decoder_gguf_quantized_amd as qdec
-    import synth
-
-    cfg = synth.get(args.config)
-    if cfg["preset_kv"]:
-        return bench_batched(cfg, args)
-    t_gen = time.perf_counter()
-    tensors = synth.generate(cfg)
-    t_gen = time.perf_counter() - t_gen
-    dev = torch.device("cuda:0")
-    if args.decode_steps is not None:
-        cfg["decode_steps"] = args.decode_steps
-    T, N, V = cfg["prompt_len"], cfg["decode_steps"], cfg["vocab"]
-    prompt = synth.prompt(cfg)
-    model = qdec.Model(cfg, tensors, max_seqs=1, max_ctx=T + N + 1)
-    pl = torch.empty(V, dtype=torch.float32, device=dev)
-    dl = torch.empty((N, V), dtype=torch.float32, device=dev)
-    toks = torch.empty((N + 1, 1), dtype=torch.int32, device=dev)
-    stream = torch.cuda.current_stream()
-
-    def one_step(ev):
-        model.kv_reset()
-        ev[0].record(stream)
-        model.prefill(0, prompt, pl, toks[0])
-        ev[1].record(stream)
-        for s in range(N):
-            model.decode_step(toks[s], dl[s:s + 1], toks[s + 1])
-        ev[2].record(stream)
-
-    def run(k):
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(k)]
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(k):
-            one_step(evs[i])
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        pre = [e[0].elapsed_time(e[1]) for e in evs]
-        dec = [e[1].elapsed_time(e[2]) for e in evs]
-        return wall, pre, dec
-
-    if args.copy_calibration:
-        a = torch.empty(64 << 20, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
-        b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
-    for _ in range(args.warmup):
-        run(1)
-    wall, pre_ms, dec_ms = run(args.steps)
-    # second pass of the same steps with per-kernel events for the roofline figure
-    model.kernel_timing(True)
-    run(args.steps)
-    kst = model.kernel_timing(False)
-    model.close()
-
-    dec_tok_s = args.steps * N / (sum(dec_ms) / 1e3)
-    pre_tok_s = args.steps * T / (sum(pre_ms) / 1e3)
-    bytes_dec = sum(step_bytes_decode(cfg, T + s) for s in range(N))
-    hbm_frac = bytes_dec / (np.mean(dec_ms) / 1e3) / HBM_PEAK
-    mfma_util = prefill_flops(cfg, T) / (np.mean(pre_ms) / 1e3) / FP32_MFMA_PEAK
-    dom = max(kst.items(), key=lambda kv: kv[1]["ms"])
-    dname, d = dom
-    if d["flops"] and d["bytes"] and dname.startswith("gemm"):
-        achieved = d["flops"] / (d["ms"] / 1e3) / 1e12
-        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=157.3, unit="TFLOP/s",
-                    frac=round(achieved / 157.3, 4), traffic=None)
-    else:
-        achieved = d["bytes"] / (d["ms"] / 1e3) / 1e9
-        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=8000.0, unit="GB/s",
-                    frac=round(achieved / 8000.0, 4), traffic=None)
-    roof.update(kernel=dname, launches=d["launches"], avg_launch_us=round(d["ms"] * 1e3 / d["launches"], 2),
-                bytes_per_launch=round(d["bytes"] / d["launches"]))
     line = {
         "metric": "decode tokens/sec + HBM GB/s fraction; prefill tokens/sec + MFMA util",
         "value": round(dec_tok_s, 2),
@@ -429,7 +323,7 @@ def main():
         "prefill_mfma_util": round(float(mfma_util), 4),
         "decode_hbm_frac": round(float(hbm_frac), 4),
         "decode_ms_per_token": round(float(np.mean(dec_ms)) / N, 4),
-        "roofline": roof,
+        "roofline": roofline_entry(kst, cfg["key"]),
         "kernels": {k: dict(launches=v["launches"], ms=round(v["ms"], 3)) for k, v in sorted(kst.items())},
     }
     if not args.no_cpu_baseline:

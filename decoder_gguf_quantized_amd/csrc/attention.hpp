@@ -37,7 +37,20 @@ struct AttnDecodeArgs {
   float scale_log2;     // hd^-1/2 * log2(e)
   float* part_o;        // [B][nq][nchunk][hd], unnormalised partial outputs
   float* part_ml;       // [B][nq][nchunk][2]: running max (log2 domain), sum
+  int* counter;         // [B][nkv] finished-chunk counters, zero between launches
+  float* out;           // [B][nq*hd] merged attention output
 };
+
+// Device-coherent (write-through / L2-bypassing) accesses for the cross-
+// workgroup partials: the L2s of the eight dies are not coherent with each
+// other, and these keep the merge free of whole-cache write-back/invalidate.
+QD_DEV void store_coherent(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+QD_DEV float load_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Most position chunks per (sequence, KV head); the launcher sizes chunks so.
+constexpr int kMaxChunks = 64;
 
 QD_DEV void attn_key_range(int p, int window, int& lo, int& hi) {
   hi = p;
@@ -71,13 +84,17 @@ QD_DEV void norm_rope_group(float (&v)[8], const float* nw, float eps, int hd, i
 // whole group of query heads.  Prologue: QK-norm + RoPE of the group's queries,
 // and, in the chunk that holds the new position, of the new key, which it also
 // appends (with the new value) to the cache.  Each workgroup writes one partial
-// (m, l, o) per query head; attn_combine_kernel merges the chunks.
+// (m, l, o) per query head; the workgroup that finishes last among the chunks
+// of its (sequence, KV head) merges them (a counter, no workgroup waits):
+//   O = sum_c o_c 2^(m_c - M) / sum_c l_c 2^(m_c - M),  M = max_c m_c.
 template <int HD, int G>
 __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
   constexpr int LG = HD / 8;      // lanes per position
   constexpr int NG = 256 / LG;    // position streams per workgroup
   __shared__ float sm_o[NG][G][HD];
   __shared__ float sm_m[NG][G], sm_l[NG][G];
+  __shared__ float sm_pm[G][kMaxChunks], sm_pl[G][kMaxChunks];
+  __shared__ int sm_last;
 
   const int c = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int p = a.pos[s];
@@ -135,8 +152,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
       vd[1] = v1;
     }
   }
-  for (int j = start + gi; j < end; j += NG) {
-    float k[8], v[8];
+  // two positions per stream per iteration: both rows are requested before use
+  auto fetch = [&](int j, float (&k)[8], float (&v)[8]) {
     if (has_new && j == p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -146,10 +163,12 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
     } else {
       const float4* kp = reinterpret_cast<const float4*>(a.kc + (head_base + j) * HD + li * 8);
       const float4* vp = reinterpret_cast<const float4*>(a.vc + (head_base + j) * HD + li * 8);
-      float4 k0 = kp[0], k1 = kp[1], v0 = vp[0], v1 = vp[1];
+      const float4 k0 = kp[0], k1 = kp[1], v0 = vp[0], v1 = vp[1];
       k[0] = k0.x; k[1] = k0.y; k[2] = k0.z; k[3] = k0.w; k[4] = k1.x; k[5] = k1.y; k[6] = k1.z; k[7] = k1.w;
       v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w; v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
     }
+  };
+  auto accumulate = [&](const float (&k)[8], const float (&v)[8]) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float dot = 0.f;
@@ -164,6 +183,19 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
       for (int e = 0; e < 8; ++e) o[h][e] = o[h][e] * corr + pr * v[e];
       m[h] = mn;
     }
+  };
+  int j = start + gi;
+  for (; j + NG < end; j += 2 * NG) {
+    float k0[8], v0[8], k1[8], v1[8];
+    fetch(j, k0, v0);
+    fetch(j + NG, k1, v1);
+    accumulate(k0, v0);
+    accumulate(k1, v1);
+  }
+  if (j < end) {
+    float k0[8], v0[8];
+    fetch(j, k0, v0);
+    accumulate(k0, v0);
   }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -188,57 +220,55 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
       }
     }
     const size_t pi = ((size_t)s * a.nq + g * G + h) * a.nchunk + c;
-    a.part_o[pi * HD + dd] = O;
+    store_coherent(a.part_o + pi * HD + dd, O);
     if (dd == 0) {
-      a.part_ml[pi * 2 + 0] = M;
-      a.part_ml[pi * 2 + 1] = L;
+      store_coherent(a.part_ml + pi * 2 + 0, M);
+      store_coherent(a.part_ml + pi * 2 + 1, L);
     }
   }
-}
-
-struct AttnCombineArgs {
-  const float* part_o;
-  const float* part_ml;
-  const int* pos;
-  int nq, window, chunk, nchunk;
-  float* out;           // [B][nq*hd]
-};
-
-// Merge of the chunks that hold keys for (query head, sequence): one wave per
-// head; lane k takes chunks k, k+64, ... and the lanes merge their running
-// (m, l) pairs; then each lane rescales and sums its dims over the chunks.
-template <int HD>
-__global__ __launch_bounds__(64) void attn_combine_kernel(AttnCombineArgs a) {
-  const int h = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
-  int lo, hi;
-  attn_key_range(a.pos[s], a.window, lo, hi);
-  const int c_lo = lo / a.chunk, c_hi = hi / a.chunk;
-  const size_t base = ((size_t)s * a.nq + h) * a.nchunk;
-  float M = -INFINITY;
-  for (int c = c_lo + lane; c <= c_hi; c += 64) M = fmaxf(M, a.part_ml[(base + c) * 2]);
-  M = wave_max(M);
-  float L = 0.f;
-  for (int c = c_lo + lane; c <= c_hi; c += 64) {
-    const float mc = a.part_ml[(base + c) * 2];
-    L += mc == -INFINITY ? 0.f : a.part_ml[(base + c) * 2 + 1] * exp2f(mc - M);
+  // every partial store of this workgroup is complete before the counter moves
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0) {
+    const int done = __hip_atomic_fetch_add(a.counter + s * a.nkv + g, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm_last = done == c_hi - c_lo;
   }
-  L = wave_sum(L);
-  const float inv = 1.0f / L;
-  constexpr int DPL = HD / 64;  // dims per lane
-  float o[DPL];
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) o[e] = 0.f;
-  for (int c = c_lo; c <= c_hi; ++c) {
-    const float mc = a.part_ml[(base + c) * 2];
-    const float w = mc == -INFINITY ? 0.f : exp2f(mc - M);
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) o[e] += a.part_o[(base + c) * HD + lane + 64 * e] * w;
+  __syncthreads();
+  if (!sm_last) return;
+  // merge: (m, l) of every chunk into LDS, then each output element requests its
+  // values of all chunks at once (one round trip) and sums them in chunk order
+  const int nact = c_hi - c_lo + 1;  // <= kMaxChunks (the launcher sizes chunks so)
+  for (int i = tid; i < G * nact; i += 256) {
+    const int h = i / nact, cc = i % nact;
+    const size_t pi = ((size_t)s * a.nq + g * G + h) * a.nchunk + c_lo + cc;
+    sm_pm[h][cc] = load_coherent(a.part_ml + pi * 2);
+    sm_pl[h][cc] = load_coherent(a.part_ml + pi * 2 + 1);
   }
-  float* dst = a.out + (size_t)s * a.nq * HD + (size_t)h * HD;
+  __syncthreads();
+  for (int idx = tid; idx < G * HD; idx += 256) {
+    const int h = idx / HD, dd = idx % HD;
+    const float* po = a.part_o + (((size_t)s * a.nq + g * G + h) * a.nchunk + c_lo) * HD + dd;
+    float M = -INFINITY;
+    for (int cc = 0; cc < nact; ++cc) M = fmaxf(M, sm_pm[h][cc]);
+    float L = 0.f, O = 0.f;
+    for (int c0 = 0; c0 < nact; c0 += 16) {  // 16 chunks' values requested per round trip
+      float ov[16];
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) dst[lane + 64 * e] = o[e] * inv;
+      for (int cc = 0; cc < 16; ++cc) ov[cc] = c0 + cc < nact ? load_coherent(po + (size_t)(c0 + cc) * HD) : 0.f;
+#pragma unroll
+      for (int cc = 0; cc < 16; ++cc) {
+        if (c0 + cc < nact) {
+          const float mc = sm_pm[h][c0 + cc];
+          const float w = mc == -INFINITY ? 0.f : exp2f(mc - M);
+          L += sm_pl[h][c0 + cc] * w;
+          O += ov[cc] * w;
+        }
+      }
+    }
+    a.out[(size_t)s * a.nq * HD + (size_t)(g * G + h) * HD + dd] = O / L;
+  }
+  if (tid == 0) __hip_atomic_store(a.counter + s * a.nkv + g, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-
 
 struct AttnPrefillArgs {
   const float* q;       // [T][nq*hd]

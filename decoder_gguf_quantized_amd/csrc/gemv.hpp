@@ -158,23 +158,30 @@ QD_DEV void group_rows(int grp, int rows, int (&r)[R]) {
 }
 
 // Issue the loads of U units per lane for R rows: unit u = base + lane + 64 k.
+// Units past the row end are clamped to the last unit (a valid address, so the
+// loads need no predicate); gemv_compute skips them.  Row bases are scalar and
+// lane offsets unsigned 32-bit, so each load is a scalar base + vector offset.
 template <int QT, int R, int U>
 QD_DEV void gemv_load(const GemvArgs& a, const int (&r)[R], int base, int lane, int nunits, WRegs<QT, R, U>& W) {
   const int kp = a.nblk * 32;
 #pragma unroll
   for (int k = 0; k < U; ++k) {
-    const int u = base + lane + 64 * k;
-    const bool ok = u < nunits;
+    const unsigned uc = (unsigned)min(base + lane + 64 * k, nunits - 1);
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       if constexpr (QT == kQ8_0) {
-        W.w[i][k] = ok ? *reinterpret_cast<const uint4*>(a.qs + (size_t)r[i] * kp + 16 * u) : make_uint4(0, 0, 0, 0);
-        W.d[i][k] = ok ? load_half(a.d + (size_t)r[i] * a.nblk + (u >> 1)) : 0.f;
+        const uint8_t* rq = a.qs + (size_t)r[i] * kp;
+        const uint16_t* rd = a.d + (size_t)r[i] * a.nblk;
+        W.w[i][k] = *reinterpret_cast<const uint4*>(rq + uc * 16u);
+        W.d[i][k] = load_half(rd + (uc >> 1));
       } else if constexpr (QT == kQ4_0) {
-        W.w[i][k] = ok ? reinterpret_cast<const uint4*>(a.qs)[(size_t)r[i] * a.nblk + u] : make_uint4(0, 0, 0, 0);
-        W.d[i][k] = ok ? load_half(a.d + (size_t)r[i] * a.nblk + u) : 0.f;
+        const uint8_t* rq = a.qs + (size_t)r[i] * a.nblk * 16;
+        const uint16_t* rd = a.d + (size_t)r[i] * a.nblk;
+        W.w[i][k] = *reinterpret_cast<const uint4*>(rq + uc * 16u);
+        W.d[i][k] = load_half(rd + uc);
       } else {
-        W.w[i][k] = ok ? reinterpret_cast<const uint4*>(a.qs)[(size_t)r[i] * (kp / 4) + u] : make_uint4(0, 0, 0, 0);
+        const uint8_t* rq = a.qs + (size_t)r[i] * kp * 4;
+        W.w[i][k] = *reinterpret_cast<const uint4*>(rq + uc * 16u);
         W.d[i][k] = 1.f;
       }
     }
@@ -241,24 +248,62 @@ QD_DEV void gemv_compute(const float4* xs4, const float* xsum, int kp, int nblk,
 // memory pipe stays busy through the arithmetic, the lane reduction and the
 // store.  The first tile is requested before the input rows are staged.
 template <int QT, int M, int MODE, int R, int U>
+QD_DEV void gemv_store(const GemvArgs& a, int grp, int lane, float (&acc)[R][M]) {
+  constexpr bool kPair = MODE == kModePairSilu || MODE == kModePairGelu;
+#pragma unroll
+  for (int mi = 0; mi < M; ++mi) {
+    float sv[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) sv[i] = wave_sum(acc[i][mi]);
+    if (lane == 0 && mi < a.m) {
+      float* yr = (a.y_ind ? *a.y_ind + a.y_off : a.y) + (size_t)mi * a.ldy;
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        if constexpr (kPair) {
+          if (i & 1) {
+            const int n = grp * (R / 2) + i / 2;
+            yr[n] = (MODE == kModePairSilu ? act_silu(sv[i - 1]) : act_gelu_tanh(sv[i - 1])) * sv[i];
+          }
+        } else {
+          const int row = grp * R + i;
+          if (row < a.rows) {
+            if constexpr (MODE == kModeAdd) yr[row] += sv[i];
+            else yr[row] = sv[i];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i) acc[i][mi] = 0.f;
+  }
+}
+
+// R rows per wave, U 16-byte units per lane in flight per row, M input rows.
+// Each wave walks its (row group, unit block) tiles with a two-deep register
+// pipeline (two register sets used alternately): the loads of tile t+1 are
+// issued before tile t is computed, so the memory pipe stays busy through the
+// arithmetic, the lane reduction and the store.  The first tile is requested
+// before the input rows are staged.  Row indices are wave-uniform (scalar
+// registers), so every load is a scalar base plus a 32-bit lane offset.
+template <int QT, int M, int MODE, int R, int U>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   extern __shared__ float4 xs4[];
   const int kp = a.nblk * 32;
   float* xsum = reinterpret_cast<float*>(xs4 + M * kp / 4);  // Q4_0 only: [M][nblk] block sums of x
   constexpr bool kPair = MODE == kModePairSilu || MODE == kModePairGelu;
   const int lane = threadIdx.x & 63;
-  const int gwave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int gwave = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   const int nwaves = gridDim.x * 4;
   const int nunits = QT == kQ8_0 ? 2 * a.nblk : (QT == kQ4_0 ? a.nblk : kp / 4);
   const int ngroups = kPair ? a.rows / R : (a.rows + R - 1) / R;
   const int tpg = (nunits + 64 * U - 1) / (64 * U);  // tiles per row group
 
-  WRegs<QT, R, U> cur, nxt;
-  int r[R], rn[R];
+  WRegs<QT, R, U> w0, w1;
+  int r[R];
   int grp = gwave, tb = 0;
   if (grp < ngroups) {
     group_rows<R, kPair>(grp, a.rows, r);
-    gemv_load<QT, R, U>(a, r, 0, lane, nunits, cur);
+    gemv_load<QT, R, U>(a, r, 0, lane, nunits, w0);
   }
 
   gemv_stage_x<QT, M>(a, xs4, kp);
@@ -283,57 +328,45 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
 #pragma unroll
     for (int mi = 0; mi < M; ++mi) acc[i][mi] = 0.f;
 
+  // advance (grp, tb) to the wave's next tile; false when the wave is done
+  auto next_tile = [&](int& g, int& t) {
+    if (++t == tpg) {
+      t = 0;
+      g += nwaves;
+    }
+    return g < ngroups;
+  };
   while (grp < ngroups) {
-    // request the next tile of this wave
-    int ngrp = grp, ntb = tb + 1;
-    if (ntb == tpg) {
-      ntb = 0;
-      ngrp = grp + nwaves;
-    }
-    const bool more = ngrp < ngroups;
-    if (more) {
-      if (ngrp != grp) group_rows<R, kPair>(ngrp, a.rows, rn);
-      else
-#pragma unroll
-        for (int i = 0; i < R; ++i) rn[i] = r[i];
-      gemv_load<QT, R, U>(a, rn, ntb * 64 * U, lane, nunits, nxt);
-    }
-    gemv_compute<QT, R, U, M>(xs4, xsum, kp, a.nblk, tb * 64 * U, lane, nunits, cur, acc);
-    if (tb == tpg - 1) {
-#pragma unroll
-      for (int mi = 0; mi < M; ++mi) {
-        float sv[R];
-#pragma unroll
-        for (int i = 0; i < R; ++i) sv[i] = wave_sum(acc[i][mi]);
-        if (lane == 0 && mi < a.m) {
-          float* yr = (a.y_ind ? *a.y_ind + a.y_off : a.y) + (size_t)mi * a.ldy;
-#pragma unroll
-          for (int i = 0; i < R; ++i) {
-            if constexpr (kPair) {
-              if (i & 1) {
-                const int n = grp * (R / 2) + i / 2;
-                yr[n] = (MODE == kModePairSilu ? act_silu(sv[i - 1]) : act_gelu_tanh(sv[i - 1])) * sv[i];
-              }
-            } else {
-              const int row = grp * R + i;
-              if (row < a.rows) {
-                if constexpr (MODE == kModeAdd) yr[row] += sv[i];
-                else yr[row] = sv[i];
-              }
-            }
-          }
-        }
+    // stage A: compute from w0 while w1 loads
+    {
+      int g1 = grp, t1 = tb;
+      const bool more = next_tile(g1, t1);
+      int r1[R];
+      if (more) {
+        group_rows<R, kPair>(g1, a.rows, r1);
+        gemv_load<QT, R, U>(a, r1, t1 * 64 * U, lane, nunits, w1);
       }
-#pragma unroll
-      for (int i = 0; i < R; ++i)
-#pragma unroll
-        for (int mi = 0; mi < M; ++mi) acc[i][mi] = 0.f;
+      gemv_compute<QT, R, U, M>(xs4, xsum, kp, a.nblk, tb * 64 * U, lane, nunits, w0, acc);
+      if (tb == tpg - 1) gemv_store<QT, M, MODE, R, U>(a, grp, lane, acc);
+      if (!more) break;
+      grp = g1;
+      tb = t1;
     }
-    cur = nxt;
-#pragma unroll
-    for (int i = 0; i < R; ++i) r[i] = rn[i];
-    grp = ngrp;
-    tb = ntb;
+    // stage B: compute from w1 while w0 loads
+    {
+      int g0 = grp, t0 = tb;
+      const bool more = next_tile(g0, t0);
+      int r0[R];
+      if (more) {
+        group_rows<R, kPair>(g0, a.rows, r0);
+        gemv_load<QT, R, U>(a, r0, t0 * 64 * U, lane, nunits, w0);
+      }
+      gemv_compute<QT, R, U, M>(xs4, xsum, kp, a.nblk, tb * 64 * U, lane, nunits, w1, acc);
+      if (tb == tpg - 1) gemv_store<QT, M, MODE, R, U>(a, grp, lane, acc);
+      if (!more) break;
+      grp = g0;
+      tb = t0;
+    }
   }
 }
 

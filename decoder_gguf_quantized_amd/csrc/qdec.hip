@@ -8,7 +8,6 @@
 // and the qwen3 architecture file on Synsema "Local inference and architectures".
 #include "../../include/qdec.h"
 
-#include <hip/hip_ext.h>
 
 #include <algorithm>
 #include <chrono>
@@ -16,6 +15,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <cstdlib>
 #include <new>
 #include <string>
 #include <thread>
@@ -114,6 +114,7 @@ struct qdec_model {
   int nvchunk = 0;
   int* d_pos = nullptr;
   int* d_tok = nullptr;
+  int* counters = nullptr;          // [max_seqs][n_head_kv] decode-attention chunk counters
   StepParams* d_params = nullptr;   // per-step values read by replayed graphs
   hipStream_t cap_stream = nullptr; // capture stream for the decode graphs
   std::unordered_map<int, hipGraphExec_t> graphs;  // decode graph per batch size
@@ -126,6 +127,8 @@ struct qdec_model {
   std::unordered_map<std::string, NameRef> names;
   bool timing = false;
   std::vector<KRec> krecs;
+  std::vector<hipEvent_t> evpool;  // timing events, reused across timing passes
+  size_t evnext = 0;
   hipStream_t last_stream = nullptr;
 
   const Mat& lm() const { return tied ? embd : out_w; }
@@ -142,39 +145,46 @@ struct qdec_model {
 
 namespace {
 
-// ------------------------------------------------------------ launch helpers
-// Per-kernel timing: while a Timed scope is open with timing on, the next launch
-// goes through hipExtLaunchKernelGGL with the scope's start/stop events, which
-// take their timestamps from the dispatch itself.
-thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
+hipEvent_t pool_event(qdec_model* m) {
+  if (m->evnext == m->evpool.size()) {
+    hipEvent_t e;
+    hipck(hipEventCreateWithFlags(&e, hipEventDisableSystemFence), "hipEventCreate");
+    m->evpool.push_back(e);
+  }
+  return m->evpool[m->evnext++];
+}
 
+// ------------------------------------------------------------ launch helpers
 template <typename... KArgs, typename... Args>
 void qlaunch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStream_t st, Args... args) {
-  if (g_ev_start) {
-    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, st, g_ev_start, g_ev_stop, 0, args...);
-    g_ev_start = g_ev_stop = nullptr;
-  } else {
-    hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
-  }
+  hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
 }
+
+// Per-kernel timing: while timing is on, each launch is bracketed by two HIP
+// events recorded on its stream.  Events come from a pool created up front
+// (hipEventDisableSystemFence: no system-scope cache flush per record), so the
+// host keeps ahead of the GPU and launches stay back to back.
+hipEvent_t pool_event(qdec_model* m);
 
 struct Timed {
   qdec_model* m;
+  hipStream_t st;
   const char* cls;
   double bytes, flops;
   hipEvent_t a = nullptr, b = nullptr;
-  Timed(qdec_model* mm, hipStream_t, const char* c, double by, double fl) : m(mm), cls(c), bytes(by), flops(fl) {
+  Timed(qdec_model* mm, hipStream_t s, const char* c, double by, double fl) : m(mm), st(s), cls(c), bytes(by), flops(fl) {
     if (m && m->timing) {
-      hipck(hipEventCreate(&a), "hipEventCreate");
-      hipck(hipEventCreate(&b), "hipEventCreate");
-      g_ev_start = a;
-      g_ev_stop = b;
+      a = pool_event(m);
+      b = pool_event(m);
+      hipck(hipEventRecord(a, st), "hipEventRecord");
     }
   }
   ~Timed() noexcept(false) {
-    g_ev_start = g_ev_stop = nullptr;
     hipck(hipGetLastError(), cls);
-    if (a) m->krecs.push_back(KRec{cls, a, b, bytes, flops});
+    if (a) {
+      hipck(hipEventRecord(b, st), "hipEventRecord");
+      m->krecs.push_back(KRec{cls, a, b, bytes, flops});
+    }
   }
 };
 
@@ -198,9 +208,17 @@ void gemv_dispatch_ru(int ru, int mode, dim3 grid, size_t lds, hipStream_t st, c
   switch (ru) {
     case 0: gemv_dispatch_mode<QT, M, 4, 1>(mode, grid, lds, st, a); break;
     case 1: gemv_dispatch_mode<QT, M, 2, 2>(mode, grid, lds, st, a); break;
+#ifdef QDEC_EXPERIMENT
+    case 3: gemv_dispatch_mode<QT, M, 4, 2>(mode, grid, lds, st, a); break;
+    case 4: gemv_dispatch_mode<QT, M, 4, 4>(mode, grid, lds, st, a); break;
+    case 5: gemv_dispatch_mode<QT, M, 2, 8>(mode, grid, lds, st, a); break;
+    case 6: gemv_dispatch_mode<QT, M, 2, 1>(mode, grid, lds, st, a); break;
+#endif
     default: gemv_dispatch_mode<QT, M, 2, 4>(mode, grid, lds, st, a); break;
   }
 }
+
+int ru_rows(int ru) { return (ru == 0 || ru == 3 || ru == 4) ? 4 : 2; }
 
 template <int QT>
 void gemv_dispatch_m(int M, int ru, int mode, dim3 grid, size_t lds, hipStream_t st, const GemvArgs& a) {
@@ -227,12 +245,20 @@ void gemv(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, 
   if (per_row > kGemvLdsMax) throw HipError{"gemv: input row too long for LDS"};
   const bool pair = mode == kModePairSilu || mode == kModePairGelu;
   const int nunits = w.type == kQ8_0 ? 2 * w.nblk : (w.type == kQ4_0 ? w.nblk : kp / 4);
-  const int ru = nunits <= 64 ? 0 : (nunits <= 128 ? 1 : 2);
-  const int R = ru == 0 ? 4 : 2;
+  int ru = nunits <= 64 ? 0 : (nunits <= 128 ? 1 : 2);
+  int grid_cap = 1024;
+#ifdef QDEC_EXPERIMENT
+  {
+    const char* e = getenv(nunits <= 64 ? "QDEC_RU_S" : (nunits <= 128 ? "QDEC_RU_M" : "QDEC_RU_L"));
+    if (e) ru = atoi(e);
+    if (const char* g = getenv("QDEC_GRID_CAP")) grid_cap = atoi(g);
+  }
+#endif
+  const int R = ru_rows(ru);
   const int ngroups = pair ? w.rows / R : (w.rows + R - 1) / R;
   // waves stay resident and loop: about four workgroups per CU, so the input
   // staging of each workgroup is amortised over many row groups
-  dim3 grid(std::max(1, std::min((ngroups + 3) / 4, 1024)));
+  dim3 grid(std::max(1, std::min((ngroups + 3) / 4, grid_cap)));
   for (int r0 = 0; r0 < nrows; r0 += cap) {
     const int mr = std::min(cap, nrows - r0);
     int M = 1;
@@ -301,7 +327,7 @@ void attention_decode(qdec_model* m, hipStream_t st, int l, int B) {
   const float scale_log2 = (float)(1.0 / std::sqrt((double)hd) * 1.4426950408889634);
   AttnDecodeArgs a{m->qkv, m->nqkv, m->kc + l * m->kv_layer, m->vc + l * m->kv_layer, m->max_ctx, m->d_pos,
                    c.n_head, c.n_head_kv, layer_window(m, l), m->chunk, m->nchunk, L.q_norm, L.k_norm, c.rms_eps,
-                   L.global ? m->rope_g : m->rope_l, scale_log2, m->part_o, m->part_ml};
+                   L.global ? m->rope_g : m->rope_l, scale_log2, m->part_o, m->part_ml, m->counters, m->a};
   double kvbytes = 0;
   for (int s = 0; s < B; ++s) {
     int p = m->kvlen[s];
@@ -315,12 +341,6 @@ void attention_decode(qdec_model* m, hipStream_t st, int l, int B) {
     else if (hd == 128) attn_decode_hd<128>(G, grid, st, a);
     else attn_decode_hd<256>(G, grid, st, a);
   }
-  AttnCombineArgs cb{m->part_o, m->part_ml, m->d_pos, c.n_head, a.window, m->chunk, m->nchunk, m->a};
-  Timed tm(m, st, "attn_combine", (double)B * c.n_head * hd * 4 * 2, 0);
-  dim3 cgrid(c.n_head, B);
-  if (hd == 64) qlaunch(attn_combine_kernel<64>, cgrid, 64, 0, st, cb);
-  else if (hd == 128) qlaunch(attn_combine_kernel<128>, cgrid, 64, 0, st, cb);
-  else qlaunch(attn_combine_kernel<256>, cgrid, 64, 0, st, cb);
 }
 
 void attention_prefill(qdec_model* m, hipStream_t st, int l, int seq, int T, int pos0) {
@@ -578,10 +598,7 @@ void free_model(qdec_model* m) {
   if (m->cap_stream) (void)hipStreamDestroy(m->cap_stream);
   for (void* p : m->allocs) (void)hipFree(p);
   m->allocs.clear();
-  for (auto& r : m->krecs) {
-    (void)hipEventDestroy(r.a);
-    (void)hipEventDestroy(r.b);
-  }
+  for (hipEvent_t e : m->evpool) (void)hipEventDestroy(e);
   if (m->err_host) (void)hipHostFree(m->err_host);
   delete m;
 }
@@ -787,10 +804,11 @@ int load(const qdec_config* cfgp, const qdec_tensor* ts, int32_t n, int32_t max_
     m->a = m->dalloc<float>(T * m->qd);
     m->m = m->dalloc<float>(T * m->Fp);
     hipck(hipMemsetAsync(m->m, 0, T * m->Fp * 4, st), "memset");
-    {  // decode split over positions: enough chunks to fill the GPU at max length
+    {  // decode split over positions: enough chunks to fill the GPU at max
+       // length, at most kMaxChunks per (sequence, KV head)
       const double want = (double)max_ctx * c.n_head_kv * max_seqs / 2048.0;
       int ch = 32;
-      while (ch < want && ch < 1024) ch *= 2;
+      while ((ch < want || (max_ctx + ch - 1) / ch > kMaxChunks) && ch < (1 << 30)) ch *= 2;
       m->chunk = ch;
       m->nchunk = (max_ctx + ch - 1) / ch;
     }
@@ -801,6 +819,8 @@ int load(const qdec_config* cfgp, const qdec_tensor* ts, int32_t n, int32_t max_
     m->s_i = m->dalloc<int>((size_t)max_seqs * m->nvchunk);
     m->d_pos = m->dalloc<int>(64);
     m->d_tok = m->dalloc<int>(64);
+    m->counters = m->dalloc<int>((size_t)max_seqs * c.n_head_kv);
+    hipck(hipMemsetAsync(m->counters, 0, (size_t)max_seqs * c.n_head_kv * 4, st), "memset");
     m->d_params = m->dalloc<StepParams>(1);
     hipck(hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking), "hipStreamCreate");
     m->d_prompt = m->dalloc<int>(T);
@@ -1109,6 +1129,16 @@ int qdec_kernel_timing(qdec_model* m, int32_t enable, qdec_kstat* out, int32_t m
   g_err.clear();
   if (int rc = check_usable(m)) return rc;
   if (enable) {
+    try {
+      while (m->evpool.size() < (1u << 17)) {
+        hipEvent_t e;
+        hipck(hipEventCreateWithFlags(&e, hipEventDisableSystemFence), "hipEventCreate");
+        m->evpool.push_back(e);
+      }
+    } catch (const HipError& e) {
+      return fail_internal(m, m->last_stream, e.msg);
+    }
+    m->evnext = 0;
     m->timing = true;
     return QDEC_OK;
   }
@@ -1130,10 +1160,9 @@ int qdec_kernel_timing(qdec_model* m, int32_t enable, qdec_kstat* out, int32_t m
       it->total_ms += ms;
       it->bytes += r.bytes;
       it->flops += r.flops;
-      (void)hipEventDestroy(r.a);
-      (void)hipEventDestroy(r.b);
     }
     m->krecs.clear();
+    m->evnext = 0;
     int k = 0;
     for (; k < (int)agg.size() && k < max_out && out; ++k) out[k] = agg[k];
     if (n_out) *n_out = k;
