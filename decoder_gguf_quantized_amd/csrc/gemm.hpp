@@ -164,4 +164,145 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
   }
 }
 
+// Small-N variant: workgroup tile 32 tokens x 64 weight rows, BK = 128 (four
+// quant blocks per stage).  Each wave owns one of the stage's four blocks over
+// the whole 32 x 64 tile (two 32x32 accumulators), i.e. the four waves split K;
+// at the end the four partial tiles are summed through LDS in a fixed order
+// (deterministic).  Four times the workgroups of the 64 x 128 tile for the same
+// problem, for projections with few output rows (O and down at small hidden
+// sizes).  Not used for the gate/up pair mode.
+template <int QT, int MODE>
+__global__ __launch_bounds__(256, 1) void gemm_ksplit_kernel(GemmArgs a) {
+  constexpr int BM = 32, BN = 64, BK = 128;
+  // LDS k-major without padding; columns XOR-swizzled so that both the staging
+  // writes and the MFMA operand reads of a half-wave hit 32 distinct banks:
+  // X[t][k] at As[k][t ^ (k / 4)], W[n][k] at Bs[k][n ^ (8 * (k / 32))].
+  __shared__ float As[2][BK][BM];
+  __shared__ float Bs[2][BK][BN];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n0 = blockIdx.x * BN, t0 = blockIdx.y * BM;
+  const int kp = a.nblk * 32;
+  const int nstage = (a.nblk + 3) / 4;
+
+  // staging: X 32 rows x 128 k = 1024 float4 (4 per thread); W 64 rows x 4 blocks
+  // (thread -> row tid / 4, block tid % 4: one quant block, 32 weights)
+  float4 xa[4];
+  uint4 wq[2];
+  float4 wf[8];
+  float wd = 0.f;
+  const int brow = tid >> 2, bblk = tid & 3;
+  const bool brow_ok = n0 + brow < a.rows;
+
+  auto load = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 256 * i, row = idx >> 5, kq = idx & 31;
+      const int t = t0 + row, k = st * BK + 4 * kq;
+      xa[i] = (t < a.T && k < kp) ? *reinterpret_cast<const float4*>(a.x + (size_t)t * a.ldx + k)
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    const int kb = st * 4 + bblk;
+    if (brow_ok && kb < a.nblk) {
+      const size_t r = n0 + brow;
+      if constexpr (QT == kQ8_0) {
+        const uint4* p = reinterpret_cast<const uint4*>(a.qs + r * kp + kb * 32);
+        wq[0] = p[0];
+        wq[1] = p[1];
+        wd = load_half(a.d + r * a.nblk + kb);
+      } else if constexpr (QT == kQ4_0) {
+        wq[0] = *reinterpret_cast<const uint4*>(a.qs + (r * a.nblk + kb) * 16);
+        wd = load_half(a.d + r * a.nblk + kb);
+      } else {
+        const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.qs) + r * kp + kb * 32);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) wf[i] = p[i];
+      }
+    } else {
+      wq[0] = wq[1] = make_uint4(0, 0, 0, 0);
+      wd = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) wf[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 256 * i, row = idx >> 5, kq = idx & 31;
+      const int c = row ^ kq;
+      As[buf][4 * kq + 0][c] = xa[i].x;
+      As[buf][4 * kq + 1][c] = xa[i].y;
+      As[buf][4 * kq + 2][c] = xa[i].z;
+      As[buf][4 * kq + 3][c] = xa[i].w;
+    }
+    const int kk = bblk * 32, bc = brow ^ (8 * bblk);
+    if constexpr (QT == kQ8_0) {
+      const uint32_t w8[8] = {wq[0].x, wq[0].y, wq[0].z, wq[0].w, wq[1].x, wq[1].y, wq[1].z, wq[1].w};
+#pragma unroll
+      for (int i = 0; i < 32; ++i) Bs[buf][kk + i][bc] = wd * (float)(int8_t)(w8[i >> 2] >> (8 * (i & 3)));
+    } else if constexpr (QT == kQ4_0) {
+      const uint32_t w4[4] = {wq[0].x, wq[0].y, wq[0].z, wq[0].w};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t byte = (w4[i >> 2] >> (8 * (i & 3))) & 0xffu;
+        Bs[buf][kk + i][bc] = wd * (float)((int)(byte & 15u) - 8);
+        Bs[buf][kk + 16 + i][bc] = wd * (float)((int)(byte >> 4) - 8);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        Bs[buf][kk + 4 * i + 0][bc] = wf[i].x;
+        Bs[buf][kk + 4 * i + 1][bc] = wf[i].y;
+        Bs[buf][kk + 4 * i + 2][bc] = wf[i].z;
+        Bs[buf][kk + 4 * i + 3][bc] = wf[i].w;
+      }
+    }
+  };
+
+  f32x16 acc0, acc1;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0.f;
+  load(0);
+  store(0);
+  __syncthreads();
+  const int li = lane & 31, lk = lane >> 5;
+  for (int st = 0; st < nstage; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < nstage) load(st + 1);
+    const int kw = wave * 32;  // this wave's quant block within the stage
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      const int k = kw + 2 * p + lk;
+      const float av = As[buf][k][li ^ (k >> 2)];
+      const float b0 = Bs[buf][k][li ^ (8 * wave)];
+      const float b1 = Bs[buf][k][32 + (li ^ (8 * wave))];
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b0, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b1, acc1, 0, 0, 0);
+    }
+    if (st + 1 < nstage) store(buf ^ 1);
+    __syncthreads();
+  }
+  // sum the four waves' partial tiles in wave order (reusing the B buffers)
+  float* red = &Bs[0][0][0];  // 4 x [32][64] floats = 32 KB = sizeof(Bs) / 2
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int i = 8 * (r >> 2) + 4 * lk + (r & 3);
+    red[(wave * BM + i) * BN + li] = acc0[r];
+    red[(wave * BM + i) * BN + 32 + li] = acc1[r];
+  }
+  __syncthreads();
+  for (int e = tid; e < BM * BN; e += 256) {
+    const int i = e / BN, j = e % BN;
+    const float v = ((red[(0 * BM + i) * BN + j] + red[(1 * BM + i) * BN + j]) + red[(2 * BM + i) * BN + j]) +
+                    red[(3 * BM + i) * BN + j];
+    const int t = t0 + i, n = n0 + j;
+    if (t < a.T && n < a.rows) {
+      float* yr = a.y + (size_t)t * a.ldy;
+      if constexpr (MODE == kModeAdd) yr[n] += v;
+      else yr[n] = v;
+    }
+  }
+}
+
 }  // namespace qd

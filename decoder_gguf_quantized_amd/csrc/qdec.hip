@@ -284,10 +284,26 @@ void gemm_dispatch(int mode, dim3 grid, hipStream_t st, const GemmArgs& a) {
   }
 }
 
+template <int QT>
+void gemm_ksplit_dispatch(int mode, dim3 grid, hipStream_t st, const GemmArgs& a) {
+  if (mode == kModeAdd) qlaunch(gemm_ksplit_kernel<QT, kModeAdd>, grid, 256, 0, st, a);
+  else qlaunch(gemm_ksplit_kernel<QT, kModeStore>, grid, 256, 0, st, a);
+}
+
 void gemm(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, int T, float* y, int ldy, int mode) {
   GemmArgs a{w.qs, w.d, w.rows, w.nblk, x, ldx, T, y, ldy};
   dim3 grid((w.rows + 127) / 128, (T + 63) / 64);
   const bool pair = mode == kModePairSilu || mode == kModePairGelu;
+  // few 64 x 128 tiles for the CUs: switch to the K-split 32 x 64 tile
+  if (!pair && (size_t)grid.x * grid.y < 512 && w.nblk >= 8) {
+    dim3 g2((w.rows + 63) / 64, (T + 31) / 32);
+    const double bytes = w.gguf_bytes + (double)T * w.nblk * 32 * 4 + (double)T * w.rows * 4;
+    Timed tm(m, st, gemm_class(w.type), bytes, 2.0 * T * (double)w.rows * w.cols);
+    if (w.type == kQ8_0) gemm_ksplit_dispatch<kQ8_0>(mode, g2, st, a);
+    else if (w.type == kQ4_0) gemm_ksplit_dispatch<kQ4_0>(mode, g2, st, a);
+    else gemm_ksplit_dispatch<kF32>(mode, g2, st, a);
+    return;
+  }
   const double bytes = w.gguf_bytes + (double)T * w.nblk * 32 * 4 + (double)T * (pair ? w.rows / 2 : w.rows) * 4;
   Timed tm(m, st, gemm_class(w.type), bytes, 2.0 * T * (double)w.rows * w.cols);
   if (w.type == kQ8_0) gemm_dispatch<kQ8_0>(mode, grid, st, a);

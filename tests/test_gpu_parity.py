@@ -110,6 +110,10 @@ MATMUL_CASES = [
     (synth.T_Q4_0, 6144, 4096, 1), (synth.T_Q4_0, 130, 14336, 2), (synth.T_Q4_0, 512, 1408, 9),
     (synth.T_Q4_0, 333, 512, 70),
     (synth.T_F32, 1024, 256, 1), (synth.T_F32, 200, 352, 5), (synth.T_F32, 129, 96, 65),
+    # prefill tiles: >= 512 tiles of 64 x 128 (ragged rows and tokens) take the
+    # wide tile; fewer take the K-split 32 x 64 tile (partial last K stage)
+    (synth.T_Q8_0, 4100, 320, 1030), (synth.T_Q4_0, 4224, 288, 1000),
+    (synth.T_Q4_0, 200, 720, 40), (synth.T_F32, 96, 300, 33), (synth.T_Q8_0, 1030, 1000, 97),
 ]
 
 
