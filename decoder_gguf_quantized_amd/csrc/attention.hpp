@@ -15,6 +15,8 @@
 // row as one contiguous, coalesced segment.  Dot products finish with a DPP
 // tree inside the group.
 #pragma once
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace qd {
@@ -33,7 +35,8 @@ struct AttnDecodeArgs {
   const float* q_norm;  // [hd] or null (no QK-norm)
   const float* k_norm;
   float eps;
-  const float2* rope;   // [ctx][hd/2] (cos, sin) of f32(pos) * inv_freq[i]
+  const float2* rope;   // [B][hd/2] (cos, sin) of f32(pos[s]) * inv_freq[i]: each sequence's
+                        // row of the layer's RoPE table, copied at step start
   float scale_log2;     // hd^-1/2 * log2(e)
   float* part_o;        // [B][nq][nchunk][hd], unnormalised partial outputs
   float* part_ml;       // [B][nq][nchunk][2]: running max (log2 domain), sum
@@ -61,16 +64,16 @@ QD_DEV void attn_key_range(int p, int window, int& lo, int& hi) {
 // held as 8 dims per lane over a group of LG = hd/8 lanes.  Dim d pairs with
 // d + hd/2, which lives in lane li ^ (LG/2) at the same slot.
 template <int LG>
-QD_DEV void norm_rope_group(float (&v)[8], const float* nw, float eps, int hd, int li, const float (&c)[8],
-                            const float (&sn)[8]) {
-  if (nw) {
+QD_DEV void norm_rope_group(float (&v)[8], bool norm, const float (&nw)[8], float eps, int hd, int li,
+                            const float (&c)[8], const float (&sn)[8]) {
+  if (norm) {
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
     ss = group_sum<LG>(ss);
     const float scale = 1.0f / sqrtf(ss / (float)hd + eps);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = v[e] * scale * nw[8 * li + e];
+    for (int e = 0; e < 8; ++e) v[e] = v[e] * scale * nw[e];
   }
   const bool first_half = li < LG / 2;
 #pragma unroll
@@ -87,28 +90,36 @@ QD_DEV void norm_rope_group(float (&v)[8], const float* nw, float eps, int hd, i
 // (m, l, o) per query head; the workgroup that finishes last among the chunks
 // of its (sequence, KV head) merges them (a counter, no workgroup waits):
 //   O = sum_c o_c 2^(m_c - M) / sum_c l_c 2^(m_c - M),  M = max_c m_c.
+//
+// Latency: the kernel is a short chain of dependent memory round trips, so
+// every request that does not need the new position goes out before it
+// arrives: the RoPE row (copied per sequence at step start), the raw queries
+// and new key/value, and on full-causal layers the chunk's first keys and
+// values (a chunk's addresses do not depend on the position; keys past it are
+// masked).  The key loop keeps two position pairs per stream in flight, and the
+// merge requests every chunk's (m, l) together with the outputs' values.
 template <int HD, int G>
 __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
   constexpr int LG = HD / 8;      // lanes per position
   constexpr int NG = 256 / LG;    // position streams per workgroup
+  constexpr int E = (G * HD + 255) / 256;  // merged outputs per thread
+  constexpr int CB = 64 / E;               // chunks per merge request batch (a multiple of 8)
   __shared__ float sm_o[NG][G][HD];
   __shared__ float sm_m[NG][G], sm_l[NG][G];
   __shared__ float sm_pm[G][kMaxChunks], sm_pl[G][kMaxChunks];
   __shared__ int sm_last;
 
   const int c = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
-  const int p = a.pos[s];
-  int lo, hi;
-  attn_key_range(p, a.window, lo, hi);
-  const int c_lo = lo / a.chunk, c_hi = hi / a.chunk;
-  if (c < c_lo || c > c_hi) return;
-  const int start = max(lo, c * a.chunk), end = min(hi + 1, (c + 1) * a.chunk);
-
   const int tid = threadIdx.x, gi = tid / LG, li = tid % LG;
   const float* row = a.qkv + (size_t)s * a.ldqkv;
+  const size_t head_base = ((size_t)s * a.nkv + g) * a.ctx;
+  const int cb = c * a.chunk;
+  const bool spec = a.window == 0;
+
+  const int p = a.pos[s];
   float cs[8], sn[8];
   {
-    const float2* rt = a.rope + (size_t)p * (HD / 2) + (8 * li) % (HD / 2);
+    const float2* rt = a.rope + (size_t)s * (HD / 2) + (8 * li) % (HD / 2);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float2 t = rt[e];
@@ -116,86 +127,124 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
       sn[e] = t.y;
     }
   }
-  float q[G][8], o[G][8], m[G], l[G];
+  float q[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const float4* qp = reinterpret_cast<const float4*>(row + (size_t)(g * G + h) * HD + li * 8);
-    float4 q0 = qp[0], q1 = qp[1];
-    float v[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-    norm_rope_group<LG>(v, a.q_norm, a.eps, HD, li, cs, sn);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) q[h][e] = v[e] * a.scale_log2;
-    m[h] = -INFINITY;
-    l[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
+    const float4 q0 = qp[0], q1 = qp[1];
+    q[h][0] = q0.x; q[h][1] = q0.y; q[h][2] = q0.z; q[h][3] = q0.w;
+    q[h][4] = q1.x; q[h][5] = q1.y; q[h][6] = q1.z; q[h][7] = q1.w;
   }
-  const size_t head_base = ((size_t)s * a.nkv + g) * a.ctx;
+  // the lane's 8 dims of the QK-norm gains (requested with the rest)
+  const bool qkn = a.q_norm != nullptr;
+  float wq[8], wk[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) wq[e] = wk[e] = 1.f;
+  if (qkn) {
+    const float4* qw = reinterpret_cast<const float4*>(a.q_norm + li * 8);
+    const float4* kw = reinterpret_cast<const float4*>(a.k_norm + li * 8);
+    const float4 q0 = qw[0], q1 = qw[1], k0 = kw[0], k1 = kw[1];
+    wq[0] = q0.x; wq[1] = q0.y; wq[2] = q0.z; wq[3] = q0.w; wq[4] = q1.x; wq[5] = q1.y; wq[6] = q1.z; wq[7] = q1.w;
+    wk[0] = k0.x; wk[1] = k0.y; wk[2] = k0.z; wk[3] = k0.w; wk[4] = k1.x; wk[5] = k1.y; wk[6] = k1.z; wk[7] = k1.w;
+  }
   float kn[8], vn[8];
-  const bool has_new = c == c_hi;
-  if (has_new) {
+  {
     const float4* kp = reinterpret_cast<const float4*>(row + (size_t)(a.nq + g) * HD + li * 8);
     const float4* vp = reinterpret_cast<const float4*>(row + (size_t)(a.nq + a.nkv + g) * HD + li * 8);
-    float4 k0 = kp[0], k1 = kp[1], v0 = vp[0], v1 = vp[1];
-    float kv8[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
-    norm_rope_group<LG>(kv8, a.k_norm, a.eps, HD, li, cs, sn);
+    const float4 k0 = kp[0], k1 = kp[1], v0 = vp[0], v1 = vp[1];
+    kn[0] = k0.x; kn[1] = k0.y; kn[2] = k0.z; kn[3] = k0.w; kn[4] = k1.x; kn[5] = k1.y; kn[6] = k1.z; kn[7] = k1.w;
+    vn[0] = v0.x; vn[1] = v0.y; vn[2] = v0.z; vn[3] = v0.w; vn[4] = v1.x; vn[5] = v1.y; vn[6] = v1.z; vn[7] = v1.w;
+  }
+  // keys/values of positions j0 and j0 + NG (addresses clamped into the cache;
+  // positions outside [start, end) are masked when accumulated)
+  auto fetch_pair = [&](int j0, float (&k)[2][8], float (&v)[2][8]) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) kn[e] = kv8[e];
-    vn[0] = v0.x; vn[1] = v0.y; vn[2] = v0.z; vn[3] = v0.w;
-    vn[4] = v1.x; vn[5] = v1.y; vn[6] = v1.z; vn[7] = v1.w;
+    for (int t = 0; t < 2; ++t) {
+      const int jj = min(j0 + t * NG, a.ctx - 1);
+      const float4* kp = reinterpret_cast<const float4*>(a.kc + (head_base + jj) * HD + li * 8);
+      const float4* vp = reinterpret_cast<const float4*>(a.vc + (head_base + jj) * HD + li * 8);
+      const float4 k0 = kp[0], k1 = kp[1], v0 = vp[0], v1 = vp[1];
+      k[t][0] = k0.x; k[t][1] = k0.y; k[t][2] = k0.z; k[t][3] = k0.w;
+      k[t][4] = k1.x; k[t][5] = k1.y; k[t][6] = k1.z; k[t][7] = k1.w;
+      v[t][0] = v0.x; v[t][1] = v0.y; v[t][2] = v0.z; v[t][3] = v0.w;
+      v[t][4] = v1.x; v[t][5] = v1.y; v[t][6] = v1.z; v[t][7] = v1.w;
+    }
+  };
+  float ka[2][8], va[2][8], kb[2][8], vb[2][8];
+  if (spec) fetch_pair(cb + gi, ka, va);
+
+  int lo, hi;
+  attn_key_range(p, a.window, lo, hi);
+  const int c_lo = lo / a.chunk, c_hi = hi / a.chunk;
+  if (c < c_lo || c > c_hi) return;
+  const int start = max(lo, cb), end = min(hi + 1, cb + a.chunk);
+  // first position pair of the chunk's walk (windowed layers skip whole pairs
+  // below the window)
+  const int jb0 = spec ? cb : cb + ((start - cb) / (2 * NG)) * (2 * NG);
+  if (!spec) fetch_pair(jb0 + gi, ka, va);
+
+  float o[G][8], m[G], l[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    norm_rope_group<LG>(q[h], qkn, wq, a.eps, HD, li, cs, sn);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      q[h][e] *= a.scale_log2;
+      o[h][e] = 0.f;
+    }
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+  }
+  const bool has_new = c == c_hi;
+  if (has_new) {
+    norm_rope_group<LG>(kn, qkn, wk, a.eps, HD, li, cs, sn);
     if (gi == 0) {
       float4* kd = reinterpret_cast<float4*>(a.kc + (head_base + p) * HD + li * 8);
       float4* vd = reinterpret_cast<float4*>(a.vc + (head_base + p) * HD + li * 8);
       kd[0] = make_float4(kn[0], kn[1], kn[2], kn[3]);
       kd[1] = make_float4(kn[4], kn[5], kn[6], kn[7]);
-      vd[0] = v0;
-      vd[1] = v1;
+      vd[0] = make_float4(vn[0], vn[1], vn[2], vn[3]);
+      vd[1] = make_float4(vn[4], vn[5], vn[6], vn[7]);
     }
   }
-  // two positions per stream per iteration: both rows are requested before use
-  auto fetch = [&](int j, float (&k)[8], float (&v)[8]) {
-    if (has_new && j == p) {
+  // online softmax over one position; masked positions leave the state as is
+  // (selects, no branch: every lane of a stream group takes the same path)
+  auto accumulate = [&](int j, const float (&kc)[8], const float (&vc)[8]) {
+    const bool valid = j >= start && j < end;
+    const bool is_new = has_new && j == p;  // the cache row is written above; use the registers
+    float k[8], v[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        k[e] = kn[e];
-        v[e] = vn[e];
-      }
-    } else {
-      const float4* kp = reinterpret_cast<const float4*>(a.kc + (head_base + j) * HD + li * 8);
-      const float4* vp = reinterpret_cast<const float4*>(a.vc + (head_base + j) * HD + li * 8);
-      const float4 k0 = kp[0], k1 = kp[1], v0 = vp[0], v1 = vp[1];
-      k[0] = k0.x; k[1] = k0.y; k[2] = k0.z; k[3] = k0.w; k[4] = k1.x; k[5] = k1.y; k[6] = k1.z; k[7] = k1.w;
-      v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w; v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+    for (int e = 0; e < 8; ++e) {
+      k[e] = is_new ? kn[e] : kc[e];
+      v[e] = is_new ? vn[e] : vc[e];
     }
-  };
-  auto accumulate = [&](const float (&k)[8], const float (&v)[8]) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float dot = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) dot += q[h][e] * k[e];
       const float sc = group_sum<LG>(dot);
-      const float mn = fmaxf(m[h], sc);
-      const float corr = exp2f(m[h] - mn);
-      const float pr = exp2f(sc - mn);
+      const float mn = valid ? fmaxf(m[h], sc) : m[h];
+      const float corr = valid ? exp2f(m[h] - mn) : 1.f;
+      const float pr = valid ? exp2f(sc - mn) : 0.f;
       l[h] = l[h] * corr + pr;
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[h][e] = o[h][e] * corr + pr * v[e];
       m[h] = mn;
     }
   };
-  int j = start + gi;
-  for (; j + NG < end; j += 2 * NG) {
-    float k0[8], v0[8], k1[8], v1[8];
-    fetch(j, k0, v0);
-    fetch(j + NG, k1, v1);
-    accumulate(k0, v0);
-    accumulate(k1, v1);
-  }
-  if (j < end) {
-    float k0[8], v0[8];
-    fetch(j, k0, v0);
-    accumulate(k0, v0);
+  // walk of the chunk in pairs of positions, two pairs in flight (wave-uniform
+  // trip count: jb and end are the same for every lane)
+  for (int jb = jb0; jb < end; jb += 4 * NG) {
+    const bool more_b = jb + 2 * NG < end;
+    if (more_b) fetch_pair(jb + 2 * NG + gi, kb, vb);
+    accumulate(jb + gi, ka[0], va[0]);
+    accumulate(jb + gi + NG, ka[1], va[1]);
+    if (!more_b) break;
+    const bool more_a = jb + 4 * NG < end;
+    if (more_a) fetch_pair(jb + 4 * NG + gi, ka, va);
+    accumulate(jb + 2 * NG + gi, kb[0], vb[0]);
+    accumulate(jb + 3 * NG + gi, kb[1], vb[1]);
   }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -235,37 +284,83 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
   }
   __syncthreads();
   if (!sm_last) return;
-  // merge: (m, l) of every chunk into LDS, then each output element requests its
-  // values of all chunks at once (one round trip) and sums them in chunk order
+  // merge.  Thread output e is element tid + 256 e of the group's G x HD block.
+  // Every chunk's (m, l) is requested first (at most NML pairs per thread),
+  // then the thread's values of CB chunks per output; loads run at clamped
+  // chunk indices (no predicates) and chunks past the last are masked in the
+  // sums, so up to CB chunks cost one round trip.  Sums run in chunk order.
+  constexpr int NML = (G * kMaxChunks + 255) / 256;
   const int nact = c_hi - c_lo + 1;  // <= kMaxChunks (the launcher sizes chunks so)
-  for (int i = tid; i < G * nact; i += 256) {
-    const int h = i / nact, cc = i % nact;
-    const size_t pi = ((size_t)s * a.nq + g * G + h) * a.nchunk + c_lo + cc;
-    sm_pm[h][cc] = load_coherent(a.part_ml + pi * 2);
-    sm_pl[h][cc] = load_coherent(a.part_ml + pi * 2 + 1);
+  const size_t pbase = ((size_t)s * a.nq + g * G) * a.nchunk + c_lo;
+  float mlm[NML], mll[NML];
+#pragma unroll
+  for (int t = 0; t < NML; ++t) {
+    const int i = min(tid + 256 * t, G * nact - 1);
+    const size_t pi = pbase + (size_t)(i / nact) * a.nchunk + i % nact;
+    mlm[t] = load_coherent(a.part_ml + pi * 2);
+    mll[t] = load_coherent(a.part_ml + pi * 2 + 1);
   }
-  __syncthreads();
-  for (int idx = tid; idx < G * HD; idx += 256) {
-    const int h = idx / HD, dd = idx % HD;
-    const float* po = a.part_o + (((size_t)s * a.nq + g * G + h) * a.nchunk + c_lo) * HD + dd;
-    float M = -INFINITY;
-    for (int cc = 0; cc < nact; ++cc) M = fmaxf(M, sm_pm[h][cc]);
-    float L = 0.f, O = 0.f;
-    for (int c0 = 0; c0 < nact; c0 += 16) {  // 16 chunks' values requested per round trip
-      float ov[16];
+  int hh[E];
+  const float* po[E];
 #pragma unroll
-      for (int cc = 0; cc < 16; ++cc) ov[cc] = c0 + cc < nact ? load_coherent(po + (size_t)(c0 + cc) * HD) : 0.f;
+  for (int e = 0; e < E; ++e) {
+    const int idx = min(tid + 256 * e, G * HD - 1);
+    hh[e] = idx / HD;
+    po[e] = a.part_o + (pbase + (size_t)hh[e] * a.nchunk) * HD + idx % HD;
+  }
+  float M[E], L[E], O[E];
 #pragma unroll
-      for (int cc = 0; cc < 16; ++cc) {
+  for (int e = 0; e < E; ++e) {
+    M[e] = -INFINITY;
+    L[e] = 0.f;
+    O[e] = 0.f;
+  }
+  // one batch of CB chunks; the first is straight-line code after the (m, l)
+  // requests so that nothing waits between them
+  auto batch = [&](int c0, auto FIRST) {
+    float ov[E][CB];
+#pragma unroll
+    for (int c8 = 0; c8 < CB; c8 += 8) {
+      if (c0 + c8 < nact) {  // whole groups of 8 past the last chunk are skipped (uniform)
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+#pragma unroll
+          for (int cc = c8; cc < c8 + 8; ++cc) ov[e][cc] = load_coherent(po[e] + (size_t)min(c0 + cc, nact - 1) * HD);
+      }
+    }
+    if constexpr (decltype(FIRST)::value) {
+#pragma unroll
+      for (int t = 0; t < NML; ++t) {
+        const int i = tid + 256 * t;
+        if (i < G * nact) {
+          sm_pm[i / nact][i % nact] = mlm[t];
+          sm_pl[i / nact][i % nact] = mll[t];
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        for (int cc = 0; cc < nact; ++cc) M[e] = fmaxf(M[e], sm_pm[hh[e]][cc]);
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+#pragma unroll
+      for (int cc = 0; cc < CB; ++cc) {
         if (c0 + cc < nact) {
-          const float mc = sm_pm[h][c0 + cc];
-          const float w = mc == -INFINITY ? 0.f : exp2f(mc - M);
-          L += sm_pl[h][c0 + cc] * w;
-          O += ov[cc] * w;
+          const float mc = sm_pm[hh[e]][c0 + cc];
+          const float w = mc == -INFINITY ? 0.f : exp2f(mc - M[e]);
+          L[e] += sm_pl[hh[e]][c0 + cc] * w;
+          O[e] += ov[e][cc] * w;
         }
       }
     }
-    a.out[(size_t)s * a.nq * HD + (size_t)(g * G + h) * HD + dd] = O / L;
+  };
+  batch(0, std::true_type{});
+  for (int c0 = CB; c0 < nact; c0 += CB) batch(c0, std::false_type{});
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int idx = tid + 256 * e;
+    if (idx < G * HD) a.out[(size_t)s * a.nq * HD + (size_t)g * G * HD + idx] = O[e] / L[e];
   }
   if (tid == 0) __hip_atomic_store(a.counter + s * a.nkv + g, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

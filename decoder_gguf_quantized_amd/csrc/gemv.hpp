@@ -23,6 +23,8 @@
 //     is folded into the block as -8 * sum(x over the block), so the per-weight
 //     cost is one conversion and one FMA.
 #pragma once
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace qd {
@@ -80,59 +82,67 @@ QD_DEV float dot16_q8(uint4 w, const float4& a, const float4& b, const float4& c
 template <int QT>
 constexpr int unit_floats() { return QT == kQ8_0 ? 16 : (QT == kQ4_0 ? 32 : 4); }
 
-// Load the input rows into LDS, optionally RMSNorm-ed with gain norm_w:
-// x'[mi][k] = x[mi][k] * rsqrt(mean_k x^2 + eps) * w[k].  Rows mi >= a.m are zero.
+// Load the input rows into LDS, times the RMSNorm gain when the prologue norm is
+// on, and return each row's norm scale rsqrt(mean_k x^2 + eps) (1 without norm).
+// The scale is a per-row scalar, so it is applied to the finished dot products
+// (sum_k W[n][k] x[k] s w[k] = s * sum_k W[n][k] (x[k] w[k])); the staging is
+// then one pass over x, with up to 8 float4 loads per thread in flight (no
+// dependent round trip per element).  Rows mi >= a.m are zero.
 // Layout: unit-transposed float4s, xs4[(mi * NV + i) * NU + u] holds floats
 // 4i..4i+3 of unit u (NV float4 per unit, NU units per row).  A lane owns one
 // unit, so for each slot i consecutive lanes read consecutive float4s: no bank
 // conflicts (the natural layout puts every lane's unit 64 or 128 bytes apart,
 // which lands all lanes on a handful of banks).
 template <int QT, int M>
-QD_DEV void gemv_stage_x(const GemvArgs& a, float4* xs4, int kp) {
+QD_DEV void gemv_stage_x(const GemvArgs& a, float4* xs4, int kp, float (&scale)[M]) {
   constexpr int US = unit_floats<QT>(), NV = US / 4;
-  const int NU = kp / US;
+  constexpr int JB = M >= 8 ? 1 : 8 / M;  // k positions per thread per batch
+  const int NU = kp / US, NK4 = kp / 4;
   __shared__ float red[4][M];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float scale[M];
+  const bool norm = a.norm_w != nullptr;
+  const float4* x4 = reinterpret_cast<const float4*>(a.x);
+  const float4* w4 = reinterpret_cast<const float4*>(a.norm_w);
+  const int ldx4 = a.ldx / 4;
+  float ss[M];
 #pragma unroll
-  for (int mi = 0; mi < M; ++mi) scale[mi] = 1.f;
-  if (a.norm_w) {
+  for (int mi = 0; mi < M; ++mi) ss[mi] = 0.f;
+  for (int k0 = tid; k0 < NK4; k0 += 256 * JB) {
+    float4 xv[JB][M], wv[JB];
 #pragma unroll
-    for (int mi = 0; mi < M; ++mi) {
-      float ss = 0.f;
-      if (mi < a.m)
-        for (int k = 4 * tid; k < kp; k += 1024) {
-          const float4 v = *reinterpret_cast<const float4*>(a.x + (size_t)mi * a.ldx + k);
-          ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-        }
-      ss = wave_sum(ss);
-      if (lane == 0) red[wave][mi] = ss;
+    for (int j = 0; j < JB; ++j) {
+      const int k4 = k0 + 256 * j;
+      const bool ok = k4 < NK4;
+      wv[j] = (ok && norm) ? w4[k4] : make_float4(1.f, 1.f, 1.f, 1.f);
+#pragma unroll
+      for (int mi = 0; mi < M; ++mi)
+        xv[j][mi] = (ok && mi < a.m) ? x4[(size_t)mi * ldx4 + k4] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    __syncthreads();
 #pragma unroll
-    for (int mi = 0; mi < M; ++mi) {
-      float ss = red[0][mi] + red[1][mi] + red[2][mi] + red[3][mi];
-      scale[mi] = 1.0f / sqrtf(ss / (float)kp + a.eps);
-    }
-  }
+    for (int j = 0; j < JB; ++j) {
+      const int k4 = k0 + 256 * j;
+      if (k4 < NK4) {
+        const int slot = (k4 % NV) * NU + k4 / NV;
 #pragma unroll
-  for (int mi = 0; mi < M; ++mi) {
-    for (int k = 4 * tid; k < kp; k += 1024) {
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (mi < a.m) {
-        v = *reinterpret_cast<const float4*>(a.x + (size_t)mi * a.ldx + k);
-        if (a.norm_w) {
-          const float4 w = *reinterpret_cast<const float4*>(a.norm_w + k);
-          v.x = v.x * scale[mi] * w.x;
-          v.y = v.y * scale[mi] * w.y;
-          v.z = v.z * scale[mi] * w.z;
-          v.w = v.w * scale[mi] * w.w;
+        for (int mi = 0; mi < M; ++mi) {
+          const float4 v = xv[j][mi], w = wv[j];
+          ss[mi] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+          xs4[mi * NK4 + slot] = make_float4(v.x * w.x, v.y * w.y, v.z * w.z, v.w * w.w);
         }
       }
-      const int u = k / US, i = (k % US) / 4;
-      xs4[(mi * NV + i) * NU + u] = v;
     }
   }
+  if (norm) {
+#pragma unroll
+    for (int mi = 0; mi < M; ++mi) {
+      const float t = wave_sum(ss[mi]);
+      if (lane == 0) red[wave][mi] = t;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int mi = 0; mi < M; ++mi)
+    scale[mi] = norm ? 1.0f / sqrtf((red[0][mi] + red[1][mi] + red[2][mi] + red[3][mi]) / (float)kp + a.eps) : 1.f;
 }
 
 // Weights of one row group held in registers between load and use.
@@ -242,19 +252,16 @@ QD_DEV void gemv_compute(const float4* xs4, const float* xsum, int kp, int nblk,
   }
 }
 
-// R rows per wave, U 16-byte units per lane in flight per row, M input rows.
-// Each wave walks its (row group, unit block) tiles with a two-deep register
-// pipeline: the loads of tile t+1 are issued before tile t is computed, so the
-// memory pipe stays busy through the arithmetic, the lane reduction and the
-// store.  The first tile is requested before the input rows are staged.
+// Finish row group `grp`: reduce each accumulator over the 64 lanes, apply the
+// input row's norm scale, and let lane 0 write with the mode's epilogue.
 template <int QT, int M, int MODE, int R, int U>
-QD_DEV void gemv_store(const GemvArgs& a, int grp, int lane, float (&acc)[R][M]) {
+QD_DEV void gemv_store(const GemvArgs& a, int grp, int lane, const float (&scale)[M], float (&acc)[R][M]) {
   constexpr bool kPair = MODE == kModePairSilu || MODE == kModePairGelu;
 #pragma unroll
   for (int mi = 0; mi < M; ++mi) {
     float sv[R];
 #pragma unroll
-    for (int i = 0; i < R; ++i) sv[i] = wave_sum(acc[i][mi]);
+    for (int i = 0; i < R; ++i) sv[i] = wave_sum(acc[i][mi]) * scale[mi];
     if (lane == 0 && mi < a.m) {
       float* yr = (a.y_ind ? *a.y_ind + a.y_off : a.y) + (size_t)mi * a.ldy;
 #pragma unroll
@@ -278,15 +285,28 @@ QD_DEV void gemv_store(const GemvArgs& a, int grp, int lane, float (&acc)[R][M])
   }
 }
 
+// Register sets of the weight pipeline: with NS sets, NS - 1 tiles are in
+// flight while one is computed.  Three sets for the small tiles (R * U <= 4,
+// 20 VGPRs per set for the quantized types), two for the 8-unit tiles.
+#ifndef QDEC_GEMV_NS
+template <int R, int U, int M>
+constexpr int gemv_sets() { return (R * U <= 4 && M <= 4) ? 3 : 2; }
+#else
+template <int R, int U, int M>
+constexpr int gemv_sets() { return QDEC_GEMV_NS; }
+#endif
+
 // R rows per wave, U 16-byte units per lane in flight per row, M input rows.
-// Each wave walks its (row group, unit block) tiles with a two-deep register
-// pipeline (two register sets used alternately): the loads of tile t+1 are
-// issued before tile t is computed, so the memory pipe stays busy through the
-// arithmetic, the lane reduction and the store.  The first tile is requested
-// before the input rows are staged.  Row indices are wave-uniform (scalar
-// registers), so every load is a scalar base plus a 32-bit lane offset.
+// Each wave walks its (row group, unit block) tiles in order through a ring of
+// NS register sets: before tile t is computed, the loads of tile t + NS - 1 are
+// issued into the set that tile t - 1 used, so NS - 1 tiles stay in flight
+// through the arithmetic, the lane reduction and the store.  The first NS - 1
+// tiles are requested before the input rows are staged.  Tile indices are
+// wave-uniform (scalar registers), so every load is a scalar base plus a 32-bit
+// lane offset.
 template <int QT, int M, int MODE, int R, int U>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
+  constexpr int NS = gemv_sets<R, U, M>();
   extern __shared__ float4 xs4[];
   const int kp = a.nblk * 32;
   float* xsum = reinterpret_cast<float*>(xs4 + M * kp / 4);  // Q4_0 only: [M][nblk] block sums of x
@@ -298,16 +318,31 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   const int ngroups = kPair ? a.rows / R : (a.rows + R - 1) / R;
   const int tpg = (nunits + 64 * U - 1) / (64 * U);  // tiles per row group
 
-  WRegs<QT, R, U> w0, w1;
-  int r[R];
-  int grp = gwave, tb = 0;
-  if (grp < ngroups) {
-    group_rows<R, kPair>(grp, a.rows, r);
-    gemv_load<QT, R, U>(a, r, 0, lane, nunits, w0);
-  }
+  // Sets are always named by compile-time indices (integral_constant
+  // arguments), so they stay in registers whether or not loops unroll.
+  WRegs<QT, R, U> ws[NS];
+  int tg[NS], tt[NS];  // (row group, tile within the group) held by each set
+  int g = gwave, t = 0;  // next tile to request
+  // request the tile (g, t) into set S and advance (g, t)
+  auto request = [&](auto S) {
+    constexpr int s = decltype(S)::value;
+    tg[s] = g;
+    tt[s] = t;
+    if (g < ngroups) {
+      int r[R];
+      group_rows<R, kPair>(g, a.rows, r);
+      gemv_load<QT, R, U>(a, r, t * 64 * U, lane, nunits, ws[s]);
+      if (++t == tpg) {
+        t = 0;
+        g += nwaves;
+      }
+    }
+  };
+  request(std::integral_constant<int, 0>{});
+  if constexpr (NS > 2) request(std::integral_constant<int, 1>{});
 
-  gemv_stage_x<QT, M>(a, xs4, kp);
-  __syncthreads();
+  float scale[M];
+  gemv_stage_x<QT, M>(a, xs4, kp, scale);  // ends with a barrier
   if constexpr (QT == kQ4_0) {
     for (int i = threadIdx.x; i < M * a.nblk; i += 256) {
       const int mi = i / a.nblk, u = i % a.nblk;
@@ -328,45 +363,23 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
 #pragma unroll
     for (int mi = 0; mi < M; ++mi) acc[i][mi] = 0.f;
 
-  // advance (grp, tb) to the wave's next tile; false when the wave is done
-  auto next_tile = [&](int& g, int& t) {
-    if (++t == tpg) {
-      t = 0;
-      g += nwaves;
+  // one ring step on set S: refill the set computed last, then compute S
+  bool done = false;
+  auto step = [&](auto S) {
+    constexpr int s = decltype(S)::value;
+    if (done) return;
+    request(std::integral_constant<int, (s + NS - 1) % NS>{});
+    if (tg[s] >= ngroups) {
+      done = true;
+      return;
     }
-    return g < ngroups;
+    gemv_compute<QT, R, U, M>(xs4, xsum, kp, a.nblk, tt[s] * 64 * U, lane, nunits, ws[s], acc);
+    if (tt[s] == tpg - 1) gemv_store<QT, M, MODE, R, U>(a, tg[s], lane, scale, acc);
   };
-  while (grp < ngroups) {
-    // stage A: compute from w0 while w1 loads
-    {
-      int g1 = grp, t1 = tb;
-      const bool more = next_tile(g1, t1);
-      int r1[R];
-      if (more) {
-        group_rows<R, kPair>(g1, a.rows, r1);
-        gemv_load<QT, R, U>(a, r1, t1 * 64 * U, lane, nunits, w1);
-      }
-      gemv_compute<QT, R, U, M>(xs4, xsum, kp, a.nblk, tb * 64 * U, lane, nunits, w0, acc);
-      if (tb == tpg - 1) gemv_store<QT, M, MODE, R, U>(a, grp, lane, acc);
-      if (!more) break;
-      grp = g1;
-      tb = t1;
-    }
-    // stage B: compute from w1 while w0 loads
-    {
-      int g0 = grp, t0 = tb;
-      const bool more = next_tile(g0, t0);
-      int r0[R];
-      if (more) {
-        group_rows<R, kPair>(g0, a.rows, r0);
-        gemv_load<QT, R, U>(a, r0, t0 * 64 * U, lane, nunits, w0);
-      }
-      gemv_compute<QT, R, U, M>(xs4, xsum, kp, a.nblk, tb * 64 * U, lane, nunits, w1, acc);
-      if (tb == tpg - 1) gemv_store<QT, M, MODE, R, U>(a, grp, lane, acc);
-      if (!more) break;
-      grp = g0;
-      tb = t0;
-    }
+  while (!done) {
+    step(std::integral_constant<int, 0>{});
+    step(std::integral_constant<int, 1>{});
+    if constexpr (NS > 2) step(std::integral_constant<int, 2>{});
   }
 }
 

@@ -50,8 +50,21 @@ __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
     if (threadIdx.x == 0 && a.err) *a.err = 1;
     tok = tok < 0 ? 0 : a.vocab - 1;
   }
-  for (int k = threadIdx.x; k < a.hidden; k += 256)
-    a.out[(size_t)t * a.ldo + k] = weight_at(a.w, (size_t)tok, k);
+  // eight elements per thread per batch: their loads are all issued before the
+  // first store, so a row costs one memory round trip per 2048 elements
+  for (int k0 = threadIdx.x; k0 < a.hidden; k0 += 256 * 8) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int k = k0 + 256 * i;
+      v[i] = k < a.hidden ? weight_at(a.w, (size_t)tok, k) : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int k = k0 + 256 * i;
+      if (k < a.hidden) a.out[(size_t)t * a.ldo + k] = v[i];
+    }
+  }
 }
 
 // ------------------------------------------------------------ RMSNorm rows
@@ -323,19 +336,34 @@ struct StepArgs {
   int* err;
   StepParams params;
   StepParams* d_params;
+  const float2* rope_g;  // RoPE tables [ctx][half] (full-attention and sliding-window layers)
+  const float2* rope_l;
+  float2* rope_cur;      // [2][max_seqs][half]: each sequence's rows at its new position
+  int half, max_seqs;
 };
 
-__global__ __launch_bounds__(64) void step_begin_kernel(StepArgs a) {
+// Per-step values of a decode step that the replayed graph reads from device
+// memory: parameters, positions, input tokens (range-checked), and each
+// sequence's RoPE rows at its new position (so decode attention can request
+// them without first waiting for the position).
+__global__ __launch_bounds__(256) void step_begin_kernel(StepArgs a) {
   const int i = threadIdx.x;
   if (i == 0) *a.d_params = a.params;
-  if (i >= a.n) return;
-  a.d_pos[i] = a.pos[i];
-  int t = a.dev_tok ? a.dev_tok[i] : a.host_tok[i];
-  if (t < 0 || t >= a.vocab) {
-    if (a.err) *a.err = 1;
-    t = t < 0 ? 0 : a.vocab - 1;
+  if (i < a.n) {
+    a.d_pos[i] = a.pos[i];
+    int t = a.dev_tok ? a.dev_tok[i] : a.host_tok[i];
+    if (t < 0 || t >= a.vocab) {
+      if (a.err) *a.err = 1;
+      t = t < 0 ? 0 : a.vocab - 1;
+    }
+    a.d_tok[i] = t;
   }
-  a.d_tok[i] = t;
+  const int per = a.n * a.half;
+  for (int e = i; e < 2 * per; e += blockDim.x) {
+    const int tbl = e / per, r = e % per, sq = r / a.half, k = r % a.half;
+    const float2* src = tbl ? a.rope_l : a.rope_g;
+    a.rope_cur[((size_t)tbl * a.max_seqs + sq) * a.half + k] = src[(size_t)a.pos[sq] * a.half + k];
+  }
 }
 
 }  // namespace qd

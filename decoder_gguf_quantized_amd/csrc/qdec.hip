@@ -101,6 +101,7 @@ struct qdec_model {
   float* output_norm = nullptr;
   float2* rope_g = nullptr;  // [max_ctx][hd/2] (cos, sin), full-attention layers
   float2* rope_l = nullptr;  // same for sliding-window layers
+  float2* rope_cur = nullptr;  // [2][max_seqs][hd/2]: rows of rope_g / rope_l at each decode position
   float* kc = nullptr;
   float* vc = nullptr;
   size_t kv_layer = 0;  // floats per layer of one cache
@@ -203,18 +204,31 @@ void gemv_dispatch_mode(int mode, dim3 grid, size_t lds, hipStream_t st, const G
 
 // (R rows per wave, U units per lane per row): R = 4, U = 1 for rows of at most
 // 64 units (one unit per lane); R = 2 with U = 2 or 4 for longer rows.
+// Largest input-row count M whose staged rows fit the 64 KB LDS budget for the
+// shortest row of each tile class (Q8_0: 16 weights per unit, Q4_0: 32, F32:
+// 4); combinations beyond it cannot be requested and are not instantiated.
+constexpr int gemv_max_m(int qt, int ru) {
+  return ru == 0 || qt == kF32 ? 16 : (qt == kQ8_0 ? (ru == 1 ? 8 : 4) : (ru == 1 ? 4 : 2));
+}
+
+template <int QT, int M, int RU, int R, int U>
+void gemv_dispatch_fit(int mode, dim3 grid, size_t lds, hipStream_t st, const GemvArgs& a) {
+  if constexpr (M <= gemv_max_m(QT, RU)) gemv_dispatch_mode<QT, M, R, U>(mode, grid, lds, st, a);
+  else throw HipError{"gemv: input rows exceed the LDS budget of the tile class"};
+}
+
 template <int QT, int M>
 void gemv_dispatch_ru(int ru, int mode, dim3 grid, size_t lds, hipStream_t st, const GemvArgs& a) {
   switch (ru) {
-    case 0: gemv_dispatch_mode<QT, M, 4, 1>(mode, grid, lds, st, a); break;
-    case 1: gemv_dispatch_mode<QT, M, 2, 2>(mode, grid, lds, st, a); break;
+    case 0: gemv_dispatch_fit<QT, M, 0, 4, 1>(mode, grid, lds, st, a); break;
+    case 1: gemv_dispatch_fit<QT, M, 1, 2, 2>(mode, grid, lds, st, a); break;
 #ifdef QDEC_EXPERIMENT
     case 3: gemv_dispatch_mode<QT, M, 4, 2>(mode, grid, lds, st, a); break;
     case 4: gemv_dispatch_mode<QT, M, 4, 4>(mode, grid, lds, st, a); break;
     case 5: gemv_dispatch_mode<QT, M, 2, 8>(mode, grid, lds, st, a); break;
     case 6: gemv_dispatch_mode<QT, M, 2, 1>(mode, grid, lds, st, a); break;
 #endif
-    default: gemv_dispatch_mode<QT, M, 2, 4>(mode, grid, lds, st, a); break;
+    default: gemv_dispatch_fit<QT, M, 2, 2, 4>(mode, grid, lds, st, a); break;
   }
 }
 
@@ -343,7 +357,8 @@ void attention_decode(qdec_model* m, hipStream_t st, int l, int B) {
   const float scale_log2 = (float)(1.0 / std::sqrt((double)hd) * 1.4426950408889634);
   AttnDecodeArgs a{m->qkv, m->nqkv, m->kc + l * m->kv_layer, m->vc + l * m->kv_layer, m->max_ctx, m->d_pos,
                    c.n_head, c.n_head_kv, layer_window(m, l), m->chunk, m->nchunk, L.q_norm, L.k_norm, c.rms_eps,
-                   L.global ? m->rope_g : m->rope_l, scale_log2, m->part_o, m->part_ml, m->counters, m->a};
+                   m->rope_cur + (L.global ? 0 : (size_t)m->max_seqs * (hd / 2)), scale_log2, m->part_o, m->part_ml,
+                   m->counters, m->a};
   double kvbytes = 0;
   for (int s = 0; s < B; ++s) {
     int p = m->kvlen[s];
@@ -804,6 +819,7 @@ int load(const qdec_config* cfgp, const qdec_tensor* ts, int32_t n, int32_t max_
       };
       m->rope_g = table(c.rope_theta);
       m->rope_l = c.window > 0 && c.rope_theta_local != c.rope_theta ? table(c.rope_theta_local) : m->rope_g;
+      m->rope_cur = m->dalloc<float2>((size_t)2 * max_seqs * half);
     }
     // KV cache [L][B][nkv][ctx][hd] f32
     m->kv_layer = (size_t)max_seqs * c.n_head_kv * max_ctx * c.head_dim;
@@ -961,9 +977,14 @@ int qdec_decode_step(qdec_model* m, const int32_t* tokens, int32_t n_seqs, float
     sa.err = m->err_dev;
     sa.params = StepParams{temperature, n_seqs, seed, step, d_logits, d_token_out};
     sa.d_params = m->d_params;
+    sa.rope_g = m->rope_g;
+    sa.rope_l = m->rope_l;
+    sa.rope_cur = m->rope_cur;
+    sa.half = c.head_dim / 2;
+    sa.max_seqs = m->max_seqs;
     {
       Timed tm(m, st, "step_begin", 0, 0);
-      qlaunch(step_begin_kernel, 1, 64, 0, st, sa);
+      qlaunch(step_begin_kernel, 1, 256, 0, st, sa);
     }
     if (m->timing) {
       decode_body(m, st, n_seqs);
