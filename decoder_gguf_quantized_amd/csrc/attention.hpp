@@ -171,7 +171,10 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
     }
   };
   float ka[2][8], va[2][8], kb[2][8], vb[2][8];
+  // full-causal layers: the chunk's first two pairs (four positions per stream)
+  bool b_ready = spec && a.chunk > 2 * NG;
   if (spec) fetch_pair(cb + gi, ka, va);
+  if (b_ready) fetch_pair(cb + 2 * NG + gi, kb, vb);
 
   int lo, hi;
   attn_key_range(p, a.window, lo, hi);
@@ -237,7 +240,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
   // trip count: jb and end are the same for every lane)
   for (int jb = jb0; jb < end; jb += 4 * NG) {
     const bool more_b = jb + 2 * NG < end;
-    if (more_b) fetch_pair(jb + 2 * NG + gi, kb, vb);
+    if (more_b && !b_ready) fetch_pair(jb + 2 * NG + gi, kb, vb);
+    b_ready = false;
     accumulate(jb + gi, ka[0], va[0]);
     accumulate(jb + gi + NG, ka[1], va[1]);
     if (!more_b) break;
@@ -256,24 +260,35 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < G * HD; idx += 256) {
-    const int h = idx / HD, dd = idx % HD;
-    float M = -INFINITY;
-    for (int k = 0; k < NG; ++k) M = fmaxf(M, sm_m[k][h]);
-    float L = 0.f, O = 0.f;
-    if (M != -INFINITY) {
-      for (int k = 0; k < NG; ++k) {
-        const float w = sm_m[k][h] == -INFINITY ? 0.f : exp2f(sm_m[k][h] - M);
-        L += sm_l[k][h] * w;
-        O += sm_o[k][h][dd] * w;
+  // streams -> one partial per head: wave w takes heads w, w + 4, ...; lane k
+  // holds stream k's (m, l), and the head's max, weights and denominator are
+  // wave reductions (NG <= 64 streams)
+  {
+    const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+    for (int h = wave; h < G; h += 4) {
+      const bool on = lane < NG;
+      const float mk = on ? sm_m[min(lane, NG - 1)][h] : -INFINITY;
+      const float lk = on ? sm_l[min(lane, NG - 1)][h] : 0.f;
+      const float M = wave_max(mk);
+      const float w = mk == -INFINITY ? 0.f : exp2f(mk - M);
+      const float L = wave_sum(w * lk);
+      if (on) sm_m[lane][h] = w;  // the stream's weight replaces its max
+      if (lane == 0) {
+        const size_t pi = ((size_t)s * a.nq + g * G + h) * a.nchunk + c;
+        store_coherent(a.part_ml + pi * 2 + 0, M);
+        store_coherent(a.part_ml + pi * 2 + 1, L);
       }
     }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * HD; idx += 256) {
+    const int h = idx / HD, dd = idx % HD;
+    float O = 0.f;
+#pragma unroll
+    for (int k = 0; k < NG; ++k) O += sm_o[k][h][dd] * sm_m[k][h];
     const size_t pi = ((size_t)s * a.nq + g * G + h) * a.nchunk + c;
     store_coherent(a.part_o + pi * HD + dd, O);
-    if (dd == 0) {
-      store_coherent(a.part_ml + pi * 2 + 0, M);
-      store_coherent(a.part_ml + pi * 2 + 1, L);
-    }
   }
   // every partial store of this workgroup is complete before the counter moves
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -284,19 +299,22 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
   }
   __syncthreads();
   if (!sm_last) return;
-  // merge.  Thread output e is element tid + 256 e of the group's G x HD block.
-  // Every chunk's (m, l) is requested first (at most NML pairs per thread),
-  // then the thread's values of CB chunks per output; loads run at clamped
-  // chunk indices (no predicates) and chunks past the last are masked in the
-  // sums, so up to CB chunks cost one round trip.  Sums run in chunk order.
-  constexpr int NML = (G * kMaxChunks + 255) / 256;
+  // merge.  Wave w takes heads w, w + 4, ...: lane cc requests chunk cc's
+  // (m, l) (nact <= kMaxChunks = 64 lanes), and the head's max M, weights
+  // 2^(m_c - M) and denominator sum_c l_c 2^(m_c - M) are wave reductions; the
+  // weights go to LDS.  Thread output e (element tid + 256 e of the group's
+  // G x HD block) requests its values of CB chunks per batch together with the
+  // (m, l) loads, at clamped chunk indices (chunks past the last are masked),
+  // so up to CB chunks cost one round trip.  Sums run in chunk order.
   const int nact = c_hi - c_lo + 1;  // <= kMaxChunks (the launcher sizes chunks so)
   const size_t pbase = ((size_t)s * a.nq + g * G) * a.nchunk + c_lo;
-  float mlm[NML], mll[NML];
+  constexpr int HW = (G + 3) / 4;  // heads per wave
+  float mlm[HW], mll[HW];
+  const int lane = tid & 63, wave = tid >> 6;
 #pragma unroll
-  for (int t = 0; t < NML; ++t) {
-    const int i = min(tid + 256 * t, G * nact - 1);
-    const size_t pi = pbase + (size_t)(i / nact) * a.nchunk + i % nact;
+  for (int t = 0; t < HW; ++t) {
+    const int h = min(wave + 4 * t, G - 1), cc = min(lane, nact - 1);
+    const size_t pi = pbase + (size_t)h * a.nchunk + cc;
     mlm[t] = load_coherent(a.part_ml + pi * 2);
     mll[t] = load_coherent(a.part_ml + pi * 2 + 1);
   }
@@ -308,15 +326,11 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
     hh[e] = idx / HD;
     po[e] = a.part_o + (pbase + (size_t)hh[e] * a.nchunk) * HD + idx % HD;
   }
-  float M[E], L[E], O[E];
+  float O[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    M[e] = -INFINITY;
-    L[e] = 0.f;
-    O[e] = 0.f;
-  }
-  // one batch of CB chunks; the first is straight-line code after the (m, l)
-  // requests so that nothing waits between them
+  for (int e = 0; e < E; ++e) O[e] = 0.f;
+  float* sm_w = &sm_pm[0][0];  // [G][kMaxChunks] chunk weights
+  float* sm_L = &sm_pl[0][0];  // [G] denominators
   auto batch = [&](int c0, auto FIRST) {
     float ov[E][CB];
 #pragma unroll
@@ -330,29 +344,26 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
     }
     if constexpr (decltype(FIRST)::value) {
 #pragma unroll
-      for (int t = 0; t < NML; ++t) {
-        const int i = tid + 256 * t;
-        if (i < G * nact) {
-          sm_pm[i / nact][i % nact] = mlm[t];
-          sm_pl[i / nact][i % nact] = mll[t];
+      for (int t = 0; t < HW; ++t) {
+        const int h = wave + 4 * t;
+        const bool on = lane < nact;
+        const float mc = on ? mlm[t] : -INFINITY;
+        const float M = wave_max(mc);
+        const float w = (on && mc != -INFINITY) ? exp2f(mc - M) : 0.f;
+        const float L = wave_sum(w * (on ? mll[t] : 0.f));
+        if (h < G) {
+          sm_w[h * kMaxChunks + lane] = w;
+          if (lane == 0) sm_L[h] = L;
         }
       }
       __syncthreads();
-#pragma unroll
-      for (int e = 0; e < E; ++e)
-        for (int cc = 0; cc < nact; ++cc) M[e] = fmaxf(M[e], sm_pm[hh[e]][cc]);
     }
 #pragma unroll
     for (int e = 0; e < E; ++e) {
+      const float* wr = sm_w + hh[e] * kMaxChunks + c0;
 #pragma unroll
-      for (int cc = 0; cc < CB; ++cc) {
-        if (c0 + cc < nact) {
-          const float mc = sm_pm[hh[e]][c0 + cc];
-          const float w = mc == -INFINITY ? 0.f : exp2f(mc - M[e]);
-          L[e] += sm_pl[hh[e]][c0 + cc] * w;
-          O[e] += ov[e][cc] * w;
-        }
-      }
+      for (int cc = 0; cc < CB; ++cc)
+        if (c0 + cc < nact) O[e] += ov[e][cc] * wr[cc];
     }
   };
   batch(0, std::true_type{});
@@ -360,7 +371,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int idx = tid + 256 * e;
-    if (idx < G * HD) a.out[(size_t)s * a.nq * HD + (size_t)g * G * HD + idx] = O[e] / L[e];
+    if (idx < G * HD) a.out[(size_t)s * a.nq * HD + (size_t)g * G * HD + idx] = O[e] / sm_L[hh[e]];
   }
   if (tid == 0) __hip_atomic_store(a.counter + s * a.nkv + g, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
