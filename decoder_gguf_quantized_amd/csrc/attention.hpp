@@ -61,11 +61,12 @@ QD_DEV void attn_key_range(int p, int window, int& lo, int& hi) {
 }
 
 // Per-head RMSNorm (gain nw, or none) and the half-split rotation of one head
-// held as 8 dims per lane over a group of LG = hd/8 lanes.  Dim d pairs with
-// d + hd/2, which lives in lane li ^ (LG/2) at the same slot.
+// held over a group of LG = hd/8 lanes: lane li holds dims 4 li + e (v[e]) and
+// hd/2 + 4 li + e (v[4 + e]), e < 4, so each rotation pair (d, d + hd/2) sits in
+// one lane and c/sn hold the lane's four angles.
 template <int LG>
-QD_DEV void norm_rope_group(float (&v)[8], bool norm, const float (&nw)[8], float eps, int hd, int li,
-                            const float (&c)[8], const float (&sn)[8]) {
+QD_DEV void norm_rope_group(float (&v)[8], bool norm, const float (&nw)[8], float eps, int hd, const float (&c)[4],
+                            const float (&sn)[4]) {
   if (norm) {
     float ss = 0.f;
 #pragma unroll
@@ -75,12 +76,36 @@ QD_DEV void norm_rope_group(float (&v)[8], bool norm, const float (&nw)[8], floa
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = v[e] * scale * nw[e];
   }
-  const bool first_half = li < LG / 2;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float other = __shfl_xor(v[e], LG / 2);
-    v[e] = first_half ? v[e] * c[e] - other * sn[e] : v[e] * c[e] + other * sn[e];
+  for (int e = 0; e < 4; ++e) {
+    const float x1 = v[e], x2 = v[4 + e];
+    v[e] = x1 * c[e] - x2 * sn[e];
+    v[4 + e] = x2 * c[e] + x1 * sn[e];
   }
+}
+
+// The lane's 8 values of a head row in the lane layout above: two float4
+// loads, each covering 16 consecutive bytes per lane (256 contiguous bytes over
+// a 16-lane group at hd = 128).
+QD_DEV void load_lane8(const float* rowp, int hd, int li, float (&v)[8]) {
+  const float4* p = reinterpret_cast<const float4*>(rowp);
+  const float4 a = p[li], b = p[hd / 8 + li];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+// Same, with non-temporal loads (cache rows are streamed once per step).
+QD_DEV void load_lane8_nt(const float* rowp, int hd, int li, float (&v)[8]) {
+  const float4* p = reinterpret_cast<const float4*>(rowp);
+  const float4 a = load_nt(p + li), b = load_nt(p + hd / 8 + li);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+QD_DEV void store_lane8(float* rowp, int hd, int li, const float (&v)[8]) {
+  float4* p = reinterpret_cast<float4*>(rowp);
+  p[li] = make_float4(v[0], v[1], v[2], v[3]);
+  p[hd / 8 + li] = make_float4(v[4], v[5], v[6], v[7]);
 }
 
 // Workgroup = (chunk of positions, KV head, sequence); it serves the KV head's
@@ -117,11 +142,12 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
   const bool spec = a.window == 0;
 
   const int p = a.pos[s];
-  float cs[8], sn[8];
+  // lane li of a stream group holds dims 4 li + e and HD/2 + 4 li + e (e < 4)
+  float cs[4], sn[4];
   {
-    const float2* rt = a.rope + (size_t)s * (HD / 2) + (8 * li) % (HD / 2);
+    const float2* rt = a.rope + (size_t)s * (HD / 2) + 4 * li;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < 4; ++e) {
       const float2 t = rt[e];
       cs[e] = t.x;
       sn[e] = t.y;
@@ -129,45 +155,27 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
   }
   float q[G][8];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float4* qp = reinterpret_cast<const float4*>(row + (size_t)(g * G + h) * HD + li * 8);
-    const float4 q0 = qp[0], q1 = qp[1];
-    q[h][0] = q0.x; q[h][1] = q0.y; q[h][2] = q0.z; q[h][3] = q0.w;
-    q[h][4] = q1.x; q[h][5] = q1.y; q[h][6] = q1.z; q[h][7] = q1.w;
-  }
+  for (int h = 0; h < G; ++h) load_lane8(row + (size_t)(g * G + h) * HD, HD, li, q[h]);
   // the lane's 8 dims of the QK-norm gains (requested with the rest)
   const bool qkn = a.q_norm != nullptr;
   float wq[8], wk[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) wq[e] = wk[e] = 1.f;
   if (qkn) {
-    const float4* qw = reinterpret_cast<const float4*>(a.q_norm + li * 8);
-    const float4* kw = reinterpret_cast<const float4*>(a.k_norm + li * 8);
-    const float4 q0 = qw[0], q1 = qw[1], k0 = kw[0], k1 = kw[1];
-    wq[0] = q0.x; wq[1] = q0.y; wq[2] = q0.z; wq[3] = q0.w; wq[4] = q1.x; wq[5] = q1.y; wq[6] = q1.z; wq[7] = q1.w;
-    wk[0] = k0.x; wk[1] = k0.y; wk[2] = k0.z; wk[3] = k0.w; wk[4] = k1.x; wk[5] = k1.y; wk[6] = k1.z; wk[7] = k1.w;
+    load_lane8(a.q_norm, HD, li, wq);
+    load_lane8(a.k_norm, HD, li, wk);
   }
   float kn[8], vn[8];
-  {
-    const float4* kp = reinterpret_cast<const float4*>(row + (size_t)(a.nq + g) * HD + li * 8);
-    const float4* vp = reinterpret_cast<const float4*>(row + (size_t)(a.nq + a.nkv + g) * HD + li * 8);
-    const float4 k0 = kp[0], k1 = kp[1], v0 = vp[0], v1 = vp[1];
-    kn[0] = k0.x; kn[1] = k0.y; kn[2] = k0.z; kn[3] = k0.w; kn[4] = k1.x; kn[5] = k1.y; kn[6] = k1.z; kn[7] = k1.w;
-    vn[0] = v0.x; vn[1] = v0.y; vn[2] = v0.z; vn[3] = v0.w; vn[4] = v1.x; vn[5] = v1.y; vn[6] = v1.z; vn[7] = v1.w;
-  }
+  load_lane8(row + (size_t)(a.nq + g) * HD, HD, li, kn);
+  load_lane8(row + (size_t)(a.nq + a.nkv + g) * HD, HD, li, vn);
   // keys/values of positions j0 and j0 + NG (addresses clamped into the cache;
   // positions outside [start, end) are masked when accumulated)
   auto fetch_pair = [&](int j0, float (&k)[2][8], float (&v)[2][8]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int jj = min(j0 + t * NG, a.ctx - 1);
-      const float4* kp = reinterpret_cast<const float4*>(a.kc + (head_base + jj) * HD + li * 8);
-      const float4* vp = reinterpret_cast<const float4*>(a.vc + (head_base + jj) * HD + li * 8);
-      const float4 k0 = kp[0], k1 = kp[1], v0 = vp[0], v1 = vp[1];
-      k[t][0] = k0.x; k[t][1] = k0.y; k[t][2] = k0.z; k[t][3] = k0.w;
-      k[t][4] = k1.x; k[t][5] = k1.y; k[t][6] = k1.z; k[t][7] = k1.w;
-      v[t][0] = v0.x; v[t][1] = v0.y; v[t][2] = v0.z; v[t][3] = v0.w;
-      v[t][4] = v1.x; v[t][5] = v1.y; v[t][6] = v1.z; v[t][7] = v1.w;
+      load_lane8_nt(a.kc + (head_base + jj) * HD, HD, li, k[t]);
+      load_lane8_nt(a.vc + (head_base + jj) * HD, HD, li, v[t]);
     }
   };
   float ka[2][8], va[2][8], kb[2][8], vb[2][8];
@@ -189,7 +197,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
   float o[G][8], m[G], l[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    norm_rope_group<LG>(q[h], qkn, wq, a.eps, HD, li, cs, sn);
+    norm_rope_group<LG>(q[h], qkn, wq, a.eps, HD, cs, sn);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       q[h][e] *= a.scale_log2;
@@ -200,14 +208,10 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
   }
   const bool has_new = c == c_hi;
   if (has_new) {
-    norm_rope_group<LG>(kn, qkn, wk, a.eps, HD, li, cs, sn);
+    norm_rope_group<LG>(kn, qkn, wk, a.eps, HD, cs, sn);
     if (gi == 0) {
-      float4* kd = reinterpret_cast<float4*>(a.kc + (head_base + p) * HD + li * 8);
-      float4* vd = reinterpret_cast<float4*>(a.vc + (head_base + p) * HD + li * 8);
-      kd[0] = make_float4(kn[0], kn[1], kn[2], kn[3]);
-      kd[1] = make_float4(kn[4], kn[5], kn[6], kn[7]);
-      vd[0] = make_float4(vn[0], vn[1], vn[2], vn[3]);
-      vd[1] = make_float4(vn[4], vn[5], vn[6], vn[7]);
+      store_lane8(a.kc + (head_base + p) * HD, HD, li, kn);
+      store_lane8(a.vc + (head_base + p) * HD, HD, li, vn);
     }
   }
   // online softmax over one position; masked positions leave the state as is
@@ -252,8 +256,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
   }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sm_o[gi][h][li * 8 + e] = o[h][e];
+    store_lane8(&sm_o[gi][h][0], HD, li, o[h]);
     if (li == 0) {
       sm_m[gi][h] = m[h];
       sm_l[gi][h] = l[h];

@@ -182,16 +182,16 @@ QD_DEV void gemv_load(const GemvArgs& a, const int (&r)[R], int base, int lane, 
       if constexpr (QT == kQ8_0) {
         const uint8_t* rq = a.qs + (size_t)r[i] * kp;
         const uint16_t* rd = a.d + (size_t)r[i] * a.nblk;
-        W.w[i][k] = *reinterpret_cast<const uint4*>(rq + uc * 16u);
-        W.d[i][k] = load_half(rd + (uc >> 1));
+        W.w[i][k] = load_nt(reinterpret_cast<const uint4*>(rq + uc * 16u));
+        W.d[i][k] = load_half_nt(rd + (uc >> 1));
       } else if constexpr (QT == kQ4_0) {
         const uint8_t* rq = a.qs + (size_t)r[i] * a.nblk * 16;
         const uint16_t* rd = a.d + (size_t)r[i] * a.nblk;
-        W.w[i][k] = *reinterpret_cast<const uint4*>(rq + uc * 16u);
-        W.d[i][k] = load_half(rd + uc);
+        W.w[i][k] = load_nt(reinterpret_cast<const uint4*>(rq + uc * 16u));
+        W.d[i][k] = load_half_nt(rd + uc);
       } else {
         const uint8_t* rq = a.qs + (size_t)r[i] * kp * 4;
-        W.w[i][k] = *reinterpret_cast<const uint4*>(rq + uc * 16u);
+        W.w[i][k] = load_nt(reinterpret_cast<const uint4*>(rq + uc * 16u));
         W.d[i][k] = 1.f;
       }
     }

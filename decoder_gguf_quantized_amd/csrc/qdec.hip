@@ -837,13 +837,15 @@ int load(const qdec_config* cfgp, const qdec_tensor* ts, int32_t n, int32_t max_
     m->m = m->dalloc<float>(T * m->Fp);
     hipck(hipMemsetAsync(m->m, 0, T * m->Fp * 4, st), "memset");
     {  // decode split over positions: at least four positions per lane group
-       // (the first two pairs are requested at once), enough chunks to fill the
-       // GPU at max length, at most kMaxChunks per (sequence, KV head)
-      const double want = (double)max_ctx * c.n_head_kv * max_seqs / 2048.0;
+       // (the first two pairs are requested at once); at max length about 8192
+       // workgroups or more (several rounds of resident workgroups, so the last
+       // round's partial fill costs little); at most kMaxChunks per (sequence,
+       // KV head)
+      const double want = (double)max_ctx * c.n_head_kv * max_seqs / 8192.0;
       int ch = 4 * (256 / (c.head_dim / 8));
       while ((ch < want || (max_ctx + ch - 1) / ch > kMaxChunks) && ch < (1 << 30)) ch *= 2;
 #ifdef QDEC_EXPERIMENT
-      if (const char* e = getenv("QDEC_CHUNK")) ch = std::max(ch, atoi(e));
+      if (const char* e = getenv("QDEC_CHUNK")) ch = std::max(atoi(e), (max_ctx + kMaxChunks - 1) / kMaxChunks);
 #endif
       m->chunk = ch;
       m->nchunk = (max_ctx + ch - 1) / ch;
