@@ -93,12 +93,13 @@ constexpr int unit_floats() { return QT == kQ8_0 ? 16 : (QT == kQ4_0 ? 32 : 4); 
 // unit, so for each slot i consecutive lanes read consecutive float4s: no bank
 // conflicts (the natural layout puts every lane's unit 64 or 128 bytes apart,
 // which lands all lanes on a handful of banks).
-template <int QT, int M>
+template <int QT, int M, int NW>
 QD_DEV void gemv_stage_x(const GemvArgs& a, float4* xs4, int kp, float (&scale)[M]) {
+  constexpr int NT = 64 * NW;  // threads of the workgroup
   constexpr int US = unit_floats<QT>(), NV = US / 4;
   constexpr int JB = M >= 8 ? 1 : 8 / M;  // k positions per thread per batch
   const int NU = kp / US, NK4 = kp / 4;
-  __shared__ float red[4][M];
+  __shared__ float red[NW][M];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool norm = a.norm_w != nullptr;
   const float4* x4 = reinterpret_cast<const float4*>(a.x);
@@ -107,11 +108,11 @@ QD_DEV void gemv_stage_x(const GemvArgs& a, float4* xs4, int kp, float (&scale)[
   float ss[M];
 #pragma unroll
   for (int mi = 0; mi < M; ++mi) ss[mi] = 0.f;
-  for (int k0 = tid; k0 < NK4; k0 += 256 * JB) {
+  for (int k0 = tid; k0 < NK4; k0 += NT * JB) {
     float4 xv[JB][M], wv[JB];
 #pragma unroll
     for (int j = 0; j < JB; ++j) {
-      const int k4 = k0 + 256 * j;
+      const int k4 = k0 + NT * j;
       const bool ok = k4 < NK4;
       wv[j] = (ok && norm) ? w4[k4] : make_float4(1.f, 1.f, 1.f, 1.f);
 #pragma unroll
@@ -120,7 +121,7 @@ QD_DEV void gemv_stage_x(const GemvArgs& a, float4* xs4, int kp, float (&scale)[
     }
 #pragma unroll
     for (int j = 0; j < JB; ++j) {
-      const int k4 = k0 + 256 * j;
+      const int k4 = k0 + NT * j;
       if (k4 < NK4) {
         const int slot = (k4 % NV) * NU + k4 / NV;
 #pragma unroll
@@ -141,8 +142,12 @@ QD_DEV void gemv_stage_x(const GemvArgs& a, float4* xs4, int kp, float (&scale)[
   }
   __syncthreads();
 #pragma unroll
-  for (int mi = 0; mi < M; ++mi)
-    scale[mi] = norm ? 1.0f / sqrtf((red[0][mi] + red[1][mi] + red[2][mi] + red[3][mi]) / (float)kp + a.eps) : 1.f;
+  for (int mi = 0; mi < M; ++mi) {
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) t += red[w][mi];
+    scale[mi] = norm ? 1.0f / sqrtf(t / (float)kp + a.eps) : 1.f;
+  }
 }
 
 // Weights of one row group held in registers between load and use.
@@ -304,16 +309,16 @@ constexpr int gemv_sets() { return QDEC_GEMV_NS; }
 // tiles are requested before the input rows are staged.  Tile indices are
 // wave-uniform (scalar registers), so every load is a scalar base plus a 32-bit
 // lane offset.
-template <int QT, int M, int MODE, int R, int U>
-__global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
+template <int QT, int M, int MODE, int R, int U, int NW>
+__global__ __launch_bounds__(64 * NW) void gemv_kernel(GemvArgs a) {
   constexpr int NS = gemv_sets<R, U, M>();
   extern __shared__ float4 xs4[];
   const int kp = a.nblk * 32;
   float* xsum = reinterpret_cast<float*>(xs4 + M * kp / 4);  // Q4_0 only: [M][nblk] block sums of x
   constexpr bool kPair = MODE == kModePairSilu || MODE == kModePairGelu;
   const int lane = threadIdx.x & 63;
-  const int gwave = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
-  const int nwaves = gridDim.x * 4;
+  const int gwave = __builtin_amdgcn_readfirstlane(blockIdx.x * NW + (threadIdx.x >> 6));
+  const int nwaves = gridDim.x * NW;
   const int nunits = QT == kQ8_0 ? 2 * a.nblk : (QT == kQ4_0 ? a.nblk : kp / 4);
   const int ngroups = kPair ? a.rows / R : (a.rows + R - 1) / R;
   const int tpg = (nunits + 64 * U - 1) / (64 * U);  // tiles per row group
@@ -342,9 +347,9 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   if constexpr (NS > 2) request(std::integral_constant<int, 1>{});
 
   float scale[M];
-  gemv_stage_x<QT, M>(a, xs4, kp, scale);  // ends with a barrier
+  gemv_stage_x<QT, M, NW>(a, xs4, kp, scale);  // ends with a barrier
   if constexpr (QT == kQ4_0) {
-    for (int i = threadIdx.x; i < M * a.nblk; i += 256) {
+    for (int i = threadIdx.x; i < M * a.nblk; i += 64 * NW) {
       const int mi = i / a.nblk, u = i % a.nblk;
       float s = 0.f;
 #pragma unroll

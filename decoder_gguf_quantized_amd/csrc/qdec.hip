@@ -192,18 +192,22 @@ struct Timed {
 const char* gemv_class(int type) { return type == kQ4_0 ? "gemv_q4_0" : type == kQ8_0 ? "gemv_q8_0" : "gemv_f32"; }
 const char* gemm_class(int type) { return type == kQ4_0 ? "gemm_q4_0" : type == kQ8_0 ? "gemm_q8_0" : "gemm_f32"; }
 
-template <int QT, int M, int R, int U>
+template <int QT, int M, int R, int U, int NW = 4>
 void gemv_dispatch_mode(int mode, dim3 grid, size_t lds, hipStream_t st, const GemvArgs& a) {
   switch (mode) {
-    case kModeStore: qlaunch(gemv_kernel<QT, M, kModeStore, R, U>, grid, 256, lds, st, a); break;
-    case kModeAdd: qlaunch(gemv_kernel<QT, M, kModeAdd, R, U>, grid, 256, lds, st, a); break;
-    case kModePairSilu: qlaunch(gemv_kernel<QT, M, kModePairSilu, R, U>, grid, 256, lds, st, a); break;
-    default: qlaunch(gemv_kernel<QT, M, kModePairGelu, R, U>, grid, 256, lds, st, a); break;
+    case kModeStore: qlaunch(gemv_kernel<QT, M, kModeStore, R, U, NW>, grid, 64 * NW, lds, st, a); break;
+    case kModeAdd: qlaunch(gemv_kernel<QT, M, kModeAdd, R, U, NW>, grid, 64 * NW, lds, st, a); break;
+    case kModePairSilu: qlaunch(gemv_kernel<QT, M, kModePairSilu, R, U, NW>, grid, 64 * NW, lds, st, a); break;
+    default: qlaunch(gemv_kernel<QT, M, kModePairGelu, R, U, NW>, grid, 64 * NW, lds, st, a); break;
   }
 }
 
-// (R rows per wave, U units per lane per row): R = 4, U = 1 for rows of at most
-// 64 units (one unit per lane); R = 2 with U = 2 or 4 for longer rows.
+// (R rows per wave, U units per lane per row, NW waves per workgroup):
+//   0: R = 4, U = 1 for rows of at most 64 units (one unit per lane);
+//   1: R = 2, U = 2 for rows of 65..128 units;
+//   2: R = 2, U = 4 for longer rows;
+//   3: as 2 with eight-wave workgroups, for long rows with many row groups:
+//      the input row is staged once per CU instead of twice (same LDS).
 // Largest input-row count M whose staged rows fit the 64 KB LDS budget for the
 // shortest row of each tile class (Q8_0: 16 weights per unit, Q4_0: 32, F32:
 // 4); combinations beyond it cannot be requested and are not instantiated.
@@ -211,9 +215,9 @@ constexpr int gemv_max_m(int qt, int ru) {
   return ru == 0 || qt == kF32 ? 16 : (qt == kQ8_0 ? (ru == 1 ? 8 : 4) : (ru == 1 ? 4 : 2));
 }
 
-template <int QT, int M, int RU, int R, int U>
+template <int QT, int M, int RU, int R, int U, int NW = 4>
 void gemv_dispatch_fit(int mode, dim3 grid, size_t lds, hipStream_t st, const GemvArgs& a) {
-  if constexpr (M <= gemv_max_m(QT, RU)) gemv_dispatch_mode<QT, M, R, U>(mode, grid, lds, st, a);
+  if constexpr (M <= gemv_max_m(QT, RU)) gemv_dispatch_mode<QT, M, R, U, NW>(mode, grid, lds, st, a);
   else throw HipError{"gemv: input rows exceed the LDS budget of the tile class"};
 }
 
@@ -222,17 +226,22 @@ void gemv_dispatch_ru(int ru, int mode, dim3 grid, size_t lds, hipStream_t st, c
   switch (ru) {
     case 0: gemv_dispatch_fit<QT, M, 0, 4, 1>(mode, grid, lds, st, a); break;
     case 1: gemv_dispatch_fit<QT, M, 1, 2, 2>(mode, grid, lds, st, a); break;
+    case 3: gemv_dispatch_fit<QT, M, 3, 2, 4, 8>(mode, grid, lds, st, a); break;
 #ifdef QDEC_EXPERIMENT
-    case 3: gemv_dispatch_mode<QT, M, 4, 2>(mode, grid, lds, st, a); break;
-    case 4: gemv_dispatch_mode<QT, M, 4, 4>(mode, grid, lds, st, a); break;
-    case 5: gemv_dispatch_mode<QT, M, 2, 8>(mode, grid, lds, st, a); break;
-    case 6: gemv_dispatch_mode<QT, M, 2, 1>(mode, grid, lds, st, a); break;
+    case 4: gemv_dispatch_mode<QT, M, 4, 2>(mode, grid, lds, st, a); break;
+    case 5: gemv_dispatch_mode<QT, M, 4, 4>(mode, grid, lds, st, a); break;
+    case 6: gemv_dispatch_mode<QT, M, 2, 8>(mode, grid, lds, st, a); break;
+    case 7: gemv_dispatch_mode<QT, M, 2, 1>(mode, grid, lds, st, a); break;
+    case 8: gemv_dispatch_mode<QT, M, 1, 4, 8>(mode, grid, lds, st, a); break;
+    case 9: gemv_dispatch_mode<QT, M, 1, 8, 8>(mode, grid, lds, st, a); break;
+    case 10: gemv_dispatch_mode<QT, M, 2, 2, 8>(mode, grid, lds, st, a); break;
 #endif
     default: gemv_dispatch_fit<QT, M, 2, 2, 4>(mode, grid, lds, st, a); break;
   }
 }
 
-int ru_rows(int ru) { return (ru == 0 || ru == 3 || ru == 4) ? 4 : 2; }
+int ru_rows(int ru) { return (ru == 0 || ru == 4 || ru == 5) ? 4 : (ru == 8 || ru == 9) ? 1 : 2; }
+int ru_waves(int ru) { return (ru == 3 || ru >= 8) ? 8 : 4; }
 
 template <int QT>
 void gemv_dispatch_m(int M, int ru, int mode, dim3 grid, size_t lds, hipStream_t st, const GemvArgs& a) {
@@ -260,6 +269,7 @@ void gemv(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, 
   const bool pair = mode == kModePairSilu || mode == kModePairGelu;
   const int nunits = w.type == kQ8_0 ? 2 * w.nblk : (w.type == kQ4_0 ? w.nblk : kp / 4);
   int ru = nunits <= 64 ? 0 : (nunits <= 128 ? 1 : 2);
+  if (ru == 2 && (pair ? w.rows / 2 : (w.rows + 1) / 2) >= 2048) ru = 3;
   int grid_cap = 1024;
 #ifdef QDEC_EXPERIMENT
   {
@@ -268,11 +278,11 @@ void gemv(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, 
     if (const char* g = getenv("QDEC_GRID_CAP")) grid_cap = atoi(g);
   }
 #endif
-  const int R = ru_rows(ru);
+  const int R = ru_rows(ru), NW = ru_waves(ru);
   const int ngroups = pair ? w.rows / R : (w.rows + R - 1) / R;
   // waves stay resident and loop: about four workgroups per CU, so the input
   // staging of each workgroup is amortised over many row groups
-  dim3 grid(std::max(1, std::min((ngroups + 3) / 4, grid_cap)));
+  dim3 grid(std::max(1, std::min((ngroups + NW - 1) / NW, grid_cap)));
   for (int r0 = 0; r0 < nrows; r0 += cap) {
     const int mr = std::min(cap, nrows - r0);
     int M = 1;

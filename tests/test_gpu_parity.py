@@ -114,6 +114,9 @@ MATMUL_CASES = [
     # wide tile; fewer take the K-split 32 x 64 tile (partial last K stage)
     (synth.T_Q8_0, 4100, 320, 1030), (synth.T_Q4_0, 4224, 288, 1000),
     (synth.T_Q4_0, 200, 720, 40), (synth.T_F32, 96, 300, 33), (synth.T_Q8_0, 1030, 1000, 97),
+    # long rows with >= 2048 row groups: eight-wave workgroups (ragged rows)
+    (synth.T_Q4_0, 4100, 8192, 1), (synth.T_Q4_0, 4097, 4608, 2), (synth.T_Q8_0, 4100, 2080, 3),
+    (synth.T_F32, 4100, 600, 5),
 ]
 
 
