@@ -13,6 +13,15 @@ generator:
   u_v = ((r >> 41) + 0.5) * 2^-23        (top 23 bits; exact in float32 and
                                           strictly inside (0, 1), so G is finite)
 
+Top-p (nucleus) sampling follows the walkthrough's Step 8 sampler: with
+probabilities p = softmax(logits / T), sort them in descending order, take the
+running sum, keep the first count(running sum < top_p) + 1 tokens (the smallest
+prefix whose mass reaches top_p), renormalise and draw.  Readings: equal
+probabilities are ordered by lower index first (a stable sort); top_p >= 1, or
+a row with a NaN or infinite logit, keeps every token.  The draw over the kept
+set is the same Gumbel-max (renormalising shifts every kept log-probability by
+one constant, which leaves the argmax unchanged).
+
 Philox4x64-10: ten rounds of
   (hi0, lo0) = M0 * c0,  (hi1, lo1) = M1 * c2          (128-bit products)
   c = (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0)
@@ -80,20 +89,75 @@ def greedy(logits):
     return int(np.argmax(np.asarray(logits)))
 
 
-def sample(logits, temperature, seed, step, seq):
-    """Greedy for temperature 0, else argmax(logits / T + Gumbel)."""
+def nucleus_from_probs(probs, top_p):
+    """Boolean mask of the tokens top-p keeps, from probabilities (float64):
+    descending order with ties by lower index, running sum, the first
+    count(running sum < top_p) + 1 tokens."""
+    p = np.asarray(probs, dtype=np.float64)
+    order = np.argsort(-p, kind="stable")
+    run = np.cumsum(p[order])
+    cutoff = int(np.sum(run < top_p)) + 1
+    keep = np.zeros(p.size, dtype=bool)
+    keep[order[:cutoff]] = True
+    return keep
+
+
+def softmax_t(logits, temperature):
+    """softmax(logits / T) in float64."""
+    z = np.asarray(logits, dtype=np.float64) / temperature
+    e = np.exp(z - np.max(z))
+    return e / np.sum(e)
+
+
+def nucleus(logits, temperature, top_p):
+    """Mask of the tokens top-p keeps for one row (every token for top_p >= 1,
+    temperature 0, or a row with a non-finite logit)."""
+    lg = np.asarray(logits, dtype=np.float64)
+    if top_p >= 1 or temperature == 0 or not np.all(np.isfinite(lg)):
+        return np.ones(lg.size, dtype=bool)
+    return nucleus_from_probs(softmax_t(lg, temperature), top_p)
+
+
+def nucleus_margin(logits, temperature, top_p):
+    """How far the kept set is from changing: the smallest of |run - top_p| /
+    top_p at the last kept and the first dropped running sum, and the smallest
+    relative gap between the probability at the boundary and its neighbours in
+    the sorted order (near-equal probabilities can swap order under rounding).
+    Infinity when every token is kept by rule."""
+    lg = np.asarray(logits, dtype=np.float64)
+    if top_p >= 1 or temperature == 0 or not np.all(np.isfinite(lg)):
+        return np.inf
+    p = softmax_t(lg, temperature)
+    order = np.argsort(-p, kind="stable")
+    ps = p[order]
+    run = np.cumsum(ps)
+    c = int(np.sum(run < top_p)) + 1
+    m = np.inf
+    for k in (c - 2, c - 1):
+        if 0 <= k < run.size:
+            m = min(m, abs(run[k] - top_p) / top_p)
+    if c < ps.size:
+        m = min(m, (ps[c - 1] - ps[c]) / ps[c - 1])
+    return m
+
+
+def sample(logits, temperature, seed, step, seq, top_p=1.0):
+    """Greedy for temperature 0, else argmax(logits / T + Gumbel) over the
+    tokens top-p keeps."""
     if temperature == 0:
         return greedy(logits)
-    lg = np.asarray(logits, dtype=np.float64)
-    return int(np.argmax(lg / temperature + gumbel(lg.size, seed, step, seq)))
+    return int(np.argmax(scores(logits, temperature, seed, step, seq, top_p)))
 
 
-def scores(logits, temperature, seed, step, seq):
-    """The perturbed scores the sampler takes the argmax of."""
+def scores(logits, temperature, seed, step, seq, top_p=1.0):
+    """The perturbed scores the sampler takes the argmax of (-inf outside the
+    kept set)."""
     lg = np.asarray(logits, dtype=np.float64)
     if temperature == 0:
         return lg
-    return lg / temperature + gumbel(lg.size, seed, step, seq)
+    sc = lg / temperature + gumbel(lg.size, seed, step, seq)
+    keep = nucleus(lg, temperature, top_p)
+    return np.where(keep, sc, -np.inf)
 
 
 def uniforms_batch(vocab, seed, steps, seq):

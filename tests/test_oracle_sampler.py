@@ -85,3 +85,93 @@ def test_low_temperature_is_greedy_and_reproducible():
 def test_greedy_ties_lowest_index():
     assert sampler.greedy([2.0, 5.0, 5.0]) == 1
     assert sampler.sample([2.0, 5.0, 5.0], 0.0, 1, 1, 1) == 1
+
+
+# ---------------------------------------------------------------- top-p
+@pytest.mark.parametrize("probs,top_p,kept", [
+    # running sums of exact binary fractions: 0.5, 0.75, 0.875, 1
+    ([0.5, 0.25, 0.125, 0.125], 0.75, [0, 1]),   # reaching top_p exactly stops there
+    ([0.5, 0.25, 0.125, 0.125], 0.7, [0, 1]),
+    ([0.5, 0.25, 0.125, 0.125], 0.76, [0, 1, 2]),
+    ([0.5, 0.25, 0.125, 0.125], 0.5, [0]),
+    ([0.5, 0.25, 0.125, 0.125], 0.4, [0]),
+    ([0.125, 0.5, 0.125, 0.25], 0.75, [1, 3]),   # order comes from the probabilities
+    ([0.25, 0.25, 0.25, 0.25], 0.5, [0, 1]),     # ties: lower index first
+    ([0.25, 0.25, 0.25, 0.25], 0.51, [0, 1, 2]),
+    ([0.125, 0.375, 0.375, 0.125], 0.5, [1, 2]),
+    ([0.125, 0.375, 0.375, 0.125], 0.8, [0, 1, 2]),   # tie at the boundary: index 0 kept, 3 dropped
+    ([0.125, 0.375, 0.375, 0.125], 0.9, [0, 1, 2, 3]),
+])
+def test_nucleus_hand_values(probs, top_p, kept):
+    keep = sampler.nucleus_from_probs(probs, top_p)
+    assert sorted(np.flatnonzero(keep).tolist()) == kept
+
+
+def test_nucleus_is_the_smallest_set_reaching_top_p_brute_force():
+    """Over every subset of a 6-token vocabulary: the kept set's size is the
+    least size of any subset with mass >= top_p, and among subsets of that size
+    it has the largest mass."""
+    import itertools
+    rng = np.random.default_rng(7)
+    for trial in range(40):
+        p = rng.dirichlet(np.ones(6))
+        for top_p in (0.1, 0.5, 0.8, 0.95, 0.999):
+            keep = sampler.nucleus_from_probs(p, top_p)
+            best_size = min(r for r in range(1, 7) for s in itertools.combinations(range(6), r)
+                            if p[list(s)].sum() >= top_p)
+            assert keep.sum() == best_size, (trial, top_p)
+            best_mass = max(p[list(s)].sum() for s in itertools.combinations(range(6), best_size))
+            assert p[keep].sum() == pytest.approx(best_mass, rel=0, abs=1e-15)
+
+
+def test_nucleus_limits():
+    lg = np.random.default_rng(3).standard_normal(300)
+    assert sampler.nucleus(lg, 1.0, 1.0).all()
+    assert sampler.nucleus(lg, 0.0, 0.5).all()            # greedy ignores top_p
+    tiny = sampler.nucleus(lg, 0.8, 1e-12)
+    assert np.flatnonzero(tiny).tolist() == [int(np.argmax(lg))]
+
+
+@pytest.mark.parametrize("temperature,top_p", [(1.0, 0.9), (0.7, 0.5), (1.5, 0.99), (1.0, 0.05)])
+def test_nucleus_invariants(temperature, top_p):
+    lg = 2.0 * np.random.default_rng(int(100 * top_p)).standard_normal(5000)
+    p = sampler.softmax_t(lg, temperature)
+    keep = sampler.nucleus(lg, temperature, top_p)
+    assert p[keep].sum() >= top_p                               # reaches top_p
+    assert p[keep].sum() - p[keep].min() < top_p                # minimal
+    assert p[keep].min() >= p[~keep].max()                      # the most probable tokens
+
+
+def test_top_p_one_equals_plain_sampling():
+    lg = np.random.default_rng(11).standard_normal(700)
+    for step in range(20):
+        assert sampler.sample(lg, 0.9, 4, step, 1, top_p=1.0) == int(
+            np.argmax(lg / 0.9 + sampler.gumbel(lg.size, 4, step, 1)))
+
+
+def test_top_p_draws_follow_the_renormalised_nucleus():
+    """Chi-square: over 20,000 steps the Gumbel-max draws restricted to the
+    nucleus match p / p(nucleus); nothing outside the nucleus is drawn."""
+    lg = np.array([2.0, 1.5, 1.2, 0.4, 0.3, -0.5, -1.0, -2.0])
+    T, top_p = 1.0, 0.8
+    keep = sampler.nucleus(lg, T, top_p)
+    assert 2 <= keep.sum() < lg.size
+    steps = np.arange(20000)
+    u = sampler.uniforms_batch(lg.size, 17, steps, 0).astype(np.float64)
+    sc = lg[None, :] / T - np.log(-np.log(u))
+    sc[:, ~keep] = -np.inf
+    draws = np.argmax(sc, axis=1)
+    # the vectorised draws equal the sampler's own for a few steps
+    for s in range(5):
+        assert draws[s] == sampler.sample(lg, T, 17, s, 0, top_p)
+    counts = np.bincount(draws, minlength=lg.size)
+    assert counts[~keep].sum() == 0
+    p = sampler.softmax_t(lg, T)[keep]
+    exp = p / p.sum() * steps.size
+    assert stats.chisquare(counts[keep], exp).pvalue > 1e-3
+
+
+def test_top_p_non_finite_row_keeps_every_token():
+    lg = np.array([0.1, np.nan, 0.3, np.nan])
+    assert sampler.nucleus(lg, 1.0, 0.5).all()
+    assert sampler.sample(lg, 1.0, 1, 0, 0, top_p=0.5) == 1   # first NaN ranks above every number
