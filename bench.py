@@ -154,12 +154,13 @@ def bench_batched(cfg, args):
     toks[0].copy_(torch.from_numpy(first))
     stream = torch.cuda.current_stream()
     seed, temp = cfg["seed"], cfg["temperature"]
+    top_p = 1.0 if args.top_p is None else args.top_p
 
     def one_step():
         for s in range(B):
             model.kv_truncate(s, P)
         for i in range(N):
-            model.decode_step(toks[i], dl, toks[i + 1], temperature=temp, seed=seed, step=i)
+            model.decode_step(toks[i], dl, toks[i + 1], temperature=temp, seed=seed, step=i, top_p=top_p)
 
     def run(k):
         e0 = torch.cuda.Event(enable_timing=True)
@@ -188,7 +189,8 @@ def bench_batched(cfg, args):
         "ms_per_step": round(wall * 1e3 / args.steps, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"{cfg['name']}: {B} sequences x {P} preset KV positions, {N} decode steps, "
-                               f"temperature {temp} (Gumbel-max over Philox4x64-10)",
+                               f"temperature {temp} (Gumbel-max over Philox4x64-10)"
+                               + (f", top-p {top_p}" if top_p < 1 else ""),
                    "batch": B, "preset_kv": P, "decode_steps": N, "weights": cfg["wtype"]},
         "decode_hbm_frac": round(bytes_dec / (ms / 1e3) / HBM_PEAK, 4),
         "roofline": roofline_entry(kst, cfg.get("key")),
@@ -231,6 +233,8 @@ def main():
     ap.add_argument("--config", default="c2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=None, help="override the workload's decode steps (profiling runs)")
+    ap.add_argument("--top-p", type=float, default=None,
+                    help="batched workload only: restrict sampling to the top-p nucleus (default: none)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 256 MiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()

@@ -79,7 +79,7 @@ def lib():
                 "qdec_load_weights": (ctypes.c_int, [ctypes.POINTER(_Config), ctypes.POINTER(_Tensor), I32, I32, I32, P,
                                                      ctypes.POINTER(P)]),
                 "qdec_prefill": (ctypes.c_int, [P, I32, P, I32, P, P, U32, P]),
-                "qdec_decode_step": (ctypes.c_int, [P, P, I32, P, P, F, U64, U64, U32, P]),
+                "qdec_decode_step": (ctypes.c_int, [P, P, I32, P, P, F, F, U64, U64, U32, P]),
                 "qdec_kv_reset": (ctypes.c_int, [P, I32]),
                 "qdec_kv_truncate": (ctypes.c_int, [P, I32, I32]),
                 "qdec_kv_write": (ctypes.c_int, [P, I32, I32, P, P, I32, P]),
@@ -88,7 +88,7 @@ def lib():
                 "qdec_free": (ctypes.c_int, [P]),
                 "qdec_debug_dequant": (ctypes.c_int, [P, ctypes.c_char_p, P, P]),
                 "qdec_debug_embed": (ctypes.c_int, [P, P, I32, P, P]),
-                "qdec_debug_sample": (ctypes.c_int, [P, I32, I32, F, U64, U64, P, P]),
+                "qdec_debug_sample": (ctypes.c_int, [P, I32, I32, F, F, U64, U64, P, P]),
                 "qdec_debug_matmul": (ctypes.c_int, [I32, I64, I64, P, I64, P, I32, P, P]),
                 "qdec_kernel_timing": (ctypes.c_int, [P, I32, ctypes.POINTER(_KStat), I32, ctypes.POINTER(I32)]),
             }
@@ -271,9 +271,10 @@ class Model:
                                 ALL_LOGITS if all_logits else 0, _stream())
         self._check(rc)
 
-    def decode_step(self, tokens, logits, token_out, temperature=0.0, seed=0, step=0):
+    def decode_step(self, tokens, logits, token_out, temperature=0.0, seed=0, step=0, top_p=1.0):
         """One token for each of sequences 0..B-1.  ``tokens``: host ids, or an
-        int32 GPU tensor (e.g. the previous ``token_out``)."""
+        int32 GPU tensor (e.g. the previous ``token_out``).  ``top_p`` < 1 with
+        ``temperature`` > 0 samples from the nucleus."""
         import numpy as np
         import torch
         h = self._handle()
@@ -292,7 +293,7 @@ class Model:
             flags = 0
         lp = _dev_ptr("logits", logits, torch.float32, n * self.vocab)
         op = _dev_ptr("token_out", token_out, torch.int32, n)
-        rc = lib().qdec_decode_step(h, tp_in, _int("n_seqs", n), lp, op, float(temperature),
+        rc = lib().qdec_decode_step(h, tp_in, _int("n_seqs", n), lp, op, float(temperature), float(top_p),
                                     _int("seed", seed, _U64), _int("step", step, _U64), flags, _stream())
         self._check(rc)
 
@@ -351,12 +352,12 @@ class Model:
                                            flops=buf[i].flops) for i in range(n.value)}
 
 
-def debug_sample(logits, temperature, seed, step, out):
+def debug_sample(logits, temperature, seed, step, out, top_p=1.0):
     """Row-wise token choice with the decode step's rule; logits [rows][vocab]."""
     import torch
     rows, vocab = logits.shape
     rc = lib().qdec_debug_sample(_dev_ptr("logits", logits, torch.float32, rows * vocab), _int("rows", rows),
-                                 _int("vocab", vocab), float(temperature), _int("seed", seed, _U64),
+                                 _int("vocab", vocab), float(temperature), float(top_p), _int("seed", seed, _U64),
                                  _int("step", step, _U64), _dev_ptr("out", out, torch.int32, rows), _stream())
     if rc:
         raise (QdecError if rc == 1 else QdecPanic)(_last_error())

@@ -186,12 +186,272 @@ constexpr int kSampleChunk = 4096;
 // Per-step values that a replayed decode graph reads from device memory.
 struct StepParams {
   float temperature;
+  float top_p;
   int n;
   uint64_t seed;
   uint64_t step;
   float* logits;   // caller's logits buffer for this step
   int* tok_out;    // caller's token buffer for this step
 };
+
+// ------------------------------------------------------------ top-p cut
+// Walkthrough, Step 8 sampler: with probabilities p = softmax(logits / T) in
+// descending order (equal ones by lower index), keep the first
+// count(running sum < top_p) + 1 tokens.  For T > 0 the probability order is
+// the logit order, so tokens are ranked by an order-preserving key of the
+// logit.  The running sums use fixed-point weights W = floor(2^40 * e) of
+// e = 2^((l - lmax) * log2(e) / T) (f32), summed as 64-bit integers: exact and
+// independent of summation order.  A token is kept when the weight of the
+// tokens ranked before it is below top_p * Z (Z = sum of all weights), which is
+// count(running sum < top_p) + 1 of the page.  The boundary token's key is
+// found by radix selection over the key's four bytes (one pass over the row
+// each), and where the boundary falls inside a run of equal logits, the index
+// of the last kept one by one more pass.  Result per row: tokens with key >
+// cut_key, or key == cut_key and index <= cut_idx, are kept.  top_p >= 1,
+// T = 0 or a non-finite logit keep every token (cut_key = 0).
+struct TopPArgs {
+  const float* logits;
+  int ld, vocab, rows;
+  float temperature, top_p;
+  uint32_t* cut_key;  // [rows]
+  int* cut_idx;       // [rows]
+  const StepParams* sp;  // if non-null: logits, temperature, top_p come from here
+};
+
+// Key that orders floats like their values (-0 and +0 alike; NaN excluded by
+// the caller).
+QD_DEV uint32_t order_key(float l) {
+  const uint32_t b = __float_as_uint(l == 0.f ? 0.f : l);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+QD_DEV float key_value(uint32_t k) { return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k); }
+
+// floor(2^40 * e) for e in [0, 1], exact (e = m * 2^(E - 23)); a row's sum stays
+// below 2^59.
+QD_DEV uint64_t fixed40(float e) {
+  const uint32_t b = __float_as_uint(e);
+  if (b < 0x00800000u) return 0ull;  // zero or below 2^-126
+  const int E = (int)(b >> 23) - 127;
+  const uint64_t m = (b & 0x7FFFFFu) | 0x800000u;
+  const int sh = E + 17;
+  return sh >= 0 ? (m << sh) : (sh > -64 ? (m >> -sh) : 0ull);
+}
+
+QD_DEV uint64_t wave_sum_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += (uint64_t)__shfl_xor((long long)v, o);
+  return v;
+}
+
+__global__ __launch_bounds__(1024) void topp_cut_kernel(TopPArgs a) {
+  constexpr int NW = 16;
+  __shared__ unsigned long long h[NW][256];  // per-wave histograms (row 0: totals)
+  __shared__ float sm_max[NW];
+  __shared__ int sm_bad[NW];
+  __shared__ unsigned long long sm_sel[2];
+  __shared__ int sm_i[2];
+  __shared__ int sm_cnt[NW];
+  if (a.sp) {
+    a.logits = a.sp->logits;
+    a.temperature = a.sp->temperature;
+    a.top_p = a.sp->top_p;
+  }
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* lg = a.logits + (size_t)row * a.ld;
+  const int V = a.vocab;
+  if (!(a.temperature > 0.f) || !(a.top_p < 1.f)) {
+    if (tid == 0) {
+      a.cut_key[row] = 0u;
+      a.cut_idx[row] = 0x7fffffff;
+    }
+    return;
+  }
+  // max logit; a non-finite logit keeps every token
+  float mx = -INFINITY;
+  int bad = 0;
+  for (int v = tid; v < V; v += 1024) {
+    const float l = lg[v];
+    bad |= !isfinite(l);
+    mx = fmaxf(mx, l);
+  }
+  mx = wave_max(mx);
+  bad = __ballot(bad) != 0ull;
+  if (lane == 0) {
+    sm_max[wave] = mx;
+    sm_bad[wave] = bad;
+  }
+  __syncthreads();
+  float lmax = sm_max[0];
+  int anybad = sm_bad[0];
+  for (int w = 1; w < NW; ++w) {
+    lmax = fmaxf(lmax, sm_max[w]);
+    anybad |= sm_bad[w];
+  }
+  const float cw = 1.4426950408889634f / a.temperature;
+  auto weight = [&](float l) { return fixed40(exp2f((l - lmax) * cw)); };
+  // coarse bin of a logit by its distance from the max, 1/8 of a log2 unit of
+  // weight per bin (the last bin takes the rest).  Monotone in the logit, so a
+  // bin is a contiguous range of keys; it spreads a row over many bins, which
+  // the key's top byte does not (logits of one row share a few exponents).
+  auto cbin = [&](float l) { return (int)fminf((lmax - l) * cw * 8.0f, 255.0f); };
+  double target = 0.0;  // top_p * Z, set after the coarse level
+  // selection over the 256 bins of h[0] (bin order given by `desc`: key bytes
+  // run high to low from bin 255, coarse bins from bin 0): the bin where the
+  // running weight crosses the target, the weight before it and its own weight
+  auto select = [&](bool desc, unsigned long long base, int& sel, unsigned long long& before,
+                    unsigned long long& mass) {
+    if (wave == 0) {
+      unsigned long long b4[4], loc = 0ull;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        b4[j] = h[0][desc ? 255 - 4 * lane - j : 4 * lane + j];
+        loc += b4[j];
+      }
+      unsigned long long inc = loc;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const unsigned long long t = (unsigned long long)__shfl_up((long long)inc, o);
+        if (lane >= o) inc += t;
+      }
+      unsigned long long run = base + (inc - loc);
+      int found = -1;
+      unsigned long long f_before = 0ull, f_bin = 0ull;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (found < 0 && b4[j] > 0ull && (double)run < target && (double)(run + b4[j]) >= target) {
+          found = desc ? 255 - 4 * lane - j : 4 * lane + j;
+          f_before = run;
+          f_bin = b4[j];
+        }
+        run += b4[j];
+      }
+      if (lane == 0) sm_i[0] = -1;
+      if (found >= 0) {  // one lane at most: the running sums increase
+        sm_i[0] = found;
+        sm_sel[0] = f_before;
+        sm_sel[1] = f_bin;
+      }
+    }
+    __syncthreads();
+    sel = sm_i[0];
+    before = sm_sel[0];
+    mass = sm_sel[1];
+    __syncthreads();  // everyone has read the selection before h is cleared again
+  };
+  auto clear = [&]() {
+    for (int i = tid; i < NW * 256; i += 1024) (&h[0][0])[i] = 0ull;
+    __syncthreads();
+  };
+  auto total = [&]() {  // per-wave histograms -> h[0]
+    __syncthreads();
+    if (tid < 256) {
+      unsigned long long t = 0ull;
+      for (int w = 0; w < NW; ++w) t += h[w][tid];
+      h[0][tid] = t;
+    }
+    __syncthreads();
+  };
+  auto keep_all = [&]() {
+    if (tid == 0) {
+      a.cut_key[row] = 0u;
+      a.cut_idx[row] = 0x7fffffff;
+    }
+  };
+  if (anybad) {
+    keep_all();
+    return;
+  }
+  // coarse level: weight per coarse bin; the total is Z
+  clear();
+  for (int v = tid; v < V; v += 1024) {
+    const float l = lg[v];
+    atomicAdd(&h[wave][cbin(l)], weight(l));
+  }
+  total();
+  if (tid < 64) {
+    unsigned long long z = h[0][tid] + h[0][tid + 64] + h[0][tid + 128] + h[0][tid + 192];
+    z = wave_sum_u64(z);
+    if (tid == 0) sm_sel[0] = z;
+  }
+  __syncthreads();
+  const unsigned long long Z = sm_sel[0];
+  target = (double)a.top_p * (double)Z;  // Z < 2^59: rounded to double, relative 2^-53
+  if (target < 0.5) target = 0.5;               // top_p <= 0: the first token only
+  __syncthreads();
+  if (target > (double)Z) {
+    keep_all();
+    return;
+  }
+  int cb;
+  unsigned long long above, tie_mass;
+  select(false, 0ull, cb, above, tie_mass);
+  if (cb < 0) {
+    keep_all();
+    return;
+  }
+  // exact levels over the key's four bytes, among the tokens of coarse bin cb
+  uint32_t prefix = 0u, mask = 0u;
+  for (int level = 0; level < 4; ++level) {
+    const int sh = 24 - 8 * level;
+    clear();
+    for (int v = tid; v < V; v += 1024) {
+      const float l = lg[v];
+      const uint32_t k = order_key(l);
+      if ((k & mask) == prefix && cbin(l) == cb) atomicAdd(&h[wave][(k >> sh) & 255u], weight(l));
+    }
+    total();
+    int d;
+    unsigned long long before, mass;
+    select(true, above, d, before, mass);
+    if (d < 0) {  // guard: the candidates' weight cannot reach the target
+      keep_all();
+      return;
+    }
+    above = before;
+    tie_mass = mass;
+    prefix |= (uint32_t)d << sh;
+    mask |= 255u << sh;
+  }
+  // prefix = key of the boundary token, above = weight of the larger keys,
+  // tie_mass = weight of the tokens with the boundary key (all equal weights)
+  int cut = 0x7fffffff;
+  const unsigned long long w1 = weight(key_value(prefix));
+  const unsigned long long cnt = w1 ? tie_mass / w1 : 0ull;
+  const double need = w1 ? ceil((target - (double)above) / (double)w1) : 0.0;  // ties to keep, >= 1
+  if (w1 && need < (double)cnt) {
+    const int n_need = (int)need;
+    // the n_need-th token (in index order) with the boundary key
+    const int seg = (V + 1023) / 1024, b0 = min(V, tid * seg), b1 = min(V, b0 + seg);
+    int c_t = 0;
+    for (int v = b0; v < b1; ++v) c_t += order_key(lg[v]) == prefix;
+    int inc = c_t;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(inc, o);
+      if (lane >= o) inc += t;
+    }
+    if (lane == 63) sm_cnt[wave] = inc;
+    if (tid == 0) sm_i[1] = 0x7fffffff;
+    __syncthreads();
+    int before = inc - c_t;
+    for (int w = 0; w < wave; ++w) before += sm_cnt[w];
+    if (before < n_need && before + c_t >= n_need) {
+      int r = before;
+      for (int v = b0; v < b1; ++v)
+        if (order_key(lg[v]) == prefix && ++r == n_need) {
+          sm_i[1] = v;
+          break;
+        }
+    }
+    __syncthreads();
+    cut = sm_i[1];
+  }
+  if (tid == 0) {
+    a.cut_key[row] = prefix;
+    a.cut_idx[row] = cut;
+  }
+}
 
 struct SampleArgs {
   const float* logits;
@@ -204,6 +464,8 @@ struct SampleArgs {
   int* out;        // [rows]
   int* out2;       // optional second copy
   const StepParams* sp;  // if non-null: logits, out, temperature, seed, step come from here
+  const uint32_t* cut_key;  // if non-null: top-p cut per row (see topp_cut_kernel)
+  const int* cut_idx;
 };
 
 QD_DEV void sample_resolve(SampleArgs& a) {
@@ -237,6 +499,8 @@ __global__ __launch_bounds__(256) void sample_stage1_kernel(SampleArgs a) {
   int bi = 0x7fffffff;
   bool have = false;
   const bool sampled = a.temperature > 0.f;
+  const uint32_t ck = a.cut_key ? a.cut_key[row] : 0u;
+  const int ci = a.cut_key ? a.cut_idx[row] : 0;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int v0 = c * kSampleChunk + 4 * (tid + 256 * k);
@@ -251,6 +515,10 @@ __global__ __launch_bounds__(256) void sample_stage1_kernel(SampleArgs a) {
       const int v = v0 + w;
       if (v >= a.vocab) break;
       float s = lg[v];
+      if (a.cut_key) {  // tokens outside the top-p nucleus take no part
+        const uint32_t k = order_key(s);
+        if (k < ck || (k == ck && v > ci)) continue;
+      }
       if (sampled) {
         float u = philox_uniform(r.v[w]);
         s = s / a.temperature - logf(-logf(u));

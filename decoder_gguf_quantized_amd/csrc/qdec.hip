@@ -112,6 +112,8 @@ struct qdec_model {
   int chunk = 0, nchunk = 0;
   float* s_v = nullptr;
   int* s_i = nullptr;
+  uint32_t* cut_key = nullptr;  // [max_seqs] top-p cut per row
+  int* cut_idx = nullptr;
   int nvchunk = 0;
   int* d_pos = nullptr;
   int* d_tok = nullptr;
@@ -424,9 +426,15 @@ void embed(qdec_model* m, hipStream_t st, const int* d_tokens, int n, float* out
 }
 
 void sample(qdec_model* m, hipStream_t st, const float* logits, int ld, int rows, float temp, uint64_t seed,
-            uint64_t step, int* out, int* out2, const StepParams* sp = nullptr) {
+            uint64_t step, int* out, int* out2, const StepParams* sp = nullptr, bool topp = false) {
   const int V = m->cfg.vocab;
-  SampleArgs a{logits, ld, V, rows, temp, seed, step, m->s_v, m->s_i, m->nvchunk, out, out2, sp};
+  SampleArgs a{logits, ld, V, rows, temp, seed, step, m->s_v, m->s_i, m->nvchunk, out, out2, sp,
+               topp ? m->cut_key : nullptr, topp ? m->cut_idx : nullptr};
+  if (topp) {
+    TopPArgs t{logits, ld, V, rows, temp, 1.f, m->cut_key, m->cut_idx, sp};
+    Timed tm(m, st, "topp_cut", (double)rows * V * 4 * 6, 0);
+    qlaunch(topp_cut_kernel, rows, 1024, 0, st, t);
+  }
   {
     Timed tm(m, st, "sample", (double)rows * V * 4, 0);
     qlaunch(sample_stage1_kernel, dim3(m->nvchunk, rows), 256, 0, st, a);
@@ -485,13 +493,13 @@ void blocks(qdec_model* m, hipStream_t st, int n, int seq, int pos0, const int* 
 
 // One decode step for sequences 0..n-1 reading tokens, positions and the
 // step's parameters from device memory (so it can be captured and replayed).
-void decode_body(qdec_model* m, hipStream_t st, int n) {
+void decode_body(qdec_model* m, hipStream_t st, int n, bool topp) {
   const qdec_config& c = m->cfg;
   embed(m, st, m->d_tok, n, m->x);
   blocks(m, st, n, 0, 0, m->d_pos);
   gemv(m, st, m->lm(), m->x, c.hidden, m->output_norm, c.rms_eps, nullptr, c.vocab, n, kModeStore,
        &m->d_params->logits);
-  sample(m, st, nullptr, c.vocab, n, 0.f, 0, 0, nullptr, nullptr, m->d_params);
+  sample(m, st, nullptr, c.vocab, n, 0.f, 0, 0, nullptr, nullptr, m->d_params, topp);
 }
 
 // ------------------------------------------------------------ error handling
@@ -865,6 +873,8 @@ int load(const qdec_config* cfgp, const qdec_tensor* ts, int32_t n, int32_t max_
     m->nvchunk = (c.vocab + kSampleChunk - 1) / kSampleChunk;
     m->s_v = m->dalloc<float>((size_t)max_seqs * m->nvchunk);
     m->s_i = m->dalloc<int>((size_t)max_seqs * m->nvchunk);
+    m->cut_key = m->dalloc<uint32_t>(max_seqs);
+    m->cut_idx = m->dalloc<int>(max_seqs);
     m->d_pos = m->dalloc<int>(64);
     m->d_tok = m->dalloc<int>(64);
     m->counters = m->dalloc<int>((size_t)max_seqs * c.n_head_kv);
@@ -961,7 +971,7 @@ int qdec_prefill(qdec_model* m, int32_t seq, const int32_t* tokens, int32_t n_to
 }
 
 int qdec_decode_step(qdec_model* m, const int32_t* tokens, int32_t n_seqs, float* d_logits, int32_t* d_token_out,
-                     float temperature, uint64_t seed, uint64_t step, uint32_t flags, void* stream) {
+                     float temperature, float top_p, uint64_t seed, uint64_t step, uint32_t flags, void* stream) {
   g_err.clear();
   if (int rc = check_usable(m)) return rc;
   hipStream_t st = (hipStream_t)stream;
@@ -969,6 +979,7 @@ int qdec_decode_step(qdec_model* m, const int32_t* tokens, int32_t n_seqs, float
   if (n_seqs < 1 || n_seqs > m->max_seqs) { set_err("n_seqs %d outside [1, %d]", n_seqs, m->max_seqs); return QDEC_REFUSED; }
   if (!tokens || !d_logits || !d_token_out) { set_err("tokens, d_logits and d_token_out must not be NULL"); return QDEC_REFUSED; }
   if (!(temperature >= 0.f) || !std::isfinite(temperature)) { set_err("temperature must be finite and >= 0"); return QDEC_REFUSED; }
+  if (std::isnan(top_p)) { set_err("top_p must not be NaN"); return QDEC_REFUSED; }
   if (flags & ~(uint32_t)QDEC_TOKENS_ON_DEVICE) { set_err("decode: unknown flag bits 0x%x", flags); return QDEC_REFUSED; }
   const bool on_dev = flags & QDEC_TOKENS_ON_DEVICE;
   for (int s = 0; s < n_seqs; ++s) {
@@ -991,7 +1002,8 @@ int qdec_decode_step(qdec_model* m, const int32_t* tokens, int32_t n_seqs, float
     sa.d_pos = m->d_pos;
     sa.d_tok = m->d_tok;
     sa.err = m->err_dev;
-    sa.params = StepParams{temperature, n_seqs, seed, step, d_logits, d_token_out};
+    sa.params = StepParams{temperature, top_p, n_seqs, seed, step, d_logits, d_token_out};
+    const bool topp = temperature > 0.f && top_p < 1.f;
     sa.d_params = m->d_params;
     sa.rope_g = m->rope_g;
     sa.rope_l = m->rope_l;
@@ -1003,14 +1015,14 @@ int qdec_decode_step(qdec_model* m, const int32_t* tokens, int32_t n_seqs, float
       qlaunch(step_begin_kernel, 1, 256, 0, st, sa);
     }
     if (m->timing) {
-      decode_body(m, st, n_seqs);
+      decode_body(m, st, n_seqs, topp);
     } else {
-      hipGraphExec_t& ge = m->graphs[n_seqs];
+      hipGraphExec_t& ge = m->graphs[2 * n_seqs + (topp ? 1 : 0)];  // graph per (batch size, top-p on)
       if (!ge) {
         hipGraph_t graph = nullptr;
         hipck(hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeThreadLocal), "hipStreamBeginCapture");
         try {
-          decode_body(m, m->cap_stream, n_seqs);
+          decode_body(m, m->cap_stream, n_seqs, topp);
         } catch (...) {
           (void)hipStreamEndCapture(m->cap_stream, &graph);
           if (graph) (void)hipGraphDestroy(graph);
@@ -1124,26 +1136,40 @@ int qdec_debug_embed(qdec_model* m, const int32_t* d_tokens, int32_t n, float* d
   return QDEC_OK;
 }
 
-int qdec_debug_sample(const float* d_logits, int32_t rows, int32_t vocab, float temperature, uint64_t seed,
-                      uint64_t step, int32_t* d_out, void* stream) {
+int qdec_debug_sample(const float* d_logits, int32_t rows, int32_t vocab, float temperature, float top_p,
+                      uint64_t seed, uint64_t step, int32_t* d_out, void* stream) {
   g_err.clear();
   if (!d_logits || !d_out || rows <= 0 || vocab <= 0) { set_err("bad arguments"); return QDEC_REFUSED; }
   if (!(temperature >= 0.f) || !std::isfinite(temperature)) { set_err("temperature must be finite and >= 0"); return QDEC_REFUSED; }
+  if (std::isnan(top_p)) { set_err("top_p must not be NaN"); return QDEC_REFUSED; }
   hipStream_t st = (hipStream_t)stream;
   const int nch = (vocab + kSampleChunk - 1) / kSampleChunk;
+  const bool topp = temperature > 0.f && top_p < 1.f;
   float* pv = nullptr;
   int* pi = nullptr;
-  if (hipMalloc(&pv, (size_t)rows * nch * 4) != hipSuccess || hipMalloc(&pi, (size_t)rows * nch * 4) != hipSuccess) {
+  uint32_t* ck = nullptr;
+  int* ci = nullptr;
+  if (hipMalloc(&pv, (size_t)rows * nch * 4) != hipSuccess || hipMalloc(&pi, (size_t)rows * nch * 4) != hipSuccess ||
+      hipMalloc(&ck, (size_t)rows * 4) != hipSuccess || hipMalloc(&ci, (size_t)rows * 4) != hipSuccess) {
     (void)hipFree(pv);
+    (void)hipFree(pi);
+    (void)hipFree(ck);
     set_err("internal: hipMalloc failed");
     return QDEC_INTERNAL;
   }
-  SampleArgs a{d_logits, vocab, vocab, rows, temperature, seed, step, pv, pi, nch, d_out, nullptr, nullptr};
+  SampleArgs a{d_logits, vocab, vocab, rows, temperature, seed, step, pv, pi, nch, d_out, nullptr, nullptr,
+               topp ? ck : nullptr, topp ? ci : nullptr};
+  if (topp) {
+    TopPArgs t{d_logits, vocab, vocab, rows, temperature, top_p, ck, ci, nullptr};
+    qlaunch(topp_cut_kernel, rows, 1024, 0, st, t);
+  }
   qlaunch(sample_stage1_kernel, dim3(nch, rows), 256, 0, st, a);
   qlaunch(sample_stage2_kernel, rows, 64, 0, st, a);
   hipError_t e = hipStreamSynchronize(st);
   (void)hipFree(pv);
   (void)hipFree(pi);
+  (void)hipFree(ck);
+  (void)hipFree(ci);
   if (e != hipSuccess) { set_err("internal: %s", hipGetErrorString(e)); return QDEC_INTERNAL; }
   return QDEC_OK;
 }

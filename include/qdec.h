@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define QDEC_ABI_VERSION 1
+#define QDEC_ABI_VERSION 2
 
 enum { QDEC_OK = 0, QDEC_REFUSED = 1, QDEC_INTERNAL = 2 };
 
@@ -119,13 +119,19 @@ int qdec_prefill(qdec_model* m, int32_t seq, const int32_t* tokens, int32_t n_to
  * greedy argmax (lowest index on ties); temperature > 0: argmax of
  * logits/temperature + Gumbel noise from Philox4x64-10 with key (seed, 0) and
  * counter (v/4, step, s, 0), word v%4, u = ((r>>41)+0.5)*2^-23.
+ * top_p < 1 with temperature > 0 restricts the draw to the nucleus ([W] Step 8
+ * sampler): with p = softmax(logits/temperature) sorted descending (equal
+ * logits by lower index), the first count(running sum < top_p) + 1 tokens
+ * (top_p <= 0: the first token).  The running sums use per-token weights
+ * floor(2^40 * 2^((l - max l) * log2(e) / temperature)) (f32) summed exactly;
+ * a row with a non-finite logit keeps every token.  top_p >= 1: no restriction.
  * With QDEC_TOKENS_ON_DEVICE, tokens is a device pointer; ids outside [0, vocab)
  * are clamped and latch an error reported as QDEC_INTERNAL by the next call.
  * Refused: n_seqs outside [1, max_seqs], any kv_len(s) == max_ctx, a host token
- * out of range, temperature < 0 or NaN, NULL outputs. */
+ * out of range, temperature < 0 or NaN, top_p NaN, NULL outputs. */
 int qdec_decode_step(qdec_model* m, const int32_t* tokens, int32_t n_seqs, float* d_logits,
-                     int32_t* d_token_out, float temperature, uint64_t seed, uint64_t step,
-                     uint32_t flags, void* stream);
+                     int32_t* d_token_out, float temperature, float top_p, uint64_t seed,
+                     uint64_t step, uint32_t flags, void* stream);
 
 /* Forget the cached positions of one sequence (seq = -1: all).  Host-side only;
  * stale KV rows are never read past kv_len. */
@@ -159,9 +165,10 @@ int qdec_debug_embed(qdec_model* m, const int32_t* d_tokens, int32_t n, float* d
 
 /* Row-wise token choice over d_logits [rows][vocab] with the decode step's rule
  * (temperature 0: argmax with the lowest index on ties, NaN ranking above every
- * number; else Gumbel-max with counter (v/4, step, row, 0)).  d_out int32 [rows]. */
+ * number; else Gumbel-max with counter (v/4, step, row, 0), restricted to the
+ * top-p nucleus when top_p < 1).  d_out int32 [rows]. */
 int qdec_debug_sample(const float* d_logits, int32_t rows, int32_t vocab, float temperature,
-                      uint64_t seed, uint64_t step, int32_t* d_out, void* stream);
+                      float top_p, uint64_t seed, uint64_t step, int32_t* d_out, void* stream);
 
 /* One projection y[r][n] = sum_k W[n][k] x[r][k] with the forward pass's kernels:
  * the decode GEMV for n_x <= 16, the prefill MFMA GEMM above.  W is given in GGUF

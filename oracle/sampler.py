@@ -119,25 +119,21 @@ def nucleus(logits, temperature, top_p):
 
 
 def nucleus_margin(logits, temperature, top_p):
-    """How far the kept set is from changing: the smallest of |run - top_p| /
-    top_p at the last kept and the first dropped running sum, and the smallest
-    relative gap between the probability at the boundary and its neighbours in
-    the sorted order (near-equal probabilities can swap order under rounding).
-    Infinity when every token is kept by rule."""
+    """How far the kept set is from changing under rounding of the running
+    sums: the smaller of |run - top_p| / top_p at the last kept and the first
+    dropped running sum (infinity when every token is kept by rule).  The order
+    itself cannot change: for T > 0 it is the order of the given logits, which
+    any implementation sees exactly."""
     lg = np.asarray(logits, dtype=np.float64)
     if top_p >= 1 or temperature == 0 or not np.all(np.isfinite(lg)):
         return np.inf
     p = softmax_t(lg, temperature)
-    order = np.argsort(-p, kind="stable")
-    ps = p[order]
-    run = np.cumsum(ps)
+    run = np.cumsum(p[np.argsort(-p, kind="stable")])
     c = int(np.sum(run < top_p)) + 1
     m = np.inf
     for k in (c - 2, c - 1):
         if 0 <= k < run.size:
             m = min(m, abs(run[k] - top_p) / top_p)
-    if c < ps.size:
-        m = min(m, (ps[c - 1] - ps[c]) / ps[c - 1])
     return m
 
 

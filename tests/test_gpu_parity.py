@@ -102,6 +102,96 @@ def test_gumbel_sampling_matches_oracle(temperature):
     assert agree >= 60
 
 
+# ---------------------------------------------------------------- top-p
+def _f32(x):
+    return float(np.float32(x))  # the value the library receives
+
+
+@pytest.mark.parametrize("temperature,top_p,V,scale", [
+    (1.0, 0.9, 151936, 3.0), (0.7, 0.5, 151936, 3.0), (1.3, 0.05, 151936, 3.0),
+    # at 0.99 a 151,936-entry row's boundary sits where running sums differ by
+    # ~1e-8: every row is within rounding of changing, so a smaller vocabulary
+    (1.0, 0.99, 8192, 1.0),
+])
+def test_top_p_sampling_matches_oracle(temperature, top_p, V, scale):
+    """Gumbel-max restricted to the nucleus on the same logits: the GPU token is
+    the oracle's wherever the nucleus boundary is more than 1e-6 (relative) from
+    changing and the top-2 perturbed scores differ by more than 1e-4; it is
+    always a token the oracle's nucleus keeps, up to boundary ambiguity."""
+    rng = np.random.default_rng(int(top_p * 100))
+    rows = 8
+    L = (rng.standard_normal((rows, V)) * scale).astype(np.float32)
+    out = torch.empty(rows, dtype=torch.int32, device=dev())
+    p = _f32(top_p)
+    agree = 0
+    for step in range(3):
+        qdec.debug_sample(torch.from_numpy(L).to(dev()), temperature, 9, step, out, top_p=p)
+        torch.cuda.synchronize()
+        got = as_np(out)
+        for r in range(rows):
+            if sampler.nucleus_margin(L[r], temperature, p) <= 1e-6:
+                continue
+            keep = sampler.nucleus(L[r], temperature, p)
+            assert keep[got[r]], (step, r)
+            s = sampler.scores(L[r], temperature, 9, step, r, p)
+            top2 = np.partition(s[keep], -2)[-2:] if keep.sum() > 1 else np.array([-np.inf, 0.0])
+            if top2[1] - top2[0] > 1e-4:
+                assert got[r] == int(np.argmax(s)), (step, r)
+                agree += 1
+    assert agree >= 8
+
+
+@pytest.mark.parametrize("top_p,kept", [(0.5, 32), (0.3, 20), (0.25, 16), (1e-9, 1), (0.0, 1)])
+def test_top_p_boundary_inside_equal_logits(top_p, kept):
+    """64 equal logits (probabilities 1/64, running sums exact): the nucleus is
+    the first `kept` tokens by index on both sides, so every draw is the
+    oracle's and stays below index `kept`."""
+    V = 64
+    L = np.zeros((4, V), np.float32)
+    L[1] += 2.5
+    L[2] -= 7.0
+    L[3, :] = -0.0
+    out = torch.empty(4, dtype=torch.int32, device=dev())
+    p = _f32(top_p)
+    for r in range(4):
+        assert sampler.nucleus(L[r], 1.0, p).sum() == kept
+    for step in range(12):
+        qdec.debug_sample(torch.from_numpy(L).to(dev()), 1.0, 3, step, out, top_p=p)
+        torch.cuda.synchronize()
+        got = as_np(out).tolist()
+        want = [sampler.sample(L[r], 1.0, 3, step, r, p) for r in range(4)]
+        assert got == want, (step, got, want)
+        assert max(got) < kept
+
+
+def test_top_p_mixed_rows_and_limits():
+    """A peaked row (small nucleus), ties straddling the boundary after a run of
+    distinct values, a row with NaN (every token kept: the first NaN wins), and
+    top_p >= 1 (plain Gumbel-max)."""
+    V = 5000
+    rng = np.random.default_rng(12)
+    L = (rng.standard_normal((3, V)) * 0.5).astype(np.float32)
+    L[0, 123] = 9.0; L[0, 4000] = 8.5; L[0, 77] = 8.0
+    L[1, :40] = 6.0; L[1, 40:] = -30.0; L[1, 3] = 6.5     # boundary inside the 6.0 run
+    L[2, 17] = np.nan
+    out = torch.empty(3, dtype=torch.int32, device=dev())
+    for top_p in (0.6, 0.95, 1.0):
+        p = _f32(top_p)
+        for step in range(6):
+            qdec.debug_sample(torch.from_numpy(L).to(dev()), 1.0, 21, step, out, top_p=p)
+            torch.cuda.synchronize()
+            got = as_np(out).tolist()
+            want = [sampler.sample(L[r], 1.0, 21, step, r, p) for r in range(3)]
+            assert got == want, (top_p, step, got, want)
+
+
+def test_top_p_nan_is_refused():
+    L = torch.zeros((1, 10), dtype=torch.float32, device=dev())
+    out = torch.empty(1, dtype=torch.int32, device=dev())
+    with pytest.raises(qdec.QdecError):
+        qdec.debug_sample(L, 1.0, 0, 0, out, top_p=float("nan"))
+
+
 # ---------------------------------------------------------------- projections
 MATMUL_CASES = [
     # (type, rows, cols, n_x)
@@ -236,6 +326,52 @@ def test_two_sequences_are_independent():
     check_row(as_np(dl)[0], o[0])
     check_row(as_np(dl)[1], o[1])
     assert m.kv_len(0) == 31 and m.kv_len(1) == 46
+
+
+def test_decode_step_top_p_follows_the_oracle_sampler():
+    """Two sequences, temperature 0.8 with top_p 0.9, tokens fed back on the
+    device: each step's logits match the oracle (teacher forced) and each
+    sampled token is the oracle sampler's on the GPU's logits wherever the
+    nucleus boundary and the top-2 perturbed scores are clear.  Greedy steps in
+    between use the graph without the top-p cut; a top_p >= 1 step equals plain
+    Gumbel-max."""
+    cfg, t, m = model_for("qwen3_hd128_g2")
+    V = cfg["vocab"]
+    p0, p1 = synth.prompt(cfg, 20), synth.prompt(cfg, 33, tag="other")
+    lg = torch.empty(V, dtype=torch.float32, device=dev())
+    m.kv_reset()
+    m.prefill(0, p0, lg)
+    m.prefill(1, p1, lg)
+    om = OracleModel(cfg, t, max_ctx=64, n_seqs=2)
+    om.forward(0, p0)
+    om.forward(1, p1)
+    T, P = 0.8, _f32(0.9)
+    toks = torch.tensor([3, 7], dtype=torch.int32, device=dev())
+    plan = [(T, P), (T, P), (0.0, 1.0), (T, P), (T, 1.0), (T, P)]
+    checked = 0
+    for step, (temp, top_p) in enumerate(plan):
+        inp = as_np(toks).tolist()
+        dl = torch.empty((2, V), dtype=torch.float32, device=dev())
+        out = torch.empty(2, dtype=torch.int32, device=dev())
+        m.decode_step(toks, dl, out, temperature=temp, seed=77, step=step, top_p=top_p)
+        torch.cuda.synchronize()
+        g = as_np(dl)
+        o = om.decode(inp)
+        got = as_np(out).tolist()
+        for sq in range(2):
+            check_row(g[sq], o[sq])
+            if temp == 0.0:
+                assert got[sq] == sampler.greedy(g[sq])
+                continue
+            if sampler.nucleus_margin(g[sq], temp, top_p) <= 1e-6:
+                continue
+            sc = sampler.scores(g[sq], temp, 77, step, sq, top_p)
+            top2 = np.partition(sc, -2)[-2:]
+            if top2[1] - top2[0] > 1e-4:
+                assert got[sq] == int(np.argmax(sc)), (step, sq)
+                checked += 1
+        toks = out
+    assert checked >= 8
 
 
 def test_refusals_leave_handle_usable():

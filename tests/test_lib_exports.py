@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version(L):
-    assert L.qdec_abi_version() == 1
+    assert L.qdec_abi_version() == 2
 
 
 def cfg(**kw):
@@ -79,14 +79,14 @@ def test_missing_and_malformed_tensors_are_refused(L):
 
 def test_null_handle_calls_are_refused(L):
     assert L.qdec_prefill(None, 0, None, 1, None, None, 0, None) == 1
-    assert L.qdec_decode_step(None, None, 1, None, None, 0.0, 0, 0, 0, None) == 1
+    assert L.qdec_decode_step(None, None, 1, None, None, 0.0, 1.0, 0, 0, 0, None) == 1
     assert L.qdec_kv_reset(None, 0) == 1
     assert L.qdec_free(None) == 1
     assert L.qdec_poisoned(None) == -1
     out = ctypes.c_int32()
     assert L.qdec_kv_len(None, 0, ctypes.byref(out)) == 1
     assert L.qdec_debug_matmul(3, 4, 4, None, 0, None, 1, None, None) == 1
-    assert L.qdec_debug_sample(None, 1, 1, 0.0, 0, 0, None, None) == 1
+    assert L.qdec_debug_sample(None, 1, 1, 0.0, 1.0, 0, 0, None, None) == 1
 
 
 def test_binding_range_checks_and_ownership():
