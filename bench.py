@@ -25,6 +25,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
 FP32_MFMA_PEAK = 157.3e12  # FLOP/s, MI355X dense FP32 matrix
+BF16_MFMA_PEAK = 2.5e15    # FLOP/s, MI355X dense BF16 matrix
+PREFILL_TERMS = {"f32": 0, "bf16x3": 3, "bf16": 1}
 
 
 def step_bytes_decode(cfg, pos):
@@ -45,6 +47,16 @@ def step_bytes_decode(cfg, pos):
             n_keys = min(n_keys, cfg["window"])
         kv += cfg["n_head_kv"] * cfg["head_dim"] * 8 * (n_keys + 1)  # read keys + write the new one
     return layer_w + head_bytes + B * (kv + row + cfg["vocab"] * 4)
+
+
+def prefill_attn_flops(cfg, T):
+    import synth
+    hd, nq = cfg["head_dim"], cfg["n_head"]
+    attn = 0
+    for l in range(cfg["n_layer"]):
+        w = 0 if synth.layer_is_global(cfg, l) else cfg["window"]
+        attn += 4 * hd * nq * sum(min(i + 1, w) if w else i + 1 for i in range(T))
+    return attn
 
 
 def prefill_flops(cfg, T):
@@ -233,6 +245,8 @@ def main():
     ap.add_argument("--config", default="c2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=None, help="override the workload's decode steps (profiling runs)")
+    ap.add_argument("--prefill-precision", default="f32", choices=sorted(PREFILL_TERMS),
+                    help="operand precision of the prefill projections (default f32)")
     ap.add_argument("--top-p", type=float, default=None,
                     help="batched workload only: restrict sampling to the top-p nucleus (default: none)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -268,6 +282,7 @@ def main():
     T, N, V = cfg["prompt_len"], cfg["decode_steps"], cfg["vocab"]
     prompt = synth.prompt(cfg)
     model = qdec.Model(cfg, tensors, max_seqs=1, max_ctx=T + N + 1)
+    model.set_prefill_precision(args.prefill_precision)
     pl = torch.empty(V, dtype=torch.float32, device=dev)
     dl = torch.empty((N, V), dtype=torch.float32, device=dev)
     toks = torch.empty((N + 1, 1), dtype=torch.int32, device=dev)
@@ -297,6 +312,13 @@ def main():
     for _ in range(args.warmup):
         run(1)
     wall, pre_ms, dec_ms = run(args.steps)
+    # the exact three-term bf16 prefill alongside the default f32 one (same prompt)
+    alt_pre_ms = None
+    if args.prefill_precision == "f32":
+        model.set_prefill_precision("bf16x3")
+        run(1)
+        alt_pre_ms = [run(1)[1][0] for _ in range(args.steps)]
+        model.set_prefill_precision("f32")
     # second pass of the same steps with per-dispatch events for the roofline figure
     model.kernel_timing(True)
     run(args.steps)
@@ -307,7 +329,12 @@ def main():
     pre_tok_s = args.steps * T / (sum(pre_ms) / 1e3)
     bytes_dec = sum(step_bytes_decode(cfg, T + s) for s in range(N))
     hbm_frac = bytes_dec / (np.mean(dec_ms) / 1e3) / HBM_PEAK
-    mfma_util = prefill_flops(cfg, T) / (np.mean(pre_ms) / 1e3) / FP32_MFMA_PEAK
+    # f32 path: algorithmic flops against the FP32 matrix peak.  bf16 paths:
+    # also the bf16 MFMA work actually issued (terms x the projections' flops)
+    # against the BF16 matrix peak.
+    pre_s = np.mean(pre_ms) / 1e3
+    mfma_util = prefill_flops(cfg, T) / pre_s / FP32_MFMA_PEAK
+    nt = PREFILL_TERMS[args.prefill_precision]
     line = {
         "metric": "decode tokens/sec + HBM GB/s fraction; prefill tokens/sec + MFMA util",
         "value": round(dec_tok_s, 2),
@@ -325,11 +352,17 @@ def main():
                    "prompt": T, "decode_steps": N, "batch": 1, "weights": cfg["wtype"]},
         "prefill_tokens_per_s": round(pre_tok_s, 1),
         "prefill_mfma_util": round(float(mfma_util), 4),
+        "prefill_precision": args.prefill_precision,
         "decode_hbm_frac": round(float(hbm_frac), 4),
         "decode_ms_per_token": round(float(np.mean(dec_ms)) / N, 4),
         "roofline": roofline_entry(kst, cfg["key"]),
         "kernels": {k: dict(launches=v["launches"], ms=round(v["ms"], 3)) for k, v in sorted(kst.items())},
     }
+    if alt_pre_ms:
+        line["prefill_tokens_per_s_bf16x3"] = round(args.steps * T / (sum(alt_pre_ms) / 1e3), 1)
+    if nt:
+        proj = prefill_flops(cfg, T) - prefill_attn_flops(cfg, T)
+        line["prefill_bf16_mfma_util"] = round(float(nt * proj / pre_s / BF16_MFMA_PEAK), 4)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, tensors)
     print(json.dumps(line), flush=True)

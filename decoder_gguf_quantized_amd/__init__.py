@@ -85,11 +85,12 @@ def lib():
                 "qdec_kv_write": (ctypes.c_int, [P, I32, I32, P, P, I32, P]),
                 "qdec_kv_len": (ctypes.c_int, [P, I32, ctypes.POINTER(I32)]),
                 "qdec_poisoned": (ctypes.c_int, [P]),
+                "qdec_set_prefill_precision": (ctypes.c_int, [P, I32]),
                 "qdec_free": (ctypes.c_int, [P]),
                 "qdec_debug_dequant": (ctypes.c_int, [P, ctypes.c_char_p, P, P]),
                 "qdec_debug_embed": (ctypes.c_int, [P, P, I32, P, P]),
                 "qdec_debug_sample": (ctypes.c_int, [P, I32, I32, F, F, U64, U64, P, P]),
-                "qdec_debug_matmul": (ctypes.c_int, [I32, I64, I64, P, I64, P, I32, P, P]),
+                "qdec_debug_matmul": (ctypes.c_int, [I32, I64, I64, P, I64, P, I32, P, I32, P]),
                 "qdec_kernel_timing": (ctypes.c_int, [P, I32, ctypes.POINTER(_KStat), I32, ctypes.POINTER(I32)]),
             }
             for name, (res, args) in sig.items():
@@ -297,6 +298,11 @@ class Model:
                                     _int("seed", seed, _U64), _int("step", step, _U64), flags, _stream())
         self._check(rc)
 
+    def set_prefill_precision(self, precision):
+        """Operand precision of later prefill projections: "f32" (default),
+        "bf16x3" (exact three-term bf16 split of the activations) or "bf16"."""
+        self._check(lib().qdec_set_prefill_precision(self._handle(), _precision(precision)))
+
     def kv_reset(self, seq=-1):
         self._check(lib().qdec_kv_reset(self._handle(), _int("seq", seq)))
 
@@ -363,9 +369,18 @@ def debug_sample(logits, temperature, seed, step, out, top_p=1.0):
         raise (QdecError if rc == 1 else QdecPanic)(_last_error())
 
 
-def debug_matmul(ttype, rows, cols, raw, x, y):
+PREFILL_PRECISIONS = {"f32": 0, "bf16x3": 1, "bf16": 2}
+
+
+def _precision(name):
+    if name not in PREFILL_PRECISIONS:
+        raise QdecError(f"prefill precision must be one of {sorted(PREFILL_PRECISIONS)}, got {name!r}")
+    return PREFILL_PRECISIONS[name]
+
+
+def debug_matmul(ttype, rows, cols, raw, x, y, precision="f32"):
     """y[r] = W x[r] with the forward pass's projection kernels (GEMV for <= 16
-    rows, MFMA GEMM above); W given as GGUF bytes."""
+    rows, MFMA GEMM above, operands in ``precision``); W given as GGUF bytes."""
     import numpy as np
     import torch
     raw = np.ascontiguousarray(np.asarray(raw, dtype=np.uint8))
@@ -373,6 +388,6 @@ def debug_matmul(ttype, rows, cols, raw, x, y):
     kp = ((cols + 31) // 32) * 32
     rc = lib().qdec_debug_matmul(_int("type", ttype), rows, cols, raw.ctypes.data, raw.nbytes,
                                  _dev_ptr("x", x, torch.float32, n * kp), _int("n_x", n),
-                                 _dev_ptr("y", y, torch.float32, n * rows), _stream())
+                                 _dev_ptr("y", y, torch.float32, n * rows), _precision(precision), _stream())
     if rc:
         raise (QdecError if rc == 1 else QdecPanic)(_last_error())

@@ -215,15 +215,18 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
     }
   }
   // online softmax over one position; masked positions leave the state as is
-  // (selects, no branch: every lane of a stream group takes the same path)
+  // (selects, no branch: every lane of a stream group takes the same path).
+  // A masked position's row may never have been written (cache rows past the
+  // new position are requested ahead), so its values are replaced by zeros
+  // before any arithmetic: 0 * NaN would otherwise reach the output.
   auto accumulate = [&](int j, const float (&kc)[8], const float (&vc)[8]) {
     const bool valid = j >= start && j < end;
     const bool is_new = has_new && j == p;  // the cache row is written above; use the registers
     float k[8], v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      k[e] = is_new ? kn[e] : kc[e];
-      v[e] = is_new ? vn[e] : vc[e];
+      k[e] = is_new ? kn[e] : (valid ? kc[e] : 0.f);
+      v[e] = is_new ? vn[e] : (valid ? vc[e] : 0.f);
     }
 #pragma unroll
     for (int h = 0; h < G; ++h) {

@@ -305,4 +305,162 @@ __global__ __launch_bounds__(256, 1) void gemm_ksplit_kernel(GemmArgs a) {
   }
 }
 
+// bf16-operand variant (Q8_0 / Q4_0 weights).  Quant values are small integers,
+// exact in bf16; the block scale d stays f32 and multiplies each block's
+// partial sums.  Activations are split into NT bf16 terms, x = x1 + x2 + x3
+// with x1 = bf16(x), x2 = bf16(x - x1), x3 = x - x1 - x2 (NT = 3: exact, since
+// f32 has 24 significant bits and each term takes 8; every product q * x_t is
+// exact in the f32 accumulator, so the path is the f32 product up to summation
+// order), or x ~ x1 (NT = 1: plain bf16 rounding of the activations).
+// V_MFMA_F32_32X32X16_BF16: A[i][k] from lane i + 32 (k / 8), element k % 8;
+// B[k][j] from lane j + 32 (k / 8); D as in the f32 32x32 forms.
+// Tile 64 tokens x 128 rows, BK = 32 (one quant block), four waves 2 x 2, each
+// 32 tokens x 64 rows: per block a wave issues 2 x NT x 2 MFMAs into a block
+// accumulator, then adds d * (block accumulator) into its f32 result.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+QD_DEV void split_bf16(float x, __bf16 (&t)[3]) {
+  t[0] = (__bf16)x;
+  const float r = x - (float)t[0];
+  t[1] = (__bf16)r;
+  t[2] = (__bf16)(r - (float)t[1]);
+}
+
+template <int QT, int MODE, int NT>
+__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs a) {
+  constexpr int BM = 64, BN = 128, BK = 32;
+  constexpr int RS = BK + 8;  // row stride in bf16 (80 bytes): conflict-free 16-byte reads
+  __shared__ __align__(16) __bf16 As[2][NT][BM][RS];
+  __shared__ __align__(16) __bf16 Bs[2][BN][RS];
+  __shared__ float Ds[2][BN];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int n0 = blockIdx.x * BN, t0 = blockIdx.y * BM;
+  const int kp = a.nblk * 32;
+
+  // staging: X row tid / 4, k (tid % 4) * 8 .. +8; W row tid / 2, k (tid % 2) * 16 .. +16
+  float4 xa[2];
+  uint4 wq;
+  float wd = 0.f;
+  const int xrow = tid >> 2, xk = (tid & 3) * 8;
+  const int brow = tid >> 1, bhalf = tid & 1;
+  const bool brow_ok = n0 + brow < a.rows;
+
+  auto load = [&](int kb) {
+    const int t = t0 + xrow;
+    if (t < a.T) {
+      const float4* p = reinterpret_cast<const float4*>(a.x + (size_t)t * a.ldx + kb * BK + xk);
+      xa[0] = p[0];
+      xa[1] = p[1];
+    } else {
+      xa[0] = xa[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (brow_ok) {
+      const size_t r = n0 + brow;
+      if constexpr (QT == kQ8_0) wq = *reinterpret_cast<const uint4*>(a.qs + r * kp + kb * BK + 16 * bhalf);
+      else wq = *reinterpret_cast<const uint4*>(a.qs + (r * a.nblk + kb) * 16);
+      wd = load_half(a.d + r * a.nblk + kb);
+    } else {
+      wq = make_uint4(0, 0, 0, 0);
+      wd = 0.f;
+    }
+  };
+
+  auto store = [&](int buf) {
+    const float xv[8] = {xa[0].x, xa[0].y, xa[0].z, xa[0].w, xa[1].x, xa[1].y, xa[1].z, xa[1].w};
+    bf16x8 xt[NT];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      __bf16 t3[3];
+      split_bf16(xv[e], t3);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) xt[t][e] = t3[t];
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) *reinterpret_cast<bf16x8*>(&As[buf][t][xrow][xk]) = xt[t];
+    const uint32_t w4[4] = {wq.x, wq.y, wq.z, wq.w};
+    bf16x8 q0, q1;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float v;
+      if constexpr (QT == kQ8_0) {
+        v = (float)(int8_t)(w4[e >> 2] >> (8 * (e & 3)));
+      } else {
+        const uint32_t byte = (w4[e >> 2] >> (8 * (e & 3))) & 0xffu;
+        v = (float)((int)(bhalf ? (byte >> 4) : (byte & 15u)) - 8);
+      }
+      if (e < 8) q0[e] = (__bf16)v;
+      else q1[e - 8] = (__bf16)v;
+    }
+    if (!brow_ok) q0 = q1 = bf16x8{};
+    *reinterpret_cast<bf16x8*>(&Bs[buf][brow][16 * bhalf]) = q0;
+    *reinterpret_cast<bf16x8*>(&Bs[buf][brow][16 * bhalf + 8]) = q1;
+    if (bhalf == 0) Ds[buf][brow] = wd;
+  };
+
+  f32x16 acc[2], blk[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[s][r] = 0.f;
+
+  load(0);
+  store(0);
+  __syncthreads();
+  const int li = lane & 31, kg = (lane >> 5) * 8;
+  for (int kb = 0; kb < a.nblk; ++kb) {
+    const int buf = kb & 1;
+    if (kb + 1 < a.nblk) load(kb + 1);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) blk[s][r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 16) {
+      bf16x8 bv[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) bv[s] = *reinterpret_cast<const bf16x8*>(&Bs[buf][wn * 64 + s * 32 + li][kk + kg]);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&As[buf][t][wm * 32 + li][kk + kg]);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) blk[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv[s], blk[s], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const float d = Ds[buf][wn * 64 + s * 32 + li];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[s][r] += d * blk[s][r];
+    }
+    if (kb + 1 < a.nblk) store(buf ^ 1);
+    __syncthreads();
+  }
+
+  constexpr bool kPair = MODE == kModePairSilu || MODE == kModePairGelu;
+  const int lk = lane >> 5;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int i = 8 * (r >> 2) + 4 * lk + (r & 3);
+    const int t = t0 + wm * 32 + i;
+    if (t >= a.T) continue;
+    float* yr = a.y + (size_t)t * a.ldy;
+    const int n = n0 + wn * 64 + li;
+    if constexpr (kPair) {
+      const int nn = (n0 + wn * 64) / 2 + li;
+      if (n + 32 < a.rows) {
+        const float g = acc[0][r], u = acc[1][r];
+        yr[nn] = (MODE == kModePairSilu ? act_silu(g) : act_gelu_tanh(g)) * u;
+      }
+    } else if constexpr (MODE == kModeAdd) {
+      if (n < a.rows) yr[n] += acc[0][r];
+      if (n + 32 < a.rows) yr[n + 32] += acc[1][r];
+    } else {
+      if (n < a.rows) yr[n] = acc[0][r];
+      if (n + 32 < a.rows) yr[n + 32] = acc[1][r];
+    }
+  }
+}
+
 }  // namespace qd

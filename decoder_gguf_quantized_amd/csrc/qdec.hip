@@ -102,6 +102,7 @@ struct qdec_model {
   float2* rope_g = nullptr;  // [max_ctx][hd/2] (cos, sin), full-attention layers
   float2* rope_l = nullptr;  // same for sliding-window layers
   float2* rope_cur = nullptr;  // [2][max_seqs][hd/2]: rows of rope_g / rope_l at each decode position
+  int prefill_prec = QDEC_PREFILL_F32;  // operand precision of the prefill GEMMs
   float* kc = nullptr;
   float* vc = nullptr;
   size_t kv_layer = 0;  // floats per layer of one cache
@@ -316,12 +317,46 @@ void gemm_ksplit_dispatch(int mode, dim3 grid, hipStream_t st, const GemmArgs& a
   else qlaunch(gemm_ksplit_kernel<QT, kModeStore>, grid, 256, 0, st, a);
 }
 
-void gemm(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, int T, float* y, int ldy, int mode) {
+template <int QT, int NT>
+void gemm_bf16_dispatch(int mode, dim3 grid, hipStream_t st, const GemmArgs& a) {
+  switch (mode) {
+    case kModeStore: qlaunch(gemm_bf16_kernel<QT, kModeStore, NT>, grid, 256, 0, st, a); break;
+    case kModeAdd: qlaunch(gemm_bf16_kernel<QT, kModeAdd, NT>, grid, 256, 0, st, a); break;
+    case kModePairSilu: qlaunch(gemm_bf16_kernel<QT, kModePairSilu, NT>, grid, 256, 0, st, a); break;
+    default: qlaunch(gemm_bf16_kernel<QT, kModePairGelu, NT>, grid, 256, 0, st, a); break;
+  }
+}
+
+// Prefill projection.  prec: QDEC_PREFILL_F32 (f32 operands, the default),
+// QDEC_PREFILL_BF16X3 (exact three-term bf16 split of the activations) or
+// QDEC_PREFILL_BF16 (activations rounded to bf16); -1 = the model's setting.
+// F32 weights always take the f32 kernels.
+void gemm(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, int T, float* y, int ldy, int mode,
+          int prec = -1) {
   GemmArgs a{w.qs, w.d, w.rows, w.nblk, x, ldx, T, y, ldy};
   dim3 grid((w.rows + 127) / 128, (T + 63) / 64);
   const bool pair = mode == kModePairSilu || mode == kModePairGelu;
+  if (prec < 0) prec = m ? m->prefill_prec : QDEC_PREFILL_F32;
+  // few 64 x 128 tiles for the CUs: the f32 K-split tile below is faster there
+  const bool few = !pair && (size_t)grid.x * grid.y < 512 && w.nblk >= 8;
+  if (prec != QDEC_PREFILL_F32 && (w.type == kQ8_0 || w.type == kQ4_0) && !few) {
+    const int nt = prec == QDEC_PREFILL_BF16X3 ? 3 : 1;
+    const double bytes = w.gguf_bytes + (double)T * w.nblk * 32 * 4 + (double)T * (pair ? w.rows / 2 : w.rows) * 4;
+    // flops: the algorithmic 2 T N K (each term's products are extra MFMA work)
+    Timed tm(m, st, nt == 3 ? (w.type == kQ8_0 ? "gemm_bf16x3_q8_0" : "gemm_bf16x3_q4_0")
+                            : (w.type == kQ8_0 ? "gemm_bf16_q8_0" : "gemm_bf16_q4_0"),
+             bytes, 2.0 * T * (double)w.rows * w.cols);
+    if (w.type == kQ8_0) {
+      if (nt == 3) gemm_bf16_dispatch<kQ8_0, 3>(mode, grid, st, a);
+      else gemm_bf16_dispatch<kQ8_0, 1>(mode, grid, st, a);
+    } else {
+      if (nt == 3) gemm_bf16_dispatch<kQ4_0, 3>(mode, grid, st, a);
+      else gemm_bf16_dispatch<kQ4_0, 1>(mode, grid, st, a);
+    }
+    return;
+  }
   // few 64 x 128 tiles for the CUs: switch to the K-split 32 x 64 tile
-  if (!pair && (size_t)grid.x * grid.y < 512 && w.nblk >= 8) {
+  if (few) {
     dim3 g2((w.rows + 63) / 64, (T + 31) / 32);
     const double bytes = w.gguf_bytes + (double)T * w.nblk * 32 * 4 + (double)T * w.rows * 4;
     Timed tm(m, st, gemm_class(w.type), bytes, 2.0 * T * (double)w.rows * w.cols);
@@ -843,6 +878,10 @@ int load(const qdec_config* cfgp, const qdec_tensor* ts, int32_t n, int32_t max_
     m->kv_layer = (size_t)max_seqs * c.n_head_kv * max_ctx * c.head_dim;
     m->kc = m->dalloc<float>(m->kv_layer * c.n_layer);
     m->vc = m->dalloc<float>(m->kv_layer * c.n_layer);
+    // rows past a sequence's length are read (and masked) by decode attention:
+    // start from finite values
+    hipck(hipMemsetAsync(m->kc, 0, m->kv_layer * c.n_layer * 4, st), "memset");
+    hipck(hipMemsetAsync(m->vc, 0, m->kv_layer * c.n_layer * 4, st), "memset");
     // workspace
     m->ws_T = std::max(std::min(max_ctx, 4096), max_seqs);
     const size_t T = m->ws_T;
@@ -1096,6 +1135,17 @@ int qdec_kv_len(const qdec_model* m, int32_t seq, int32_t* out) {
 
 int qdec_poisoned(const qdec_model* m) { return m ? (m->poisoned ? 1 : 0) : -1; }
 
+int qdec_set_prefill_precision(qdec_model* m, int32_t precision) {
+  g_err.clear();
+  if (int rc = check_usable(m)) return rc;
+  if (precision != QDEC_PREFILL_F32 && precision != QDEC_PREFILL_BF16X3 && precision != QDEC_PREFILL_BF16) {
+    set_err("unknown prefill precision %d", precision);
+    return QDEC_REFUSED;
+  }
+  m->prefill_prec = precision;
+  return QDEC_OK;
+}
+
 int qdec_free(qdec_model* m) {
   g_err.clear();
   if (!m) { set_err("model handle is NULL"); return QDEC_REFUSED; }
@@ -1175,8 +1225,12 @@ int qdec_debug_sample(const float* d_logits, int32_t rows, int32_t vocab, float 
 }
 
 int qdec_debug_matmul(int32_t type, int64_t rows, int64_t cols, const void* host_data, int64_t n_bytes,
-                      const float* d_x, int32_t n_x, float* d_y, void* stream) {
+                      const float* d_x, int32_t n_x, float* d_y, int32_t precision, void* stream) {
   g_err.clear();
+  if (precision != QDEC_PREFILL_F32 && precision != QDEC_PREFILL_BF16X3 && precision != QDEC_PREFILL_BF16) {
+    set_err("unknown prefill precision %d", precision);
+    return QDEC_REFUSED;
+  }
   if (type != kF32 && type != kQ8_0 && type != kQ4_0) { set_err("type %d unsupported", type); return QDEC_REFUSED; }
   if (rows <= 0 || cols <= 0 || rows > (1 << 24) || cols > (1 << 20) || !host_data || !d_x || !d_y || n_x <= 0) {
     set_err("bad arguments");
@@ -1193,7 +1247,7 @@ int qdec_debug_matmul(int32_t type, int64_t rows, int64_t cols, const void* host
     Mat w = upload(&tmp, s, (int)rows, (int)cols, (double)n_bytes, st);
     const int kp = w.nblk * 32;
     if (n_x <= 16) gemv(nullptr, st, w, d_x, kp, nullptr, 0.f, d_y, (int)rows, n_x, kModeStore);
-    else gemm(nullptr, st, w, d_x, kp, n_x, d_y, (int)rows, kModeStore);
+    else gemm(nullptr, st, w, d_x, kp, n_x, d_y, (int)rows, kModeStore, precision);
     hipck(hipStreamSynchronize(st), "matmul sync");
   } catch (const HipError& e) {
     set_err("internal: %s", e.msg.c_str());

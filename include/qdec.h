@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define QDEC_ABI_VERSION 2
+#define QDEC_ABI_VERSION 3
 
 enum { QDEC_OK = 0, QDEC_REFUSED = 1, QDEC_INTERNAL = 2 };
 
@@ -55,6 +55,17 @@ enum { QDEC_OK = 0, QDEC_REFUSED = 1, QDEC_INTERNAL = 2 };
 enum { QDEC_T_F32 = 0, QDEC_T_Q4_0 = 2, QDEC_T_Q8_0 = 8 };
 
 enum { QDEC_ACT_SILU = 0, QDEC_ACT_GELU_TANH = 1 };
+
+/* Operand precision of the prefill projections (quantized weights; f32 weights
+ * always use f32 operands).  F32: f32 operands on V_MFMA_F32_32X32X2_F32, the
+ * [S] "Choose the engine" contract (weights decoded exactly, products in f32).
+ * BF16X3: quant values (exact in bf16) against a three-term bf16 split of the
+ * activations, x = x1 + x2 + x3 with 8 significant bits each, on
+ * V_MFMA_F32_32X32X16_BF16: every product is exact and accumulated in f32, so
+ * the result is the f32 one up to summation order.  BF16: activations rounded
+ * to bf16 (one term); not f32-accurate.  Projections with too few 64 x 128
+ * tiles to fill the GPU keep the f32 K-split kernel in every mode. */
+enum { QDEC_PREFILL_F32 = 0, QDEC_PREFILL_BF16X3 = 1, QDEC_PREFILL_BF16 = 2 };
 
 enum {
   QDEC_ALL_LOGITS = 1u << 0,       /* prefill: logits of every position, not only the last */
@@ -148,6 +159,10 @@ int qdec_kv_write(qdec_model* m, int32_t seq, int32_t layer, const float* d_k, c
                   int32_t n_pos, void* stream);
 
 int qdec_kv_len(const qdec_model* m, int32_t seq, int32_t* out);
+
+/* Operand precision of later prefill projections (QDEC_PREFILL_*; default F32).
+ * Refused: an unknown value. */
+int qdec_set_prefill_precision(qdec_model* m, int32_t precision);
 int qdec_poisoned(const qdec_model* m); /* 1 if latched, 0 if not, -1 for NULL */
 
 /* Release everything the handle owns, after draining its last stream (bounded
@@ -171,11 +186,13 @@ int qdec_debug_sample(const float* d_logits, int32_t rows, int32_t vocab, float 
                       float top_p, uint64_t seed, uint64_t step, int32_t* d_out, void* stream);
 
 /* One projection y[r][n] = sum_k W[n][k] x[r][k] with the forward pass's kernels:
- * the decode GEMV for n_x <= 16, the prefill MFMA GEMM above.  W is given in GGUF
- * bytes on the host (uploaded and repacked per call; synchronous).  d_x f32
- * [n_x][ceil(cols/32)*32] (zero padded), d_y f32 [n_x][rows]. */
+ * the decode GEMV for n_x <= 16, the prefill MFMA GEMM above (operands in
+ * `precision`, QDEC_PREFILL_*).  W is given in GGUF bytes on the host (uploaded
+ * and repacked per call; synchronous).  d_x f32 [n_x][ceil(cols/32)*32] (zero
+ * padded), d_y f32 [n_x][rows]. */
 int qdec_debug_matmul(int32_t type, int64_t rows, int64_t cols, const void* host_data,
-                      int64_t n_bytes, const float* d_x, int32_t n_x, float* d_y, void* stream);
+                      int64_t n_bytes, const float* d_x, int32_t n_x, float* d_y, int32_t precision,
+                      void* stream);
 
 /* Per-kernel timing with HIP events on the launch stream.  enable = 1 starts
  * recording every launch; enable = 0 synchronizes, writes up to max_out records

@@ -227,6 +227,47 @@ def test_projection_matches_oracle(ttype, rows, cols, n_x):
         check_row(got[r], want[r])
 
 
+GEMM_CASES = [c for c in MATMUL_CASES if c[3] > 16 and c[0] != synth.T_F32]
+
+
+@pytest.mark.parametrize("ttype,rows,cols,n_x", GEMM_CASES)
+def test_projection_bf16x3_matches_oracle(ttype, rows, cols, n_x):
+    """The three-term bf16 split is exact: same bar as the f32 kernels, and in
+    practice f32-level agreement (max relative error per row below 1e-5)."""
+    rng = np.random.default_rng(rows * 7 + cols + n_x)
+    w = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
+    raw = synth.encode(ttype, w)
+    kp = ((cols + 31) // 32) * 32
+    x = np.zeros((n_x, kp), np.float32)
+    x[:, :cols] = rng.standard_normal((n_x, cols))
+    y = torch.empty((n_x, rows), dtype=torch.float32, device=dev())
+    qdec.debug_matmul(ttype, rows, cols, raw, torch.from_numpy(x).to(dev()), y, precision="bf16x3")
+    W = blocks.dequant(ttype, raw, rows, cols).astype(np.float64)
+    want = x[:, :cols].astype(np.float64) @ W.T
+    got = as_np(y)
+    errs = [check_row(got[r], want[r]) for r in range(n_x)]
+    assert max(errs) < 1e-5, max(errs)
+
+
+def test_projection_bf16_plain_error_is_reported():
+    """Activations rounded to bf16 (one term): the error is bf16's (about 2^-9
+    per product, averaging down over K); it is measured, not held to 2e-3.
+    (The shape fills >= 512 wide tiles, so the bf16 kernel runs.)"""
+    rng = np.random.default_rng(44)
+    rows, cols, n_x = 4096, 512, 1024
+    w = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
+    raw = synth.encode(synth.T_Q8_0, w)
+    x = rng.standard_normal((n_x, cols)).astype(np.float32)
+    y = torch.empty((n_x, rows), dtype=torch.float32, device=dev())
+    qdec.debug_matmul(synth.T_Q8_0, rows, cols, raw, torch.from_numpy(x).to(dev()), y, precision="bf16")
+    W = blocks.dequant(synth.T_Q8_0, raw, rows, cols).astype(np.float64)
+    want = x.astype(np.float64) @ W.T
+    got = as_np(y)
+    err = max(float(np.max(np.abs(got[r] - want[r])) / np.max(np.abs(want[r]))) for r in range(n_x))
+    print(f"plain bf16 activations: max relative error per row {err:.2e}")
+    assert 1e-5 < err < 2e-2
+
+
 # ---------------------------------------------------------------- whole model
 def run_gpu(m, cfg, prompt, n_steps, seq=0):
     """Prefill (all logits) then n_steps greedy decode steps chained on device.
@@ -268,6 +309,24 @@ def test_prefill_and_decode_match_oracle(key):
     for s in range(n):
         assert token_agrees(g_tok[s + 1], o_dl[s])
     print(f"{key}: max rel err {max(errs):.2e}")
+
+
+@pytest.mark.parametrize("key", ["llama_q4_hd64_g4", "qwen3_hd128_g2", "gemma_hd256_g4"])
+def test_bf16x3_prefill_matches_oracle(key):
+    """Prefill with the three-term bf16 split in every quantized projection:
+    every position's logits within the f32 path's tolerance."""
+    cfg, t, m = model_for(key)
+    T = 70
+    prompt = synth.prompt(cfg, T)
+    m.set_prefill_precision("bf16x3")
+    try:
+        g_pl, _, g_tok = run_gpu(m, cfg, prompt, 0)
+    finally:
+        m.set_prefill_precision("f32")
+    o_pl, _ = oracle_run(cfg, t, prompt, g_tok, 0)
+    errs = [check_row(g_pl[i], o_pl[i]) for i in range(T)]
+    assert token_agrees(g_tok[0], o_pl[-1])
+    print(f"{key} bf16x3: max rel err {max(errs):.2e}")
 
 
 @pytest.mark.parametrize("key", ["c1", "gemma_hd256_g4"])
@@ -372,6 +431,33 @@ def test_decode_step_top_p_follows_the_oracle_sampler():
                 checked += 1
         toks = out
     assert checked >= 8
+
+
+def test_decode_ignores_cache_rows_past_the_length():
+    """Cache rows past a sequence's length hold NaN (written, then truncated
+    away); decode attention requests whole chunks ahead of the position, so it
+    reads them, and must mask them without letting 0 * NaN through."""
+    cfg, t, m = model_for("qwen3_hd128_g2")
+    V, nkv, hd = cfg["vocab"], cfg["n_head_kv"], cfg["head_dim"]
+    keep, n_pos = 60, 100
+    rng = np.random.default_rng(31)
+    om = OracleModel(cfg, t, max_ctx=128, n_seqs=1)
+    m.kv_reset()
+    for layer in range(cfg["n_layer"]):
+        k = rng.standard_normal((nkv, n_pos, hd)).astype(np.float32)
+        v = rng.standard_normal((nkv, n_pos, hd)).astype(np.float32)
+        om.kv_write(0, layer, k[:, :keep], v[:, :keep])
+        k[:, keep:] = np.nan
+        v[:, keep:] = np.nan
+        m.kv_write(0, layer, torch.from_numpy(k).to(dev()), torch.from_numpy(v).to(dev()))
+    m.kv_truncate(0, keep)
+    om.set_kv_len(0, keep)
+    dl = torch.empty((1, V), dtype=torch.float32, device=dev())
+    out = torch.empty(1, dtype=torch.int32, device=dev())
+    for step, tok in enumerate([11, 29, 7]):
+        m.decode_step([tok], dl, out)
+        torch.cuda.synchronize()
+        check_row(as_np(dl)[0], om.forward(0, [tok])[0])
 
 
 def test_refusals_leave_handle_usable():

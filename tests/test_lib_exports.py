@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version(L):
-    assert L.qdec_abi_version() == 2
+    assert L.qdec_abi_version() == 3
 
 
 def cfg(**kw):
@@ -85,7 +85,8 @@ def test_null_handle_calls_are_refused(L):
     assert L.qdec_poisoned(None) == -1
     out = ctypes.c_int32()
     assert L.qdec_kv_len(None, 0, ctypes.byref(out)) == 1
-    assert L.qdec_debug_matmul(3, 4, 4, None, 0, None, 1, None, None) == 1
+    assert L.qdec_debug_matmul(3, 4, 4, None, 0, None, 1, None, 0, None) == 1
+    assert L.qdec_set_prefill_precision(None, 0) == 1
     assert L.qdec_debug_sample(None, 1, 1, 0.0, 1.0, 0, 0, None, None) == 1
 
 
