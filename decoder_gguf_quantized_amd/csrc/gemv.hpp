@@ -45,6 +45,12 @@ struct GemvArgs {
   int m;                 // input rows in this launch (<= template M)
   float* const* y_ind;   // if non-null, the output base is *y_ind + y_off (graph replays)
   long y_off;
+  // Residual prologue (sandwich norms): if res_add is non-null, the input row
+  // is h = x + RMSNorm(res_add) * res_w (rows [m][ldx]), which the norm_w
+  // prologue then normalises; workgroup 0 writes h to res_out (if non-null).
+  const float* res_add;
+  const float* res_w;
+  float* res_out;
 };
 
 QD_DEV float act_silu(float g) { return g / (1.0f + expf(-g)); }
@@ -93,11 +99,14 @@ constexpr int unit_floats() { return QT == kQ8_0 ? 16 : (QT == kQ4_0 ? 32 : 4); 
 // unit, so for each slot i consecutive lanes read consecutive float4s: no bank
 // conflicts (the natural layout puts every lane's unit 64 or 128 bytes apart,
 // which lands all lanes on a handful of banks).
-template <int QT, int M, int NW>
+template <int QT, int M, int NW, bool RES>
 QD_DEV void gemv_stage_x(const GemvArgs& a, float4* xs4, int kp, float (&scale)[M]) {
   constexpr int NT = 64 * NW;  // threads of the workgroup
   constexpr int US = unit_floats<QT>(), NV = US / 4;
-  constexpr int JB = M >= 8 ? 1 : 8 / M;  // k positions per thread per batch
+  // k positions per thread per batch (loads in flight); the residual prologue
+  // loads four float4 per position, so it batches fewer to stay within the
+  // register budget of the plain kernels (the weight tiles are live meanwhile)
+  constexpr int JB = RES ? (M >= 2 ? 1 : 2) : (M >= 8 ? 1 : 8 / M);
   const int NU = kp / US, NK4 = kp / 4;
   __shared__ float red[NW][M];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -108,6 +117,47 @@ QD_DEV void gemv_stage_x(const GemvArgs& a, float4* xs4, int kp, float (&scale)[
   float ss[M];
 #pragma unroll
   for (int mi = 0; mi < M; ++mi) ss[mi] = 0.f;
+  // residual prologue: the RMS scale of res_add first (one more pass over it)
+  constexpr bool resid = RES;  // residual prologue (compiled only where used)
+  const float4* t4 = reinterpret_cast<const float4*>(a.res_add);
+  const float4* r4 = reinterpret_cast<const float4*>(a.res_w);
+  float4* o4 = reinterpret_cast<float4*>(a.res_out);
+  const bool write_h = resid && o4 && blockIdx.x == 0;
+  float ts[M];
+  if constexpr (RES) {
+    __shared__ float red_t[NW][M];
+#pragma unroll
+    for (int mi = 0; mi < M; ++mi) ts[mi] = 0.f;
+    for (int k0 = tid; k0 < NK4; k0 += NT * JB) {
+      float4 tv[JB][M];
+#pragma unroll
+      for (int j = 0; j < JB; ++j)
+#pragma unroll
+        for (int mi = 0; mi < M; ++mi)
+          tv[j][mi] = (k0 + NT * j < NK4 && mi < a.m) ? t4[(size_t)mi * ldx4 + k0 + NT * j]
+                                                      : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int j = 0; j < JB; ++j)
+#pragma unroll
+        for (int mi = 0; mi < M; ++mi) {
+          const float4 v = tv[j][mi];
+          ts[mi] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+        }
+    }
+#pragma unroll
+    for (int mi = 0; mi < M; ++mi) {
+      const float t = wave_sum(ts[mi]);
+      if (lane == 0) red_t[wave][mi] = t;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int mi = 0; mi < M; ++mi) {
+      float t = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) t += red_t[w][mi];
+      ts[mi] = 1.0f / sqrtf(t / (float)kp + a.eps);
+    }
+  }
   for (int k0 = tid; k0 < NK4; k0 += NT * JB) {
     float4 xv[JB][M], wv[JB];
 #pragma unroll
@@ -118,6 +168,18 @@ QD_DEV void gemv_stage_x(const GemvArgs& a, float4* xs4, int kp, float (&scale)[
 #pragma unroll
       for (int mi = 0; mi < M; ++mi)
         xv[j][mi] = (ok && mi < a.m) ? x4[(size_t)mi * ldx4 + k4] : make_float4(0.f, 0.f, 0.f, 0.f);
+      if constexpr (RES) {
+        const float4 rw = ok ? r4[k4] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int mi = 0; mi < M; ++mi) {
+          const float4 t = (ok && mi < a.m) ? t4[(size_t)mi * ldx4 + k4] : make_float4(0.f, 0.f, 0.f, 0.f);
+          const float s = ts[mi];
+          xv[j][mi].x += t.x * s * rw.x;
+          xv[j][mi].y += t.y * s * rw.y;
+          xv[j][mi].z += t.z * s * rw.z;
+          xv[j][mi].w += t.w * s * rw.w;
+        }
+      }
     }
 #pragma unroll
     for (int j = 0; j < JB; ++j) {
@@ -127,6 +189,7 @@ QD_DEV void gemv_stage_x(const GemvArgs& a, float4* xs4, int kp, float (&scale)[
 #pragma unroll
         for (int mi = 0; mi < M; ++mi) {
           const float4 v = xv[j][mi], w = wv[j];
+          if (write_h && mi < a.m) o4[(size_t)mi * ldx4 + k4] = v;
           ss[mi] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
           xs4[mi * NK4 + slot] = make_float4(v.x * w.x, v.y * w.y, v.z * w.z, v.w * w.w);
         }
@@ -309,7 +372,7 @@ constexpr int gemv_sets() { return QDEC_GEMV_NS; }
 // tiles are requested before the input rows are staged.  Tile indices are
 // wave-uniform (scalar registers), so every load is a scalar base plus a 32-bit
 // lane offset.
-template <int QT, int M, int MODE, int R, int U, int NW>
+template <int QT, int M, int MODE, int R, int U, int NW, bool RES>
 __global__ __launch_bounds__(64 * NW) void gemv_kernel(GemvArgs a) {
   constexpr int NS = gemv_sets<R, U, M>();
   extern __shared__ float4 xs4[];
@@ -347,7 +410,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(GemvArgs a) {
   if constexpr (NS > 2) request(std::integral_constant<int, 1>{});
 
   float scale[M];
-  gemv_stage_x<QT, M, NW>(a, xs4, kp, scale);  // ends with a barrier
+  gemv_stage_x<QT, M, NW, RES>(a, xs4, kp, scale);  // ends with a barrier
   if constexpr (QT == kQ4_0) {
     for (int i = threadIdx.x; i < M * a.nblk; i += 64 * NW) {
       const int mi = i / a.nblk, u = i % a.nblk;

@@ -108,6 +108,7 @@ struct qdec_model {
   size_t kv_layer = 0;  // floats per layer of one cache
   int ws_T = 0;
   float *x = nullptr, *h = nullptr, *qkv = nullptr, *q = nullptr, *a = nullptr, *m = nullptr, *y = nullptr;
+  float* x2 = nullptr;  // second residual buffer (decode with sandwich norms)
   float* part_o = nullptr;
   float* part_ml = nullptr;
   int chunk = 0, nchunk = 0;
@@ -197,11 +198,21 @@ const char* gemm_class(int type) { return type == kQ4_0 ? "gemm_q4_0" : type == 
 
 template <int QT, int M, int R, int U, int NW = 4>
 void gemv_dispatch_mode(int mode, dim3 grid, size_t lds, hipStream_t st, const GemvArgs& a) {
+  const unsigned nt = 64 * NW;
+  if (a.res_add) {  // residual prologue (sandwich norms): store and pair modes
+    switch (mode) {
+      case kModeStore: qlaunch(gemv_kernel<QT, M, kModeStore, R, U, NW, true>, grid, nt, lds, st, a); break;
+      case kModePairSilu: qlaunch(gemv_kernel<QT, M, kModePairSilu, R, U, NW, true>, grid, nt, lds, st, a); break;
+      case kModePairGelu: qlaunch(gemv_kernel<QT, M, kModePairGelu, R, U, NW, true>, grid, nt, lds, st, a); break;
+      default: throw HipError{"gemv: residual prologue with an add epilogue"};
+    }
+    return;
+  }
   switch (mode) {
-    case kModeStore: qlaunch(gemv_kernel<QT, M, kModeStore, R, U, NW>, grid, 64 * NW, lds, st, a); break;
-    case kModeAdd: qlaunch(gemv_kernel<QT, M, kModeAdd, R, U, NW>, grid, 64 * NW, lds, st, a); break;
-    case kModePairSilu: qlaunch(gemv_kernel<QT, M, kModePairSilu, R, U, NW>, grid, 64 * NW, lds, st, a); break;
-    default: qlaunch(gemv_kernel<QT, M, kModePairGelu, R, U, NW>, grid, 64 * NW, lds, st, a); break;
+    case kModeStore: qlaunch(gemv_kernel<QT, M, kModeStore, R, U, NW, false>, grid, nt, lds, st, a); break;
+    case kModeAdd: qlaunch(gemv_kernel<QT, M, kModeAdd, R, U, NW, false>, grid, nt, lds, st, a); break;
+    case kModePairSilu: qlaunch(gemv_kernel<QT, M, kModePairSilu, R, U, NW, false>, grid, nt, lds, st, a); break;
+    default: qlaunch(gemv_kernel<QT, M, kModePairGelu, R, U, NW, false>, grid, nt, lds, st, a); break;
   }
 }
 
@@ -261,8 +272,16 @@ constexpr size_t kGemvLdsMax = 64 * 1024;
 
 // y[r][*] (op)= W x[r] for rows r < nrows, in launches of up to 16 rows that fit
 // the LDS budget.  y_ind: read the output base from device memory instead.
+// Residual prologue for sandwich norms: the input is x + RMSNorm(add) * add_w,
+// written to out by the first workgroup (out may be null).
+struct Resid {
+  const float* add = nullptr;
+  const float* add_w = nullptr;
+  float* out = nullptr;
+};
+
 void gemv(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, const float* norm_w, float eps,
-          float* y, int ldy, int nrows, int mode, float* const* y_ind = nullptr) {
+          float* y, int ldy, int nrows, int mode, float* const* y_ind = nullptr, Resid res = Resid{}) {
   const int kp = w.nblk * 32;
   const size_t per_row = (size_t)kp * 4 + (w.type == kQ4_0 ? (size_t)w.nblk * 4 : 0);
   // rows per launch: a power of two (the kernel's M) whose staged inputs fit the LDS budget
@@ -291,7 +310,9 @@ void gemv(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, 
     int M = 1;
     while (M < mr) M *= 2;
     GemvArgs a{w.qs, w.d, w.rows, w.nblk, x + (size_t)r0 * ldx, ldx, norm_w, eps,
-               y ? y + (size_t)r0 * ldy : nullptr, ldy, mr, y_ind, (long)r0 * ldy};
+               y ? y + (size_t)r0 * ldy : nullptr, ldy, mr, y_ind, (long)r0 * ldy,
+               res.add ? res.add + (size_t)r0 * ldx : nullptr, res.add_w,
+               res.out ? res.out + (size_t)r0 * ldx : nullptr};
     const size_t lds = per_row * M;
     const double bytes = w.gguf_bytes + (double)mr * kp * 4 + (double)mr * (pair ? w.rows / 2 : w.rows) * 4;
     Timed tm(m, st, gemv_class(w.type), bytes, 2.0 * mr * w.rows * (double)w.cols);
@@ -485,10 +506,18 @@ void blocks(qdec_model* m, hipStream_t st, int n, int seq, int pos0, const int* 
   const int H = c.hidden;
   const bool dec = dpos != nullptr;
   const int act_mode = c.act == QDEC_ACT_GELU_TANH ? kModePairGelu : kModePairSilu;
+  // Decode with sandwich norms: each post-norm and its residual add run in the
+  // prologue of the next GEMV (Resid), which writes the new residual row to the
+  // other of two buffers (the kernel's other workgroups still read the old
+  // one): R_l in x, R_l + post-attention term in x2, the next R in x again.
+  const bool fuse = dec && c.sandwich_norm;
   for (int l = 0; l < c.n_layer; ++l) {
     const Layer& L = m->layers[l];
     // attention sublayer
-    if (dec) {
+    if (fuse && l > 0) {
+      gemv(m, st, L.qkv, m->x2, H, L.attn_norm, c.rms_eps, m->qkv, m->nqkv, n, kModeStore, nullptr,
+           Resid{m->y, m->layers[l - 1].post_ffw, m->x});
+    } else if (dec) {
       gemv(m, st, L.qkv, m->x, H, L.attn_norm, c.rms_eps, m->qkv, m->nqkv, n, kModeStore);
     } else {
       rmsnorm_rows(m, st, m->x, H, L.attn_norm, H, m->h, H, n, 0);
@@ -500,24 +529,29 @@ void blocks(qdec_model* m, hipStream_t st, int n, int seq, int pos0, const int* 
       rope_kv(m, st, l, n, seq, pos0, nullptr);
       attention_prefill(m, st, l, seq, n, pos0);
     }
-    if (c.sandwich_norm) {
-      if (dec) gemv(m, st, L.o, m->a, m->qd, nullptr, 0.f, m->y, H, n, kModeStore);
-      else gemm(m, st, L.o, m->a, m->qd, n, m->y, H, kModeStore);
+    if (fuse) {
+      gemv(m, st, L.o, m->a, m->qd, nullptr, 0.f, m->y, H, n, kModeStore);
+    } else if (c.sandwich_norm) {
+      gemm(m, st, L.o, m->a, m->qd, n, m->y, H, kModeStore);
       rmsnorm_rows(m, st, m->y, H, L.post_attn, H, m->x, H, n, 1);
     } else {
       if (dec) gemv(m, st, L.o, m->a, m->qd, nullptr, 0.f, m->x, H, n, kModeAdd);
       else gemm(m, st, L.o, m->a, m->qd, n, m->x, H, kModeAdd);
     }
     // feed-forward sublayer
-    if (dec) {
+    if (fuse) {
+      gemv(m, st, L.gu, m->x, H, L.ffn_norm, c.rms_eps, m->m, m->Fp, n, act_mode, nullptr,
+           Resid{m->y, L.post_attn, m->x2});
+    } else if (dec) {
       gemv(m, st, L.gu, m->x, H, L.ffn_norm, c.rms_eps, m->m, m->Fp, n, act_mode);
     } else {
       rmsnorm_rows(m, st, m->x, H, L.ffn_norm, H, m->h, H, n, 0);
       gemm(m, st, L.gu, m->h, H, n, m->m, m->Fp, act_mode);
     }
-    if (c.sandwich_norm) {
-      if (dec) gemv(m, st, L.down, m->m, m->Fp, nullptr, 0.f, m->y, H, n, kModeStore);
-      else gemm(m, st, L.down, m->m, m->Fp, n, m->y, H, kModeStore);
+    if (fuse) {
+      gemv(m, st, L.down, m->m, m->Fp, nullptr, 0.f, m->y, H, n, kModeStore);
+    } else if (c.sandwich_norm) {
+      gemm(m, st, L.down, m->m, m->Fp, n, m->y, H, kModeStore);
       rmsnorm_rows(m, st, m->y, H, L.post_ffw, H, m->x, H, n, 1);
     } else {
       if (dec) gemv(m, st, L.down, m->m, m->Fp, nullptr, 0.f, m->x, H, n, kModeAdd);
@@ -532,8 +566,12 @@ void decode_body(qdec_model* m, hipStream_t st, int n, bool topp) {
   const qdec_config& c = m->cfg;
   embed(m, st, m->d_tok, n, m->x);
   blocks(m, st, n, 0, 0, m->d_pos);
-  gemv(m, st, m->lm(), m->x, c.hidden, m->output_norm, c.rms_eps, nullptr, c.vocab, n, kModeStore,
-       &m->d_params->logits);
+  if (c.sandwich_norm)  // the last post-FFN norm and residual add run in the head's prologue
+    gemv(m, st, m->lm(), m->x2, c.hidden, m->output_norm, c.rms_eps, nullptr, c.vocab, n, kModeStore,
+         &m->d_params->logits, Resid{m->y, m->layers[c.n_layer - 1].post_ffw, nullptr});
+  else
+    gemv(m, st, m->lm(), m->x, c.hidden, m->output_norm, c.rms_eps, nullptr, c.vocab, n, kModeStore,
+         &m->d_params->logits);
   sample(m, st, nullptr, c.vocab, n, 0.f, 0, 0, nullptr, nullptr, m->d_params, topp);
 }
 
@@ -886,6 +924,7 @@ int load(const qdec_config* cfgp, const qdec_tensor* ts, int32_t n, int32_t max_
     m->ws_T = std::max(std::min(max_ctx, 4096), max_seqs);
     const size_t T = m->ws_T;
     m->x = m->dalloc<float>(T * H);
+    m->x2 = m->dalloc<float>(T * H);
     m->h = m->dalloc<float>(T * H);
     m->y = m->dalloc<float>(T * H);
     m->qkv = m->dalloc<float>(T * m->nqkv);
