@@ -15,6 +15,9 @@ Readings where the pages are silent (each also listed in the design notes):
     i % window_period == window_period - 1; local layers use rope_theta_local;
   * sandwich norms: RMSNorm of each sublayer output (own gain) before its
     residual add;
+  * q/k/v biases (qwen2, which the same page says differs from llama only by
+    its three bias lines): each added to its projection's output, before the
+    per-head norm and RoPE;
   * positions are absolute: a call appends at kv_len and advances it.
 
 Weights are decoded exactly (``oracle.blocks``) and all arithmetic is float64,
@@ -120,6 +123,10 @@ class OracleModel:
             q = h @ self.mat(p + "attn_q.weight").T
             k = h @ self.mat(p + "attn_k.weight").T
             v = h @ self.mat(p + "attn_v.weight").T
+            if c.get("qkv_bias"):
+                q = q + self.mat(p + "attn_q.bias")
+                k = k + self.mat(p + "attn_k.bias")
+                v = v + self.mat(p + "attn_v.bias")
             q = q.reshape(T, nq, hd).transpose(1, 0, 2)
             k = k.reshape(T, nkv, hd).transpose(1, 0, 2)
             v = v.reshape(T, nkv, hd).transpose(1, 0, 2)

@@ -11,6 +11,7 @@ indexes fixed row ranges of about 4M values, so large tensors are drawn in
 parallel with a result independent of the thread count.
   * 2-D matrices: N(0, 0.02), then block-encoded in the config's type
   * 1-D gains: 1 + N(0, 0.02), float32
+  * 1-D q/k/v biases (qkv_bias): N(0, 0.5), float32
   * prompts: uniform ids in [0, vocab)
   * preset K/V (batched long-context workload): N(0, 1) float32
 
@@ -152,7 +153,7 @@ def encode(ttype, x):
 
 # ---------------------------------------------------------------- tensors
 def tensor_specs(cfg):
-    """List of (name, type id, rows, cols, kind) for a config, kind in {matrix, gain}."""
+    """List of (name, type id, rows, cols, kind) for a config, kind in {matrix, gain, bias}."""
     H, hd = cfg["hidden"], cfg["head_dim"]
     qd, kd, F, V = cfg["n_head"] * hd, cfg["n_head_kv"] * hd, cfg["ffn"], cfg["vocab"]
     wt = TYPE_IDS[cfg["wtype"]]
@@ -165,6 +166,10 @@ def tensor_specs(cfg):
             (p + "attn_k.weight", wt, kd, H, "matrix"),
             (p + "attn_v.weight", wt, kd, H, "matrix"),
         ]
+        if cfg.get("qkv_bias"):
+            specs += [(p + "attn_q.bias", T_F32, 1, qd, "bias"),
+                      (p + "attn_k.bias", T_F32, 1, kd, "bias"),
+                      (p + "attn_v.bias", T_F32, 1, kd, "bias")]
         if cfg["qk_norm"]:
             specs += [(p + "attn_q_norm.weight", T_F32, 1, hd, "gain"),
                       (p + "attn_k_norm.weight", T_F32, 1, hd, "gain")]
@@ -192,6 +197,9 @@ def _chunk_rows(cols):
 def _gen_tensor(seed, name, ttype, rows, cols, kind, pool):
     if kind == "gain":
         x = 1.0 + 0.02 * _rng(seed, name, 0).standard_normal(cols, dtype=np.float32)
+        return SynthTensor(name, T_F32, 1, cols, x.astype(np.float32).view(np.uint8).copy())
+    if kind == "bias":
+        x = 0.5 * _rng(seed, name, 0).standard_normal(cols, dtype=np.float32)
         return SynthTensor(name, T_F32, 1, cols, x.astype(np.float32).view(np.uint8).copy())
     cr = _chunk_rows(cols)
     starts = list(range(0, rows, cr))

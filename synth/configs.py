@@ -11,6 +11,7 @@ Each entry describes a decoder by its shape only; the weights are drawn by
   window, window_period -- sliding window length; layer i is global iff
                         i % window_period == window_period - 1
   qk_norm            -- per-head RMSNorm of Q and K before RoPE (Qwen3)
+  qkv_bias           -- the q, k and v projections add a bias (Qwen2); absent = False
   sandwich_norm      -- RMSNorm of each sublayer output before its residual add
   act                -- "silu" (SwiGLU) or "gelu_tanh" (GeGLU)
   wtype              -- block type of every 2-D layer matrix

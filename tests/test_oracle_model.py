@@ -188,3 +188,81 @@ def test_rmsnorm_and_rope_order_in_block():
     a = ops.apply_rope(ops.rmsnorm(x, w2, 1e-6), ang)
     b = ops.rmsnorm(ops.apply_rope(x, ang), w2, 1e-6)
     assert not np.allclose(a, b)
+
+
+# ---------------------------------------------------------------- q/k/v biases (qwen2)
+BIAS = dict(TINY, n_layer=1, qkv_bias=True)
+
+
+def bias_fill(seed, zero=(), bias_override=None):
+    """Random f32 tensors; names ending in an entry of ``zero`` are all zeros;
+    ``bias_override`` maps a bias name suffix to a fixed vector."""
+    r = np.random.default_rng(seed)
+    bias_override = bias_override or {}
+
+    def fill(name, rows, cols):
+        for suffix, vec in bias_override.items():
+            if name.endswith(suffix):
+                return np.asarray(vec, dtype=np.float64).reshape(rows, cols)
+        if any(name.endswith(z) for z in zero):
+            return np.zeros((rows, cols))
+        if name.endswith(".bias"):
+            return r.standard_normal((rows, cols))
+        if rows == 1:
+            return 1 + 0.1 * r.standard_normal((rows, cols))
+        return r.standard_normal((rows, cols))
+    return fill
+
+
+def f32_of(t):
+    return np.frombuffer(t.data.tobytes(), np.float32).astype(np.float64).reshape(t.rows, t.cols)
+
+
+def test_v_bias_with_zero_v_weight_is_the_attention_output():
+    """attn_v = 0 makes every value row equal b_v; the softmax weights of any
+    query sum to one, so each query head's attention output is b_v of its KV
+    head whatever q, k and their biases are.  With ffn_down = 0 as well the
+    residual after the layer is embed + W_o (b_v repeated over each query
+    group), at every position."""
+    t = f32_model(BIAS, bias_fill(3, zero=("attn_v.weight", "ffn_down.weight")))
+    m = OracleModel(BIAS, t, max_ctx=8)
+    toks = [4, 1, 7, 7, 2]
+    x = m.hidden(0, toks)
+    E = f32_of(t["token_embd.weight"])
+    bv = f32_of(t["blk.0.attn_v.bias"]).reshape(BIAS["n_head_kv"], BIAS["head_dim"])
+    group = BIAS["n_head"] // BIAS["n_head_kv"]
+    a = np.repeat(bv, group, axis=0).reshape(-1)
+    want = E[toks] + a @ f32_of(t["blk.0.attn_output.weight"]).T
+    assert np.allclose(x, want, rtol=1e-12, atol=1e-12)
+
+
+def test_zero_biases_equal_the_model_without_biases():
+    cfg_b = dict(TINY, qkv_bias=True)
+    zero = {s: np.zeros(n) for s, n in (("attn_q.bias", 16), ("attn_k.bias", 8), ("attn_v.bias", 8))}
+    tb = f32_model(cfg_b, bias_fill(5, bias_override=zero))
+    tn = f32_model(TINY, bias_fill(5))
+    toks = [1, 2, 3, 9, 0]
+    lb = OracleModel(cfg_b, tb, max_ctx=8).forward(0, toks, all_logits=True)
+    ln = OracleModel(TINY, tn, max_ctx=8).forward(0, toks, all_logits=True)
+    assert np.array_equal(lb, ln)
+
+
+def test_q_bias_is_irrelevant_when_keys_are_zero_and_k_bias_is_not():
+    """attn_k = 0 and b_k = 0 make every key zero, so every score is zero and
+    the q bias cannot move the output; a non-zero b_k makes the scores depend
+    on the q bias again."""
+    toks = [5, 5, 8, 0, 3, 1]
+    zk = {"attn_k.bias": np.zeros(8)}
+
+    def run(bq, bk):
+        over = {"attn_q.bias": bq}
+        if bk is not None:
+            over["attn_k.bias"] = bk
+        t = f32_model(BIAS, bias_fill(9, zero=("attn_k.weight",), bias_override=over))
+        return OracleModel(BIAS, t, max_ctx=8).forward(0, toks, all_logits=True)
+
+    r = np.random.default_rng(1)
+    bq1, bq2, bk = 3 * r.standard_normal(16), 3 * r.standard_normal(16), 3 * r.standard_normal(8)
+    assert np.array_equal(run(bq1, zk["attn_k.bias"]), run(bq2, zk["attn_k.bias"]))
+    d = np.max(np.abs(run(bq1, bk) - run(bq2, bk)))
+    assert d > 1e-3
