@@ -40,7 +40,8 @@ class QdecPoisoned(QdecError):
 class _Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("n_layer", "hidden", "n_head", "n_head_kv", "head_dim", "ffn", "vocab")] + \
                [(n, ctypes.c_float) for n in ("rms_eps", "rope_theta", "rope_theta_local")] + \
-               [(n, ctypes.c_int32) for n in ("window", "window_period", "qk_norm", "sandwich_norm", "act")]
+               [(n, ctypes.c_int32) for n in ("window", "window_period", "qk_norm", "sandwich_norm", "act",
+                                              "qkv_bias")]
 
 
 class _Tensor(ctypes.Structure):
@@ -154,6 +155,7 @@ def config_struct(cfg):
     c.rope_theta_local = float(cfg.get("rope_theta_local", cfg["rope_theta"]))
     c.qk_norm = 1 if cfg["qk_norm"] else 0
     c.sandwich_norm = 1 if cfg["sandwich_norm"] else 0
+    c.qkv_bias = 1 if cfg.get("qkv_bias") else 0
     act = cfg["act"]
     c.act = _ACTS[act] if isinstance(act, str) else int(act)
     return c

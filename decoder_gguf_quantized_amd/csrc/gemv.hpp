@@ -51,6 +51,7 @@ struct GemvArgs {
   const float* res_add;
   const float* res_w;
   float* res_out;
+  const float* bias;     // store mode: y[n] += bias[n] (qwen2's q/k/v bias adds), or null
 };
 
 QD_DEV float act_silu(float g) { return g / (1.0f + expf(-g)); }
@@ -343,7 +344,7 @@ QD_DEV void gemv_store(const GemvArgs& a, int grp, int lane, const float (&scale
           const int row = grp * R + i;
           if (row < a.rows) {
             if constexpr (MODE == kModeAdd) yr[row] += sv[i];
-            else yr[row] = sv[i];
+            else yr[row] = a.bias ? sv[i] + a.bias[row] : sv[i];
           }
         }
       }

@@ -118,6 +118,7 @@ struct RopeArgs {
   const float2* rope;   // [ctx][hd/2] (cos, sin) of f32(pos) * inv_freq[i]
   int seq0, pos0;       // prefill: token t -> (seq0, pos0 + t)
   const int* dpos;      // decode (non-null): token t -> (seq t, dpos[t])
+  const float* bias;    // [(nq + 2 nkv) hd] q|k|v projection bias added first, or null
 };
 
 __global__ __launch_bounds__(256) void rope_kv_kernel(RopeArgs a) {
@@ -137,6 +138,10 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(RopeArgs a) {
       int i = lane + 64 * r;
       x1[r] = i < half ? src[i] : 0.f;
       x2[r] = i < half ? src[i + half] : 0.f;
+      if (a.bias && i < half) {
+        x1[r] += a.bias[(size_t)hh * a.hd + i];
+        x2[r] += a.bias[(size_t)hh * a.hd + i + half];
+      }
       ss += x1[r] * x1[r] + x2[r] * x2[r];
     }
     const float* nw = is_q ? a.q_norm : (is_k ? a.k_norm : nullptr);

@@ -58,6 +58,7 @@ struct Layer {
   float* post_attn = nullptr;
   float* ffn_norm = nullptr;
   float* post_ffw = nullptr;
+  float* qkv_bias = nullptr;  // [nqkv] q|k|v projection bias, or null
   Mat qkv, o, gu, down;
   bool global = true;
 };
@@ -281,7 +282,9 @@ struct Resid {
 };
 
 void gemv(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, const float* norm_w, float eps,
-          float* y, int ldy, int nrows, int mode, float* const* y_ind = nullptr, Resid res = Resid{}) {
+          float* y, int ldy, int nrows, int mode, float* const* y_ind = nullptr, Resid res = Resid{},
+          const float* bias = nullptr) {
+  if (bias && mode != kModeStore) throw HipError{"gemv: a bias needs the store epilogue"};
   const int kp = w.nblk * 32;
   const size_t per_row = (size_t)kp * 4 + (w.type == kQ4_0 ? (size_t)w.nblk * 4 : 0);
   // rows per launch: a power of two (the kernel's M) whose staged inputs fit the LDS budget
@@ -312,7 +315,7 @@ void gemv(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, 
     GemvArgs a{w.qs, w.d, w.rows, w.nblk, x + (size_t)r0 * ldx, ldx, norm_w, eps,
                y ? y + (size_t)r0 * ldy : nullptr, ldy, mr, y_ind, (long)r0 * ldy,
                res.add ? res.add + (size_t)r0 * ldx : nullptr, res.add_w,
-               res.out ? res.out + (size_t)r0 * ldx : nullptr};
+               res.out ? res.out + (size_t)r0 * ldx : nullptr, bias};
     const size_t lds = per_row * M;
     const double bytes = w.gguf_bytes + (double)mr * kp * 4 + (double)mr * (pair ? w.rows / 2 : w.rows) * 4;
     Timed tm(m, st, gemv_class(w.type), bytes, 2.0 * mr * w.rows * (double)w.cols);
@@ -468,7 +471,7 @@ void rope_kv(qdec_model* m, hipStream_t st, int l, int n, int seq0, int pos0, co
   const Layer& L = m->layers[l];
   RopeArgs a{m->qkv, m->nqkv, m->q, m->kc + l * m->kv_layer, m->vc + l * m->kv_layer, m->max_ctx, c.n_head,
              c.n_head_kv, c.head_dim, L.q_norm, L.k_norm, c.rms_eps, L.global ? m->rope_g : m->rope_l,
-             seq0, pos0, dpos};
+             seq0, pos0, dpos, L.qkv_bias};
   Timed tm(m, st, "rope_kv", (double)n * m->nqkv * 8, 0);
   qlaunch(rope_kv_kernel, n, 256, 0, st, a);
 }
@@ -516,9 +519,10 @@ void blocks(qdec_model* m, hipStream_t st, int n, int seq, int pos0, const int* 
     // attention sublayer
     if (fuse && l > 0) {
       gemv(m, st, L.qkv, m->x2, H, L.attn_norm, c.rms_eps, m->qkv, m->nqkv, n, kModeStore, nullptr,
-           Resid{m->y, m->layers[l - 1].post_ffw, m->x});
+           Resid{m->y, m->layers[l - 1].post_ffw, m->x}, L.qkv_bias);
     } else if (dec) {
-      gemv(m, st, L.qkv, m->x, H, L.attn_norm, c.rms_eps, m->qkv, m->nqkv, n, kModeStore);
+      gemv(m, st, L.qkv, m->x, H, L.attn_norm, c.rms_eps, m->qkv, m->nqkv, n, kModeStore, nullptr, Resid{},
+           L.qkv_bias);
     } else {
       rmsnorm_rows(m, st, m->x, H, L.attn_norm, H, m->h, H, n, 0);
       gemm(m, st, L.qkv, m->h, H, n, m->qkv, m->nqkv, kModeStore);
@@ -635,6 +639,11 @@ std::vector<Expect> expected_tensors(const qdec_config& c) {
     e.push_back({p + "attn_q.weight", qd, H, true, true});
     e.push_back({p + "attn_k.weight", kd, H, true, true});
     e.push_back({p + "attn_v.weight", kd, H, true, true});
+    if (c.qkv_bias) {
+      e.push_back({p + "attn_q.bias", 1, qd, false, true});
+      e.push_back({p + "attn_k.bias", 1, kd, false, true});
+      e.push_back({p + "attn_v.bias", 1, kd, false, true});
+    }
     if (c.qk_norm) {
       e.push_back({p + "attn_q_norm.weight", 1, hd, false, true});
       e.push_back({p + "attn_k_norm.weight", 1, hd, false, true});
@@ -779,7 +788,7 @@ int load(const qdec_config* cfgp, const qdec_tensor* ts, int32_t n, int32_t max_
       set_err("tensor '%s': type %d unsupported (F32 = 0, Q4_0 = 2, Q8_0 = 8)", t.name, t.type);
       return QDEC_REFUSED;
     }
-    if (!e.matrix && t.type != kF32) { set_err("tensor '%s': norm gains must be F32", t.name); return QDEC_REFUSED; }
+    if (!e.matrix && t.type != kF32) { set_err("tensor '%s': norm gains and biases must be F32", t.name); return QDEC_REFUSED; }
     if (t.rows != e.rows || t.cols != e.cols) {
       set_err("tensor '%s': dims [%lld][%lld], expected [%lld][%lld]", t.name, (long long)t.rows, (long long)t.cols,
               (long long)e.rows, (long long)e.cols);
@@ -847,6 +856,16 @@ int load(const qdec_config* cfgp, const qdec_tensor* ts, int32_t n, int32_t max_
       if (c.qk_norm) {
         L.q_norm = upload_vec(m, TN(p + "attn_q_norm.weight"), st);
         L.k_norm = upload_vec(m, TN(p + "attn_k_norm.weight"), st);
+      }
+      if (c.qkv_bias) {  // one fused q|k|v vector, in the row order of the fused matrix
+        L.qkv_bias = m->dalloc<float>((size_t)m->nqkv);
+        const char* part[3] = {"attn_q.bias", "attn_k.bias", "attn_v.bias"};
+        const int off[3] = {0, m->qd, m->qd + m->kd};
+        for (int j = 0; j < 3; ++j) {
+          const qdec_tensor& tb = TN(p + part[j]);
+          hipck(hipMemcpyAsync(L.qkv_bias + off[j], tb.host_data, (size_t)tb.cols * 4, hipMemcpyHostToDevice, st),
+                "upload");
+        }
       }
       if (c.sandwich_norm) {
         L.post_attn = upload_vec(m, TN(p + "post_attention_norm.weight"), st);

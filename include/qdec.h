@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define QDEC_ABI_VERSION 3
+#define QDEC_ABI_VERSION 4
 
 enum { QDEC_OK = 0, QDEC_REFUSED = 1, QDEC_INTERNAL = 2 };
 
@@ -86,13 +86,17 @@ typedef struct {
   int32_t qk_norm;       /* per-head RMSNorm of q and k (gain [head_dim]) before RoPE */
   int32_t sandwich_norm; /* RMSNorm of each sublayer output before its residual add */
   int32_t act;           /* QDEC_ACT_* */
+  int32_t qkv_bias;      /* q, k and v projections add a bias vector ([S] "The format": the
+                            qwen2 architecture differs from llama by these three bias adds);
+                            tensors blk.i.attn_{q,k,v}.bias, F32, rows = 1 */
 } qdec_config;
 
 /* One tensor in GGUF naming ("token_embd.weight", "blk.3.attn_q.weight",
  * "blk.3.attn_q_norm.weight", "blk.3.post_attention_norm.weight",
- * "blk.3.post_ffw_norm.weight", "output_norm.weight", "output.weight", ...).
- * Matrices are [rows = output dim][cols = input dim]; 1-D gains have rows = 1,
- * type QDEC_T_F32.  host_data is borrowed for the duration of the call. */
+ * "blk.3.post_ffw_norm.weight", "blk.3.attn_q.bias", "output_norm.weight",
+ * "output.weight", ...).
+ * Matrices are [rows = output dim][cols = input dim]; 1-D gains and biases have
+ * rows = 1, type QDEC_T_F32.  host_data is borrowed for the duration of the call. */
 typedef struct {
   const char* name;
   int32_t type;

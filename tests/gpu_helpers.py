@@ -7,12 +7,13 @@ import synth
 TOL = 2e-3  # max |gpu - oracle| / max |oracle| per logits row
 
 BASE = dict(rms_eps=1e-6, rope_theta=1e4, rope_theta_local=1e4, window=0, window_period=0, qk_norm=False,
-            sandwich_norm=False, act="silu", wtype="q8_0", embd_type="q8_0", tied=True, prompt_len=0,
+            sandwich_norm=False, qkv_bias=False, act="silu", wtype="q8_0", embd_type="q8_0", tied=True, prompt_len=0,
             decode_steps=0, batch=1, temperature=0.0, preset_kv=0)
 
 # Small models, one per kernel variant: head_dim 64/128/256, query heads per KV
 # head 1/2/4/8, Q8_0/Q4_0/F32, tied/untied head, QK-norm, sliding window,
-# sandwich norms, gelu_tanh, FFN widths that are not multiples of 32 or 64.
+# sandwich norms, gelu_tanh, FFN widths that are not multiples of 32 or 64,
+# q/k/v biases.
 SMALL = {
     "qwen3_hd128_g2": dict(BASE, name="qwen3_hd128_g2", n_layer=2, hidden=256, n_head=4, n_head_kv=2, head_dim=128,
                            ffn=512, vocab=5000, qk_norm=True, rope_theta=1e6, rope_theta_local=1e6, seed=11),
@@ -26,6 +27,9 @@ SMALL = {
                              ffn=336, vocab=1100, wtype="f32", embd_type="f32", seed=14),
     "gqa8_hd128": dict(BASE, name="gqa8_hd128", n_layer=1, hidden=1024, n_head=8, n_head_kv=1, head_dim=128,
                        ffn=96, vocab=4200, qk_norm=True, seed=15),
+    "qwen2_bias_hd64_g2": dict(BASE, name="qwen2_bias_hd64_g2", n_layer=2, hidden=384, n_head=6, n_head_kv=3,
+                               head_dim=64, ffn=1024, vocab=3000, qkv_bias=True, embd_type="f32", tied=False,
+                               rope_theta=1e6, rope_theta_local=1e6, seed=16),
 }
 
 

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version(L):
-    assert L.qdec_abi_version() == 3
+    assert L.qdec_abi_version() == 4
 
 
 def cfg(**kw):
