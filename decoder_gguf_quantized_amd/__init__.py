@@ -16,7 +16,7 @@ import os
 import threading
 
 __all__ = ["Model", "QdecError", "QdecPanic", "QdecPoisoned", "lib", "config_struct",
-           "debug_sample", "debug_matmul", "T_F32", "T_Q4_0", "T_Q8_0", "ALL_LOGITS", "TOKENS_ON_DEVICE"]
+           "debug_sample", "debug_matmul", "gguf_config", "archdef_builtin", "T_F32", "T_Q4_0", "T_Q8_0", "ALL_LOGITS", "TOKENS_ON_DEVICE"]
 
 T_F32, T_Q4_0, T_Q8_0 = 0, 2, 8
 ALL_LOGITS, TOKENS_ON_DEVICE = 1, 2
@@ -93,6 +93,9 @@ def lib():
                 "qdec_debug_sample": (ctypes.c_int, [P, I32, I32, F, F, U64, U64, P, P]),
                 "qdec_debug_matmul": (ctypes.c_int, [I32, I64, I64, P, I64, P, I32, P, I32, P]),
                 "qdec_kernel_timing": (ctypes.c_int, [P, I32, ctypes.POINTER(_KStat), I32, ctypes.POINTER(I32)]),
+                "qdec_gguf_config": (ctypes.c_int, [ctypes.c_char_p, ctypes.c_char_p, ctypes.POINTER(_Config)]),
+                "qdec_load_gguf": (ctypes.c_int, [ctypes.c_char_p, ctypes.c_char_p, I32, I32, P, ctypes.POINTER(P)]),
+                "qdec_archdef_builtin": (ctypes.c_char_p, [ctypes.c_char_p]),
             }
             for name, (res, args) in sig.items():
                 fn = getattr(L, name)
@@ -161,6 +164,42 @@ def config_struct(cfg):
     return c
 
 
+def _config_dict(c):
+    d = {k: int(getattr(c, k)) for k in ("n_layer", "hidden", "n_head", "n_head_kv", "head_dim", "ffn", "vocab",
+                                         "window", "window_period")}
+    d.update(rms_eps=float(c.rms_eps), rope_theta=float(c.rope_theta), rope_theta_local=float(c.rope_theta_local),
+             qk_norm=bool(c.qk_norm), sandwich_norm=bool(c.sandwich_norm), qkv_bias=bool(c.qkv_bias),
+             act={v: k for k, v in _ACTS.items()}.get(int(c.act), int(c.act)))
+    return d
+
+
+def _path_arg(name, v):
+    if isinstance(v, os.PathLike):
+        v = os.fspath(v)
+    if not isinstance(v, str):
+        raise QdecError(f"{name} must be a path string")
+    return v.encode()
+
+
+def gguf_config(path, archdef=None):
+    """The model shape a GGUF file and an architecture definition give (no GPU
+    work): a dict with the keys of ``config_struct``.  ``archdef`` is the
+    definition's text, or None for the library's built-in one for the file's
+    architecture."""
+    c = _Config()
+    ad = None if archdef is None else str(archdef).encode()
+    rc = lib().qdec_gguf_config(_path_arg("path", path), ad, ctypes.byref(c))
+    if rc != 0:
+        raise QdecError(_last_error())
+    return _config_dict(c)
+
+
+def archdef_builtin(arch):
+    """Text of the library's built-in definition of ``arch``, or None."""
+    t = lib().qdec_archdef_builtin(str(arch).encode())
+    return t.decode() if t else None
+
+
 class Model:
     """One loaded model (a libqdec handle).  ``tensors`` maps GGUF names to
     records with ``type``, ``rows``, ``cols`` and ``data`` (raw bytes as a
@@ -193,6 +232,28 @@ class Model:
         if rc != 0:
             raise QdecPanic(_last_error())
         self._h = h
+
+    @classmethod
+    def from_gguf(cls, path, archdef=None, max_seqs=1, max_ctx=4096):
+        """Load a GGUF file; the block layout comes from ``archdef`` (text) or the
+        library's built-in definition for the file's architecture."""
+        cfg = gguf_config(path, archdef)
+        m = cls.__new__(cls)
+        m._h = None
+        m._thread = threading.get_ident()
+        m.cfg = cfg
+        m.vocab = cfg["vocab"]
+        m.max_seqs = _int("max_seqs", max_seqs)
+        m.max_ctx = _int("max_ctx", max_ctx)
+        h = ctypes.c_void_p()
+        ad = None if archdef is None else str(archdef).encode()
+        rc = lib().qdec_load_gguf(_path_arg("path", path), ad, m.max_seqs, m.max_ctx, _stream(), ctypes.byref(h))
+        if rc == 1:
+            raise QdecError(_last_error())
+        if rc != 0:
+            raise QdecPanic(_last_error())
+        m._h = h
+        return m
 
     # ------------------------------------------------------------ ownership
     def __copy__(self):

@@ -1,6 +1,10 @@
 """Compile libqdec.so (HIP, gfx950) in place.
 
     python -m decoder_gguf_quantized_amd.build
+
+Two translation units, compiled in parallel into _build/ and linked with
+hipcc: csrc/qdec.hip (kernels, launchers and the C ABI) and csrc/gguf.cpp
+(host-only: GGUF files and architecture definitions).
 """
 import os
 import subprocess
@@ -8,15 +12,18 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "csrc", "qdec.hip")
+SRC_HOST = os.path.join(HERE, "csrc", "gguf.cpp")
+BUILD = os.path.join(HERE, "_build")
 OUT = os.path.join(HERE, "libqdec.so")
 
 HIPCC_FLAGS = [
-    "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
+    "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",
     # packed-FP32 VALU forms stay off (the compiler would otherwise emit them
     # from plain float code)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
 
 
 def hipcc():
@@ -26,17 +33,36 @@ def hipcc():
     return "hipcc"
 
 
+def _noise(text):
+    return [ln for ln in text.splitlines() if "packed-fp32-ops" not in ln and ln.strip()]
+
+
 def build(verbose=False):
+    os.makedirs(BUILD, exist_ok=True)
+    objs = [os.path.join(BUILD, "qdec.o"), os.path.join(BUILD, "gguf.o")]
+    jobs = [[hipcc()] + HIPCC_FLAGS + ["-c", "-o", objs[0], SRC],
+            [os.environ.get("CXX", "g++")] + HOST_FLAGS + ["-c", "-o", objs[1], SRC_HOST]]
+    procs = []
+    for cmd in jobs:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True))
+    errors = []
+    for cmd, p in zip(jobs, procs):
+        out, _ = p.communicate()
+        if p.returncode != 0:
+            errors.append(f"{cmd[0]} {cmd[-1]} failed:\n" + "\n".join(_noise(out)))
+        elif verbose and _noise(out):
+            print("\n".join(_noise(out)))
+    if errors:
+        raise RuntimeError("\n".join(errors))
     tmp = OUT + ".tmp"
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-o", tmp, SRC]
+    link = [hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + objs
     if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    noise = [ln for ln in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in ln and ln.strip()]
+        print(" ".join(link), flush=True)
+    r = subprocess.run(link, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(noise))
-    if verbose and noise:
-        print("\n".join(noise))
+        raise RuntimeError("link failed:\n" + "\n".join(_noise(r.stdout + r.stderr)))
     os.replace(tmp, OUT)
     return OUT
 

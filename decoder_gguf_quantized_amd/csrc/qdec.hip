@@ -1001,6 +1001,9 @@ int load(const qdec_config* cfgp, const qdec_tensor* ts, int32_t n, int32_t max_
 }  // namespace
 
 // ================================================================= C ABI
+// Error text for the host-only sources of the library (model files).
+__attribute__((visibility("hidden"))) void qdec_set_error_text(const std::string& s) { g_err = s; }
+
 extern "C" {
 
 int32_t qdec_abi_version(void) { return QDEC_ABI_VERSION; }

@@ -119,6 +119,42 @@ const char* qdec_last_error(void); /* valid until the next call on this thread *
 int qdec_load_weights(const qdec_config* cfg, const qdec_tensor* tensors, int32_t n_tensors,
                       int32_t max_seqs, int32_t max_ctx, void* stream, qdec_model** out);
 
+/* Model files.  `path` names a GGUF file (the public GGUF container, versions 2
+ * and 3, little-endian; tensors named as in qdec_tensor); `archdef` is the text
+ * of an architecture definition in the format of [S] "The format" (header
+ * `arch` / `kind decoder` / `param`, sections prologue, block (per layer, {i}),
+ * epilogue; `dst = op(...)` or `op(dst, ...)`; `a | b`), or NULL for the
+ * built-in definition of the file's general.architecture (llama, qwen2, qwen3,
+ * gemma3: qdec_archdef_builtin).  The definition is compiled, not interpreted:
+ * each statement is evaluated symbolically and what the block computes must be
+ * one of the layouts the kernels run -- llama's pre-norm block with a silu or
+ * gelu_tanh gate, optionally with q/k/v biases, per-head q/k norms before RoPE,
+ * and sandwich norms; the prologue must be x = embed(token_embd.weight) and the
+ * epilogue logits = matmul(last(rms_norm(x, output_norm.weight)), output.weight
+ * | token_embd.weight).  Anything else is refused with the reason.
+ * Shape from the metadata of the definition's arch: <arch>.block_count,
+ * .embedding_length, .feed_forward_length, .attention.head_count,
+ * .attention.head_count_kv (default head_count), .attention.key_length
+ * (default embedding_length / head_count; value_length must equal it),
+ * .attention.layer_norm_rms_epsilon, .rope.freq_base (default 10000),
+ * .attention.sliding_window (default 0); vocab = rows of token_embd.weight.  A
+ * file with a window needs the definition's `param window_pattern P` (layer i
+ * is global iff i % P == P - 1); `param rope_freq_base_local B` sets the
+ * rotary base of window layers (default: the global one).  general.architecture
+ * must equal the definition's arch.
+ * qdec_gguf_config: the config only; no GPU work.  Status 1 on any refusal. */
+int qdec_gguf_config(const char* path, const char* archdef, qdec_config* out);
+
+/* qdec_gguf_config, then qdec_load_weights over the tensors the compiled
+ * layout reads, borrowed from a read-only mapping of the file until the weights
+ * are on the device.  Tensor types F32, Q4_0, Q8_0; a quantized row holds whole
+ * 32-value blocks.  Other tensors in the file are ignored. */
+int qdec_load_gguf(const char* path, const char* archdef, int32_t max_seqs, int32_t max_ctx, void* stream,
+                   qdec_model** out);
+
+/* Text of the built-in definition of `arch` (static storage), or NULL. */
+const char* qdec_archdef_builtin(const char* arch);
+
 /* Prefill ([W] Step 9, phase 1): append n_tokens host token ids at positions
  * kv_len(seq).. and advance kv_len(seq) by n_tokens.  Writes logits f32 [vocab]
  * of the last position (or [n_tokens][vocab] with QDEC_ALL_LOGITS) to d_logits,
