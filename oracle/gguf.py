@@ -11,8 +11,9 @@ bytes; an array is a u32 element type, a u64 count and the elements.
 
 Plain and slow on purpose: every field is read with ``struct`` in file order.
 It shares nothing with the GPU library's reader.  The tensor types the
-decoder uses are F32 (0), Q4_0 (2) and Q8_0 (8); other types are read as
-opaque records with their byte size unknown and refused when used.
+decoder uses are F32 (0), Q4_0 (2), Q8_0 (8), Q4_K (12) and Q6_K (14); other
+types are read as opaque records with their byte size unknown and refused
+when used.
 """
 import struct
 from dataclasses import dataclass, field
@@ -23,6 +24,7 @@ _SCALARS = {0: ("<B", 1), 1: ("<b", 1), 2: ("<H", 2), 3: ("<h", 2), 4: ("<I", 4)
             6: ("<f", 4), 7: ("<?", 1), 10: ("<Q", 8), 11: ("<q", 8), 12: ("<d", 8)}
 T_STRING, T_ARRAY = 8, 9
 BLOCK_BYTES = {8: 34, 2: 18}
+SUPER_BYTES = {12: 144, 14: 210}  # Q4_K, Q6_K: 256-value super-blocks
 
 
 class GGUFError(ValueError):
@@ -103,6 +105,10 @@ def tensor_nbytes(ttype, ne):
         if ne[0] % 32:
             raise GGUFError(f"row length {ne[0]} is not a whole number of 32-value blocks")
         return n // 32 * BLOCK_BYTES[ttype]
+    if ttype in SUPER_BYTES:
+        if ne[0] % 256:
+            raise GGUFError(f"row length {ne[0]} is not a whole number of 256-value super-blocks")
+        return n // 256 * SUPER_BYTES[ttype]
     return None
 
 

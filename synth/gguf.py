@@ -33,7 +33,7 @@ import struct
 
 import numpy as np
 
-from . import T_F32, T_Q4_0, T_Q8_0, tensor_specs
+from . import T_F32, T_Q4_0, T_Q4_K, T_Q6_K, T_Q8_0, tensor_specs
 
 MAGIC = b"GGUF"
 # metadata value types
@@ -125,7 +125,9 @@ def write(path, cfg, tensors, arch=None, alignment=32, order=None, vocab_strings
         t = tensors[n]
         if t.type in (T_Q8_0, T_Q4_0) and t.cols % 32:
             raise ValueError(f"{n}: {t.cols} columns is not a whole number of blocks")
-        if t.type not in (T_F32, T_Q8_0, T_Q4_0):
+        if t.type in (T_Q4_K, T_Q6_K) and t.cols % 256:
+            raise ValueError(f"{n}: {t.cols} columns is not a whole number of super-blocks")
+        if t.type not in (T_F32, T_Q8_0, T_Q4_0, T_Q4_K, T_Q6_K):
             raise ValueError(f"{n}: type {t.type}")
         ne = [t.cols] if t.rows == 1 and not n.endswith("embd.weight") and n != "output.weight" else [t.cols, t.rows]
         pad = (-off) % alignment
