@@ -2,17 +2,21 @@
 
     python -m decoder_gguf_quantized_amd.build
 
-Two translation units, compiled in parallel into _build/ and linked with
-hipcc: csrc/qdec.hip (kernels, launchers and the C ABI) and csrc/gguf.cpp
-(host-only: GGUF files and architecture definitions).
+Translation units, compiled in parallel into _build/ and linked with hipcc:
+csrc/qdec.hip (runtime, attention / sampling / misc kernels and the C ABI),
+csrc/kern_<type>.hip (the GEMV and GEMM instantiations of one weight type
+each) and csrc/gguf.cpp (host-only: GGUF files and architecture definitions).
 """
 import os
 import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(HERE, "csrc", "qdec.hip")
-SRC_HOST = os.path.join(HERE, "csrc", "gguf.cpp")
+CSRC = os.path.join(HERE, "csrc")
+SRC = os.path.join(CSRC, "qdec.hip")
+KERNEL_TYPES = ("f32", "q4_0", "q8_0", "q4_k", "q6_k")
+SRCS_HIP = [SRC] + [os.path.join(CSRC, f"kern_{t}.hip") for t in KERNEL_TYPES]
+SRC_HOST = os.path.join(CSRC, "gguf.cpp")
 BUILD = os.path.join(HERE, "_build")
 OUT = os.path.join(HERE, "libqdec.so")
 
@@ -39,9 +43,10 @@ def _noise(text):
 
 def build(verbose=False):
     os.makedirs(BUILD, exist_ok=True)
-    objs = [os.path.join(BUILD, "qdec.o"), os.path.join(BUILD, "gguf.o")]
-    jobs = [[hipcc()] + HIPCC_FLAGS + ["-c", "-o", objs[0], SRC],
-            [os.environ.get("CXX", "g++")] + HOST_FLAGS + ["-c", "-o", objs[1], SRC_HOST]]
+    objs = [os.path.join(BUILD, os.path.splitext(os.path.basename(f))[0] + ".o") for f in SRCS_HIP]
+    jobs = [[hipcc()] + HIPCC_FLAGS + ["-c", "-o", o, f] for o, f in zip(objs, SRCS_HIP)]
+    objs.append(os.path.join(BUILD, "gguf.o"))
+    jobs.append([os.environ.get("CXX", "g++")] + HOST_FLAGS + ["-c", "-o", objs[-1], SRC_HOST])
     procs = []
     for cmd in jobs:
         if verbose:

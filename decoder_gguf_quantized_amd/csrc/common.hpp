@@ -10,10 +10,20 @@ namespace qd {
 
 constexpr int kWave = 64;
 
-// ggml type ids
+// ggml type ids.  K-quant tensors are repacked at load into the 32-value block
+// layouts of the legacy types with exact f32 scales:
+//   Q4_K: Q4_0's nibble layout per 32-value sub-block, and a float2 (scale,
+//         min) per sub-block, w = scale * n - min (n the raw nibble);
+//   Q6_K: Q8_0's int8 layout (q - 32), and an f32 scale per 16 values.
 constexpr int kF32 = 0;
 constexpr int kQ4_0 = 2;
 constexpr int kQ8_0 = 8;
+constexpr int kQ4_K = 12;
+constexpr int kQ6_K = 14;
+
+// Types stored as 16 nibble bytes per 32-value block / as int8 per value.
+constexpr bool nibble_layout(int qt) { return qt == kQ4_0 || qt == kQ4_K; }
+constexpr bool int8_layout(int qt) { return qt == kQ8_0 || qt == kQ6_K; }
 
 template <int CTRL, int ROW_MASK = 0xf>
 QD_DEV float dpp_add(float v) {
@@ -71,6 +81,12 @@ QD_DEV float4 load_nt(const float4* p) {
   return make_float4(v.x, v.y, v.z, v.w);
 }
 QD_DEV float load_half_nt(const uint16_t* p) { return half_bits_to_float(__builtin_nontemporal_load(p)); }
+QD_DEV float load_nt(const float* p) { return __builtin_nontemporal_load(p); }
+typedef float qd_f32x2 __attribute__((ext_vector_type(2)));
+QD_DEV float2 load_nt(const float2* p) {
+  const qd_f32x2 v = __builtin_nontemporal_load(reinterpret_cast<const qd_f32x2*>(p));
+  return make_float2(v.x, v.y);
+}
 
 // v & m through an opaque instruction, so that the byte-wise conversions of the
 // masked word stay v_cvt_f32_ubyteN instead of being folded into bit-field

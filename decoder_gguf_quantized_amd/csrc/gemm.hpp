@@ -48,9 +48,9 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
 
   // staging registers
   float4 xa[2];
-  uint4 wq;        // Q8_0: 16 int8; F32 uses wf[4]; Q4_0 uses the low 8 bytes
+  uint4 wq;        // int8 layouts: 16 int8; F32 uses wf[4]; nibble layouts use the low 8 bytes
   float4 wf[4];
-  float wd = 0.f;
+  float wd = 0.f, wmin = 0.f;  // block scale (Q6_K: of this thread's 16 values); Q4_K min
   const int brow = tid >> 1, bhalf = tid & 1;
   const bool brow_ok = n0 + brow < a.rows;
 
@@ -64,14 +64,21 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
     }
     if (brow_ok) {
       size_t r = n0 + brow;
-      if constexpr (QT == kQ8_0) {
+      if constexpr (int8_layout(QT)) {
         wq = *reinterpret_cast<const uint4*>(a.qs + r * kp + kb * BK + 16 * bhalf);
-        wd = load_half(a.d + r * a.nblk + kb);
-      } else if constexpr (QT == kQ4_0) {
+        if constexpr (QT == kQ8_0) wd = load_half(a.d + r * a.nblk + kb);
+        else wd = reinterpret_cast<const float*>(a.d)[r * 2 * a.nblk + 2 * kb + bhalf];
+      } else if constexpr (nibble_layout(QT)) {
         uint2 v = *reinterpret_cast<const uint2*>(a.qs + (r * a.nblk + kb) * 16 + 8 * bhalf);
         wq.x = v.x;
         wq.y = v.y;
-        wd = load_half(a.d + r * a.nblk + kb);
+        if constexpr (QT == kQ4_0) {
+          wd = load_half(a.d + r * a.nblk + kb);
+        } else {
+          const float2 sm = reinterpret_cast<const float2*>(a.d)[r * a.nblk + kb];
+          wd = sm.x;
+          wmin = sm.y;
+        }
       } else {
         const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.qs) + r * kp + kb * BK + 16 * bhalf);
 #pragma unroll
@@ -89,20 +96,28 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
       As[buf][4 * kq + 2][row] = xa[i].z;
       As[buf][4 * kq + 3][row] = xa[i].w;
     }
-    if constexpr (QT == kQ8_0) {
+    if constexpr (int8_layout(QT)) {
       uint32_t w4[4] = {wq.x, wq.y, wq.z, wq.w};
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float v = brow_ok ? wd * (float)(int8_t)(w4[i >> 2] >> (8 * (i & 3))) : 0.f;
         Bs[buf][16 * bhalf + i][brow] = v;
       }
-    } else if constexpr (QT == kQ4_0) {
+    } else if constexpr (nibble_layout(QT)) {
       uint32_t w2[2] = {wq.x, wq.y};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         uint32_t byte = (w2[i >> 2] >> (8 * (i & 3))) & 0xffu;
-        float lo = brow_ok ? wd * (float)((int)(byte & 15u) - 8) : 0.f;
-        float hi = brow_ok ? wd * (float)((int)(byte >> 4) - 8) : 0.f;
+        float lo, hi;
+        if constexpr (QT == kQ4_0) {
+          lo = wd * (float)((int)(byte & 15u) - 8);
+          hi = wd * (float)((int)(byte >> 4) - 8);
+        } else {  // scale * n - min, rounded once
+          lo = fmaf(wd, (float)(byte & 15u), -wmin);
+          hi = fmaf(wd, (float)(byte >> 4), -wmin);
+        }
+        lo = brow_ok ? lo : 0.f;
+        hi = brow_ok ? hi : 0.f;
         Bs[buf][8 * bhalf + i][brow] = lo;
         Bs[buf][16 + 8 * bhalf + i][brow] = hi;
       }
@@ -190,7 +205,7 @@ __global__ __launch_bounds__(256, 1) void gemm_ksplit_kernel(GemmArgs a) {
   float4 xa[4];
   uint4 wq[2];
   float4 wf[8];
-  float wd = 0.f;
+  float wd = 0.f, wd2 = 0.f, wmin = 0.f;  // scale (Q6_K: of values 0..15, wd2 of 16..31); Q4_K min
   const int brow = tid >> 2, bblk = tid & 3;
   const bool brow_ok = n0 + brow < a.rows;
 
@@ -205,14 +220,26 @@ __global__ __launch_bounds__(256, 1) void gemm_ksplit_kernel(GemmArgs a) {
     const int kb = st * 4 + bblk;
     if (brow_ok && kb < a.nblk) {
       const size_t r = n0 + brow;
-      if constexpr (QT == kQ8_0) {
+      if constexpr (int8_layout(QT)) {
         const uint4* p = reinterpret_cast<const uint4*>(a.qs + r * kp + kb * 32);
         wq[0] = p[0];
         wq[1] = p[1];
-        wd = load_half(a.d + r * a.nblk + kb);
-      } else if constexpr (QT == kQ4_0) {
+        if constexpr (QT == kQ8_0) {
+          wd = wd2 = load_half(a.d + r * a.nblk + kb);
+        } else {
+          const float2 s2 = reinterpret_cast<const float2*>(a.d)[r * a.nblk + kb];
+          wd = s2.x;
+          wd2 = s2.y;
+        }
+      } else if constexpr (nibble_layout(QT)) {
         wq[0] = *reinterpret_cast<const uint4*>(a.qs + (r * a.nblk + kb) * 16);
-        wd = load_half(a.d + r * a.nblk + kb);
+        if constexpr (QT == kQ4_0) {
+          wd = load_half(a.d + r * a.nblk + kb);
+        } else {
+          const float2 sm = reinterpret_cast<const float2*>(a.d)[r * a.nblk + kb];
+          wd = sm.x;
+          wmin = sm.y;
+        }
       } else {
         const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.qs) + r * kp + kb * 32);
 #pragma unroll
@@ -220,7 +247,7 @@ __global__ __launch_bounds__(256, 1) void gemm_ksplit_kernel(GemmArgs a) {
       }
     } else {
       wq[0] = wq[1] = make_uint4(0, 0, 0, 0);
-      wd = 0.f;
+      wd = wd2 = wmin = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) wf[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
@@ -237,10 +264,19 @@ __global__ __launch_bounds__(256, 1) void gemm_ksplit_kernel(GemmArgs a) {
       As[buf][4 * kq + 3][c] = xa[i].w;
     }
     const int kk = bblk * 32, bc = brow ^ (8 * bblk);
-    if constexpr (QT == kQ8_0) {
+    if constexpr (int8_layout(QT)) {
       const uint32_t w8[8] = {wq[0].x, wq[0].y, wq[0].z, wq[0].w, wq[1].x, wq[1].y, wq[1].z, wq[1].w};
 #pragma unroll
-      for (int i = 0; i < 32; ++i) Bs[buf][kk + i][bc] = wd * (float)(int8_t)(w8[i >> 2] >> (8 * (i & 3)));
+      for (int i = 0; i < 32; ++i)
+        Bs[buf][kk + i][bc] = (i < 16 ? wd : wd2) * (float)(int8_t)(w8[i >> 2] >> (8 * (i & 3)));
+    } else if constexpr (QT == kQ4_K) {
+      const uint32_t w4[4] = {wq[0].x, wq[0].y, wq[0].z, wq[0].w};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t byte = (w4[i >> 2] >> (8 * (i & 3))) & 0xffu;
+        Bs[buf][kk + i][bc] = fmaf(wd, (float)(byte & 15u), -wmin);
+        Bs[buf][kk + 16 + i][bc] = fmaf(wd, (float)(byte >> 4), -wmin);
+      }
     } else if constexpr (QT == kQ4_0) {
       const uint32_t w4[4] = {wq[0].x, wq[0].y, wq[0].z, wq[0].w};
 #pragma unroll

@@ -85,9 +85,10 @@ QD_DEV float dot16_q8(uint4 w, const float4& a, const float4& b, const float4& c
   return s;
 }
 
-// Activations per lane unit: Q8_0 16, Q4_0 32, F32 4.
+// Activations per lane unit: int8 layouts (Q8_0, Q6_K) 16, nibble layouts
+// (Q4_0, Q4_K) 32, F32 4.
 template <int QT>
-constexpr int unit_floats() { return QT == kQ8_0 ? 16 : (QT == kQ4_0 ? 32 : 4); }
+constexpr int unit_floats() { return int8_layout(QT) ? 16 : (nibble_layout(QT) ? 32 : 4); }
 
 // Load the input rows into LDS, times the RMSNorm gain when the prologue norm is
 // on, and return each row's norm scale rsqrt(mean_k x^2 + eps) (1 without norm).
@@ -219,6 +220,7 @@ template <int QT, int R, int U>
 struct WRegs {
   uint4 w[R][U];
   float d[R][U];
+  float m[R][U];  // Q4_K sub-block mins (unused, and optimised away, for the other types)
 };
 
 // Rows of group `grp`: R consecutive rows, or for the pair modes R/2 outputs,
@@ -258,6 +260,18 @@ QD_DEV void gemv_load(const GemvArgs& a, const int (&r)[R], int base, int lane, 
         const uint16_t* rd = a.d + (size_t)r[i] * a.nblk;
         W.w[i][k] = load_nt(reinterpret_cast<const uint4*>(rq + uc * 16u));
         W.d[i][k] = load_half_nt(rd + uc);
+      } else if constexpr (QT == kQ4_K) {
+        const uint8_t* rq = a.qs + (size_t)r[i] * a.nblk * 16;
+        const float2* rs = reinterpret_cast<const float2*>(a.d) + (size_t)r[i] * a.nblk;
+        W.w[i][k] = load_nt(reinterpret_cast<const uint4*>(rq + uc * 16u));
+        const float2 sm = load_nt(rs + uc);
+        W.d[i][k] = sm.x;
+        W.m[i][k] = sm.y;
+      } else if constexpr (QT == kQ6_K) {
+        const uint8_t* rq = a.qs + (size_t)r[i] * kp;
+        const float* rs = reinterpret_cast<const float*>(a.d) + (size_t)r[i] * 2 * a.nblk;
+        W.w[i][k] = load_nt(reinterpret_cast<const uint4*>(rq + uc * 16u));
+        W.d[i][k] = load_nt(rs + uc);
       } else {
         const uint8_t* rq = a.qs + (size_t)r[i] * kp * 4;
         W.w[i][k] = load_nt(reinterpret_cast<const uint4*>(rq + uc * 16u));
@@ -302,13 +316,17 @@ QD_DEV void gemv_compute(const float4* xs4, const float* xsum, int kp, int nblk,
       float4 xv[NV];
 #pragma unroll
       for (int i = 0; i < NV; ++i) xv[i] = xs4[(mi * NV + i) * nunits + u];
-      if constexpr (QT == kQ8_0) {
+      if constexpr (int8_layout(QT)) {
 #pragma unroll
         for (int i = 0; i < R; ++i) acc[i][mi] += W.d[i][k] * dot16_q8(W.w[i][k], xv[0], xv[1], xv[2], xv[3]);
       } else if constexpr (QT == kQ4_0) {
         const float bs = 8.0f * xsum[mi * nblk + u];
 #pragma unroll
         for (int i = 0; i < R; ++i) acc[i][mi] += W.d[i][k] * (dot32_q4_raw4(W.w[i][k], xv) - bs);
+      } else if constexpr (QT == kQ4_K) {
+        const float xs = xsum[mi * nblk + u];
+#pragma unroll
+        for (int i = 0; i < R; ++i) acc[i][mi] += W.d[i][k] * dot32_q4_raw4(W.w[i][k], xv) - W.m[i][k] * xs;
       } else {
 #pragma unroll
         for (int i = 0; i < R; ++i) {
@@ -378,12 +396,12 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(GemvArgs a) {
   constexpr int NS = gemv_sets<R, U, M>();
   extern __shared__ float4 xs4[];
   const int kp = a.nblk * 32;
-  float* xsum = reinterpret_cast<float*>(xs4 + M * kp / 4);  // Q4_0 only: [M][nblk] block sums of x
+  float* xsum = reinterpret_cast<float*>(xs4 + M * kp / 4);  // nibble layouts: [M][nblk] block sums of x
   constexpr bool kPair = MODE == kModePairSilu || MODE == kModePairGelu;
   const int lane = threadIdx.x & 63;
   const int gwave = __builtin_amdgcn_readfirstlane(blockIdx.x * NW + (threadIdx.x >> 6));
   const int nwaves = gridDim.x * NW;
-  const int nunits = QT == kQ8_0 ? 2 * a.nblk : (QT == kQ4_0 ? a.nblk : kp / 4);
+  const int nunits = int8_layout(QT) ? 2 * a.nblk : (nibble_layout(QT) ? a.nblk : kp / 4);
   const int ngroups = kPair ? a.rows / R : (a.rows + R - 1) / R;
   const int tpg = (nunits + 64 * U - 1) / (64 * U);  // tiles per row group
 
@@ -412,7 +430,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(GemvArgs a) {
 
   float scale[M];
   gemv_stage_x<QT, M, NW, RES>(a, xs4, kp, scale);  // ends with a barrier
-  if constexpr (QT == kQ4_0) {
+  if constexpr (nibble_layout(QT)) {
     for (int i = threadIdx.x; i < M * a.nblk; i += 64 * NW) {
       const int mi = i / a.nblk, u = i % a.nblk;
       float s = 0.f;

@@ -165,7 +165,7 @@ void read_value(Cursor& c, uint32_t t, int depth, Meta* out) {
   fail("GGUF: metadata value type %u unknown", t);
 }
 
-// Bytes of a tensor the decoder can read (F32, Q4_0, Q8_0), -1 for others.
+// Bytes of a tensor the decoder can read (F32, Q4_0, Q8_0, Q4_K, Q6_K), -1 for others.
 int64_t tensor_nbytes(const TInfo& t) {
   uint64_t n = 1;
   for (uint32_t d = 0; d < t.n_dims; ++d)
@@ -175,6 +175,11 @@ int64_t tensor_nbytes(const TInfo& t) {
     if (t.ne[0] % 32) fail("GGUF: tensor '%s': row of %llu values is not whole 32-value blocks", t.name.c_str(),
                            (unsigned long long)t.ne[0]);
     return (int64_t)(n / 32 * (t.type == QDEC_T_Q8_0 ? 34 : 18));
+  }
+  if (t.type == QDEC_T_Q4_K || t.type == QDEC_T_Q6_K) {
+    if (t.ne[0] % 256) fail("GGUF: tensor '%s': row of %llu values is not whole 256-value super-blocks",
+                            t.name.c_str(), (unsigned long long)t.ne[0]);
+    return (int64_t)(n / 256 * (t.type == QDEC_T_Q4_K ? 144 : 210));
   }
   return -1;
 }
@@ -781,7 +786,7 @@ int qdec_load_gguf(const char* path, const char* archdef, int32_t max_seqs, int3
       if (it == f.by_name.end()) continue;  // qdec_load_weights names what is missing
       const TInfo& t = f.tensors[it->second];
       const int64_t nb = tensor_nbytes(t);
-      if (nb < 0) fail("GGUF: tensor '%s' has type %u (this library reads F32 = 0, Q4_0 = 2, Q8_0 = 8)", n.c_str(), t.type);
+      if (nb < 0) fail("GGUF: tensor '%s' has type %u (this library reads F32 = 0, Q4_0 = 2, Q8_0 = 8, Q4_K = 12, Q6_K = 14)", n.c_str(), t.type);
       if (t.n_dims > 2) fail("GGUF: tensor '%s' has %u dimensions", n.c_str(), t.n_dims);
       qdec_tensor q;
       q.name = it->first.c_str();

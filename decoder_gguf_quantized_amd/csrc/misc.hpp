@@ -21,12 +21,20 @@ QD_DEV float weight_at(const WView& w, size_t row, int k) {
     float d = load_half(w.d + row * w.nblk + (k >> 5));
     return d * (float)reinterpret_cast<const int8_t*>(w.qs)[row * kp + k];
   }
-  if (w.type == kQ4_0) {
+  if (w.type == kQ4_0 || w.type == kQ4_K) {
     const int b = k >> 5, j = k & 31;
     uint32_t byte = w.qs[(row * w.nblk + b) * 16 + (j & 15)];
     uint32_t n = j < 16 ? (byte & 15u) : (byte >> 4);
+    if (w.type == kQ4_K) {  // scale * n - min, rounded once
+      const float2 sm = reinterpret_cast<const float2*>(w.d)[row * w.nblk + b];
+      return fmaf(sm.x, (float)n, -sm.y);
+    }
     float d = load_half(w.d + row * w.nblk + b);
     return d * (float)((int)n - 8);
+  }
+  if (w.type == kQ6_K) {
+    const float s = reinterpret_cast<const float*>(w.d)[row * 2 * w.nblk + (k >> 4)];
+    return s * (float)reinterpret_cast<const int8_t*>(w.qs)[row * kp + k];
   }
   return reinterpret_cast<const float*>(w.qs)[row * kp + k];
 }

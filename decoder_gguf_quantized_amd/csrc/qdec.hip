@@ -27,6 +27,7 @@
 #include "gemm.hpp"
 #include "gemv.hpp"
 #include "misc.hpp"
+#include "dispatch.hpp"
 
 using namespace qd;
 
@@ -60,6 +61,8 @@ struct Layer {
   float* post_ffw = nullptr;
   float* qkv_bias = nullptr;  // [nqkv] q|k|v projection bias, or null
   Mat qkv, o, gu, down;
+  bool qkv_split = false;  // q, k, v of different types: three matrices instead of qkv
+  Mat qkv_part[3];
   bool global = true;
 };
 
@@ -75,16 +78,25 @@ struct KRec {
   double bytes, flops;
 };
 
-bool is_quant(int t) { return t == kQ8_0 || t == kQ4_0; }
+bool is_quant(int t) { return t == kQ8_0 || t == kQ4_0; }  // 32-value blocks with an fp16 scale
+bool is_kquant(int t) { return t == kQ4_K || t == kQ6_K; }  // 256-value super-blocks
+bool known_type(int t) { return t == kF32 || is_quant(t) || is_kquant(t); }
 int64_t blk_bytes(int t) { return t == kQ8_0 ? 34 : 18; }
+int64_t super_bytes(int t) { return t == kQ4_K ? 144 : 210; }
 int64_t nblocks(int64_t cols) { return (cols + 31) / 32; }
 int64_t tensor_bytes(int t, int64_t rows, int64_t cols) {
-  return t == kF32 ? rows * cols * 4 : rows * nblocks(cols) * blk_bytes(t);
+  if (t == kF32) return rows * cols * 4;
+  if (is_kquant(t)) return rows * (cols / 256) * super_bytes(t);
+  return rows * nblocks(cols) * blk_bytes(t);
 }
 
-struct HipError {
-  std::string msg;
-};
+// IEEE binary16 -> float, exact (for the load-time repack of K-quant scales).
+float half_to_float_host(uint16_t h) {
+  const int e = (h >> 10) & 31, mant = h & 1023;
+  float v = e == 0 ? std::ldexp((float)mant, -24)
+                   : e == 31 ? (mant ? NAN : INFINITY) : std::ldexp((float)(1024 + mant), e - 25);
+  return (h & 0x8000) ? -v : v;
+}
 
 void hipck(hipError_t e, const char* what) {
   if (e != hipSuccess) throw HipError{std::string(what) + ": " + hipGetErrorString(e)};
@@ -161,10 +173,6 @@ hipEvent_t pool_event(qdec_model* m) {
 }
 
 // ------------------------------------------------------------ launch helpers
-template <typename... KArgs, typename... Args>
-void qlaunch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStream_t st, Args... args) {
-  hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
-}
 
 // Per-kernel timing: while timing is on, each launch is bracketed by two HIP
 // events recorded on its stream.  Events come from a pool created up front
@@ -194,78 +202,42 @@ struct Timed {
   }
 };
 
-const char* gemv_class(int type) { return type == kQ4_0 ? "gemv_q4_0" : type == kQ8_0 ? "gemv_q8_0" : "gemv_f32"; }
-const char* gemm_class(int type) { return type == kQ4_0 ? "gemm_q4_0" : type == kQ8_0 ? "gemm_q8_0" : "gemm_f32"; }
-
-template <int QT, int M, int R, int U, int NW = 4>
-void gemv_dispatch_mode(int mode, dim3 grid, size_t lds, hipStream_t st, const GemvArgs& a) {
-  const unsigned nt = 64 * NW;
-  if (a.res_add) {  // residual prologue (sandwich norms): store and pair modes
-    switch (mode) {
-      case kModeStore: qlaunch(gemv_kernel<QT, M, kModeStore, R, U, NW, true>, grid, nt, lds, st, a); break;
-      case kModePairSilu: qlaunch(gemv_kernel<QT, M, kModePairSilu, R, U, NW, true>, grid, nt, lds, st, a); break;
-      case kModePairGelu: qlaunch(gemv_kernel<QT, M, kModePairGelu, R, U, NW, true>, grid, nt, lds, st, a); break;
-      default: throw HipError{"gemv: residual prologue with an add epilogue"};
-    }
-    return;
+const char* gemv_class(int type) {
+  switch (type) {
+    case kQ4_0: return "gemv_q4_0";
+    case kQ8_0: return "gemv_q8_0";
+    case kQ4_K: return "gemv_q4_k";
+    case kQ6_K: return "gemv_q6_k";
+    default: return "gemv_f32";
   }
-  switch (mode) {
-    case kModeStore: qlaunch(gemv_kernel<QT, M, kModeStore, R, U, NW, false>, grid, nt, lds, st, a); break;
-    case kModeAdd: qlaunch(gemv_kernel<QT, M, kModeAdd, R, U, NW, false>, grid, nt, lds, st, a); break;
-    case kModePairSilu: qlaunch(gemv_kernel<QT, M, kModePairSilu, R, U, NW, false>, grid, nt, lds, st, a); break;
-    default: qlaunch(gemv_kernel<QT, M, kModePairGelu, R, U, NW, false>, grid, nt, lds, st, a); break;
+}
+const char* gemm_class(int type) {
+  switch (type) {
+    case kQ4_0: return "gemm_q4_0";
+    case kQ8_0: return "gemm_q8_0";
+    case kQ4_K: return "gemm_q4_k";
+    case kQ6_K: return "gemm_q6_k";
+    default: return "gemm_f32";
   }
 }
 
-// (R rows per wave, U units per lane per row, NW waves per workgroup):
-//   0: R = 4, U = 1 for rows of at most 64 units (one unit per lane);
-//   1: R = 2, U = 2 for rows of 65..128 units;
-//   2: R = 2, U = 4 for longer rows;
-//   3: as 2 with eight-wave workgroups, for long rows with many row groups:
-//      the input row is staged once per CU instead of twice (same LDS).
-// Largest input-row count M whose staged rows fit the 64 KB LDS budget for the
-// shortest row of each tile class (Q8_0: 16 weights per unit, Q4_0: 32, F32:
-// 4); combinations beyond it cannot be requested and are not instantiated.
-constexpr int gemv_max_m(int qt, int ru) {
-  return ru == 0 || qt == kF32 ? 16 : (qt == kQ8_0 ? (ru == 1 ? 8 : 4) : (ru == 1 ? 4 : 2));
-}
-
-template <int QT, int M, int RU, int R, int U, int NW = 4>
-void gemv_dispatch_fit(int mode, dim3 grid, size_t lds, hipStream_t st, const GemvArgs& a) {
-  if constexpr (M <= gemv_max_m(QT, RU)) gemv_dispatch_mode<QT, M, R, U, NW>(mode, grid, lds, st, a);
-  else throw HipError{"gemv: input rows exceed the LDS budget of the tile class"};
-}
-
-template <int QT, int M>
-void gemv_dispatch_ru(int ru, int mode, dim3 grid, size_t lds, hipStream_t st, const GemvArgs& a) {
-  switch (ru) {
-    case 0: gemv_dispatch_fit<QT, M, 0, 4, 1>(mode, grid, lds, st, a); break;
-    case 1: gemv_dispatch_fit<QT, M, 1, 2, 2>(mode, grid, lds, st, a); break;
-    case 3: gemv_dispatch_fit<QT, M, 3, 2, 4, 8>(mode, grid, lds, st, a); break;
-#ifdef QDEC_EXPERIMENT
-    case 4: gemv_dispatch_mode<QT, M, 4, 2>(mode, grid, lds, st, a); break;
-    case 5: gemv_dispatch_mode<QT, M, 4, 4>(mode, grid, lds, st, a); break;
-    case 6: gemv_dispatch_mode<QT, M, 2, 8>(mode, grid, lds, st, a); break;
-    case 7: gemv_dispatch_mode<QT, M, 2, 1>(mode, grid, lds, st, a); break;
-    case 8: gemv_dispatch_mode<QT, M, 1, 4, 8>(mode, grid, lds, st, a); break;
-    case 9: gemv_dispatch_mode<QT, M, 1, 8, 8>(mode, grid, lds, st, a); break;
-    case 10: gemv_dispatch_mode<QT, M, 2, 2, 8>(mode, grid, lds, st, a); break;
-#endif
-    default: gemv_dispatch_fit<QT, M, 2, 2, 4>(mode, grid, lds, st, a); break;
+void gemv_type(int type, int M, int ru, int mode, dim3 grid, size_t lds, hipStream_t st, const GemvArgs& a) {
+  switch (type) {
+    case kQ8_0: gemv_launch<kQ8_0>(M, ru, mode, grid, lds, st, a); break;
+    case kQ4_0: gemv_launch<kQ4_0>(M, ru, mode, grid, lds, st, a); break;
+    case kQ4_K: gemv_launch<kQ4_K>(M, ru, mode, grid, lds, st, a); break;
+    case kQ6_K: gemv_launch<kQ6_K>(M, ru, mode, grid, lds, st, a); break;
+    default: gemv_launch<kF32>(M, ru, mode, grid, lds, st, a); break;
   }
 }
 
-int ru_rows(int ru) { return (ru == 0 || ru == 4 || ru == 5) ? 4 : (ru == 8 || ru == 9) ? 1 : 2; }
-int ru_waves(int ru) { return (ru == 3 || ru >= 8) ? 8 : 4; }
-
-template <int QT>
-void gemv_dispatch_m(int M, int ru, int mode, dim3 grid, size_t lds, hipStream_t st, const GemvArgs& a) {
-  switch (M) {
-    case 1: gemv_dispatch_ru<QT, 1>(ru, mode, grid, lds, st, a); break;
-    case 2: gemv_dispatch_ru<QT, 2>(ru, mode, grid, lds, st, a); break;
-    case 4: gemv_dispatch_ru<QT, 4>(ru, mode, grid, lds, st, a); break;
-    case 8: gemv_dispatch_ru<QT, 8>(ru, mode, grid, lds, st, a); break;
-    default: gemv_dispatch_ru<QT, 16>(ru, mode, grid, lds, st, a); break;
+void gemm_type(int type, int kind, int mode, dim3 grid, hipStream_t st, const GemmArgs& a) {
+  switch (type) {
+    case kQ8_0: gemm_launch<kQ8_0>(kind, mode, grid, st, a); break;
+    case kQ4_0: gemm_launch<kQ4_0>(kind, mode, grid, st, a); break;
+    case kQ4_K: gemm_launch<kQ4_K>(kind, mode, grid, st, a); break;
+    case kQ6_K: gemm_launch<kQ6_K>(kind, mode, grid, st, a); break;
+    default: gemm_launch<kF32>(kind, mode, grid, st, a); break;
   }
 }
 
@@ -286,13 +258,13 @@ void gemv(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, 
           const float* bias = nullptr) {
   if (bias && mode != kModeStore) throw HipError{"gemv: a bias needs the store epilogue"};
   const int kp = w.nblk * 32;
-  const size_t per_row = (size_t)kp * 4 + (w.type == kQ4_0 ? (size_t)w.nblk * 4 : 0);
+  const size_t per_row = (size_t)kp * 4 + (nibble_layout(w.type) ? (size_t)w.nblk * 4 : 0);
   // rows per launch: a power of two (the kernel's M) whose staged inputs fit the LDS budget
   int cap = 16;
   while (cap > 1 && per_row * cap > kGemvLdsMax) cap /= 2;
   if (per_row > kGemvLdsMax) throw HipError{"gemv: input row too long for LDS"};
   const bool pair = mode == kModePairSilu || mode == kModePairGelu;
-  const int nunits = w.type == kQ8_0 ? 2 * w.nblk : (w.type == kQ4_0 ? w.nblk : kp / 4);
+  const int nunits = int8_layout(w.type) ? 2 * w.nblk : (nibble_layout(w.type) ? w.nblk : kp / 4);
   int ru = nunits <= 64 ? 0 : (nunits <= 128 ? 1 : 2);
   if (ru == 2 && (pair ? w.rows / 2 : (w.rows + 1) / 2) >= 2048) ru = 3;
   int grid_cap = 1024;
@@ -319,42 +291,14 @@ void gemv(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, 
     const size_t lds = per_row * M;
     const double bytes = w.gguf_bytes + (double)mr * kp * 4 + (double)mr * (pair ? w.rows / 2 : w.rows) * 4;
     Timed tm(m, st, gemv_class(w.type), bytes, 2.0 * mr * w.rows * (double)w.cols);
-    if (w.type == kQ8_0) gemv_dispatch_m<kQ8_0>(M, ru, mode, grid, lds, st, a);
-    else if (w.type == kQ4_0) gemv_dispatch_m<kQ4_0>(M, ru, mode, grid, lds, st, a);
-    else gemv_dispatch_m<kF32>(M, ru, mode, grid, lds, st, a);
-  }
-}
-
-template <int QT>
-void gemm_dispatch(int mode, dim3 grid, hipStream_t st, const GemmArgs& a) {
-  switch (mode) {
-    case kModeStore: qlaunch(gemm_kernel<QT, kModeStore>, grid, 256, 0, st, a); break;
-    case kModeAdd: qlaunch(gemm_kernel<QT, kModeAdd>, grid, 256, 0, st, a); break;
-    case kModePairSilu: qlaunch(gemm_kernel<QT, kModePairSilu>, grid, 256, 0, st, a); break;
-    default: qlaunch(gemm_kernel<QT, kModePairGelu>, grid, 256, 0, st, a); break;
-  }
-}
-
-template <int QT>
-void gemm_ksplit_dispatch(int mode, dim3 grid, hipStream_t st, const GemmArgs& a) {
-  if (mode == kModeAdd) qlaunch(gemm_ksplit_kernel<QT, kModeAdd>, grid, 256, 0, st, a);
-  else qlaunch(gemm_ksplit_kernel<QT, kModeStore>, grid, 256, 0, st, a);
-}
-
-template <int QT, int NT>
-void gemm_bf16_dispatch(int mode, dim3 grid, hipStream_t st, const GemmArgs& a) {
-  switch (mode) {
-    case kModeStore: qlaunch(gemm_bf16_kernel<QT, kModeStore, NT>, grid, 256, 0, st, a); break;
-    case kModeAdd: qlaunch(gemm_bf16_kernel<QT, kModeAdd, NT>, grid, 256, 0, st, a); break;
-    case kModePairSilu: qlaunch(gemm_bf16_kernel<QT, kModePairSilu, NT>, grid, 256, 0, st, a); break;
-    default: qlaunch(gemm_bf16_kernel<QT, kModePairGelu, NT>, grid, 256, 0, st, a); break;
+    gemv_type(w.type, M, ru, mode, grid, lds, st, a);
   }
 }
 
 // Prefill projection.  prec: QDEC_PREFILL_F32 (f32 operands, the default),
 // QDEC_PREFILL_BF16X3 (exact three-term bf16 split of the activations) or
 // QDEC_PREFILL_BF16 (activations rounded to bf16); -1 = the model's setting.
-// F32 weights always take the f32 kernels.
+// F32 and K-quant weights always take the f32 kernels.
 void gemm(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, int T, float* y, int ldy, int mode,
           int prec = -1) {
   GemmArgs a{w.qs, w.d, w.rows, w.nblk, x, ldx, T, y, ldy};
@@ -370,13 +314,7 @@ void gemm(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, 
     Timed tm(m, st, nt == 3 ? (w.type == kQ8_0 ? "gemm_bf16x3_q8_0" : "gemm_bf16x3_q4_0")
                             : (w.type == kQ8_0 ? "gemm_bf16_q8_0" : "gemm_bf16_q4_0"),
              bytes, 2.0 * T * (double)w.rows * w.cols);
-    if (w.type == kQ8_0) {
-      if (nt == 3) gemm_bf16_dispatch<kQ8_0, 3>(mode, grid, st, a);
-      else gemm_bf16_dispatch<kQ8_0, 1>(mode, grid, st, a);
-    } else {
-      if (nt == 3) gemm_bf16_dispatch<kQ4_0, 3>(mode, grid, st, a);
-      else gemm_bf16_dispatch<kQ4_0, 1>(mode, grid, st, a);
-    }
+    gemm_type(w.type, nt == 3 ? kGemmBf16x3 : kGemmBf16, mode, grid, st, a);
     return;
   }
   // few 64 x 128 tiles for the CUs: switch to the K-split 32 x 64 tile
@@ -384,16 +322,12 @@ void gemm(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, 
     dim3 g2((w.rows + 63) / 64, (T + 31) / 32);
     const double bytes = w.gguf_bytes + (double)T * w.nblk * 32 * 4 + (double)T * w.rows * 4;
     Timed tm(m, st, gemm_class(w.type), bytes, 2.0 * T * (double)w.rows * w.cols);
-    if (w.type == kQ8_0) gemm_ksplit_dispatch<kQ8_0>(mode, g2, st, a);
-    else if (w.type == kQ4_0) gemm_ksplit_dispatch<kQ4_0>(mode, g2, st, a);
-    else gemm_ksplit_dispatch<kF32>(mode, g2, st, a);
+    gemm_type(w.type, kGemmKSplit, mode, g2, st, a);
     return;
   }
   const double bytes = w.gguf_bytes + (double)T * w.nblk * 32 * 4 + (double)T * (pair ? w.rows / 2 : w.rows) * 4;
   Timed tm(m, st, gemm_class(w.type), bytes, 2.0 * T * (double)w.rows * w.cols);
-  if (w.type == kQ8_0) gemm_dispatch<kQ8_0>(mode, grid, st, a);
-  else if (w.type == kQ4_0) gemm_dispatch<kQ4_0>(mode, grid, st, a);
-  else gemm_dispatch<kF32>(mode, grid, st, a);
+  gemm_type(w.type, kGemmWide, mode, grid, st, a);
 }
 
 void rmsnorm_rows(qdec_model* m, hipStream_t st, const float* x, int ldx, const float* w, int n, float* out, int ldo,
@@ -502,6 +436,22 @@ void sample(qdec_model* m, hipStream_t st, const float* logits, int ld, int rows
   qlaunch(sample_stage2_kernel, rows, 64, 0, st, a);
 }
 
+// q|k|v projection of decode rows into m->qkv (RMSNorm prologue, optional
+// residual prologue, bias epilogue): one launch over the fused rows, or three
+// when q, k and v have different types.  With a residual prologue each of the
+// three launches writes the same new residual row.
+void qkv_gemv(qdec_model* m, hipStream_t st, const Layer& L, const float* x, int n, Resid res) {
+  const qdec_config& c = m->cfg;
+  if (!L.qkv_split) {
+    gemv(m, st, L.qkv, x, c.hidden, L.attn_norm, c.rms_eps, m->qkv, m->nqkv, n, kModeStore, nullptr, res, L.qkv_bias);
+    return;
+  }
+  const int off[3] = {0, m->qd, m->qd + m->kd};
+  for (int j = 0; j < 3; ++j)
+    gemv(m, st, L.qkv_part[j], x, c.hidden, L.attn_norm, c.rms_eps, m->qkv + off[j], m->nqkv, n, kModeStore, nullptr,
+         res, L.qkv_bias ? L.qkv_bias + off[j] : nullptr);
+}
+
 // The blocks over n tokens of one sequence (prefill) or one token of each of n
 // sequences (decode, dpos != null); the residual stream is m->x.
 void blocks(qdec_model* m, hipStream_t st, int n, int seq, int pos0, const int* dpos) {
@@ -518,14 +468,17 @@ void blocks(qdec_model* m, hipStream_t st, int n, int seq, int pos0, const int* 
     const Layer& L = m->layers[l];
     // attention sublayer
     if (fuse && l > 0) {
-      gemv(m, st, L.qkv, m->x2, H, L.attn_norm, c.rms_eps, m->qkv, m->nqkv, n, kModeStore, nullptr,
-           Resid{m->y, m->layers[l - 1].post_ffw, m->x}, L.qkv_bias);
+      qkv_gemv(m, st, L, m->x2, n, Resid{m->y, m->layers[l - 1].post_ffw, m->x});
     } else if (dec) {
-      gemv(m, st, L.qkv, m->x, H, L.attn_norm, c.rms_eps, m->qkv, m->nqkv, n, kModeStore, nullptr, Resid{},
-           L.qkv_bias);
+      qkv_gemv(m, st, L, m->x, n, Resid{});
     } else {
       rmsnorm_rows(m, st, m->x, H, L.attn_norm, H, m->h, H, n, 0);
-      gemm(m, st, L.qkv, m->h, H, n, m->qkv, m->nqkv, kModeStore);
+      if (!L.qkv_split) {
+        gemm(m, st, L.qkv, m->h, H, n, m->qkv, m->nqkv, kModeStore);
+      } else {
+        const int off[3] = {0, m->qd, m->qd + m->kd};
+        for (int j = 0; j < 3; ++j) gemm(m, st, L.qkv_part[j], m->h, H, n, m->qkv + off[j], m->nqkv, kModeStore);
+      }
     }
     if (dec) {
       attention_decode(m, st, l, n);  // QK-norm, RoPE and the KV append run inside
@@ -662,30 +615,97 @@ std::vector<Expect> expected_tensors(const qdec_config& c) {
 }
 
 bool scales_finite(const qdec_tensor& t) {
-  if (!is_quant(t.type)) return true;
+  auto finite = [](const uint8_t* p) { return ((p[1] >> 2) & 0x1f) != 0x1f; };
   const uint8_t* b = static_cast<const uint8_t*>(t.host_data);
-  const int64_t nb = t.rows * nblocks(t.cols), bb = blk_bytes(t.type);
-  for (int64_t i = 0; i < nb; ++i) {
-    uint16_t h = (uint16_t)b[i * bb] | ((uint16_t)b[i * bb + 1] << 8);
-    if (((h >> 10) & 0x1f) == 0x1f) return false;
+  if (is_kquant(t.type)) {
+    const int64_t nb = t.rows * (t.cols / 256), bb = super_bytes(t.type);
+    for (int64_t i = 0; i < nb; ++i) {
+      const uint8_t* sb = b + i * bb;
+      if (t.type == kQ4_K ? !(finite(sb) && finite(sb + 2)) : !finite(sb + 208)) return false;
+    }
+    return true;
   }
+  if (!is_quant(t.type)) return true;
+  const int64_t nb = t.rows * nblocks(t.cols), bb = blk_bytes(t.type);
+  for (int64_t i = 0; i < nb; ++i)
+    if (!finite(b + i * bb)) return false;
   return true;
 }
 
 // Repack GGUF rows [src_rows][blocks] into (quants, scales) at device row dst_row
 // of a host staging buffer of the fused matrix.
+// K-quant super-blocks are repacked into the 32-value layouts of the legacy
+// types with exact f32 scales (GGUF's public K-quant layouts):
+//   Q4_K (fp16 d, fp16 dmin, 12 bytes of eight 6-bit (scale, min) pairs, 128
+//   quant bytes whose low / high nibbles hold sub-blocks 2c / 2c + 1) -> per
+//   sub-block the Q4_0 nibble order and a float2 (d * sc, dmin * m);
+//   Q6_K (128 low-nibble bytes, 64 bytes of 2-bit high parts, 16 int8 scales,
+//   fp16 d) -> int8 q - 32 per value and an f32 d * scale per 16 values.
+// Both scale products are exact in f32 (at most 11 + 8 significant bits).
 struct Stage {
   int type;
   int64_t rows, nblk;
   std::vector<uint8_t> qs;
   std::vector<uint16_t> d;
+  std::vector<float> f;  // K-quants: two floats per 32-value block
   Stage(int t, int64_t r, int64_t nb) : type(t), rows(r), nblk(nb) {
-    qs.assign((size_t)(t == kQ4_0 ? r * nb * 16 : t == kQ8_0 ? r * nb * 32 : r * nb * 32 * 4), 0);
+    const bool nib = t == kQ4_0 || t == kQ4_K, i8 = t == kQ8_0 || t == kQ6_K;
+    qs.assign((size_t)(nib ? r * nb * 16 : i8 ? r * nb * 32 : r * nb * 32 * 4), 0);
     if (is_quant(t)) d.assign((size_t)(r * nb), 0);
+    if (is_kquant(t)) f.assign((size_t)(2 * r * nb), 0.f);
+  }
+  void put_q4_k(int64_t dst_row, const uint8_t* src, int64_t nsb) {
+    for (int64_t sbi = 0; sbi < nsb; ++sbi) {
+      const uint8_t* sb = src + sbi * 144;
+      const float dd = half_to_float_host((uint16_t)(sb[0] | sb[1] << 8));
+      const float dm = half_to_float_host((uint16_t)(sb[2] | sb[3] << 8));
+      const uint8_t* sc = sb + 4;
+      const uint8_t* q = sb + 16;
+      for (int j = 0; j < 8; ++j) {
+        const int scale = j < 4 ? sc[j] & 63 : (sc[j + 4] & 15) | ((sc[j - 4] >> 6) << 4);
+        const int mn = j < 4 ? sc[j + 4] & 63 : (sc[j + 4] >> 4) | ((sc[j] >> 6) << 4);
+        const int64_t b = dst_row * nblk + sbi * 8 + j;
+        f[(size_t)(2 * b)] = dd * (float)scale;
+        f[(size_t)(2 * b + 1)] = dm * (float)mn;
+        const uint8_t* qc = q + 32 * (j / 2);
+        const int sh = 4 * (j & 1);
+        for (int i = 0; i < 16; ++i) {
+          const uint8_t lo = (qc[i] >> sh) & 15, hi = (qc[i + 16] >> sh) & 15;
+          qs[(size_t)(b * 16 + i)] = (uint8_t)(lo | hi << 4);
+        }
+      }
+    }
+  }
+  void put_q6_k(int64_t dst_row, const uint8_t* src, int64_t nsb) {
+    int8_t* out = reinterpret_cast<int8_t*>(qs.data()) + dst_row * nblk * 32;
+    for (int64_t sbi = 0; sbi < nsb; ++sbi) {
+      const uint8_t* sb = src + sbi * 210;
+      const float dd = half_to_float_host((uint16_t)(sb[208] | sb[209] << 8));
+      for (int h = 0; h < 2; ++h) {
+        const uint8_t* ql = sb + 64 * h;
+        const uint8_t* qh = sb + 128 + 32 * h;
+        int8_t* o = out + sbi * 256 + 128 * h;
+        for (int l = 0; l < 32; ++l) {
+          o[l] = (int8_t)(((ql[l] & 15) | ((qh[l] & 3) << 4)) - 32);
+          o[l + 32] = (int8_t)(((ql[l + 32] & 15) | (((qh[l] >> 2) & 3) << 4)) - 32);
+          o[l + 64] = (int8_t)(((ql[l] >> 4) | (((qh[l] >> 4) & 3) << 4)) - 32);
+          o[l + 96] = (int8_t)(((ql[l + 32] >> 4) | ((qh[l] >> 6) << 4)) - 32);
+        }
+      }
+      for (int g = 0; g < 16; ++g)
+        f[(size_t)(dst_row * 2 * nblk + sbi * 16 + g)] = dd * (float)(int8_t)sb[192 + g];
+    }
   }
   void put_row(int64_t dst_row, const qdec_tensor& t, int64_t src_row) {
     const uint8_t* src = static_cast<const uint8_t*>(t.host_data);
     const int64_t nb = nblocks(t.cols);
+    if (is_kquant(type)) {
+      const int64_t nsb = t.cols / 256;
+      const uint8_t* row = src + src_row * nsb * super_bytes(type);
+      if (type == kQ4_K) put_q4_k(dst_row, row, nsb);
+      else put_q6_k(dst_row, row, nsb);
+      return;
+    }
     if (type == kF32) {
       std::memcpy(&qs[(size_t)dst_row * nblk * 32 * 4], src + src_row * t.cols * 4, (size_t)t.cols * 4);
       return;
@@ -711,6 +731,11 @@ Mat upload(qdec_model* m, const Stage& s, int rows, int cols, double gguf_bytes,
   if (is_quant(s.type)) {
     w.d = m->dalloc<uint16_t>(s.d.size());
     hipck(hipMemcpyAsync(w.d, s.d.data(), s.d.size() * 2, hipMemcpyHostToDevice, st), "upload");
+  }
+  if (is_kquant(s.type)) {  // f32 scales, passed to the kernels through the same pointer
+    float* f = m->dalloc<float>(s.f.size());
+    hipck(hipMemcpyAsync(f, s.f.data(), s.f.size() * 4, hipMemcpyHostToDevice, st), "upload");
+    w.d = reinterpret_cast<uint16_t*>(f);
   }
   hipck(hipStreamSynchronize(st), "upload sync");
   return w;
@@ -784,8 +809,12 @@ int load(const qdec_config* cfgp, const qdec_tensor* ts, int32_t n, int32_t max_
     if (it == byname.end()) { set_err("tensor '%s': not a tensor of this configuration", t.name); return QDEC_REFUSED; }
     if (got.count(t.name)) { set_err("tensor '%s': given twice", t.name); return QDEC_REFUSED; }
     const Expect& e = *it->second;
-    if (t.type != kF32 && t.type != kQ8_0 && t.type != kQ4_0) {
-      set_err("tensor '%s': type %d unsupported (F32 = 0, Q4_0 = 2, Q8_0 = 8)", t.name, t.type);
+    if (!known_type(t.type)) {
+      set_err("tensor '%s': type %d unsupported (F32 = 0, Q4_0 = 2, Q8_0 = 8, Q4_K = 12, Q6_K = 14)", t.name, t.type);
+      return QDEC_REFUSED;
+    }
+    if (is_kquant(t.type) && t.cols % 256) {
+      set_err("tensor '%s': K-quant rows need a multiple of 256 values, got %lld", t.name, (long long)t.cols);
       return QDEC_REFUSED;
     }
     if (!e.matrix && t.type != kF32) { set_err("tensor '%s': norm gains and biases must be F32", t.name); return QDEC_REFUSED; }
@@ -807,11 +836,6 @@ int load(const qdec_config* cfgp, const qdec_tensor* ts, int32_t n, int32_t max_
     if (e.required && !got.count(e.name)) { set_err("tensor '%s' is missing", e.name.c_str()); return QDEC_REFUSED; }
   for (int i = 0; i < c.n_layer; ++i) {
     std::string p = "blk." + std::to_string(i) + ".";
-    int tq = got[p + "attn_q.weight"]->type;
-    if (got[p + "attn_k.weight"]->type != tq || got[p + "attn_v.weight"]->type != tq) {
-      set_err("layer %d: attn_q, attn_k and attn_v must share one type", i);
-      return QDEC_REFUSED;
-    }
     if (got[p + "ffn_gate.weight"]->type != got[p + "ffn_up.weight"]->type) {
       set_err("layer %d: ffn_gate and ffn_up must share one type", i);
       return QDEC_REFUSED;
@@ -871,8 +895,18 @@ int load(const qdec_config* cfgp, const qdec_tensor* ts, int32_t n, int32_t max_
         L.post_attn = upload_vec(m, TN(p + "post_attention_norm.weight"), st);
         L.post_ffw = upload_vec(m, TN(p + "post_ffw_norm.weight"), st);
       }
-      {  // fused q|k|v rows
-        const qdec_tensor &tq = TN(p + "attn_q.weight"), &tk = TN(p + "attn_k.weight"), &tv = TN(p + "attn_v.weight");
+      const qdec_tensor &tq = TN(p + "attn_q.weight"), &tk = TN(p + "attn_k.weight"), &tv = TN(p + "attn_v.weight");
+      L.qkv_split = tk.type != tq.type || tv.type != tq.type;
+      if (L.qkv_split) {  // mixed types (K-quant files): one matrix each
+        const qdec_tensor* part[3] = {&tq, &tk, &tv};
+        for (int j = 0; j < 3; ++j) {
+          const qdec_tensor& tj = *part[j];
+          Stage s(tj.type, tj.rows, nblocks(H));
+          for (int64_t r = 0; r < tj.rows; ++r) s.put_row(r, tj, r);
+          L.qkv_part[j] = upload(m, s, (int)tj.rows, H, (double)tj.n_bytes, st);
+          m->names[tj.name] = NameRef{&L.qkv_part[j], 0, (int)tj.rows, H, 0, nullptr};
+        }
+      } else {  // fused q|k|v rows
         Stage s(tq.type, m->nqkv, nblocks(H));
         for (int64_t r = 0; r < tq.rows; ++r) s.put_row(r, tq, r);
         for (int64_t r = 0; r < tk.rows; ++r) s.put_row(m->qd + r, tk, r);
@@ -1292,7 +1326,8 @@ int qdec_debug_matmul(int32_t type, int64_t rows, int64_t cols, const void* host
     set_err("unknown prefill precision %d", precision);
     return QDEC_REFUSED;
   }
-  if (type != kF32 && type != kQ8_0 && type != kQ4_0) { set_err("type %d unsupported", type); return QDEC_REFUSED; }
+  if (!known_type(type)) { set_err("type %d unsupported", type); return QDEC_REFUSED; }
+  if (is_kquant(type) && cols % 256) { set_err("K-quant rows need a multiple of 256 values"); return QDEC_REFUSED; }
   if (rows <= 0 || cols <= 0 || rows > (1 << 24) || cols > (1 << 20) || !host_data || !d_x || !d_y || n_x <= 0) {
     set_err("bad arguments");
     return QDEC_REFUSED;

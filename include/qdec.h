@@ -51,8 +51,15 @@ enum { QDEC_OK = 0, QDEC_REFUSED = 1, QDEC_INTERNAL = 2 };
  * Q8_0: 34-byte blocks = fp16 scale d + 32 int8 q, w = d*q.
  * Q4_0: 18-byte blocks = fp16 scale d + 16 bytes; byte j holds element j in its
  *       low nibble and element j+16 in its high nibble, w = d*(n-8).
- * Blocks run along a row's input dimension; a row holds ceil(cols/32) blocks. */
-enum { QDEC_T_F32 = 0, QDEC_T_Q4_0 = 2, QDEC_T_Q8_0 = 8 };
+ * Blocks run along a row's input dimension; a row holds ceil(cols/32) blocks.
+ * Q4_K, Q6_K (the K-quants of GGUF files such as Q4_K_M): 256-value
+ *       super-blocks of 144 / 210 bytes in GGUF's layout; rows hold cols/256 of
+ *       them (cols a multiple of 256).  Q4_K: fp16 d, fp16 dmin, eight 6-bit
+ *       (scale, min) pairs, w = d*sc*q - dmin*m; Q6_K: 6-bit q, sixteen int8
+ *       scales, fp16 d, w = d*scale*(q - 32).  They are repacked at load into
+ *       32-value blocks with exact f32 scales (more bytes than the file: 0.75
+ *       and 1.25 per weight instead of 0.5625 and 0.8203) and stream as such. */
+enum { QDEC_T_F32 = 0, QDEC_T_Q4_0 = 2, QDEC_T_Q8_0 = 8, QDEC_T_Q4_K = 12, QDEC_T_Q6_K = 14 };
 
 enum { QDEC_ACT_SILU = 0, QDEC_ACT_GELU_TANH = 1 };
 
@@ -102,7 +109,7 @@ typedef struct {
   int32_t type;
   int64_t rows, cols;
   const void* host_data;
-  int64_t n_bytes; /* rows*ceil(cols/32)*{34|18}, or rows*cols*4 for F32 */
+  int64_t n_bytes; /* rows*ceil(cols/32)*{34|18}, rows*(cols/256)*{144|210}, or rows*cols*4 (F32) */
 } qdec_tensor;
 
 int32_t qdec_abi_version(void);

@@ -13,7 +13,7 @@ BASE = dict(rms_eps=1e-6, rope_theta=1e4, rope_theta_local=1e4, window=0, window
 # Small models, one per kernel variant: head_dim 64/128/256, query heads per KV
 # head 1/2/4/8, Q8_0/Q4_0/F32, tied/untied head, QK-norm, sliding window,
 # sandwich norms, gelu_tanh, FFN widths that are not multiples of 32 or 64,
-# q/k/v biases.
+# q/k/v biases, K-quants (mixed per matrix).
 SMALL = {
     "qwen3_hd128_g2": dict(BASE, name="qwen3_hd128_g2", n_layer=2, hidden=256, n_head=4, n_head_kv=2, head_dim=128,
                            ffn=512, vocab=5000, qk_norm=True, rope_theta=1e6, rope_theta_local=1e6, seed=11),
@@ -30,6 +30,15 @@ SMALL = {
     "qwen2_bias_hd64_g2": dict(BASE, name="qwen2_bias_hd64_g2", n_layer=2, hidden=384, n_head=6, n_head_kv=3,
                                head_dim=64, ffn=1024, vocab=3000, qkv_bias=True, embd_type="f32", tied=False,
                                rope_theta=1e6, rope_theta_local=1e6, seed=16),
+    # a Q4_K_M-like mix: Q4_K matrices, Q6_K for attn_v, ffn_down and the
+    # head (so q, k and v have different types and run as three launches)
+    "q4km_mixed_hd64_g4": dict(BASE, name="q4km_mixed_hd64_g4", n_layer=2, hidden=512, n_head=8, n_head_kv=2,
+                               head_dim=64, ffn=1024, vocab=3000, wtype="q4_k", embd_type="q4_k", tied=False,
+                               types={"attn_v": "q6_k", "ffn_down": "q6_k", "output": "q6_k"}, rope_theta=5e5,
+                               rope_theta_local=5e5, seed=17),
+    "q6k_tied_hd128": dict(BASE, name="q6k_tied_hd128", n_layer=2, hidden=256, n_head=2, n_head_kv=1,
+                           head_dim=128, ffn=512, vocab=2048, wtype="q6_k", embd_type="q6_k", qk_norm=True,
+                           rope_theta=1e6, rope_theta_local=1e6, seed=18),
 }
 
 

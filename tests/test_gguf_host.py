@@ -184,6 +184,25 @@ def test_corrupt_files_are_refused(tmp_path, patch, msg):
         qdec.gguf_config(str(p))
 
 
+def test_k_quant_rows_must_hold_whole_super_blocks(tmp_path):
+    """A Q4_K tensor whose rows are not a multiple of 256 values cannot be laid
+    out; the writer refuses it, and a patched file is refused by the reader."""
+    from tests.gpu_helpers import SMALL
+    cfg = dict(SMALL["q4km_mixed_hd64_g4"])
+    t = synth.generate(cfg)
+    p = sg.write(str(tmp_path / "k.gguf"), cfg, t)
+    b = open(p, "rb").read()
+    # token_embd.weight's ne[0] = 512 -> 500: the reader's row-length check
+    key = b"token_embd.weight"
+    at = b.index(key) + len(key) + 4
+    assert struct.unpack("<Q", b[at:at + 8])[0] == 512
+    bad = tmp_path / "bad.gguf"
+    bad.write_bytes(b[:at] + struct.pack("<Q", 500) + b[at + 8:])
+    with pytest.raises(qdec.QdecError, match="256"):
+        qdec.gguf_config(str(bad))
+    assert qdec.gguf_config(p)["hidden"] == 512
+
+
 def test_missing_file_and_null_arguments(tmp_path):
     with pytest.raises(qdec.QdecError, match="cannot open"):
         qdec.gguf_config(str(tmp_path / "none.gguf"))

@@ -66,6 +66,7 @@ CASES = {
     "gemma3_pattern3": (cfg_for("gemma_hd256_g4"),
                         sg.archdef_text("gemma3").replace("window_pattern 6", "window_pattern 3")),
     "gemma3_builtin_7l": (cfg_for("gemma_hd256_g4", n_layer=7, window_period=6, name="gemma_7l"), None),
+    "llama_q4_k_m": (cfg_for("q4km_mixed_hd64_g4"), None),
 }
 
 

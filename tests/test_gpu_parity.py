@@ -207,6 +207,12 @@ MATMUL_CASES = [
     # long rows with >= 2048 row groups: eight-wave workgroups (ragged rows)
     (synth.T_Q4_0, 4100, 8192, 1), (synth.T_Q4_0, 4097, 4608, 2), (synth.T_Q8_0, 4100, 2080, 3),
     (synth.T_F32, 4100, 600, 5),
+    # K-quants (repacked to 32-value blocks with f32 scales): every GEMV tile
+    # class, the eight-wave class, a split into two 8-row launches, both GEMM tiles
+    (synth.T_Q4_K, 4096, 1024, 1), (synth.T_Q4_K, 1000, 2816, 3), (synth.T_Q4_K, 4100, 4608, 2),
+    (synth.T_Q4_K, 300, 512, 17), (synth.T_Q4_K, 4224, 256, 1000),
+    (synth.T_Q6_K, 4096, 1024, 1), (synth.T_Q6_K, 257, 1536, 16), (synth.T_Q6_K, 130, 14336, 2),
+    (synth.T_Q6_K, 4100, 2048, 3), (synth.T_Q6_K, 1030, 1024, 97), (synth.T_Q6_K, 4100, 512, 1030),
 ]
 
 
@@ -227,7 +233,7 @@ def test_projection_matches_oracle(ttype, rows, cols, n_x):
         check_row(got[r], want[r])
 
 
-GEMM_CASES = [c for c in MATMUL_CASES if c[3] > 16 and c[0] != synth.T_F32]
+GEMM_CASES = [c for c in MATMUL_CASES if c[3] > 16 and c[0] in (synth.T_Q8_0, synth.T_Q4_0)]
 
 
 @pytest.mark.parametrize("ttype,rows,cols,n_x", GEMM_CASES)
