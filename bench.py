@@ -27,6 +27,10 @@ HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
 FP32_MFMA_PEAK = 157.3e12  # FLOP/s, MI355X dense FP32 matrix
 BF16_MFMA_PEAK = 2.5e15    # FLOP/s, MI355X dense BF16 matrix
 PREFILL_TERMS = {"f32": 0, "bf16x3": 3, "bf16": 1}
+# mixed-type weight sets, as GGUF files ship them (the type of each matrix)
+WEIGHT_MIXES = {
+    "q4_k_m": dict(wtype="q4_k", embd_type="q4_k", types={"attn_v": "q6_k", "ffn_down": "q6_k", "output": "q6_k"}),
+}
 
 
 def step_bytes_decode(cfg, pos):
@@ -244,6 +248,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="c2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--weights", default=None, choices=sorted(WEIGHT_MIXES),
+                    help="re-type the workload's matrices, e.g. q4_k_m: Q4_K with Q6_K attn_v, ffn_down and head")
     ap.add_argument("--decode-steps", type=int, default=None, help="override the workload's decode steps (profiling runs)")
     ap.add_argument("--prefill-precision", default="f32", choices=sorted(PREFILL_TERMS),
                     help="operand precision of the prefill projections (default f32)")
@@ -267,6 +273,9 @@ def main():
 
     cfg = synth.get(args.config)
     cfg["key"] = args.config
+    if args.weights:
+        cfg.update(WEIGHT_MIXES[args.weights])
+        cfg["key"] = f"{args.config}-{args.weights}"
     if args.copy_calibration:
         a = torch.empty(64 << 20, dtype=torch.float32, device="cuda:0")
         b = torch.empty_like(a)
@@ -348,8 +357,9 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"{cfg['name']}, {cfg['wtype'].upper()} weights, prompt {T}, decode {N} greedy, batch 1",
-                   "prompt": T, "decode_steps": N, "batch": 1, "weights": cfg["wtype"]},
+        "config": {"workload": f"{cfg['name']}, {(args.weights or cfg['wtype']).upper()} weights, prompt {T}, "
+                               f"decode {N} greedy, batch 1",
+                   "prompt": T, "decode_steps": N, "batch": 1, "weights": args.weights or cfg["wtype"]},
         "prefill_tokens_per_s": round(pre_tok_s, 1),
         "prefill_mfma_util": round(float(mfma_util), 4),
         "prefill_precision": args.prefill_precision,
