@@ -96,6 +96,9 @@ def lib():
                 "qdec_gguf_config": (ctypes.c_int, [ctypes.c_char_p, ctypes.c_char_p, ctypes.POINTER(_Config)]),
                 "qdec_load_gguf": (ctypes.c_int, [ctypes.c_char_p, ctypes.c_char_p, I32, I32, P, ctypes.POINTER(P)]),
                 "qdec_archdef_builtin": (ctypes.c_char_p, [ctypes.c_char_p]),
+                "qdec_decode_batch": (ctypes.c_int, [P, P, P, I32, P, P, F, F, U64, U64, U32, P]),
+                "qdec_kv_paged": (ctypes.c_int, [P, I32, I32, P]),
+                "qdec_kv_pages": (ctypes.c_int, [P, ctypes.POINTER(I32), ctypes.POINTER(I32), ctypes.POINTER(I32)]),
             }
             for name, (res, args) in sig.items():
                 fn = getattr(L, name)
@@ -339,6 +342,16 @@ class Model:
         """One token for each of sequences 0..B-1.  ``tokens``: host ids, or an
         int32 GPU tensor (e.g. the previous ``token_out``).  ``top_p`` < 1 with
         ``temperature`` > 0 samples from the nucleus."""
+        self._decode(None, tokens, logits, token_out, temperature, seed, step, top_p)
+
+    def decode_batch(self, seqs, tokens, logits, token_out, temperature=0.0, seed=0, step=0, top_p=1.0):
+        """One token for each sequence slot in ``seqs`` (distinct host ints): row
+        r of ``tokens`` / ``logits`` / ``token_out`` serves sequence seqs[r]."""
+        import numpy as np
+        sq = np.ascontiguousarray(np.asarray([_int("seq", int(x)) for x in seqs], dtype=np.int32))
+        self._decode(sq, tokens, logits, token_out, temperature, seed, step, top_p)
+
+    def _decode(self, seqs, tokens, logits, token_out, temperature, seed, step, top_p):
         import numpy as np
         import torch
         h = self._handle()
@@ -357,9 +370,27 @@ class Model:
             flags = 0
         lp = _dev_ptr("logits", logits, torch.float32, n * self.vocab)
         op = _dev_ptr("token_out", token_out, torch.int32, n)
-        rc = lib().qdec_decode_step(h, tp_in, _int("n_seqs", n), lp, op, float(temperature), float(top_p),
-                                    _int("seed", seed, _U64), _int("step", step, _U64), flags, _stream())
+        args = (lp, op, float(temperature), float(top_p), _int("seed", seed, _U64), _int("step", step, _U64), flags,
+                _stream())
+        if seqs is None:
+            rc = lib().qdec_decode_step(h, tp_in, _int("n_seqs", n), *args)
+        else:
+            if seqs.size != n:
+                raise QdecError(f"{seqs.size} sequence slots for {n} tokens")
+            rc = lib().qdec_decode_batch(h, seqs.ctypes.data, tp_in, _int("n", n), *args)
         self._check(rc)
+
+    def kv_paged(self, page_size, n_pages):
+        """Switch to a paged KV cache: a pool of ``n_pages`` pages of
+        ``page_size`` positions shared by all sequences (every sequence empty)."""
+        self._check(lib().qdec_kv_paged(self._handle(), _int("page_size", page_size), _int("n_pages", n_pages),
+                                        _stream()))
+
+    def kv_pages(self):
+        """(page_size, n_pages, n_free); page_size 0 = contiguous cache."""
+        a, b, c = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        self._check(lib().qdec_kv_pages(self._handle(), ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+        return a.value, b.value, c.value
 
     def set_prefill_precision(self, precision):
         """Operand precision of later prefill projections: "f32" (default),

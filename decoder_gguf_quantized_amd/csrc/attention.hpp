@@ -42,6 +42,8 @@ struct AttnDecodeArgs {
   float* part_ml;       // [B][nq][nchunk][2]: running max (log2 domain), sum
   int* counter;         // [B][nkv] finished-chunk counters, zero between launches
   float* out;           // [B][nq*hd] merged attention output
+  const int* seq;       // [B] sequence slot of each row, or null (row b is sequence b)
+  KvMap map;            // cache layout (the paged kernel reads map.table)
 };
 
 // Device-coherent (write-through / L2-bypassing) accesses for the cross-
@@ -123,7 +125,9 @@ QD_DEV void store_lane8(float* rowp, int hd, int li, const float (&v)[8]) {
 // values (a chunk's addresses do not depend on the position; keys past it are
 // masked).  The key loop keeps two position pairs per stream in flight, and the
 // merge requests every chunk's (m, l) together with the outputs' values.
-template <int HD, int G>
+// PAGED: the cache is paged; a chunk lies in one page (the host keeps chunks
+// no longer than a page), so one table entry per workgroup places all of it.
+template <int HD, int G, bool PAGED>
 __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
   constexpr int LG = HD / 8;      // lanes per position
   constexpr int NG = 256 / LG;    // position streams per workgroup
@@ -137,8 +141,17 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
   const int c = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x, gi = tid / LG, li = tid % LG;
   const float* row = a.qkv + (size_t)s * a.ldqkv;
-  const size_t head_base = ((size_t)s * a.nkv + g) * a.ctx;
+  const int sq = a.seq ? a.seq[s] : s;
   const int cb = c * a.chunk;
+  // cache row of position j is head_base + j for every j of this chunk
+  size_t head_base;
+  if constexpr (PAGED) {
+    const int pi = cb >> a.map.log2p;
+    const int pg = a.map.table[sq * a.map.tw + pi];
+    head_base = (((size_t)pg * a.nkv + g) << a.map.log2p) - ((size_t)pi << a.map.log2p);
+  } else {
+    head_base = ((size_t)sq * a.nkv + g) * a.ctx;
+  }
   const bool spec = a.window == 0;
 
   const int p = a.pos[s];
@@ -384,11 +397,13 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
 
 struct AttnPrefillArgs {
   const float* q;       // [T][nq*hd]
-  const float* kc;      // cache of this (layer, sequence): [nkv][ctx][hd]
+  const float* kc;      // cache of this layer (rows placed by map)
   const float* vc;
   int ctx, T, pos0, nq, nkv, window;
   float scale_log2;
   float* out;           // [T][nq*hd]
+  int seq;
+  KvMap map;
 };
 
 // Workgroup = (tile of 256/LG consecutive queries, one query head).  K/V tiles
@@ -419,18 +434,21 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = 0.f;
-  const float4* kbase = reinterpret_cast<const float4*>(a.kc + (size_t)g * a.ctx * HD);
-  const float4* vbase = reinterpret_cast<const float4*>(a.vc + (size_t)g * a.ctx * HD);
+  const float4* kc4 = reinterpret_cast<const float4*>(a.kc);
+  const float4* vc4 = reinterpret_cast<const float4*>(a.vc);
   const int jlo = active ? (a.window > 0 ? max(0, p - a.window + 1) : 0) : 1;
   const int jhi = active ? p : 0;
 
   for (int j0 = kmin; j0 <= kmax; j0 += KT) {
     const int nk = min(KT, kmax - j0 + 1);
     __syncthreads();
+    // rows placed one by one: a window layer's tiles start anywhere, so a tile
+    // may straddle two pages
     for (int i = tid; i < nk * (HD / 4); i += 256) {
       int kk = i / (HD / 4), dv = i % (HD / 4);
-      Ks[kk][dv] = kbase[(size_t)(j0 + kk) * (HD / 4) + dv];
-      Vs[kk][dv] = vbase[(size_t)(j0 + kk) * (HD / 4) + dv];
+      const size_t r = kv_row(a.map, a.nkv, a.ctx, a.seq, g, j0 + kk);
+      Ks[kk][dv] = kc4[r * (HD / 4) + dv];
+      Vs[kk][dv] = vc4[r * (HD / 4) + dv];
     }
     __syncthreads();
     const int a0 = max(jlo, j0), a1 = min(jhi, j0 + nk - 1);

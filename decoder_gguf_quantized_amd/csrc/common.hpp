@@ -21,6 +21,22 @@ constexpr int kQ8_0 = 8;
 constexpr int kQ4_K = 12;
 constexpr int kQ6_K = 14;
 
+// Where a layer's K/V row lives.  Contiguous (table null): [seq][nkv][ctx]
+// rows.  Paged: [page][nkv][P] rows, P = 2^log2p positions per page, and
+// sequence s's position j in page table[s * tw + j / P] (pages are handed out
+// by the host; entries past a sequence's length hold any valid page).
+struct KvMap {
+  const int* table;
+  int tw, log2p;
+};
+
+// Row index (in head_dim units) of position j of KV head g of sequence s.
+QD_DEV size_t kv_row(const KvMap& mp, int nkv, int ctx, int s, int g, int j) {
+  if (!mp.table) return ((size_t)s * nkv + g) * ctx + j;
+  const int pg = mp.table[s * mp.tw + (j >> mp.log2p)];
+  return (((size_t)pg * nkv + g) << mp.log2p) + (j & ((1 << mp.log2p) - 1));
+}
+
 // Types stored as 16 nibble bytes per 32-value block / as int8 per value.
 constexpr bool nibble_layout(int qt) { return qt == kQ4_0 || qt == kQ4_K; }
 constexpr bool int8_layout(int qt) { return qt == kQ8_0 || qt == kQ6_K; }

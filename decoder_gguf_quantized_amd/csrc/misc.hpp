@@ -127,6 +127,7 @@ struct RopeArgs {
   int seq0, pos0;       // prefill: token t -> (seq0, pos0 + t)
   const int* dpos;      // decode (non-null): token t -> (seq t, dpos[t])
   const float* bias;    // [(nq + 2 nkv) hd] q|k|v projection bias added first, or null
+  KvMap map;            // cache layout
 };
 
 __global__ __launch_bounds__(256) void rope_kv_kernel(RopeArgs a) {
@@ -171,7 +172,7 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(RopeArgs a) {
     } else {
       const int g = is_k ? hh - a.nq : hh - a.nq - a.nkv;
       float* base = is_k ? a.kc : a.vc;
-      dst = base + (((size_t)seq * a.nkv + g) * a.ctx + pos) * a.hd;
+      dst = base + kv_row(a.map, a.nkv, a.ctx, seq, g, pos) * a.hd;
     }
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
@@ -479,6 +480,7 @@ struct SampleArgs {
   const StepParams* sp;  // if non-null: logits, out, temperature, seed, step come from here
   const uint32_t* cut_key;  // if non-null: top-p cut per row (see topp_cut_kernel)
   const int* cut_idx;
+  const int* seq;  // if non-null: sequence slot of each row, the row index of the random stream
 };
 
 QD_DEV void sample_resolve(SampleArgs& a) {
@@ -520,7 +522,7 @@ __global__ __launch_bounds__(256) void sample_stage1_kernel(SampleArgs a) {
     if (v0 >= a.vocab) break;
     u64x4 r;
     if (sampled) {
-      u64x4 ctr = {{(uint64_t)(v0 >> 2), a.step, (uint64_t)row, 0ull}};
+      u64x4 ctr = {{(uint64_t)(v0 >> 2), a.step, (uint64_t)(a.seq ? a.seq[row] : row), 0ull}};
       r = philox4x64_10(ctr, a.seed, 0ull);
     }
 #pragma unroll
@@ -610,6 +612,11 @@ struct StepArgs {
   int n;
   int pos[64];
   int host_tok[64];
+  int seq[64];          // sequence slot of each row (written to d_seq if non-null)
+  int* d_seq;
+  int tbl_n;            // page-table entries to set before the step (paged cache)
+  int tbl_idx[64], tbl_val[64];
+  int* d_table;
   const int* dev_tok;   // non-null: tokens come from device memory
   int vocab;
   int* d_pos;
@@ -630,7 +637,9 @@ struct StepArgs {
 __global__ __launch_bounds__(256) void step_begin_kernel(StepArgs a) {
   const int i = threadIdx.x;
   if (i == 0) *a.d_params = a.params;
+  if (i < a.tbl_n) a.d_table[a.tbl_idx[i]] = a.tbl_val[i];
   if (i < a.n) {
+    if (a.d_seq) a.d_seq[i] = a.seq[i];
     a.d_pos[i] = a.pos[i];
     int t = a.dev_tok ? a.dev_tok[i] : a.host_tok[i];
     if (t < 0 || t >= a.vocab) {
@@ -645,6 +654,37 @@ __global__ __launch_bounds__(256) void step_begin_kernel(StepArgs a) {
     const float2* src = tbl ? a.rope_l : a.rope_g;
     a.rope_cur[((size_t)tbl * a.max_seqs + sq) * a.half + k] = src[(size_t)a.pos[sq] * a.half + k];
   }
+}
+
+// ------------------------------------------------------------ paged-cache upkeep
+// Page-table entries set in stream order (the host hands out pages and passes
+// the new entries by value).
+struct TableSet {
+  int n;
+  int idx[64], val[64];
+  int* table;
+};
+
+__global__ __launch_bounds__(64) void table_set_kernel(TableSet t) {
+  if ((int)threadIdx.x < t.n) t.table[t.idx[threadIdx.x]] = t.val[threadIdx.x];
+}
+
+// Copy preset K and V rows ([nkv][n][hd] each) of one (sequence, layer) into
+// the cache at positions 0..n-1.  Grid (n, nkv, 2: K / V), hd / 4 threads.
+struct KvScatter {
+  const float* src_k;
+  const float* src_v;
+  float* kc;            // layer base of the caches
+  float* vc;
+  int n, nkv, ctx, hd, seq;
+  KvMap map;
+};
+
+__global__ __launch_bounds__(64) void kv_scatter_kernel(KvScatter a) {
+  const int j = blockIdx.x, g = blockIdx.y, which = blockIdx.z, e = threadIdx.x;
+  const float4* src = reinterpret_cast<const float4*>((which ? a.src_v : a.src_k) + ((size_t)g * a.n + j) * a.hd);
+  float4* dst = reinterpret_cast<float4*>((which ? a.vc : a.kc) + kv_row(a.map, a.nkv, a.ctx, a.seq, g, j) * a.hd);
+  if (e < a.hd / 4) dst[e] = src[e];
 }
 
 }  // namespace qd

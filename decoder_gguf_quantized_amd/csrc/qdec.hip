@@ -125,6 +125,7 @@ struct qdec_model {
   float* part_o = nullptr;
   float* part_ml = nullptr;
   int chunk = 0, nchunk = 0;
+  int chunk_base = 0;  // decode chunk chosen at load (a paged cache caps it at the page size)
   float* s_v = nullptr;
   int* s_i = nullptr;
   uint32_t* cut_key = nullptr;  // [max_seqs] top-p cut per row
@@ -132,6 +133,13 @@ struct qdec_model {
   int nvchunk = 0;
   int* d_pos = nullptr;
   int* d_tok = nullptr;
+  int* d_seq = nullptr;             // [64] sequence slot of each row of a slotted decode step
+  std::vector<int> row_seq;         // slots of the decode step being enqueued
+  // paged KV cache (qdec_kv_paged); page_size 0 = contiguous [seq][nkv][max_ctx]
+  int page_size = 0, log2p = 0, n_pages = 0, table_w = 0;
+  int* d_table = nullptr;           // [max_seqs][table_w] page of each position block
+  std::vector<int> free_pages;      // pages no sequence holds (a stack)
+  std::vector<std::vector<int>> seq_pages;  // pages each sequence holds, in position order
   int* counters = nullptr;          // [max_seqs][n_head_kv] decode-attention chunk counters
   StepParams* d_params = nullptr;   // per-step values read by replayed graphs
   hipStream_t cap_stream = nullptr; // capture stream for the decode graphs
@@ -150,6 +158,7 @@ struct qdec_model {
   hipStream_t last_stream = nullptr;
 
   const Mat& lm() const { return tied ? embd : out_w; }
+  KvMap map() const { return KvMap{page_size ? d_table : nullptr, table_w, log2p}; }
 
   template <typename T>
   T* dalloc(size_t count) {
@@ -158,6 +167,13 @@ struct qdec_model {
     hipck(hipMalloc(&p, bytes), "hipMalloc");
     allocs.push_back(p);
     return reinterpret_cast<T*>(p);
+  }
+  void dfree(void* p) {
+    auto it = std::find(allocs.begin(), allocs.end(), p);
+    if (it != allocs.end()) {
+      allocs.erase(it);
+      (void)hipFree(p);
+    }
   }
 };
 
@@ -337,25 +353,22 @@ void rmsnorm_rows(qdec_model* m, hipStream_t st, const float* x, int ldx, const 
   qlaunch(rmsnorm_kernel, rows, 256, 0, st, a);
 }
 
-template <int HD>
+template <int HD, bool PAGED>
 void attn_decode_hd(int G, dim3 grid, hipStream_t st, const AttnDecodeArgs& a) {
   switch (G) {
-    case 1: qlaunch(attn_decode_kernel<HD, 1>, grid, 256, 0, st, a); break;
-    case 2: qlaunch(attn_decode_kernel<HD, 2>, grid, 256, 0, st, a); break;
-    case 4: qlaunch(attn_decode_kernel<HD, 4>, grid, 256, 0, st, a); break;
+    case 1: qlaunch(attn_decode_kernel<HD, 1, PAGED>, grid, 256, 0, st, a); break;
+    case 2: qlaunch(attn_decode_kernel<HD, 2, PAGED>, grid, 256, 0, st, a); break;
+    case 4: qlaunch(attn_decode_kernel<HD, 4, PAGED>, grid, 256, 0, st, a); break;
     default:
-      if constexpr (HD == 128) qlaunch(attn_decode_kernel<HD, 8>, grid, 256, 0, st, a);
+      if constexpr (HD == 128) qlaunch(attn_decode_kernel<HD, 8, PAGED>, grid, 256, 0, st, a);
       break;
   }
 }
 
-size_t l_off(const qdec_model* m, int layer, int seq, int g) {
-  return (size_t)layer * m->kv_layer + ((size_t)seq * m->cfg.n_head_kv + g) * m->max_ctx * m->cfg.head_dim;
-}
-
 int layer_window(const qdec_model* m, int l) { return m->layers[l].global ? 0 : m->cfg.window; }
 
-void attention_decode(qdec_model* m, hipStream_t st, int l, int B) {
+// slotted: row b serves sequence d_seq[b] (continuous batching), else b.
+void attention_decode(qdec_model* m, hipStream_t st, int l, int B, bool slotted) {
   const qdec_config& c = m->cfg;
   const Layer& L = m->layers[l];
   const int hd = c.head_dim, G = c.n_head / c.n_head_kv;
@@ -363,29 +376,29 @@ void attention_decode(qdec_model* m, hipStream_t st, int l, int B) {
   AttnDecodeArgs a{m->qkv, m->nqkv, m->kc + l * m->kv_layer, m->vc + l * m->kv_layer, m->max_ctx, m->d_pos,
                    c.n_head, c.n_head_kv, layer_window(m, l), m->chunk, m->nchunk, L.q_norm, L.k_norm, c.rms_eps,
                    m->rope_cur + (L.global ? 0 : (size_t)m->max_seqs * (hd / 2)), scale_log2, m->part_o, m->part_ml,
-                   m->counters, m->a};
+                   m->counters, m->a, slotted ? m->d_seq : nullptr, m->map()};
   double kvbytes = 0;
   for (int s = 0; s < B; ++s) {
-    int p = m->kvlen[s];
+    int p = m->kvlen[(size_t)s < m->row_seq.size() ? m->row_seq[s] : s];
     int lo = a.window > 0 ? std::max(0, p - a.window + 1) : 0;
     kvbytes += (double)(p - lo + 1) * c.n_head_kv * hd * 8;
   }
   {
     Timed tm(m, st, "attn_decode", kvbytes + (double)B * m->nqkv * 4, 4.0 * kvbytes / 8 * G);
     dim3 grid(m->nchunk, c.n_head_kv, B);
-    if (hd == 64) attn_decode_hd<64>(G, grid, st, a);
-    else if (hd == 128) attn_decode_hd<128>(G, grid, st, a);
-    else attn_decode_hd<256>(G, grid, st, a);
+    const bool pg = m->page_size > 0;
+    if (hd == 64) pg ? attn_decode_hd<64, true>(G, grid, st, a) : attn_decode_hd<64, false>(G, grid, st, a);
+    else if (hd == 128) pg ? attn_decode_hd<128, true>(G, grid, st, a) : attn_decode_hd<128, false>(G, grid, st, a);
+    else pg ? attn_decode_hd<256, true>(G, grid, st, a) : attn_decode_hd<256, false>(G, grid, st, a);
   }
 }
 
 void attention_prefill(qdec_model* m, hipStream_t st, int l, int seq, int T, int pos0) {
   const qdec_config& c = m->cfg;
   const int hd = c.head_dim;
-  const size_t seq_off = (size_t)seq * c.n_head_kv * m->max_ctx * hd;
-  AttnPrefillArgs a{m->q, m->kc + l * m->kv_layer + seq_off, m->vc + l * m->kv_layer + seq_off, m->max_ctx, T, pos0,
+  AttnPrefillArgs a{m->q, m->kc + l * m->kv_layer, m->vc + l * m->kv_layer, m->max_ctx, T, pos0,
                     c.n_head, c.n_head_kv, layer_window(m, l),
-                    (float)(1.0 / std::sqrt((double)hd) * 1.4426950408889634), m->a};
+                    (float)(1.0 / std::sqrt((double)hd) * 1.4426950408889634), m->a, seq, m->map()};
   double pairs = 0;
   for (int t = 0; t < T; ++t) {
     int p = pos0 + t, lo = a.window > 0 ? std::max(0, p - a.window + 1) : 0;
@@ -405,7 +418,7 @@ void rope_kv(qdec_model* m, hipStream_t st, int l, int n, int seq0, int pos0, co
   const Layer& L = m->layers[l];
   RopeArgs a{m->qkv, m->nqkv, m->q, m->kc + l * m->kv_layer, m->vc + l * m->kv_layer, m->max_ctx, c.n_head,
              c.n_head_kv, c.head_dim, L.q_norm, L.k_norm, c.rms_eps, L.global ? m->rope_g : m->rope_l,
-             seq0, pos0, dpos, L.qkv_bias};
+             seq0, pos0, dpos, L.qkv_bias, m->map()};
   Timed tm(m, st, "rope_kv", (double)n * m->nqkv * 8, 0);
   qlaunch(rope_kv_kernel, n, 256, 0, st, a);
 }
@@ -419,10 +432,11 @@ void embed(qdec_model* m, hipStream_t st, const int* d_tokens, int n, float* out
 }
 
 void sample(qdec_model* m, hipStream_t st, const float* logits, int ld, int rows, float temp, uint64_t seed,
-            uint64_t step, int* out, int* out2, const StepParams* sp = nullptr, bool topp = false) {
+            uint64_t step, int* out, int* out2, const StepParams* sp = nullptr, bool topp = false,
+            const int* seq = nullptr) {
   const int V = m->cfg.vocab;
   SampleArgs a{logits, ld, V, rows, temp, seed, step, m->s_v, m->s_i, m->nvchunk, out, out2, sp,
-               topp ? m->cut_key : nullptr, topp ? m->cut_idx : nullptr};
+               topp ? m->cut_key : nullptr, topp ? m->cut_idx : nullptr, seq};
   if (topp) {
     TopPArgs t{logits, ld, V, rows, temp, 1.f, m->cut_key, m->cut_idx, sp};
     Timed tm(m, st, "topp_cut", (double)rows * V * 4 * 6, 0);
@@ -454,7 +468,7 @@ void qkv_gemv(qdec_model* m, hipStream_t st, const Layer& L, const float* x, int
 
 // The blocks over n tokens of one sequence (prefill) or one token of each of n
 // sequences (decode, dpos != null); the residual stream is m->x.
-void blocks(qdec_model* m, hipStream_t st, int n, int seq, int pos0, const int* dpos) {
+void blocks(qdec_model* m, hipStream_t st, int n, int seq, int pos0, const int* dpos, bool slotted = false) {
   const qdec_config& c = m->cfg;
   const int H = c.hidden;
   const bool dec = dpos != nullptr;
@@ -481,7 +495,7 @@ void blocks(qdec_model* m, hipStream_t st, int n, int seq, int pos0, const int* 
       }
     }
     if (dec) {
-      attention_decode(m, st, l, n);  // QK-norm, RoPE and the KV append run inside
+      attention_decode(m, st, l, n, slotted);  // QK-norm, RoPE and the KV append run inside
     } else {
       rope_kv(m, st, l, n, seq, pos0, nullptr);
       attention_prefill(m, st, l, seq, n, pos0);
@@ -519,17 +533,17 @@ void blocks(qdec_model* m, hipStream_t st, int n, int seq, int pos0, const int* 
 
 // One decode step for sequences 0..n-1 reading tokens, positions and the
 // step's parameters from device memory (so it can be captured and replayed).
-void decode_body(qdec_model* m, hipStream_t st, int n, bool topp) {
+void decode_body(qdec_model* m, hipStream_t st, int n, bool topp, bool slotted) {
   const qdec_config& c = m->cfg;
   embed(m, st, m->d_tok, n, m->x);
-  blocks(m, st, n, 0, 0, m->d_pos);
+  blocks(m, st, n, 0, 0, m->d_pos, slotted);
   if (c.sandwich_norm)  // the last post-FFN norm and residual add run in the head's prologue
     gemv(m, st, m->lm(), m->x2, c.hidden, m->output_norm, c.rms_eps, nullptr, c.vocab, n, kModeStore,
          &m->d_params->logits, Resid{m->y, m->layers[c.n_layer - 1].post_ffw, nullptr});
   else
     gemv(m, st, m->lm(), m->x, c.hidden, m->output_norm, c.rms_eps, nullptr, c.vocab, n, kModeStore,
          &m->d_params->logits);
-  sample(m, st, nullptr, c.vocab, n, 0.f, 0, 0, nullptr, nullptr, m->d_params, topp);
+  sample(m, st, nullptr, c.vocab, n, 0.f, 0, 0, nullptr, nullptr, m->d_params, topp, slotted ? m->d_seq : nullptr);
 }
 
 // ------------------------------------------------------------ error handling
@@ -997,6 +1011,7 @@ int load(const qdec_config* cfgp, const qdec_tensor* ts, int32_t n, int32_t max_
       if (const char* e = getenv("QDEC_CHUNK")) ch = std::max(atoi(e), (max_ctx + kMaxChunks - 1) / kMaxChunks);
 #endif
       m->chunk = ch;
+      m->chunk_base = ch;
       m->nchunk = (max_ctx + ch - 1) / ch;
     }
     m->part_o = m->dalloc<float>((size_t)max_seqs * c.n_head * m->nchunk * c.head_dim);
@@ -1008,6 +1023,8 @@ int load(const qdec_config* cfgp, const qdec_tensor* ts, int32_t n, int32_t max_
     m->cut_idx = m->dalloc<int>(max_seqs);
     m->d_pos = m->dalloc<int>(64);
     m->d_tok = m->dalloc<int>(64);
+    m->d_seq = m->dalloc<int>(64);
+    m->seq_pages.assign(max_seqs, {});
     m->counters = m->dalloc<int>((size_t)max_seqs * c.n_head_kv);
     hipck(hipMemsetAsync(m->counters, 0, (size_t)max_seqs * c.n_head_kv * 4, st), "memset");
     m->d_params = m->dalloc<StepParams>(1);
@@ -1029,6 +1046,169 @@ int load(const qdec_config* cfgp, const qdec_tensor* ts, int32_t n, int32_t max_
     return QDEC_INTERNAL;
   }
   *out = m;
+  return QDEC_OK;
+}
+
+// ------------------------------------------------------------ paged KV cache
+// Pages are handed out from a free stack as sequences grow and returned on
+// reset / truncate.  New page-table entries reach the device in stream order,
+// as kernel arguments (table_set_kernel, or step_begin_kernel for decode), so
+// no host buffer is read asynchronously.  A page returned by one call and
+// handed to another sequence by a later call is safe because both calls' work
+// runs in stream order on the caller's stream.
+struct PageSet {
+  std::vector<std::pair<int, int>> sets;  // (table index, page)
+  std::vector<std::pair<int, int>> taken; // (seq, count) to roll back
+};
+
+// Make sequence seq hold pages for positions [0, len); false (nothing changed)
+// when the free pages do not suffice.
+bool grow_pages(qdec_model* m, int seq, int len, PageSet& ps) {
+  if (!m->page_size) return true;
+  const int need = (len + m->page_size - 1) >> m->log2p;
+  auto& held = m->seq_pages[seq];
+  const int add = need - (int)held.size();
+  if (add <= 0) return true;
+  if (add > (int)m->free_pages.size()) return false;
+  for (int i = 0; i < add; ++i) {
+    const int pg = m->free_pages.back();
+    m->free_pages.pop_back();
+    ps.sets.push_back({seq * m->table_w + (int)held.size(), pg});
+    held.push_back(pg);
+  }
+  ps.taken.push_back({seq, add});
+  return true;
+}
+
+void undo_pages(qdec_model* m, PageSet& ps) {
+  for (auto it = ps.taken.rbegin(); it != ps.taken.rend(); ++it)
+    for (int i = 0; i < it->second; ++i) {
+      m->free_pages.push_back(m->seq_pages[it->first].back());
+      m->seq_pages[it->first].pop_back();
+    }
+  ps.sets.clear();
+  ps.taken.clear();
+}
+
+// Return the pages of seq past the first ceil(len / P).
+void shrink_pages(qdec_model* m, int seq, int len) {
+  if (!m->page_size) return;
+  const int keep = (len + m->page_size - 1) >> m->log2p;
+  auto& held = m->seq_pages[seq];
+  while ((int)held.size() > keep) {
+    m->free_pages.push_back(held.back());
+    held.pop_back();
+  }
+}
+
+void launch_table_sets(qdec_model* m, hipStream_t st, const PageSet& ps) {
+  for (size_t i0 = 0; i0 < ps.sets.size(); i0 += 64) {
+    TableSet t{};
+    t.n = (int)std::min<size_t>(64, ps.sets.size() - i0);
+    for (int i = 0; i < t.n; ++i) {
+      t.idx[i] = ps.sets[i0 + i].first;
+      t.val[i] = ps.sets[i0 + i].second;
+    }
+    t.table = m->d_table;
+    Timed tm(m, st, "table_set", 0, 0);
+    qlaunch(table_set_kernel, 1, 64, 0, st, t);
+  }
+}
+
+// One decode step for rows 0..n-1.  seqs: the sequence slot of each row
+// (host array, distinct), or null for rows = sequences 0..n-1.
+int decode_impl(qdec_model* m, const int32_t* seqs, const int32_t* tokens, int32_t n_seqs, float* d_logits,
+                int32_t* d_token_out, float temperature, float top_p, uint64_t seed, uint64_t step, uint32_t flags,
+                hipStream_t st) {
+  const qdec_config& c = m->cfg;
+  if (n_seqs < 1 || n_seqs > m->max_seqs) { set_err("n_seqs %d outside [1, %d]", n_seqs, m->max_seqs); return QDEC_REFUSED; }
+  if (!tokens || !d_logits || !d_token_out) { set_err("tokens, d_logits and d_token_out must not be NULL"); return QDEC_REFUSED; }
+  if (!(temperature >= 0.f) || !std::isfinite(temperature)) { set_err("temperature must be finite and >= 0"); return QDEC_REFUSED; }
+  if (std::isnan(top_p)) { set_err("top_p must not be NaN"); return QDEC_REFUSED; }
+  if (flags & ~(uint32_t)QDEC_TOKENS_ON_DEVICE) { set_err("decode: unknown flag bits 0x%x", flags); return QDEC_REFUSED; }
+  const bool on_dev = flags & QDEC_TOKENS_ON_DEVICE;
+  std::vector<int> slot(n_seqs);
+  std::vector<char> used(m->max_seqs, 0);
+  for (int r = 0; r < n_seqs; ++r) {
+    const int s = seqs ? seqs[r] : r;
+    if (s < 0 || s >= m->max_seqs) { set_err("seqs[%d] = %d outside [0, %d)", r, s, m->max_seqs); return QDEC_REFUSED; }
+    if (used[s]) { set_err("sequence %d appears twice in one step", s); return QDEC_REFUSED; }
+    used[s] = 1;
+    slot[r] = s;
+    if (m->kvlen[s] >= m->max_ctx) { set_err("seq %d: KV cache full (max_ctx %d)", s, m->max_ctx); return QDEC_REFUSED; }
+    if (!on_dev && (tokens[r] < 0 || tokens[r] >= c.vocab)) {
+      set_err("tokens[%d] = %d outside [0, %d)", r, tokens[r], c.vocab);
+      return QDEC_REFUSED;
+    }
+  }
+  PageSet ps;
+  for (int r = 0; r < n_seqs; ++r)
+    if (!grow_pages(m, slot[r], m->kvlen[slot[r]] + 1, ps)) {
+      undo_pages(m, ps);
+      set_err("KV pages exhausted (%d pages of %d positions)", m->n_pages, m->page_size);
+      return QDEC_REFUSED;
+    }
+  const bool slotted = seqs != nullptr;
+  try {
+    m->last_stream = st;
+    m->row_seq = slot;
+    StepArgs sa{};
+    sa.n = n_seqs;
+    for (int r = 0; r < n_seqs; ++r) {
+      sa.pos[r] = m->kvlen[slot[r]];
+      sa.host_tok[r] = on_dev ? 0 : tokens[r];
+      sa.seq[r] = slot[r];
+    }
+    sa.d_seq = slotted ? m->d_seq : nullptr;
+    sa.tbl_n = (int)ps.sets.size();  // at most one new page per row
+    for (int i = 0; i < sa.tbl_n; ++i) {
+      sa.tbl_idx[i] = ps.sets[i].first;
+      sa.tbl_val[i] = ps.sets[i].second;
+    }
+    sa.d_table = m->d_table;
+    sa.dev_tok = on_dev ? tokens : nullptr;
+    sa.vocab = c.vocab;
+    sa.d_pos = m->d_pos;
+    sa.d_tok = m->d_tok;
+    sa.err = m->err_dev;
+    sa.params = StepParams{temperature, top_p, n_seqs, seed, step, d_logits, d_token_out};
+    const bool topp = temperature > 0.f && top_p < 1.f;
+    sa.d_params = m->d_params;
+    sa.rope_g = m->rope_g;
+    sa.rope_l = m->rope_l;
+    sa.rope_cur = m->rope_cur;
+    sa.half = c.head_dim / 2;
+    sa.max_seqs = m->max_seqs;
+    {
+      Timed tm(m, st, "step_begin", 0, 0);
+      qlaunch(step_begin_kernel, 1, 256, 0, st, sa);
+    }
+    if (m->timing) {
+      decode_body(m, st, n_seqs, topp, slotted);
+    } else {
+      // graph per (batch size, slotted, top-p on)
+      hipGraphExec_t& ge = m->graphs[4 * n_seqs + (slotted ? 2 : 0) + (topp ? 1 : 0)];
+      if (!ge) {
+        hipGraph_t graph = nullptr;
+        hipck(hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeThreadLocal), "hipStreamBeginCapture");
+        try {
+          decode_body(m, m->cap_stream, n_seqs, topp, slotted);
+        } catch (...) {
+          (void)hipStreamEndCapture(m->cap_stream, &graph);
+          if (graph) (void)hipGraphDestroy(graph);
+          throw;
+        }
+        hipck(hipStreamEndCapture(m->cap_stream, &graph), "hipStreamEndCapture");
+        hipError_t e = hipGraphInstantiate(&ge, graph, nullptr, nullptr, 0);
+        (void)hipGraphDestroy(graph);
+        hipck(e, "hipGraphInstantiate");
+      }
+      hipck(hipGraphLaunch(ge, st), "hipGraphLaunch");
+    }
+    for (int r = 0; r < n_seqs; ++r) m->kvlen[slot[r]] += 1;
+  } catch (const HipError& e) {
+    return fail_internal(m, st, e.msg);
+  }
   return QDEC_OK;
 }
 
@@ -1075,8 +1255,14 @@ int qdec_prefill(qdec_model* m, int32_t seq, const int32_t* tokens, int32_t n_to
       return QDEC_REFUSED;
     }
   const bool all = flags & QDEC_ALL_LOGITS;
+  PageSet ps;
+  if (!grow_pages(m, seq, m->kvlen[seq] + n_tokens, ps)) {
+    set_err("KV pages exhausted (%d pages of %d positions)", m->n_pages, m->page_size);
+    return QDEC_REFUSED;
+  }
   try {
     m->last_stream = st;
+    launch_table_sets(m, st, ps);
     const int H = c.hidden, V = c.vocab;
     const int pos_start = m->kvlen[seq];
     for (int c0 = 0; c0 < n_tokens; c0 += m->ws_T) {
@@ -1108,80 +1294,29 @@ int qdec_decode_step(qdec_model* m, const int32_t* tokens, int32_t n_seqs, float
                      float temperature, float top_p, uint64_t seed, uint64_t step, uint32_t flags, void* stream) {
   g_err.clear();
   if (int rc = check_usable(m)) return rc;
-  hipStream_t st = (hipStream_t)stream;
-  const qdec_config& c = m->cfg;
-  if (n_seqs < 1 || n_seqs > m->max_seqs) { set_err("n_seqs %d outside [1, %d]", n_seqs, m->max_seqs); return QDEC_REFUSED; }
-  if (!tokens || !d_logits || !d_token_out) { set_err("tokens, d_logits and d_token_out must not be NULL"); return QDEC_REFUSED; }
-  if (!(temperature >= 0.f) || !std::isfinite(temperature)) { set_err("temperature must be finite and >= 0"); return QDEC_REFUSED; }
-  if (std::isnan(top_p)) { set_err("top_p must not be NaN"); return QDEC_REFUSED; }
-  if (flags & ~(uint32_t)QDEC_TOKENS_ON_DEVICE) { set_err("decode: unknown flag bits 0x%x", flags); return QDEC_REFUSED; }
-  const bool on_dev = flags & QDEC_TOKENS_ON_DEVICE;
-  for (int s = 0; s < n_seqs; ++s) {
-    if (m->kvlen[s] >= m->max_ctx) { set_err("seq %d: KV cache full (max_ctx %d)", s, m->max_ctx); return QDEC_REFUSED; }
-    if (!on_dev && (tokens[s] < 0 || tokens[s] >= c.vocab)) {
-      set_err("tokens[%d] = %d outside [0, %d)", s, tokens[s], c.vocab);
-      return QDEC_REFUSED;
-    }
-  }
-  try {
-    m->last_stream = st;
-    StepArgs sa{};
-    sa.n = n_seqs;
-    for (int s = 0; s < n_seqs; ++s) {
-      sa.pos[s] = m->kvlen[s];
-      sa.host_tok[s] = on_dev ? 0 : tokens[s];
-    }
-    sa.dev_tok = on_dev ? tokens : nullptr;
-    sa.vocab = c.vocab;
-    sa.d_pos = m->d_pos;
-    sa.d_tok = m->d_tok;
-    sa.err = m->err_dev;
-    sa.params = StepParams{temperature, top_p, n_seqs, seed, step, d_logits, d_token_out};
-    const bool topp = temperature > 0.f && top_p < 1.f;
-    sa.d_params = m->d_params;
-    sa.rope_g = m->rope_g;
-    sa.rope_l = m->rope_l;
-    sa.rope_cur = m->rope_cur;
-    sa.half = c.head_dim / 2;
-    sa.max_seqs = m->max_seqs;
-    {
-      Timed tm(m, st, "step_begin", 0, 0);
-      qlaunch(step_begin_kernel, 1, 256, 0, st, sa);
-    }
-    if (m->timing) {
-      decode_body(m, st, n_seqs, topp);
-    } else {
-      hipGraphExec_t& ge = m->graphs[2 * n_seqs + (topp ? 1 : 0)];  // graph per (batch size, top-p on)
-      if (!ge) {
-        hipGraph_t graph = nullptr;
-        hipck(hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeThreadLocal), "hipStreamBeginCapture");
-        try {
-          decode_body(m, m->cap_stream, n_seqs, topp);
-        } catch (...) {
-          (void)hipStreamEndCapture(m->cap_stream, &graph);
-          if (graph) (void)hipGraphDestroy(graph);
-          throw;
-        }
-        hipck(hipStreamEndCapture(m->cap_stream, &graph), "hipStreamEndCapture");
-        hipError_t e = hipGraphInstantiate(&ge, graph, nullptr, nullptr, 0);
-        (void)hipGraphDestroy(graph);
-        hipck(e, "hipGraphInstantiate");
-      }
-      hipck(hipGraphLaunch(ge, st), "hipGraphLaunch");
-    }
-    for (int s = 0; s < n_seqs; ++s) m->kvlen[s] += 1;
-  } catch (const HipError& e) {
-    return fail_internal(m, st, e.msg);
-  }
-  return QDEC_OK;
+  return decode_impl(m, nullptr, tokens, n_seqs, d_logits, d_token_out, temperature, top_p, seed, step, flags,
+                     (hipStream_t)stream);
+}
+
+int qdec_decode_batch(qdec_model* m, const int32_t* seqs, const int32_t* tokens, int32_t n, float* d_logits,
+                      int32_t* d_token_out, float temperature, float top_p, uint64_t seed, uint64_t step,
+                      uint32_t flags, void* stream) {
+  g_err.clear();
+  if (int rc = check_usable(m)) return rc;
+  if (!seqs) { set_err("seqs must not be NULL"); return QDEC_REFUSED; }
+  return decode_impl(m, seqs, tokens, n, d_logits, d_token_out, temperature, top_p, seed, step, flags,
+                     (hipStream_t)stream);
 }
 
 int qdec_kv_reset(qdec_model* m, int32_t seq) {
   g_err.clear();
   if (int rc = check_usable(m)) return rc;
   if (seq < -1 || seq >= m->max_seqs) { set_err("seq %d outside [-1, %d)", seq, m->max_seqs); return QDEC_REFUSED; }
-  if (seq < 0) std::fill(m->kvlen.begin(), m->kvlen.end(), 0);
-  else m->kvlen[seq] = 0;
+  for (int s = 0; s < m->max_seqs; ++s)
+    if (seq < 0 || s == seq) {
+      m->kvlen[s] = 0;
+      shrink_pages(m, s, 0);
+    }
   return QDEC_OK;
 }
 
@@ -1191,6 +1326,7 @@ int qdec_kv_truncate(qdec_model* m, int32_t seq, int32_t n) {
   if (seq < 0 || seq >= m->max_seqs) { set_err("seq %d outside [0, %d)", seq, m->max_seqs); return QDEC_REFUSED; }
   if (n < 0 || n > m->kvlen[seq]) { set_err("n %d outside [0, kv_len %d]", n, m->kvlen[seq]); return QDEC_REFUSED; }
   m->kvlen[seq] = n;
+  shrink_pages(m, seq, n);
   return QDEC_OK;
 }
 
@@ -1204,19 +1340,109 @@ int qdec_kv_write(qdec_model* m, int32_t seq, int32_t layer, const float* d_k, c
   if (layer < 0 || layer >= c.n_layer) { set_err("layer %d outside [0, %d)", layer, c.n_layer); return QDEC_REFUSED; }
   if (n_pos < 0 || n_pos > m->max_ctx) { set_err("n_pos %d outside [0, %d]", n_pos, m->max_ctx); return QDEC_REFUSED; }
   if (n_pos > 0 && (!d_k || !d_v)) { set_err("d_k and d_v must not be NULL"); return QDEC_REFUSED; }
+  PageSet ps;
+  if (!grow_pages(m, seq, n_pos, ps)) {
+    set_err("KV pages exhausted (%d pages of %d positions)", m->n_pages, m->page_size);
+    return QDEC_REFUSED;
+  }
   try {
-    const size_t row = (size_t)c.head_dim * 4;
-    for (int g = 0; g < c.n_head_kv; ++g) {
-      const size_t dst = l_off(m, layer, seq, g);
-      if (n_pos) {
-        hipck(hipMemcpyAsync(m->kc + dst, d_k + (size_t)g * n_pos * c.head_dim, n_pos * row, hipMemcpyDeviceToDevice, st), "kv copy");
-        hipck(hipMemcpyAsync(m->vc + dst, d_v + (size_t)g * n_pos * c.head_dim, n_pos * row, hipMemcpyDeviceToDevice, st), "kv copy");
-      }
+    m->last_stream = st;
+    launch_table_sets(m, st, ps);
+    shrink_pages(m, seq, n_pos);
+    if (n_pos) {
+      KvScatter a{d_k, d_v, m->kc + layer * m->kv_layer, m->vc + layer * m->kv_layer, n_pos, c.n_head_kv, m->max_ctx,
+                  c.head_dim, seq, m->map()};
+      Timed tm(m, st, "kv_scatter", (double)n_pos * c.n_head_kv * c.head_dim * 16, 0);
+      qlaunch(kv_scatter_kernel, dim3(n_pos, c.n_head_kv, 2), 64, 0, st, a);
     }
     m->kvlen[seq] = n_pos;
   } catch (const HipError& e) {
     return fail_internal(m, st, e.msg);
   }
+  return QDEC_OK;
+}
+
+int qdec_kv_paged(qdec_model* m, int32_t page_size, int32_t n_pages, void* stream) {
+  g_err.clear();
+  if (int rc = check_usable(m)) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  const qdec_config& c = m->cfg;
+  if (page_size < 16 || page_size > (1 << 20) || (page_size & (page_size - 1))) {
+    set_err("page_size %d must be a power of two in [16, 2^20]", page_size);
+    return QDEC_REFUSED;
+  }
+  if (n_pages < 1) { set_err("n_pages must be >= 1"); return QDEC_REFUSED; }
+  for (int s = 0; s < m->max_seqs; ++s)
+    if (m->kvlen[s]) {
+      set_err("the KV cache is in use (seq %d holds %d positions): reset it first", s, m->kvlen[s]);
+      return QDEC_REFUSED;
+    }
+  // a decode chunk lies in one page: chunks of min(chunk, page_size) positions,
+  // at least the kernel's minimum and at most kMaxChunks of them per sequence
+  const int ch_min = 4 * (256 / (c.head_dim / 8));
+  if (page_size < ch_min) {
+    set_err("page_size %d is below the decode chunk of %d positions at head_dim %d", page_size, ch_min, c.head_dim);
+    return QDEC_REFUSED;
+  }
+  const int chunk = std::min(m->chunk_base, page_size);
+  const int nchunk = (m->max_ctx + chunk - 1) / chunk;
+  if (nchunk > kMaxChunks) {
+    int need = 1;
+    while ((int64_t)need * kMaxChunks < m->max_ctx) need *= 2;
+    set_err("page_size %d is too small for max_ctx %d (at least %d)", page_size, m->max_ctx, need);
+    return QDEC_REFUSED;
+  }
+  const size_t layer = (size_t)n_pages * c.n_head_kv * page_size * c.head_dim;
+  if ((double)layer * c.n_layer * 8.0 > 256.0 * (1ull << 30)) {
+    set_err("a pool of %d pages of %d positions needs more than 256 GiB", n_pages, page_size);
+    return QDEC_REFUSED;
+  }
+  try {
+    m->last_stream = st;
+    hipck(hipStreamSynchronize(st), "sync");  // nothing reads the old cache any more
+    for (auto& g : m->graphs)  // captured with the old cache and kernels
+      if (g.second) (void)hipGraphExecDestroy(g.second);
+    m->graphs.clear();
+    m->dfree(m->kc);
+    m->dfree(m->vc);
+    m->kc = m->vc = nullptr;
+    if (m->d_table) m->dfree(m->d_table);
+    m->kc = m->dalloc<float>(layer * c.n_layer);
+    m->vc = m->dalloc<float>(layer * c.n_layer);
+    hipck(hipMemsetAsync(m->kc, 0, layer * c.n_layer * 4, st), "memset");
+    hipck(hipMemsetAsync(m->vc, 0, layer * c.n_layer * 4, st), "memset");
+    m->table_w = (m->max_ctx + page_size - 1) / page_size;
+    m->d_table = m->dalloc<int>((size_t)m->max_seqs * m->table_w);
+    hipck(hipMemsetAsync(m->d_table, 0, (size_t)m->max_seqs * m->table_w * 4, st), "memset");
+    if (nchunk > m->nchunk) {
+      m->dfree(m->part_o);
+      m->dfree(m->part_ml);
+      m->part_o = m->dalloc<float>((size_t)m->max_seqs * c.n_head * nchunk * c.head_dim);
+      m->part_ml = m->dalloc<float>((size_t)m->max_seqs * c.n_head * nchunk * 2);
+    }
+    m->chunk = chunk;
+    m->nchunk = nchunk;
+    m->kv_layer = layer;
+    m->page_size = page_size;
+    m->log2p = 0;
+    while ((1 << m->log2p) < page_size) ++m->log2p;
+    m->n_pages = n_pages;
+    m->free_pages.resize(n_pages);
+    for (int i = 0; i < n_pages; ++i) m->free_pages[i] = n_pages - 1 - i;  // page 0 handed out first
+    m->seq_pages.assign(m->max_seqs, {});
+    hipck(hipStreamSynchronize(st), "sync");
+  } catch (const HipError& e) {
+    return fail_internal(m, st, e.msg);
+  }
+  return QDEC_OK;
+}
+
+int qdec_kv_pages(const qdec_model* m, int32_t* page_size, int32_t* n_pages, int32_t* n_free) {
+  g_err.clear();
+  if (!m || !page_size || !n_pages || !n_free) { set_err("model and outputs must not be NULL"); return QDEC_REFUSED; }
+  *page_size = m->page_size;
+  *n_pages = m->n_pages;
+  *n_free = (int32_t)m->free_pages.size();
   return QDEC_OK;
 }
 

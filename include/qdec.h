@@ -18,6 +18,9 @@
  *        errors" and "How the buffers cross": opaque handle freed exactly once,
  *        status 1 = refusal / status 2 = bug caught at the boundary, a poisoned
  *        latch after GPU failure, waiting for in-flight work on failure.
+ *   [P]  "PyTensor Beyond PyMC: Building LLM Inference in Python": its
+ *        engineering-roadmap table (a paged KV cache and continuous batching)
+ *        and its Q4_K_M GGUF file.
  *
  * Conventions for every call:
  *   - `d_*` arguments are device pointers on the current HIP device; other
@@ -190,6 +193,35 @@ int qdec_prefill(qdec_model* m, int32_t seq, const int32_t* tokens, int32_t n_to
 int qdec_decode_step(qdec_model* m, const int32_t* tokens, int32_t n_seqs, float* d_logits,
                      int32_t* d_token_out, float temperature, float top_p, uint64_t seed,
                      uint64_t step, uint32_t flags, void* stream);
+
+/* Continuous batching ([P] "PyTensor Beyond PyMC: Building LLM Inference in
+ * Python", engineering-roadmap table, KV-cache row: continuous batching; [W]
+ * Step 9's loop, run for several sequences): one decode step for an arbitrary
+ * set of sequence slots, so sequences can join and leave between steps.  Row r
+ * of tokens / d_logits / d_token_out serves sequence seqs[r] (host array of n
+ * distinct slots in [0, max_seqs)) at position kv_len(seqs[r]).  The random
+ * stream of row r is sequence seqs[r]'s (Philox counter (v/4, step, seqs[r],
+ * 0)), so a sequence's draws do not depend on which others share the step.
+ * Otherwise as qdec_decode_step, which is this call with seqs = 0..n-1.
+ * Refused: a slot out of range or given twice, and the qdec_decode_step cases. */
+int qdec_decode_batch(qdec_model* m, const int32_t* seqs, const int32_t* tokens, int32_t n, float* d_logits,
+                      int32_t* d_token_out, float temperature, float top_p, uint64_t seed, uint64_t step,
+                      uint32_t flags, void* stream);
+
+/* Paged KV cache ([P], same table row: a paged cache).  Replaces the
+ * contiguous max_seqs x max_ctx cache by a pool of n_pages pages of page_size
+ * positions shared by all sequences.  Pages are handed out as a sequence grows
+ * (qdec_prefill, decode, qdec_kv_write) and returned by qdec_kv_reset /
+ * qdec_kv_truncate; a call that needs more pages than are free is refused
+ * (status 1) before anything is enqueued.  page_size: a power of two in
+ * [16, 2^20], at least the decode chunk (64 positions at head_dim 128, 32 at
+ * 256, 128 at 64), and large enough that max_ctx / page_size <= 64.  Every
+ * sequence must be empty (status 1 otherwise).  max_ctx still bounds each
+ * sequence.  Results are those of the contiguous cache.  Synchronizes stream. */
+int qdec_kv_paged(qdec_model* m, int32_t page_size, int32_t n_pages, void* stream);
+
+/* The cache's page size (0 = contiguous), pool size and free pages. */
+int qdec_kv_pages(const qdec_model* m, int32_t* page_size, int32_t* n_pages, int32_t* n_free);
 
 /* Forget the cached positions of one sequence (seq = -1: all).  Host-side only;
  * stale KV rows are never read past kv_len. */

@@ -88,6 +88,11 @@ def test_null_handle_calls_are_refused(L):
     assert L.qdec_debug_matmul(3, 4, 4, None, 0, None, 1, None, 0, None) == 1
     assert L.qdec_set_prefill_precision(None, 0) == 1
     assert L.qdec_debug_sample(None, 1, 1, 0.0, 1.0, 0, 0, None, None) == 1
+    seqs = (ctypes.c_int32 * 1)(0)
+    assert L.qdec_decode_batch(None, seqs, None, 1, None, None, 0.0, 1.0, 0, 0, 0, None) == 1
+    assert L.qdec_kv_paged(None, 64, 4, None) == 1
+    a, b, c = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    assert L.qdec_kv_pages(None, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)) == 1
 
 
 def test_binding_range_checks_and_ownership():
