@@ -161,6 +161,9 @@ def bench_batched(cfg, args):
     B, P, N, V = cfg["batch"], cfg["preset_kv"], cfg["decode_steps"], cfg["vocab"]
     tensors = synth.generate(cfg)
     model = qdec.Model(cfg, tensors, max_seqs=B, max_ctx=P + N + 1)
+    if args.kv_page:  # a pool that holds every sequence at its final length
+        per_seq = -(-(P + N + 1) // args.kv_page)
+        model.kv_paged(args.kv_page, B * per_seq)
     for s, l, k, v in synth.preset_kv_all(cfg):
         model.kv_write(s, l, torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev))
     torch.cuda.synchronize()
@@ -207,7 +210,8 @@ def bench_batched(cfg, args):
         "config": {"workload": f"{cfg['name']}: {B} sequences x {P} preset KV positions, {N} decode steps, "
                                f"temperature {temp} (Gumbel-max over Philox4x64-10)"
                                + (f", top-p {top_p}" if top_p < 1 else ""),
-                   "batch": B, "preset_kv": P, "decode_steps": N, "weights": cfg["wtype"]},
+                   "batch": B, "preset_kv": P, "decode_steps": N, "weights": cfg["wtype"],
+                   "kv_page": args.kv_page or None},
         "decode_hbm_frac": round(bytes_dec / (ms / 1e3) / HBM_PEAK, 4),
         "roofline": roofline_entry(kst, cfg.get("key")),
         "kernels": {k: dict(launches=v["launches"], ms=round(v["ms"], 3)) for k, v in sorted(kst.items())},
@@ -248,6 +252,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="c2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kv-page", type=int, default=0,
+                    help="paged KV cache with pages of this many positions (0: contiguous cache)")
     ap.add_argument("--weights", default=None, choices=sorted(WEIGHT_MIXES),
                     help="re-type the workload's matrices, e.g. q4_k_m: Q4_K with Q6_K attn_v, ffn_down and head")
     ap.add_argument("--decode-steps", type=int, default=None, help="override the workload's decode steps (profiling runs)")
@@ -291,6 +297,8 @@ def main():
     T, N, V = cfg["prompt_len"], cfg["decode_steps"], cfg["vocab"]
     prompt = synth.prompt(cfg)
     model = qdec.Model(cfg, tensors, max_seqs=1, max_ctx=T + N + 1)
+    if args.kv_page:
+        model.kv_paged(args.kv_page, -(-(T + N + 1) // args.kv_page))
     model.set_prefill_precision(args.prefill_precision)
     pl = torch.empty(V, dtype=torch.float32, device=dev)
     dl = torch.empty((N, V), dtype=torch.float32, device=dev)
@@ -359,7 +367,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{cfg['name']}, {(args.weights or cfg['wtype']).upper()} weights, prompt {T}, "
                                f"decode {N} greedy, batch 1",
-                   "prompt": T, "decode_steps": N, "batch": 1, "weights": args.weights or cfg["wtype"]},
+                   "prompt": T, "decode_steps": N, "batch": 1, "weights": args.weights or cfg["wtype"],
+                   "kv_page": args.kv_page or None},
         "prefill_tokens_per_s": round(pre_tok_s, 1),
         "prefill_mfma_util": round(float(mfma_util), 4),
         "prefill_precision": args.prefill_precision,
