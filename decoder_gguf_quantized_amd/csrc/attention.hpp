@@ -478,4 +478,157 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
   }
 }
 
+// ------------------------------------------------------------ prefill attention on the matrix cores
+// The same online softmax as attn_prefill_kernel, with both products on
+// V_MFMA_F32_32X32X2_F32 (f32 operands, f32 accumulation).  Workgroup = 32
+// queries x one query head; its four waves take the 32-key tiles of the
+// queries' key range in turn and merge their (max, sum, output) at the end.
+//
+// Per tile the wave computes S^T = K Q^T (keys as rows, queries as columns),
+// contracting over dims in the order c(t, h) = h * HD/2 + t (lane half h,
+// step t), so each lane streams half of its key's row and keeps half of its
+// query's row in registers.  The D layout of S^T puts query j in lanes j and
+// j + 32 and keys 8(r/4) + 4h + r%4 in register r of lane half h; taking the
+// P V contraction over keys in exactly that order, register t of P^T is the B
+// operand of step t of O^T = V^T P^T, so the probabilities never move.  The A
+// operand of that step is V[key][32 b + lane%32]: 32 consecutive floats of a
+// value row per half-wave.  Scores are in the log2 domain (q scaled by
+// log2(e)/sqrt(hd)); masked keys get probability 0.
+template <int HD>
+__global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnPrefillArgs a) {
+  constexpr int HH = HD / 2;  // contraction steps of S^T (two dims per step)
+  constexpr int NB = HD / 32; // 32-dim blocks of the output
+  __shared__ float sm_o[3][NB][16][64];
+  __shared__ float sm_ml[3][2][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 31, lk = lane >> 5;
+  const int q0 = (int)blockIdx.x * 32, h = (int)blockIdx.y, g = h / (a.nq / a.nkv);
+  const int tq = q0 + li;  // this lane's query (token index)
+  const bool q_ok = tq < a.T;
+  const int p = a.pos0 + tq;
+  const int tlast = min(a.T, q0 + 32) - 1;
+  const int kmax = a.pos0 + tlast;
+  const int kmin = a.window > 0 ? max(0, a.pos0 + q0 - a.window + 1) : 0;
+  const int kt0 = kmin & ~31;
+  const int ntile = (kmax - kt0) / 32 + 1;
+
+  float q[HH];
+  {
+    const float4* qp = reinterpret_cast<const float4*>(a.q + (size_t)(q_ok ? tq : 0) * a.nq * HD + (size_t)h * HD +
+                                                       lk * HH);
+#pragma unroll
+    for (int e = 0; e < HH / 4; ++e) {
+      const float4 v = qp[e];
+      q[4 * e + 0] = v.x * a.scale_log2;
+      q[4 * e + 1] = v.y * a.scale_log2;
+      q[4 * e + 2] = v.z * a.scale_log2;
+      q[4 * e + 3] = v.w * a.scale_log2;
+    }
+  }
+  f32x16 o[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[b][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int it = wave; it < ntile; it += 4) {
+    const int key0 = kt0 + 32 * it;
+    // S^T = K Q^T: lane (li, lk) supplies K[key0 + li][lk * HH + t]
+    f32x16 sacc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+    {
+      const int kr = min(key0 + li, kmax);
+      const float4* kp = reinterpret_cast<const float4*>(a.kc + kv_row(a.map, a.nkv, a.ctx, a.seq, g, kr) * HD +
+                                                         lk * HH);
+#pragma unroll
+      for (int e = 0; e < HH / 4; ++e) {
+        const float4 kv = kp[e];
+        sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.x, q[4 * e + 0], sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.y, q[4 * e + 1], sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.z, q[4 * e + 2], sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.w, q[4 * e + 3], sacc, 0, 0, 0);
+      }
+    }
+    // online softmax of query li over the tile's keys (16 here, 16 in lane ^ 32)
+    float pr[16];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = key0 + 8 * (r >> 2) + 4 * lk + (r & 3);
+      const bool ok = q_ok && key <= p && (a.window == 0 || key > p - a.window);
+      pr[r] = ok ? sacc[r] : -INFINITY;
+      mt = fmaxf(mt, pr[r]);
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float mn = fmaxf(m_run, mt);
+    const float corr = mn == -INFINITY ? 1.f : exp2f(m_run - mn);
+    float ps = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      pr[r] = pr[r] == -INFINITY ? 0.f : exp2f(pr[r] - mn);
+      ps += pr[r];
+    }
+    ps += __shfl_xor(ps, 32);
+    l_run = l_run * corr + ps;
+    m_run = mn;
+    // O^T = V^T P^T: step t contracts keys 8(t/4) + 4h + t%4 (lane half h)
+    int vrow[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+      vrow[t] = (int)kv_row(a.map, a.nkv, a.ctx, a.seq, g, min(key0 + 8 * (t >> 2) + 4 * lk + (t & 3), kmax));
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[b][r] *= corr;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const float vv = a.vc[(size_t)vrow[t] * HD + 32 * b + li];
+        o[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv, pr[t], o[b], 0, 0, 0);
+      }
+    }
+  }
+  // merge the four waves' partial results into wave 0
+  if (wave > 0) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sm_o[wave - 1][b][r][lane] = o[b][r];
+    sm_ml[wave - 1][0][lane] = m_run;
+    sm_ml[wave - 1][1][lane] = l_run;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float M = m_run;
+#pragma unroll
+  for (int w = 0; w < 3; ++w) M = fmaxf(M, sm_ml[w][0][lane]);
+  const float w0 = M == -INFINITY ? 0.f : exp2f(m_run - M);
+  float L = l_run * w0;
+  float ww[3];
+#pragma unroll
+  for (int w = 0; w < 3; ++w) {
+    ww[w] = M == -INFINITY ? 0.f : exp2f(sm_ml[w][0][lane] - M);
+    L += ww[w] * sm_ml[w][1][lane];
+  }
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  if (!q_ok) return;
+  float* orow = a.out + (size_t)tq * a.nq * HD + (size_t)h * HD;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * r4 + e;
+        float acc = o[b][r] * w0;
+#pragma unroll
+        for (int w = 0; w < 3; ++w) acc += ww[w] * sm_o[w][b][r][lane];
+        v[e] = acc * inv;
+      }
+      *reinterpret_cast<float4*>(orow + 32 * b + 8 * r4 + 4 * lk) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+  }
+}
+
 }  // namespace qd

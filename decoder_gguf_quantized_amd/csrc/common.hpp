@@ -10,6 +10,9 @@ namespace qd {
 
 constexpr int kWave = 64;
 
+// Accumulator of a 32 x 32 MFMA tile (16 floats per lane).
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
 // ggml type ids.  K-quant tensors are repacked at load into the 32-value block
 // layouts of the legacy types with exact f32 scales:
 //   Q4_K: Q4_0's nibble layout per 32-value sub-block, and a float2 (scale,

@@ -20,7 +20,6 @@
 
 namespace qd {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 struct GemmArgs {
   const uint8_t* qs;    // weights, same layout as GemvArgs
