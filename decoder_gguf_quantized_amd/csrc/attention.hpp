@@ -498,7 +498,8 @@ template <int HD>
 __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnPrefillArgs a) {
   constexpr int HH = HD / 2;  // contraction steps of S^T (two dims per step)
   constexpr int NB = HD / 32; // 32-dim blocks of the output
-  __shared__ float sm_o[3][NB][16][64];
+  constexpr int MB = NB < 4 ? NB : 4;  // blocks per merge pass (48 KB of LDS)
+  __shared__ float sm_o[3][MB][16][64];
   __shared__ float sm_ml[3][2][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 31, lk = lane >> 5;
   const int q0 = (int)blockIdx.x * 32, h = (int)blockIdx.y, g = h / (a.nq / a.nkv);
@@ -533,6 +534,23 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnPrefillArgs 
 
   for (int it = wave; it < ntile; it += 4) {
     const int key0 = kt0 + 32 * it;
+    // rows of the tile's values for O^T = V^T P^T: step t contracts keys
+    // 8(t/4) + 4h + t%4 (lane half h).  Up to head_dim 128 the values are
+    // requested here, before the scores (which they do not depend on), so
+    // their latency overlaps the first product; at 256 that would not fit the
+    // registers and they are requested block by block below.
+    size_t vrow[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+      vrow[t] = kv_row(a.map, a.nkv, a.ctx, a.seq, g, min(key0 + 8 * (t >> 2) + 4 * lk + (t & 3), kmax));
+    constexpr bool kEarlyV = HD <= 128;
+    float vv[kEarlyV ? NB : 1][16];
+    if constexpr (kEarlyV) {
+#pragma unroll
+      for (int t = 0; t < 16; ++t)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) vv[b][t] = a.vc[vrow[t] * HD + 32 * b + li];
+    }
     // S^T = K Q^T: lane (li, lk) supplies K[key0 + li][lk * HH + t]
     f32x16 sacc;
 #pragma unroll
@@ -561,44 +579,47 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnPrefillArgs 
       mt = fmaxf(mt, pr[r]);
     }
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float mn = fmaxf(m_run, mt);
-    const float corr = mn == -INFINITY ? 1.f : exp2f(m_run - mn);
+    // lazy rescale: the reference max moves only when a score exceeds it by
+    // more than 8 (probabilities stay below 2^8, exact in f32 either way), so
+    // the output accumulators are rescaled on few tiles, and only when some
+    // lane of the wave needs it
+    float corr = 1.f;
+    if (m_run == -INFINITY) {
+      m_run = mt;  // first scores of this query: nothing accumulated yet
+    } else if (mt > m_run + 8.f) {
+      corr = exp2f(m_run - mt);
+      m_run = mt;
+    }
+    const bool rescale = __any(corr != 1.f);
     float ps = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      pr[r] = pr[r] == -INFINITY ? 0.f : exp2f(pr[r] - mn);
+      pr[r] = pr[r] == -INFINITY ? 0.f : exp2f(pr[r] - m_run);
       ps += pr[r];
     }
     ps += __shfl_xor(ps, 32);
     l_run = l_run * corr + ps;
-    m_run = mn;
-    // O^T = V^T P^T: step t contracts keys 8(t/4) + 4h + t%4 (lane half h)
-    int vrow[16];
-#pragma unroll
-    for (int t = 0; t < 16; ++t)
-      vrow[t] = (int)kv_row(a.map, a.nkv, a.ctx, a.seq, g, min(key0 + 8 * (t >> 2) + 4 * lk + (t & 3), kmax));
+    // O^T = V^T P^T
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
+      if (rescale) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[b][r] *= corr;
+        for (int r = 0; r < 16; ++r) o[b][r] *= corr;
+      }
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
-        const float vv = a.vc[(size_t)vrow[t] * HD + 32 * b + li];
-        o[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv, pr[t], o[b], 0, 0, 0);
+        const float v = kEarlyV ? vv[kEarlyV ? b : 0][t] : a.vc[vrow[t] * HD + 32 * b + li];
+        o[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(v, pr[t], o[b], 0, 0, 0);
       }
     }
   }
-  // merge the four waves' partial results into wave 0
+  // merge the four waves' partial results into wave 0 (output blocks in
+  // passes of MB, so the exchange fits in LDS at every head_dim)
   if (wave > 0) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sm_o[wave - 1][b][r][lane] = o[b][r];
     sm_ml[wave - 1][0][lane] = m_run;
     sm_ml[wave - 1][1][lane] = l_run;
   }
   __syncthreads();
-  if (wave != 0) return;
   float M = m_run;
 #pragma unroll
   for (int w = 0; w < 3; ++w) M = fmaxf(M, sm_ml[w][0][lane]);
@@ -611,23 +632,35 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnPrefillArgs 
     L += ww[w] * sm_ml[w][1][lane];
   }
   const float inv = L > 0.f ? 1.0f / L : 0.f;
-  if (!q_ok) return;
   float* orow = a.out + (size_t)tq * a.nq * HD + (size_t)h * HD;
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
+  for (int b0 = 0; b0 < NB; b0 += MB) {
+    if (wave > 0) {
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      float v[4];
+      for (int b = 0; b < MB; ++b)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * r4 + e;
-        float acc = o[b][r] * w0;
-#pragma unroll
-        for (int w = 0; w < 3; ++w) acc += ww[w] * sm_o[w][b][r][lane];
-        v[e] = acc * inv;
-      }
-      *reinterpret_cast<float4*>(orow + 32 * b + 8 * r4 + 4 * lk) = make_float4(v[0], v[1], v[2], v[3]);
+        for (int r = 0; r < 16; ++r) sm_o[wave - 1][b][r][lane] = o[b0 + b][r];
     }
+    __syncthreads();
+    if (wave == 0 && q_ok) {
+#pragma unroll
+      for (int b = 0; b < MB; ++b) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * r4 + e;
+            float acc = o[b0 + b][r] * w0;
+#pragma unroll
+            for (int w = 0; w < 3; ++w) acc += ww[w] * sm_o[w][b][r][lane];
+            v[e] = acc * inv;
+          }
+          *reinterpret_cast<float4*>(orow + 32 * (b0 + b) + 8 * r4 + 4 * lk) = make_float4(v[0], v[1], v[2], v[3]);
+        }
+      }
+    }
+    __syncthreads();
   }
 }
 

@@ -323,7 +323,10 @@ void gemm(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, 
   if (prec < 0) prec = m ? m->prefill_prec : QDEC_PREFILL_F32;
   // few 64 x 128 tiles for the CUs: the f32 K-split tile below is faster there
   const bool few = !pair && (size_t)grid.x * grid.y < 512 && w.nblk >= 8;
-  if (prec != QDEC_PREFILL_F32 && (w.type == kQ8_0 || w.type == kQ4_0) && !few) {
+  // the bf16 tile keeps the wide shape down to one 64 x 128 tile per CU (its
+  // per-CU rate is many times the f32 tile's); below that the f32 K-split wins
+  const bool few_bf16 = !pair && (size_t)grid.x * grid.y < 256 && w.nblk >= 8;
+  if (prec != QDEC_PREFILL_F32 && (w.type == kQ8_0 || w.type == kQ4_0) && !few_bf16) {
     const int nt = prec == QDEC_PREFILL_BF16X3 ? 3 : 1;
     const double bytes = w.gguf_bytes + (double)T * w.nblk * 32 * 4 + (double)T * (pair ? w.rows / 2 : w.rows) * 4;
     // flops: the algorithmic 2 T N K (each term's products are extra MFMA work)
@@ -408,10 +411,11 @@ void attention_prefill(qdec_model* m, hipStream_t st, int l, int seq, int T, int
            4.0 * hd * c.n_head * pairs);
   // head_dim 64 / 128: the matrix-core kernel (32 queries per workgroup; its
   // key rows are 32-bit indices); 256 keeps the VALU kernel (registers)
-  if (hd != 256 && m->kv_layer / hd < (size_t)INT32_MAX) {
+  if (m->kv_layer / hd < (size_t)INT32_MAX) {
     dim3 grid((T + 31) / 32, c.n_head);
     if (hd == 64) qlaunch(attn_prefill_mfma_kernel<64>, grid, 256, 0, st, a);
-    else qlaunch(attn_prefill_mfma_kernel<128>, grid, 256, 0, st, a);
+    else if (hd == 128) qlaunch(attn_prefill_mfma_kernel<128>, grid, 256, 0, st, a);
+    else qlaunch(attn_prefill_mfma_kernel<256>, grid, 256, 0, st, a);
     return;
   }
   const int QT = 256 / (hd / 8);

@@ -213,6 +213,9 @@ MATMUL_CASES = [
     (synth.T_Q4_K, 300, 512, 17), (synth.T_Q4_K, 4224, 256, 1000),
     (synth.T_Q6_K, 4096, 1024, 1), (synth.T_Q6_K, 257, 1536, 16), (synth.T_Q6_K, 130, 14336, 2),
     (synth.T_Q6_K, 4100, 2048, 3), (synth.T_Q6_K, 1030, 1024, 97), (synth.T_Q6_K, 4100, 512, 1030),
+    # 256..511 tiles of 64 x 128: the f32 path takes the K-split tile, the bf16
+    # paths the wide bf16 tile
+    (synth.T_Q8_0, 2048, 512, 1000), (synth.T_Q4_0, 2304, 288, 900),
 ]
 
 
