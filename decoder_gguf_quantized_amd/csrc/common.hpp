@@ -14,10 +14,13 @@ constexpr int kWave = 64;
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // ggml type ids.  K-quant tensors are repacked at load into the 32-value block
-// layouts of the legacy types with exact f32 scales:
-//   Q4_K: Q4_0's nibble layout per 32-value sub-block, and a float2 (scale,
-//         min) per sub-block, w = scale * n - min (n the raw nibble);
-//   Q6_K: Q8_0's int8 layout (q - 32), and an f32 scale per 16 values.
+// layouts of the legacy types; their scales stay in the file's precision:
+//   Q4_K: Q4_0's nibble layout per 32-value sub-block; per sub-block a u16
+//         (6-bit scale sc | 6-bit min m << 8) and per 256-value super-block a
+//         u32 (fp16 d | fp16 dmin << 16); w = (d sc) n - (dmin m);
+//   Q6_K: Q8_0's int8 layout (q - 32); per 16 values an int8 scale and per
+//         super-block a u32 holding fp16 d; w = (d scale) q.
+// The products d sc, dmin m, d scale are exact in f32.
 constexpr int kF32 = 0;
 constexpr int kQ4_0 = 2;
 constexpr int kQ8_0 = 8;
@@ -101,6 +104,18 @@ QD_DEV float4 load_nt(const float4* p) {
 }
 QD_DEV float load_half_nt(const uint16_t* p) { return half_bits_to_float(__builtin_nontemporal_load(p)); }
 QD_DEV float load_nt(const float* p) { return __builtin_nontemporal_load(p); }
+QD_DEV uint32_t load_nt(const uint32_t* p) { return __builtin_nontemporal_load(p); }
+QD_DEV uint32_t load_nt(const uint16_t* p) { return __builtin_nontemporal_load(p); }
+QD_DEV uint32_t load_nt(const int8_t* p) { return (uint32_t)(int32_t)__builtin_nontemporal_load(p); }
+
+// K-quant scale pairs from their packed words: Q4_K (scale, min) of a
+// sub-block from sm = sc | m << 8 and sd = d | dmin << 16; Q6_K scale from an
+// int8 (sign-extended in sc) and sd = d.
+QD_DEV float q4k_scale(uint32_t sm, uint32_t sd) { return half_bits_to_float((uint16_t)sd) * (float)(sm & 0xffu); }
+QD_DEV float q4k_min(uint32_t sm, uint32_t sd) {
+  return half_bits_to_float((uint16_t)(sd >> 16)) * (float)((sm >> 8) & 0xffu);
+}
+QD_DEV float q6k_scale(uint32_t sc, uint32_t sd) { return half_bits_to_float((uint16_t)sd) * (float)(int32_t)sc; }
 typedef float qd_f32x2 __attribute__((ext_vector_type(2)));
 QD_DEV float2 load_nt(const float2* p) {
   const qd_f32x2 v = __builtin_nontemporal_load(reinterpret_cast<const qd_f32x2*>(p));

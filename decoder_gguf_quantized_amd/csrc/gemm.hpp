@@ -31,6 +31,7 @@ struct GemmArgs {
   int T;
   float* y;             // [T][ldy]
   int ldy;
+  const uint32_t* sd;   // K-quant super-block scales (as GemvArgs)
 };
 
 template <int QT, int MODE>
@@ -50,6 +51,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
   uint4 wq;        // int8 layouts: 16 int8; F32 uses wf[4]; nibble layouts use the low 8 bytes
   float4 wf[4];
   float wd = 0.f, wmin = 0.f;  // block scale (Q6_K: of this thread's 16 values); Q4_K min
+  uint32_t wks = 0, wkd = 0;   // K-quants: raw scale words, decoded when stored
   const int brow = tid >> 1, bhalf = tid & 1;
   const bool brow_ok = n0 + brow < a.rows;
 
@@ -65,8 +67,12 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
       size_t r = n0 + brow;
       if constexpr (int8_layout(QT)) {
         wq = *reinterpret_cast<const uint4*>(a.qs + r * kp + kb * BK + 16 * bhalf);
-        if constexpr (QT == kQ8_0) wd = load_half(a.d + r * a.nblk + kb);
-        else wd = reinterpret_cast<const float*>(a.d)[r * 2 * a.nblk + 2 * kb + bhalf];
+        if constexpr (QT == kQ8_0) {
+          wd = load_half(a.d + r * a.nblk + kb);
+        } else {
+          wks = (uint32_t)(int32_t)reinterpret_cast<const int8_t*>(a.d)[r * 2 * a.nblk + 2 * kb + bhalf];
+          wkd = a.sd[r * (a.nblk >> 3) + (kb >> 3)];
+        }
       } else if constexpr (nibble_layout(QT)) {
         uint2 v = *reinterpret_cast<const uint2*>(a.qs + (r * a.nblk + kb) * 16 + 8 * bhalf);
         wq.x = v.x;
@@ -74,9 +80,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
         if constexpr (QT == kQ4_0) {
           wd = load_half(a.d + r * a.nblk + kb);
         } else {
-          const float2 sm = reinterpret_cast<const float2*>(a.d)[r * a.nblk + kb];
-          wd = sm.x;
-          wmin = sm.y;
+          wks = a.d[r * a.nblk + kb];
+          wkd = a.sd[r * (a.nblk >> 3) + (kb >> 3)];
         }
       } else {
         const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.qs) + r * kp + kb * BK + 16 * bhalf);
@@ -94,6 +99,12 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
       As[buf][4 * kq + 1][row] = xa[i].y;
       As[buf][4 * kq + 2][row] = xa[i].z;
       As[buf][4 * kq + 3][row] = xa[i].w;
+    }
+    if constexpr (QT == kQ4_K) {
+      wd = q4k_scale(wks, wkd);
+      wmin = q4k_min(wks, wkd);
+    } else if constexpr (QT == kQ6_K) {
+      wd = q6k_scale(wks, wkd);
     }
     if constexpr (int8_layout(QT)) {
       uint32_t w4[4] = {wq.x, wq.y, wq.z, wq.w};
@@ -205,6 +216,7 @@ __global__ __launch_bounds__(256, 1) void gemm_ksplit_kernel(GemmArgs a) {
   uint4 wq[2];
   float4 wf[8];
   float wd = 0.f, wd2 = 0.f, wmin = 0.f;  // scale (Q6_K: of values 0..15, wd2 of 16..31); Q4_K min
+  uint32_t wks = 0, wkd = 0;              // K-quants: raw scale words, decoded when stored
   const int brow = tid >> 2, bblk = tid & 3;
   const bool brow_ok = n0 + brow < a.rows;
 
@@ -225,19 +237,17 @@ __global__ __launch_bounds__(256, 1) void gemm_ksplit_kernel(GemmArgs a) {
         wq[1] = p[1];
         if constexpr (QT == kQ8_0) {
           wd = wd2 = load_half(a.d + r * a.nblk + kb);
-        } else {
-          const float2 s2 = reinterpret_cast<const float2*>(a.d)[r * a.nblk + kb];
-          wd = s2.x;
-          wd2 = s2.y;
+        } else {  // the two int8 scales of the block's 16-value halves
+          wks = a.d[r * a.nblk + kb];
+          wkd = a.sd[r * (a.nblk >> 3) + (kb >> 3)];
         }
       } else if constexpr (nibble_layout(QT)) {
         wq[0] = *reinterpret_cast<const uint4*>(a.qs + (r * a.nblk + kb) * 16);
         if constexpr (QT == kQ4_0) {
           wd = load_half(a.d + r * a.nblk + kb);
         } else {
-          const float2 sm = reinterpret_cast<const float2*>(a.d)[r * a.nblk + kb];
-          wd = sm.x;
-          wmin = sm.y;
+          wks = a.d[r * a.nblk + kb];
+          wkd = a.sd[r * (a.nblk >> 3) + (kb >> 3)];
         }
       } else {
         const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.qs) + r * kp + kb * 32);
@@ -247,6 +257,7 @@ __global__ __launch_bounds__(256, 1) void gemm_ksplit_kernel(GemmArgs a) {
     } else {
       wq[0] = wq[1] = make_uint4(0, 0, 0, 0);
       wd = wd2 = wmin = 0.f;
+      wks = wkd = 0;
 #pragma unroll
       for (int i = 0; i < 8; ++i) wf[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
@@ -263,6 +274,13 @@ __global__ __launch_bounds__(256, 1) void gemm_ksplit_kernel(GemmArgs a) {
       As[buf][4 * kq + 3][c] = xa[i].w;
     }
     const int kk = bblk * 32, bc = brow ^ (8 * bblk);
+    if constexpr (QT == kQ4_K) {
+      wd = q4k_scale(wks, wkd);
+      wmin = q4k_min(wks, wkd);
+    } else if constexpr (QT == kQ6_K) {
+      wd = q6k_scale((uint32_t)(int32_t)(int8_t)(wks & 0xffu), wkd);
+      wd2 = q6k_scale((uint32_t)(int32_t)(int8_t)(wks >> 8), wkd);
+    }
     if constexpr (int8_layout(QT)) {
       const uint32_t w8[8] = {wq[0].x, wq[0].y, wq[0].z, wq[0].w, wq[1].x, wq[1].y, wq[1].z, wq[1].w};
 #pragma unroll

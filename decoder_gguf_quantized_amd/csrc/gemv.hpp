@@ -52,6 +52,8 @@ struct GemvArgs {
   const float* res_w;
   float* res_out;
   const float* bias;     // store mode: y[n] += bias[n] (qwen2's q/k/v bias adds), or null
+  const uint32_t* sd;    // K-quants: super-block scales [rows][nblk / 8]; `d` then holds the
+                         // per-sub-block words (Q4_K u16, Q6_K int8 per 16 values)
 };
 
 QD_DEV float act_silu(float g) { return g / (1.0f + expf(-g)); }
@@ -220,7 +222,7 @@ template <int QT, int R, int U>
 struct WRegs {
   uint4 w[R][U];
   float d[R][U];
-  float m[R][U];  // Q4_K sub-block mins (unused, and optimised away, for the other types)
+  uint32_t ks[R][U], kd[R][U];  // K-quants: raw scale words, decoded when used (optimised away otherwise)
 };
 
 // Rows of group `grp`: R consecutive rows, or for the pair modes R/2 outputs,
@@ -262,16 +264,14 @@ QD_DEV void gemv_load(const GemvArgs& a, const int (&r)[R], int base, int lane, 
         W.d[i][k] = load_half_nt(rd + uc);
       } else if constexpr (QT == kQ4_K) {
         const uint8_t* rq = a.qs + (size_t)r[i] * a.nblk * 16;
-        const float2* rs = reinterpret_cast<const float2*>(a.d) + (size_t)r[i] * a.nblk;
         W.w[i][k] = load_nt(reinterpret_cast<const uint4*>(rq + uc * 16u));
-        const float2 sm = load_nt(rs + uc);
-        W.d[i][k] = sm.x;
-        W.m[i][k] = sm.y;
+        W.ks[i][k] = load_nt(a.d + (size_t)r[i] * a.nblk + uc);
+        W.kd[i][k] = load_nt(a.sd + (size_t)r[i] * (a.nblk >> 3) + (uc >> 3));
       } else if constexpr (QT == kQ6_K) {
         const uint8_t* rq = a.qs + (size_t)r[i] * kp;
-        const float* rs = reinterpret_cast<const float*>(a.d) + (size_t)r[i] * 2 * a.nblk;
         W.w[i][k] = load_nt(reinterpret_cast<const uint4*>(rq + uc * 16u));
-        W.d[i][k] = load_nt(rs + uc);
+        W.ks[i][k] = load_nt(reinterpret_cast<const int8_t*>(a.d) + (size_t)r[i] * 2 * a.nblk + uc);
+        W.kd[i][k] = load_nt(a.sd + (size_t)r[i] * (a.nblk >> 3) + (uc >> 4));
       } else {
         const uint8_t* rq = a.qs + (size_t)r[i] * kp * 4;
         W.w[i][k] = load_nt(reinterpret_cast<const uint4*>(rq + uc * 16u));
@@ -316,7 +316,11 @@ QD_DEV void gemv_compute(const float4* xs4, const float* xsum, int kp, int nblk,
       float4 xv[NV];
 #pragma unroll
       for (int i = 0; i < NV; ++i) xv[i] = xs4[(mi * NV + i) * nunits + u];
-      if constexpr (int8_layout(QT)) {
+      if constexpr (QT == kQ6_K) {
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+          acc[i][mi] += q6k_scale(W.ks[i][k], W.kd[i][k]) * dot16_q8(W.w[i][k], xv[0], xv[1], xv[2], xv[3]);
+      } else if constexpr (QT == kQ8_0) {
 #pragma unroll
         for (int i = 0; i < R; ++i) acc[i][mi] += W.d[i][k] * dot16_q8(W.w[i][k], xv[0], xv[1], xv[2], xv[3]);
       } else if constexpr (QT == kQ4_0) {
@@ -326,7 +330,9 @@ QD_DEV void gemv_compute(const float4* xs4, const float* xsum, int kp, int nblk,
       } else if constexpr (QT == kQ4_K) {
         const float xs = xsum[mi * nblk + u];
 #pragma unroll
-        for (int i = 0; i < R; ++i) acc[i][mi] += W.d[i][k] * dot32_q4_raw4(W.w[i][k], xv) - W.m[i][k] * xs;
+        for (int i = 0; i < R; ++i)
+          acc[i][mi] += q4k_scale(W.ks[i][k], W.kd[i][k]) * dot32_q4_raw4(W.w[i][k], xv) -
+                        q4k_min(W.ks[i][k], W.kd[i][k]) * xs;
       } else {
 #pragma unroll
         for (int i = 0; i < R; ++i) {

@@ -13,6 +13,7 @@ struct WView {
   const uint16_t* d;
   int type;
   int nblk;
+  const uint32_t* sd;  // K-quant super-block scales
 };
 
 QD_DEV float weight_at(const WView& w, size_t row, int k) {
@@ -26,14 +27,15 @@ QD_DEV float weight_at(const WView& w, size_t row, int k) {
     uint32_t byte = w.qs[(row * w.nblk + b) * 16 + (j & 15)];
     uint32_t n = j < 16 ? (byte & 15u) : (byte >> 4);
     if (w.type == kQ4_K) {  // scale * n - min, rounded once
-      const float2 sm = reinterpret_cast<const float2*>(w.d)[row * w.nblk + b];
-      return fmaf(sm.x, (float)n, -sm.y);
+      const uint32_t sm = w.d[row * w.nblk + b], sd = w.sd[row * (w.nblk >> 3) + (b >> 3)];
+      return fmaf(q4k_scale(sm, sd), (float)n, -q4k_min(sm, sd));
     }
     float d = load_half(w.d + row * w.nblk + b);
     return d * (float)((int)n - 8);
   }
   if (w.type == kQ6_K) {
-    const float s = reinterpret_cast<const float*>(w.d)[row * 2 * w.nblk + (k >> 4)];
+    const uint32_t sc = (uint32_t)(int32_t)reinterpret_cast<const int8_t*>(w.d)[row * 2 * w.nblk + (k >> 4)];
+    const float s = q6k_scale(sc, w.sd[row * (w.nblk >> 3) + (k >> 8)]);
     return s * (float)reinterpret_cast<const int8_t*>(w.qs)[row * kp + k];
   }
   return reinterpret_cast<const float*>(w.qs)[row * kp + k];

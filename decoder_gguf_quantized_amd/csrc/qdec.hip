@@ -48,7 +48,8 @@ struct Mat {
   int type = -1;
   int rows = 0, cols = 0, nblk = 0;
   uint8_t* qs = nullptr;   // quants (or f32 values for F32)
-  uint16_t* d = nullptr;   // fp16 scales
+  uint16_t* d = nullptr;   // fp16 scales (K-quants: per-sub-block scale words)
+  uint32_t* sd = nullptr;  // K-quants: per-super-block scales
   double gguf_bytes = 0;   // bytes of the tensor in GGUF layout (what a step streams)
 };
 
@@ -88,14 +89,6 @@ int64_t tensor_bytes(int t, int64_t rows, int64_t cols) {
   if (t == kF32) return rows * cols * 4;
   if (is_kquant(t)) return rows * (cols / 256) * super_bytes(t);
   return rows * nblocks(cols) * blk_bytes(t);
-}
-
-// IEEE binary16 -> float, exact (for the load-time repack of K-quant scales).
-float half_to_float_host(uint16_t h) {
-  const int e = (h >> 10) & 31, mant = h & 1023;
-  float v = e == 0 ? std::ldexp((float)mant, -24)
-                   : e == 31 ? (mant ? NAN : INFINITY) : std::ldexp((float)(1024 + mant), e - 25);
-  return (h & 0x8000) ? -v : v;
 }
 
 void hipck(hipError_t e, const char* what) {
@@ -303,7 +296,7 @@ void gemv(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, 
     GemvArgs a{w.qs, w.d, w.rows, w.nblk, x + (size_t)r0 * ldx, ldx, norm_w, eps,
                y ? y + (size_t)r0 * ldy : nullptr, ldy, mr, y_ind, (long)r0 * ldy,
                res.add ? res.add + (size_t)r0 * ldx : nullptr, res.add_w,
-               res.out ? res.out + (size_t)r0 * ldx : nullptr, bias};
+               res.out ? res.out + (size_t)r0 * ldx : nullptr, bias, w.sd};
     const size_t lds = per_row * M;
     const double bytes = w.gguf_bytes + (double)mr * kp * 4 + (double)mr * (pair ? w.rows / 2 : w.rows) * 4;
     Timed tm(m, st, gemv_class(w.type), bytes, 2.0 * mr * w.rows * (double)w.cols);
@@ -317,7 +310,7 @@ void gemv(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, 
 // F32 and K-quant weights always take the f32 kernels.
 void gemm(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, int T, float* y, int ldy, int mode,
           int prec = -1) {
-  GemmArgs a{w.qs, w.d, w.rows, w.nblk, x, ldx, T, y, ldy};
+  GemmArgs a{w.qs, w.d, w.rows, w.nblk, x, ldx, T, y, ldy, w.sd};
   dim3 grid((w.rows + 127) / 128, (T + 63) / 64);
   const bool pair = mode == kModePairSilu || mode == kModePairGelu;
   if (prec < 0) prec = m ? m->prefill_prec : QDEC_PREFILL_F32;
@@ -437,7 +430,7 @@ void rope_kv(qdec_model* m, hipStream_t st, int l, int n, int seq0, int pos0, co
 
 void embed(qdec_model* m, hipStream_t st, const int* d_tokens, int n, float* out) {
   const qdec_config& c = m->cfg;
-  EmbedArgs a{WView{m->embd.qs, m->embd.d, m->embd.type, m->embd.nblk}, c.hidden, c.vocab, n, d_tokens, out,
+  EmbedArgs a{WView{m->embd.qs, m->embd.d, m->embd.type, m->embd.nblk, m->embd.sd}, c.hidden, c.vocab, n, d_tokens, out,
               c.hidden, m->err_dev};
   Timed tm(m, st, "embed", (double)n * (m->embd.gguf_bytes / m->embd.rows + c.hidden * 4), 0);
   qlaunch(embed_kernel, n, 256, 0, st, a);
@@ -661,38 +654,46 @@ bool scales_finite(const qdec_tensor& t) {
 // Repack GGUF rows [src_rows][blocks] into (quants, scales) at device row dst_row
 // of a host staging buffer of the fused matrix.
 // K-quant super-blocks are repacked into the 32-value layouts of the legacy
-// types with exact f32 scales (GGUF's public K-quant layouts):
+// types (GGUF's public K-quant layouts), keeping the scales as the file has
+// them, unpacked to whole bytes:
 //   Q4_K (fp16 d, fp16 dmin, 12 bytes of eight 6-bit (scale, min) pairs, 128
 //   quant bytes whose low / high nibbles hold sub-blocks 2c / 2c + 1) -> per
-//   sub-block the Q4_0 nibble order and a float2 (d * sc, dmin * m);
+//   sub-block the Q4_0 nibble order and a u16 sc | m << 8; per super-block a
+//   u32 d | dmin << 16;
 //   Q6_K (128 low-nibble bytes, 64 bytes of 2-bit high parts, 16 int8 scales,
-//   fp16 d) -> int8 q - 32 per value and an f32 d * scale per 16 values.
-// Both scale products are exact in f32 (at most 11 + 8 significant bits).
+//   fp16 d) -> int8 q - 32 per value, the int8 scale per 16 values, and per
+//   super-block a u32 holding d.
+// The kernels form d * sc, dmin * m, d * scale in f32 (exact: at most 11 + 8
+// significant bits).
 struct Stage {
   int type;
   int64_t rows, nblk;
   std::vector<uint8_t> qs;
   std::vector<uint16_t> d;
-  std::vector<float> f;  // K-quants: two floats per 32-value block
+  std::vector<uint8_t> ks;   // K-quants: 2 bytes per 32-value block (Q4_K sc, m; Q6_K two int8 scales)
+  std::vector<uint32_t> sd;  // K-quants: one word per 256-value super-block
   Stage(int t, int64_t r, int64_t nb) : type(t), rows(r), nblk(nb) {
     const bool nib = t == kQ4_0 || t == kQ4_K, i8 = t == kQ8_0 || t == kQ6_K;
     qs.assign((size_t)(nib ? r * nb * 16 : i8 ? r * nb * 32 : r * nb * 32 * 4), 0);
     if (is_quant(t)) d.assign((size_t)(r * nb), 0);
-    if (is_kquant(t)) f.assign((size_t)(2 * r * nb), 0.f);
+    if (is_kquant(t)) {
+      ks.assign((size_t)(2 * r * nb), 0);
+      sd.assign((size_t)(r * (nb / 8)), 0);
+    }
   }
   void put_q4_k(int64_t dst_row, const uint8_t* src, int64_t nsb) {
     for (int64_t sbi = 0; sbi < nsb; ++sbi) {
       const uint8_t* sb = src + sbi * 144;
-      const float dd = half_to_float_host((uint16_t)(sb[0] | sb[1] << 8));
-      const float dm = half_to_float_host((uint16_t)(sb[2] | sb[3] << 8));
+      sd[(size_t)(dst_row * (nblk / 8) + sbi)] =
+          (uint32_t)(sb[0] | sb[1] << 8) | (uint32_t)(sb[2] | sb[3] << 8) << 16;
       const uint8_t* sc = sb + 4;
       const uint8_t* q = sb + 16;
       for (int j = 0; j < 8; ++j) {
         const int scale = j < 4 ? sc[j] & 63 : (sc[j + 4] & 15) | ((sc[j - 4] >> 6) << 4);
         const int mn = j < 4 ? sc[j + 4] & 63 : (sc[j + 4] >> 4) | ((sc[j] >> 6) << 4);
         const int64_t b = dst_row * nblk + sbi * 8 + j;
-        f[(size_t)(2 * b)] = dd * (float)scale;
-        f[(size_t)(2 * b + 1)] = dm * (float)mn;
+        ks[(size_t)(2 * b)] = (uint8_t)scale;
+        ks[(size_t)(2 * b + 1)] = (uint8_t)mn;
         const uint8_t* qc = q + 32 * (j / 2);
         const int sh = 4 * (j & 1);
         for (int i = 0; i < 16; ++i) {
@@ -706,7 +707,7 @@ struct Stage {
     int8_t* out = reinterpret_cast<int8_t*>(qs.data()) + dst_row * nblk * 32;
     for (int64_t sbi = 0; sbi < nsb; ++sbi) {
       const uint8_t* sb = src + sbi * 210;
-      const float dd = half_to_float_host((uint16_t)(sb[208] | sb[209] << 8));
+      sd[(size_t)(dst_row * (nblk / 8) + sbi)] = (uint32_t)(sb[208] | sb[209] << 8);
       for (int h = 0; h < 2; ++h) {
         const uint8_t* ql = sb + 64 * h;
         const uint8_t* qh = sb + 128 + 32 * h;
@@ -718,8 +719,7 @@ struct Stage {
           o[l + 96] = (int8_t)(((ql[l + 32] >> 4) | ((qh[l] >> 6) << 4)) - 32);
         }
       }
-      for (int g = 0; g < 16; ++g)
-        f[(size_t)(dst_row * 2 * nblk + sbi * 16 + g)] = dd * (float)(int8_t)sb[192 + g];
+      for (int g = 0; g < 16; ++g) ks[(size_t)(dst_row * 2 * nblk + sbi * 16 + g)] = sb[192 + g];
     }
   }
   void put_row(int64_t dst_row, const qdec_tensor& t, int64_t src_row) {
@@ -758,10 +758,11 @@ Mat upload(qdec_model* m, const Stage& s, int rows, int cols, double gguf_bytes,
     w.d = m->dalloc<uint16_t>(s.d.size());
     hipck(hipMemcpyAsync(w.d, s.d.data(), s.d.size() * 2, hipMemcpyHostToDevice, st), "upload");
   }
-  if (is_kquant(s.type)) {  // f32 scales, passed to the kernels through the same pointer
-    float* f = m->dalloc<float>(s.f.size());
-    hipck(hipMemcpyAsync(f, s.f.data(), s.f.size() * 4, hipMemcpyHostToDevice, st), "upload");
-    w.d = reinterpret_cast<uint16_t*>(f);
+  if (is_kquant(s.type)) {  // per-sub-block scale words (through d) and super-block scales
+    w.d = m->dalloc<uint16_t>(s.ks.size() / 2);
+    hipck(hipMemcpyAsync(w.d, s.ks.data(), s.ks.size(), hipMemcpyHostToDevice, st), "upload");
+    w.sd = m->dalloc<uint32_t>(s.sd.size());
+    hipck(hipMemcpyAsync(w.sd, s.sd.data(), s.sd.size() * 4, hipMemcpyHostToDevice, st), "upload");
   }
   hipck(hipStreamSynchronize(st), "upload sync");
   return w;
@@ -1497,7 +1498,7 @@ int qdec_debug_dequant(qdec_model* m, const char* name, float* d_out, void* stre
   const NameRef& r = it->second;
   hipStream_t st = (hipStream_t)stream;
   try {
-    DequantArgs a{WView{r.mat->qs, r.mat->d, r.mat->type, r.mat->nblk}, nullptr, r.row_off, r.rows, r.cols, r.pair, d_out};
+    DequantArgs a{WView{r.mat->qs, r.mat->d, r.mat->type, r.mat->nblk, r.mat->sd}, nullptr, r.row_off, r.rows, r.cols, r.pair, d_out};
     Timed tm(m, st, "dequant", 0, 0);
     qlaunch(dequant_kernel, r.rows, 256, 0, st, a);
   } catch (const HipError& e) {
