@@ -60,8 +60,9 @@ enum { QDEC_OK = 0, QDEC_REFUSED = 1, QDEC_INTERNAL = 2 };
  *       them (cols a multiple of 256).  Q4_K: fp16 d, fp16 dmin, eight 6-bit
  *       (scale, min) pairs, w = d*sc*q - dmin*m; Q6_K: 6-bit q, sixteen int8
  *       scales, fp16 d, w = d*scale*(q - 32).  They are repacked at load into
- *       32-value blocks with exact f32 scales (more bytes than the file: 0.75
- *       and 1.25 per weight instead of 0.5625 and 0.8203) and stream as such. */
+ *       32-value blocks that keep the file's scales unpacked to whole bytes
+ *       (0.578 and 1.078 bytes per weight against the file's 0.5625 and
+ *       0.8203) and stream as such. */
 enum { QDEC_T_F32 = 0, QDEC_T_Q4_0 = 2, QDEC_T_Q8_0 = 8, QDEC_T_Q4_K = 12, QDEC_T_Q6_K = 14 };
 
 enum { QDEC_ACT_SILU = 0, QDEC_ACT_GELU_TANH = 1 };
