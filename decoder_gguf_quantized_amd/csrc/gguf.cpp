@@ -30,8 +30,10 @@
 
 #include <algorithm>
 #include <cerrno>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <string>
@@ -414,7 +416,11 @@ ArchDef parse_archdef(const std::string& text) {
     for (size_t k = 0; k < st.args.size(); ++k) {
       if (kinds[k] == 'r' && !is_ident(st.args[k]))
         fail("archdef line %d: '%s' is not a register", line, st.args[k].c_str());
-      if (kinds[k] == 't') st.args[k] = tensor_arg(st.args[k], line);
+      if (kinds[k] == 't') {
+        st.args[k] = tensor_arg(st.args[k], line);
+        if (section != 1 && st.args[k].find("{i}") != std::string::npos)
+          fail("archdef line %d: {i} names a layer only inside the block", line);
+      }
     }
     if (it->second.needs_dst && st.dst.empty()) fail("archdef line %d: %s needs a destination", line, st.op.c_str());
     if (st.dst.empty()) st.dst = st.args[0];
@@ -483,6 +489,51 @@ std::string block_layout(bool bias, bool qkn, bool sandwich, const char* act) {
   std::string d = fn("matmul", {commutative("mul", g, fn("matmul", {h2, w("ffn_up.weight")})), w("ffn_down.weight")});
   if (sandwich) d = fn("rms_norm", {d, w("post_ffw_norm.weight")});
   return commutative("add", x1, d);
+}
+
+// Every name a statement uses must resolve in the file, statements whose
+// results are never used included: a tensor argument (one of its '|'
+// alternatives, in every layer for the block) must be one of the file's
+// tensors, a number argument a head count, a number, or a metadata key of the
+// architecture.
+void check_names(const ArchDef& d, const File& f, int32_t n_layer) {
+  auto is_number = [](const std::string& s) {
+    char* end = nullptr;
+    errno = 0;
+    const double v = strtod(s.c_str(), &end);
+    return !s.empty() && end && !*end && errno == 0 && std::isfinite(v);
+  };
+  for (int sec = 0; sec < 3; ++sec)
+    for (const Stmt& st : d.sec[sec]) {
+      const char* kinds = op_table().at(st.op).kinds;
+      for (size_t k = 0; k < st.args.size(); ++k) {
+        const std::string& a = st.args[k];
+        if (kinds[k] == 'n' && a != "head_count" && a != "head_count_kv" && !is_number(a) &&
+            !find_meta(f, d.arch + "." + a))
+          fail("archdef line %d: '%s' is neither a number nor a metadata key of the file", st.line, a.c_str());
+        if (kinds[k] != 't') continue;
+        const bool per_layer = a.find("{i}") != std::string::npos;
+        // distinct layers give distinct names, so a missing one is met within
+        // (number of tensors + 1) layers
+        for (int32_t i = 0; i < (per_layer ? n_layer : 1); ++i) {
+          bool present = false;
+          size_t start = 0;
+          while (!present) {
+            const size_t bar = a.find('|', start);
+            std::string name = a.substr(start, bar == std::string::npos ? std::string::npos : bar - start);
+            for (size_t at; (at = name.find("{i}")) != std::string::npos;) name.replace(at, 3, std::to_string(i));
+            present = f.by_name.count(name) > 0;
+            if (bar == std::string::npos) break;
+            start = bar + 1;
+          }
+          if (!present) {
+            std::string shown = a;
+            for (size_t at; (at = shown.find("{i}")) != std::string::npos;) shown.replace(at, 3, std::to_string(i));
+            fail("archdef line %d: tensor '%s' is not in the file", st.line, shown.c_str());
+          }
+        }
+      }
+    }
 }
 
 enum Head { kHeadEither, kHeadOutput, kHeadEmbd };
@@ -580,6 +631,7 @@ Compiled compile(const ArchDef& d, const File& f) {
   c.vocab = (int32_t)te.ne[1];
   if (r.head == kHeadOutput && !f.by_name.count("output.weight"))
     fail("archdef: the head names output.weight, which the file lacks");
+  check_names(d, f, c.n_layer);
   return r;
 }
 

@@ -142,7 +142,12 @@ int qdec_load_weights(const qdec_config* cfg, const qdec_tensor* tensors, int32_
  * gelu_tanh gate, optionally with q/k/v biases, per-head q/k norms before RoPE,
  * and sandwich norms; the prologue must be x = embed(token_embd.weight) and the
  * epilogue logits = matmul(last(rms_norm(x, output_norm.weight)), output.weight
- * | token_embd.weight).  Anything else is refused with the reason.
+ * | token_embd.weight).  Anything else is refused with the reason.  Every name
+ * a statement uses must resolve, in statements whose results are never used
+ * too: a tensor (one of its `|` alternatives; for the block, in every layer)
+ * must be in the file, a number argument must be head_count, head_count_kv, a
+ * finite number or an <arch>. metadata key of the file, and {i} may appear only
+ * in the block.
  * Shape from the metadata of the definition's arch: <arch>.block_count,
  * .embedding_length, .feed_forward_length, .attention.head_count,
  * .attention.head_count_kv (default head_count), .attention.key_length
@@ -158,8 +163,9 @@ int qdec_gguf_config(const char* path, const char* archdef, qdec_config* out);
 
 /* qdec_gguf_config, then qdec_load_weights over the tensors the compiled
  * layout reads, borrowed from a read-only mapping of the file until the weights
- * are on the device.  Tensor types F32, Q4_0, Q8_0; a quantized row holds whole
- * 32-value blocks.  Other tensors in the file are ignored. */
+ * are on the device.  Tensor types F32, Q4_0, Q8_0, Q4_K, Q6_K; a quantized row
+ * holds whole blocks (32 values; 256 for the K-quants).  Other tensors in the
+ * file are ignored. */
 int qdec_load_gguf(const char* path, const char* archdef, int32_t max_seqs, int32_t max_ctx, void* stream,
                    qdec_model** out);
 

@@ -209,3 +209,38 @@ def test_missing_file_and_null_arguments(tmp_path):
     L = qdec.lib()
     assert L.qdec_gguf_config(None, None, None) == 1
     assert L.qdec_load_gguf(None, None, 1, 16, None, None) == 1
+
+
+def test_every_name_in_a_definition_must_resolve(files):
+    """Statements whose results are never used are still checked: their
+    tensors must be in the file (in every layer, for the block), their numbers
+    numbers or metadata keys, and {i} appears only in the block."""
+    _, path = files["qwen3"]
+    text = sg.archdef_text("qwen3")
+    dead_missing = text.replace("block\n", "block\n  z = rms_norm(x, blk.{i}.no_such.weight)\n")
+    with pytest.raises(qdec.QdecError, match="'blk.0.no_such.weight' is not in the file"):
+        qdec.gguf_config(path, dead_missing)
+    dead_short = text.replace("block\n", "block\n  z = rms_norm(x, output_norm.weight)\n")
+    assert qdec.gguf_config(path, dead_short) == qdec.gguf_config(path)
+    epi_layer = text.replace("epilogue\n", "epilogue\n  z = rms_norm(x, blk.{i}.attn_norm.weight)\n")
+    with pytest.raises(qdec.QdecError, match=r"\{i\} names a layer only inside the block"):
+        qdec.gguf_config(path, epi_layer)
+    dead_number = text.replace("block\n", "block\n  z = scale(x, no_such_key)\n")
+    with pytest.raises(qdec.QdecError, match="neither a number nor a metadata key"):
+        qdec.gguf_config(path, dead_number)
+    dead_key = text.replace("block\n", "block\n  z = scale(x, block_count)\n  w = scale(x, 0.5)\n")
+    assert qdec.gguf_config(path, dead_key) == qdec.gguf_config(path)
+
+
+def test_block_tensors_resolve_in_every_layer(tmp_path):
+    """A tensor that only layer 0 has fails at layer 1 when the block names it."""
+    cfg = cfg_for("qwen3_hd128_g2")
+    assert cfg["n_layer"] >= 2
+    t = synth.generate(cfg)
+    t["blk.0.extra.weight"] = t["blk.0.attn_norm.weight"]
+    order = [s[0] for s in sg.tensor_specs(cfg)] + ["blk.0.extra.weight"]
+    path = sg.write(str(tmp_path / "x.gguf"), cfg, t, order=order)
+    text = sg.archdef_text("qwen3")
+    assert qdec.gguf_config(path, text) == qdec.gguf_config(path)
+    with pytest.raises(qdec.QdecError, match="'blk.1.extra.weight' is not in the file"):
+        qdec.gguf_config(path, text.replace("block\n", "block\n  z = rms_norm(x, blk.{i}.extra.weight)\n"))
