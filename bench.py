@@ -101,14 +101,17 @@ def cpu_baseline(cfg, tensors, budget_s=20.0):
 
 
 def kernel_sources_hash():
-    """sha256 (first 16 hex) of the HIP sources, to tell whether stored counter
-    readings still describe the kernels being timed."""
+    """sha256 (first 16 hex) of the device sources (csrc/*.hip and *.hpp in
+    name order: the kernels and their launches; the host-only model-file
+    reader is left out), to tell whether stored counter readings still
+    describe the kernels being timed."""
     import glob
     import hashlib
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(ROOT, "decoder_gguf_quantized_amd", "csrc", "*"))):
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        if f.endswith((".hip", ".hpp")):
+            with open(f, "rb") as fh:
+                h.update(fh.read())
     return h.hexdigest()[:16]
 
 
