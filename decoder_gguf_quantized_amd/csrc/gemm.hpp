@@ -21,6 +21,15 @@
 namespace qd {
 
 
+// LDS stages of the f32 tiles.  The next stage's global loads go to registers
+// while the current stage is multiplied, so one LDS buffer (one more barrier
+// per stage) suffices and halves the LDS per workgroup.
+#ifndef QDEC_GEMM_BUFS
+#define QDEC_GEMM_BUFS 1
+#endif
+constexpr int kGemmBufs = QDEC_GEMM_BUFS;
+static_assert(kGemmBufs == 1 || kGemmBufs == 2, "one or two LDS stages");
+
 struct GemmArgs {
   const uint8_t* qs;    // weights, same layout as GemvArgs
   const uint16_t* d;
@@ -38,8 +47,8 @@ template <int QT, int MODE>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
   constexpr int BM = 64, BN = 128, BK = 32;
   constexpr int AP = BM + 4, BP = BN + 4;
-  __shared__ float As[2][BK][AP];
-  __shared__ float Bs[2][BK][BP];
+  __shared__ float As[kGemmBufs][BK][AP];
+  __shared__ float Bs[kGemmBufs][BK][BP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -151,7 +160,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
   __syncthreads();
   const int li = lane & 31, lk = lane >> 5;
   for (int kb = 0; kb < a.nblk; ++kb) {
-    const int buf = kb & 1;
+    const int buf = kGemmBufs == 2 ? kb & 1 : 0;
     if (kb + 1 < a.nblk) load(kb + 1);
 #pragma unroll
     for (int p = 0; p < BK / 2; ++p) {
@@ -161,7 +170,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
       acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b0, acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b1, acc1, 0, 0, 0);
     }
-    if (kb + 1 < a.nblk) store(buf ^ 1);
+    if constexpr (kGemmBufs == 1) __syncthreads();  // every wave is done reading the stage
+    if (kb + 1 < a.nblk) store(kGemmBufs == 2 ? buf ^ 1 : 0);
     __syncthreads();
   }
 
@@ -202,8 +212,8 @@ __global__ __launch_bounds__(256, 1) void gemm_ksplit_kernel(GemmArgs a) {
   // LDS k-major without padding; columns XOR-swizzled so that both the staging
   // writes and the MFMA operand reads of a half-wave hit 32 distinct banks:
   // X[t][k] at As[k][t ^ (k / 4)], W[n][k] at Bs[k][n ^ (8 * (k / 32))].
-  __shared__ float As[2][BK][BM];
-  __shared__ float Bs[2][BK][BN];
+  __shared__ float As[kGemmBufs][BK][BM];
+  __shared__ float Bs[kGemmBufs][BK][BN];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = blockIdx.x * BN, t0 = blockIdx.y * BM;
@@ -321,7 +331,7 @@ __global__ __launch_bounds__(256, 1) void gemm_ksplit_kernel(GemmArgs a) {
   __syncthreads();
   const int li = lane & 31, lk = lane >> 5;
   for (int st = 0; st < nstage; ++st) {
-    const int buf = st & 1;
+    const int buf = kGemmBufs == 2 ? st & 1 : 0;
     if (st + 1 < nstage) load(st + 1);
     const int kw = wave * 32;  // this wave's quant block within the stage
 #pragma unroll
@@ -333,11 +343,13 @@ __global__ __launch_bounds__(256, 1) void gemm_ksplit_kernel(GemmArgs a) {
       acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b0, acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b1, acc1, 0, 0, 0);
     }
-    if (st + 1 < nstage) store(buf ^ 1);
+    if constexpr (kGemmBufs == 1) __syncthreads();  // every wave is done reading the stage
+    if (st + 1 < nstage) store(kGemmBufs == 2 ? buf ^ 1 : 0);
     __syncthreads();
   }
-  // sum the four waves' partial tiles in wave order (reusing the B buffers)
-  float* red = &Bs[0][0][0];  // 4 x [32][64] floats = 32 KB = sizeof(Bs) / 2
+  // sum the four waves' partial tiles in wave order (reusing the B buffer)
+  static_assert(sizeof(Bs) >= 4 * BM * BN * sizeof(float), "reduction buffer");
+  float* red = &Bs[0][0][0];  // 4 x [32][64] floats = 32 KB
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int i = 8 * (r >> 2) + 4 * lk + (r & 3);
