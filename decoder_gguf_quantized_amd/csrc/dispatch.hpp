@@ -116,8 +116,12 @@ void gemm_dispatch(int mode, dim3 grid, hipStream_t st, const GemmArgs& a) {
 
 template <int QT>
 void gemm_ksplit_dispatch(int mode, dim3 grid, hipStream_t st, const GemmArgs& a) {
-  if (mode == kModeAdd) qlaunch(gemm_ksplit_kernel<QT, kModeAdd>, grid, 256, 0, st, a);
-  else qlaunch(gemm_ksplit_kernel<QT, kModeStore>, grid, 256, 0, st, a);
+  switch (mode) {
+    case kModeStore: qlaunch(gemm_ksplit_kernel<QT, kModeStore>, grid, 256, 0, st, a); break;
+    case kModeAdd: qlaunch(gemm_ksplit_kernel<QT, kModeAdd>, grid, 256, 0, st, a); break;
+    case kModePairSilu: qlaunch(gemm_ksplit_kernel<QT, kModePairSilu>, grid, 256, 0, st, a); break;
+    default: qlaunch(gemm_ksplit_kernel<QT, kModePairGelu>, grid, 256, 0, st, a); break;
+  }
 }
 
 template <int QT, int NT>

@@ -205,7 +205,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
 // at the end the four partial tiles are summed through LDS in a fixed order
 // (deterministic).  Four times the workgroups of the 64 x 128 tile for the same
 // problem, for projections with few output rows (O and down at small hidden
-// sizes).  Not used for the gate/up pair mode.
+// sizes, gate/up of short prompts).
 template <int QT, int MODE>
 __global__ __launch_bounds__(256, 1) void gemm_ksplit_kernel(GemmArgs a) {
   constexpr int BM = 32, BN = 64, BK = 128;
@@ -357,15 +357,31 @@ __global__ __launch_bounds__(256, 1) void gemm_ksplit_kernel(GemmArgs a) {
     red[(wave * BM + i) * BN + 32 + li] = acc1[r];
   }
   __syncthreads();
-  for (int e = tid; e < BM * BN; e += 256) {
-    const int i = e / BN, j = e % BN;
-    const float v = ((red[(0 * BM + i) * BN + j] + red[(1 * BM + i) * BN + j]) + red[(2 * BM + i) * BN + j]) +
-                    red[(3 * BM + i) * BN + j];
-    const int t = t0 + i, n = n0 + j;
-    if (t < a.T && n < a.rows) {
-      float* yr = a.y + (size_t)t * a.ldy;
-      if constexpr (MODE == kModeAdd) yr[n] += v;
-      else yr[n] = v;
+  auto sum4 = [&](int i, int j) {
+    return ((red[(0 * BM + i) * BN + j] + red[(1 * BM + i) * BN + j]) + red[(2 * BM + i) * BN + j]) +
+           red[(3 * BM + i) * BN + j];
+  };
+  if constexpr (MODE == kModePairSilu || MODE == kModePairGelu) {
+    // the tile's 64 rows are one (gate 32, up 32) group of the interleaved
+    // layout: outputs n0 / 2 + j, j < 32
+    for (int e = tid; e < BM * 32; e += 256) {
+      const int i = e / 32, j = e % 32;
+      const int t = t0 + i;
+      if (t < a.T && n0 + j + 32 < a.rows) {
+        const float g = sum4(i, j), u = sum4(i, j + 32);
+        a.y[(size_t)t * a.ldy + n0 / 2 + j] = (MODE == kModePairSilu ? act_silu(g) : act_gelu_tanh(g)) * u;
+      }
+    }
+  } else {
+    for (int e = tid; e < BM * BN; e += 256) {
+      const int i = e / BN, j = e % BN;
+      const int t = t0 + i, n = n0 + j;
+      if (t < a.T && n < a.rows) {
+        const float v = sum4(i, j);
+        float* yr = a.y + (size_t)t * a.ldy;
+        if constexpr (MODE == kModeAdd) yr[n] += v;
+        else yr[n] = v;
+      }
     }
   }
 }

@@ -315,7 +315,7 @@ void gemm(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, 
   const bool pair = mode == kModePairSilu || mode == kModePairGelu;
   if (prec < 0) prec = m ? m->prefill_prec : QDEC_PREFILL_F32;
   // few 64 x 128 tiles for the CUs: the f32 K-split tile below is faster there
-  const bool few = !pair && (size_t)grid.x * grid.y < 512 && w.nblk >= 8;
+  const bool few = (size_t)grid.x * grid.y < 512 && w.nblk >= 8;
   // the bf16 tile keeps the wide shape down to one 64 x 128 tile per CU (its
   // per-CU rate is many times the f32 tile's); below that the f32 K-split wins
   const bool few_bf16 = !pair && (size_t)grid.x * grid.y < 256 && w.nblk >= 8;
@@ -332,7 +332,7 @@ void gemm(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, 
   // few 64 x 128 tiles for the CUs: switch to the K-split 32 x 64 tile
   if (few) {
     dim3 g2((w.rows + 63) / 64, (T + 31) / 32);
-    const double bytes = w.gguf_bytes + (double)T * w.nblk * 32 * 4 + (double)T * w.rows * 4;
+    const double bytes = w.gguf_bytes + (double)T * w.nblk * 32 * 4 + (double)T * (pair ? w.rows / 2 : w.rows) * 4;
     Timed tm(m, st, gemm_class(w.type), bytes, 2.0 * T * (double)w.rows * w.cols);
     gemm_type(w.type, kGemmKSplit, mode, g2, st, a);
     return;
