@@ -9,9 +9,9 @@
 // of the tile.
 //
 // Tiling: workgroup tile 64 tokens x 128 weight rows, BK = 32 (one quant block),
-// double-buffered LDS (k-major, so each MFMA operand read is 32 consecutive
-// floats).  Four waves in a 2 x 2 arrangement, each owning 32 tokens x 64 rows as
-// two 32x32 accumulators.  MFMA lane layout (32x32x2 f32): A[i][k] from lane
+// LDS k-major (each MFMA operand read is 32 consecutive columns of one k row).
+// Four waves in a 2 x 2 arrangement, each owning 32 tokens x 64 rows as two
+// 32x32 accumulators.  MFMA lane layout (32x32x2 f32): A[i][k] from lane
 // i + 32k, B[k][j] from lane j + 32k, D[i][j] in lane j + 32*((i/4)%2), register
 // (i%4) + 4*(i/8).
 #pragma once
@@ -46,9 +46,15 @@ struct GemmArgs {
 template <int QT, int MODE>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
   constexpr int BM = 64, BN = 128, BK = 32;
-  constexpr int AP = BM + 4, BP = BN + 4;
-  __shared__ float As[kGemmBufs][BK][AP];
-  __shared__ float Bs[kGemmBufs][BK][BP];
+  // Columns XOR-swizzled within aligned 32-column blocks so that the staging
+  // stores of a half-wave hit 32 distinct banks (X: four tokens x eight k
+  // quads per half-wave; W: sixteen rows x the two k halves) while each MFMA
+  // operand read stays a permutation of one aligned 32-column block:
+  // X[t][k] at As[k][t ^ (k & 28)], W[n][k] at Bs[k][n ^ (16 * (bit 4 ^ bit 3 of k))].
+  __shared__ float As[kGemmBufs][BK][BM];
+  __shared__ float Bs[kGemmBufs][BK][BN];
+  auto sa = [](int k) { return k & 28; };
+  auto sb = [](int k) { return (k ^ (k << 1)) & 16; };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -104,10 +110,10 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       int idx = tid + 256 * i, row = idx >> 3, kq = idx & 7;
-      As[buf][4 * kq + 0][row] = xa[i].x;
-      As[buf][4 * kq + 1][row] = xa[i].y;
-      As[buf][4 * kq + 2][row] = xa[i].z;
-      As[buf][4 * kq + 3][row] = xa[i].w;
+      As[buf][4 * kq + 0][row ^ sa(4 * kq)] = xa[i].x;
+      As[buf][4 * kq + 1][row ^ sa(4 * kq + 1)] = xa[i].y;
+      As[buf][4 * kq + 2][row ^ sa(4 * kq + 2)] = xa[i].z;
+      As[buf][4 * kq + 3][row ^ sa(4 * kq + 3)] = xa[i].w;
     }
     if constexpr (QT == kQ4_K) {
       wd = q4k_scale(wks, wkd);
@@ -120,7 +126,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float v = brow_ok ? wd * (float)(int8_t)(w4[i >> 2] >> (8 * (i & 3))) : 0.f;
-        Bs[buf][16 * bhalf + i][brow] = v;
+        Bs[buf][16 * bhalf + i][brow ^ sb(16 * bhalf + i)] = v;
       }
     } else if constexpr (nibble_layout(QT)) {
       uint32_t w2[2] = {wq.x, wq.y};
@@ -137,16 +143,16 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
         }
         lo = brow_ok ? lo : 0.f;
         hi = brow_ok ? hi : 0.f;
-        Bs[buf][8 * bhalf + i][brow] = lo;
-        Bs[buf][16 + 8 * bhalf + i][brow] = hi;
+        Bs[buf][8 * bhalf + i][brow ^ sb(8 * bhalf + i)] = lo;
+        Bs[buf][16 + 8 * bhalf + i][brow ^ sb(16 + 8 * bhalf + i)] = hi;
       }
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        Bs[buf][16 * bhalf + 4 * i + 0][brow] = brow_ok ? wf[i].x : 0.f;
-        Bs[buf][16 * bhalf + 4 * i + 1][brow] = brow_ok ? wf[i].y : 0.f;
-        Bs[buf][16 * bhalf + 4 * i + 2][brow] = brow_ok ? wf[i].z : 0.f;
-        Bs[buf][16 * bhalf + 4 * i + 3][brow] = brow_ok ? wf[i].w : 0.f;
+        Bs[buf][16 * bhalf + 4 * i + 0][brow ^ sb(16 * bhalf + 4 * i + 0)] = brow_ok ? wf[i].x : 0.f;
+        Bs[buf][16 * bhalf + 4 * i + 1][brow ^ sb(16 * bhalf + 4 * i + 1)] = brow_ok ? wf[i].y : 0.f;
+        Bs[buf][16 * bhalf + 4 * i + 2][brow ^ sb(16 * bhalf + 4 * i + 2)] = brow_ok ? wf[i].z : 0.f;
+        Bs[buf][16 * bhalf + 4 * i + 3][brow ^ sb(16 * bhalf + 4 * i + 3)] = brow_ok ? wf[i].w : 0.f;
       }
     }
   };
@@ -164,9 +170,10 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
     if (kb + 1 < a.nblk) load(kb + 1);
 #pragma unroll
     for (int p = 0; p < BK / 2; ++p) {
-      float av = As[buf][2 * p + lk][wm * 32 + li];
-      float b0 = Bs[buf][2 * p + lk][wn * 64 + li];
-      float b1 = Bs[buf][2 * p + lk][wn * 64 + 32 + li];
+      const int k = 2 * p + lk;
+      float av = As[buf][k][(wm * 32 + li) ^ sa(k)];
+      float b0 = Bs[buf][k][(wn * 64 + li) ^ sb(k)];
+      float b1 = Bs[buf][k][(wn * 64 + 32 + li) ^ sb(k)];
       acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b0, acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b1, acc1, 0, 0, 0);
     }
