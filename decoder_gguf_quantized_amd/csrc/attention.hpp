@@ -480,9 +480,10 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
 
 // ------------------------------------------------------------ prefill attention on the matrix cores
 // The same online softmax as attn_prefill_kernel, with both products on
-// V_MFMA_F32_32X32X2_F32 (f32 operands, f32 accumulation).  Workgroup = 32
-// queries x one query head; its four waves take the 32-key tiles of the
-// queries' key range in turn and merge their (max, sum, output) at the end.
+// V_MFMA_F32_32X32X2_F32 (f32 operands, f32 accumulation); head_dim 64 and
+// 128.  Workgroup = 32 queries x one query head; its four waves take the
+// 32-key tiles of the queries' key range in turn and merge their (max, sum,
+// output) at the end.
 //
 // Per tile the wave computes S^T = K Q^T (keys as rows, queries as columns),
 // contracting over dims in the order c(t, h) = h * HD/2 + t (lane half h,
@@ -661,6 +662,162 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnPrefillArgs 
       }
     }
     __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------ prefill attention, head-dim split
+// head_dim 256 (at 128 the whole-head kernel above, which requests a tile's
+// values before its scores, measured faster).  Same workgroup (32 queries x
+// one query head) and the
+// same MFMA layouts as attn_prefill_mfma_kernel, but the four waves walk every
+// key tile together, each owning a quarter of the head dimension: wave w
+// contracts dims [w HD/4, (w+1) HD/4) of S^T = K Q^T (contraction order
+// c(t, h) = w HD/4 + h HD/8 + t), the four partial score tiles are summed
+// through LDS in wave order (so every wave holds the same scores, maximum and
+// sum), and wave w accumulates output dims [w HD/4, (w+1) HD/4) of
+// O^T = V^T P^T.  A wave then needs a quarter of the query, output, key and
+// value registers of the whole-head kernel, which leaves room to request the
+// next tile's keys and values while the current tile is multiplied; no merge
+// of partial outputs is needed at the end.
+template <int HD>
+__global__ __launch_bounds__(256) void attn_prefill_dsplit_kernel(AttnPrefillArgs a) {
+  static_assert(HD % 128 == 0, "a wave owns whole 32-dim output blocks");
+  constexpr int D = HD / 4;     // dims owned by a wave
+  constexpr int DH = D / 2;     // contraction steps of the wave's partial S^T
+  constexpr int NBW = D / 32;   // 32-dim output blocks of the wave
+  __shared__ float sm_s[2][4][16][64];  // partial S^T per wave, double-buffered by tile parity
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 31, lk = lane >> 5;
+  const int q0 = (int)blockIdx.x * 32, h = (int)blockIdx.y, g = h / (a.nq / a.nkv);
+  const int tq = q0 + li;  // this lane's query (token index)
+  const bool q_ok = tq < a.T;
+  const int p = a.pos0 + tq;
+  const int tlast = min(a.T, q0 + 32) - 1;
+  const int kmax = a.pos0 + tlast;
+  const int kmin = a.window > 0 ? max(0, a.pos0 + q0 - a.window + 1) : 0;
+  const int kt0 = kmin & ~31;
+  const int ntile = (kmax - kt0) / 32 + 1;
+  const int dk = wave * D + lk * DH;  // first contraction dim of this lane
+
+  float q[DH];
+  {
+    const float4* qp =
+        reinterpret_cast<const float4*>(a.q + (size_t)(q_ok ? tq : 0) * a.nq * HD + (size_t)h * HD + dk);
+#pragma unroll
+    for (int e = 0; e < DH / 4; ++e) {
+      const float4 v = qp[e];
+      q[4 * e + 0] = v.x * a.scale_log2;
+      q[4 * e + 1] = v.y * a.scale_log2;
+      q[4 * e + 2] = v.z * a.scale_log2;
+      q[4 * e + 3] = v.w * a.scale_log2;
+    }
+  }
+
+  // one tile's operands: K[key0 + li][dk .. dk + DH) and, for O^T step t,
+  // V[key0 + 8(t/4) + 4 lk + t%4][w D + 32 b + li]
+  struct Tile {
+    float4 k[DH / 4];
+    float v[NBW][16];
+  };
+  auto load = [&](Tile& b, int it) {
+    const int key0 = kt0 + 32 * it;
+    const float4* kp = reinterpret_cast<const float4*>(
+        a.kc + kv_row(a.map, a.nkv, a.ctx, a.seq, g, min(key0 + li, kmax)) * HD + dk);
+#pragma unroll
+    for (int e = 0; e < DH / 4; ++e) b.k[e] = kp[e];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const size_t r = kv_row(a.map, a.nkv, a.ctx, a.seq, g, min(key0 + 8 * (t >> 2) + 4 * lk + (t & 3), kmax));
+#pragma unroll
+      for (int bb = 0; bb < NBW; ++bb) b.v[bb][t] = a.vc[r * HD + wave * D + 32 * bb + li];
+    }
+  };
+
+  f32x16 o[NBW];
+#pragma unroll
+  for (int bb = 0; bb < NBW; ++bb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[bb][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  auto compute = [&](const Tile& b, int it) {
+    const int key0 = kt0 + 32 * it;
+    f32x16 sacc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+#pragma unroll
+    for (int e = 0; e < DH / 4; ++e) {
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(b.k[e].x, q[4 * e + 0], sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(b.k[e].y, q[4 * e + 1], sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(b.k[e].z, q[4 * e + 2], sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(b.k[e].w, q[4 * e + 3], sacc, 0, 0, 0);
+    }
+    // the whole-head scores: partial tiles summed in wave order
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sm_s[it & 1][wave][r][lane] = sacc[r];
+    __syncthreads();
+    float pr[16];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float sc = ((sm_s[it & 1][0][r][lane] + sm_s[it & 1][1][r][lane]) + sm_s[it & 1][2][r][lane]) +
+                       sm_s[it & 1][3][r][lane];
+      const int key = key0 + 8 * (r >> 2) + 4 * lk + (r & 3);
+      const bool ok = q_ok && key <= p && (a.window == 0 || key > p - a.window);
+      pr[r] = ok ? sc : -INFINITY;
+      mt = fmaxf(mt, pr[r]);
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    // lazy rescale, as in attn_prefill_mfma_kernel (every wave takes the same
+    // decisions: its scores are the same)
+    float corr = 1.f;
+    if (m_run == -INFINITY) {
+      m_run = mt;
+    } else if (mt > m_run + 8.f) {
+      corr = exp2f(m_run - mt);
+      m_run = mt;
+    }
+    const bool rescale = __any(corr != 1.f);
+    float ps = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      pr[r] = pr[r] == -INFINITY ? 0.f : exp2f(pr[r] - m_run);
+      ps += pr[r];
+    }
+    ps += __shfl_xor(ps, 32);
+    l_run = l_run * corr + ps;
+#pragma unroll
+    for (int bb = 0; bb < NBW; ++bb) {
+      if (rescale) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[bb][r] *= corr;
+      }
+#pragma unroll
+      for (int t = 0; t < 16; ++t) o[bb] = __builtin_amdgcn_mfma_f32_32x32x2f32(b.v[bb][t], pr[t], o[bb], 0, 0, 0);
+    }
+  };
+
+  // two register sets: the next tile's loads are in flight while a tile is
+  // multiplied (every wave runs the same tiles, so the barriers match)
+  Tile ta, tb;
+  load(ta, 0);
+  for (int it = 0; it < ntile; it += 2) {
+    if (it + 1 < ntile) load(tb, it + 1);
+    compute(ta, it);
+    if (it + 1 >= ntile) break;
+    if (it + 2 < ntile) load(ta, it + 2);
+    compute(tb, it + 1);
+  }
+
+  if (q_ok) {
+    const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+    float* orow = a.out + (size_t)tq * a.nq * HD + (size_t)h * HD + wave * D;
+#pragma unroll
+    for (int bb = 0; bb < NBW; ++bb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<float4*>(orow + 32 * bb + 8 * r4 + 4 * lk) =
+            make_float4(o[bb][4 * r4] * inv, o[bb][4 * r4 + 1] * inv, o[bb][4 * r4 + 2] * inv,
+                        o[bb][4 * r4 + 3] * inv);
   }
 }
 

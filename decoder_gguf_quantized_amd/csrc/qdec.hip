@@ -402,13 +402,14 @@ void attention_prefill(qdec_model* m, hipStream_t st, int l, int seq, int T, int
   }
   Timed tm(m, st, "attn_prefill", (double)T * c.n_head * hd * 8 + (double)(pos0 + T) * c.n_head_kv * hd * 8,
            4.0 * hd * c.n_head * pairs);
-  // head_dim 64 / 128: the matrix-core kernel (32 queries per workgroup; its
-  // key rows are 32-bit indices); 256 keeps the VALU kernel (registers)
+  // the matrix-core kernels (32 queries per workgroup): head_dim 64 and 128
+  // whole-head per wave, 256 split over the four waves; caches of 2^31 rows
+  // per layer or more take the VALU kernel
   if (m->kv_layer / hd < (size_t)INT32_MAX) {
     dim3 grid((T + 31) / 32, c.n_head);
     if (hd == 64) qlaunch(attn_prefill_mfma_kernel<64>, grid, 256, 0, st, a);
     else if (hd == 128) qlaunch(attn_prefill_mfma_kernel<128>, grid, 256, 0, st, a);
-    else qlaunch(attn_prefill_mfma_kernel<256>, grid, 256, 0, st, a);
+    else qlaunch(attn_prefill_dsplit_kernel<256>, grid, 256, 0, st, a);
     return;
   }
   const int QT = 256 / (hd / 8);
