@@ -70,21 +70,14 @@ void gemv_dispatch_ru(int ru, int mode, dim3 grid, size_t lds, hipStream_t st, c
     case 0: gemv_dispatch_fit<QT, M, 0, 4, 1>(mode, grid, lds, st, a); break;
     case 1: gemv_dispatch_fit<QT, M, 1, 2, 2>(mode, grid, lds, st, a); break;
     case 3: gemv_dispatch_fit<QT, M, 3, 2, 4, 8>(mode, grid, lds, st, a); break;
-#ifdef QDEC_EXPERIMENT
-    case 4: gemv_dispatch_mode<QT, M, 4, 2>(mode, grid, lds, st, a); break;
-    case 5: gemv_dispatch_mode<QT, M, 4, 4>(mode, grid, lds, st, a); break;
-    case 6: gemv_dispatch_mode<QT, M, 2, 8>(mode, grid, lds, st, a); break;
-    case 7: gemv_dispatch_mode<QT, M, 2, 1>(mode, grid, lds, st, a); break;
-    case 8: gemv_dispatch_mode<QT, M, 1, 4, 8>(mode, grid, lds, st, a); break;
-    case 9: gemv_dispatch_mode<QT, M, 1, 8, 8>(mode, grid, lds, st, a); break;
-    case 10: gemv_dispatch_mode<QT, M, 2, 2, 8>(mode, grid, lds, st, a); break;
-#endif
     default: gemv_dispatch_fit<QT, M, 2, 2, 4>(mode, grid, lds, st, a); break;
   }
 }
 
-inline int ru_rows(int ru) { return (ru == 0 || ru == 4 || ru == 5) ? 4 : (ru == 8 || ru == 9) ? 1 : 2; }
-inline int ru_waves(int ru) { return (ru == 3 || ru >= 8) ? 8 : 4; }
+// tile classes: 0 = four rows x one unit per lane, 1 = two rows x two units,
+// 2 = two rows x four units, 3 = class 2 in eight-wave workgroups
+inline int ru_rows(int ru) { return ru == 0 ? 4 : 2; }
+inline int ru_waves(int ru) { return ru == 3 ? 8 : 4; }
 
 template <int QT>
 void gemv_dispatch_m(int M, int ru, int mode, dim3 grid, size_t lds, hipStream_t st, const GemvArgs& a) {

@@ -21,15 +21,6 @@
 namespace qd {
 
 
-// LDS stages of the f32 tiles.  The next stage's global loads go to registers
-// while the current stage is multiplied, so one LDS buffer (one more barrier
-// per stage) suffices and halves the LDS per workgroup.
-#ifndef QDEC_GEMM_BUFS
-#define QDEC_GEMM_BUFS 1
-#endif
-constexpr int kGemmBufs = QDEC_GEMM_BUFS;
-static_assert(kGemmBufs == 1 || kGemmBufs == 2, "one or two LDS stages");
-
 struct GemmArgs {
   const uint8_t* qs;    // weights, same layout as GemvArgs
   const uint16_t* d;
@@ -51,8 +42,11 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
   // quads per half-wave; W: sixteen rows x the two k halves) while each MFMA
   // operand read stays a permutation of one aligned 32-column block:
   // X[t][k] at As[k][t ^ (k & 28)], W[n][k] at Bs[k][n ^ (16 * (bit 4 ^ bit 3 of k))].
-  __shared__ float As[kGemmBufs][BK][BM];
-  __shared__ float Bs[kGemmBufs][BK][BN];
+  // One LDS stage: the next stage's global loads land in registers while the
+  // current stage is multiplied, and a second barrier per stage guards the
+  // overwrite (a second buffer only cost occupancy).
+  __shared__ float As[BK][BM];
+  __shared__ float Bs[BK][BN];
   auto sa = [](int k) { return k & 28; };
   auto sb = [](int k) { return (k ^ (k << 1)) & 16; };
 
@@ -106,14 +100,14 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
     }
   };
 
-  auto store = [&](int buf) {
+  auto store = [&]() {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       int idx = tid + 256 * i, row = idx >> 3, kq = idx & 7;
-      As[buf][4 * kq + 0][row ^ sa(4 * kq)] = xa[i].x;
-      As[buf][4 * kq + 1][row ^ sa(4 * kq + 1)] = xa[i].y;
-      As[buf][4 * kq + 2][row ^ sa(4 * kq + 2)] = xa[i].z;
-      As[buf][4 * kq + 3][row ^ sa(4 * kq + 3)] = xa[i].w;
+      As[4 * kq + 0][row ^ sa(4 * kq)] = xa[i].x;
+      As[4 * kq + 1][row ^ sa(4 * kq + 1)] = xa[i].y;
+      As[4 * kq + 2][row ^ sa(4 * kq + 2)] = xa[i].z;
+      As[4 * kq + 3][row ^ sa(4 * kq + 3)] = xa[i].w;
     }
     if constexpr (QT == kQ4_K) {
       wd = q4k_scale(wks, wkd);
@@ -126,7 +120,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float v = brow_ok ? wd * (float)(int8_t)(w4[i >> 2] >> (8 * (i & 3))) : 0.f;
-        Bs[buf][16 * bhalf + i][brow ^ sb(16 * bhalf + i)] = v;
+        Bs[16 * bhalf + i][brow ^ sb(16 * bhalf + i)] = v;
       }
     } else if constexpr (nibble_layout(QT)) {
       uint32_t w2[2] = {wq.x, wq.y};
@@ -143,16 +137,16 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
         }
         lo = brow_ok ? lo : 0.f;
         hi = brow_ok ? hi : 0.f;
-        Bs[buf][8 * bhalf + i][brow ^ sb(8 * bhalf + i)] = lo;
-        Bs[buf][16 + 8 * bhalf + i][brow ^ sb(16 + 8 * bhalf + i)] = hi;
+        Bs[8 * bhalf + i][brow ^ sb(8 * bhalf + i)] = lo;
+        Bs[16 + 8 * bhalf + i][brow ^ sb(16 + 8 * bhalf + i)] = hi;
       }
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        Bs[buf][16 * bhalf + 4 * i + 0][brow ^ sb(16 * bhalf + 4 * i + 0)] = brow_ok ? wf[i].x : 0.f;
-        Bs[buf][16 * bhalf + 4 * i + 1][brow ^ sb(16 * bhalf + 4 * i + 1)] = brow_ok ? wf[i].y : 0.f;
-        Bs[buf][16 * bhalf + 4 * i + 2][brow ^ sb(16 * bhalf + 4 * i + 2)] = brow_ok ? wf[i].z : 0.f;
-        Bs[buf][16 * bhalf + 4 * i + 3][brow ^ sb(16 * bhalf + 4 * i + 3)] = brow_ok ? wf[i].w : 0.f;
+        Bs[16 * bhalf + 4 * i + 0][brow ^ sb(16 * bhalf + 4 * i + 0)] = brow_ok ? wf[i].x : 0.f;
+        Bs[16 * bhalf + 4 * i + 1][brow ^ sb(16 * bhalf + 4 * i + 1)] = brow_ok ? wf[i].y : 0.f;
+        Bs[16 * bhalf + 4 * i + 2][brow ^ sb(16 * bhalf + 4 * i + 2)] = brow_ok ? wf[i].z : 0.f;
+        Bs[16 * bhalf + 4 * i + 3][brow ^ sb(16 * bhalf + 4 * i + 3)] = brow_ok ? wf[i].w : 0.f;
       }
     }
   };
@@ -162,23 +156,22 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
   for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0.f;
 
   load(0);
-  store(0);
+  store();
   __syncthreads();
   const int li = lane & 31, lk = lane >> 5;
   for (int kb = 0; kb < a.nblk; ++kb) {
-    const int buf = kGemmBufs == 2 ? kb & 1 : 0;
     if (kb + 1 < a.nblk) load(kb + 1);
 #pragma unroll
     for (int p = 0; p < BK / 2; ++p) {
       const int k = 2 * p + lk;
-      float av = As[buf][k][(wm * 32 + li) ^ sa(k)];
-      float b0 = Bs[buf][k][(wn * 64 + li) ^ sb(k)];
-      float b1 = Bs[buf][k][(wn * 64 + 32 + li) ^ sb(k)];
+      float av = As[k][(wm * 32 + li) ^ sa(k)];
+      float b0 = Bs[k][(wn * 64 + li) ^ sb(k)];
+      float b1 = Bs[k][(wn * 64 + 32 + li) ^ sb(k)];
       acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b0, acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b1, acc1, 0, 0, 0);
     }
-    if constexpr (kGemmBufs == 1) __syncthreads();  // every wave is done reading the stage
-    if (kb + 1 < a.nblk) store(kGemmBufs == 2 ? buf ^ 1 : 0);
+    __syncthreads();  // every wave is done reading the stage
+    if (kb + 1 < a.nblk) store();
     __syncthreads();
   }
 
@@ -219,8 +212,9 @@ __global__ __launch_bounds__(256, 1) void gemm_ksplit_kernel(GemmArgs a) {
   // LDS k-major without padding; columns XOR-swizzled so that both the staging
   // writes and the MFMA operand reads of a half-wave hit 32 distinct banks:
   // X[t][k] at As[k][t ^ (k / 4)], W[n][k] at Bs[k][n ^ (8 * (k / 32))].
-  __shared__ float As[kGemmBufs][BK][BM];
-  __shared__ float Bs[kGemmBufs][BK][BN];
+  // one LDS stage, as in gemm_kernel
+  __shared__ float As[BK][BM];
+  __shared__ float Bs[BK][BN];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = blockIdx.x * BN, t0 = blockIdx.y * BM;
@@ -280,15 +274,15 @@ __global__ __launch_bounds__(256, 1) void gemm_ksplit_kernel(GemmArgs a) {
     }
   };
 
-  auto store = [&](int buf) {
+  auto store = [&]() {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int idx = tid + 256 * i, row = idx >> 5, kq = idx & 31;
       const int c = row ^ kq;
-      As[buf][4 * kq + 0][c] = xa[i].x;
-      As[buf][4 * kq + 1][c] = xa[i].y;
-      As[buf][4 * kq + 2][c] = xa[i].z;
-      As[buf][4 * kq + 3][c] = xa[i].w;
+      As[4 * kq + 0][c] = xa[i].x;
+      As[4 * kq + 1][c] = xa[i].y;
+      As[4 * kq + 2][c] = xa[i].z;
+      As[4 * kq + 3][c] = xa[i].w;
     }
     const int kk = bblk * 32, bc = brow ^ (8 * bblk);
     if constexpr (QT == kQ4_K) {
@@ -302,30 +296,30 @@ __global__ __launch_bounds__(256, 1) void gemm_ksplit_kernel(GemmArgs a) {
       const uint32_t w8[8] = {wq[0].x, wq[0].y, wq[0].z, wq[0].w, wq[1].x, wq[1].y, wq[1].z, wq[1].w};
 #pragma unroll
       for (int i = 0; i < 32; ++i)
-        Bs[buf][kk + i][bc] = (i < 16 ? wd : wd2) * (float)(int8_t)(w8[i >> 2] >> (8 * (i & 3)));
+        Bs[kk + i][bc] = (i < 16 ? wd : wd2) * (float)(int8_t)(w8[i >> 2] >> (8 * (i & 3)));
     } else if constexpr (QT == kQ4_K) {
       const uint32_t w4[4] = {wq[0].x, wq[0].y, wq[0].z, wq[0].w};
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const uint32_t byte = (w4[i >> 2] >> (8 * (i & 3))) & 0xffu;
-        Bs[buf][kk + i][bc] = fmaf(wd, (float)(byte & 15u), -wmin);
-        Bs[buf][kk + 16 + i][bc] = fmaf(wd, (float)(byte >> 4), -wmin);
+        Bs[kk + i][bc] = fmaf(wd, (float)(byte & 15u), -wmin);
+        Bs[kk + 16 + i][bc] = fmaf(wd, (float)(byte >> 4), -wmin);
       }
     } else if constexpr (QT == kQ4_0) {
       const uint32_t w4[4] = {wq[0].x, wq[0].y, wq[0].z, wq[0].w};
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const uint32_t byte = (w4[i >> 2] >> (8 * (i & 3))) & 0xffu;
-        Bs[buf][kk + i][bc] = wd * (float)((int)(byte & 15u) - 8);
-        Bs[buf][kk + 16 + i][bc] = wd * (float)((int)(byte >> 4) - 8);
+        Bs[kk + i][bc] = wd * (float)((int)(byte & 15u) - 8);
+        Bs[kk + 16 + i][bc] = wd * (float)((int)(byte >> 4) - 8);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        Bs[buf][kk + 4 * i + 0][bc] = wf[i].x;
-        Bs[buf][kk + 4 * i + 1][bc] = wf[i].y;
-        Bs[buf][kk + 4 * i + 2][bc] = wf[i].z;
-        Bs[buf][kk + 4 * i + 3][bc] = wf[i].w;
+        Bs[kk + 4 * i + 0][bc] = wf[i].x;
+        Bs[kk + 4 * i + 1][bc] = wf[i].y;
+        Bs[kk + 4 * i + 2][bc] = wf[i].z;
+        Bs[kk + 4 * i + 3][bc] = wf[i].w;
       }
     }
   };
@@ -334,29 +328,28 @@ __global__ __launch_bounds__(256, 1) void gemm_ksplit_kernel(GemmArgs a) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0.f;
   load(0);
-  store(0);
+  store();
   __syncthreads();
   const int li = lane & 31, lk = lane >> 5;
   for (int st = 0; st < nstage; ++st) {
-    const int buf = kGemmBufs == 2 ? st & 1 : 0;
     if (st + 1 < nstage) load(st + 1);
     const int kw = wave * 32;  // this wave's quant block within the stage
 #pragma unroll
     for (int p = 0; p < 16; ++p) {
       const int k = kw + 2 * p + lk;
-      const float av = As[buf][k][li ^ (k >> 2)];
-      const float b0 = Bs[buf][k][li ^ (8 * wave)];
-      const float b1 = Bs[buf][k][32 + (li ^ (8 * wave))];
+      const float av = As[k][li ^ (k >> 2)];
+      const float b0 = Bs[k][li ^ (8 * wave)];
+      const float b1 = Bs[k][32 + (li ^ (8 * wave))];
       acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b0, acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b1, acc1, 0, 0, 0);
     }
-    if constexpr (kGemmBufs == 1) __syncthreads();  // every wave is done reading the stage
-    if (st + 1 < nstage) store(kGemmBufs == 2 ? buf ^ 1 : 0);
+    __syncthreads();  // every wave is done reading the stage
+    if (st + 1 < nstage) store();
     __syncthreads();
   }
   // sum the four waves' partial tiles in wave order (reusing the B buffer)
   static_assert(sizeof(Bs) >= 4 * BM * BN * sizeof(float), "reduction buffer");
-  float* red = &Bs[0][0][0];  // 4 x [32][64] floats = 32 KB
+  float* red = &Bs[0][0];  // 4 x [32][64] floats = 32 KB
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int i = 8 * (r >> 2) + 4 * lk + (r & 3);

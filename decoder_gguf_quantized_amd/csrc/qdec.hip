@@ -276,14 +276,7 @@ void gemv(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, 
   const int nunits = int8_layout(w.type) ? 2 * w.nblk : (nibble_layout(w.type) ? w.nblk : kp / 4);
   int ru = nunits <= 64 ? 0 : (nunits <= 128 ? 1 : 2);
   if (ru == 2 && (pair ? w.rows / 2 : (w.rows + 1) / 2) >= 2048) ru = 3;
-  int grid_cap = 1024;
-#ifdef QDEC_EXPERIMENT
-  {
-    const char* e = getenv(nunits <= 64 ? "QDEC_RU_S" : (nunits <= 128 ? "QDEC_RU_M" : "QDEC_RU_L"));
-    if (e) ru = atoi(e);
-    if (const char* g = getenv("QDEC_GRID_CAP")) grid_cap = atoi(g);
-  }
-#endif
+  const int grid_cap = 1024;
   const int R = ru_rows(ru), NW = ru_waves(ru);
   const int ngroups = pair ? w.rows / R : (w.rows + R - 1) / R;
   // waves stay resident and loop: about four workgroups per CU, so the input
@@ -1021,9 +1014,6 @@ int load(const qdec_config* cfgp, const qdec_tensor* ts, int32_t n, int32_t max_
       const double want = (double)max_ctx * c.n_head_kv * max_seqs / 8192.0;
       int ch = 4 * (256 / (c.head_dim / 8));
       while ((ch < want || (max_ctx + ch - 1) / ch > kMaxChunks) && ch < (1 << 30)) ch *= 2;
-#ifdef QDEC_EXPERIMENT
-      if (const char* e = getenv("QDEC_CHUNK")) ch = std::max(atoi(e), (max_ctx + kMaxChunks - 1) / kMaxChunks);
-#endif
       m->chunk = ch;
       m->chunk_base = ch;
       m->nchunk = (max_ctx + ch - 1) / ch;
