@@ -132,6 +132,9 @@ struct RopeArgs {
   KvMap map;            // cache layout
 };
 
+// Grid (token, group of four heads): one wave per head, so every wave makes a
+// single round of loads (a wave looping over heads waited on each head's loads
+// in turn).  No barriers: a wave past the last head returns.
 __global__ __launch_bounds__(256) void rope_kv_kernel(RopeArgs a) {
   const int t = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int seq = a.dpos ? t : a.seq0;
@@ -139,7 +142,8 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(RopeArgs a) {
   const int half = a.hd / 2;
   const int nheads = a.nq + 2 * a.nkv;
   const float2* rt = a.rope + (size_t)pos * half;
-  for (int hh = wave; hh < nheads; hh += 4) {
+  const int hh = (int)blockIdx.y * 4 + wave;
+  if (hh < nheads) {
     const float* src = a.qkv + (size_t)t * a.ldqkv + (size_t)hh * a.hd;
     const bool is_q = hh < a.nq, is_k = !is_q && hh < a.nq + a.nkv;
     float x1[2], x2[2];

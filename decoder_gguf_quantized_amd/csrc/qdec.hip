@@ -419,7 +419,7 @@ void rope_kv(qdec_model* m, hipStream_t st, int l, int n, int seq0, int pos0, co
              c.n_head_kv, c.head_dim, L.q_norm, L.k_norm, c.rms_eps, L.global ? m->rope_g : m->rope_l,
              seq0, pos0, dpos, L.qkv_bias, m->map()};
   Timed tm(m, st, "rope_kv", (double)n * m->nqkv * 8, 0);
-  qlaunch(rope_kv_kernel, n, 256, 0, st, a);
+  qlaunch(rope_kv_kernel, dim3(n, (c.n_head + 2 * c.n_head_kv + 3) / 4), 256, 0, st, a);
 }
 
 void embed(qdec_model* m, hipStream_t st, const int* d_tokens, int n, float* out) {
