@@ -107,13 +107,14 @@ void gemm_dispatch(int mode, dim3 grid, hipStream_t st, const GemmArgs& a) {
   }
 }
 
-template <int QT>
+template <int QT, int NWV>
 void gemm_ksplit_dispatch(int mode, dim3 grid, hipStream_t st, const GemmArgs& a) {
+  const unsigned nt = 64 * NWV;
   switch (mode) {
-    case kModeStore: qlaunch(gemm_ksplit_kernel<QT, kModeStore>, grid, 256, 0, st, a); break;
-    case kModeAdd: qlaunch(gemm_ksplit_kernel<QT, kModeAdd>, grid, 256, 0, st, a); break;
-    case kModePairSilu: qlaunch(gemm_ksplit_kernel<QT, kModePairSilu>, grid, 256, 0, st, a); break;
-    default: qlaunch(gemm_ksplit_kernel<QT, kModePairGelu>, grid, 256, 0, st, a); break;
+    case kModeStore: qlaunch(gemm_ksplit_kernel<QT, kModeStore, NWV>, grid, nt, 0, st, a); break;
+    case kModeAdd: qlaunch(gemm_ksplit_kernel<QT, kModeAdd, NWV>, grid, nt, 0, st, a); break;
+    case kModePairSilu: qlaunch(gemm_ksplit_kernel<QT, kModePairSilu, NWV>, grid, nt, 0, st, a); break;
+    default: qlaunch(gemm_ksplit_kernel<QT, kModePairGelu, NWV>, grid, nt, 0, st, a); break;
   }
 }
 
@@ -128,13 +129,16 @@ void gemm_bf16_dispatch(int mode, dim3 grid, hipStream_t st, const GemmArgs& a) 
 }
 
 // Prefill GEMM kinds: the wide 64 x 128 f32 tile, the K-split 32 x 64 f32
-// tile, and the bf16 tile with one or three activation terms.
-enum { kGemmWide = 0, kGemmKSplit = 1, kGemmBf16 = 2, kGemmBf16x3 = 3 };
+// tile (four or eight waves), and the bf16 tile with one or three activation
+// terms.
+enum { kGemmWide = 0, kGemmKSplit = 1, kGemmBf16 = 2, kGemmBf16x3 = 3, kGemmKSplit8 = 4 };
 
 template <int QT>
 void gemm_launch(int kind, int mode, dim3 grid, hipStream_t st, const GemmArgs& a) {
   if (kind == kGemmKSplit) {
-    gemm_ksplit_dispatch<QT>(mode, grid, st, a);
+    gemm_ksplit_dispatch<QT, 4>(mode, grid, st, a);
+  } else if (kind == kGemmKSplit8) {
+    gemm_ksplit_dispatch<QT, 8>(mode, grid, st, a);
   } else if (kind == kGemmWide) {
     gemm_dispatch<QT>(mode, grid, st, a);
   } else {

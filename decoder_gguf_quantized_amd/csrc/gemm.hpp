@@ -199,47 +199,51 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
   }
 }
 
-// Small-N variant: workgroup tile 32 tokens x 64 weight rows, BK = 128 (four
-// quant blocks per stage).  Each wave owns one of the stage's four blocks over
-// the whole 32 x 64 tile (two 32x32 accumulators), i.e. the four waves split K;
-// at the end the four partial tiles are summed through LDS in a fixed order
-// (deterministic).  Four times the workgroups of the 64 x 128 tile for the same
-// problem, for projections with few output rows (O and down at small hidden
-// sizes, gate/up of short prompts).
-template <int QT, int MODE>
-__global__ __launch_bounds__(256, 1) void gemm_ksplit_kernel(GemmArgs a) {
-  constexpr int BM = 32, BN = 64, BK = 128;
+// Small-N variant: workgroup tile 32 tokens x 64 weight rows, NWV waves (4 or
+// 8), BK = 32 NWV (one quant block per wave per stage).  Each wave owns its
+// block of the stage over the whole 32 x 64 tile (two 32x32 accumulators),
+// i.e. the waves split K; at the end the NWV partial tiles are summed through
+// LDS in wave order (deterministic).  Four times the workgroups of the
+// 64 x 128 tile for the same problem, for projections with few output rows (O
+// and down at small hidden sizes, gate/up of short prompts); eight waves when
+// even that grid leaves a CU with one workgroup.
+template <int QT, int MODE, int NWV>
+__global__ __launch_bounds__(64 * NWV, 1) void gemm_ksplit_kernel(GemmArgs a) {
+  static_assert(NWV == 4 || NWV == 8, "four or eight waves");
+  constexpr int BM = 32, BN = 64, BK = 32 * NWV, NT = 64 * NWV;
   // LDS k-major without padding; columns XOR-swizzled so that both the staging
   // writes and the MFMA operand reads of a half-wave hit 32 distinct banks:
-  // X[t][k] at As[k][t ^ (k / 4)], W[n][k] at Bs[k][n ^ (8 * (k / 32))].
-  // one LDS stage, as in gemm_kernel
+  // X[t][k] at As[k][t ^ ((k / 4) % 32)], W[n][k] at Bs[k][n ^ (32 / NWV) (k / 32)].
+  // One LDS stage, as in gemm_kernel.
   __shared__ float As[BK][BM];
   __shared__ float Bs[BK][BN];
+  constexpr int SW = 32 / NWV;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = blockIdx.x * BN, t0 = blockIdx.y * BM;
   const int kp = a.nblk * 32;
-  const int nstage = (a.nblk + 3) / 4;
+  const int nstage = (a.nblk + NWV - 1) / NWV;
 
-  // staging: X 32 rows x 128 k = 1024 float4 (4 per thread); W 64 rows x 4 blocks
-  // (thread -> row tid / 4, block tid % 4: one quant block, 32 weights)
+  // staging: X 32 rows x BK k = 8 NWV float4 per row, 4 per thread; W 64 rows
+  // x NWV blocks (thread -> row tid / NWV, block tid % NWV: one quant block,
+  // 32 weights)
   float4 xa[4];
   uint4 wq[2];
   float4 wf[8];
   float wd = 0.f, wd2 = 0.f, wmin = 0.f;  // scale (Q6_K: of values 0..15, wd2 of 16..31); Q4_K min
   uint32_t wks = 0, wkd = 0;              // K-quants: raw scale words, decoded when stored
-  const int brow = tid >> 2, bblk = tid & 3;
+  const int brow = tid / NWV, bblk = tid % NWV;
   const bool brow_ok = n0 + brow < a.rows;
 
   auto load = [&](int st) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int idx = tid + 256 * i, row = idx >> 5, kq = idx & 31;
+      const int idx = tid + NT * i, row = idx / (BK / 4), kq = idx % (BK / 4);
       const int t = t0 + row, k = st * BK + 4 * kq;
       xa[i] = (t < a.T && k < kp) ? *reinterpret_cast<const float4*>(a.x + (size_t)t * a.ldx + k)
                                   : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    const int kb = st * 4 + bblk;
+    const int kb = st * NWV + bblk;
     if (brow_ok && kb < a.nblk) {
       const size_t r = n0 + brow;
       if constexpr (int8_layout(QT)) {
@@ -277,14 +281,14 @@ __global__ __launch_bounds__(256, 1) void gemm_ksplit_kernel(GemmArgs a) {
   auto store = [&]() {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int idx = tid + 256 * i, row = idx >> 5, kq = idx & 31;
-      const int c = row ^ kq;
+      const int idx = tid + NT * i, row = idx / (BK / 4), kq = idx % (BK / 4);
+      const int c = row ^ (kq & 31);
       As[4 * kq + 0][c] = xa[i].x;
       As[4 * kq + 1][c] = xa[i].y;
       As[4 * kq + 2][c] = xa[i].z;
       As[4 * kq + 3][c] = xa[i].w;
     }
-    const int kk = bblk * 32, bc = brow ^ (8 * bblk);
+    const int kk = bblk * 32, bc = brow ^ (SW * bblk);
     if constexpr (QT == kQ4_K) {
       wd = q4k_scale(wks, wkd);
       wmin = q4k_min(wks, wkd);
@@ -337,9 +341,9 @@ __global__ __launch_bounds__(256, 1) void gemm_ksplit_kernel(GemmArgs a) {
 #pragma unroll
     for (int p = 0; p < 16; ++p) {
       const int k = kw + 2 * p + lk;
-      const float av = As[k][li ^ (k >> 2)];
-      const float b0 = Bs[k][li ^ (8 * wave)];
-      const float b1 = Bs[k][32 + (li ^ (8 * wave))];
+      const float av = As[k][li ^ ((k >> 2) & 31)];
+      const float b0 = Bs[k][li ^ (SW * wave)];
+      const float b1 = Bs[k][32 + (li ^ (SW * wave))];
       acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b0, acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b1, acc1, 0, 0, 0);
     }
@@ -347,9 +351,9 @@ __global__ __launch_bounds__(256, 1) void gemm_ksplit_kernel(GemmArgs a) {
     if (st + 1 < nstage) store();
     __syncthreads();
   }
-  // sum the four waves' partial tiles in wave order (reusing the B buffer)
-  static_assert(sizeof(Bs) >= 4 * BM * BN * sizeof(float), "reduction buffer");
-  float* red = &Bs[0][0];  // 4 x [32][64] floats = 32 KB
+  // sum the waves' partial tiles in wave order (reusing the B buffer)
+  static_assert(sizeof(Bs) >= NWV * BM * BN * sizeof(float), "reduction buffer");
+  float* red = &Bs[0][0];  // NWV x [32][64] floats
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int i = 8 * (r >> 2) + 4 * lk + (r & 3);
@@ -357,27 +361,29 @@ __global__ __launch_bounds__(256, 1) void gemm_ksplit_kernel(GemmArgs a) {
     red[(wave * BM + i) * BN + 32 + li] = acc1[r];
   }
   __syncthreads();
-  auto sum4 = [&](int i, int j) {
-    return ((red[(0 * BM + i) * BN + j] + red[(1 * BM + i) * BN + j]) + red[(2 * BM + i) * BN + j]) +
-           red[(3 * BM + i) * BN + j];
+  auto sum_waves = [&](int i, int j) {
+    float v = red[i * BN + j];
+#pragma unroll
+    for (int w = 1; w < NWV; ++w) v += red[(w * BM + i) * BN + j];
+    return v;
   };
   if constexpr (MODE == kModePairSilu || MODE == kModePairGelu) {
     // the tile's 64 rows are one (gate 32, up 32) group of the interleaved
     // layout: outputs n0 / 2 + j, j < 32
-    for (int e = tid; e < BM * 32; e += 256) {
+    for (int e = tid; e < BM * 32; e += NT) {
       const int i = e / 32, j = e % 32;
       const int t = t0 + i;
       if (t < a.T && n0 + j + 32 < a.rows) {
-        const float g = sum4(i, j), u = sum4(i, j + 32);
+        const float g = sum_waves(i, j), u = sum_waves(i, j + 32);
         a.y[(size_t)t * a.ldy + n0 / 2 + j] = (MODE == kModePairSilu ? act_silu(g) : act_gelu_tanh(g)) * u;
       }
     }
   } else {
-    for (int e = tid; e < BM * BN; e += 256) {
+    for (int e = tid; e < BM * BN; e += NT) {
       const int i = e / BN, j = e % BN;
       const int t = t0 + i, n = n0 + j;
       if (t < a.T && n < a.rows) {
-        const float v = sum4(i, j);
+        const float v = sum_waves(i, j);
         float* yr = a.y + (size_t)t * a.ldy;
         if constexpr (MODE == kModeAdd) yr[n] += v;
         else yr[n] = v;

@@ -322,12 +322,14 @@ void gemm(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, 
     gemm_type(w.type, nt == 3 ? kGemmBf16x3 : kGemmBf16, mode, grid, st, a);
     return;
   }
-  // few 64 x 128 tiles for the CUs: switch to the K-split 32 x 64 tile
+  // few 64 x 128 tiles for the CUs: switch to the K-split 32 x 64 tile, with
+  // eight waves when even its grid gives a CU about one workgroup
   if (few) {
     dim3 g2((w.rows + 63) / 64, (T + 31) / 32);
+    const bool eight = (size_t)g2.x * g2.y < 512 && w.nblk >= 16;
     const double bytes = w.gguf_bytes + (double)T * w.nblk * 32 * 4 + (double)T * (pair ? w.rows / 2 : w.rows) * 4;
     Timed tm(m, st, gemm_class(w.type), bytes, 2.0 * T * (double)w.rows * w.cols);
-    gemm_type(w.type, kGemmKSplit, mode, g2, st, a);
+    gemm_type(w.type, eight ? kGemmKSplit8 : kGemmKSplit, mode, g2, st, a);
     return;
   }
   const double bytes = w.gguf_bytes + (double)T * w.nblk * 32 * 4 + (double)T * (pair ? w.rows / 2 : w.rows) * 4;
