@@ -381,13 +381,8 @@ QD_DEV void gemv_store(const GemvArgs& a, int grp, int lane, const float (&scale
 // Register sets of the weight pipeline: with NS sets, NS - 1 tiles are in
 // flight while one is computed.  Three sets for the small tiles (R * U <= 4,
 // 20 VGPRs per set for the quantized types), two for the 8-unit tiles.
-#ifndef QDEC_GEMV_NS
 template <int R, int U, int M>
 constexpr int gemv_sets() { return (R * U <= 4 && M <= 4) ? 3 : 2; }
-#else
-template <int R, int U, int M>
-constexpr int gemv_sets() { return QDEC_GEMV_NS; }
-#endif
 
 // R rows per wave, U 16-byte units per lane in flight per row, M input rows.
 // Each wave walks its (row group, unit block) tiles in order through a ring of

@@ -118,7 +118,8 @@ struct qdec_model {
   float* part_o = nullptr;
   float* part_ml = nullptr;
   int chunk = 0, nchunk = 0;
-  int chunk_base = 0;  // decode chunk chosen at load (a paged cache caps it at the page size)
+  int chunk_base = 0;  // decode chunk for a paged cache: the load-time chunk rounded up to a
+                       // power of two (then capped at the page size)
   float* s_v = nullptr;
   int* s_i = nullptr;
   uint32_t* cut_key = nullptr;  // [max_seqs] top-p cut per row
@@ -1012,12 +1013,21 @@ int load(const qdec_config* cfgp, const qdec_tensor* ts, int32_t n, int32_t max_
        // (the first two pairs are requested at once); at max length about 8192
        // workgroups or more (several rounds of resident workgroups, so the last
        // round's partial fill costs little); at most kMaxChunks per (sequence,
-       // KV head)
+       // KV head).  Past that bound the chunk grows by two positions per lane
+       // group rather than doubling (chunks need not be a power of two in the
+       // contiguous cache: 48 positions instead of 64 at head_dim 256 and 2,177
+       // positions); a paged cache takes the next power of two, which divides
+       // its pages.
       const double want = (double)max_ctx * c.n_head_kv * max_seqs / 8192.0;
-      int ch = 4 * (256 / (c.head_dim / 8));
-      while ((ch < want || (max_ctx + ch - 1) / ch > kMaxChunks) && ch < (1 << 30)) ch *= 2;
+      const int ng = 256 / (c.head_dim / 8);  // lane groups per workgroup
+      int ch = 4 * ng;
+      while (ch < want && ch < (1 << 30)) ch *= 2;
+      const int64_t need = ((int64_t)max_ctx + kMaxChunks - 1) / kMaxChunks;
+      if (ch < need) ch = (int)((need + 2 * ng - 1) / (2 * ng) * (2 * ng));
+      int p2 = 1;
+      while (p2 < ch) p2 *= 2;
       m->chunk = ch;
-      m->chunk_base = ch;
+      m->chunk_base = p2;
       m->nchunk = (max_ctx + ch - 1) / ch;
     }
     m->part_o = m->dalloc<float>((size_t)max_seqs * c.n_head * m->nchunk * c.head_dim);
