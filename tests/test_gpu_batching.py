@@ -223,3 +223,35 @@ def test_refusals_leave_the_handle_usable(qwen3_pair):
         m.kv_reset()
         assert m.kv_pages() == (64, 3, 3)
         torch.cuda.synchronize()
+
+
+def test_decode_chunk_that_is_not_a_power_of_two():
+    """head_dim 256 with max_ctx 2,100: 32-position chunks would exceed the
+    merge's 64 chunks, so the contiguous cache splits decode attention into
+    48-position chunks (the prompt crosses two chunk boundaries); a paged cache
+    of 64-position pages on the same model uses 64-position chunks.  Both match
+    the oracle."""
+    cfg = dict(SMALL["gemma_hd256_g4"])
+    t = synth.generate(cfg)
+    dev()
+    V = cfg["vocab"]
+    prompt = synth.prompt(cfg, 100, tag="np2")
+    for paged in (False, True):
+        with qdec.Model(cfg, t, max_seqs=1, max_ctx=2100) as m:
+            if paged:
+                m.kv_paged(64, 40)
+            om = OracleModel(cfg, t, max_ctx=120, n_seqs=1)
+            pl = torch.empty((1, V), dtype=torch.float32, device=dev())
+            tok = torch.empty(1, dtype=torch.int32, device=dev())
+            m.prefill(0, prompt, pl, tok)
+            torch.cuda.synchronize()
+            check_row(as_np(pl)[0], om.forward(0, prompt)[0])
+            dl = torch.empty((1, V), dtype=torch.float32, device=dev())
+            out = torch.empty(1, dtype=torch.int32, device=dev())
+            cur = int(as_np(tok)[0])
+            for step in range(6):
+                m.decode_batch([0], [cur], dl, out)
+                torch.cuda.synchronize()
+                o = om.forward(0, [cur])[0]
+                check_row(as_np(dl)[0], o)
+                cur = int(as_np(out)[0])
