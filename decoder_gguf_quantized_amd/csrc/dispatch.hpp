@@ -21,6 +21,12 @@ struct HipError {
 
 template <typename... KArgs, typename... Args>
 void qlaunch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStream_t st, Args... args) {
+  // dynamic LDS beyond 64 KB (up to the CU's 160 KB) must be allowed per kernel
+  if (lds > 64 * 1024) {
+    const hipError_t e =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) throw HipError{std::string("hipFuncSetAttribute: ") + hipGetErrorString(e)};
+  }
   hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
 }
 
@@ -51,11 +57,23 @@ void gemv_dispatch_mode(int mode, dim3 grid, size_t lds, hipStream_t st, const G
 //   2: R = 2, U = 4 for longer rows;
 //   3: as 2 with eight-wave workgroups, for long rows with many row groups:
 //      the input row is staged once per CU instead of twice (same LDS).
-// Largest input-row count M whose staged rows fit the 64 KB LDS budget for the
-// shortest row of each tile class (Q8_0: 16 weights per unit, Q4_0: 32, F32:
-// 4); combinations beyond it cannot be requested and are not instantiated.
+// LDS budget of the GEMV's staged input rows (the CU has 160 KB; the rest is
+// left for the kernel's own small arrays).
+constexpr size_t kGemvLdsMax = 128 * 1024;
+
+// Largest input-row count M (a power of two, at most 16) whose staged rows fit
+// the LDS budget for the shortest row of each tile class (class 0: any row;
+// class 1: 65 units; classes 2 and 3: 129 units; Q8_0 / Q6_K 16 weights per
+// unit, Q4_0 / Q4_K 32, F32 4); combinations beyond it cannot be requested and
+// are not instantiated.
 constexpr int gemv_max_m(int qt, int ru) {
-  return ru == 0 || qt == kF32 ? 16 : (int8_layout(qt) ? (ru == 1 ? 8 : 4) : (ru == 1 ? 4 : 2));
+  if (ru == 0) return 16;
+  const size_t units = ru == 1 ? 65 : 129;
+  const size_t k = units * (int8_layout(qt) ? 16 : (nibble_layout(qt) ? 32 : 4));
+  const size_t per_row = k * 4 + (nibble_layout(qt) ? k / 32 * 4 : 0);
+  int m = 16;
+  while (m > 1 && per_row * m > kGemvLdsMax) m /= 2;
+  return m;
 }
 
 template <int QT, int M, int RU, int R, int U, int NW = 4>

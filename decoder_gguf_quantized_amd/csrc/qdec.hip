@@ -251,8 +251,6 @@ void gemm_type(int type, int kind, int mode, dim3 grid, hipStream_t st, const Ge
   }
 }
 
-constexpr size_t kGemvLdsMax = 64 * 1024;
-
 // y[r][*] (op)= W x[r] for rows r < nrows, in launches of up to 16 rows that fit
 // the LDS budget.  y_ind: read the output base from device memory instead.
 // Residual prologue for sandwich norms: the input is x + RMSNorm(add) * add_w,
