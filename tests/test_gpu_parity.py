@@ -208,7 +208,8 @@ MATMUL_CASES = [
     (synth.T_Q4_0, 4100, 8192, 1), (synth.T_Q4_0, 4097, 4608, 2), (synth.T_Q8_0, 4100, 2080, 3),
     (synth.T_F32, 4100, 600, 5),
     # K-quants (repacked to 32-value blocks with f32 scales): every GEMV tile
-    # class, the eight-wave class, a split into two 8-row launches, both GEMM tiles
+    # class, the eight-wave class, staged input rows above 64 KB of LDS, both
+    # GEMM tiles
     (synth.T_Q4_K, 4096, 1024, 1), (synth.T_Q4_K, 1000, 2816, 3), (synth.T_Q4_K, 4100, 4608, 2),
     (synth.T_Q4_K, 300, 512, 17), (synth.T_Q4_K, 4224, 256, 1000),
     (synth.T_Q6_K, 4096, 1024, 1), (synth.T_Q6_K, 257, 1536, 16), (synth.T_Q6_K, 130, 14336, 2),
@@ -216,6 +217,9 @@ MATMUL_CASES = [
     # 256..511 tiles of 64 x 128: the f32 path takes the K-split tile, the bf16
     # paths the wide bf16 tile
     (synth.T_Q8_0, 2048, 512, 1000), (synth.T_Q4_0, 2304, 288, 900),
+    # input rows beyond the 128 KB LDS budget of one launch: two 8-row launches,
+    # and three launches of 2, 2 and 1 rows
+    (synth.T_Q8_0, 300, 4096, 16), (synth.T_Q4_0, 100, 14336, 5),
 ]
 
 
