@@ -266,3 +266,105 @@ def test_q_bias_is_irrelevant_when_keys_are_zero_and_k_bias_is_not():
     assert np.array_equal(run(bq1, zk["attn_k.bias"]), run(bq2, zk["attn_k.bias"]))
     d = np.max(np.abs(run(bq1, bk) - run(bq2, bk)))
     assert d > 1e-3
+
+
+def _post_norm_gains(name, cols):
+    """Distinct gains for the two sublayer post-norms, so that taking the other
+    sublayer's gain changes the result at every index."""
+    if name.endswith("post_attention_norm.weight"):
+        return np.linspace(0.5, 2.0, cols)
+    if name.endswith("post_ffw_norm.weight"):
+        return np.linspace(2.25, 0.75, cols)
+    return None
+
+
+def _post_normed_one_hot(y, gain, H, eps):
+    """RMSNorm of a vector whose only non-zero entry is y: mean square y^2 / H,
+    so the entry becomes gain * y / sqrt(y^2 / H + eps) (about sign(y) sqrt(H)
+    gain when y^2 >> H eps) and every other entry stays 0."""
+    return gain * y / math.sqrt(y * y / H + eps)
+
+
+@pytest.mark.parametrize("rv,head", [(5, 2), (2, 1)])
+def test_sandwich_attention_post_norm_closed_form(rv, head):
+    """Gemma-3 block reading (sandwich norms): the attention sublayer's output
+    W_o a is RMS-normalised with its own gain post_attention_norm and only then
+    added to the residual.  With Q = K = 0 (uniform attention), attn_v one-hot at
+    (rv, cv) and attn_output one-hot at (ro, co), the sublayer output is a
+    one-hot vector y e_ro with y = wo * mean_{j<=i}(wv h_j[cv]); its RMSNorm is
+    the closed form above, so x_i = e_{t_i} + that at ro.  The zero FFN adds
+    RMSNorm(0) = 0.  A norm after the residual add, the FFN's gain, a norm of
+    the attention output before W_o, or no norm all give other values."""
+    cfg = dict(TINY, n_layer=1, sandwich_norm=True)
+    H, hd = 16, 4
+    co = head * hd + rv % hd
+    cv, ro, wv, wo = 11, 6, 0.75, -1.25
+    base = rand_embed_zero_rest(3)
+
+    def fill(name, rows, cols):
+        if name.endswith("attn_v.weight"):
+            a = np.zeros((rows, cols)); a[rv, cv] = wv; return a
+        if name.endswith("attn_output.weight"):
+            a = np.zeros((rows, cols)); a[ro, co] = wo; return a
+        g = _post_norm_gains(name, cols)
+        return g if g is not None else base(name, rows, cols)
+    t = f32_model(cfg, fill)
+    m = OracleModel(cfg, t, max_ctx=8)
+    toks = [1, 4, 4, 7, 2]
+    x = m.hidden(0, toks)
+    E = np.frombuffer(t["token_embd.weight"].data.tobytes(), np.float32).reshape(10, 16).astype(np.float64)
+    ga = np.frombuffer(t["blk.0.attn_norm.weight"].data.tobytes(), np.float32).astype(np.float64)
+    gpa = np.linspace(0.5, 2.0, H).astype(np.float32).astype(np.float64)
+    h = np.array([E[k] / math.sqrt(np.mean(E[k] ** 2) + 1e-6) * ga for k in toks])
+    for i in range(len(toks)):
+        want = E[toks[i]].copy()
+        y = wo * np.mean(wv * h[:i + 1, cv])
+        want[ro] += _post_normed_one_hot(y, gpa[ro], H, 1e-6)
+        assert np.allclose(x[i], want, rtol=1e-12, atol=1e-13)
+        # the one-hot post-norm is about sign(y) sqrt(H) gain: far from y itself
+        assert abs(x[i][ro] - E[toks[i]][ro]) > 3.0 * abs(y)
+
+
+@pytest.mark.parametrize("act", ["silu", "gelu_tanh"])
+def test_sandwich_ffn_post_norm_closed_form(act):
+    """The FFN sublayer's output is RMS-normalised with post_ffw_norm before its
+    residual add.  Zero attention (attn_v = 0: the post-attention norm of a zero
+    vector is 0), ffn_gate and ffn_up one-hot in row kf (columns c1, c2) and
+    ffn_down one-hot at (ro, kf): per position m[kf] = act(wg h[c1]) (wu h[c2])
+    with h = RMSNorm(e_t, ffn_norm), the FFN output is wd m[kf] e_ro, and
+    x = e_t + (its one-hot RMSNorm) at ro."""
+    cfg = dict(TINY, n_layer=1, sandwich_norm=True, act=act)
+    H = 16
+    kf, c1, c2, ro = 7, 3, 12, 9
+    wg, wu, wd = 1.5, -0.75, 0.625  # exact in f32
+    base = rand_embed_zero_rest(4)
+
+    def fill(name, rows, cols):
+        a = np.zeros((rows, cols))
+        if name.endswith("ffn_gate.weight"):
+            a[kf, c1] = wg; return a
+        if name.endswith("ffn_up.weight"):
+            a[kf, c2] = wu; return a
+        if name.endswith("ffn_down.weight"):
+            a[ro, kf] = wd; return a
+        g = _post_norm_gains(name, cols)
+        return g if g is not None else base(name, rows, cols)
+    t = f32_model(cfg, fill)
+    m = OracleModel(cfg, t, max_ctx=8)
+    toks = [0, 5, 5, 8]
+    x = m.hidden(0, toks)
+    E = np.frombuffer(t["token_embd.weight"].data.tobytes(), np.float32).reshape(10, 16).astype(np.float64)
+    gf = np.frombuffer(t["blk.0.ffn_norm.weight"].data.tobytes(), np.float32).astype(np.float64)
+    gpf = np.linspace(2.25, 0.75, H).astype(np.float32).astype(np.float64)
+
+    def f(g):
+        if act == "silu":
+            return g / (1.0 + math.exp(-g))
+        return 0.5 * g * (1.0 + math.tanh(math.sqrt(2.0 / math.pi) * (g + 0.044715 * g ** 3)))
+    for i, tok in enumerate(toks):
+        e = E[tok]
+        h = e / math.sqrt(np.mean(e * e) + 1e-6) * gf
+        y = wd * f(wg * h[c1]) * (wu * h[c2])
+        want = e.copy()
+        want[ro] += _post_normed_one_hot(y, gpf[ro], H, 1e-6)
+        assert np.allclose(x[i], want, rtol=1e-12, atol=1e-13)
