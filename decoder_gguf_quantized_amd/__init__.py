@@ -99,6 +99,8 @@ def lib():
                 "qdec_decode_batch": (ctypes.c_int, [P, P, P, I32, P, P, F, F, U64, U64, U32, P]),
                 "qdec_kv_paged": (ctypes.c_int, [P, I32, I32, P]),
                 "qdec_kv_pages": (ctypes.c_int, [P, ctypes.POINTER(I32), ctypes.POINTER(I32), ctypes.POINTER(I32)]),
+                "qdec_decode_chunks": (ctypes.c_int, [P, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
+                "qdec_debug_inject_fault": (ctypes.c_int, [P, I32]),
             }
             for name, (res, args) in sig.items():
                 fn = getattr(L, name)
@@ -147,7 +149,11 @@ def _dev_ptr(name, t, dtype, min_numel):
 
 
 def _stream():
+    """The current HIP stream of torch, or the null stream when no GPU is
+    visible (host-only runs against a stand-in library: QDEC_LIB)."""
     import torch
+    if not torch.cuda.is_available():
+        return None
     return torch.cuda.current_stream().cuda_stream
 
 
@@ -415,6 +421,17 @@ class Model:
         vp = _dev_ptr("v", v, torch.float32, v.numel())
         self._check(lib().qdec_kv_write(h, _int("seq", seq), _int("layer", layer), kp, vp, _int("n_pos", n_pos),
                                         _stream()))
+
+    def decode_chunks(self):
+        """(positions per decode-attention chunk, chunks per sequence and KV head)."""
+        a, b = ctypes.c_int32(), ctypes.c_int32()
+        self._check(lib().qdec_decode_chunks(self._handle(), ctypes.byref(a), ctypes.byref(b)))
+        return a.value, b.value
+
+    def debug_inject_fault(self, armed=True):
+        """Arm (or disarm) a synthetic HIP error on the next kernel launch of a
+        call: that call then fails with status 2 and poisons the handle."""
+        self._check(lib().qdec_debug_inject_fault(self._handle(), 1 if armed else 0))
 
     def kv_len(self, seq):
         out = ctypes.c_int32()

@@ -15,6 +15,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <exception>
 #include <cstdlib>
 #include <new>
 #include <string>
@@ -143,6 +144,7 @@ struct qdec_model {
   int* err_dev = nullptr;
   std::vector<int> kvlen;
   bool poisoned = false;
+  int inject_fault = 0;  // qdec_debug_inject_fault: the next launch reports a synthetic error
   std::vector<void*> allocs;
   std::unordered_map<std::string, NameRef> names;
   bool timing = false;
@@ -204,10 +206,15 @@ struct Timed {
     }
   }
   ~Timed() noexcept(false) {
+    if (std::uncaught_exceptions()) return;  // unwinding already: the first error is reported
     hipck(hipGetLastError(), cls);
     if (a) {
       hipck(hipEventRecord(b, st), "hipEventRecord");
       m->krecs.push_back(KRec{cls, a, b, bytes, flops});
+    }
+    if (m && m->inject_fault) {  // the launch above is enqueued: the failure path drains it
+      m->inject_fault = 0;
+      throw HipError{std::string("injected fault after enqueueing ") + cls + " (qdec_debug_inject_fault)"};
     }
   }
 };
@@ -397,20 +404,13 @@ void attention_prefill(qdec_model* m, hipStream_t st, int l, int seq, int T, int
   Timed tm(m, st, "attn_prefill", (double)T * c.n_head * hd * 8 + (double)(pos0 + T) * c.n_head_kv * hd * 8,
            4.0 * hd * c.n_head * pairs);
   // the matrix-core kernels (32 queries per workgroup): head_dim 64 and 128
-  // whole-head per wave, 256 split over the four waves; caches of 2^31 rows
-  // per layer or more take the VALU kernel
-  if (m->kv_layer / hd < (size_t)INT32_MAX) {
-    dim3 grid((T + 31) / 32, c.n_head);
-    if (hd == 64) qlaunch(attn_prefill_mfma_kernel<64>, grid, 256, 0, st, a);
-    else if (hd == 128) qlaunch(attn_prefill_mfma_kernel<128>, grid, 256, 0, st, a);
-    else qlaunch(attn_prefill_dsplit_kernel<256>, grid, 256, 0, st, a);
-    return;
-  }
-  const int QT = 256 / (hd / 8);
-  dim3 grid((T + QT - 1) / QT, c.n_head);
-  if (hd == 64) qlaunch(attn_prefill_kernel<64, 64>, grid, 256, 0, st, a);
-  else if (hd == 128) qlaunch(attn_prefill_kernel<128, 32>, grid, 256, 0, st, a);
-  else qlaunch(attn_prefill_kernel<256, 16>, grid, 256, 0, st, a);
+  // whole-head per wave, 256 split over the four waves.  They index cache rows
+  // in 32 bits: the loader and qdec_kv_paged keep a layer below 2^31 rows.
+  if (m->kv_layer / hd >= (size_t)INT32_MAX) throw HipError{"prefill attention: cache layer of 2^31 rows or more"};
+  dim3 grid((T + 31) / 32, c.n_head);
+  if (hd == 64) qlaunch(attn_prefill_mfma_kernel<64>, grid, 256, 0, st, a);
+  else if (hd == 128) qlaunch(attn_prefill_mfma_kernel<128>, grid, 256, 0, st, a);
+  else qlaunch(attn_prefill_dsplit_kernel<256>, grid, 256, 0, st, a);
 }
 
 void rope_kv(qdec_model* m, hipStream_t st, int l, int n, int seq0, int pos0, const int* dpos) {
@@ -817,6 +817,11 @@ int load(const qdec_config* cfgp, const qdec_tensor* ts, int32_t n, int32_t max_
   }
   if (max_seqs < 1 || max_seqs > 64) { set_err("max_seqs must be in [1, 64], got %d", max_seqs); return QDEC_REFUSED; }
   if (max_ctx < 1) { set_err("max_ctx must be >= 1"); return QDEC_REFUSED; }
+  if ((int64_t)max_seqs * c.n_head_kv * max_ctx >= INT32_MAX) {
+    set_err("max_seqs x n_head_kv x max_ctx = %lld cache rows per layer; the kernels index fewer than 2^31",
+            (long long)max_seqs * c.n_head_kv * max_ctx);
+    return QDEC_REFUSED;
+  }
   if (n < 0 || (n > 0 && !ts)) { set_err("tensors: NULL array or negative count"); return QDEC_REFUSED; }
 
   // validate every tensor before allocating anything
@@ -1406,6 +1411,10 @@ int qdec_kv_paged(qdec_model* m, int32_t page_size, int32_t n_pages, void* strea
     set_err("page_size %d is too small for max_ctx %d (at least %d)", page_size, m->max_ctx, need);
     return QDEC_REFUSED;
   }
+  if ((int64_t)n_pages * c.n_head_kv * page_size >= INT32_MAX) {
+    set_err("a pool of %d pages of %d positions holds 2^31 cache rows per layer or more", n_pages, page_size);
+    return QDEC_REFUSED;
+  }
   const size_t layer = (size_t)n_pages * c.n_head_kv * page_size * c.head_dim;
   if ((double)layer * c.n_layer * 8.0 > 256.0 * (1ull << 30)) {
     set_err("a pool of %d pages of %d positions needs more than 256 GiB", n_pages, page_size);
@@ -1469,6 +1478,22 @@ int qdec_kv_len(const qdec_model* m, int32_t seq, int32_t* out) {
 }
 
 int qdec_poisoned(const qdec_model* m) { return m ? (m->poisoned ? 1 : 0) : -1; }
+
+int qdec_decode_chunks(const qdec_model* m, int32_t* chunk, int32_t* n_chunks) {
+  g_err.clear();
+  if (!m || !chunk || !n_chunks) { set_err("model and outputs must not be NULL"); return QDEC_REFUSED; }
+  *chunk = m->chunk;
+  *n_chunks = m->nchunk;
+  return QDEC_OK;
+}
+
+int qdec_debug_inject_fault(qdec_model* m, int32_t where) {
+  g_err.clear();
+  if (int rc = check_usable(m)) return rc;
+  if (where != 0 && where != 1) { set_err("where must be 0 (disarm) or 1 (arm), got %d", where); return QDEC_REFUSED; }
+  m->inject_fault = where;
+  return QDEC_OK;
+}
 
 int qdec_set_prefill_precision(qdec_model* m, int32_t precision) {
   g_err.clear();

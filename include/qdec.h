@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define QDEC_ABI_VERSION 4
+#define QDEC_ABI_VERSION 5
 
 enum { QDEC_OK = 0, QDEC_REFUSED = 1, QDEC_INTERNAL = 2 };
 
@@ -126,7 +126,8 @@ const char* qdec_last_error(void); /* valid until the next call on this thread *
  * positions.  `output.weight` is optional (absent: the head reuses
  * token_embd.weight, [S] `a | b`).  Synchronizes `stream` before returning.
  * Limits: 1 <= max_seqs <= 64; hidden and head_dim multiples of 32 and head_dim
- * in {64, 128, 256}; n_head a multiple of n_head_kv. */
+ * in {64, 128, 256}; n_head a multiple of n_head_kv; fewer than 2^31 cache rows
+ * per layer (max_seqs * n_head_kv * max_ctx). */
 int qdec_load_weights(const qdec_config* cfg, const qdec_tensor* tensors, int32_t n_tensors,
                       int32_t max_seqs, int32_t max_ctx, void* stream, qdec_model** out);
 
@@ -194,7 +195,8 @@ int qdec_prefill(qdec_model* m, int32_t seq, const int32_t* tokens, int32_t n_to
  * floor(2^40 * 2^((l - max l) * log2(e) / temperature)) (f32) summed exactly;
  * a row with a non-finite logit keeps every token.  top_p >= 1: no restriction.
  * With QDEC_TOKENS_ON_DEVICE, tokens is a device pointer; ids outside [0, vocab)
- * are clamped and latch an error reported as QDEC_INTERNAL by the next call.
+ * are clamped and latch a host-mapped error word: the first call made after
+ * the stream has run that step returns QDEC_INTERNAL and poisons the handle.
  * Refused: n_seqs outside [1, max_seqs], any kv_len(s) == max_ctx, a host token
  * out of range, temperature < 0 or NaN, top_p NaN, NULL outputs. */
 int qdec_decode_step(qdec_model* m, const int32_t* tokens, int32_t n_seqs, float* d_logits,
@@ -230,8 +232,11 @@ int qdec_kv_paged(qdec_model* m, int32_t page_size, int32_t n_pages, void* strea
 /* The cache's page size (0 = contiguous), pool size and free pages. */
 int qdec_kv_pages(const qdec_model* m, int32_t* page_size, int32_t* n_pages, int32_t* n_free);
 
-/* Forget the cached positions of one sequence (seq = -1: all).  Host-side only;
- * stale KV rows are never read past kv_len. */
+/* Forget the cached positions of one sequence (seq = -1: all), so that its next
+ * prefill starts at position 0 ([W] Step 9: each generation starts from an empty
+ * cache; a new prompt is a new sequence).  Host-side only, nothing is enqueued;
+ * stale KV rows are never read past kv_len.  Refused: seq outside [-1, max_seqs),
+ * a poisoned handle. */
 int qdec_kv_reset(qdec_model* m, int32_t seq);
 
 /* Roll sequence seq back to its first n positions (0 <= n <= kv_len(seq)), for
@@ -244,21 +249,38 @@ int qdec_kv_truncate(qdec_model* m, int32_t seq, int32_t n);
 int qdec_kv_write(qdec_model* m, int32_t seq, int32_t layer, const float* d_k, const float* d_v,
                   int32_t n_pos, void* stream);
 
+/* Number of cached positions of sequence seq ([W] Step 9: the position of the
+ * next token), written to *out.  Host-side only.  Refused: NULL pointers, seq out
+ * of range. */
 int qdec_kv_len(const qdec_model* m, int32_t seq, int32_t* out);
+
+/* Positions per decode-attention chunk and chunks per (sequence, KV head) of the
+ * split over positions ([W] Step 5's attention, summed chunk by chunk with an
+ * online softmax), as sized at load (and by qdec_kv_paged).  Host-side only. */
+int qdec_decode_chunks(const qdec_model* m, int32_t* chunk, int32_t* n_chunks);
 
 /* Operand precision of later prefill projections (QDEC_PREFILL_*; default F32).
  * Refused: an unknown value. */
 int qdec_set_prefill_precision(qdec_model* m, int32_t precision);
 int qdec_poisoned(const qdec_model* m); /* 1 if latched, 0 if not, -1 for NULL */
 
-/* Release everything the handle owns, after draining its last stream (bounded
- * wait, 30 s).  Call exactly once per handle. */
+/* Release everything the handle owns -- weights, KV cache, workspace, captured
+ * graphs -- after draining its last stream (bounded wait, 30 s), as [T]
+ * "Handle ownership, closing and errors" requires of a handle's close: work in
+ * flight may still read or write the memory.  Call exactly once per handle: a
+ * second call is undefined behaviour (there is no registry of live handles).
+ * A poisoned handle is freed the same way.  Refused: NULL. */
 int qdec_free(qdec_model* m);
 
 /* ---------------------------------------------------------------- tests and measurement */
 
-/* Decode the named tensor (as loaded) to f32 [rows][cols] in d_out with the same
- * in-kernel dequantization the forward pass uses.  Bit-exact by construction. */
+/* Decode the named tensor (as loaded) to f32 [rows][cols] in d_out: element
+ * (r, k) is d * q (Q8_0), d * (n - 8) (Q4_0) or the K-quant forms, one exact
+ * f32 product each (an fp16 scale times a small integer needs at most 19
+ * significant bits), so any exact decode matches it bit for bit.  This is a
+ * separate decode kernel: the projection kernels never form d * q (the GEMV
+ * scales each block's dot product, the GEMMs decode their own LDS tiles);
+ * qdec_debug_matmul with one-hot input rows checks those bit for bit. */
 int qdec_debug_dequant(qdec_model* m, const char* name, float* d_out, void* stream);
 
 /* Embedding gather of n device token ids into d_out f32 [n][hidden]. */
@@ -279,6 +301,14 @@ int qdec_debug_sample(const float* d_logits, int32_t rows, int32_t vocab, float 
 int qdec_debug_matmul(int32_t type, int64_t rows, int64_t cols, const void* host_data,
                       int64_t n_bytes, const float* d_x, int32_t n_x, float* d_y, int32_t precision,
                       void* stream);
+
+/* Test hook for the failure path of [T] "Handle ownership, closing and errors"
+ * (status 2, drain, poisoned latch).  where = 1 arms it: the next call that
+ * launches a kernel enqueues that kernel, then fails as a HIP error would --
+ * status QDEC_INTERNAL, the stream drained with the bounded wait, the handle
+ * latched as poisoned.  Host-side: no device fault occurs.  where = 0 disarms.
+ * Refused: other values, a NULL or poisoned handle. */
+int qdec_debug_inject_fault(qdec_model* m, int32_t where);
 
 /* Per-kernel timing with HIP events on the launch stream.  enable = 1 starts
  * recording every launch; enable = 0 synchronizes, writes up to max_out records

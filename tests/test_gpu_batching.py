@@ -240,6 +240,9 @@ def test_decode_chunk_that_is_not_a_power_of_two():
         with qdec.Model(cfg, t, max_seqs=1, max_ctx=2100) as m:
             if paged:
                 m.kv_paged(64, 40)
+            # the split the library chose: 48-position chunks (44 of them), or
+            # the 64-position pages' chunk (33 of them)
+            assert m.decode_chunks() == ((64, 33) if paged else (48, 44))
             om = OracleModel(cfg, t, max_ctx=120, n_seqs=1)
             pl = torch.empty((1, V), dtype=torch.float32, device=dev())
             tok = torch.empty(1, dtype=torch.int32, device=dev())

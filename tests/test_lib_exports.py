@@ -34,7 +34,8 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version(L):
-    assert L.qdec_abi_version() == 4
+    want = int(re.search(r"#define QDEC_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert L.qdec_abi_version() == want
 
 
 def cfg(**kw):
@@ -93,6 +94,8 @@ def test_null_handle_calls_are_refused(L):
     assert L.qdec_kv_paged(None, 64, 4, None) == 1
     a, b, c = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     assert L.qdec_kv_pages(None, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)) == 1
+    assert L.qdec_decode_chunks(None, ctypes.byref(a), ctypes.byref(b)) == 1
+    assert L.qdec_debug_inject_fault(None, 1) == 1
 
 
 def test_binding_range_checks_and_ownership():
