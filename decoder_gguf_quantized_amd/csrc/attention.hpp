@@ -406,82 +406,11 @@ struct AttnPrefillArgs {
   KvMap map;
 };
 
-// Workgroup = (tile of 256/LG consecutive queries, one query head).  K/V tiles
-// of KT keys are staged in LDS and shared by all queries of the tile.
-template <int HD, int KT>
-__global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
-  constexpr int LG = HD / 8;
-  constexpr int QT = 256 / LG;
-  __shared__ float4 Ks[KT][HD / 4];
-  __shared__ float4 Vs[KT][HD / 4];
-  const int tid = threadIdx.x, gi = tid / LG, li = tid % LG;
-  // signed copies: the window bound below goes negative for early tiles
-  const int bx = (int)blockIdx.x, h = (int)blockIdx.y, g = h / (a.nq / a.nkv);
-  const int t = bx * QT + gi;
-  const bool active = t < a.T;
-  const int p = a.pos0 + t;
-  const int tlast = min(a.T, (bx + 1) * QT) - 1;
-  const int kmax = a.pos0 + tlast;
-  const int kmin = a.window > 0 ? max(0, a.pos0 + bx * QT - a.window + 1) : 0;
-
-  float q[8], o[8], m = -INFINITY, l = 0.f;
-  {
-    const int tq = active ? t : 0;
-    const float4* qp = reinterpret_cast<const float4*>(a.q + (size_t)tq * a.nq * HD + (size_t)h * HD + li * 8);
-    float4 q0 = qp[0], q1 = qp[1];
-    q[0] = q0.x * a.scale_log2; q[1] = q0.y * a.scale_log2; q[2] = q0.z * a.scale_log2; q[3] = q0.w * a.scale_log2;
-    q[4] = q1.x * a.scale_log2; q[5] = q1.y * a.scale_log2; q[6] = q1.z * a.scale_log2; q[7] = q1.w * a.scale_log2;
-  }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = 0.f;
-  const float4* kc4 = reinterpret_cast<const float4*>(a.kc);
-  const float4* vc4 = reinterpret_cast<const float4*>(a.vc);
-  const int jlo = active ? (a.window > 0 ? max(0, p - a.window + 1) : 0) : 1;
-  const int jhi = active ? p : 0;
-
-  for (int j0 = kmin; j0 <= kmax; j0 += KT) {
-    const int nk = min(KT, kmax - j0 + 1);
-    __syncthreads();
-    // rows placed one by one: a window layer's tiles start anywhere, so a tile
-    // may straddle two pages
-    for (int i = tid; i < nk * (HD / 4); i += 256) {
-      int kk = i / (HD / 4), dv = i % (HD / 4);
-      const size_t r = kv_row(a.map, a.nkv, a.ctx, a.seq, g, j0 + kk);
-      Ks[kk][dv] = kc4[r * (HD / 4) + dv];
-      Vs[kk][dv] = vc4[r * (HD / 4) + dv];
-    }
-    __syncthreads();
-    const int a0 = max(jlo, j0), a1 = min(jhi, j0 + nk - 1);
-    for (int j = a0; j <= a1; ++j) {
-      const int kk = j - j0;
-      float4 k0 = Ks[kk][li * 2], k1 = Ks[kk][li * 2 + 1];
-      float dot = q[0] * k0.x + q[1] * k0.y + q[2] * k0.z + q[3] * k0.w +
-                  q[4] * k1.x + q[5] * k1.y + q[6] * k1.z + q[7] * k1.w;
-      float sc = group_sum<LG>(dot);
-      float mn = fmaxf(m, sc);
-      float corr = exp2f(m - mn);
-      float pr = exp2f(sc - mn);
-      l = l * corr + pr;
-      float4 v0 = Vs[kk][li * 2], v1 = Vs[kk][li * 2 + 1];
-      o[0] = o[0] * corr + pr * v0.x; o[1] = o[1] * corr + pr * v0.y;
-      o[2] = o[2] * corr + pr * v0.z; o[3] = o[3] * corr + pr * v0.w;
-      o[4] = o[4] * corr + pr * v1.x; o[5] = o[5] * corr + pr * v1.y;
-      o[6] = o[6] * corr + pr * v1.z; o[7] = o[7] * corr + pr * v1.w;
-      m = mn;
-    }
-  }
-  if (active) {
-    float inv = 1.0f / l;
-    float4* op = reinterpret_cast<float4*>(a.out + (size_t)t * a.nq * HD + (size_t)h * HD + li * 8);
-    op[0] = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
-    op[1] = make_float4(o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv);
-  }
-}
-
 // ------------------------------------------------------------ prefill attention on the matrix cores
-// The same online softmax as attn_prefill_kernel, with both products on
-// V_MFMA_F32_32X32X2_F32 (f32 operands, f32 accumulation); head_dim 64 and
-// 128.  Workgroup = 32 queries x one query head; its four waves take the
+// The online softmax of the decode kernel for T queries at once, with both
+// products on V_MFMA_F32_32X32X2_F32 (f32 operands, f32 accumulation); head_dim
+// 64 and 128.  Cache rows are indexed in 32 bits (the loader keeps every
+// layer's cache below 2^31 rows).  Workgroup = 32 queries x one query head; its four waves take the
 // 32-key tiles of the queries' key range in turn and merge their (max, sum,
 // output) at the end.
 //

@@ -24,6 +24,7 @@
 //     cost is one conversion and one FMA.
 #pragma once
 #include <type_traits>
+#include <utility>
 
 #include "common.hpp"
 
@@ -378,6 +379,16 @@ QD_DEV void gemv_store(const GemvArgs& a, int grp, int lane, const float (&scale
   }
 }
 
+// f(integral_constant<int, i>) for i = 0 .. N-1, in order (compile-time indices).
+template <typename F, int... I>
+QD_DEV void for_idx_seq(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+QD_DEV void for_idx(F& f) {
+  for_idx_seq(f, std::make_integer_sequence<int, N>{});
+}
+
 // Register sets of the weight pipeline: with NS sets, NS - 1 tiles are in
 // flight while one is computed.  Three sets for the small tiles (R * U <= 4,
 // 20 VGPRs per set for the quantized types), two for the 8-unit tiles.
@@ -392,9 +403,9 @@ constexpr int gemv_sets() { return (R * U <= 4 && M <= 4) ? 3 : 2; }
 // tiles are requested before the input rows are staged.  Tile indices are
 // wave-uniform (scalar registers), so every load is a scalar base plus a 32-bit
 // lane offset.
-template <int QT, int M, int MODE, int R, int U, int NW, bool RES>
+template <int QT, int M, int MODE, int R, int U, int NW, bool RES, int NSO = 0>
 __global__ __launch_bounds__(64 * NW) void gemv_kernel(GemvArgs a) {
-  constexpr int NS = gemv_sets<R, U, M>();
+  constexpr int NS = NSO ? NSO : gemv_sets<R, U, M>();
   extern __shared__ float4 xs4[];
   const int kp = a.nblk * 32;
   float* xsum = reinterpret_cast<float*>(xs4 + M * kp / 4);  // nibble layouts: [M][nblk] block sums of x
@@ -426,8 +437,8 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(GemvArgs a) {
       }
     }
   };
-  request(std::integral_constant<int, 0>{});
-  if constexpr (NS > 2) request(std::integral_constant<int, 1>{});
+  // the first NS - 1 tiles
+  for_idx<NS - 1>(request);
 
   float scale[M];
   gemv_stage_x<QT, M, NW, RES>(a, xs4, kp, scale);  // ends with a barrier
@@ -465,9 +476,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(GemvArgs a) {
     if (tt[s] == tpg - 1) gemv_store<QT, M, MODE, R, U>(a, tg[s], lane, scale, acc);
   };
   while (!done) {
-    step(std::integral_constant<int, 0>{});
-    step(std::integral_constant<int, 1>{});
-    if constexpr (NS > 2) step(std::integral_constant<int, 2>{});
+    for_idx<NS>(step);
   }
 }
 

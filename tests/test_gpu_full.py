@@ -2,10 +2,11 @@
 bench.py uses (same max_ctx / max_seqs, hence the same split-position chunking).
 
 Where the oracle cannot redo a whole workload in seconds, the comparison is on
-sampled outputs: a shorter prompt through the full-size model (every layer,
-every matrix at full shape), sampled rows, sampled sequences of the batch.  The
-full-length prompt is covered by a property that holds at any size: decode
-logits equal the logits of a prefill over the same tokens.
+sampled outputs: sampled rows of the prompt (the 8B shape's whole 1,024-token
+prompt; shorter prompts through the full-size models elsewhere), a few decode
+steps, sampled sequences of the batch.  Decode at the full length is also
+covered by a property that holds at any size: decode logits equal the logits
+of a prefill over the same tokens.
 """
 import gc
 
@@ -55,7 +56,10 @@ def oracle_rows(cfg, tensors, tokens, rows, cache_weights=True):
 @pytest.mark.parametrize("key,T,n,sample_rows", [
     ("c2", 512, 8, [0, 100, 511]),
     ("c4", 600, 4, [0, 511, 512, 599]),
-    ("c3", 96, 4, [0, 95]),
+    # the 8B shape's whole 1,024-token prompt (wide prefill tiles at 8B
+    # projection shapes, 1,024-key MFMA attention), then two decode steps; the
+    # oracle decodes each matrix as it goes (its float64 weights would need 60 GB)
+    ("c3", 1024, 2, [0, 511, 1023]),
 ])
 def test_full_shape_prefill_and_decode(key, T, n, sample_rows):
     cfg = synth.get(key)

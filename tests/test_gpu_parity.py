@@ -243,6 +243,40 @@ def test_projection_matches_oracle(ttype, rows, cols, n_x):
 GEMM_CASES = [c for c in MATMUL_CASES if c[3] > 16 and c[0] in (synth.T_Q8_0, synth.T_Q4_0)]
 
 
+def one_hot_columns(cols, n_x):
+    """Columns k_t picked by input row t: the first and last column, block
+    edges and a spread over the row, cycling when n_x exceeds them."""
+    base = sorted({0, cols - 1, min(31, cols - 1), min(32, cols - 1), cols // 2, max(0, cols - 33)})
+    spread = [(t * 7919) % cols for t in range(n_x)]
+    return [(base + spread)[t] for t in range(n_x)]
+
+
+@pytest.mark.parametrize("precision", ["f32", "bf16x3"])
+@pytest.mark.parametrize("ttype,rows,cols,n_x", MATMUL_CASES)
+def test_projection_kernels_decode_weights_bit_exact(ttype, rows, cols, n_x, precision):
+    """The projection kernels themselves decode every weight exactly: with input
+    row t one-hot at column k_t, output (t, n) is the single product W[n][k_t] * 1
+    plus exact zeros, so it must equal the oracle's exact dequantisation bit for
+    bit (up to the sign of zero) -- through each GEMV tile class (n_x <= 16), the
+    wide and K-split f32 GEMM tiles and the three-term bf16 tile."""
+    if precision == "bf16x3" and (n_x <= 16 or ttype not in (synth.T_Q8_0, synth.T_Q4_0)):
+        pytest.skip("the bf16 tile serves Q8_0 / Q4_0 prefill projections only")
+    rng = np.random.default_rng(rows * 3 + cols + n_x)
+    w = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
+    raw = synth.encode(ttype, w)
+    kp = ((cols + 31) // 32) * 32
+    ks = one_hot_columns(cols, n_x)
+    x = np.zeros((n_x, kp), np.float32)
+    x[np.arange(n_x), ks] = 1.0
+    y = torch.empty((n_x, rows), dtype=torch.float32, device=dev())
+    qdec.debug_matmul(ttype, rows, cols, raw, torch.from_numpy(x).to(dev()), y, precision=precision)
+    W = blocks.dequant(ttype, raw, rows, cols)
+    want = W[:, ks].T
+    got = as_np(y)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} outputs differ, first at {tuple(bad[0])}: {got[tuple(bad[0])]!r} vs {want[tuple(bad[0])]!r}"
+
+
 @pytest.mark.parametrize("ttype,rows,cols,n_x", GEMM_CASES)
 def test_projection_bf16x3_matches_oracle(ttype, rows, cols, n_x):
     """The three-term bf16 split is exact: same bar as the f32 kernels, and in
