@@ -16,7 +16,7 @@ import os
 import threading
 
 __all__ = ["Model", "QdecError", "QdecPanic", "QdecPoisoned", "lib", "config_struct",
-           "debug_sample", "debug_matmul", "gguf_config", "archdef_builtin", "T_F32", "T_Q4_0", "T_Q8_0", "ALL_LOGITS", "TOKENS_ON_DEVICE"]
+           "debug_sample", "sample_noalloc", "debug_matmul", "gguf_config", "archdef_builtin", "T_F32", "T_Q4_0", "T_Q8_0", "ALL_LOGITS", "TOKENS_ON_DEVICE"]
 
 T_F32, T_Q4_0, T_Q8_0 = 0, 2, 8
 ALL_LOGITS, TOKENS_ON_DEVICE = 1, 2
@@ -101,6 +101,7 @@ def lib():
                 "qdec_kv_pages": (ctypes.c_int, [P, ctypes.POINTER(I32), ctypes.POINTER(I32), ctypes.POINTER(I32)]),
                 "qdec_decode_chunks": (ctypes.c_int, [P, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
                 "qdec_debug_inject_fault": (ctypes.c_int, [P, I32]),
+                "qdec_sample_noalloc": (ctypes.c_int, [P, I32, I32, F, F, U64, U64, P, P]),
             }
             for name, (res, args) in sig.items():
                 fn = getattr(L, name)
@@ -476,6 +477,19 @@ def debug_sample(logits, temperature, seed, step, out, top_p=1.0):
     rc = lib().qdec_debug_sample(_dev_ptr("logits", logits, torch.float32, rows * vocab), _int("rows", rows),
                                  _int("vocab", vocab), float(temperature), float(top_p), _int("seed", seed, _U64),
                                  _int("step", step, _U64), _dev_ptr("out", out, torch.int32, rows), _stream())
+    if rc:
+        raise (QdecError if rc == 1 else QdecPanic)(_last_error())
+
+
+def sample_noalloc(logits, temperature, seed, step, out, top_p=1.0):
+    """debug_sample's rule through the allocation-free entry point (partials in
+    the library's fixed device scratch; rows <= 64, vocab <= 2^20; no host
+    wait)."""
+    import torch
+    rows, vocab = logits.shape
+    rc = lib().qdec_sample_noalloc(_dev_ptr("logits", logits, torch.float32, rows * vocab), _int("rows", rows),
+                                   _int("vocab", vocab), float(temperature), float(top_p), _int("seed", seed, _U64),
+                                   _int("step", step, _U64), _dev_ptr("out", out, torch.int32, rows), _stream())
     if rc:
         raise (QdecError if rc == 1 else QdecPanic)(_last_error())
 

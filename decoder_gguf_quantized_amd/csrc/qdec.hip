@@ -19,6 +19,7 @@
 #include <cstdlib>
 #include <new>
 #include <string>
+#include <mutex>
 #include <thread>
 #include <unordered_map>
 #include <vector>
@@ -1233,6 +1234,52 @@ int decode_impl(qdec_model* m, const int32_t* seqs, const int32_t* tokens, int32
 
 }  // namespace
 
+// ------------------------------------------------------------ allocation-free sampling
+// qdec_sample_noalloc keeps its partial results in this file-scope device
+// array instead of memory it allocates: per row, one (value, index) pair per
+// 4,096-entry vocab chunk, and the top-p cut (key, index).  Offsets are fixed:
+// values at 0, indices at 64 KiB, cut keys at 128 KiB, cut indices 256 bytes
+// later.  Each GPU the library runs on holds its own copy until the process
+// ends.  Host code never passes the array's name to a kernel (on the host it
+// is only a stand-in for the symbol): the device address comes from
+// hipGetSymbolAddress, taken once per device.
+constexpr int kNoAllocRows = 64;
+constexpr int kNoAllocVocab = 1 << 20;
+constexpr size_t kNoAllocPart = (size_t)kNoAllocRows * (kNoAllocVocab / kSampleChunk) * 4;  // 64 KiB
+constexpr size_t kNoAllocScratch = 2 * kNoAllocPart + 2 * kNoAllocRows * 4;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratch];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];  // device address of `scratch` on each device, once looked up
+
+// The device address of `scratch` on the current device (looked up on the
+// first call made on that device).  Null with the error text set on failure.
+unsigned char* scratch_address() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    set_err("internal: hipGetDevice: %s", hipGetErrorString(e));
+    return nullptr;
+  }
+  if (dev < 0 || dev >= 64) {
+    set_err("internal: device %d outside the 64 the scratch table holds", dev);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      set_err("internal: hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return static_cast<unsigned char*>(g_scratch_ptr[dev]);
+}
+}  // namespace
+
 // ================================================================= C ABI
 // Error text for the host-only sources of the library (model files).
 __attribute__((visibility("hidden"))) void qdec_set_error_text(const std::string& s) { g_err = s; }
@@ -1581,6 +1628,49 @@ int qdec_debug_sample(const float* d_logits, int32_t rows, int32_t vocab, float 
   (void)hipFree(ck);
   (void)hipFree(ci);
   if (e != hipSuccess) { set_err("internal: %s", hipGetErrorString(e)); return QDEC_INTERNAL; }
+  return QDEC_OK;
+}
+
+int qdec_sample_noalloc(const float* d_logits, int32_t rows, int32_t vocab, float temperature, float top_p,
+                        uint64_t seed, uint64_t step, int32_t* d_out, void* stream) {
+  g_err.clear();
+  if (!d_logits || !d_out) { set_err("d_logits and d_out must not be NULL"); return QDEC_REFUSED; }
+  if (rows < 1 || rows > kNoAllocRows) {
+    set_err("rows %d outside [1, %d] (the fixed scratch holds %d rows)", rows, kNoAllocRows, kNoAllocRows);
+    return QDEC_REFUSED;
+  }
+  if (vocab < 1 || vocab > kNoAllocVocab) {
+    set_err("vocab %d outside [1, %d] (the fixed scratch holds %d chunks of %d per row)", vocab, kNoAllocVocab,
+            kNoAllocVocab / kSampleChunk, kSampleChunk);
+    return QDEC_REFUSED;
+  }
+  if (!(temperature >= 0.f) || !std::isfinite(temperature)) { set_err("temperature must be finite and >= 0"); return QDEC_REFUSED; }
+  if (std::isnan(top_p)) { set_err("top_p must not be NaN"); return QDEC_REFUSED; }
+  unsigned char* ptr = scratch_address();
+  if (!ptr) return QDEC_INTERNAL;
+  hipStream_t st = (hipStream_t)stream;
+  const int nch = (vocab + kSampleChunk - 1) / kSampleChunk;
+  const bool topp = temperature > 0.f && top_p < 1.f;
+  float* pv = reinterpret_cast<float*>(ptr);
+  int* pi = reinterpret_cast<int*>(ptr + kNoAllocPart);
+  uint32_t* ck = reinterpret_cast<uint32_t*>(ptr + 2 * kNoAllocPart);
+  int* ci = reinterpret_cast<int*>(ptr + 2 * kNoAllocPart + kNoAllocRows * 4);
+  // every partial the sampling kernels read is written first in the same call
+  // (stage 1 writes all rows x chunks, the top-p cut all rows): nothing to clear
+  SampleArgs a{d_logits, vocab, vocab, rows, temperature, seed, step, pv, pi, nch, d_out, nullptr, nullptr,
+               topp ? ck : nullptr, topp ? ci : nullptr};
+  try {
+    if (topp) {
+      TopPArgs t{d_logits, vocab, vocab, rows, temperature, top_p, ck, ci, nullptr};
+      qlaunch(topp_cut_kernel, rows, 1024, 0, st, t);
+    }
+    qlaunch(sample_stage1_kernel, dim3(nch, rows), 256, 0, st, a);
+    qlaunch(sample_stage2_kernel, rows, 64, 0, st, a);
+    hipck(hipGetLastError(), "sampling launch");
+  } catch (const HipError& e) {
+    set_err("internal: %s", e.msg.c_str());
+    return QDEC_INTERNAL;
+  }
   return QDEC_OK;
 }
 

@@ -293,6 +293,19 @@ int qdec_debug_embed(qdec_model* m, const int32_t* d_tokens, int32_t n, float* d
 int qdec_debug_sample(const float* d_logits, int32_t rows, int32_t vocab, float temperature,
                       float top_p, uint64_t seed, uint64_t step, int32_t* d_out, void* stream);
 
+/* qdec_debug_sample without allocation, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same rule and same kernels as qdec_debug_sample; the
+ * partial results live in a fixed file-scope device array of the library
+ * (131,584 bytes per GPU, held until the process ends), so rows <= 64 and
+ * vocab <= 2^20 (refused otherwise, status 1).  Enqueued on `stream` without a
+ * host wait (qdec_debug_sample synchronizes).  Calls that overlap on one GPU --
+ * on different streams, or from several threads -- share that array and race:
+ * the caller orders them (one stream, or events).  Status 2 on a launch error
+ * (no handle is involved, so nothing is poisoned). */
+int qdec_sample_noalloc(const float* d_logits, int32_t rows, int32_t vocab, float temperature, float top_p,
+                        uint64_t seed, uint64_t step, int32_t* d_out, void* stream);
+
 /* One projection y[r][n] = sum_k W[n][k] x[r][k] with the forward pass's kernels:
  * the decode GEMV for n_x <= 16, the prefill MFMA GEMM above (operands in
  * `precision`, QDEC_PREFILL_*).  W is given in GGUF bytes on the host (uploaded

@@ -223,6 +223,12 @@ int qdec_debug_sample(const float* d_logits, int32_t rows, int32_t vocab, float 
   (void)d_logits; (void)temp; (void)top_p; (void)seed; (void)step; (void)d_out; (void)stream;
   return QDEC_REFUSED;
 }
+int qdec_sample_noalloc(const float* d_logits, int32_t rows, int32_t vocab, float temp, float top_p, uint64_t seed,
+                        uint64_t step, int32_t* d_out, void* stream) {
+  rec("sample_noalloc %d %d", rows, vocab);
+  (void)d_logits; (void)temp; (void)top_p; (void)seed; (void)step; (void)d_out; (void)stream;
+  return QDEC_REFUSED;
+}
 int qdec_debug_matmul(int32_t type, int64_t rows, int64_t cols, const void* host_data, int64_t n_bytes,
                       const float* d_x, int32_t n_x, float* d_y, int32_t precision, void* stream) {
   rec("debug_matmul %d", type);
