@@ -38,23 +38,18 @@ struct AttnDecodeArgs {
   const float2* rope;   // [B][hd/2] (cos, sin) of f32(pos[s]) * inv_freq[i]: each sequence's
                         // row of the layer's RoPE table, copied at step start
   float scale_log2;     // hd^-1/2 * log2(e)
-  float* part_o;        // [B][nq][nchunk][hd], unnormalised partial outputs
-  float* part_ml;       // [B][nq][nchunk][2]: running max (log2 domain), sum
-  int* counter;         // [B][nkv] finished-chunk counters, zero between launches
-  float* out;           // [B][nq*hd] merged attention output
+  float* acc;           // this layer's accumulators: kAccCopies blocks of o [rows][nq][hd]
+                        // then l [rows][nq] (zero on entry); chunk c adds into block
+                        // c % kAccCopies
+  float* acc_clear;     // the other layer parity's accumulators, zeroed here for the next layer
+  int acc_rows;         // rows (max_seqs) of each accumulator block
+  int* err;             // host-mapped error word (2: a chunk's scores beyond the merge's range)
   const int* seq;       // [B] sequence slot of each row, or null (row b is sequence b)
   KvMap map;            // cache layout (the paged kernel reads map.table)
 };
 
-// Device-coherent (write-through / L2-bypassing) accesses for the cross-
-// workgroup partials: the L2s of the eight dies are not coherent with each
-// other, and these keep the merge free of whole-cache write-back/invalidate.
-QD_DEV void store_coherent(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-QD_DEV float load_coherent(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Most position chunks per (sequence, KV head); the launcher sizes chunks so.
+// Most position chunks per (sequence, KV head); the launcher sizes chunks so
+// (it bounds the grid at long contexts).
 constexpr int kMaxChunks = 64;
 
 QD_DEV void attn_key_range(int p, int window, int& lo, int& hi) {
@@ -111,32 +106,49 @@ QD_DEV void store_lane8(float* rowp, int hd, int li, const float (&v)[8]) {
 }
 
 // Workgroup = (chunk of positions, KV head, sequence); it serves the KV head's
-// whole group of query heads.  Prologue: QK-norm + RoPE of the group's queries,
-// and, in the chunk that holds the new position, of the new key, which it also
-// appends (with the new value) to the cache.  Each workgroup writes one partial
-// (m, l, o) per query head; the workgroup that finishes last among the chunks
-// of its (sequence, KV head) merges them (a counter, no workgroup waits):
-//   O = sum_c o_c 2^(m_c - M) / sum_c l_c 2^(m_c - M),  M = max_c m_c.
+// whole group of query heads.  Prologue: QK-norm + RoPE of the group's queries
+// and of the new key; the chunk that holds the new position also appends the
+// new key and value to the cache.
+//
+// Merge without a second round trip.  A split softmax needs a common reference
+// for the chunks' maxima.  Every workgroup can compute the same one without
+// communicating: the new token's own score R_h = q_h . k_new (every query sees
+// its own key, on every layer, windowed or not), evaluated by every workgroup
+// with the same operations on the same registers, so the values agree bit for
+// bit.  A workgroup reduces its streams to (M, L, O) per head, rescales them
+// to R_h by f = 2^(M - R_h) and adds f L and f O into f32 accumulators with
+// hardware atomic adds: no counter, no wait, no last-workgroup merge (which
+// cost about 4.5 us of the 8B-shape layer's 11.9 us: store acknowledgements,
+// the counter's round trip, the merging workgroup's loads).  Chunks alternate
+// between two accumulator blocks: adds to one address are serialised in the
+// memory system, and two blocks halve that chain.  The consumer (the O
+// projection's input staging) sums the blocks and divides:
+//   o_h = sum_c f_c O_c / sum_c f_c L_c,
+// the softmax-weighted sum of the values, as with any common reference.  The
+// new key's own term has weight 2^0 = 1, so the denominator is at least 1; a
+// chunk whose maximum lies 100 or more log2 units above R_h (or whose scores
+// are NaN) would leave f32's range, so it latches *err = 2 (the next call
+// reports it) instead.  The adds are f32 and their order varies from run to
+// run, so decode results agree to f32 rounding, not bit for bit.
+// The accumulators of the two layer parities alternate: this launch zeroes
+// the other parity's blocks, which the previous layer's O projection has
+// finished reading and the next layer's attention adds into.
 //
 // Latency: the kernel is a short chain of dependent memory round trips, so
 // every request that does not need the new position goes out before it
 // arrives: the RoPE row (copied per sequence at step start), the raw queries
 // and new key/value, and on full-causal layers the chunk's first keys and
 // values (a chunk's addresses do not depend on the position; keys past it are
-// masked).  The key loop keeps two position pairs per stream in flight, and the
-// merge requests every chunk's (m, l) together with the outputs' values.
+// masked).  The key loop keeps two position pairs per stream in flight.
 // PAGED: the cache is paged; a chunk lies in one page (the host keeps chunks
 // no longer than a page), so one table entry per workgroup places all of it.
 template <int HD, int G, bool PAGED>
 __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
   constexpr int LG = HD / 8;      // lanes per position
   constexpr int NG = 256 / LG;    // position streams per workgroup
-  constexpr int E = (G * HD + 255) / 256;  // merged outputs per thread
-  constexpr int CB = 64 / E;               // chunks per merge request batch (a multiple of 8)
   __shared__ float sm_o[NG][G][HD];
   __shared__ float sm_m[NG][G], sm_l[NG][G];
-  __shared__ float sm_pm[G][kMaxChunks], sm_pl[G][kMaxChunks];
-  __shared__ int sm_last;
+  __shared__ float sm_f[G];
 
   const int c = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x, gi = tid / LG, li = tid % LG;
@@ -197,6 +209,15 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
   if (spec) fetch_pair(cb + gi, ka, va);
   if (b_ready) fetch_pair(cb + 2 * NG + gi, kb, vb);
 
+  // the other parity's accumulators are zeroed by all workgroups together,
+  // before any of them can return
+  {
+    const int nwg = gridDim.x * gridDim.y * gridDim.z;
+    const int wg = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const size_t n = (size_t)kAccCopies * a.acc_rows * a.nq * (HD + 1);
+    for (size_t i = (size_t)wg * 256 + tid; i < n; i += (size_t)nwg * 256) a.acc_clear[i] = 0.f;
+  }
+
   int lo, hi;
   attn_key_range(p, a.window, lo, hi);
   const int c_lo = lo / a.chunk, c_hi = hi / a.chunk;
@@ -207,7 +228,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
   const int jb0 = spec ? cb : cb + ((start - cb) / (2 * NG)) * (2 * NG);
   if (!spec) fetch_pair(jb0 + gi, ka, va);
 
-  float o[G][8], m[G], l[G];
+  float o[G][8], m[G], l[G], ref[G];
+  norm_rope_group<LG>(kn, qkn, wk, a.eps, HD, cs, sn);
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     norm_rope_group<LG>(q[h], qkn, wq, a.eps, HD, cs, sn);
@@ -218,14 +240,17 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
     }
     m[h] = -INFINITY;
     l[h] = 0.f;
+    // the merge reference: the new key's score (the same expression as its
+    // score in the walk below)
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dot += q[h][e] * kn[e];
+    ref[h] = group_sum<LG>(dot);
   }
   const bool has_new = c == c_hi;
-  if (has_new) {
-    norm_rope_group<LG>(kn, qkn, wk, a.eps, HD, cs, sn);
-    if (gi == 0) {
-      store_lane8(a.kc + (head_base + p) * HD, HD, li, kn);
-      store_lane8(a.vc + (head_base + p) * HD, HD, li, vn);
-    }
+  if (has_new && gi == 0) {
+    store_lane8(a.kc + (head_base + p) * HD, HD, li, kn);
+    store_lane8(a.vc + (head_base + p) * HD, HD, li, vn);
   }
   // online softmax over one position; masked positions leave the state as is
   // (selects, no branch: every lane of a stream group takes the same path).
@@ -279,9 +304,13 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
     }
   }
   __syncthreads();
-  // streams -> one partial per head: wave w takes heads w, w + 4, ...; lane k
+  // streams -> one (M, L) per head: wave w takes heads w, w + 4, ...; lane k
   // holds stream k's (m, l), and the head's max, weights and denominator are
-  // wave reductions (NG <= 64 streams)
+  // wave reductions (NG <= 64 streams).  Then the factor to the reference, and
+  // the denominator's add.
+  float* acc_blk = a.acc + (size_t)(c % kAccCopies) * ((size_t)a.acc_rows * a.nq * (HD + 1));
+  float* acc_o = acc_blk + ((size_t)s * a.nq + g * G) * HD;
+  float* acc_l = acc_blk + (size_t)a.acc_rows * a.nq * HD + (size_t)s * a.nq + g * G;
   {
     const int lane = tid & 63, wave = tid >> 6;
 #pragma unroll
@@ -293,10 +322,18 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
       const float w = mk == -INFINITY ? 0.f : exp2f(mk - M);
       const float L = wave_sum(w * lk);
       if (on) sm_m[lane][h] = w;  // the stream's weight replaces its max
+      float rh = ref[0];  // ref[h] without a dynamic register index
+#pragma unroll
+      for (int t = 1; t < G; ++t) rh = t == h ? ref[t] : rh;
       if (lane == 0) {
-        const size_t pi = ((size_t)s * a.nq + g * G + h) * a.nchunk + c;
-        store_coherent(a.part_ml + pi * 2 + 0, M);
-        store_coherent(a.part_ml + pi * 2 + 1, L);
+        float d = M - rh;
+        if (!(d < 100.f)) {  // beyond f32's exponent range (or NaN scores): report, add nothing
+          if (a.err) *a.err = 2;
+          d = -INFINITY;
+        }
+        const float f = exp2f(d);
+        sm_f[h] = f;
+        unsafeAtomicAdd(acc_l + h, L * f);
       }
     }
   }
@@ -306,93 +343,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
     float O = 0.f;
 #pragma unroll
     for (int k = 0; k < NG; ++k) O += sm_o[k][h][dd] * sm_m[k][h];
-    const size_t pi = ((size_t)s * a.nq + g * G + h) * a.nchunk + c;
-    store_coherent(a.part_o + pi * HD + dd, O);
+    unsafeAtomicAdd(acc_o + idx, O * sm_f[h]);
   }
-  // every partial store of this workgroup is complete before the counter moves
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (tid == 0) {
-    const int done = __hip_atomic_fetch_add(a.counter + s * a.nkv + g, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sm_last = done == c_hi - c_lo;
-  }
-  __syncthreads();
-  if (!sm_last) return;
-  // merge.  Wave w takes heads w, w + 4, ...: lane cc requests chunk cc's
-  // (m, l) (nact <= kMaxChunks = 64 lanes), and the head's max M, weights
-  // 2^(m_c - M) and denominator sum_c l_c 2^(m_c - M) are wave reductions; the
-  // weights go to LDS.  Thread output e (element tid + 256 e of the group's
-  // G x HD block) requests its values of CB chunks per batch together with the
-  // (m, l) loads, at clamped chunk indices (chunks past the last are masked),
-  // so up to CB chunks cost one round trip.  Sums run in chunk order.
-  const int nact = c_hi - c_lo + 1;  // <= kMaxChunks (the launcher sizes chunks so)
-  const size_t pbase = ((size_t)s * a.nq + g * G) * a.nchunk + c_lo;
-  constexpr int HW = (G + 3) / 4;  // heads per wave
-  float mlm[HW], mll[HW];
-  const int lane = tid & 63, wave = tid >> 6;
-#pragma unroll
-  for (int t = 0; t < HW; ++t) {
-    const int h = min(wave + 4 * t, G - 1), cc = min(lane, nact - 1);
-    const size_t pi = pbase + (size_t)h * a.nchunk + cc;
-    mlm[t] = load_coherent(a.part_ml + pi * 2);
-    mll[t] = load_coherent(a.part_ml + pi * 2 + 1);
-  }
-  int hh[E];
-  const float* po[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int idx = min(tid + 256 * e, G * HD - 1);
-    hh[e] = idx / HD;
-    po[e] = a.part_o + (pbase + (size_t)hh[e] * a.nchunk) * HD + idx % HD;
-  }
-  float O[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) O[e] = 0.f;
-  float* sm_w = &sm_pm[0][0];  // [G][kMaxChunks] chunk weights
-  float* sm_L = &sm_pl[0][0];  // [G] denominators
-  auto batch = [&](int c0, auto FIRST) {
-    float ov[E][CB];
-#pragma unroll
-    for (int c8 = 0; c8 < CB; c8 += 8) {
-      if (c0 + c8 < nact) {  // whole groups of 8 past the last chunk are skipped (uniform)
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-#pragma unroll
-          for (int cc = c8; cc < c8 + 8; ++cc) ov[e][cc] = load_coherent(po[e] + (size_t)min(c0 + cc, nact - 1) * HD);
-      }
-    }
-    if constexpr (decltype(FIRST)::value) {
-#pragma unroll
-      for (int t = 0; t < HW; ++t) {
-        const int h = wave + 4 * t;
-        const bool on = lane < nact;
-        const float mc = on ? mlm[t] : -INFINITY;
-        const float M = wave_max(mc);
-        const float w = (on && mc != -INFINITY) ? exp2f(mc - M) : 0.f;
-        const float L = wave_sum(w * (on ? mll[t] : 0.f));
-        if (h < G) {
-          sm_w[h * kMaxChunks + lane] = w;
-          if (lane == 0) sm_L[h] = L;
-        }
-      }
-      __syncthreads();
-    }
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const float* wr = sm_w + hh[e] * kMaxChunks + c0;
-#pragma unroll
-      for (int cc = 0; cc < CB; ++cc)
-        if (c0 + cc < nact) O[e] += ov[e][cc] * wr[cc];
-    }
-  };
-  batch(0, std::true_type{});
-  for (int c0 = CB; c0 < nact; c0 += CB) batch(c0, std::false_type{});
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int idx = tid + 256 * e;
-    if (idx < G * HD) a.out[(size_t)s * a.nq * HD + (size_t)g * G * HD + idx] = O[e] / sm_L[hh[e]];
-  }
-  if (tid == 0) __hip_atomic_store(a.counter + s * a.nkv + g, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 struct AttnPrefillArgs {

@@ -43,6 +43,10 @@ QD_DEV size_t kv_row(const KvMap& mp, int nkv, int ctx, int s, int g, int j) {
   return (((size_t)pg * nkv + g) << mp.log2p) + (j & ((1 << mp.log2p) - 1));
 }
 
+// Accumulator blocks per layer parity of decode attention's merge (chunk c adds
+// into block c % kAccCopies; the O projection's input staging sums them).
+constexpr int kAccCopies = 2;
+
 // Types stored as 16 nibble bytes per 32-value block / as int8 per value.
 constexpr bool nibble_layout(int qt) { return qt == kQ4_0 || qt == kQ4_K; }
 constexpr bool int8_layout(int qt) { return qt == kQ8_0 || qt == kQ6_K; }

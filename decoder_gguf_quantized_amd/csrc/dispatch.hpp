@@ -43,6 +43,14 @@ void gemv_dispatch_mode(int mode, dim3 grid, size_t lds, hipStream_t st, const G
     }
     return;
   }
+  if (a.xd) {  // input from decode attention's accumulators: the O projection (store or add)
+    switch (mode) {
+      case kModeStore: qlaunch(gemv_kernel<QT, M, kModeStore, R, U, NW, false, true>, grid, nt, lds, st, a); break;
+      case kModeAdd: qlaunch(gemv_kernel<QT, M, kModeAdd, R, U, NW, false, true>, grid, nt, lds, st, a); break;
+      default: throw HipError{"gemv: attention-accumulator input with a pair epilogue"};
+    }
+    return;
+  }
   switch (mode) {
     case kModeStore: qlaunch(gemv_kernel<QT, M, kModeStore, R, U, NW, false>, grid, nt, lds, st, a); break;
     case kModeAdd: qlaunch(gemv_kernel<QT, M, kModeAdd, R, U, NW, false>, grid, nt, lds, st, a); break;

@@ -24,7 +24,6 @@
 //     cost is one conversion and one FMA.
 #pragma once
 #include <type_traits>
-#include <utility>
 
 #include "common.hpp"
 
@@ -55,7 +54,45 @@ struct GemvArgs {
   const float* bias;     // store mode: y[n] += bias[n] (qwen2's q/k/v bias adds), or null
   const uint32_t* sd;    // K-quants: super-block scales [rows][nblk / 8]; `d` then holds the
                          // per-sub-block words (Q4_K u16, Q6_K int8 per 16 values)
+  // Input from decode attention's accumulators instead of x: element k of row
+  // mi is sum_b xd[b][mi][k] / sum_b xl[b][mi][k / xhd] over the kAccCopies
+  // blocks b (xcstride floats apart; rows [m][ldx] and [m][ldx / xhd]): the
+  // split softmax's final division.
+  const float* xd;
+  const float* xl;
+  int xhd;
+  long xcstride;
 };
+
+// Input row mi, floats 4 k4 .. 4 k4 + 3 (zero past the launch's rows).  ACC:
+// from decode attention's accumulators (a separate instantiation, so that the
+// plain kernels keep their register budget).
+template <bool ACC>
+QD_DEV float4 load_x4(const GemvArgs& a, int mi, int k4, bool ok) {
+  if (!ok || mi >= a.m) return make_float4(0.f, 0.f, 0.f, 0.f);
+  if constexpr (ACC) {
+    float4 u[kAccCopies];
+    float lb[kAccCopies];
+#pragma unroll
+    for (int b = 0; b < kAccCopies; ++b) {  // every block's loads go out together
+      u[b] = reinterpret_cast<const float4*>(a.xd + b * a.xcstride + (size_t)mi * a.ldx)[k4];
+      lb[b] = a.xl[b * a.xcstride + (size_t)mi * (a.ldx / a.xhd) + (4 * k4) / a.xhd];
+    }
+    float4 o = u[0];
+    float l = lb[0];
+#pragma unroll
+    for (int b = 1; b < kAccCopies; ++b) {
+      o.x += u[b].x;
+      o.y += u[b].y;
+      o.z += u[b].z;
+      o.w += u[b].w;
+      l += lb[b];
+    }
+    const float r = 1.0f / l;
+    return make_float4(o.x * r, o.y * r, o.z * r, o.w * r);
+  }
+  return reinterpret_cast<const float4*>(a.x)[(size_t)mi * (a.ldx / 4) + k4];
+}
 
 QD_DEV float act_silu(float g) { return g / (1.0f + expf(-g)); }
 QD_DEV float act_gelu_tanh(float x) {
@@ -104,7 +141,7 @@ constexpr int unit_floats() { return int8_layout(QT) ? 16 : (nibble_layout(QT) ?
 // unit, so for each slot i consecutive lanes read consecutive float4s: no bank
 // conflicts (the natural layout puts every lane's unit 64 or 128 bytes apart,
 // which lands all lanes on a handful of banks).
-template <int QT, int M, int NW, bool RES>
+template <int QT, int M, int NW, bool RES, bool ACC>
 QD_DEV void gemv_stage_x(const GemvArgs& a, float4* xs4, int kp, float (&scale)[M]) {
   constexpr int NT = 64 * NW;  // threads of the workgroup
   constexpr int US = unit_floats<QT>(), NV = US / 4;
@@ -116,7 +153,6 @@ QD_DEV void gemv_stage_x(const GemvArgs& a, float4* xs4, int kp, float (&scale)[
   __shared__ float red[NW][M];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool norm = a.norm_w != nullptr;
-  const float4* x4 = reinterpret_cast<const float4*>(a.x);
   const float4* w4 = reinterpret_cast<const float4*>(a.norm_w);
   const int ldx4 = a.ldx / 4;
   float ss[M];
@@ -171,8 +207,7 @@ QD_DEV void gemv_stage_x(const GemvArgs& a, float4* xs4, int kp, float (&scale)[
       const bool ok = k4 < NK4;
       wv[j] = (ok && norm) ? w4[k4] : make_float4(1.f, 1.f, 1.f, 1.f);
 #pragma unroll
-      for (int mi = 0; mi < M; ++mi)
-        xv[j][mi] = (ok && mi < a.m) ? x4[(size_t)mi * ldx4 + k4] : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int mi = 0; mi < M; ++mi) xv[j][mi] = load_x4<ACC>(a, mi, k4, ok);
       if constexpr (RES) {
         const float4 rw = ok ? r4[k4] : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -379,16 +414,6 @@ QD_DEV void gemv_store(const GemvArgs& a, int grp, int lane, const float (&scale
   }
 }
 
-// f(integral_constant<int, i>) for i = 0 .. N-1, in order (compile-time indices).
-template <typename F, int... I>
-QD_DEV void for_idx_seq(F& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-QD_DEV void for_idx(F& f) {
-  for_idx_seq(f, std::make_integer_sequence<int, N>{});
-}
-
 // Register sets of the weight pipeline: with NS sets, NS - 1 tiles are in
 // flight while one is computed.  Three sets for the small tiles (R * U <= 4,
 // 20 VGPRs per set for the quantized types), two for the 8-unit tiles.
@@ -403,9 +428,9 @@ constexpr int gemv_sets() { return (R * U <= 4 && M <= 4) ? 3 : 2; }
 // tiles are requested before the input rows are staged.  Tile indices are
 // wave-uniform (scalar registers), so every load is a scalar base plus a 32-bit
 // lane offset.
-template <int QT, int M, int MODE, int R, int U, int NW, bool RES, int NSO = 0>
+template <int QT, int M, int MODE, int R, int U, int NW, bool RES, bool ACC = false>
 __global__ __launch_bounds__(64 * NW) void gemv_kernel(GemvArgs a) {
-  constexpr int NS = NSO ? NSO : gemv_sets<R, U, M>();
+  constexpr int NS = gemv_sets<R, U, M>();
   extern __shared__ float4 xs4[];
   const int kp = a.nblk * 32;
   float* xsum = reinterpret_cast<float*>(xs4 + M * kp / 4);  // nibble layouts: [M][nblk] block sums of x
@@ -437,11 +462,11 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(GemvArgs a) {
       }
     }
   };
-  // the first NS - 1 tiles
-  for_idx<NS - 1>(request);
+  request(std::integral_constant<int, 0>{});
+  if constexpr (NS > 2) request(std::integral_constant<int, 1>{});
 
   float scale[M];
-  gemv_stage_x<QT, M, NW, RES>(a, xs4, kp, scale);  // ends with a barrier
+  gemv_stage_x<QT, M, NW, RES, ACC>(a, xs4, kp, scale);  // ends with a barrier
   if constexpr (nibble_layout(QT)) {
     for (int i = threadIdx.x; i < M * a.nblk; i += 64 * NW) {
       const int mi = i / a.nblk, u = i % a.nblk;
@@ -476,7 +501,9 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(GemvArgs a) {
     if (tt[s] == tpg - 1) gemv_store<QT, M, MODE, R, U>(a, tg[s], lane, scale, acc);
   };
   while (!done) {
-    for_idx<NS>(step);
+    step(std::integral_constant<int, 0>{});
+    step(std::integral_constant<int, 1>{});
+    if constexpr (NS > 2) step(std::integral_constant<int, 2>{});
   }
 }
 

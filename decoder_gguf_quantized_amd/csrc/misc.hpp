@@ -634,6 +634,8 @@ struct StepArgs {
   const float2* rope_l;
   float2* rope_cur;      // [2][max_seqs][half]: each sequence's rows at its new position
   int half, max_seqs;
+  float* acc_clear;      // decode attention's layer-0 accumulators to zero (models with an odd
+  long acc_n;            // number of layers, where the last layer does not clear them), or null
 };
 
 // Per-step values of a decode step that the replayed graph reads from device
@@ -654,6 +656,8 @@ __global__ __launch_bounds__(256) void step_begin_kernel(StepArgs a) {
     }
     a.d_tok[i] = t;
   }
+  if (a.acc_clear)
+    for (long e = i; e < a.acc_n; e += blockDim.x) a.acc_clear[e] = 0.f;
   const int per = a.n * a.half;
   for (int e = i; e < 2 * per; e += blockDim.x) {
     const int tbl = e / per, r = e % per, sq = r / a.half, k = r % a.half;

@@ -117,8 +117,10 @@ struct qdec_model {
   int ws_T = 0;
   float *x = nullptr, *h = nullptr, *qkv = nullptr, *q = nullptr, *a = nullptr, *m = nullptr, *y = nullptr;
   float* x2 = nullptr;  // second residual buffer (decode with sandwich norms)
-  float* part_o = nullptr;
-  float* part_ml = nullptr;
+  float* acc = nullptr;   // decode attention's accumulators: two layer parities, each
+                          // kAccCopies blocks of [max_seqs][n_head][head_dim] (o) then
+                          // [max_seqs][n_head] (l)
+  size_t acc_blk = 0;     // floats per block (a parity holds kAccCopies blocks)
   int chunk = 0, nchunk = 0;
   int chunk_base = 0;  // decode chunk for a paged cache: the load-time chunk rounded up to a
                        // power of two (then capped at the page size)
@@ -136,7 +138,6 @@ struct qdec_model {
   int* d_table = nullptr;           // [max_seqs][table_w] page of each position block
   std::vector<int> free_pages;      // pages no sequence holds (a stack)
   std::vector<std::vector<int>> seq_pages;  // pages each sequence holds, in position order
-  int* counters = nullptr;          // [max_seqs][n_head_kv] decode-attention chunk counters
   StepParams* d_params = nullptr;   // per-step values read by replayed graphs
   hipStream_t cap_stream = nullptr; // capture stream for the decode graphs
   std::unordered_map<int, hipGraphExec_t> graphs;  // decode graph per batch size
@@ -269,9 +270,17 @@ struct Resid {
   float* out = nullptr;
 };
 
+// Input from decode attention's accumulators (row r, element k: o[r][k] / l[r][k / hd]).
+struct AccIn {
+  const float* o = nullptr;
+  const float* l = nullptr;
+  int hd = 0;
+  size_t stride = 0;  // floats between accumulator blocks
+};
+
 void gemv(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, const float* norm_w, float eps,
           float* y, int ldy, int nrows, int mode, float* const* y_ind = nullptr, Resid res = Resid{},
-          const float* bias = nullptr) {
+          const float* bias = nullptr, AccIn acc = AccIn{}) {
   if (bias && mode != kModeStore) throw HipError{"gemv: a bias needs the store epilogue"};
   const int kp = w.nblk * 32;
   const size_t per_row = (size_t)kp * 4 + (nibble_layout(w.type) ? (size_t)w.nblk * 4 : 0);
@@ -293,12 +302,19 @@ void gemv(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, 
     const int mr = std::min(cap, nrows - r0);
     int M = 1;
     while (M < mr) M *= 2;
-    GemvArgs a{w.qs, w.d, w.rows, w.nblk, x + (size_t)r0 * ldx, ldx, norm_w, eps,
+    GemvArgs a{w.qs, w.d, w.rows, w.nblk, x ? x + (size_t)r0 * ldx : nullptr, ldx, norm_w, eps,
                y ? y + (size_t)r0 * ldy : nullptr, ldy, mr, y_ind, (long)r0 * ldy,
                res.add ? res.add + (size_t)r0 * ldx : nullptr, res.add_w,
                res.out ? res.out + (size_t)r0 * ldx : nullptr, bias, w.sd};
+    if (acc.o) {
+      a.xd = acc.o + (size_t)r0 * ldx;
+      a.xl = acc.l + (size_t)r0 * (ldx / acc.hd);
+      a.xhd = acc.hd;
+      a.xcstride = (long)acc.stride;
+    }
     const size_t lds = per_row * M;
-    const double bytes = w.gguf_bytes + (double)mr * kp * 4 + (double)mr * (pair ? w.rows / 2 : w.rows) * 4;
+    const double bytes =
+        w.gguf_bytes + (double)mr * kp * (acc.o ? 4 * kAccCopies : 4) + (double)mr * (pair ? w.rows / 2 : w.rows) * 4;
     Timed tm(m, st, gemv_class(w.type), bytes, 2.0 * mr * w.rows * (double)w.cols);
     gemv_type(w.type, M, ru, mode, grid, lds, st, a);
   }
@@ -373,8 +389,10 @@ void attention_decode(qdec_model* m, hipStream_t st, int l, int B, bool slotted)
   const float scale_log2 = (float)(1.0 / std::sqrt((double)hd) * 1.4426950408889634);
   AttnDecodeArgs a{m->qkv, m->nqkv, m->kc + l * m->kv_layer, m->vc + l * m->kv_layer, m->max_ctx, m->d_pos,
                    c.n_head, c.n_head_kv, layer_window(m, l), m->chunk, m->nchunk, L.q_norm, L.k_norm, c.rms_eps,
-                   m->rope_cur + (L.global ? 0 : (size_t)m->max_seqs * (hd / 2)), scale_log2, m->part_o, m->part_ml,
-                   m->counters, m->a, slotted ? m->d_seq : nullptr, m->map()};
+                   m->rope_cur + (L.global ? 0 : (size_t)m->max_seqs * (hd / 2)), scale_log2,
+                   m->acc + (size_t)(l % 2) * kAccCopies * m->acc_blk,
+                   m->acc + (size_t)((l + 1) % 2) * kAccCopies * m->acc_blk, m->max_seqs, m->err_dev,
+                   slotted ? m->d_seq : nullptr, m->map()};
   double kvbytes = 0;
   for (int s = 0; s < B; ++s) {
     int p = m->kvlen[(size_t)s < m->row_seq.size() ? m->row_seq[s] : s];
@@ -501,13 +519,17 @@ void blocks(qdec_model* m, hipStream_t st, int n, int seq, int pos0, const int* 
       rope_kv(m, st, l, n, seq, pos0, nullptr);
       attention_prefill(m, st, l, seq, n, pos0);
     }
+    // decode: the O projection's input is attention's merge, o / l from the
+    // accumulators of this layer's parity
+    const float* acc_o = m->acc + (size_t)(l % 2) * kAccCopies * m->acc_blk;
+    const AccIn acc{acc_o, acc_o + (size_t)m->max_seqs * m->qd, c.head_dim, m->acc_blk};
     if (fuse) {
-      gemv(m, st, L.o, m->a, m->qd, nullptr, 0.f, m->y, H, n, kModeStore);
+      gemv(m, st, L.o, nullptr, m->qd, nullptr, 0.f, m->y, H, n, kModeStore, nullptr, Resid{}, nullptr, acc);
     } else if (c.sandwich_norm) {
       gemm(m, st, L.o, m->a, m->qd, n, m->y, H, kModeStore);
       rmsnorm_rows(m, st, m->y, H, L.post_attn, H, m->x, H, n, 1);
     } else {
-      if (dec) gemv(m, st, L.o, m->a, m->qd, nullptr, 0.f, m->x, H, n, kModeAdd);
+      if (dec) gemv(m, st, L.o, nullptr, m->qd, nullptr, 0.f, m->x, H, n, kModeAdd, nullptr, Resid{}, nullptr, acc);
       else gemm(m, st, L.o, m->a, m->qd, n, m->x, H, kModeAdd);
     }
     // feed-forward sublayer
@@ -581,10 +603,17 @@ int check_usable(qdec_model* m) {
     set_err("poisoned: an earlier GPU failure latched this handle; free it and load again");
     return QDEC_REFUSED;
   }
-  if (m->err_host && __atomic_load_n(m->err_host, __ATOMIC_ACQUIRE)) {
-    m->poisoned = true;
-    set_err("internal: a device-resident token id was outside [0, vocab) (clamped); handle poisoned");
-    return QDEC_INTERNAL;
+  if (m->err_host) {
+    const int e = __atomic_load_n(m->err_host, __ATOMIC_ACQUIRE);
+    if (e) {
+      m->poisoned = true;
+      if (e == 2)
+        set_err("internal: decode attention met scores 100 or more log2 units above the new token's own "
+                "score (or NaN scores); handle poisoned");
+      else
+        set_err("internal: a device-resident token id was outside [0, vocab) (clamped); handle poisoned");
+      return QDEC_INTERNAL;
+    }
   }
   return QDEC_OK;
 }
@@ -1034,8 +1063,9 @@ int load(const qdec_config* cfgp, const qdec_tensor* ts, int32_t n, int32_t max_
       m->chunk_base = p2;
       m->nchunk = (max_ctx + ch - 1) / ch;
     }
-    m->part_o = m->dalloc<float>((size_t)max_seqs * c.n_head * m->nchunk * c.head_dim);
-    m->part_ml = m->dalloc<float>((size_t)max_seqs * c.n_head * m->nchunk * 2);
+    m->acc_blk = (size_t)max_seqs * c.n_head * (c.head_dim + 1);
+    m->acc = m->dalloc<float>(2 * kAccCopies * m->acc_blk);
+    hipck(hipMemsetAsync(m->acc, 0, 2 * kAccCopies * m->acc_blk * sizeof(float), st), "memset");
     m->nvchunk = (c.vocab + kSampleChunk - 1) / kSampleChunk;
     m->s_v = m->dalloc<float>((size_t)max_seqs * m->nvchunk);
     m->s_i = m->dalloc<int>((size_t)max_seqs * m->nvchunk);
@@ -1045,8 +1075,6 @@ int load(const qdec_config* cfgp, const qdec_tensor* ts, int32_t n, int32_t max_
     m->d_tok = m->dalloc<int>(64);
     m->d_seq = m->dalloc<int>(64);
     m->seq_pages.assign(max_seqs, {});
-    m->counters = m->dalloc<int>((size_t)max_seqs * c.n_head_kv);
-    hipck(hipMemsetAsync(m->counters, 0, (size_t)max_seqs * c.n_head_kv * 4, st), "memset");
     m->d_params = m->dalloc<StepParams>(1);
     hipck(hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking), "hipStreamCreate");
     m->d_prompt = m->dalloc<int>(T);
@@ -1199,6 +1227,11 @@ int decode_impl(qdec_model* m, const int32_t* seqs, const int32_t* tokens, int32
     sa.rope_cur = m->rope_cur;
     sa.half = c.head_dim / 2;
     sa.max_seqs = m->max_seqs;
+    // attention of layer l clears the accumulators of layer l + 1's parity;
+    // with an odd layer count the last layer has layer 0's parity, so the step
+    // clears it here
+    sa.acc_clear = c.n_layer % 2 ? m->acc : nullptr;
+    sa.acc_n = (long)(kAccCopies * m->acc_blk);
     {
       Timed tm(m, st, "step_begin", 0, 0);
       qlaunch(step_begin_kernel, 1, 256, 0, st, sa);
@@ -1484,12 +1517,6 @@ int qdec_kv_paged(qdec_model* m, int32_t page_size, int32_t n_pages, void* strea
     m->table_w = (m->max_ctx + page_size - 1) / page_size;
     m->d_table = m->dalloc<int>((size_t)m->max_seqs * m->table_w);
     hipck(hipMemsetAsync(m->d_table, 0, (size_t)m->max_seqs * m->table_w * 4, st), "memset");
-    if (nchunk > m->nchunk) {
-      m->dfree(m->part_o);
-      m->dfree(m->part_ml);
-      m->part_o = m->dalloc<float>((size_t)m->max_seqs * c.n_head * nchunk * c.head_dim);
-      m->part_ml = m->dalloc<float>((size_t)m->max_seqs * c.n_head * nchunk * 2);
-    }
     m->chunk = chunk;
     m->nchunk = nchunk;
     m->kv_layer = layer;

@@ -7,7 +7,7 @@
   each slot as its own sequence; greedy tokens as in the other parity tests,
   fed back by teacher forcing.
 - The same schedule on a paged cache (pages recycled between sequences) and
-  on the contiguous cache: bit-identical logits (the paging changes addresses
+  on the contiguous cache: the same logits up to f32 rounding (the paging changes addresses
   only; the page size equals the decode chunk, so the split is the same).
 - A sliding-window model whose prefill tiles straddle pages.
 - Sampled decode of a slot: the token is the oracle sampler's on the GPU's own
@@ -20,7 +20,7 @@ import pytest
 
 import synth
 from oracle import OracleModel, sampler
-from tests.gpu_helpers import SMALL, as_np, check_row, token_agrees
+from tests.gpu_helpers import SMALL, as_np, check_row, rel_err, token_agrees
 
 pytestmark = pytest.mark.gpu
 
@@ -124,7 +124,9 @@ def test_paged_cache_is_bit_identical_to_the_contiguous_one(qwen3_pair):
     b = run_schedule(paged, cfg, pages=True)
     assert a.keys() == b.keys()
     for k in a:
-        assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32)), k
+        # decode attention adds its chunks' partials with f32 atomics, whose
+        # order varies from run to run: agreement to f32 rounding, not bits
+        assert rel_err(b[k], a[k]) < 1e-5, k
     om = OracleModel(cfg, t, max_ctx=256, n_seqs=4)
     run_schedule(paged, cfg, om, pages=True)
 
