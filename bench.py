@@ -18,7 +18,12 @@ import os
 import sys
 import time
 
-import numpy as np
+if "--cpu-threads" in sys.argv:  # BLAS thread counts are fixed when numpy first loads
+    _n = sys.argv[sys.argv.index("--cpu-threads") + 1]
+    for _k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[_k] = _n
+
+import numpy as np  # noqa: E402
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -118,6 +123,31 @@ def cpu_baseline(cfg, tensors, budget_s=20.0):
     return dict(value=1.0 / per_tok, unit="tokens/s", cores=cores, kind="oracle",
                 sample=f"{cfg['name']}: {T0}-token prefill ({t_pre:.1f} s), then {n} greedy decode steps timed "
                        f"({t_dec:.1f} s){what}; float64 numpy, {cores} host threads")
+
+
+def cpu_oracle_full(cfg, threads):
+    """The oracle over a whole workload (prefill of the full prompt, then every
+    greedy decode step), timed with perf_counter; ``threads`` host threads.
+    Returns one JSON-able record.  Runs without a GPU."""
+    from oracle import OracleModel
+    import synth
+    tensors = synth.generate(cfg)
+    T, N = cfg["prompt_len"], cfg["decode_steps"]
+    om = OracleModel(cfg, tensors, max_ctx=T + N + 1)
+    prompt = synth.prompt(cfg)
+    t0 = time.perf_counter()
+    logits = om.forward(0, prompt)
+    t_pre = time.perf_counter() - t0
+    tok = int(np.argmax(logits[-1]))
+    t0 = time.perf_counter()
+    for _ in range(N):
+        logits = om.forward(0, [tok])
+        tok = int(np.argmax(logits[-1]))
+    t_dec = time.perf_counter() - t0
+    return dict(workload=cfg["name"], kind="oracle", cores=threads, prompt=T, decode_steps=N,
+                prefill_s=round(t_pre, 3), prefill_tokens_per_s=round(T / t_pre, 3),
+                decode_s=round(t_dec, 3), decode_tokens_per_s=round(N / t_dec, 3),
+                note="float64 numpy; prefill includes decoding every matrix once to float64")
 
 
 def kernel_sources_hash():
@@ -285,6 +315,10 @@ def main():
                     help="operand precision of the prefill projections (default f32)")
     ap.add_argument("--top-p", type=float, default=None,
                     help="batched workload only: restrict sampling to the top-p nucleus (default: none)")
+    ap.add_argument("--cpu-oracle-full", default=None, metavar="CONFIG",
+                    help="time the CPU oracle over the whole workload (no GPU) and print its record")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="with --cpu-oracle-full: host threads (default: all available)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 256 MiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -294,6 +328,11 @@ def main():
         sys.exit(2)
 
     cores = len(os.sched_getaffinity(0))
+    if args.cpu_oracle_full:
+        n = args.cpu_threads or cores  # (set in the environment at import when given)
+        import synth
+        print(json.dumps(cpu_oracle_full(synth.get(args.cpu_oracle_full), n)), flush=True)
+        return
     os.environ.setdefault("OMP_NUM_THREADS", str(cores))
     os.environ.setdefault("OPENBLAS_NUM_THREADS", str(cores))
     import torch

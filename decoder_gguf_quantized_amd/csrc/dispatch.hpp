@@ -34,6 +34,16 @@ void qlaunch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStr
 template <int QT, int M, int R, int U, int NW = 4>
 void gemv_dispatch_mode(int mode, dim3 grid, size_t lds, hipStream_t st, const GemvArgs& a) {
   const unsigned nt = 64 * NW;
+  if (a.amax_v) {  // the LM head of one row with the greedy choice in its epilogue
+    if constexpr (M == 1) {
+      if (mode != kModeStore || a.xd) throw HipError{"gemv: the fused argmax needs the plain store epilogue"};
+      if (a.res_add) qlaunch(gemv_kernel<QT, M, kModeStore, R, U, NW, true, false, true>, grid, nt, lds, st, a);
+      else qlaunch(gemv_kernel<QT, M, kModeStore, R, U, NW, false, false, true>, grid, nt, lds, st, a);
+      return;
+    } else {
+      throw HipError{"gemv: the fused argmax takes one input row"};
+    }
+  }
   if (a.res_add) {  // residual prologue (sandwich norms): store and pair modes
     switch (mode) {
       case kModeStore: qlaunch(gemv_kernel<QT, M, kModeStore, R, U, NW, true>, grid, nt, lds, st, a); break;

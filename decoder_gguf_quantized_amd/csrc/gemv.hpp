@@ -62,6 +62,13 @@ struct GemvArgs {
   const float* xl;
   int xhd;
   long xcstride;
+  // Greedy token choice fused into the store epilogue (the LM head of one input
+  // row): each wave keeps the best (value, lowest index) of the rows it stores,
+  // ranked as the sampler ranks them (NaN above every number), and writes it to
+  // amax_v / amax_i [nwaves]; a one-wave pass then reduces the waves' results.
+  // Null: no argmax.
+  float* amax_v;
+  int* amax_i;
 };
 
 // Input row mi, floats 4 k4 .. 4 k4 + 3 (zero past the launch's rows).  ACC:
@@ -382,9 +389,11 @@ QD_DEV void gemv_compute(const float4* xs4, const float* xsum, int kp, int nblk,
 }
 
 // Finish row group `grp`: reduce each accumulator over the 64 lanes, apply the
-// input row's norm scale, and let lane 0 write with the mode's epilogue.
-template <int QT, int M, int MODE, int R, int U>
-QD_DEV void gemv_store(const GemvArgs& a, int grp, int lane, const float (&scale)[M], float (&acc)[R][M]) {
+// input row's norm scale, and let lane 0 write with the mode's epilogue (AM:
+// and keep the wave's best (value, index) of the stored rows in bv / bi).
+template <int QT, int M, int MODE, int R, int U, bool AM = false>
+QD_DEV void gemv_store(const GemvArgs& a, int grp, int lane, const float (&scale)[M], float (&acc)[R][M],
+                       float (&bv)[M], int (&bi)[M]) {
   constexpr bool kPair = MODE == kModePairSilu || MODE == kModePairGelu;
 #pragma unroll
   for (int mi = 0; mi < M; ++mi) {
@@ -403,8 +412,18 @@ QD_DEV void gemv_store(const GemvArgs& a, int grp, int lane, const float (&scale
         } else {
           const int row = grp * R + i;
           if (row < a.rows) {
-            if constexpr (MODE == kModeAdd) yr[row] += sv[i];
-            else yr[row] = a.bias ? sv[i] + a.bias[row] : sv[i];
+            if constexpr (MODE == kModeAdd) {
+              yr[row] += sv[i];
+            } else {
+              const float v = a.bias ? sv[i] + a.bias[row] : sv[i];
+              yr[row] = v;
+              if constexpr (AM) {
+                if (ranks_before(v, row, bv[mi], bi[mi])) {
+                  bv[mi] = v;
+                  bi[mi] = row;
+                }
+              }
+            }
           }
         }
       }
@@ -416,9 +435,12 @@ QD_DEV void gemv_store(const GemvArgs& a, int grp, int lane, const float (&scale
 
 // Register sets of the weight pipeline: with NS sets, NS - 1 tiles are in
 // flight while one is computed.  Three sets for the small tiles (R * U <= 4,
-// 20 VGPRs per set for the quantized types), two for the 8-unit tiles.
-template <int R, int U, int M>
-constexpr int gemv_sets() { return (R * U <= 4 && M <= 4) ? 3 : 2; }
+// 20 VGPRs per set for the quantized types) and for the 8-unit tiles of
+// eight-wave workgroups at one input row (two waves per SIMD there, so the
+// extra set costs no occupancy; the 8B shape's down projection 13.2 -> 12.4
+// us), two otherwise.
+template <int R, int U, int M, int NW>
+constexpr int gemv_sets() { return (R * U <= 4 && M <= 4) ? 3 : (NW == 8 && M == 1 ? 3 : 2); }
 
 // R rows per wave, U 16-byte units per lane in flight per row, M input rows.
 // Each wave walks its (row group, unit block) tiles in order through a ring of
@@ -428,9 +450,9 @@ constexpr int gemv_sets() { return (R * U <= 4 && M <= 4) ? 3 : 2; }
 // tiles are requested before the input rows are staged.  Tile indices are
 // wave-uniform (scalar registers), so every load is a scalar base plus a 32-bit
 // lane offset.
-template <int QT, int M, int MODE, int R, int U, int NW, bool RES, bool ACC = false>
+template <int QT, int M, int MODE, int R, int U, int NW, bool RES, bool ACC = false, bool AM = false>
 __global__ __launch_bounds__(64 * NW) void gemv_kernel(GemvArgs a) {
-  constexpr int NS = gemv_sets<R, U, M>();
+  constexpr int NS = gemv_sets<R, U, M, NW>();
   extern __shared__ float4 xs4[];
   const int kp = a.nblk * 32;
   float* xsum = reinterpret_cast<float*>(xs4 + M * kp / 4);  // nibble layouts: [M][nblk] block sums of x
@@ -486,6 +508,13 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(GemvArgs a) {
   for (int i = 0; i < R; ++i)
 #pragma unroll
     for (int mi = 0; mi < M; ++mi) acc[i][mi] = 0.f;
+  float bv[M];  // AM: the wave's best stored value and its row (lane 0)
+  int bi[M];
+#pragma unroll
+  for (int mi = 0; mi < M; ++mi) {
+    bv[mi] = -INFINITY;
+    bi[mi] = 0x7fffffff;
+  }
 
   // one ring step on set S: refill the set computed last, then compute S
   bool done = false;
@@ -498,12 +527,22 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(GemvArgs a) {
       return;
     }
     gemv_compute<QT, R, U, M>(xs4, xsum, kp, a.nblk, tt[s] * 64 * U, lane, nunits, ws[s], acc);
-    if (tt[s] == tpg - 1) gemv_store<QT, M, MODE, R, U>(a, tg[s], lane, scale, acc);
+    if (tt[s] == tpg - 1) gemv_store<QT, M, MODE, R, U, AM>(a, tg[s], lane, scale, acc, bv, bi);
   };
   while (!done) {
     step(std::integral_constant<int, 0>{});
     step(std::integral_constant<int, 1>{});
     if constexpr (NS > 2) step(std::integral_constant<int, 2>{});
+  }
+  if constexpr (AM) {
+    if (lane == 0) {
+#pragma unroll
+      for (int mi = 0; mi < M; ++mi)
+        if (mi < a.m) {
+          a.amax_v[(size_t)mi * nwaves + gwave] = bv[mi];
+          a.amax_i[(size_t)mi * nwaves + gwave] = bi[mi];
+        }
+    }
   }
 }
 

@@ -37,6 +37,10 @@ namespace {
 
 thread_local std::string g_err;
 
+// Most waves one GEMV launch runs (at most 1,024 workgroups of at most eight
+// waves): the size of the LM head's argmax partials.
+constexpr int kAmaxWaves = 8192;
+
 void set_err(const char* fmt, ...) {
   char buf[1024];
   va_list ap;
@@ -126,6 +130,8 @@ struct qdec_model {
                        // power of two (then capped at the page size)
   float* s_v = nullptr;
   int* s_i = nullptr;
+  float* am_v = nullptr;  // [kAmaxWaves] the LM head's per-wave greedy choices (one row)
+  int* am_i = nullptr;
   uint32_t* cut_key = nullptr;  // [max_seqs] top-p cut per row
   int* cut_idx = nullptr;
   int nvchunk = 0;
@@ -278,10 +284,15 @@ struct AccIn {
   size_t stride = 0;  // floats between accumulator blocks
 };
 
-void gemv(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, const float* norm_w, float eps,
-          float* y, int ldy, int nrows, int mode, float* const* y_ind = nullptr, Resid res = Resid{},
-          const float* bias = nullptr, AccIn acc = AccIn{}) {
+// amax: one input row whose greedy choice the epilogue also takes, into
+// m->am_v / m->am_i (see argmax_final).  Returns the number of waves of the
+// launch (the argmax partials).
+int gemv(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, const float* norm_w, float eps,
+         float* y, int ldy, int nrows, int mode, float* const* y_ind = nullptr, Resid res = Resid{},
+         const float* bias = nullptr, AccIn acc = AccIn{}, bool amax = false) {
   if (bias && mode != kModeStore) throw HipError{"gemv: a bias needs the store epilogue"};
+  if (amax && (nrows != 1 || mode != kModeStore || acc.o))
+    throw HipError{"gemv: the fused argmax takes one row and the store epilogue"};
   const int kp = w.nblk * 32;
   const size_t per_row = (size_t)kp * 4 + (nibble_layout(w.type) ? (size_t)w.nblk * 4 : 0);
   // rows per launch: a power of two (the kernel's M) whose staged inputs fit the LDS budget
@@ -292,7 +303,8 @@ void gemv(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, 
   const int nunits = int8_layout(w.type) ? 2 * w.nblk : (nibble_layout(w.type) ? w.nblk : kp / 4);
   int ru = nunits <= 64 ? 0 : (nunits <= 128 ? 1 : 2);
   if (ru == 2 && (pair ? w.rows / 2 : (w.rows + 1) / 2) >= 2048) ru = 3;
-  const int grid_cap = 1024;
+  // about four workgroups of four waves (two of eight) per CU
+  const int grid_cap = ru_waves(ru) == 8 ? 512 : 1024;
   const int R = ru_rows(ru), NW = ru_waves(ru);
   const int ngroups = pair ? w.rows / R : (w.rows + R - 1) / R;
   // waves stay resident and loop: about four workgroups per CU, so the input
@@ -312,12 +324,18 @@ void gemv(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, 
       a.xhd = acc.hd;
       a.xcstride = (long)acc.stride;
     }
+    if (amax) {
+      if ((int)grid.x * NW > kAmaxWaves) throw HipError{"gemv: too many waves for the argmax partials"};
+      a.amax_v = m->am_v;
+      a.amax_i = m->am_i;
+    }
     const size_t lds = per_row * M;
     const double bytes =
         w.gguf_bytes + (double)mr * kp * (acc.o ? 4 * kAccCopies : 4) + (double)mr * (pair ? w.rows / 2 : w.rows) * 4;
     Timed tm(m, st, gemv_class(w.type), bytes, 2.0 * mr * w.rows * (double)w.cols);
     gemv_type(w.type, M, ru, mode, grid, lds, st, a);
   }
+  return (int)grid.x * NW;
 }
 
 // Prefill projection.  prec: QDEC_PREFILL_F32 (f32 operands, the default),
@@ -469,6 +487,18 @@ void sample(qdec_model* m, hipStream_t st, const float* logits, int ld, int rows
   qlaunch(sample_stage2_kernel, rows, 64, 0, st, a);
 }
 
+// The greedy token of one row from the LM head's fused per-wave choices
+// (gemv with amax): one workgroup reduces the nwaves partials.  out, or the
+// step parameters' token buffer when sp is given.
+void argmax_final(qdec_model* m, hipStream_t st, int nwaves, int* out, const StepParams* sp = nullptr) {
+  static_assert(kAmaxWaves <= 8 * 1024, "argmax_waves_kernel: eight partials per thread of 1,024");
+  if (nwaves > kAmaxWaves) throw HipError{"argmax_final: too many partials"};
+  SampleArgs a{nullptr, 0, m->cfg.vocab, 1, 0.f, 0, 0, m->am_v, m->am_i, nwaves, out, nullptr, sp,
+               nullptr, nullptr, nullptr};
+  Timed tm(m, st, "argmax_final", (double)nwaves * 8, 0);
+  qlaunch(argmax_waves_kernel, 1, 1024, 0, st, a);
+}
+
 // q|k|v projection of decode rows into m->qkv (RMSNorm prologue, optional
 // residual prologue, bias epilogue): one launch over the fused rows, or three
 // when q, k and v have different types.  With a residual prologue each of the
@@ -556,17 +586,21 @@ void blocks(qdec_model* m, hipStream_t st, int n, int seq, int pos0, const int* 
 
 // One decode step for sequences 0..n-1 reading tokens, positions and the
 // step's parameters from device memory (so it can be captured and replayed).
-void decode_body(qdec_model* m, hipStream_t st, int n, bool topp, bool slotted) {
+// greedy1: one row at temperature 0, whose token the LM head's epilogue picks
+void decode_body(qdec_model* m, hipStream_t st, int n, bool topp, bool slotted, bool greedy1) {
   const qdec_config& c = m->cfg;
   embed(m, st, m->d_tok, n, m->x);
   blocks(m, st, n, 0, 0, m->d_pos, slotted);
+  int nw;
   if (c.sandwich_norm)  // the last post-FFN norm and residual add run in the head's prologue
-    gemv(m, st, m->lm(), m->x2, c.hidden, m->output_norm, c.rms_eps, nullptr, c.vocab, n, kModeStore,
-         &m->d_params->logits, Resid{m->y, m->layers[c.n_layer - 1].post_ffw, nullptr});
+    nw = gemv(m, st, m->lm(), m->x2, c.hidden, m->output_norm, c.rms_eps, nullptr, c.vocab, n, kModeStore,
+              &m->d_params->logits, Resid{m->y, m->layers[c.n_layer - 1].post_ffw, nullptr}, nullptr,
+              AccIn{}, greedy1);
   else
-    gemv(m, st, m->lm(), m->x, c.hidden, m->output_norm, c.rms_eps, nullptr, c.vocab, n, kModeStore,
-         &m->d_params->logits);
-  sample(m, st, nullptr, c.vocab, n, 0.f, 0, 0, nullptr, nullptr, m->d_params, topp, slotted ? m->d_seq : nullptr);
+    nw = gemv(m, st, m->lm(), m->x, c.hidden, m->output_norm, c.rms_eps, nullptr, c.vocab, n, kModeStore,
+              &m->d_params->logits, Resid{}, nullptr, AccIn{}, greedy1);
+  if (greedy1) argmax_final(m, st, nw, nullptr, m->d_params);
+  else sample(m, st, nullptr, c.vocab, n, 0.f, 0, 0, nullptr, nullptr, m->d_params, topp, slotted ? m->d_seq : nullptr);
 }
 
 // ------------------------------------------------------------ error handling
@@ -1069,6 +1103,8 @@ int load(const qdec_config* cfgp, const qdec_tensor* ts, int32_t n, int32_t max_
     m->nvchunk = (c.vocab + kSampleChunk - 1) / kSampleChunk;
     m->s_v = m->dalloc<float>((size_t)max_seqs * m->nvchunk);
     m->s_i = m->dalloc<int>((size_t)max_seqs * m->nvchunk);
+    m->am_v = m->dalloc<float>(kAmaxWaves);
+    m->am_i = m->dalloc<int>(kAmaxWaves);
     m->cut_key = m->dalloc<uint32_t>(max_seqs);
     m->cut_idx = m->dalloc<int>(max_seqs);
     m->d_pos = m->dalloc<int>(64);
@@ -1221,6 +1257,7 @@ int decode_impl(qdec_model* m, const int32_t* seqs, const int32_t* tokens, int32
     sa.err = m->err_dev;
     sa.params = StepParams{temperature, top_p, n_seqs, seed, step, d_logits, d_token_out};
     const bool topp = temperature > 0.f && top_p < 1.f;
+    const bool greedy1 = n_seqs == 1 && !(temperature > 0.f);
     sa.d_params = m->d_params;
     sa.rope_g = m->rope_g;
     sa.rope_l = m->rope_l;
@@ -1237,15 +1274,15 @@ int decode_impl(qdec_model* m, const int32_t* seqs, const int32_t* tokens, int32
       qlaunch(step_begin_kernel, 1, 256, 0, st, sa);
     }
     if (m->timing) {
-      decode_body(m, st, n_seqs, topp, slotted);
+      decode_body(m, st, n_seqs, topp, slotted, greedy1);
     } else {
-      // graph per (batch size, slotted, top-p on)
-      hipGraphExec_t& ge = m->graphs[4 * n_seqs + (slotted ? 2 : 0) + (topp ? 1 : 0)];
+      // graph per (batch size, slotted, top-p on, fused greedy choice)
+      hipGraphExec_t& ge = m->graphs[8 * n_seqs + (greedy1 ? 4 : 0) + (slotted ? 2 : 0) + (topp ? 1 : 0)];
       if (!ge) {
         hipGraph_t graph = nullptr;
         hipck(hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeThreadLocal), "hipStreamBeginCapture");
         try {
-          decode_body(m, m->cap_stream, n_seqs, topp, slotted);
+          decode_body(m, m->cap_stream, n_seqs, topp, slotted, greedy1);
         } catch (...) {
           (void)hipStreamEndCapture(m->cap_stream, &graph);
           if (graph) (void)hipGraphDestroy(graph);
@@ -1375,9 +1412,11 @@ int qdec_prefill(qdec_model* m, int32_t seq, const int32_t* tokens, int32_t n_to
         rmsnorm_rows(m, st, m->x, H, m->output_norm, H, m->h, H, T, 0);
         gemm(m, st, m->lm(), m->h, H, T, d_logits + (size_t)c0 * V, V, kModeStore);
       } else if (last) {
-        gemv(m, st, m->lm(), m->x + (size_t)(T - 1) * H, H, m->output_norm, c.rms_eps, d_logits, V, 1, kModeStore);
+        const int nw = gemv(m, st, m->lm(), m->x + (size_t)(T - 1) * H, H, m->output_norm, c.rms_eps, d_logits, V,
+                            1, kModeStore, nullptr, Resid{}, nullptr, AccIn{}, d_token_out != nullptr);
+        if (d_token_out) argmax_final(m, st, nw, d_token_out);
       }
-      if (last && d_token_out) {
+      if (last && d_token_out && all) {
         const float* row = all ? d_logits + (size_t)(n_tokens - 1) * V : d_logits;
         sample(m, st, row, V, 1, 0.f, 0, 0, d_token_out, nullptr);
       }

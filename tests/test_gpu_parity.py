@@ -82,6 +82,62 @@ def test_argmax_bit_exact_with_ties_and_nan():
     assert as_np(out).tolist() == want
 
 
+def _head_rows(t, name):
+    """The raw GGUF rows of a matrix as a writable [rows][row_bytes] uint8 view."""
+    w = t[name]
+    return w.data.reshape(w.rows, -1)
+
+
+@pytest.mark.parametrize("key,case", [
+    ("llama_q4_hd64_g4", "periodic"),      # Q4_0 head, four-row groups
+    ("mha_hd128_g1_f32", "nan"),           # F32 head (the loader refuses non-finite block scales)
+    ("qwen2_bias_hd64_g2", "periodic"),    # Q8_0 head
+    ("gemma_hd256_g4", "periodic"),        # tied head, sandwich-norm prologue
+])
+def test_fused_greedy_choice_ties_and_nan(key, case):
+    """At one row and temperature 0 the LM head's epilogue picks the token (each
+    wave keeps the best of the rows it stores, then one pass over the waves):
+    the token must be the greedy rule's on the GPU's own logits row, lowest
+    index first among equals and the first NaN above every number.
+    periodic: every head row r is a copy of row r mod 37, so the maximum is
+    held by about vocab / 37 rows in many waves and the lowest one (below 37)
+    must win.  nan: rows 300 and 900 of an F32 head hold a NaN; 300 must win.
+    Checked through prefill's last row and through graph-replayed decode."""
+    cfg = dict(SMALL[key])
+    t = synth.generate(cfg)
+    name = "output.weight" if "output.weight" in t else "token_embd.weight"
+    rows = _head_rows(t, name)
+    V = cfg["vocab"]
+    if case == "periodic":
+        rows[:] = rows[np.arange(V) % 37]
+    else:
+        rows.view(np.float32)[[300, 900], 5] = np.nan
+    dev()
+    # input tokens outside the changed rows' range (a tied head is the embedding)
+    prompt = (synth.prompt(cfg, 6, tag="amax") % 30).astype(np.int32) + 1
+    with qdec.Model(cfg, t, max_seqs=1, max_ctx=64) as m:
+        pl = torch.empty(V, dtype=torch.float32, device=dev())
+        tok = torch.empty(1, dtype=torch.int32, device=dev())
+        m.prefill(0, prompt, pl, tok)
+        torch.cuda.synchronize()
+        seen = [(as_np(pl).copy(), int(as_np(tok)[0]))]
+        dl = torch.empty((1, V), dtype=torch.float32, device=dev())
+        out = torch.empty(1, dtype=torch.int32, device=dev())
+        for step in range(3):
+            m.decode_step([int(prompt[step])], dl, out)
+            torch.cuda.synchronize()
+            seen.append((as_np(dl)[0].copy(), int(as_np(out)[0])))
+    for lg, got in seen:
+        assert got == sampler.greedy(lg)
+        if case == "periodic":
+            # copies of a row give bit-identical logits
+            assert np.array_equal(lg.view(np.uint32), lg[np.arange(V) % 37].view(np.uint32))
+            assert got < 37
+        else:
+            assert np.isnan(lg[300]) and np.isnan(lg[900])
+            assert got == 300
+
+
 @pytest.mark.parametrize("temperature", [1.0, 0.7])
 def test_gumbel_sampling_matches_oracle(temperature):
     rng = np.random.default_rng(6)
