@@ -126,12 +126,13 @@ QD_DEV float2 load_nt(const float2* p) {
   return make_float2(v.x, v.y);
 }
 
-// v & m through an opaque instruction, so that the byte-wise conversions of the
-// masked word stay v_cvt_f32_ubyteN instead of being folded into bit-field
-// extracts (one extra op per element).
+// v & m through an instruction the compiler cannot see into, so that it uses
+// the masked word as written (whole-word masks whose bytes or fp16 halves are
+// then read directly) instead of folding the mask into a bit-field extract per
+// element.  Not volatile: the scheduler may move it like any other ALU op.
 QD_DEV uint32_t opaque_and(uint32_t v, uint32_t m) {
   uint32_t r;
-  asm volatile("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(v), "v"(m));
+  asm("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(v), "v"(m));
   return r;
 }
 
@@ -141,6 +142,18 @@ QD_DEV bool ranks_before(float a, int ia, float b, int ib) {
   bool an = a != a, bn = b != b;
   if (an || bn) return an && bn ? ia < ib : an;
   return a > b || (a == b && ia < ib);
+}
+
+// The best (value, index) of the wave in ranks_before's order, in every lane.
+QD_DEV void argmax_pair_wave(float& v, int& i) {
+  for (int o = 32; o > 0; o >>= 1) {
+    float ov = __shfl_xor(v, o);
+    int oi = __shfl_xor(i, o);
+    if (ranks_before(ov, oi, v, i)) {
+      v = ov;
+      i = oi;
+    }
+  }
 }
 
 // Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two 64x64->128

@@ -31,105 +31,94 @@ void qlaunch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStr
 }
 
 // ------------------------------------------------------------ GEMV
-template <int QT, int M, int R, int U, int NW = 4>
+// Modes of a tile class: PAIRC = the gate/up pair modes (SiLU or gelu_tanh,
+// with or without the residual prologue); otherwise store and add, the
+// residual prologue (store), the attention-accumulator input (store, add) and
+// the fused argmax (store, one input row).
+template <int QT, int M, int R, int U, int NW, bool PAIRC>
 void gemv_dispatch_mode(int mode, dim3 grid, size_t lds, hipStream_t st, const GemvArgs& a) {
   const unsigned nt = 64 * NW;
-  if (a.amax_v) {  // the LM head of one row with the greedy choice in its epilogue
-    if constexpr (M == 1) {
-      if (mode != kModeStore || a.xd) throw HipError{"gemv: the fused argmax needs the plain store epilogue"};
-      if (a.res_add) qlaunch(gemv_kernel<QT, M, kModeStore, R, U, NW, true, false, true>, grid, nt, lds, st, a);
-      else qlaunch(gemv_kernel<QT, M, kModeStore, R, U, NW, false, false, true>, grid, nt, lds, st, a);
-      return;
+  if constexpr (PAIRC) {
+    if (mode != kModePairSilu && mode != kModePairGelu) throw HipError{"gemv: a pair tile class needs a pair mode"};
+    if (a.xd || a.amax_v) throw HipError{"gemv: pair modes take a plain input row"};
+    const bool silu = mode == kModePairSilu;
+    if (a.res_add) {
+      if (silu) qlaunch(gemv_kernel<QT, M, kModePairSilu, R, U, NW, true>, grid, nt, lds, st, a);
+      else qlaunch(gemv_kernel<QT, M, kModePairGelu, R, U, NW, true>, grid, nt, lds, st, a);
     } else {
-      throw HipError{"gemv: the fused argmax takes one input row"};
+      if (silu) qlaunch(gemv_kernel<QT, M, kModePairSilu, R, U, NW, false>, grid, nt, lds, st, a);
+      else qlaunch(gemv_kernel<QT, M, kModePairGelu, R, U, NW, false>, grid, nt, lds, st, a);
     }
-  }
-  if (a.res_add) {  // residual prologue (sandwich norms): store and pair modes
-    switch (mode) {
-      case kModeStore: qlaunch(gemv_kernel<QT, M, kModeStore, R, U, NW, true>, grid, nt, lds, st, a); break;
-      case kModePairSilu: qlaunch(gemv_kernel<QT, M, kModePairSilu, R, U, NW, true>, grid, nt, lds, st, a); break;
-      case kModePairGelu: qlaunch(gemv_kernel<QT, M, kModePairGelu, R, U, NW, true>, grid, nt, lds, st, a); break;
-      default: throw HipError{"gemv: residual prologue with an add epilogue"};
+  } else {
+    if (mode != kModeStore && mode != kModeAdd) throw HipError{"gemv: a row tile class needs store or add"};
+    const bool add = mode == kModeAdd;
+    if (a.amax_v) {  // the LM head of one row with the greedy choice in its epilogue
+      if constexpr (M == 1) {
+        if (add || a.xd) throw HipError{"gemv: the fused argmax needs the plain store epilogue"};
+        if (a.res_add) qlaunch(gemv_kernel<QT, M, kModeStore, R, U, NW, true, false, true>, grid, nt, lds, st, a);
+        else qlaunch(gemv_kernel<QT, M, kModeStore, R, U, NW, false, false, true>, grid, nt, lds, st, a);
+      } else {
+        throw HipError{"gemv: the fused argmax takes one input row"};
+      }
+    } else if (a.res_add) {  // residual prologue (sandwich norms)
+      if (add || a.xd) throw HipError{"gemv: the residual prologue needs the store epilogue"};
+      qlaunch(gemv_kernel<QT, M, kModeStore, R, U, NW, true>, grid, nt, lds, st, a);
+    } else if (a.xd) {  // input from decode attention's accumulators
+      if (add) qlaunch(gemv_kernel<QT, M, kModeAdd, R, U, NW, false, true>, grid, nt, lds, st, a);
+      else qlaunch(gemv_kernel<QT, M, kModeStore, R, U, NW, false, true>, grid, nt, lds, st, a);
+    } else {
+      if (add) qlaunch(gemv_kernel<QT, M, kModeAdd, R, U, NW, false>, grid, nt, lds, st, a);
+      else qlaunch(gemv_kernel<QT, M, kModeStore, R, U, NW, false>, grid, nt, lds, st, a);
     }
-    return;
-  }
-  if (a.xd) {  // input from decode attention's accumulators: the O projection (store or add)
-    switch (mode) {
-      case kModeStore: qlaunch(gemv_kernel<QT, M, kModeStore, R, U, NW, false, true>, grid, nt, lds, st, a); break;
-      case kModeAdd: qlaunch(gemv_kernel<QT, M, kModeAdd, R, U, NW, false, true>, grid, nt, lds, st, a); break;
-      default: throw HipError{"gemv: attention-accumulator input with a pair epilogue"};
-    }
-    return;
-  }
-  switch (mode) {
-    case kModeStore: qlaunch(gemv_kernel<QT, M, kModeStore, R, U, NW, false>, grid, nt, lds, st, a); break;
-    case kModeAdd: qlaunch(gemv_kernel<QT, M, kModeAdd, R, U, NW, false>, grid, nt, lds, st, a); break;
-    case kModePairSilu: qlaunch(gemv_kernel<QT, M, kModePairSilu, R, U, NW, false>, grid, nt, lds, st, a); break;
-    default: qlaunch(gemv_kernel<QT, M, kModePairGelu, R, U, NW, false>, grid, nt, lds, st, a); break;
   }
 }
 
-// (R rows per wave, U units per lane per row, NW waves per workgroup):
-//   0: R = 4, U = 1 for rows of at most 64 units (one unit per lane);
-//   1: R = 2, U = 2 for rows of 65..128 units;
-//   2: R = 2, U = 4 for longer rows;
-//   3: as 2 with eight-wave workgroups, for long rows with many row groups:
-//      the input row is staged once per CU instead of twice (same LDS).
+// Tile classes.  Every class gives a lane one 16-byte unit per row and tile
+// (U = 1): small tiles keep several in flight per wave through the ring and
+// spread each wave's arithmetic over the stream, which measured faster than
+// two or four units per lane on every decode shape of the 0.6B and 8B models.
+//   0: one row per wave, four-wave workgroups (store / add on fewer than 4,096
+//      rows: two-row groups would leave CUs without a workgroup);
+//   1: two rows per wave, eight-wave workgroups (store / add, 4,096 rows or
+//      more);
+//   2: one gate/up pair per wave, four-wave workgroups (pair modes, up to
+//      four input rows);
+//   3: two gate/up pairs per wave, four-wave workgroups (pair modes, eight or
+//      sixteen input rows).
 // LDS budget of the GEMV's staged input rows (the CU has 160 KB; the rest is
 // left for the kernel's own small arrays).
 constexpr size_t kGemvLdsMax = 128 * 1024;
 
-// Largest input-row count M (a power of two, at most 16) whose staged rows fit
-// the LDS budget for the shortest row of each tile class (class 0: any row;
-// class 1: 65 units; classes 2 and 3: 129 units; Q8_0 / Q6_K 16 weights per
-// unit, Q4_0 / Q4_K 32, F32 4); combinations beyond it cannot be requested and
-// are not instantiated.
-constexpr int gemv_max_m(int qt, int ru) {
-  if (ru == 0) return 16;
-  const size_t units = ru == 1 ? 65 : 129;
-  const size_t k = units * (int8_layout(qt) ? 16 : (nibble_layout(qt) ? 32 : 4));
-  const size_t per_row = k * 4 + (nibble_layout(qt) ? k / 32 * 4 : 0);
-  int m = 16;
-  while (m > 1 && per_row * m > kGemvLdsMax) m /= 2;
-  return m;
-}
-
-template <int QT, int M, int RU, int R, int U, int NW = 4>
-void gemv_dispatch_fit(int mode, dim3 grid, size_t lds, hipStream_t st, const GemvArgs& a) {
-  if constexpr (M <= gemv_max_m(QT, RU)) gemv_dispatch_mode<QT, M, R, U, NW>(mode, grid, lds, st, a);
-  else throw HipError{"gemv: input rows exceed the LDS budget of the tile class"};
-}
+inline int gemv_tile_class(bool pair, int rows, int m) { return pair ? (m <= 4 ? 2 : 3) : (rows >= 4096 ? 1 : 0); }
+inline int class_rows(int c) { return c == 0 ? 1 : (c == 3 ? 4 : 2); }
+inline int class_waves(int c) { return c == 1 ? 8 : 4; }
 
 template <int QT, int M>
-void gemv_dispatch_ru(int ru, int mode, dim3 grid, size_t lds, hipStream_t st, const GemvArgs& a) {
-  switch (ru) {
-    case 0: gemv_dispatch_fit<QT, M, 0, 4, 1>(mode, grid, lds, st, a); break;
-    case 1: gemv_dispatch_fit<QT, M, 1, 2, 2>(mode, grid, lds, st, a); break;
-    case 3: gemv_dispatch_fit<QT, M, 3, 2, 4, 8>(mode, grid, lds, st, a); break;
-    default: gemv_dispatch_fit<QT, M, 2, 2, 4>(mode, grid, lds, st, a); break;
+void gemv_dispatch_class(int cls, int mode, dim3 grid, size_t lds, hipStream_t st, const GemvArgs& a) {
+  switch (cls) {
+    case 0: gemv_dispatch_mode<QT, M, 1, 1, 4, false>(mode, grid, lds, st, a); break;
+    case 1: gemv_dispatch_mode<QT, M, 2, 1, 8, false>(mode, grid, lds, st, a); break;
+    case 2:
+      if constexpr (M <= 4) gemv_dispatch_mode<QT, M, 2, 1, 4, true>(mode, grid, lds, st, a);
+      else throw HipError{"gemv: tile class 2 takes at most four input rows"};
+      break;
+    default:
+      if constexpr (M >= 8) gemv_dispatch_mode<QT, M, 4, 1, 4, true>(mode, grid, lds, st, a);
+      else throw HipError{"gemv: tile class 3 takes eight or sixteen input rows"};
+      break;
   }
 }
 
-// tile classes: 0 = four rows x one unit per lane, 1 = two rows x two units,
-// 2 = two rows x four units, 3 = class 2 in eight-wave workgroups
-inline int ru_rows(int ru) { return ru == 0 ? 4 : 2; }
-inline int ru_waves(int ru) { return ru == 3 ? 8 : 4; }
-
+// GEMV over M input rows (a power of two, at most 16) with tile class cls.
 template <int QT>
-void gemv_dispatch_m(int M, int ru, int mode, dim3 grid, size_t lds, hipStream_t st, const GemvArgs& a) {
+void gemv_launch(int M, int cls, int mode, dim3 grid, size_t lds, hipStream_t st, const GemvArgs& a) {
   switch (M) {
-    case 1: gemv_dispatch_ru<QT, 1>(ru, mode, grid, lds, st, a); break;
-    case 2: gemv_dispatch_ru<QT, 2>(ru, mode, grid, lds, st, a); break;
-    case 4: gemv_dispatch_ru<QT, 4>(ru, mode, grid, lds, st, a); break;
-    case 8: gemv_dispatch_ru<QT, 8>(ru, mode, grid, lds, st, a); break;
-    default: gemv_dispatch_ru<QT, 16>(ru, mode, grid, lds, st, a); break;
+    case 1: gemv_dispatch_class<QT, 1>(cls, mode, grid, lds, st, a); break;
+    case 2: gemv_dispatch_class<QT, 2>(cls, mode, grid, lds, st, a); break;
+    case 4: gemv_dispatch_class<QT, 4>(cls, mode, grid, lds, st, a); break;
+    case 8: gemv_dispatch_class<QT, 8>(cls, mode, grid, lds, st, a); break;
+    default: gemv_dispatch_class<QT, 16>(cls, mode, grid, lds, st, a); break;
   }
-}
-
-// GEMV over M input rows with tile class ru (see gemv_dispatch_ru).
-template <int QT>
-void gemv_launch(int M, int ru, int mode, dim3 grid, size_t lds, hipStream_t st, const GemvArgs& a) {
-  gemv_dispatch_m<QT>(M, ru, mode, grid, lds, st, a);
 }
 
 // ------------------------------------------------------------ GEMM

@@ -15,13 +15,19 @@
 //     LDS (RMSNorm prologue fused), so a unit's activations are read once for
 //     all R rows.  The first row group's weights are requested before the
 //     prologue, so the input staging overlaps the first weight fetch.
-//   * the reduction over the 64 lanes is a DPP tree; lane 0 writes the result
-//     with the mode's epilogue (store, residual add, or gate/up pair with the
-//     activation: act(gate) * up).
+//   * the reduction over the 64 lanes is a DPP tree; a wave keeps its finished
+//     outputs in a register (one lane each) and writes them all at the end with
+//     the mode's epilogue (store, residual add, or gate/up pair with the
+//     activation: act(gate) * up).  The ring of weight tiles then issues only
+//     loads, the same number on every path, so each wait is for exactly the
+//     tile about to be used (loads and stores share one in-order counter: a
+//     store, or a conditional load, inside the ring turns every later wait into
+//     a wait for all loads in flight).
 //   * Q8_0: int8 -> f32 is one SDWA conversion per weight.  Q4_0: nibbles are
-//     masked a word at a time and converted with v_cvt_f32_ubyteN; the offset 8
-//     is folded into the block as -8 * sum(x over the block), so the per-weight
-//     cost is one conversion and one FMA.
+//     masked a word at a time into fp16 subnormals that the mixed-precision FMA
+//     reads directly (dot32_q4_raw4); the offset 8 is folded into the block as
+//     -8 * sum(x over the block), so the per-weight cost is one FMA and 5/8 of
+//     a mask or shift.
 #pragma once
 #include <type_traits>
 
@@ -71,34 +77,52 @@ struct GemvArgs {
   int* amax_i;
 };
 
-// Input row mi, floats 4 k4 .. 4 k4 + 3 (zero past the launch's rows).  ACC:
-// from decode attention's accumulators (a separate instantiation, so that the
-// plain kernels keep their register budget).
+// Input row mi, floats 4 k4 .. 4 k4 + 3, in two steps: the loads (always
+// issued, at a clamped in-bounds index, so every thread issues the same loads)
+// and the arithmetic on them (zero past the row or past the launch's rows).
+// ACC: the row comes from decode attention's accumulators, kAccCopies blocks
+// summed and divided by their softmax denominators (a separate instantiation,
+// so that the plain kernels keep their register budget).
 template <bool ACC>
-QD_DEV float4 load_x4(const GemvArgs& a, int mi, int k4, bool ok) {
-  if (!ok || mi >= a.m) return make_float4(0.f, 0.f, 0.f, 0.f);
+struct XRaw {
+  float4 u[ACC ? kAccCopies : 1];
+  float l[ACC ? kAccCopies : 1];
+};
+
+template <bool ACC>
+QD_DEV XRaw<ACC> load_x4_raw(const GemvArgs& a, int mi, int k4, bool ok) {
+  const int m = min(mi, a.m - 1), k = ok ? k4 : 0;
+  XRaw<ACC> r;
   if constexpr (ACC) {
-    float4 u[kAccCopies];
-    float lb[kAccCopies];
 #pragma unroll
     for (int b = 0; b < kAccCopies; ++b) {  // every block's loads go out together
-      u[b] = reinterpret_cast<const float4*>(a.xd + b * a.xcstride + (size_t)mi * a.ldx)[k4];
-      lb[b] = a.xl[b * a.xcstride + (size_t)mi * (a.ldx / a.xhd) + (4 * k4) / a.xhd];
+      r.u[b] = reinterpret_cast<const float4*>(a.xd + b * a.xcstride + (size_t)m * a.ldx)[k];
+      r.l[b] = a.xl[b * a.xcstride + (size_t)m * (a.ldx / a.xhd) + (4 * k) / a.xhd];
     }
-    float4 o = u[0];
-    float l = lb[0];
+  } else {
+    r.u[0] = reinterpret_cast<const float4*>(a.x)[(size_t)m * (a.ldx / 4) + k];
+  }
+  return r;
+}
+
+template <bool ACC>
+QD_DEV float4 x4_value(const GemvArgs& a, const XRaw<ACC>& r, int mi, bool ok) {
+  if (!ok || mi >= a.m) return make_float4(0.f, 0.f, 0.f, 0.f);
+  if constexpr (ACC) {
+    float4 o = r.u[0];
+    float l = r.l[0];
 #pragma unroll
     for (int b = 1; b < kAccCopies; ++b) {
-      o.x += u[b].x;
-      o.y += u[b].y;
-      o.z += u[b].z;
-      o.w += u[b].w;
-      l += lb[b];
+      o.x += r.u[b].x;
+      o.y += r.u[b].y;
+      o.z += r.u[b].z;
+      o.w += r.u[b].w;
+      l += r.l[b];
     }
-    const float r = 1.0f / l;
-    return make_float4(o.x * r, o.y * r, o.z * r, o.w * r);
+    const float q = 1.0f / l;
+    return make_float4(o.x * q, o.y * q, o.z * q, o.w * q);
   }
-  return reinterpret_cast<const float4*>(a.x)[(size_t)mi * (a.ldx / 4) + k4];
+  return r.u[0];
 }
 
 QD_DEV float act_silu(float g) { return g / (1.0f + expf(-g)); }
@@ -148,13 +172,19 @@ constexpr int unit_floats() { return int8_layout(QT) ? 16 : (nibble_layout(QT) ?
 // unit, so for each slot i consecutive lanes read consecutive float4s: no bank
 // conflicts (the natural layout puts every lane's unit 64 or 128 bytes apart,
 // which lands all lanes on a handful of banks).
-template <int QT, int M, int NW, bool RES, bool ACC>
-QD_DEV void gemv_stage_x(const GemvArgs& a, float4* xs4, int kp, float (&scale)[M]) {
+// issue(): called once, right after the loads of the first batch of inputs
+// (before them with the residual prologue): the caller requests its first
+// weight tiles there.  Loads return in order, so inputs requested behind the
+// weight tiles could not be staged before those tiles arrive.
+template <int QT, int M, int NW, bool RES, bool ACC, typename F>
+QD_DEV void gemv_stage_x(const GemvArgs& a, float4* xs4, int kp, float (&scale)[M], F&& issue) {
   constexpr int NT = 64 * NW;  // threads of the workgroup
   constexpr int US = unit_floats<QT>(), NV = US / 4;
   // k positions per thread per batch (loads in flight); the residual prologue
   // loads four float4 per position, so it batches fewer to stay within the
-  // register budget of the plain kernels (the weight tiles are live meanwhile)
+  // register budget of the plain kernels (the weight tiles are live meanwhile).
+  // Slots of a batch that start past the row are skipped as a whole (a
+  // workgroup-uniform test), so short rows issue no extra loads.
   constexpr int JB = RES ? (M >= 2 ? 1 : 2) : (M >= 8 ? 1 : 8 / M);
   const int NU = kp / US, NK4 = kp / 4;
   __shared__ float red[NW][M];
@@ -172,6 +202,7 @@ QD_DEV void gemv_stage_x(const GemvArgs& a, float4* xs4, int kp, float (&scale)[
   float4* o4 = reinterpret_cast<float4*>(a.res_out);
   const bool write_h = resid && o4 && blockIdx.x == 0;
   float ts[M];
+  if constexpr (RES) issue();
   if constexpr (RES) {
     __shared__ float red_t[NW][M];
 #pragma unroll
@@ -206,15 +237,30 @@ QD_DEV void gemv_stage_x(const GemvArgs& a, float4* xs4, int kp, float (&scale)[
       ts[mi] = 1.0f / sqrtf(t / (float)kp + a.eps);
     }
   }
-  for (int k0 = tid; k0 < NK4; k0 += NT * JB) {
+  // one batch of JB positions per thread, from position b0 of the row (a
+  // multiple of NT JB); the first batch is run by every thread, as
+  // straight-line code, so that issue() is unconditional
+  auto batch = [&](int b0, auto first) {
     float4 xv[JB][M], wv[JB];
+    XRaw<ACC> xr[JB][M];
 #pragma unroll
     for (int j = 0; j < JB; ++j) {
-      const int k4 = k0 + NT * j;
+      if (b0 + NT * j >= NK4) break;  // the same for every thread
+      const int k4 = b0 + NT * j + tid;
       const bool ok = k4 < NK4;
-      wv[j] = (ok && norm) ? w4[k4] : make_float4(1.f, 1.f, 1.f, 1.f);
+      if (norm) wv[j] = w4[ok ? k4 : 0];
 #pragma unroll
-      for (int mi = 0; mi < M; ++mi) xv[j][mi] = load_x4<ACC>(a, mi, k4, ok);
+      for (int mi = 0; mi < M; ++mi) xr[j][mi] = load_x4_raw<ACC>(a, mi, k4, ok);
+    }
+    if constexpr (decltype(first)::value && !RES) issue();
+#pragma unroll
+    for (int j = 0; j < JB; ++j) {
+      if (b0 + NT * j >= NK4) break;
+      const int k4 = b0 + NT * j + tid;
+      const bool ok = k4 < NK4;
+      if (!(ok && norm)) wv[j] = make_float4(1.f, 1.f, 1.f, 1.f);
+#pragma unroll
+      for (int mi = 0; mi < M; ++mi) xv[j][mi] = x4_value<ACC>(a, xr[j][mi], mi, ok);
       if constexpr (RES) {
         const float4 rw = ok ? r4[k4] : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -230,7 +276,8 @@ QD_DEV void gemv_stage_x(const GemvArgs& a, float4* xs4, int kp, float (&scale)[
     }
 #pragma unroll
     for (int j = 0; j < JB; ++j) {
-      const int k4 = k0 + NT * j;
+      if (b0 + NT * j >= NK4) break;
+      const int k4 = b0 + NT * j + tid;
       if (k4 < NK4) {
         const int slot = (k4 % NV) * NU + k4 / NV;
 #pragma unroll
@@ -242,7 +289,9 @@ QD_DEV void gemv_stage_x(const GemvArgs& a, float4* xs4, int kp, float (&scale)[
         }
       }
     }
-  }
+  };
+  batch(0, std::true_type{});
+  for (int b0 = NT * JB; b0 < NK4; b0 += NT * JB) batch(b0, std::false_type{});
   if (norm) {
 #pragma unroll
     for (int mi = 0; mi < M; ++mi) {
@@ -260,12 +309,13 @@ QD_DEV void gemv_stage_x(const GemvArgs& a, float4* xs4, int kp, float (&scale)[
   }
 }
 
-// Weights of one row group held in registers between load and use.
+// Weights of one row group held in registers between load and use.  Scales
+// stay raw words until the tile is computed: converting them on arrival would
+// make the wave wait for its newest loads right after issuing them.
 template <int QT, int R, int U>
 struct WRegs {
   uint4 w[R][U];
-  float d[R][U];
-  uint32_t ks[R][U], kd[R][U];  // K-quants: raw scale words, decoded when used (optimised away otherwise)
+  uint32_t ks[R][U], kd[R][U];  // fp16 scale bits (Q8_0, Q4_0); K-quants: packed scale words
 };
 
 // Rows of group `grp`: R consecutive rows, or for the pair modes R/2 outputs,
@@ -287,64 +337,79 @@ QD_DEV void group_rows(int grp, int rows, int (&r)[R]) {
 // Units past the row end are clamped to the last unit (a valid address, so the
 // loads need no predicate); gemv_compute skips them.  Row bases are scalar and
 // lane offsets unsigned 32-bit, so each load is a scalar base + vector offset.
+// live = false (a tile past the wave's last one) points every lane's loads at
+// the first bytes of `park`, the input row the workgroup has just read: one
+// cache line per load, an L2 hit, no HBM bytes.  The loads are issued either
+// way: with the same number of loads on every path through the ring, the
+// compiler can wait for exactly the tile it is about to use instead of for all
+// loads.
 template <int QT, int R, int U>
-QD_DEV void gemv_load(const GemvArgs& a, const int (&r)[R], int base, int lane, int nunits, WRegs<QT, R, U>& W) {
+QD_DEV void gemv_load(const GemvArgs& a, const int (&r)[R], int base, int lane, int nunits, WRegs<QT, R, U>& W,
+                      bool live, const uint8_t* park) {
   const int kp = a.nblk * 32;
+  auto at = [&](const void* p, size_t off) { return live ? static_cast<const uint8_t*>(p) + off : park; };
 #pragma unroll
   for (int k = 0; k < U; ++k) {
-    const unsigned uc = (unsigned)min(base + lane + 64 * k, nunits - 1);
+    const unsigned uc = live ? (unsigned)min(base + lane + 64 * k, nunits - 1) : 0u;
 #pragma unroll
     for (int i = 0; i < R; ++i) {
+      const size_t row = (size_t)r[i];
       if constexpr (QT == kQ8_0) {
-        const uint8_t* rq = a.qs + (size_t)r[i] * kp;
-        const uint16_t* rd = a.d + (size_t)r[i] * a.nblk;
-        W.w[i][k] = load_nt(reinterpret_cast<const uint4*>(rq + uc * 16u));
-        W.d[i][k] = load_half_nt(rd + (uc >> 1));
+        W.w[i][k] = load_nt(reinterpret_cast<const uint4*>(at(a.qs, row * kp) + uc * 16u));
+        W.ks[i][k] = load_nt(reinterpret_cast<const uint16_t*>(at(a.d, row * a.nblk * 2)) + (uc >> 1));
       } else if constexpr (QT == kQ4_0) {
-        const uint8_t* rq = a.qs + (size_t)r[i] * a.nblk * 16;
-        const uint16_t* rd = a.d + (size_t)r[i] * a.nblk;
-        W.w[i][k] = load_nt(reinterpret_cast<const uint4*>(rq + uc * 16u));
-        W.d[i][k] = load_half_nt(rd + uc);
+        W.w[i][k] = load_nt(reinterpret_cast<const uint4*>(at(a.qs, row * a.nblk * 16) + uc * 16u));
+        W.ks[i][k] = load_nt(reinterpret_cast<const uint16_t*>(at(a.d, row * a.nblk * 2)) + uc);
       } else if constexpr (QT == kQ4_K) {
-        const uint8_t* rq = a.qs + (size_t)r[i] * a.nblk * 16;
-        W.w[i][k] = load_nt(reinterpret_cast<const uint4*>(rq + uc * 16u));
-        W.ks[i][k] = load_nt(a.d + (size_t)r[i] * a.nblk + uc);
-        W.kd[i][k] = load_nt(a.sd + (size_t)r[i] * (a.nblk >> 3) + (uc >> 3));
+        W.w[i][k] = load_nt(reinterpret_cast<const uint4*>(at(a.qs, row * a.nblk * 16) + uc * 16u));
+        W.ks[i][k] = load_nt(reinterpret_cast<const uint16_t*>(at(a.d, row * a.nblk * 2)) + uc);
+        W.kd[i][k] = load_nt(reinterpret_cast<const uint32_t*>(at(a.sd, row * (a.nblk >> 3) * 4)) + (uc >> 3));
       } else if constexpr (QT == kQ6_K) {
-        const uint8_t* rq = a.qs + (size_t)r[i] * kp;
-        W.w[i][k] = load_nt(reinterpret_cast<const uint4*>(rq + uc * 16u));
-        W.ks[i][k] = load_nt(reinterpret_cast<const int8_t*>(a.d) + (size_t)r[i] * 2 * a.nblk + uc);
-        W.kd[i][k] = load_nt(a.sd + (size_t)r[i] * (a.nblk >> 3) + (uc >> 4));
+        W.w[i][k] = load_nt(reinterpret_cast<const uint4*>(at(a.qs, row * kp) + uc * 16u));
+        W.ks[i][k] = load_nt(reinterpret_cast<const int8_t*>(at(a.d, row * 2 * a.nblk)) + uc);
+        W.kd[i][k] = load_nt(reinterpret_cast<const uint32_t*>(at(a.sd, row * (a.nblk >> 3) * 4)) + (uc >> 4));
       } else {
-        const uint8_t* rq = a.qs + (size_t)r[i] * kp * 4;
-        W.w[i][k] = load_nt(reinterpret_cast<const uint4*>(rq + uc * 16u));
-        W.d[i][k] = 1.f;
+        W.w[i][k] = load_nt(reinterpret_cast<const uint4*>(at(a.qs, row * kp * 4) + uc * 16u));
       }
     }
   }
 }
 
 // One Q4_0 block given its 32 activations as 8 float4 (elements 0..15 in
-// xv[0..3], 16..31 in xv[4..7]): sum_j n_j x_j with the raw nibbles n (no offset).
+// xv[0..3], 16..31 in xv[4..7]): 2^-24 * sum_j n_j x_j with the raw nibbles n
+// (no offset).  Word i of the block holds elements 4i..4i+3 in its low nibbles
+// and 4i+16..4i+19 in its high nibbles.  Masking a word with 0x000F000F leaves
+// two nibbles in the low bits of its 16-bit halves, where they read as fp16
+// subnormals n * 2^-24 (0x00F000F0: 16 n * 2^-24); the mixed-precision FMA
+// takes an fp16 half directly (op_sel), so a weight costs one FMA plus 5/8 of
+// a mask or shift, where a byte conversion would add a whole instruction.  The
+// fp16 values are exact, and the power-of-two factor leaves every product and
+// every rounding of the sums as for n x (f32 has the exponent range to spare;
+// denormals are preserved), so the result is the f32 sum times 2^-24.
 QD_DEV float dot32_q4_raw4(uint4 w, const float4 (&xv)[8]) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
   float lo = 0.f, hi = 0.f;
-  uint32_t words[4] = {w.x, w.y, w.z, w.w};
+  const uint32_t words[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    uint32_t l = opaque_and(words[i], 0x0F0F0F0Fu);
-    uint32_t h = opaque_and(words[i], 0xF0F0F0F0u);
+    const uint32_t s = words[i] >> 8;
+    const h2 a = __builtin_bit_cast(h2, opaque_and(words[i], 0x000F000Fu));  // elements 4i, 4i+2
+    const h2 c = __builtin_bit_cast(h2, opaque_and(s, 0x000F000Fu));         // 4i+1, 4i+3
+    const h2 b = __builtin_bit_cast(h2, opaque_and(words[i], 0x00F000F0u));  // 4i+16, 4i+18 (x16)
+    const h2 e = __builtin_bit_cast(h2, opaque_and(s, 0x00F000F0u));         // 4i+17, 4i+19 (x16)
     const float4 xl = xv[i], xh = xv[4 + i];
-    lo += (float)(l & 0xffu) * xl.x;
-    lo += (float)((l >> 8) & 0xffu) * xl.y;
-    lo += (float)((l >> 16) & 0xffu) * xl.z;
-    lo += (float)(l >> 24) * xl.w;
-    hi += (float)(h & 0xffu) * xh.x;
-    hi += (float)((h >> 8) & 0xffu) * xh.y;
-    hi += (float)((h >> 16) & 0xffu) * xh.z;
-    hi += (float)(h >> 24) * xh.w;
+    lo = fmaf((float)a.x, xl.x, lo);
+    lo = fmaf((float)c.x, xl.y, lo);
+    lo = fmaf((float)a.y, xl.z, lo);
+    lo = fmaf((float)c.y, xl.w, lo);
+    hi = fmaf((float)b.x, xh.x, hi);
+    hi = fmaf((float)e.x, xh.y, hi);
+    hi = fmaf((float)b.y, xh.z, hi);
+    hi = fmaf((float)e.y, xh.w, hi);
   }
   return lo + 0.0625f * hi;
 }
+constexpr float kTwo24 = 16777216.0f;
 
 template <int QT, int R, int U, int M>
 QD_DEV void gemv_compute(const float4* xs4, const float* xsum, int kp, int nblk, int base, int lane, int nunits,
@@ -365,16 +430,18 @@ QD_DEV void gemv_compute(const float4* xs4, const float* xsum, int kp, int nblk,
           acc[i][mi] += q6k_scale(W.ks[i][k], W.kd[i][k]) * dot16_q8(W.w[i][k], xv[0], xv[1], xv[2], xv[3]);
       } else if constexpr (QT == kQ8_0) {
 #pragma unroll
-        for (int i = 0; i < R; ++i) acc[i][mi] += W.d[i][k] * dot16_q8(W.w[i][k], xv[0], xv[1], xv[2], xv[3]);
+        for (int i = 0; i < R; ++i)
+          acc[i][mi] += half_bits_to_float((uint16_t)W.ks[i][k]) * dot16_q8(W.w[i][k], xv[0], xv[1], xv[2], xv[3]);
       } else if constexpr (QT == kQ4_0) {
         const float bs = 8.0f * xsum[mi * nblk + u];
 #pragma unroll
-        for (int i = 0; i < R; ++i) acc[i][mi] += W.d[i][k] * (dot32_q4_raw4(W.w[i][k], xv) - bs);
+        for (int i = 0; i < R; ++i)
+          acc[i][mi] += half_bits_to_float((uint16_t)W.ks[i][k]) * fmaf(dot32_q4_raw4(W.w[i][k], xv), kTwo24, -bs);
       } else if constexpr (QT == kQ4_K) {
         const float xs = xsum[mi * nblk + u];
 #pragma unroll
         for (int i = 0; i < R; ++i)
-          acc[i][mi] += q4k_scale(W.ks[i][k], W.kd[i][k]) * dot32_q4_raw4(W.w[i][k], xv) -
+          acc[i][mi] += q4k_scale(W.ks[i][k], W.kd[i][k]) * (dot32_q4_raw4(W.w[i][k], xv) * kTwo24) -
                         q4k_min(W.ks[i][k], W.kd[i][k]) * xs;
       } else {
 #pragma unroll
@@ -388,48 +455,63 @@ QD_DEV void gemv_compute(const float4* xs4, const float* xsum, int kp, int nblk,
   }
 }
 
-// Finish row group `grp`: reduce each accumulator over the 64 lanes, apply the
-// input row's norm scale, and let lane 0 write with the mode's epilogue (AM:
-// and keep the wave's best (value, index) of the stored rows in bv / bi).
-template <int QT, int M, int MODE, int R, int U, bool AM = false>
-QD_DEV void gemv_store(const GemvArgs& a, int grp, int lane, const float (&scale)[M], float (&acc)[R][M],
-                       float (&bv)[M], int (&bi)[M]) {
+// Outputs of the wave's row groups are held in registers until the wave is
+// done (obuf[mi], lane l = the l-th output of the wave) and written by one
+// pass at the end: a store (or the residual add's load) inside the ring would
+// make every later wait for a weight tile a wait for all loads in flight,
+// since loads and stores share one in-order counter.
+// Outputs per row group: R rows, or R / 2 (gate, up) pairs.
+template <int MODE, int R>
+constexpr int group_outputs() { return (MODE == kModePairSilu || MODE == kModePairGelu) ? R / 2 : R; }
+
+// Finish a row group: reduce each accumulator over the 64 lanes, apply the
+// input row's norm scale (and the pair activation), and put the group's
+// outputs into lanes nslot.. of obuf.
+template <int M, int MODE, int R>
+QD_DEV void gemv_group_end(const float (&scale)[M], float (&acc)[R][M], float (&obuf)[M], int lane, int nslot) {
   constexpr bool kPair = MODE == kModePairSilu || MODE == kModePairGelu;
 #pragma unroll
   for (int mi = 0; mi < M; ++mi) {
     float sv[R];
 #pragma unroll
     for (int i = 0; i < R; ++i) sv[i] = wave_sum(acc[i][mi]) * scale[mi];
-    if (lane == 0 && mi < a.m) {
-      float* yr = (a.y_ind ? *a.y_ind + a.y_off : a.y) + (size_t)mi * a.ldy;
 #pragma unroll
-      for (int i = 0; i < R; ++i) {
-        if constexpr (kPair) {
-          if (i & 1) {
-            const int n = grp * (R / 2) + i / 2;
-            yr[n] = (MODE == kModePairSilu ? act_silu(sv[i - 1]) : act_gelu_tanh(sv[i - 1])) * sv[i];
-          }
-        } else {
-          const int row = grp * R + i;
-          if (row < a.rows) {
-            if constexpr (MODE == kModeAdd) {
-              yr[row] += sv[i];
-            } else {
-              const float v = a.bias ? sv[i] + a.bias[row] : sv[i];
-              yr[row] = v;
-              if constexpr (AM) {
-                if (ranks_before(v, row, bv[mi], bi[mi])) {
-                  bv[mi] = v;
-                  bi[mi] = row;
-                }
-              }
-            }
-          }
-        }
-      }
+    for (int j = 0; j < group_outputs<MODE, R>(); ++j) {
+      float v;
+      if constexpr (kPair) v = (MODE == kModePairSilu ? act_silu(sv[2 * j]) : act_gelu_tanh(sv[2 * j])) * sv[2 * j + 1];
+      else v = sv[j];
+      if (lane == nslot + j) obuf[mi] = v;
     }
 #pragma unroll
     for (int i = 0; i < R; ++i) acc[i][mi] = 0.f;
+  }
+}
+
+// Write the nslot outputs held in obuf: lane l holds output j = l % RO of the
+// wave's k-th row group, k = l / RO (row group gwave + k * nwaves), with the
+// mode's epilogue (store: + bias; add: added to y).  AM: each lane keeps the
+// best (value, index) it has written in bv / bi.
+template <int M, int MODE, int R, bool AM>
+QD_DEV void gemv_flush(const GemvArgs& a, float* ybase, int lane, int gwave, int nwaves, int nslot,
+                       const float (&obuf)[M], float (&bv)[M], int (&bi)[M]) {
+  constexpr int RO = group_outputs<MODE, R>();
+  const int nout = (MODE == kModePairSilu || MODE == kModePairGelu) ? a.rows / 2 : a.rows;
+  const int o = (gwave + (lane / RO) * nwaves) * RO + lane % RO;
+  if (lane >= nslot || o >= nout) return;
+#pragma unroll
+  for (int mi = 0; mi < M; ++mi) {
+    if (mi >= a.m) break;
+    float* yr = ybase + (size_t)mi * a.ldy;
+    float v = obuf[mi];
+    if constexpr (MODE == kModeAdd) v = yr[o] + v;
+    else if constexpr (MODE == kModeStore) v = a.bias ? v + a.bias[o] : v;
+    yr[o] = v;
+    if constexpr (AM) {
+      if (ranks_before(v, o, bv[mi], bi[mi])) {
+        bv[mi] = v;
+        bi[mi] = o;
+      }
+    }
   }
 }
 
@@ -464,31 +546,34 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(GemvArgs a) {
   const int ngroups = kPair ? a.rows / R : (a.rows + R - 1) / R;
   const int tpg = (nunits + 64 * U - 1) / (64 * U);  // tiles per row group
 
+  const uint8_t* const park = reinterpret_cast<const uint8_t*>(a.x ? a.x : a.xd);
+
   // Sets are always named by compile-time indices (integral_constant
   // arguments), so they stay in registers whether or not loops unroll.
   WRegs<QT, R, U> ws[NS];
   int tg[NS], tt[NS];  // (row group, tile within the group) held by each set
   int g = gwave, t = 0;  // next tile to request
-  // request the tile (g, t) into set S and advance (g, t)
+  // request the tile (g, t) into set S and advance (g, t); past the wave's
+  // last tile the set's loads are parked (see gemv_load)
   auto request = [&](auto S) {
     constexpr int s = decltype(S)::value;
     tg[s] = g;
     tt[s] = t;
-    if (g < ngroups) {
-      int r[R];
-      group_rows<R, kPair>(g, a.rows, r);
-      gemv_load<QT, R, U>(a, r, t * 64 * U, lane, nunits, ws[s]);
-      if (++t == tpg) {
-        t = 0;
-        g += nwaves;
-      }
+    const bool live = g < ngroups;
+    int r[R];
+    group_rows<R, kPair>(live ? g : 0, a.rows, r);
+    gemv_load<QT, R, U>(a, r, t * 64 * U, lane, nunits, ws[s], live, park);
+    if (live && ++t == tpg) {
+      t = 0;
+      g += nwaves;
     }
   };
-  request(std::integral_constant<int, 0>{});
-  if constexpr (NS > 2) request(std::integral_constant<int, 1>{});
-
   float scale[M];
-  gemv_stage_x<QT, M, NW, RES, ACC>(a, xs4, kp, scale);  // ends with a barrier
+  // the first NS - 1 tiles are requested right behind the first input loads
+  gemv_stage_x<QT, M, NW, RES, ACC>(a, xs4, kp, scale, [&] {
+    request(std::integral_constant<int, 0>{});
+    if constexpr (NS > 2) request(std::integral_constant<int, 1>{});
+  });  // ends with a barrier
   if constexpr (nibble_layout(QT)) {
     for (int i = threadIdx.x; i < M * a.nblk; i += 64 * NW) {
       const int mi = i / a.nblk, u = i % a.nblk;
@@ -508,40 +593,54 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(GemvArgs a) {
   for (int i = 0; i < R; ++i)
 #pragma unroll
     for (int mi = 0; mi < M; ++mi) acc[i][mi] = 0.f;
-  float bv[M];  // AM: the wave's best stored value and its row (lane 0)
+  float obuf[M];  // the wave's finished outputs, one per lane (gemv_group_end)
+  float bv[M];    // AM: each lane's best written value and its row
   int bi[M];
 #pragma unroll
   for (int mi = 0; mi < M; ++mi) {
+    obuf[mi] = 0.f;
     bv[mi] = -INFINITY;
     bi[mi] = 0x7fffffff;
   }
+  // the output rows, resolved once (y_ind: a pointer in device memory)
+  float* const ybase = a.y_ind ? *a.y_ind + a.y_off : a.y;
+  constexpr int RO = group_outputs<MODE, R>();
+  int nslot = 0;  // outputs held in obuf (the launch gives a wave at most 64)
 
-  // one ring step on set S: refill the set computed last, then compute S
-  bool done = false;
+  // One ring step on set S: refill the set computed last (a parked load past
+  // the wave's last tile), then compute S.  Every step that runs issues the
+  // same loads, and the loop is left right after the wave's last tile, so no
+  // path skips a step and then continues with the next one.
   auto step = [&](auto S) {
     constexpr int s = decltype(S)::value;
-    if (done) return;
     request(std::integral_constant<int, (s + NS - 1) % NS>{});
-    if (tg[s] >= ngroups) {
-      done = true;
-      return;
-    }
     gemv_compute<QT, R, U, M>(xs4, xsum, kp, a.nblk, tt[s] * 64 * U, lane, nunits, ws[s], acc);
-    if (tt[s] == tpg - 1) gemv_store<QT, M, MODE, R, U, AM>(a, tg[s], lane, scale, acc, bv, bi);
+    if (tt[s] == tpg - 1) {
+      gemv_group_end<M, MODE, R>(scale, acc, obuf, lane, nslot);
+      nslot += RO;
+    }
   };
-  while (!done) {
+  // the wave's tiles: row groups gwave, gwave + nwaves, ... below ngroups
+  int left = gwave < ngroups ? ((ngroups - 1 - gwave) / nwaves + 1) * tpg : 0;
+  while (left > 0) {
     step(std::integral_constant<int, 0>{});
+    if (--left == 0) break;
     step(std::integral_constant<int, 1>{});
-    if constexpr (NS > 2) step(std::integral_constant<int, 2>{});
+    if (--left == 0) break;
+    if constexpr (NS > 2) {
+      step(std::integral_constant<int, 2>{});
+      --left;
+    }
   }
+  gemv_flush<M, MODE, R, AM>(a, ybase, lane, gwave, nwaves, nslot, obuf, bv, bi);
   if constexpr (AM) {
-    if (lane == 0) {
 #pragma unroll
-      for (int mi = 0; mi < M; ++mi)
-        if (mi < a.m) {
-          a.amax_v[(size_t)mi * nwaves + gwave] = bv[mi];
-          a.amax_i[(size_t)mi * nwaves + gwave] = bi[mi];
-        }
+    for (int mi = 0; mi < M; ++mi) {
+      argmax_pair_wave(bv[mi], bi[mi]);
+      if (lane == 0 && mi < a.m) {
+        a.amax_v[(size_t)mi * nwaves + gwave] = bv[mi];
+        a.amax_i[(size_t)mi * nwaves + gwave] = bi[mi];
+      }
     }
   }
 }

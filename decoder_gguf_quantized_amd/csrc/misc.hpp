@@ -499,17 +499,6 @@ QD_DEV void sample_resolve(SampleArgs& a) {
   }
 }
 
-QD_DEV void argmax_pair_wave(float& v, int& i) {
-  for (int o = 32; o > 0; o >>= 1) {
-    float ov = __shfl_xor(v, o);
-    int oi = __shfl_xor(i, o);
-    if (ranks_before(ov, oi, v, i)) {
-      v = ov;
-      i = oi;
-    }
-  }
-}
-
 __global__ __launch_bounds__(256) void sample_stage1_kernel(SampleArgs a) {
   sample_resolve(a);
   __shared__ float sv[4];

@@ -246,13 +246,13 @@ const char* gemm_class(int type) {
   }
 }
 
-void gemv_type(int type, int M, int ru, int mode, dim3 grid, size_t lds, hipStream_t st, const GemvArgs& a) {
+void gemv_type(int type, int M, int cls, int mode, dim3 grid, size_t lds, hipStream_t st, const GemvArgs& a) {
   switch (type) {
-    case kQ8_0: gemv_launch<kQ8_0>(M, ru, mode, grid, lds, st, a); break;
-    case kQ4_0: gemv_launch<kQ4_0>(M, ru, mode, grid, lds, st, a); break;
-    case kQ4_K: gemv_launch<kQ4_K>(M, ru, mode, grid, lds, st, a); break;
-    case kQ6_K: gemv_launch<kQ6_K>(M, ru, mode, grid, lds, st, a); break;
-    default: gemv_launch<kF32>(M, ru, mode, grid, lds, st, a); break;
+    case kQ8_0: gemv_launch<kQ8_0>(M, cls, mode, grid, lds, st, a); break;
+    case kQ4_0: gemv_launch<kQ4_0>(M, cls, mode, grid, lds, st, a); break;
+    case kQ4_K: gemv_launch<kQ4_K>(M, cls, mode, grid, lds, st, a); break;
+    case kQ6_K: gemv_launch<kQ6_K>(M, cls, mode, grid, lds, st, a); break;
+    default: gemv_launch<kF32>(M, cls, mode, grid, lds, st, a); break;
   }
 }
 
@@ -300,20 +300,23 @@ int gemv(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, c
   while (cap > 1 && per_row * cap > kGemvLdsMax) cap /= 2;
   if (per_row > kGemvLdsMax) throw HipError{"gemv: input row too long for LDS"};
   const bool pair = mode == kModePairSilu || mode == kModePairGelu;
-  const int nunits = int8_layout(w.type) ? 2 * w.nblk : (nibble_layout(w.type) ? w.nblk : kp / 4);
-  int ru = nunits <= 64 ? 0 : (nunits <= 128 ? 1 : 2);
-  if (ru == 2 && (pair ? w.rows / 2 : (w.rows + 1) / 2) >= 2048) ru = 3;
-  // about four workgroups of four waves (two of eight) per CU
-  const int grid_cap = ru_waves(ru) == 8 ? 512 : 1024;
-  const int R = ru_rows(ru), NW = ru_waves(ru);
-  const int ngroups = pair ? w.rows / R : (w.rows + R - 1) / R;
-  // waves stay resident and loop: about four workgroups per CU, so the input
-  // staging of each workgroup is amortised over many row groups
-  dim3 grid(std::max(1, std::min((ngroups + NW - 1) / NW, grid_cap)));
+  int nwaves = 0;
   for (int r0 = 0; r0 < nrows; r0 += cap) {
     const int mr = std::min(cap, nrows - r0);
     int M = 1;
     while (M < mr) M *= 2;
+    const int cls = gemv_tile_class(pair, w.rows, M);
+    const int R = class_rows(cls), NW = class_waves(cls);
+    const int ngroups = pair ? w.rows / R : (w.rows + R - 1) / R;
+    // waves stay resident and loop: about four workgroups of four waves (two
+    // of eight) per CU, so the input staging of each workgroup is amortised
+    // over many row groups; enough waves that none finishes more than 64
+    // outputs (each wave holds its outputs in one register, a lane per output,
+    // until it is done)
+    const int grid_cap = NW == 8 ? 512 : 1024;
+    const int per_wave = 64 / (pair ? R / 2 : R);  // row groups per wave at most
+    const int grid_min = (ngroups + per_wave * NW - 1) / (per_wave * NW);
+    dim3 grid(std::max({1, grid_min, std::min((ngroups + NW - 1) / NW, grid_cap)}));
     GemvArgs a{w.qs, w.d, w.rows, w.nblk, x ? x + (size_t)r0 * ldx : nullptr, ldx, norm_w, eps,
                y ? y + (size_t)r0 * ldy : nullptr, ldy, mr, y_ind, (long)r0 * ldy,
                res.add ? res.add + (size_t)r0 * ldx : nullptr, res.add_w,
@@ -333,9 +336,10 @@ int gemv(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, c
     const double bytes =
         w.gguf_bytes + (double)mr * kp * (acc.o ? 4 * kAccCopies : 4) + (double)mr * (pair ? w.rows / 2 : w.rows) * 4;
     Timed tm(m, st, gemv_class(w.type), bytes, 2.0 * mr * w.rows * (double)w.cols);
-    gemv_type(w.type, M, ru, mode, grid, lds, st, a);
+    gemv_type(w.type, M, cls, mode, grid, lds, st, a);
+    nwaves = (int)grid.x * NW;
   }
-  return (int)grid.x * NW;
+  return nwaves;
 }
 
 // Prefill projection.  prec: QDEC_PREFILL_F32 (f32 operands, the default),
