@@ -74,9 +74,11 @@ void gemv_dispatch_mode(int mode, dim3 grid, size_t lds, hipStream_t st, const G
 }
 
 // Tile classes.  Every class gives a lane one 16-byte unit per row and tile
-// (U = 1): small tiles keep several in flight per wave through the ring and
-// spread each wave's arithmetic over the stream, which measured faster than
-// two or four units per lane on every decode shape of the 0.6B and 8B models.
+// (U = 1): small tiles spread each wave's arithmetic over the stream, which
+// measured faster than two or four units per lane on every decode shape of
+// the 0.6B and 8B models.  Eight-wave workgroups halve the input staging per
+// CU, which pays on long rows (the 8B down projection 12.4 -> 10.1 us) but not
+// for the gate/up pairs.
 //   0: one row per wave, four-wave workgroups (store / add on fewer than 4,096
 //      rows: two-row groups would leave CUs without a workgroup);
 //   1: two rows per wave, eight-wave workgroups (store / add, 4,096 rows or

@@ -516,13 +516,12 @@ QD_DEV void gemv_flush(const GemvArgs& a, float* ybase, int lane, int gwave, int
 }
 
 // Register sets of the weight pipeline: with NS sets, NS - 1 tiles are in
-// flight while one is computed.  Three sets for the small tiles (R * U <= 4,
-// 20 VGPRs per set for the quantized types) and for the 8-unit tiles of
-// eight-wave workgroups at one input row (two waves per SIMD there, so the
-// extra set costs no occupancy; the 8B shape's down projection 13.2 -> 12.4
-// us), two otherwise.
+// flight while one is computed.  Two sets for two-row tiles and three for
+// one-row tiles: with one 16-byte unit per lane a deeper ring costs more in
+// occupancy than it gains in loads in flight (measured on the decode shapes of
+// the 0.6B and 8B models, one and sixteen input rows).
 template <int R, int U, int M, int NW>
-constexpr int gemv_sets() { return (R * U <= 4 && M <= 4) ? 3 : (NW == 8 && M == 1 ? 3 : 2); }
+constexpr int gemv_sets() { return R * U == 1 ? 3 : 2; }
 
 // R rows per wave, U 16-byte units per lane in flight per row, M input rows.
 // Each wave walks its (row group, unit block) tiles in order through a ring of
@@ -573,6 +572,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(GemvArgs a) {
   gemv_stage_x<QT, M, NW, RES, ACC>(a, xs4, kp, scale, [&] {
     request(std::integral_constant<int, 0>{});
     if constexpr (NS > 2) request(std::integral_constant<int, 1>{});
+    if constexpr (NS > 3) request(std::integral_constant<int, 2>{});
   });  // ends with a barrier
   if constexpr (nibble_layout(QT)) {
     for (int i = threadIdx.x; i < M * a.nblk; i += 64 * NW) {
@@ -622,6 +622,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(GemvArgs a) {
   };
   // the wave's tiles: row groups gwave, gwave + nwaves, ... below ngroups
   int left = gwave < ngroups ? ((ngroups - 1 - gwave) / nwaves + 1) * tpg : 0;
+  static_assert(NS >= 2 && NS <= 4, "gemv: two to four register sets");
   while (left > 0) {
     step(std::integral_constant<int, 0>{});
     if (--left == 0) break;
@@ -629,6 +630,10 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(GemvArgs a) {
     if (--left == 0) break;
     if constexpr (NS > 2) {
       step(std::integral_constant<int, 2>{});
+      if (--left == 0) break;
+    }
+    if constexpr (NS > 3) {
+      step(std::integral_constant<int, 3>{});
       --left;
     }
   }

@@ -308,12 +308,11 @@ int gemv(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, c
     const int cls = gemv_tile_class(pair, w.rows, M);
     const int R = class_rows(cls), NW = class_waves(cls);
     const int ngroups = pair ? w.rows / R : (w.rows + R - 1) / R;
-    // waves stay resident and loop: about four workgroups of four waves (two
-    // of eight) per CU, so the input staging of each workgroup is amortised
-    // over many row groups; enough waves that none finishes more than 64
-    // outputs (each wave holds its outputs in one register, a lane per output,
-    // until it is done)
-    const int grid_cap = NW == 8 ? 512 : 1024;
+    // waves stay resident and loop: at most four workgroups per CU, so the
+    // input staging of each workgroup is amortised over many row groups;
+    // enough waves that none finishes more than 64 outputs (each wave holds
+    // its outputs in one register, a lane per output, until it is done)
+    const int grid_cap = 1024;
     const int per_wave = 64 / (pair ? R / 2 : R);  // row groups per wave at most
     const int grid_min = (ngroups + per_wave * NW - 1) / (per_wave * NW);
     dim3 grid(std::max({1, grid_min, std::min((ngroups + NW - 1) / NW, grid_cap)}));
