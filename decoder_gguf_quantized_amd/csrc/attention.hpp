@@ -139,16 +139,16 @@ QD_DEV void store_lane8(float* rowp, int hd, int li, const float (&v)[8]) {
 // arrives: the RoPE row (copied per sequence at step start), the raw queries
 // and new key/value, and on full-causal layers the chunk's first keys and
 // values (a chunk's addresses do not depend on the position; keys past it are
-// masked).  The key loop keeps two position pairs per stream in flight.
+// masked).  The walk takes two position pairs per stream per round.
 // PAGED: the cache is paged; a chunk lies in one page (the host keeps chunks
 // no longer than a page), so one table entry per workgroup places all of it.
 template <int HD, int G, bool PAGED>
 __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
   constexpr int LG = HD / 8;      // lanes per position
   constexpr int NG = 256 / LG;    // position streams per workgroup
-  __shared__ float sm_o[NG][G][HD];
-  __shared__ float sm_m[NG][G], sm_l[NG][G];
-  __shared__ float sm_f[G];
+  // each wave's streams merged to one (M, L, O) per head (stream_reduce)
+  __shared__ float sm_o[4][G][HD];
+  __shared__ float sm_m[4][G], sm_l[4][G];
 
   const int c = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x, gi = tid / LG, li = tid % LG;
@@ -181,15 +181,13 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
   float q[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h) load_lane8(row + (size_t)(g * G + h) * HD, HD, li, q[h]);
-  // the lane's 8 dims of the QK-norm gains (requested with the rest)
+  // the lane's 8 dims of the QK-norm gains, requested with the rest (without
+  // a norm the row itself stands in, unused: every path issues the same loads,
+  // so that each wait below is for exactly the data it needs)
   const bool qkn = a.q_norm != nullptr;
   float wq[8], wk[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) wq[e] = wk[e] = 1.f;
-  if (qkn) {
-    load_lane8(a.q_norm, HD, li, wq);
-    load_lane8(a.k_norm, HD, li, wk);
-  }
+  load_lane8(qkn ? a.q_norm : row, HD, li, wq);
+  load_lane8(qkn ? a.k_norm : row, HD, li, wk);
   float kn[8], vn[8];
   load_lane8(row + (size_t)(a.nq + g) * HD, HD, li, kn);
   load_lane8(row + (size_t)(a.nq + a.nkv + g) * HD, HD, li, vn);
@@ -204,29 +202,40 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
     }
   };
   float ka[2][8], va[2][8], kb[2][8], vb[2][8];
-  // full-causal layers: the chunk's first two pairs (four positions per stream)
-  bool b_ready = spec && a.chunk > 2 * NG;
-  if (spec) fetch_pair(cb + gi, ka, va);
-  if (b_ready) fetch_pair(cb + 2 * NG + gi, kb, vb);
+  // the chunk's first two pairs (four positions per stream), requested before
+  // the new position arrives: their addresses do not depend on it.  They go
+  // out after the loads above (the scheduler may not move loads across this
+  // point): loads return in order, and the queries must not wait for the cache.
+  __builtin_amdgcn_sched_barrier(0);
+  fetch_pair(cb + gi, ka, va);
+  fetch_pair(cb + 2 * NG + gi, kb, vb);
 
-  // the other parity's accumulators are zeroed by all workgroups together,
-  // before any of them can return
-  {
+  // The other parity's accumulators are zeroed by all workgroups together;
+  // workgroups with work do their share after their last load (loads and
+  // stores share one in-order counter: a store in flight would turn every
+  // wait for a load into a wait for all of them).
+  auto clear_other = [&] {
     const int nwg = gridDim.x * gridDim.y * gridDim.z;
     const int wg = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
     const size_t n = (size_t)kAccCopies * a.acc_rows * a.nq * (HD + 1);
     for (size_t i = (size_t)wg * 256 + tid; i < n; i += (size_t)nwg * 256) a.acc_clear[i] = 0.f;
-  }
+  };
 
   int lo, hi;
   attn_key_range(p, a.window, lo, hi);
   const int c_lo = lo / a.chunk, c_hi = hi / a.chunk;
-  if (c < c_lo || c > c_hi) return;
+  if (c < c_lo || c > c_hi) {
+    clear_other();
+    return;
+  }
   const int start = max(lo, cb), end = min(hi + 1, cb + a.chunk);
   // first position pair of the chunk's walk (windowed layers skip whole pairs
   // below the window)
   const int jb0 = spec ? cb : cb + ((start - cb) / (2 * NG)) * (2 * NG);
-  if (!spec) fetch_pair(jb0 + gi, ka, va);
+  if (jb0 != cb) {  // a windowed layer whose walk starts further in
+    fetch_pair(jb0 + gi, ka, va);
+    fetch_pair(jb0 + 2 * NG + gi, kb, vb);
+  }
 
   float o[G][8], m[G], l[G], ref[G];
   norm_rope_group<LG>(kn, qkn, wk, a.eps, HD, cs, sn);
@@ -248,102 +257,114 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
     ref[h] = group_sum<LG>(dot);
   }
   const bool has_new = c == c_hi;
-  if (has_new && gi == 0) {
-    store_lane8(a.kc + (head_base + p) * HD, HD, li, kn);
-    store_lane8(a.vc + (head_base + p) * HD, HD, li, vn);
-  }
-  // online softmax over one position; masked positions leave the state as is
-  // (selects, no branch: every lane of a stream group takes the same path).
-  // A masked position's row may never have been written (cache rows past the
-  // new position are requested ahead), so its values are replaced by zeros
-  // before any arithmetic: 0 * NaN would otherwise reach the output.
-  auto accumulate = [&](int j, const float (&kc)[8], const float (&vc)[8]) {
-    const bool valid = j >= start && j < end;
-    const bool is_new = has_new && j == p;  // the cache row is written above; use the registers
-    float k[8], v[8];
+  // online softmax over the two positions of a pair (j0, j0 + NG): one
+  // rescale of the state per pair.  Masked positions take no part (selects, no
+  // branch: every lane of a stream group takes the same path).  A masked
+  // position's row may never have been written (cache rows past the new
+  // position are requested ahead), so its values are replaced by zeros before
+  // any arithmetic: 0 * NaN would otherwise reach the output.
+  auto accumulate = [&](int j0, const float (&kc)[2][8], const float (&vc)[2][8]) {
+    bool valid[2];
+    float k[2][8], v[2][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      k[e] = is_new ? kn[e] : (valid ? kc[e] : 0.f);
-      v[e] = is_new ? vn[e] : (valid ? vc[e] : 0.f);
+    for (int t = 0; t < 2; ++t) {
+      const int j = j0 + t * NG;
+      valid[t] = j >= start && j < end;
+      const bool is_new = has_new && j == p;  // its cache row is written at the end: use the registers
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        k[t][e] = is_new ? kn[e] : (valid[t] ? kc[t][e] : 0.f);
+        v[t][e] = is_new ? vn[e] : (valid[t] ? vc[t][e] : 0.f);
+      }
     }
+    const bool any = valid[0] || valid[1];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float dot = 0.f;
+      float sc[2];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dot += q[h][e] * k[e];
-      const float sc = group_sum<LG>(dot);
-      const float mn = valid ? fmaxf(m[h], sc) : m[h];
-      const float corr = valid ? exp2f(m[h] - mn) : 1.f;
-      const float pr = valid ? exp2f(sc - mn) : 0.f;
-      l[h] = l[h] * corr + pr;
+      for (int t = 0; t < 2; ++t) {
+        float dot = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[h][e] = o[h][e] * corr + pr * v[e];
+        for (int e = 0; e < 8; ++e) dot += q[h][e] * k[t][e];
+        sc[t] = group_sum<LG>(dot);
+      }
+      const float mn = any ? fmaxf(m[h], fmaxf(valid[0] ? sc[0] : -INFINITY, valid[1] ? sc[1] : -INFINITY)) : m[h];
+      const float corr = any ? exp2f(m[h] - mn) : 1.f;
+      const float p0 = valid[0] ? exp2f(sc[0] - mn) : 0.f;
+      const float p1 = valid[1] ? exp2f(sc[1] - mn) : 0.f;
+      l[h] = l[h] * corr + (p0 + p1);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[h][e] = o[h][e] * corr + (p0 * v[0][e] + p1 * v[1][e]);
       m[h] = mn;
     }
   };
-  // walk of the chunk in pairs of positions, two pairs in flight (wave-uniform
-  // trip count: jb and end are the same for every lane)
-  for (int jb = jb0; jb < end; jb += 4 * NG) {
-    const bool more_b = jb + 2 * NG < end;
-    if (more_b && !b_ready) fetch_pair(jb + 2 * NG + gi, kb, vb);
-    b_ready = false;
-    accumulate(jb + gi, ka[0], va[0]);
-    accumulate(jb + gi + NG, ka[1], va[1]);
-    if (!more_b) break;
-    const bool more_a = jb + 4 * NG < end;
-    if (more_a) fetch_pair(jb + 4 * NG + gi, ka, va);
-    accumulate(jb + 2 * NG + gi, kb[0], vb[0]);
-    accumulate(jb + 3 * NG + gi, kb[1], vb[1]);
+  // walk of the chunk two pairs at a time (wave-uniform trip count: jb and end
+  // are the same for every lane); both pairs are in flight when a round
+  // starts, and the loads of a round are issued on every path that reaches it
+  for (int jb = jb0;; jb += 4 * NG) {
+    accumulate(jb + gi, ka, va);
+    accumulate(jb + 2 * NG + gi, kb, vb);
+    if (jb + 4 * NG >= end) break;
+    fetch_pair(jb + 4 * NG + gi, ka, va);
+    fetch_pair(jb + 6 * NG + gi, kb, vb);
   }
+  // Merge the streams.  Inside a wave (64 / LG streams, lanes l and l + LG k
+  // hold the same dims) the maxima, weights and sums move between lane rows
+  // with cross-lane swaps (no LDS); then one (M, L, O) per wave and head goes
+  // through LDS, the workgroup's four are merged, rescaled to the reference and
+  // added to the accumulators.
+  const int wave = tid >> 6;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    store_lane8(&sm_o[gi][h][0], HD, li, o[h]);
-    if (li == 0) {
-      sm_m[gi][h] = m[h];
-      sm_l[gi][h] = l[h];
-    }
-  }
-  __syncthreads();
-  // streams -> one (M, L) per head: wave w takes heads w, w + 4, ...; lane k
-  // holds stream k's (m, l), and the head's max, weights and denominator are
-  // wave reductions (NG <= 64 streams).  Then the factor to the reference, and
-  // the denominator's add.
-  float* acc_blk = a.acc + (size_t)(c % kAccCopies) * ((size_t)a.acc_rows * a.nq * (HD + 1));
-  float* acc_o = acc_blk + ((size_t)s * a.nq + g * G) * HD;
-  float* acc_l = acc_blk + (size_t)a.acc_rows * a.nq * HD + (size_t)s * a.nq + g * G;
-  {
-    const int lane = tid & 63, wave = tid >> 6;
+    const float M = stream_reduce<LG, true>(m[h]);
+    const float w = m[h] == -INFINITY ? 0.f : exp2f(m[h] - M);
+    const float L = stream_reduce<LG, false>(w * l[h]);
+    float ow[8];
 #pragma unroll
-    for (int h = wave; h < G; h += 4) {
-      const bool on = lane < NG;
-      const float mk = on ? sm_m[min(lane, NG - 1)][h] : -INFINITY;
-      const float lk = on ? sm_l[min(lane, NG - 1)][h] : 0.f;
-      const float M = wave_max(mk);
-      const float w = mk == -INFINITY ? 0.f : exp2f(mk - M);
-      const float L = wave_sum(w * lk);
-      if (on) sm_m[lane][h] = w;  // the stream's weight replaces its max
-      float rh = ref[0];  // ref[h] without a dynamic register index
-#pragma unroll
-      for (int t = 1; t < G; ++t) rh = t == h ? ref[t] : rh;
-      if (lane == 0) {
-        float d = M - rh;
-        if (!(d < 100.f)) {  // beyond f32's exponent range (or NaN scores): report, add nothing
-          if (a.err) *a.err = 2;
-          d = -INFINITY;
-        }
-        const float f = exp2f(d);
-        sm_f[h] = f;
-        unsafeAtomicAdd(acc_l + h, L * f);
+    for (int e = 0; e < 8; ++e) ow[e] = stream_reduce<LG, false>(w * o[h][e]);
+    if (gi % (64 / LG) == 0) {  // the wave's first stream writes the merged values
+      store_lane8(&sm_o[wave][h][0], HD, li, ow);
+      if (li == 0) {
+        sm_m[wave][h] = M;
+        sm_l[wave][h] = L;
       }
     }
   }
   __syncthreads();
+  // every load of the kernel has been waited for: now the stores (the new key
+  // and value into the cache, for the next steps; the other parity's clear)
+  if (has_new && gi == 0) {
+    store_lane8(a.kc + (head_base + p) * HD, HD, li, kn);
+    store_lane8(a.vc + (head_base + p) * HD, HD, li, vn);
+  }
+  clear_other();
+  float* acc_blk = a.acc + (size_t)(c % kAccCopies) * ((size_t)a.acc_rows * a.nq * (HD + 1));
+  float* acc_o = acc_blk + ((size_t)s * a.nq + g * G) * HD;
+  float* acc_l = acc_blk + (size_t)a.acc_rows * a.nq * HD + (size_t)s * a.nq + g * G;
   for (int idx = tid; idx < G * HD; idx += 256) {
     const int h = idx / HD, dd = idx % HD;
-    float O = 0.f;
+    float M = sm_m[0][h];
 #pragma unroll
-    for (int k = 0; k < NG; ++k) O += sm_o[k][h][dd] * sm_m[k][h];
-    unsafeAtomicAdd(acc_o + idx, O * sm_f[h]);
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, sm_m[w][h]);
+    float O = 0.f, L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = sm_m[w][h];
+      const float ww = mw == -INFINITY ? 0.f : exp2f(mw - M);
+      O += ww * sm_o[w][h][dd];
+      L += ww * sm_l[w][h];
+    }
+    float rh = ref[0];  // ref[h] without a dynamic register index
+#pragma unroll
+    for (int t = 1; t < G; ++t) rh = t == h ? ref[t] : rh;
+    float d = M - rh;
+    if (!(d < 100.f)) {  // beyond f32's exponent range (or NaN scores): report, add nothing
+      if (dd == 0 && a.err) *a.err = 2;
+      d = -INFINITY;
+    }
+    const float f = exp2f(d);
+    if (dd == 0) unsafeAtomicAdd(acc_l + h, L * f);
+    unsafeAtomicAdd(acc_o + idx, O * f);
   }
 }
 

@@ -69,6 +69,30 @@ QD_DEV float group_sum(float v) {
   return v;
 }
 
+// Sum (MAX: maximum) of v over the lanes of the wave that hold the same place
+// in groups of LG consecutive lanes (LG in {8, 16, 32}): lanes l, l + LG,
+// l + 2 LG, ...; every lane receives its result.  Lanes move between 16-lane
+// rows with gfx950's row swaps (v_permlane16_swap: odd rows of one operand
+// with even rows of the other; v_permlane32_swap: the wave's halves), both
+// plain VALU instructions, and within a row (LG = 8) with a DPP rotation.
+template <bool MAX>
+QD_DEV float lane_combine(float a, float b) { return MAX ? fmaxf(a, b) : a + b; }
+
+template <int LG, bool MAX>
+QD_DEV float stream_reduce(float v) {
+  static_assert(LG == 8 || LG == 16 || LG == 32, "stream_reduce: LG in {8, 16, 32}");
+  if constexpr (LG == 8) {  // lanes l and l ^ 8 of each row: rotate the row by 8
+    const float r = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false));
+    v = lane_combine<MAX>(v, r);
+  }
+  if constexpr (LG <= 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = lane_combine<MAX>(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return lane_combine<MAX>(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Full-wave sum, returned uniformly to every lane.
 QD_DEV float wave_sum(float v) {
   v = dpp_add<0xB1>(v);
