@@ -138,11 +138,15 @@ def cpu_oracle_full(cfg, threads):
     t0 = time.perf_counter()
     logits = om.forward(0, prompt)
     t_pre = time.perf_counter() - t0
+    print(f"[cpu-oracle-full] {cfg['name']}: prefill of {T} tokens {t_pre:.1f} s", file=sys.stderr, flush=True)
     tok = int(np.argmax(logits[-1]))
     t0 = time.perf_counter()
-    for _ in range(N):
+    for i in range(N):
         logits = om.forward(0, [tok])
         tok = int(np.argmax(logits[-1]))
+        if (i + 1) % 16 == 0:
+            print(f"[cpu-oracle-full] {cfg['name']}: decode step {i + 1}/{N}, {time.perf_counter() - t0:.1f} s",
+                  file=sys.stderr, flush=True)
     t_dec = time.perf_counter() - t0
     return dict(workload=cfg["name"], kind="oracle", cores=threads, prompt=T, decode_steps=N,
                 prefill_s=round(t_pre, 3), prefill_tokens_per_s=round(T / t_pre, 3),
