@@ -125,10 +125,19 @@ QD_DEV float4 x4_value(const GemvArgs& a, const XRaw<ACC>& r, int mi, bool ok) {
   return r.u[0];
 }
 
-QD_DEV float act_silu(float g) { return g / (1.0f + expf(-g)); }
+// Activations from the hardware exp2 and reciprocal (about one ulp each): a
+// precise division and expf cost ~30 instructions per output, which the
+// gate/up GEMV (bound by its vector ALU) pays once per row pair.
+//   silu(g)      = g / (1 + e^-g)
+//   gelu_tanh(x) = 0.5 x (1 + tanh u) = x / (1 + e^-2u),  u = sqrt(2/pi) (x + 0.044715 x^3)
+// Far tails: e^-g overflows to inf and the output is -0 (silu) / -0 (gelu);
+// e^-g underflows to 0 and the output is g.
+QD_DEV float act_silu(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g));
+}
 QD_DEV float act_gelu_tanh(float x) {
-  const float c = 0.7978845608028654f;  // sqrt(2/pi)
-  return 0.5f * x * (1.0f + tanhf(c * (x + 0.044715f * x * x * x)));
+  const float u = 0.7978845608028654f * (x + 0.044715f * x * x * x);  // sqrt(2/pi) (x + 0.044715 x^3)
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-2.8853900817779268f * u));
 }
 
 // Gate/up interleave used by the pair modes: weight rows [64b, 64b+32) hold gate
