@@ -584,33 +584,35 @@ __global__ __launch_bounds__(64) void sample_stage2_kernel(SampleArgs a) {
 }
 
 // The greedy token of one row from the LM head GEMV's per-wave choices
-// (part_v / part_i [nchunk], nchunk <= 8 * 1024): each thread takes up to eight
-// entries with all loads in flight at once (a single wave looping over
-// thousands of entries would pay one memory round trip per eight), then a wave
-// and a workgroup reduction in the sampler's ranking.
+// (part_v / part_i [nchunk]): each thread takes eight entries per round with
+// all loads in flight at once (a single wave looping over thousands of
+// entries would pay one memory round trip per 64), then a wave and a
+// workgroup reduction in the sampler's ranking.
 __global__ __launch_bounds__(1024) void argmax_waves_kernel(SampleArgs a) {
   sample_resolve(a);
   constexpr int kPer = 8;
   __shared__ float sv[16];
   __shared__ int si[16];
   const int tid = threadIdx.x;
-  float v[kPer];
-  int id[kPer];
+  float best = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int c0 = 0; c0 < a.nchunk; c0 += 1024 * kPer) {
+    float v[kPer];
+    int id[kPer];
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const int c = tid + 1024 * k;
-    const bool ok = c < a.nchunk;
-    v[k] = ok ? a.part_v[c] : -INFINITY;
-    id[k] = ok ? a.part_i[c] : 0x7fffffff;
-  }
-  float best = v[0];
-  int bi = id[0];
-#pragma unroll
-  for (int k = 1; k < kPer; ++k)
-    if (ranks_before(v[k], id[k], best, bi)) {
-      best = v[k];
-      bi = id[k];
+    for (int k = 0; k < kPer; ++k) {
+      const int c = c0 + tid + 1024 * k;
+      const bool ok = c < a.nchunk;
+      v[k] = ok ? a.part_v[c] : -INFINITY;
+      id[k] = ok ? a.part_i[c] : 0x7fffffff;
     }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+      if (ranks_before(v[k], id[k], best, bi)) {
+        best = v[k];
+        bi = id[k];
+      }
+  }
   argmax_pair_wave(best, bi);
   if ((tid & 63) == 0) {
     sv[tid >> 6] = best;

@@ -37,9 +37,6 @@ namespace {
 
 thread_local std::string g_err;
 
-// Most waves one GEMV launch runs (at most 1,024 workgroups of at most eight
-// waves): the size of the LM head's argmax partials.
-constexpr int kAmaxWaves = 8192;
 
 void set_err(const char* fmt, ...) {
   char buf[1024];
@@ -130,8 +127,9 @@ struct qdec_model {
                        // power of two (then capped at the page size)
   float* s_v = nullptr;
   int* s_i = nullptr;
-  float* am_v = nullptr;  // [kAmaxWaves] the LM head's per-wave greedy choices (one row)
+  float* am_v = nullptr;  // [am_n] the LM head's per-wave greedy choices (one row)
   int* am_i = nullptr;
+  int am_n = 0;           // the most waves an LM-head launch can have (set at load)
   uint32_t* cut_key = nullptr;  // [max_seqs] top-p cut per row
   int* cut_idx = nullptr;
   int nvchunk = 0;
@@ -327,7 +325,7 @@ int gemv(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, c
       a.xcstride = (long)acc.stride;
     }
     if (amax) {
-      if ((int)grid.x * NW > kAmaxWaves) throw HipError{"gemv: too many waves for the argmax partials"};
+      if ((int)grid.x * NW > m->am_n) throw HipError{"gemv: too many waves for the argmax partials"};
       a.amax_v = m->am_v;
       a.amax_i = m->am_i;
     }
@@ -494,8 +492,7 @@ void sample(qdec_model* m, hipStream_t st, const float* logits, int ld, int rows
 // (gemv with amax): one workgroup reduces the nwaves partials.  out, or the
 // step parameters' token buffer when sp is given.
 void argmax_final(qdec_model* m, hipStream_t st, int nwaves, int* out, const StepParams* sp = nullptr) {
-  static_assert(kAmaxWaves <= 8 * 1024, "argmax_waves_kernel: eight partials per thread of 1,024");
-  if (nwaves > kAmaxWaves) throw HipError{"argmax_final: too many partials"};
+  if (nwaves > m->am_n) throw HipError{"argmax_final: too many partials"};
   SampleArgs a{nullptr, 0, m->cfg.vocab, 1, 0.f, 0, 0, m->am_v, m->am_i, nwaves, out, nullptr, sp,
                nullptr, nullptr, nullptr};
   Timed tm(m, st, "argmax_final", (double)nwaves * 8, 0);
@@ -1106,8 +1103,11 @@ int load(const qdec_config* cfgp, const qdec_tensor* ts, int32_t n, int32_t max_
     m->nvchunk = (c.vocab + kSampleChunk - 1) / kSampleChunk;
     m->s_v = m->dalloc<float>((size_t)max_seqs * m->nvchunk);
     m->s_i = m->dalloc<int>((size_t)max_seqs * m->nvchunk);
-    m->am_v = m->dalloc<float>(kAmaxWaves);
-    m->am_i = m->dalloc<int>(kAmaxWaves);
+    // the LM head's waves: at most 1,024 workgroups of eight, or more when a
+    // wave would otherwise hold more than 64 outputs (gemv's grid_min)
+    m->am_n = std::max(8192, c.vocab / 64 + 64);
+    m->am_v = m->dalloc<float>(m->am_n);
+    m->am_i = m->dalloc<int>(m->am_n);
     m->cut_key = m->dalloc<uint32_t>(max_seqs);
     m->cut_idx = m->dalloc<int>(max_seqs);
     m->d_pos = m->dalloc<int>(64);

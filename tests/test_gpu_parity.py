@@ -138,6 +138,39 @@ def test_fused_greedy_choice_ties_and_nan(key, case):
             assert got == 300
 
 
+def test_lm_head_past_the_grid_cap():
+    """A 600,000-token vocabulary: the LM head GEMV needs more than its usual
+    1,024 workgroups (a wave holds at most 64 outputs), so the greedy choice
+    reduces more than 8,192 per-wave partials.  Logits within the tolerance of
+    the oracle's, tokens the greedy rule's on the GPU's logits, through prefill
+    and replayed decode."""
+    cfg = dict(SMALL["qwen3_hd128_g2"], name="wide_vocab", n_layer=1, vocab=600_000, seed=21)
+    t = synth.generate(cfg)
+    dev()
+    V = cfg["vocab"]
+    prompt = synth.prompt(cfg, 5, tag="wide")
+    om = OracleModel(cfg, t, max_ctx=16)
+    with qdec.Model(cfg, t, max_seqs=1, max_ctx=16) as m:
+        pl = torch.empty(V, dtype=torch.float32, device=dev())
+        tok = torch.empty(1, dtype=torch.int32, device=dev())
+        m.prefill(0, prompt, pl, tok)
+        torch.cuda.synchronize()
+        g = as_np(pl).copy()
+        check_row(g, om.forward(0, prompt)[0])
+        assert int(as_np(tok)[0]) == sampler.greedy(g)
+        dl = torch.empty((1, V), dtype=torch.float32, device=dev())
+        out = torch.empty(1, dtype=torch.int32, device=dev())
+        cur = int(as_np(tok)[0])
+        for step in range(3):
+            m.decode_step([cur], dl, out)
+            torch.cuda.synchronize()
+            g = as_np(dl)[0].copy()
+            check_row(g, om.forward(0, [cur])[0])
+            got = int(as_np(out)[0])
+            assert got == sampler.greedy(g)
+            cur = got
+
+
 @pytest.mark.parametrize("temperature", [1.0, 0.7])
 def test_gumbel_sampling_matches_oracle(temperature):
     rng = np.random.default_rng(6)
