@@ -382,10 +382,10 @@ struct AttnPrefillArgs {
 // ------------------------------------------------------------ prefill attention on the matrix cores
 // The online softmax of the decode kernel for T queries at once, with both
 // products on V_MFMA_F32_32X32X2_F32 (f32 operands, f32 accumulation); head_dim
-// 64 and 128.  Cache rows are indexed in 32 bits (the loader keeps every
-// layer's cache below 2^31 rows).  Workgroup = 32 queries x one query head; its four waves take the
+// 64 and 128.  Workgroup = 32 queries x one query head; its four waves take the
 // 32-key tiles of the queries' key range in turn and merge their (max, sum,
-// output) at the end.
+// output) at the end.  Query tiles are dispatched last first, so the longest
+// key ranges start first.
 //
 // Per tile the wave computes S^T = K Q^T (keys as rows, queries as columns),
 // contracting over dims in the order c(t, h) = h * HD/2 + t (lane half h,
@@ -393,19 +393,44 @@ struct AttnPrefillArgs {
 // query's row in registers.  The D layout of S^T puts query j in lanes j and
 // j + 32 and keys 8(r/4) + 4h + r%4 in register r of lane half h; taking the
 // P V contraction over keys in exactly that order, register t of P^T is the B
-// operand of step t of O^T = V^T P^T, so the probabilities never move.  The A
-// operand of that step is V[key][32 b + lane%32]: 32 consecutive floats of a
-// value row per half-wave.  Scores are in the log2 domain (q scaled by
+// operand of step t of O^T = V^T P^T, so the probabilities never move.  Row i
+// of output block b is dim NB i + b (NB = HD / 32 blocks), so the A operands a
+// lane needs from one value row, one per block, are NB consecutive floats: one
+// vector load per key.  Scores are in the log2 domain (q scaled by
 // log2(e)/sqrt(hd)); masked keys get probability 0.
+//
+// Two workgroups per CU (two waves per SIMD): the queries, scaled, sit in LDS
+// (read four dims at a time per step group) rather than in registers, so a
+// wave fits in 256 registers and one wave's loads, softmax and merges overlap
+// the other's matrix products.  A tile's values are requested together with
+// its keys, before the scores (which they do not depend on).  A 32-aligned
+// tile lies in one page of a paged cache (pages hold at least 32 positions),
+// so one table entry places all of its rows.
 template <int HD>
-__global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnPrefillArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnPrefillArgs a) {
+  static_assert(HD == 64 || HD == 128, "whole-head kernel: head_dim 64 or 128");
   constexpr int HH = HD / 2;  // contraction steps of S^T (two dims per step)
   constexpr int NB = HD / 32; // 32-dim blocks of the output
-  constexpr int MB = NB < 4 ? NB : 4;  // blocks per merge pass (48 KB of LDS)
-  __shared__ float sm_o[3][MB][16][64];
-  __shared__ float sm_ml[3][2][64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 31, lk = lane >> 5;
-  const int q0 = (int)blockIdx.x * 32, h = (int)blockIdx.y, g = h / (a.nq / a.nkv);
+  constexpr int QS = HD + 4;  // LDS row stride of the queries (bank spread for row-per-lane reads)
+  typedef float vnb __attribute__((ext_vector_type(NB)));
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  // the queries during the walk, then the waves' partial results for the merge
+  __shared__ float sm_raw[3 * NB * 16 * 64 + 3 * 2 * 64 > 32 * QS ? 3 * NB * 16 * 64 + 3 * 2 * 64 : 32 * QS];
+  float (*q_s)[QS] = reinterpret_cast<float (*)[QS]>(sm_raw);
+  float (*sm_o)[NB][16][64] = reinterpret_cast<float (*)[NB][16][64]>(sm_raw);
+  float (*sm_ml)[2][64] = reinterpret_cast<float (*)[2][64]>(sm_raw + 3 * NB * 16 * 64);
+  const int tid = threadIdx.x, lane = tid & 63, li = lane & 31, lk = lane >> 5;
+  // wave index as a uniform value, so tile addresses (and a page-table
+  // lookup) are scalar work
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Workgroup id -> (KV head, query head, query tile): consecutive ids take
+  // consecutive KV heads, so with 8 KV heads (the XCD count) every workgroup of
+  // a KV head runs on one XCD and its keys and values stay in that XCD's L2;
+  // query tiles go last first, so the longest key ranges start first.
+  const int G = a.nq / a.nkv, nqt = (int)gridDim.x / a.nq;
+  const int g = (int)blockIdx.x % a.nkv, rest = (int)blockIdx.x / a.nkv;
+  const int h = g * G + rest % G, q0 = (nqt - 1 - rest / G) * 32;
   const int tq = q0 + li;  // this lane's query (token index)
   const bool q_ok = tq < a.T;
   const int p = a.pos0 + tq;
@@ -414,19 +439,16 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnPrefillArgs 
   const int kmin = a.window > 0 ? max(0, a.pos0 + q0 - a.window + 1) : 0;
   const int kt0 = kmin & ~31;
   const int ntile = (kmax - kt0) / 32 + 1;
+  // the lane's query sees keys [k_lo, k_hi] (none past the prompt's end)
+  const int k_hi = q_ok ? p : -1, k_lo = a.window > 0 ? p - a.window + 1 : 0;
 
-  float q[HH];
-  {
-    const float4* qp = reinterpret_cast<const float4*>(a.q + (size_t)(q_ok ? tq : 0) * a.nq * HD + (size_t)h * HD +
-                                                       lk * HH);
-#pragma unroll
-    for (int e = 0; e < HH / 4; ++e) {
-      const float4 v = qp[e];
-      q[4 * e + 0] = v.x * a.scale_log2;
-      q[4 * e + 1] = v.y * a.scale_log2;
-      q[4 * e + 2] = v.z * a.scale_log2;
-      q[4 * e + 3] = v.w * a.scale_log2;
-    }
+  // the 32 queries of head h, scaled, into LDS (rows past the prompt read row 0)
+  for (int i = tid; i < 32 * HD / 4; i += 256) {
+    const int r = i / (HD / 4), c4 = i % (HD / 4);
+    const int t = q0 + r < a.T ? q0 + r : 0;
+    const float4 v = *reinterpret_cast<const float4*>(a.q + (size_t)t * a.nq * HD + (size_t)h * HD + 4 * c4);
+    *reinterpret_cast<float4*>(&q_s[r][4 * c4]) =
+        make_float4(v.x * a.scale_log2, v.y * a.scale_log2, v.z * a.scale_log2, v.w * a.scale_log2);
   }
   f32x16 o[NB];
 #pragma unroll
@@ -434,95 +456,113 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnPrefillArgs 
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[b][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
+  // Tile rows are read through a buffer descriptor that starts at the tile's
+  // first row and ends after row kmax: rows past it read as zeros (finite, and
+  // masked), and every address is a per-lane constant plus an immediate.
+  // keys: lane (li, lk) reads K[key0 + li][lk * HH ...]; values: step t of
+  // O^T = V^T P^T contracts keys 8(t/4) + 4h + t%4 (lane half h), the NB dims
+  // NB li .. NB li + NB - 1 of each
+  const int k_off = (li * HD + lk * HH) * 4;
+  const int v_off = ((4 * lk) * HD + NB * li) * 4;
+  // tiles that no query of the workgroup sees only in part skip the mask
+  const int p_first = a.pos0 + q0, p_last = a.pos0 + tlast;
+  __syncthreads();
 
   for (int it = wave; it < ntile; it += 4) {
     const int key0 = kt0 + 32 * it;
-    // rows of the tile's values for O^T = V^T P^T: step t contracts keys
-    // 8(t/4) + 4h + t%4 (lane half h).  Up to head_dim 128 the values are
-    // requested here, before the scores (which they do not depend on), so
-    // their latency overlaps the first product; at 256 that would not fit the
-    // registers and they are requested block by block below.
-    size_t vrow[16];
+    const size_t base = kv_row(a.map, a.nkv, a.ctx, a.seq, g, key0);  // row of key0 + x is base + x
+    const int bytes = (min(kmax - key0, 31) + 1) * HD * 4;
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(a.kc + base * HD), (short)0, bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(a.vc + base * HD), (short)0, bytes, 0x00020000);
+    u32x4 kb[HH / 4];
 #pragma unroll
-    for (int t = 0; t < 16; ++t)
-      vrow[t] = kv_row(a.map, a.nkv, a.ctx, a.seq, g, min(key0 + 8 * (t >> 2) + 4 * lk + (t & 3), kmax));
-    constexpr bool kEarlyV = HD <= 128;
-    float vv[kEarlyV ? NB : 1][16];
-    if constexpr (kEarlyV) {
+    for (int e = 0; e < HH / 4; ++e) kb[e] = __builtin_amdgcn_raw_buffer_load_b128(kr, k_off + 16 * e, 0, 0);
+    vnb vb[16];
 #pragma unroll
-      for (int t = 0; t < 16; ++t)
-#pragma unroll
-        for (int b = 0; b < NB; ++b) vv[b][t] = a.vc[vrow[t] * HD + 32 * b + li];
+    for (int t = 0; t < 16; ++t) {
+      const int off = v_off + (8 * (t >> 2) + (t & 3)) * HD * 4;
+      if constexpr (NB == 4) {
+        const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0);
+        vb[t] = vnb{__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z), __uint_as_float(w.w)};
+      } else {
+        const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(vr, off, 0, 0);
+        vb[t] = vnb{__uint_as_float(w.x), __uint_as_float(w.y)};
+      }
     }
-    // S^T = K Q^T: lane (li, lk) supplies K[key0 + li][lk * HH + t]
+    // S^T = K Q^T (the queries are read from LDS on every tile: an opaque zero
+    // in the address keeps the compiler from hoisting them into registers)
+    int qz;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(qz));
+    const float* qrow = &q_s[li][lk * HH + qz];
     f32x16 sacc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
-    {
-      const int kr = min(key0 + li, kmax);
-      const float4* kp = reinterpret_cast<const float4*>(a.kc + kv_row(a.map, a.nkv, a.ctx, a.seq, g, kr) * HD +
-                                                         lk * HH);
 #pragma unroll
-      for (int e = 0; e < HH / 4; ++e) {
-        const float4 kv = kp[e];
-        sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.x, q[4 * e + 0], sacc, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.y, q[4 * e + 1], sacc, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.z, q[4 * e + 2], sacc, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.w, q[4 * e + 3], sacc, 0, 0, 0);
-      }
+    for (int e = 0; e < HH / 4; ++e) {
+      const float4 qv = *reinterpret_cast<const float4*>(qrow + 4 * e);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(kb[e].x), qv.x, sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(kb[e].y), qv.y, sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(kb[e].z), qv.z, sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(kb[e].w), qv.w, sacc, 0, 0, 0);
     }
     // online softmax of query li over the tile's keys (16 here, 16 in lane ^ 32)
-    float pr[16];
+    const bool inner = key0 + 31 <= p_first && (a.window == 0 || key0 > p_last - a.window);
+    if (!inner) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 8 * (r >> 2) + 4 * lk + (r & 3);
+        sacc[r] = (key >= k_lo) & (key <= k_hi) ? sacc[r] : -INFINITY;
+      }
+    }
     float mt = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = key0 + 8 * (r >> 2) + 4 * lk + (r & 3);
-      const bool ok = q_ok && key <= p && (a.window == 0 || key > p - a.window);
-      pr[r] = ok ? sacc[r] : -INFINITY;
-      mt = fmaxf(mt, pr[r]);
-    }
+    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[r]);
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     // lazy rescale: the reference max moves only when a score exceeds it by
     // more than 8 (probabilities stay below 2^8, exact in f32 either way), so
     // the output accumulators are rescaled on few tiles, and only when some
-    // lane of the wave needs it
-    float corr = 1.f;
-    if (m_run == -INFINITY) {
-      m_run = mt;  // first scores of this query: nothing accumulated yet
-    } else if (mt > m_run + 8.f) {
-      corr = exp2f(m_run - mt);
-      m_run = mt;
-    }
-    const bool rescale = __any(corr != 1.f);
-    float ps = 0.f;
+    // lane of the wave needs it.  A query with no key seen yet keeps -inf and
+    // probabilities 0.
+    const bool first = m_run == -INFINITY;
+    const bool bump = !first && mt > m_run + 8.f;
+    const float corr = bump ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;
+    m_run = first || bump ? mt : m_run;
+    const float mref = m_run == -INFINITY ? 0.f : m_run;
+    float pr[16], ps = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      pr[r] = pr[r] == -INFINITY ? 0.f : exp2f(pr[r] - m_run);
+      pr[r] = __builtin_amdgcn_exp2f(sacc[r] - mref);  // exp2(-inf) = 0 for masked keys
       ps += pr[r];
     }
     ps += __shfl_xor(ps, 32);
     l_run = l_run * corr + ps;
-    // O^T = V^T P^T
+    // O^T += V^T P^T
+    if (__any(corr != 1.f)) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      if (rescale) {
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[b][r] *= corr;
-      }
-#pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const float v = kEarlyV ? vv[kEarlyV ? b : 0][t] : a.vc[vrow[t] * HD + 32 * b + li];
-        o[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(v, pr[t], o[b], 0, 0, 0);
-      }
     }
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) o[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(vb[t][b], pr[t], o[b], 0, 0, 0);
   }
-  // merge the four waves' partial results into wave 0 (output blocks in
-  // passes of MB, so the exchange fits in LDS at every head_dim)
+  // merge the four waves' partial results into wave 0 (the LDS held the
+  // queries until every wave's last product)
+  __syncthreads();
   if (wave > 0) {
     sm_ml[wave - 1][0][lane] = m_run;
     sm_ml[wave - 1][1][lane] = l_run;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sm_o[wave - 1][b][r][lane] = o[b][r];
   }
   __syncthreads();
+  if (wave > 0 || !q_ok) return;
   float M = m_run;
 #pragma unroll
   for (int w = 0; w < 3; ++w) M = fmaxf(M, sm_ml[w][0][lane]);
@@ -536,34 +576,18 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnPrefillArgs 
   }
   const float inv = L > 0.f ? 1.0f / L : 0.f;
   float* orow = a.out + (size_t)tq * a.nq * HD + (size_t)h * HD;
+  // register r holds MFMA row i = 8(r/4) + 4 lk + r%4 of every block: dims NB i .. NB i + NB - 1
 #pragma unroll
-  for (int b0 = 0; b0 < NB; b0 += MB) {
-    if (wave > 0) {
+  for (int r = 0; r < 16; ++r) {
+    vnb v;
 #pragma unroll
-      for (int b = 0; b < MB; ++b)
+    for (int b = 0; b < NB; ++b) {
+      float acc = o[b][r] * w0;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sm_o[wave - 1][b][r][lane] = o[b0 + b][r];
+      for (int w = 0; w < 3; ++w) acc += ww[w] * sm_o[w][b][r][lane];
+      v[b] = acc * inv;
     }
-    __syncthreads();
-    if (wave == 0 && q_ok) {
-#pragma unroll
-      for (int b = 0; b < MB; ++b) {
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          float v[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * r4 + e;
-            float acc = o[b0 + b][r] * w0;
-#pragma unroll
-            for (int w = 0; w < 3; ++w) acc += ww[w] * sm_o[w][b][r][lane];
-            v[e] = acc * inv;
-          }
-          *reinterpret_cast<float4*>(orow + 32 * (b0 + b) + 8 * r4 + 4 * lk) = make_float4(v[0], v[1], v[2], v[3]);
-        }
-      }
-    }
-    __syncthreads();
+    *reinterpret_cast<vnb*>(orow + NB * (8 * (r >> 2) + 4 * lk + (r & 3))) = v;
   }
 }
 

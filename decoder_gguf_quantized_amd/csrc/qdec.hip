@@ -445,10 +445,10 @@ void attention_prefill(qdec_model* m, hipStream_t st, int l, int seq, int T, int
   // whole-head per wave, 256 split over the four waves.  They index cache rows
   // in 32 bits: the loader and qdec_kv_paged keep a layer below 2^31 rows.
   if (m->kv_layer / hd >= (size_t)INT32_MAX) throw HipError{"prefill attention: cache layer of 2^31 rows or more"};
-  dim3 grid((T + 31) / 32, c.n_head);
-  if (hd == 64) qlaunch(attn_prefill_mfma_kernel<64>, grid, 256, 0, st, a);
-  else if (hd == 128) qlaunch(attn_prefill_mfma_kernel<128>, grid, 256, 0, st, a);
-  else qlaunch(attn_prefill_dsplit_kernel<256>, grid, 256, 0, st, a);
+  const int nqt = (T + 31) / 32;
+  if (hd == 64) qlaunch(attn_prefill_mfma_kernel<64>, dim3(nqt * c.n_head), 256, 0, st, a);
+  else if (hd == 128) qlaunch(attn_prefill_mfma_kernel<128>, dim3(nqt * c.n_head), 256, 0, st, a);
+  else qlaunch(attn_prefill_dsplit_kernel<256>, dim3(nqt, c.n_head), 256, 0, st, a);
 }
 
 void rope_kv(qdec_model* m, hipStream_t st, int l, int n, int seq0, int pos0, const int* dpos) {
