@@ -20,6 +20,22 @@
 
 namespace qd {
 
+// Q4_0 / Q8_0 decode from unsigned bytes: with u = q + c (c = 8 for a nibble,
+// 128 for an int8 byte with its sign bit flipped), d q = fma(d, u, -c d).  Both
+// products are exact in f32 (an fp16 scale times an integer below 2^8), and so
+// is their difference, so the fma rounds nothing and the value equals d * q
+// (an exact zero comes out +0).  Byte E of w converts in one instruction
+// (V_CVT_F32_UBYTE0..3, written out: the compiler would otherwise extract a
+// masked nibble with a bit-field instruction first).
+template <int E>
+QD_DEV float dq_byte(float d, float cd, uint32_t w) {
+  float f;
+  if constexpr (E == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(f) : "v"(w));
+  else if constexpr (E == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(f) : "v"(w));
+  else if constexpr (E == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(f) : "v"(w));
+  else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(f) : "v"(w));
+  return fmaf(d, f, cd);
+}
 
 struct GemmArgs {
   const uint8_t* qs;    // weights, same layout as GemvArgs
@@ -57,7 +73,9 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
 
   // staging registers
   float4 xa[2];
-  uint4 wq;        // int8 layouts: 16 int8; F32 uses wf[4]; nibble layouts use the low 8 bytes
+  // rows past the matrix never load: their quant bytes and scale stay zero,
+  // which decodes to zeros without a select (Q4_0, Q8_0)
+  uint4 wq = make_uint4(0, 0, 0, 0);  // int8 layouts: 16 int8; F32 uses wf[4]; nibble layouts use the low 8 bytes
   float4 wf[4];
   float wd = 0.f, wmin = 0.f;  // block scale (Q6_K: of this thread's 16 values); Q4_K min
   uint32_t wks = 0, wkd = 0;   // K-quants: raw scale words, decoded when stored
@@ -115,7 +133,34 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
     } else if constexpr (QT == kQ6_K) {
       wd = q6k_scale(wks, wkd);
     }
-    if constexpr (int8_layout(QT)) {
+    if constexpr (QT == kQ8_0) {
+      const uint32_t w4[4] = {wq.x, wq.y, wq.z, wq.w};
+      const float cd = -128.f * wd;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t u = w4[j] ^ 0x80808080u;
+        Bs[16 * bhalf + 4 * j + 0][brow ^ sb(16 * bhalf + 4 * j + 0)] = dq_byte<0>(wd, cd, u);
+        Bs[16 * bhalf + 4 * j + 1][brow ^ sb(16 * bhalf + 4 * j + 1)] = dq_byte<1>(wd, cd, u);
+        Bs[16 * bhalf + 4 * j + 2][brow ^ sb(16 * bhalf + 4 * j + 2)] = dq_byte<2>(wd, cd, u);
+        Bs[16 * bhalf + 4 * j + 3][brow ^ sb(16 * bhalf + 4 * j + 3)] = dq_byte<3>(wd, cd, u);
+      }
+    } else if constexpr (QT == kQ4_0) {
+      const uint32_t w2[2] = {wq.x, wq.y};
+      const float cd = -8.f * wd;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t lo = w2[j] & 0x0f0f0f0fu, hi = (w2[j] >> 4) & 0x0f0f0f0fu;
+        const int i = 4 * j;
+        Bs[8 * bhalf + i + 0][brow ^ sb(8 * bhalf + i + 0)] = dq_byte<0>(wd, cd, lo);
+        Bs[8 * bhalf + i + 1][brow ^ sb(8 * bhalf + i + 1)] = dq_byte<1>(wd, cd, lo);
+        Bs[8 * bhalf + i + 2][brow ^ sb(8 * bhalf + i + 2)] = dq_byte<2>(wd, cd, lo);
+        Bs[8 * bhalf + i + 3][brow ^ sb(8 * bhalf + i + 3)] = dq_byte<3>(wd, cd, lo);
+        Bs[16 + 8 * bhalf + i + 0][brow ^ sb(16 + 8 * bhalf + i + 0)] = dq_byte<0>(wd, cd, hi);
+        Bs[16 + 8 * bhalf + i + 1][brow ^ sb(16 + 8 * bhalf + i + 1)] = dq_byte<1>(wd, cd, hi);
+        Bs[16 + 8 * bhalf + i + 2][brow ^ sb(16 + 8 * bhalf + i + 2)] = dq_byte<2>(wd, cd, hi);
+        Bs[16 + 8 * bhalf + i + 3][brow ^ sb(16 + 8 * bhalf + i + 3)] = dq_byte<3>(wd, cd, hi);
+      }
+    } else if constexpr (int8_layout(QT)) {
       uint32_t w4[4] = {wq.x, wq.y, wq.z, wq.w};
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -127,14 +172,9 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         uint32_t byte = (w2[i >> 2] >> (8 * (i & 3))) & 0xffu;
-        float lo, hi;
-        if constexpr (QT == kQ4_0) {
-          lo = wd * (float)((int)(byte & 15u) - 8);
-          hi = wd * (float)((int)(byte >> 4) - 8);
-        } else {  // scale * n - min, rounded once
-          lo = fmaf(wd, (float)(byte & 15u), -wmin);
-          hi = fmaf(wd, (float)(byte >> 4), -wmin);
-        }
+        // Q4_K: scale * n - min, rounded once
+        float lo = fmaf(wd, (float)(byte & 15u), -wmin);
+        float hi = fmaf(wd, (float)(byte >> 4), -wmin);
         lo = brow_ok ? lo : 0.f;
         hi = brow_ok ? hi : 0.f;
         Bs[8 * bhalf + i][brow ^ sb(8 * bhalf + i)] = lo;
@@ -296,7 +336,18 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_ksplit_kernel(GemmArgs a) {
       wd = q6k_scale((uint32_t)(int32_t)(int8_t)(wks & 0xffu), wkd);
       wd2 = q6k_scale((uint32_t)(int32_t)(int8_t)(wks >> 8), wkd);
     }
-    if constexpr (int8_layout(QT)) {
+    if constexpr (QT == kQ8_0) {
+      const uint32_t w8[8] = {wq[0].x, wq[0].y, wq[0].z, wq[0].w, wq[1].x, wq[1].y, wq[1].z, wq[1].w};
+      const float cd = -128.f * wd;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t u = w8[j] ^ 0x80808080u;
+        Bs[kk + 4 * j + 0][bc] = dq_byte<0>(wd, cd, u);
+        Bs[kk + 4 * j + 1][bc] = dq_byte<1>(wd, cd, u);
+        Bs[kk + 4 * j + 2][bc] = dq_byte<2>(wd, cd, u);
+        Bs[kk + 4 * j + 3][bc] = dq_byte<3>(wd, cd, u);
+      }
+    } else if constexpr (int8_layout(QT)) {
       const uint32_t w8[8] = {wq[0].x, wq[0].y, wq[0].z, wq[0].w, wq[1].x, wq[1].y, wq[1].z, wq[1].w};
 #pragma unroll
       for (int i = 0; i < 32; ++i)
@@ -311,11 +362,18 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_ksplit_kernel(GemmArgs a) {
       }
     } else if constexpr (QT == kQ4_0) {
       const uint32_t w4[4] = {wq[0].x, wq[0].y, wq[0].z, wq[0].w};
+      const float cd = -8.f * wd;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint32_t byte = (w4[i >> 2] >> (8 * (i & 3))) & 0xffu;
-        Bs[kk + i][bc] = wd * (float)((int)(byte & 15u) - 8);
-        Bs[kk + 16 + i][bc] = wd * (float)((int)(byte >> 4) - 8);
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = w4[j] & 0x0f0f0f0fu, hi = (w4[j] >> 4) & 0x0f0f0f0fu;
+        Bs[kk + 4 * j + 0][bc] = dq_byte<0>(wd, cd, lo);
+        Bs[kk + 4 * j + 1][bc] = dq_byte<1>(wd, cd, lo);
+        Bs[kk + 4 * j + 2][bc] = dq_byte<2>(wd, cd, lo);
+        Bs[kk + 4 * j + 3][bc] = dq_byte<3>(wd, cd, lo);
+        Bs[kk + 16 + 4 * j + 0][bc] = dq_byte<0>(wd, cd, hi);
+        Bs[kk + 16 + 4 * j + 1][bc] = dq_byte<1>(wd, cd, hi);
+        Bs[kk + 16 + 4 * j + 2][bc] = dq_byte<2>(wd, cd, hi);
+        Bs[kk + 16 + 4 * j + 3][bc] = dq_byte<3>(wd, cd, hi);
       }
     } else {
 #pragma unroll
