@@ -99,6 +99,8 @@ def lib():
                 "qdec_decode_batch": (ctypes.c_int, [P, P, P, I32, P, P, F, F, U64, U64, U32, P]),
                 "qdec_kv_paged": (ctypes.c_int, [P, I32, I32, P]),
                 "qdec_kv_pages": (ctypes.c_int, [P, ctypes.POINTER(I32), ctypes.POINTER(I32), ctypes.POINTER(I32)]),
+                "qdec_kv_ring": (ctypes.c_int, [P, I32, P]),
+                "qdec_kv_ring_positions": (ctypes.c_int, [P, I32, ctypes.POINTER(I32)]),
                 "qdec_decode_chunks": (ctypes.c_int, [P, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
                 "qdec_debug_inject_fault": (ctypes.c_int, [P, I32]),
                 "qdec_sample_noalloc": (ctypes.c_int, [P, I32, I32, F, F, U64, U64, P, P]),
@@ -392,6 +394,17 @@ class Model:
         ``page_size`` positions shared by all sequences (every sequence empty)."""
         self._check(lib().qdec_kv_paged(self._handle(), _int("page_size", page_size), _int("n_pages", n_pages),
                                         _stream()))
+
+    def kv_ring(self, enable):
+        """Sliding-window layers keep a ring of their last positions (True, the
+        state after load) or every position (False); every sequence empty."""
+        self._check(lib().qdec_kv_ring(self._handle(), 1 if enable else 0, _stream()))
+
+    def kv_ring_positions(self, layer):
+        """Positions of ``layer``'s ring, 0 when it keeps max_ctx positions."""
+        out = ctypes.c_int32()
+        self._check(lib().qdec_kv_ring_positions(self._handle(), _int("layer", layer), ctypes.byref(out)))
+        return out.value
 
     def kv_pages(self):
         """(page_size, n_pages, n_free); page_size 0 = contiguous cache."""

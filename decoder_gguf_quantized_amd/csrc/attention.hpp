@@ -155,12 +155,17 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
   const float* row = a.qkv + (size_t)s * a.ldqkv;
   const int sq = a.seq ? a.seq[s] : s;
   const int cb = c * a.chunk;
-  // cache row of position j is head_base + j for every j of this chunk
+  // cache row of position j is head_base + (j & pmask) for every j of this
+  // chunk (pmask: a window layer's ring, else all ones)
   size_t head_base;
+  int pmask = -1;
   if constexpr (PAGED) {
     const int pi = cb >> a.map.log2p;
     const int pg = a.map.table[sq * a.map.tw + pi];
     head_base = (((size_t)pg * a.nkv + g) << a.map.log2p) - ((size_t)pi << a.map.log2p);
+  } else if (a.map.ring) {
+    head_base = ((size_t)sq * a.nkv + g) << a.map.ring;
+    pmask = (1 << a.map.ring) - 1;
   } else {
     head_base = ((size_t)sq * a.nkv + g) * a.ctx;
   }
@@ -197,8 +202,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int jj = min(j0 + t * NG, a.ctx - 1);
-      load_lane8_nt(a.kc + (head_base + jj) * HD, HD, li, k[t]);
-      load_lane8_nt(a.vc + (head_base + jj) * HD, HD, li, v[t]);
+      load_lane8_nt(a.kc + (head_base + (jj & pmask)) * HD, HD, li, k[t]);
+      load_lane8_nt(a.vc + (head_base + (jj & pmask)) * HD, HD, li, v[t]);
     }
   };
   float ka[2][8], va[2][8], kb[2][8], vb[2][8];
@@ -334,8 +339,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
   // every load of the kernel has been waited for: now the stores (the new key
   // and value into the cache, for the next steps; the other parity's clear)
   if (has_new && gi == 0) {
-    store_lane8(a.kc + (head_base + p) * HD, HD, li, kn);
-    store_lane8(a.vc + (head_base + p) * HD, HD, li, vn);
+    store_lane8(a.kc + (head_base + (p & pmask)) * HD, HD, li, kn);
+    store_lane8(a.vc + (head_base + (p & pmask)) * HD, HD, li, vn);
   }
   clear_other();
   float* acc_blk = a.acc + (size_t)(c % kAccCopies) * ((size_t)a.acc_rows * a.nq * (HD + 1));

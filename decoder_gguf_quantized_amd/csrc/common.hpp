@@ -32,15 +32,20 @@ constexpr int kQ6_K = 14;
 // sequence s's position j in page table[s * tw + j / P] (pages are handed out
 // by the host; entries past a sequence's length hold any valid page).
 struct KvMap {
-  const int* table;
+  const int* table;     // paged: [seq][tw] page of each block of 2^log2p positions, else null
   int tw, log2p;
+  int ring;             // contiguous sliding-window layer: log2 of its ring of positions
+                        // (position j in slot j mod 2^ring), 0 = every position kept
 };
 
 // Row index (in head_dim units) of position j of KV head g of sequence s.
 QD_DEV size_t kv_row(const KvMap& mp, int nkv, int ctx, int s, int g, int j) {
-  if (!mp.table) return ((size_t)s * nkv + g) * ctx + j;
-  const int pg = mp.table[s * mp.tw + (j >> mp.log2p)];
-  return (((size_t)pg * nkv + g) << mp.log2p) + (j & ((1 << mp.log2p) - 1));
+  if (mp.table) {
+    const int pg = mp.table[s * mp.tw + (j >> mp.log2p)];
+    return (((size_t)pg * nkv + g) << mp.log2p) + (j & ((1 << mp.log2p) - 1));
+  }
+  if (mp.ring) return (((size_t)s * nkv + g) << mp.ring) + (j & ((1 << mp.ring) - 1));
+  return ((size_t)s * nkv + g) * ctx + j;
 }
 
 // Accumulator blocks per layer parity of decode attention's merge (chunk c adds

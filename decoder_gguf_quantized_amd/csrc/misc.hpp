@@ -716,7 +716,8 @@ __global__ __launch_bounds__(64) void table_set_kernel(TableSet t) {
 }
 
 // Copy preset K and V rows ([nkv][n][hd] each) of one (sequence, layer) into
-// the cache at positions 0..n-1.  Grid (n, nkv, 2: K / V), hd / 4 threads.
+// the cache at positions j0..n-1 (j0 > 0 for a ring that keeps only the last
+// positions).  Grid (n - j0, nkv, 2: K / V), hd / 4 threads.
 struct KvScatter {
   const float* src_k;
   const float* src_v;
@@ -724,10 +725,11 @@ struct KvScatter {
   float* vc;
   int n, nkv, ctx, hd, seq;
   KvMap map;
+  int j0;
 };
 
 __global__ __launch_bounds__(64) void kv_scatter_kernel(KvScatter a) {
-  const int j = blockIdx.x, g = blockIdx.y, which = blockIdx.z, e = threadIdx.x;
+  const int j = a.j0 + (int)blockIdx.x, g = blockIdx.y, which = blockIdx.z, e = threadIdx.x;
   const float4* src = reinterpret_cast<const float4*>((which ? a.src_v : a.src_k) + ((size_t)g * a.n + j) * a.hd);
   float4* dst = reinterpret_cast<float4*>((which ? a.vc : a.kc) + kv_row(a.map, a.nkv, a.ctx, a.seq, g, j) * a.hd);
   if (e < a.hd / 4) dst[e] = src[e];

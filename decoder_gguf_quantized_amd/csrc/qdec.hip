@@ -114,7 +114,10 @@ struct qdec_model {
   int prefill_prec = QDEC_PREFILL_F32;  // operand precision of the prefill GEMMs
   float* kc = nullptr;
   float* vc = nullptr;
-  size_t kv_layer = 0;  // floats per layer of one cache
+  size_t kv_layer = 0;  // floats of the largest layer of one cache
+  std::vector<size_t> kv_off;  // float offset of each layer in kc / vc
+  std::vector<int> kv_ring;    // a contiguous window layer's ring: log2 of its positions, 0 = none
+  bool ring_on = true;         // window layers keep a ring (qdec_kv_ring)
   int ws_T = 0;
   float *x = nullptr, *h = nullptr, *qkv = nullptr, *q = nullptr, *a = nullptr, *m = nullptr, *y = nullptr;
   float* x2 = nullptr;  // second residual buffer (decode with sandwich norms)
@@ -160,7 +163,15 @@ struct qdec_model {
   hipStream_t last_stream = nullptr;
 
   const Mat& lm() const { return tied ? embd : out_w; }
-  KvMap map() const { return KvMap{page_size ? d_table : nullptr, table_w, log2p}; }
+  KvMap map() const { return KvMap{page_size ? d_table : nullptr, table_w, log2p, 0}; }
+  // layer l's caches and row map
+  float* lkc(int l) const { return kc + kv_off[l]; }
+  float* lvc(int l) const { return vc + kv_off[l]; }
+  KvMap lmap(int l) const {
+    KvMap mp = map();
+    mp.ring = kv_ring[l];
+    return mp;
+  }
 
   template <typename T>
   T* dalloc(size_t count) {
@@ -400,18 +411,56 @@ void attn_decode_hd(int G, dim3 grid, hipStream_t st, const AttnDecodeArgs& a) {
 
 int layer_window(const qdec_model* m, int l) { return m->layers[l].global ? 0 : m->cfg.window; }
 
+// Ring of a sliding-window layer in the contiguous cache: R = the power of two
+// >= window + ws_T - 1 (ws_T: the rows of one prefill pass), at least 64, used
+// when it at most halves the layer (R <= max_ctx / 2).  A prefill pass appends
+// ws_T positions at most, and its queries need the window - 1 positions before
+// them: all of them fit in the ring, so the pass appends and attends as with
+// the full cache.
+int ring_log2(const qdec_model* m, int l) {
+  const int w = layer_window(m, l);
+  if (!m->ring_on || m->page_size || w <= 0) return 0;
+  int lg = 6;
+  while ((int64_t)1 << lg < (int64_t)w + m->ws_T - 1) ++lg;
+  return ((int64_t)2 << lg) <= m->max_ctx ? lg : 0;
+}
+
+// Lay out and clear the contiguous caches: each layer [max_seqs][nkv][positions][hd]
+// with max_ctx positions, or its ring.
+void layout_contiguous(qdec_model* m, hipStream_t st) {
+  const qdec_config& c = m->cfg;
+  m->kv_off.assign(c.n_layer, 0);
+  m->kv_ring.assign(c.n_layer, 0);
+  size_t total = 0;
+  m->kv_layer = 0;
+  for (int l = 0; l < c.n_layer; ++l) {
+    m->kv_ring[l] = ring_log2(m, l);
+    const size_t pos = m->kv_ring[l] ? (size_t)1 << m->kv_ring[l] : (size_t)m->max_ctx;
+    const size_t layer = (size_t)m->max_seqs * c.n_head_kv * pos * c.head_dim;
+    m->kv_off[l] = total;
+    total += layer;
+    m->kv_layer = std::max(m->kv_layer, layer);
+  }
+  m->kc = m->dalloc<float>(total);
+  m->vc = m->dalloc<float>(total);
+  // rows past a sequence's length are read (and masked) by decode attention:
+  // start from finite values
+  hipck(hipMemsetAsync(m->kc, 0, total * 4, st), "memset");
+  hipck(hipMemsetAsync(m->vc, 0, total * 4, st), "memset");
+}
+
 // slotted: row b serves sequence d_seq[b] (continuous batching), else b.
 void attention_decode(qdec_model* m, hipStream_t st, int l, int B, bool slotted) {
   const qdec_config& c = m->cfg;
   const Layer& L = m->layers[l];
   const int hd = c.head_dim, G = c.n_head / c.n_head_kv;
   const float scale_log2 = (float)(1.0 / std::sqrt((double)hd) * 1.4426950408889634);
-  AttnDecodeArgs a{m->qkv, m->nqkv, m->kc + l * m->kv_layer, m->vc + l * m->kv_layer, m->max_ctx, m->d_pos,
+  AttnDecodeArgs a{m->qkv, m->nqkv, m->lkc(l), m->lvc(l), m->max_ctx, m->d_pos,
                    c.n_head, c.n_head_kv, layer_window(m, l), m->chunk, m->nchunk, L.q_norm, L.k_norm, c.rms_eps,
                    m->rope_cur + (L.global ? 0 : (size_t)m->max_seqs * (hd / 2)), scale_log2,
                    m->acc + (size_t)(l % 2) * kAccCopies * m->acc_blk,
                    m->acc + (size_t)((l + 1) % 2) * kAccCopies * m->acc_blk, m->max_seqs, m->err_dev,
-                   slotted ? m->d_seq : nullptr, m->map()};
+                   slotted ? m->d_seq : nullptr, m->lmap(l)};
   double kvbytes = 0;
   for (int s = 0; s < B; ++s) {
     int p = m->kvlen[(size_t)s < m->row_seq.size() ? m->row_seq[s] : s];
@@ -431,9 +480,8 @@ void attention_decode(qdec_model* m, hipStream_t st, int l, int B, bool slotted)
 void attention_prefill(qdec_model* m, hipStream_t st, int l, int seq, int T, int pos0) {
   const qdec_config& c = m->cfg;
   const int hd = c.head_dim;
-  AttnPrefillArgs a{m->q, m->kc + l * m->kv_layer, m->vc + l * m->kv_layer, m->max_ctx, T, pos0,
-                    c.n_head, c.n_head_kv, layer_window(m, l),
-                    (float)(1.0 / std::sqrt((double)hd) * 1.4426950408889634), m->a, seq, m->map()};
+  AttnPrefillArgs a{m->q, m->lkc(l), m->lvc(l), m->max_ctx, T, pos0, c.n_head, c.n_head_kv, layer_window(m, l),
+                    (float)(1.0 / std::sqrt((double)hd) * 1.4426950408889634), m->a, seq, m->lmap(l)};
   double pairs = 0;
   for (int t = 0; t < T; ++t) {
     int p = pos0 + t, lo = a.window > 0 ? std::max(0, p - a.window + 1) : 0;
@@ -454,9 +502,9 @@ void attention_prefill(qdec_model* m, hipStream_t st, int l, int seq, int T, int
 void rope_kv(qdec_model* m, hipStream_t st, int l, int n, int seq0, int pos0, const int* dpos) {
   const qdec_config& c = m->cfg;
   const Layer& L = m->layers[l];
-  RopeArgs a{m->qkv, m->nqkv, m->q, m->kc + l * m->kv_layer, m->vc + l * m->kv_layer, m->max_ctx, c.n_head,
-             c.n_head_kv, c.head_dim, L.q_norm, L.k_norm, c.rms_eps, L.global ? m->rope_g : m->rope_l,
-             seq0, pos0, dpos, L.qkv_bias, m->map()};
+  RopeArgs a{m->qkv, m->nqkv, m->q, m->lkc(l), m->lvc(l), m->max_ctx, c.n_head, c.n_head_kv, c.head_dim,
+             L.q_norm, L.k_norm, c.rms_eps, L.global ? m->rope_g : m->rope_l, seq0, pos0, dpos, L.qkv_bias,
+             m->lmap(l)};
   Timed tm(m, st, "rope_kv", (double)n * m->nqkv * 8, 0);
   qlaunch(rope_kv_kernel, dim3(n, (c.n_head + 2 * c.n_head_kv + 3) / 4), 256, 0, st, a);
 }
@@ -546,6 +594,9 @@ void blocks(qdec_model* m, hipStream_t st, int n, int seq, int pos0, const int* 
     if (dec) {
       attention_decode(m, st, l, n, slotted);  // QK-norm, RoPE and the KV append run inside
     } else {
+      // a ring holds the window plus a whole pass (ring_log2)
+      if (m->kv_ring[l] && n > (1 << m->kv_ring[l]) - layer_window(m, l) + 1)
+        throw HipError{"prefill pass longer than the window layer's ring"};
       rope_kv(m, st, l, n, seq, pos0, nullptr);
       attention_prefill(m, st, l, seq, n, pos0);
     }
@@ -1056,16 +1107,11 @@ int load(const qdec_config* cfgp, const qdec_tensor* ts, int32_t n, int32_t max_
       m->rope_l = c.window > 0 && c.rope_theta_local != c.rope_theta ? table(c.rope_theta_local) : m->rope_g;
       m->rope_cur = m->dalloc<float2>((size_t)2 * max_seqs * half);
     }
-    // KV cache [L][B][nkv][ctx][hd] f32
-    m->kv_layer = (size_t)max_seqs * c.n_head_kv * max_ctx * c.head_dim;
-    m->kc = m->dalloc<float>(m->kv_layer * c.n_layer);
-    m->vc = m->dalloc<float>(m->kv_layer * c.n_layer);
-    // rows past a sequence's length are read (and masked) by decode attention:
-    // start from finite values
-    hipck(hipMemsetAsync(m->kc, 0, m->kv_layer * c.n_layer * 4, st), "memset");
-    hipck(hipMemsetAsync(m->vc, 0, m->kv_layer * c.n_layer * 4, st), "memset");
-    // workspace
+    // workspace rows (one prefill pass; the rings are sized by it)
     m->ws_T = std::max(std::min(max_ctx, 4096), max_seqs);
+    // KV cache f32, per layer [B][nkv][positions][hd]
+    layout_contiguous(m, st);
+    // workspace
     const size_t T = m->ws_T;
     m->x = m->dalloc<float>(T * H);
     m->x2 = m->dalloc<float>(T * H);
@@ -1466,6 +1512,15 @@ int qdec_kv_truncate(qdec_model* m, int32_t seq, int32_t n) {
   if (int rc = check_usable(m)) return rc;
   if (seq < 0 || seq >= m->max_seqs) { set_err("seq %d outside [0, %d)", seq, m->max_seqs); return QDEC_REFUSED; }
   if (n < 0 || n > m->kvlen[seq]) { set_err("n %d outside [0, kv_len %d]", n, m->kvlen[seq]); return QDEC_REFUSED; }
+  // a ring has overwritten the slots of positions more than R - window behind
+  // the length: the window of position n is still whole only this close
+  for (int l = 0; l < m->cfg.n_layer; ++l)
+    if (m->kv_ring[l] && m->kvlen[seq] - n > (1 << m->kv_ring[l]) - layer_window(m, l)) {
+      set_err("seq %d: truncating %d positions exceeds the window layers' ring of %d positions (window %d); "
+              "turn the ring off (qdec_kv_ring) to truncate further", seq, m->kvlen[seq] - n, 1 << m->kv_ring[l],
+              layer_window(m, l));
+      return QDEC_REFUSED;
+    }
   m->kvlen[seq] = n;
   shrink_pages(m, seq, n);
   return QDEC_OK;
@@ -1491,10 +1546,12 @@ int qdec_kv_write(qdec_model* m, int32_t seq, int32_t layer, const float* d_k, c
     launch_table_sets(m, st, ps);
     shrink_pages(m, seq, n_pos);
     if (n_pos) {
-      KvScatter a{d_k, d_v, m->kc + layer * m->kv_layer, m->vc + layer * m->kv_layer, n_pos, c.n_head_kv, m->max_ctx,
-                  c.head_dim, seq, m->map()};
-      Timed tm(m, st, "kv_scatter", (double)n_pos * c.n_head_kv * c.head_dim * 16, 0);
-      qlaunch(kv_scatter_kernel, dim3(n_pos, c.n_head_kv, 2), 64, 0, st, a);
+      // a ring keeps the last 2^ring positions (earlier ones would share their slots)
+      const int j0 = m->kv_ring[layer] ? std::max(0, n_pos - (1 << m->kv_ring[layer])) : 0;
+      KvScatter a{d_k, d_v, m->lkc(layer), m->lvc(layer), n_pos, c.n_head_kv, m->max_ctx, c.head_dim, seq,
+                  m->lmap(layer), j0};
+      Timed tm(m, st, "kv_scatter", (double)(n_pos - j0) * c.n_head_kv * c.head_dim * 16, 0);
+      qlaunch(kv_scatter_kernel, dim3(n_pos - j0, c.n_head_kv, 2), 64, 0, st, a);
     }
     m->kvlen[seq] = n_pos;
   } catch (const HipError& e) {
@@ -1562,6 +1619,9 @@ int qdec_kv_paged(qdec_model* m, int32_t page_size, int32_t n_pages, void* strea
     m->chunk = chunk;
     m->nchunk = nchunk;
     m->kv_layer = layer;
+    m->kv_off.assign(c.n_layer, 0);
+    for (int l = 0; l < c.n_layer; ++l) m->kv_off[l] = (size_t)l * layer;
+    m->kv_ring.assign(c.n_layer, 0);  // pages hold every position
     m->page_size = page_size;
     m->log2p = 0;
     while ((1 << m->log2p) < page_size) ++m->log2p;
@@ -1582,6 +1642,44 @@ int qdec_kv_pages(const qdec_model* m, int32_t* page_size, int32_t* n_pages, int
   *page_size = m->page_size;
   *n_pages = m->n_pages;
   *n_free = (int32_t)m->free_pages.size();
+  return QDEC_OK;
+}
+
+int qdec_kv_ring(qdec_model* m, int32_t enable, void* stream) {
+  g_err.clear();
+  if (int rc = check_usable(m)) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  if (enable != 0 && enable != 1) { set_err("enable must be 0 or 1"); return QDEC_REFUSED; }
+  if (m->page_size) { set_err("the cache is paged: its pages hold every position"); return QDEC_REFUSED; }
+  for (int s = 0; s < m->max_seqs; ++s)
+    if (m->kvlen[s]) {
+      set_err("the KV cache is in use (seq %d holds %d positions): reset it first", s, m->kvlen[s]);
+      return QDEC_REFUSED;
+    }
+  if ((enable == 1) == m->ring_on) return QDEC_OK;
+  try {
+    m->last_stream = st;
+    hipck(hipStreamSynchronize(st), "sync");  // nothing reads the old cache any more
+    for (auto& g : m->graphs)  // captured with the old cache
+      if (g.second) (void)hipGraphExecDestroy(g.second);
+    m->graphs.clear();
+    m->dfree(m->kc);
+    m->dfree(m->vc);
+    m->kc = m->vc = nullptr;
+    m->ring_on = enable == 1;
+    layout_contiguous(m, st);
+    hipck(hipStreamSynchronize(st), "sync");
+  } catch (const HipError& e) {
+    return fail_internal(m, st, e.msg);
+  }
+  return QDEC_OK;
+}
+
+int qdec_kv_ring_positions(const qdec_model* m, int32_t layer, int32_t* out) {
+  g_err.clear();
+  if (!m || !out) { set_err("model and out must not be NULL"); return QDEC_REFUSED; }
+  if (layer < 0 || layer >= m->cfg.n_layer) { set_err("layer %d outside [0, %d)", layer, m->cfg.n_layer); return QDEC_REFUSED; }
+  *out = m->kv_ring[layer] ? 1 << m->kv_ring[layer] : 0;
   return QDEC_OK;
 }
 

@@ -232,6 +232,23 @@ int qdec_kv_paged(qdec_model* m, int32_t page_size, int32_t n_pages, void* strea
 /* The cache's page size (0 = contiguous), pool size and free pages. */
 int qdec_kv_pages(const qdec_model* m, int32_t* page_size, int32_t* n_pages, int32_t* n_free);
 
+/* Ring-buffer cache for sliding-window layers ([P], the same roadmap row: a
+ * paged or ring-buffer cache).  A window layer attends to its last `window`
+ * positions only, so in the contiguous cache it keeps a ring of R positions,
+ * position j in slot j mod R: R is the power of two >= window + P - 1 (P: the
+ * positions of one prefill pass, min(max_ctx, 4096), or max_seqs if larger), at
+ * least 64, and the ring is used when R <= max_ctx / 2 (enable = 1, the state
+ * after load); enable = 0 gives every layer max_ctx positions.  Results are
+ * the same either way.  With a ring, qdec_kv_write keeps the last R of the
+ * preset positions and qdec_kv_truncate may drop at most R - window positions.
+ * Refused (status 1): enable not 0 or 1, a paged cache (pages hold every
+ * position), a sequence holding positions.  Synchronizes stream. */
+int qdec_kv_ring(qdec_model* m, int32_t enable, void* stream);
+
+/* Positions of layer's ring (0: the layer keeps max_ctx positions, or the cache
+ * is paged), written to *out.  Host-side only. */
+int qdec_kv_ring_positions(const qdec_model* m, int32_t layer, int32_t* out);
+
 /* Forget the cached positions of one sequence (seq = -1: all), so that its next
  * prefill starts at position 0 ([W] Step 9: each generation starts from an empty
  * cache; a new prompt is a new sequence).  Host-side only, nothing is enqueued;
@@ -240,12 +257,14 @@ int qdec_kv_pages(const qdec_model* m, int32_t* page_size, int32_t* n_pages, int
 int qdec_kv_reset(qdec_model* m, int32_t seq);
 
 /* Roll sequence seq back to its first n positions (0 <= n <= kv_len(seq)), for
- * instance to rerun decode steps over a preset cache.  Host-side only. */
+ * instance to rerun decode steps over a preset cache.  With window-layer rings
+ * (qdec_kv_ring) at most R - window positions may go (status 1 otherwise).
+ * Host-side only. */
 int qdec_kv_truncate(qdec_model* m, int32_t seq, int32_t n);
 
 /* Install preset post-RoPE K and V, each f32 [n_head_kv][n_pos][head_dim]
  * (device), for one (sequence, layer) at positions 0..n_pos-1, and set
- * kv_len(seq) = n_pos. */
+ * kv_len(seq) = n_pos (a window layer's ring keeps the last R of them). */
 int qdec_kv_write(qdec_model* m, int32_t seq, int32_t layer, const float* d_k, const float* d_v,
                   int32_t n_pos, void* stream);
 

@@ -152,6 +152,17 @@ int qdec_kv_paged(qdec_model* m, int32_t page_size, int32_t n_pages, void* strea
   (void)stream;
   return status_of(m, "kv_paged");
 }
+int qdec_kv_ring(qdec_model* m, int32_t enable, void* stream) {
+  rec("kv_ring %d", enable);
+  (void)stream;
+  return status_of(m, "kv_ring");
+}
+int qdec_kv_ring_positions(const qdec_model* m, int32_t layer, int32_t* out) {
+  rec("kv_ring_positions %d", layer);
+  if (!m || !out) return QDEC_REFUSED;
+  *out = 0;
+  return QDEC_OK;
+}
 int qdec_kv_pages(const qdec_model* m, int32_t* page_size, int32_t* n_pages, int32_t* n_free) {
   rec("kv_pages");
   if (!m || !page_size || !n_pages || !n_free) return QDEC_REFUSED;

@@ -481,6 +481,71 @@ def test_gpu_decode_equals_gpu_prefill_recompute(key):
         check_row(g_dl[s], rec[20 + s])
 
 
+def test_window_ring_matches_the_full_cache():
+    """Window layers' rings ([P] roadmap table: a paged or ring-buffer cache)
+    give the results of caches that keep every position: a prompt longer than
+    the ring (three prefill passes, wrapped slots) bit for bit, decode steps
+    past it to f32 rounding (the merge's adds vary in order), and preset
+    positions written past the ring's length."""
+    cfg, t, _ = model_for("gemma_hd256_g4")
+    V, L = cfg["vocab"], cfg["n_layer"]
+    # window 8, passes of 4,096 positions: rings of 8,192 positions
+    prompt = synth.prompt(cfg, 9000, tag="ring")
+    follow = synth.prompt(cfg, 24, tag="ring-next")
+    with qdec.Model(cfg, t, max_seqs=1, max_ctx=16384) as m:
+        rings = [m.kv_ring_positions(l) for l in range(L)]
+        assert sorted(set(rings)) == [0, 8192], rings  # global layers keep every position
+        last = list(range(len(prompt) - 40, len(prompt)))  # prefill rows compared
+
+        def run():
+            pl = torch.empty((len(prompt), V), dtype=torch.float32, device=dev())
+            dl = torch.empty((len(follow), V), dtype=torch.float32, device=dev())
+            tk = torch.empty(1, dtype=torch.int32, device=dev())
+            m.kv_reset()
+            m.prefill(0, prompt, pl, None, all_logits=True)
+            for s, tok in enumerate(follow):  # the same host tokens on both layouts
+                m.decode_step([tok], dl[s:s + 1], tk)
+            torch.cuda.synchronize()
+            return as_np(pl[last]), as_np(dl)
+
+        ring_pl, ring_dl = run()
+        with pytest.raises(qdec.QdecError):
+            m.kv_ring(False)  # sequence 0 holds positions
+        m.kv_reset()
+        m.kv_ring(False)
+        assert [m.kv_ring_positions(l) for l in range(L)] == [0] * L
+        full_pl, full_dl = run()
+        assert np.array_equal(ring_pl, full_pl)
+        for s in range(len(follow)):
+            check_row(ring_dl[s], full_dl[s], tol=1e-5)
+
+        # preset positions: 8,392 per layer (the ring keeps the last 8,192),
+        # written on both layouts, then one step
+        n_pos = 8192 + 200
+        rng = np.random.default_rng(5)
+        shape = (cfg["n_head_kv"], n_pos, cfg["head_dim"])
+        kv = [(torch.from_numpy(rng.standard_normal(shape).astype(np.float32)).to(dev()),
+               torch.from_numpy(rng.standard_normal(shape).astype(np.float32)).to(dev())) for _ in range(L)]
+        out = {}
+        for ring in (False, True):
+            m.kv_reset()
+            m.kv_ring(ring)
+            for l in range(L):
+                m.kv_write(0, l, *kv[l])
+            row = torch.empty((1, V), dtype=torch.float32, device=dev())
+            m.decode_step([follow[0]], row, torch.empty(1, dtype=torch.int32, device=dev()))
+            torch.cuda.synchronize()
+            out[ring] = as_np(row)[0]
+        check_row(out[True], out[False], tol=1e-5)
+
+        # truncation keeps the window whole only within R - window positions
+        n = n_pos + 1
+        with pytest.raises(qdec.QdecError):
+            m.kv_truncate(0, n - (8192 - 8) - 1)
+        m.kv_truncate(0, n - (8192 - 8))
+        assert m.kv_len(0) == n - (8192 - 8)
+
+
 def test_split_prefill_and_reset_are_consistent():
     cfg, t, m = model_for("qwen3_hd128_g2")
     V = cfg["vocab"]

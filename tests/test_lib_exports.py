@@ -95,6 +95,8 @@ def test_null_handle_calls_are_refused(L):
     a, b, c = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     assert L.qdec_kv_pages(None, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)) == 1
     assert L.qdec_decode_chunks(None, ctypes.byref(a), ctypes.byref(b)) == 1
+    assert L.qdec_kv_ring(None, 1, None) == 1
+    assert L.qdec_kv_ring_positions(None, 0, ctypes.byref(a)) == 1
     assert L.qdec_debug_inject_fault(None, 1) == 1
 
 
