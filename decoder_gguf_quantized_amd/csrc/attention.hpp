@@ -597,28 +597,36 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnPrefillAr
 }
 
 // ------------------------------------------------------------ prefill attention, head-dim split
-// head_dim 256 (at 128 the whole-head kernel above, which requests a tile's
-// values before its scores, measured faster).  Same workgroup (32 queries x
-// one query head) and the
-// same MFMA layouts as attn_prefill_mfma_kernel, but the four waves walk every
-// key tile together, each owning a quarter of the head dimension: wave w
-// contracts dims [w HD/4, (w+1) HD/4) of S^T = K Q^T (contraction order
-// c(t, h) = w HD/4 + h HD/8 + t), the four partial score tiles are summed
-// through LDS in wave order (so every wave holds the same scores, maximum and
-// sum), and wave w accumulates output dims [w HD/4, (w+1) HD/4) of
-// O^T = V^T P^T.  A wave then needs a quarter of the query, output, key and
-// value registers of the whole-head kernel, which leaves room to request the
-// next tile's keys and values while the current tile is multiplied; no merge
-// of partial outputs is needed at the end.
+// head_dim 256 (at 128 the whole-head kernel above measured faster).  Same
+// workgroup (32 queries x one query head), the same MFMA layouts and the same
+// tile loads (buffer descriptors ending after the last key, the mask on edge
+// tiles only, workgroup order) as attn_prefill_mfma_kernel, but the four waves
+// walk every key tile together, each owning a quarter of the head dimension:
+// wave w contracts dims [w HD/4, (w+1) HD/4) of S^T = K Q^T (contraction
+// order c(t, h) = w HD/4 + h HD/8 + t), the four partial score tiles are
+// summed through LDS in wave order (so every wave holds the same scores,
+// maximum and sum), and wave w accumulates output dims [w HD/4, (w+1) HD/4)
+// of O^T = V^T P^T (row i of its block b: dim w HD/4 + NBW i + b).  A wave
+// then needs a quarter of the query, output, key and value registers of the
+// whole-head kernel, which leaves room to request the next tile's keys and
+// values while the current tile is multiplied; no merge of partial outputs is
+// needed at the end.
 template <int HD>
 __global__ __launch_bounds__(256) void attn_prefill_dsplit_kernel(AttnPrefillArgs a) {
   static_assert(HD % 128 == 0, "a wave owns whole 32-dim output blocks");
   constexpr int D = HD / 4;     // dims owned by a wave
   constexpr int DH = D / 2;     // contraction steps of the wave's partial S^T
   constexpr int NBW = D / 32;   // 32-dim output blocks of the wave
+  typedef float vnb __attribute__((ext_vector_type(NBW)));
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  typedef unsigned int uvnb __attribute__((ext_vector_type(NBW)));
   __shared__ float sm_s[2][4][16][64];  // partial S^T per wave, double-buffered by tile parity
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 31, lk = lane >> 5;
-  const int q0 = (int)blockIdx.x * 32, h = (int)blockIdx.y, g = h / (a.nq / a.nkv);
+  const int tid = threadIdx.x, lane = tid & 63, li = lane & 31, lk = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // workgroup id -> (KV head, query head, query tile) as in attn_prefill_mfma_kernel
+  const int G = a.nq / a.nkv, nqt = (int)gridDim.x / a.nq;
+  const int g = (int)blockIdx.x % a.nkv, rest = (int)blockIdx.x / a.nkv;
+  const int h = g * G + rest % G, q0 = (nqt - 1 - rest / G) * 32;
   const int tq = q0 + li;  // this lane's query (token index)
   const bool q_ok = tq < a.T;
   const int p = a.pos0 + tq;
@@ -628,6 +636,8 @@ __global__ __launch_bounds__(256) void attn_prefill_dsplit_kernel(AttnPrefillArg
   const int kt0 = kmin & ~31;
   const int ntile = (kmax - kt0) / 32 + 1;
   const int dk = wave * D + lk * DH;  // first contraction dim of this lane
+  const int k_hi = q_ok ? p : -1, k_lo = a.window > 0 ? p - a.window + 1 : 0;
+  const int p_first = a.pos0 + q0, p_last = a.pos0 + tlast;
 
   float q[DH];
   {
@@ -644,22 +654,32 @@ __global__ __launch_bounds__(256) void attn_prefill_dsplit_kernel(AttnPrefillArg
   }
 
   // one tile's operands: K[key0 + li][dk .. dk + DH) and, for O^T step t,
-  // V[key0 + 8(t/4) + 4 lk + t%4][w D + 32 b + li]
+  // V[key0 + 8(t/4) + 4 lk + t%4][w D + NBW li .. + NBW), through descriptors
+  // that end after row kmax (rows past it read as zeros)
   struct Tile {
-    float4 k[DH / 4];
-    float v[NBW][16];
+    u32x4 k[DH / 4];
+    vnb v[16];
   };
+  const int k_off = (li * HD + dk) * 4;
+  const int v_off = (4 * lk * HD + wave * D + NBW * li) * 4;
   auto load = [&](Tile& b, int it) {
     const int key0 = kt0 + 32 * it;
-    const float4* kp = reinterpret_cast<const float4*>(
-        a.kc + kv_row(a.map, a.nkv, a.ctx, a.seq, g, min(key0 + li, kmax)) * HD + dk);
+    const size_t base = kv_row(a.map, a.nkv, a.ctx, a.seq, g, key0);  // row of key0 + x is base + x
+    const int bytes = (min(kmax - key0, 31) + 1) * HD * 4;
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(a.kc + base * HD), (short)0, bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(a.vc + base * HD), (short)0, bytes, 0x00020000);
 #pragma unroll
-    for (int e = 0; e < DH / 4; ++e) b.k[e] = kp[e];
+    for (int e = 0; e < DH / 4; ++e) b.k[e] = __builtin_amdgcn_raw_buffer_load_b128(kr, k_off + 16 * e, 0, 0);
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      const size_t r = kv_row(a.map, a.nkv, a.ctx, a.seq, g, min(key0 + 8 * (t >> 2) + 4 * lk + (t & 3), kmax));
+      const int off = v_off + (8 * (t >> 2) + (t & 3)) * HD * 4;
+      uvnb w;
+      if constexpr (NBW == 2) w = __builtin_amdgcn_raw_buffer_load_b64(vr, off, 0, 0);
+      else w = __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0);
 #pragma unroll
-      for (int bb = 0; bb < NBW; ++bb) b.v[bb][t] = a.vc[r * HD + wave * D + 32 * bb + li];
+      for (int bb = 0; bb < NBW; ++bb) b.v[t][bb] = __uint_as_float(w[bb]);
     }
   };
 
@@ -677,54 +697,58 @@ __global__ __launch_bounds__(256) void attn_prefill_dsplit_kernel(AttnPrefillArg
     for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
 #pragma unroll
     for (int e = 0; e < DH / 4; ++e) {
-      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(b.k[e].x, q[4 * e + 0], sacc, 0, 0, 0);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(b.k[e].y, q[4 * e + 1], sacc, 0, 0, 0);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(b.k[e].z, q[4 * e + 2], sacc, 0, 0, 0);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(b.k[e].w, q[4 * e + 3], sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(b.k[e].x), q[4 * e + 0], sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(b.k[e].y), q[4 * e + 1], sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(b.k[e].z), q[4 * e + 2], sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(b.k[e].w), q[4 * e + 3], sacc, 0, 0, 0);
     }
     // the whole-head scores: partial tiles summed in wave order
 #pragma unroll
     for (int r = 0; r < 16; ++r) sm_s[it & 1][wave][r][lane] = sacc[r];
     __syncthreads();
-    float pr[16];
+    float sc[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      sc[r] = ((sm_s[it & 1][0][r][lane] + sm_s[it & 1][1][r][lane]) + sm_s[it & 1][2][r][lane]) +
+              sm_s[it & 1][3][r][lane];
+    // tiles that no query of the workgroup sees only in part skip the mask
+    const bool inner = key0 + 31 <= p_first && (a.window == 0 || key0 > p_last - a.window);
+    if (!inner) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 8 * (r >> 2) + 4 * lk + (r & 3);
+        sc[r] = (key >= k_lo) & (key <= k_hi) ? sc[r] : -INFINITY;
+      }
+    }
     float mt = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float sc = ((sm_s[it & 1][0][r][lane] + sm_s[it & 1][1][r][lane]) + sm_s[it & 1][2][r][lane]) +
-                       sm_s[it & 1][3][r][lane];
-      const int key = key0 + 8 * (r >> 2) + 4 * lk + (r & 3);
-      const bool ok = q_ok && key <= p && (a.window == 0 || key > p - a.window);
-      pr[r] = ok ? sc : -INFINITY;
-      mt = fmaxf(mt, pr[r]);
-    }
+    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sc[r]);
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     // lazy rescale, as in attn_prefill_mfma_kernel (every wave takes the same
     // decisions: its scores are the same)
-    float corr = 1.f;
-    if (m_run == -INFINITY) {
-      m_run = mt;
-    } else if (mt > m_run + 8.f) {
-      corr = exp2f(m_run - mt);
-      m_run = mt;
-    }
-    const bool rescale = __any(corr != 1.f);
-    float ps = 0.f;
+    const bool first = m_run == -INFINITY;
+    const bool bump = !first && mt > m_run + 8.f;
+    const float corr = bump ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;
+    m_run = first || bump ? mt : m_run;
+    const float mref = m_run == -INFINITY ? 0.f : m_run;
+    float pr[16], ps = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      pr[r] = pr[r] == -INFINITY ? 0.f : exp2f(pr[r] - m_run);
+      pr[r] = __builtin_amdgcn_exp2f(sc[r] - mref);  // exp2(-inf) = 0 for masked keys
       ps += pr[r];
     }
     ps += __shfl_xor(ps, 32);
     l_run = l_run * corr + ps;
+    if (__any(corr != 1.f)) {
 #pragma unroll
-    for (int bb = 0; bb < NBW; ++bb) {
-      if (rescale) {
+      for (int bb = 0; bb < NBW; ++bb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[bb][r] *= corr;
-      }
-#pragma unroll
-      for (int t = 0; t < 16; ++t) o[bb] = __builtin_amdgcn_mfma_f32_32x32x2f32(b.v[bb][t], pr[t], o[bb], 0, 0, 0);
     }
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+#pragma unroll
+      for (int bb = 0; bb < NBW; ++bb) o[bb] = __builtin_amdgcn_mfma_f32_32x32x2f32(b.v[t][bb], pr[t], o[bb], 0, 0, 0);
   };
 
   // two register sets: the next tile's loads are in flight while a tile is
@@ -742,13 +766,14 @@ __global__ __launch_bounds__(256) void attn_prefill_dsplit_kernel(AttnPrefillArg
   if (q_ok) {
     const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
     float* orow = a.out + (size_t)tq * a.nq * HD + (size_t)h * HD + wave * D;
+    // register r holds MFMA row i = 8(r/4) + 4 lk + r%4 of every block: dims NBW i .. NBW i + NBW - 1
 #pragma unroll
-    for (int bb = 0; bb < NBW; ++bb)
+    for (int r = 0; r < 16; ++r) {
+      vnb v;
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4)
-        *reinterpret_cast<float4*>(orow + 32 * bb + 8 * r4 + 4 * lk) =
-            make_float4(o[bb][4 * r4] * inv, o[bb][4 * r4 + 1] * inv, o[bb][4 * r4 + 2] * inv,
-                        o[bb][4 * r4 + 3] * inv);
+      for (int bb = 0; bb < NBW; ++bb) v[bb] = o[bb][r] * inv;
+      *reinterpret_cast<vnb*>(orow + NBW * (8 * (r >> 2) + 4 * lk + (r & 3))) = v;
+    }
   }
 }
 

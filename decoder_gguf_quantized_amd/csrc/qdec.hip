@@ -496,7 +496,7 @@ void attention_prefill(qdec_model* m, hipStream_t st, int l, int seq, int T, int
   const int nqt = (T + 31) / 32;
   if (hd == 64) qlaunch(attn_prefill_mfma_kernel<64>, dim3(nqt * c.n_head), 256, 0, st, a);
   else if (hd == 128) qlaunch(attn_prefill_mfma_kernel<128>, dim3(nqt * c.n_head), 256, 0, st, a);
-  else qlaunch(attn_prefill_dsplit_kernel<256>, dim3(nqt, c.n_head), 256, 0, st, a);
+  else qlaunch(attn_prefill_dsplit_kernel<256>, dim3(nqt * c.n_head), 256, 0, st, a);
 }
 
 void rope_kv(qdec_model* m, hipStream_t st, int l, int n, int seq0, int pos0, const int* dpos) {
