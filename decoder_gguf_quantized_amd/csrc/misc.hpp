@@ -229,14 +229,6 @@ struct StepParams {
 // of the last kept one by one more pass.  Result per row: tokens with key >
 // cut_key, or key == cut_key and index <= cut_idx, are kept.  top_p >= 1,
 // T = 0 or a non-finite logit keep every token (cut_key = 0).
-struct TopPArgs {
-  const float* logits;
-  int ld, vocab, rows;
-  float temperature, top_p;
-  uint32_t* cut_key;  // [rows]
-  int* cut_idx;       // [rows]
-  const StepParams* sp;  // if non-null: logits, temperature, top_p come from here
-};
 
 // Key that orders floats like their values (-0 and +0 alike; NaN excluded by
 // the caller).
@@ -264,9 +256,57 @@ QD_DEV uint64_t wave_sum_u64(uint64_t v) {
   return v;
 }
 
-__global__ __launch_bounds__(1024) void topp_cut_kernel(TopPArgs a) {
-  constexpr int NW = 16;
-  __shared__ unsigned long long h[NW][256];  // per-wave histograms (row 0: totals)
+// The cut is found in passes over the row, each a launch of topp_pass_kernel
+// with grid (kTopPChunks, rows): workgroup c takes the c-th chunk of the row.
+// pass 0: each chunk's max (and whether it holds a non-finite logit);
+// pass 1: the coarse histogram; passes 2..5: select in the previous level's
+// histogram, then histogram the next byte of the key among the candidates;
+// pass 6 (one workgroup per row): select the last byte, then resolve ties.
+// Histograms are sums of 64-bit integer weights with atomic adds, so every
+// order of the adds gives the same sums; every workgroup of a pass repeats the
+// selection from the same histogram and state and reaches the same result, so
+// the workgroups of a pass never wait for one another.  Buffers: the level-c
+// histogram (c = 0 coarse, 1..4 key bytes) is accumulated in hist[c % 3] by
+// pass c + 1, which also clears hist[(c + 1) % 3] (read last by the pass
+// before); the state is written by each pass's first chunk into state[pass % 2]
+// and read by the next pass from state[(pass - 1) % 2].
+constexpr int kTopPChunks = 64;
+
+struct TopPState {
+  float lmax;
+  int mode;                       // 0: cut in progress, 1: decided (keep all)
+  double target;                  // top_p * Z
+  unsigned long long above;       // weight of the tokens ranked before the candidates
+  unsigned long long tie_mass;    // weight of the selected bin
+  uint32_t prefix, mask;          // key bytes selected so far
+  int cb;                         // coarse bin of the candidates
+};
+
+struct TopPArgs {
+  const float* logits;
+  int ld, vocab, rows;
+  float temperature, top_p;
+  uint32_t* cut_key;  // [rows]
+  int* cut_idx;       // [rows]
+  const StepParams* sp;  // if non-null: logits, temperature, top_p come from here
+  float* pmax;        // [rows][kTopPChunks]
+  int* pbad;          // [rows][kTopPChunks]
+  unsigned long long* hist;  // [3][rows][256]
+  TopPState* state;   // [2][rows]
+  int pass;
+};
+
+// Device buffers of the passes for up to `rows` rows.
+struct TopPScratch {
+  float* pmax;                // [rows][kTopPChunks]
+  int* pbad;                  // [rows][kTopPChunks]
+  unsigned long long* hist;   // [3][rows][256]
+  TopPState* state;           // [2][rows]
+};
+
+__global__ __launch_bounds__(256) void topp_pass_kernel(TopPArgs a) {
+  constexpr int NW = 4;
+  __shared__ unsigned long long h[NW][256];  // per-wave histograms; h[0] also holds a read level
   __shared__ float sm_max[NW];
   __shared__ int sm_bad[NW];
   __shared__ unsigned long long sm_sel[2];
@@ -277,45 +317,83 @@ __global__ __launch_bounds__(1024) void topp_cut_kernel(TopPArgs a) {
     a.temperature = a.sp->temperature;
     a.top_p = a.sp->top_p;
   }
-  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int chunk = blockIdx.x, row = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* lg = a.logits + (size_t)row * a.ld;
   const int V = a.vocab;
-  if (!(a.temperature > 0.f) || !(a.top_p < 1.f)) {
-    if (tid == 0) {
+  const int per = (V + kTopPChunks - 1) / kTopPChunks;
+  const int c0 = min(V, chunk * per), c1 = min(V, c0 + per);
+  unsigned long long* hrow = a.hist + (size_t)row * 256;
+  const size_t hstride = (size_t)a.rows * 256;
+  auto hbuf = [&](int c) { return hrow + (size_t)(c % 3) * hstride; };
+  TopPState* out_state = a.state + (size_t)(a.pass % 2) * a.rows + row;
+  const TopPState* in_state = a.state + (size_t)((a.pass + 1) % 2) * a.rows + row;
+  auto keep_all = [&]() {  // the first chunk records the result and the decision
+    if (chunk == 0 && tid == 0) {
       a.cut_key[row] = 0u;
       a.cut_idx[row] = 0x7fffffff;
+      TopPState st{};
+      st.mode = 1;
+      *out_state = st;
     }
+  };
+  if (!(a.temperature > 0.f) || !(a.top_p < 1.f)) {
+    keep_all();
     return;
   }
-  // max logit; a non-finite logit keeps every token
-  float mx = -INFINITY;
-  int bad = 0;
-  for (int v = tid; v < V; v += 1024) {
-    const float l = lg[v];
-    bad |= !isfinite(l);
-    mx = fmaxf(mx, l);
+  if (a.pass == 0) {  // chunk max; a non-finite logit keeps every token
+    float mx = -INFINITY;
+    int bad = 0;
+    for (int v = c0 + tid; v < c1; v += 256) {
+      const float l = lg[v];
+      bad |= !isfinite(l);
+      mx = fmaxf(mx, l);
+    }
+    mx = wave_max(mx);
+    bad = __ballot(bad) != 0ull;
+    if (lane == 0) {
+      sm_max[wave] = mx;
+      sm_bad[wave] = bad;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      for (int w = 1; w < NW; ++w) {
+        mx = fmaxf(mx, sm_max[w]);
+        bad |= sm_bad[w];
+      }
+      a.pmax[(size_t)row * kTopPChunks + chunk] = fmaxf(sm_max[0], mx);
+      a.pbad[(size_t)row * kTopPChunks + chunk] = bad | sm_bad[0];
+    }
+    if (chunk == 0) hbuf(0)[tid] = 0ull;  // accumulated by pass 1
+    return;
   }
-  mx = wave_max(mx);
-  bad = __ballot(bad) != 0ull;
-  if (lane == 0) {
-    sm_max[wave] = mx;
-    sm_bad[wave] = bad;
-  }
-  __syncthreads();
-  float lmax = sm_max[0];
-  int anybad = sm_bad[0];
-  for (int w = 1; w < NW; ++w) {
-    lmax = fmaxf(lmax, sm_max[w]);
-    anybad |= sm_bad[w];
+  TopPState st;
+  if (a.pass == 1) {
+    st = TopPState{};
+    float lmax = -INFINITY;
+    int anybad = 0;
+    for (int c = 0; c < kTopPChunks; ++c) {
+      lmax = fmaxf(lmax, a.pmax[(size_t)row * kTopPChunks + c]);
+      anybad |= a.pbad[(size_t)row * kTopPChunks + c];
+    }
+    if (anybad) {
+      keep_all();
+      return;
+    }
+    st.lmax = lmax;
+  } else {
+    st = *in_state;
+    if (st.mode) {
+      if (chunk == 0 && tid == 0) *out_state = st;
+      return;
+    }
   }
   const float cw = 1.4426950408889634f / a.temperature;
-  auto weight = [&](float l) { return fixed40(exp2f((l - lmax) * cw)); };
+  auto weight = [&](float l) { return fixed40(exp2f((l - st.lmax) * cw)); };
   // coarse bin of a logit by its distance from the max, 1/8 of a log2 unit of
   // weight per bin (the last bin takes the rest).  Monotone in the logit, so a
   // bin is a contiguous range of keys; it spreads a row over many bins, which
   // the key's top byte does not (logits of one row share a few exponents).
-  auto cbin = [&](float l) { return (int)fminf((lmax - l) * cw * 8.0f, 255.0f); };
-  double target = 0.0;  // top_p * Z, set after the coarse level
+  auto cbin = [&](float l) { return (int)fminf((st.lmax - l) * cw * 8.0f, 255.0f); };
   // selection over the 256 bins of h[0] (bin order given by `desc`: key bytes
   // run high to low from bin 255, coarse bins from bin 0): the bin where the
   // running weight crosses the target, the weight before it and its own weight
@@ -339,7 +417,7 @@ __global__ __launch_bounds__(1024) void topp_cut_kernel(TopPArgs a) {
       unsigned long long f_before = 0ull, f_bin = 0ull;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if (found < 0 && b4[j] > 0ull && (double)run < target && (double)(run + b4[j]) >= target) {
+        if (found < 0 && b4[j] > 0ull && (double)run < st.target && (double)(run + b4[j]) >= st.target) {
           found = desc ? 255 - 4 * lane - j : 4 * lane + j;
           f_before = run;
           f_bin = b4[j];
@@ -359,92 +437,90 @@ __global__ __launch_bounds__(1024) void topp_cut_kernel(TopPArgs a) {
     mass = sm_sel[1];
     __syncthreads();  // everyone has read the selection before h is cleared again
   };
-  auto clear = [&]() {
-    for (int i = tid; i < NW * 256; i += 1024) (&h[0][0])[i] = 0ull;
+  // the previous level's histogram into h[0]; after the coarse level, its total is Z
+  if (a.pass >= 2) {
+    h[0][tid] = hbuf(a.pass - 2)[tid];
     __syncthreads();
-  };
-  auto total = [&]() {  // per-wave histograms -> h[0]
+    if (a.pass == 2) {
+      if (tid < 64) {
+        unsigned long long z = h[0][tid] + h[0][tid + 64] + h[0][tid + 128] + h[0][tid + 192];
+        z = wave_sum_u64(z);
+        if (tid == 0) sm_sel[0] = z;
+      }
+      __syncthreads();
+      const unsigned long long Z = sm_sel[0];
+      __syncthreads();
+      st.target = (double)a.top_p * (double)Z;  // Z < 2^59: rounded to double, relative 2^-53
+      if (st.target < 0.5) st.target = 0.5;     // top_p <= 0: the first token only
+      if (st.target > (double)Z) {
+        keep_all();
+        return;
+      }
+      int cb;
+      unsigned long long above, tie_mass;
+      select(false, 0ull, cb, above, tie_mass);
+      if (cb < 0) {
+        keep_all();
+        return;
+      }
+      st.cb = cb;
+      st.above = above;
+      st.tie_mass = tie_mass;
+    } else {  // key byte level pass - 3
+      int d;
+      unsigned long long before, mass;
+      select(true, st.above, d, before, mass);
+      if (d < 0) {  // guard: the candidates' weight cannot reach the target
+        keep_all();
+        return;
+      }
+      const int sh = 24 - 8 * (a.pass - 3);
+      st.above = before;
+      st.tie_mass = mass;
+      st.prefix |= (uint32_t)d << sh;
+      st.mask |= 255u << sh;
+    }
+  }
+  if (a.pass <= 5) {
+    // this chunk's share of the next level: the coarse bins (pass 1) or key
+    // byte pass - 2 among the candidates (coarse bin cb, key bytes so far)
+    for (int i = tid; i < NW * 256; i += 256) (&h[0][0])[i] = 0ull;
     __syncthreads();
-    if (tid < 256) {
-      unsigned long long t = 0ull;
-      for (int w = 0; w < NW; ++w) t += h[w][tid];
-      h[0][tid] = t;
+    if (a.pass == 1) {
+      for (int v = c0 + tid; v < c1; v += 256) {
+        const float l = lg[v];
+        atomicAdd(&h[wave][cbin(l)], weight(l));
+      }
+    } else {
+      const int sh = 24 - 8 * (a.pass - 2);
+      for (int v = c0 + tid; v < c1; v += 256) {
+        const float l = lg[v];
+        const uint32_t k = order_key(l);
+        if ((k & st.mask) == st.prefix && cbin(l) == st.cb) atomicAdd(&h[wave][(k >> sh) & 255u], weight(l));
+      }
     }
     __syncthreads();
-  };
-  auto keep_all = [&]() {
-    if (tid == 0) {
-      a.cut_key[row] = 0u;
-      a.cut_idx[row] = 0x7fffffff;
+    unsigned long long t = 0ull;
+    for (int w = 0; w < NW; ++w) t += h[w][tid];
+    if (t) atomicAdd(hbuf(a.pass - 1) + tid, t);
+    if (chunk == 0) {
+      hbuf(a.pass)[tid] = 0ull;  // accumulated by the next pass
+      if (tid == 0) *out_state = st;
     }
-  };
-  if (anybad) {
-    keep_all();
     return;
   }
-  // coarse level: weight per coarse bin; the total is Z
-  clear();
-  for (int v = tid; v < V; v += 1024) {
-    const float l = lg[v];
-    atomicAdd(&h[wave][cbin(l)], weight(l));
-  }
-  total();
-  if (tid < 64) {
-    unsigned long long z = h[0][tid] + h[0][tid + 64] + h[0][tid + 128] + h[0][tid + 192];
-    z = wave_sum_u64(z);
-    if (tid == 0) sm_sel[0] = z;
-  }
-  __syncthreads();
-  const unsigned long long Z = sm_sel[0];
-  target = (double)a.top_p * (double)Z;  // Z < 2^59: rounded to double, relative 2^-53
-  if (target < 0.5) target = 0.5;               // top_p <= 0: the first token only
-  __syncthreads();
-  if (target > (double)Z) {
-    keep_all();
-    return;
-  }
-  int cb;
-  unsigned long long above, tie_mass;
-  select(false, 0ull, cb, above, tie_mass);
-  if (cb < 0) {
-    keep_all();
-    return;
-  }
-  // exact levels over the key's four bytes, among the tokens of coarse bin cb
-  uint32_t prefix = 0u, mask = 0u;
-  for (int level = 0; level < 4; ++level) {
-    const int sh = 24 - 8 * level;
-    clear();
-    for (int v = tid; v < V; v += 1024) {
-      const float l = lg[v];
-      const uint32_t k = order_key(l);
-      if ((k & mask) == prefix && cbin(l) == cb) atomicAdd(&h[wave][(k >> sh) & 255u], weight(l));
-    }
-    total();
-    int d;
-    unsigned long long before, mass;
-    select(true, above, d, before, mass);
-    if (d < 0) {  // guard: the candidates' weight cannot reach the target
-      keep_all();
-      return;
-    }
-    above = before;
-    tie_mass = mass;
-    prefix |= (uint32_t)d << sh;
-    mask |= 255u << sh;
-  }
-  // prefix = key of the boundary token, above = weight of the larger keys,
-  // tie_mass = weight of the tokens with the boundary key (all equal weights)
+  // pass 6: prefix = key of the boundary token, above = weight of the larger
+  // keys, tie_mass = weight of the tokens with the boundary key (equal weights)
   int cut = 0x7fffffff;
-  const unsigned long long w1 = weight(key_value(prefix));
-  const unsigned long long cnt = w1 ? tie_mass / w1 : 0ull;
-  const double need = w1 ? ceil((target - (double)above) / (double)w1) : 0.0;  // ties to keep, >= 1
+  const unsigned long long w1 = weight(key_value(st.prefix));
+  const unsigned long long cnt = w1 ? st.tie_mass / w1 : 0ull;
+  const double need = w1 ? ceil((st.target - (double)st.above) / (double)w1) : 0.0;  // ties to keep, >= 1
   if (w1 && need < (double)cnt) {
     const int n_need = (int)need;
     // the n_need-th token (in index order) with the boundary key
-    const int seg = (V + 1023) / 1024, b0 = min(V, tid * seg), b1 = min(V, b0 + seg);
+    const int seg = (V + 255) / 256, b0 = min(V, tid * seg), b1 = min(V, b0 + seg);
     int c_t = 0;
-    for (int v = b0; v < b1; ++v) c_t += order_key(lg[v]) == prefix;
+    for (int v = b0; v < b1; ++v) c_t += order_key(lg[v]) == st.prefix;
     int inc = c_t;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -459,7 +535,7 @@ __global__ __launch_bounds__(1024) void topp_cut_kernel(TopPArgs a) {
     if (before < n_need && before + c_t >= n_need) {
       int r = before;
       for (int v = b0; v < b1; ++v)
-        if (order_key(lg[v]) == prefix && ++r == n_need) {
+        if (order_key(lg[v]) == st.prefix && ++r == n_need) {
           sm_i[1] = v;
           break;
         }
@@ -468,7 +544,7 @@ __global__ __launch_bounds__(1024) void topp_cut_kernel(TopPArgs a) {
     cut = sm_i[1];
   }
   if (tid == 0) {
-    a.cut_key[row] = prefix;
+    a.cut_key[row] = st.prefix;
     a.cut_idx[row] = cut;
   }
 }
@@ -484,7 +560,7 @@ struct SampleArgs {
   int* out;        // [rows]
   int* out2;       // optional second copy
   const StepParams* sp;  // if non-null: logits, out, temperature, seed, step come from here
-  const uint32_t* cut_key;  // if non-null: top-p cut per row (see topp_cut_kernel)
+  const uint32_t* cut_key;  // if non-null: top-p cut per row (see topp_pass_kernel)
   const int* cut_idx;
   const int* seq;  // if non-null: sequence slot of each row, the row index of the random stream
 };

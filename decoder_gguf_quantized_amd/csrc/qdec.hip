@@ -135,6 +135,7 @@ struct qdec_model {
   int am_n = 0;           // the most waves an LM-head launch can have (set at load)
   uint32_t* cut_key = nullptr;  // [max_seqs] top-p cut per row
   int* cut_idx = nullptr;
+  TopPScratch topp;             // the top-p passes' partials, histograms and state
   int nvchunk = 0;
   int* d_pos = nullptr;
   int* d_tok = nullptr;
@@ -517,6 +518,14 @@ void embed(qdec_model* m, hipStream_t st, const int* d_tokens, int n, float* out
   qlaunch(embed_kernel, n, 256, 0, st, a);
 }
 
+// The top-p cut of rows x vocab logits: the seven passes of topp_pass_kernel.
+void topp_cut(hipStream_t st, TopPArgs t) {
+  for (int pass = 0; pass <= 6; ++pass) {
+    t.pass = pass;
+    qlaunch(topp_pass_kernel, pass < 6 ? dim3(kTopPChunks, t.rows) : dim3(1, t.rows), 256, 0, st, t);
+  }
+}
+
 void sample(qdec_model* m, hipStream_t st, const float* logits, int ld, int rows, float temp, uint64_t seed,
             uint64_t step, int* out, int* out2, const StepParams* sp = nullptr, bool topp = false,
             const int* seq = nullptr) {
@@ -524,9 +533,10 @@ void sample(qdec_model* m, hipStream_t st, const float* logits, int ld, int rows
   SampleArgs a{logits, ld, V, rows, temp, seed, step, m->s_v, m->s_i, m->nvchunk, out, out2, sp,
                topp ? m->cut_key : nullptr, topp ? m->cut_idx : nullptr, seq};
   if (topp) {
-    TopPArgs t{logits, ld, V, rows, temp, 1.f, m->cut_key, m->cut_idx, sp};
+    TopPArgs t{logits, ld, V, rows, temp, 1.f, m->cut_key, m->cut_idx, sp, m->topp.pmax, m->topp.pbad,
+               m->topp.hist, m->topp.state, 0};
     Timed tm(m, st, "topp_cut", (double)rows * V * 4 * 6, 0);
-    qlaunch(topp_cut_kernel, rows, 1024, 0, st, t);
+    topp_cut(st, t);
   }
   {
     Timed tm(m, st, "sample", (double)rows * V * 4, 0);
@@ -1156,6 +1166,9 @@ int load(const qdec_config* cfgp, const qdec_tensor* ts, int32_t n, int32_t max_
     m->am_i = m->dalloc<int>(m->am_n);
     m->cut_key = m->dalloc<uint32_t>(max_seqs);
     m->cut_idx = m->dalloc<int>(max_seqs);
+    m->topp = TopPScratch{m->dalloc<float>((size_t)max_seqs * kTopPChunks), m->dalloc<int>((size_t)max_seqs * kTopPChunks),
+                          m->dalloc<unsigned long long>((size_t)3 * max_seqs * 256),
+                          m->dalloc<TopPState>((size_t)2 * max_seqs)};
     m->d_pos = m->dalloc<int>(64);
     m->d_tok = m->dalloc<int>(64);
     m->d_seq = m->dalloc<int>(64);
@@ -1365,7 +1378,12 @@ int decode_impl(qdec_model* m, const int32_t* seqs, const int32_t* tokens, int32
 constexpr int kNoAllocRows = 64;
 constexpr int kNoAllocVocab = 1 << 20;
 constexpr size_t kNoAllocPart = (size_t)kNoAllocRows * (kNoAllocVocab / kSampleChunk) * 4;  // 64 KiB
-constexpr size_t kNoAllocScratch = 2 * kNoAllocPart + 2 * kNoAllocRows * 4;
+// then the top-p passes': histograms [3][rows][256] u64, state [2][rows],
+// chunk maxima and flags [rows][kTopPChunks]
+constexpr size_t kNoAllocHist = 2 * kNoAllocPart + 2 * kNoAllocRows * 4;
+constexpr size_t kNoAllocState = kNoAllocHist + (size_t)3 * kNoAllocRows * 256 * 8;
+constexpr size_t kNoAllocPmax = kNoAllocState + (size_t)2 * kNoAllocRows * sizeof(TopPState);
+constexpr size_t kNoAllocScratch = kNoAllocPmax + (size_t)2 * kNoAllocRows * kTopPChunks * 4;
 static __device__ __align__(256) unsigned char scratch[kNoAllocScratch];
 
 namespace {
@@ -1773,27 +1791,35 @@ int qdec_debug_sample(const float* d_logits, int32_t rows, int32_t vocab, float 
   int* pi = nullptr;
   uint32_t* ck = nullptr;
   int* ci = nullptr;
-  if (hipMalloc(&pv, (size_t)rows * nch * 4) != hipSuccess || hipMalloc(&pi, (size_t)rows * nch * 4) != hipSuccess ||
-      hipMalloc(&ck, (size_t)rows * 4) != hipSuccess || hipMalloc(&ci, (size_t)rows * 4) != hipSuccess) {
+  TopPScratch tp{};
+  auto release = [&]() {
     (void)hipFree(pv);
     (void)hipFree(pi);
     (void)hipFree(ck);
+    (void)hipFree(ci);
+    (void)hipFree(tp.pmax);
+    (void)hipFree(tp.pbad);
+    (void)hipFree(tp.hist);
+    (void)hipFree(tp.state);
+  };
+  if (hipMalloc(&pv, (size_t)rows * nch * 4) != hipSuccess || hipMalloc(&pi, (size_t)rows * nch * 4) != hipSuccess ||
+      hipMalloc(&ck, (size_t)rows * 4) != hipSuccess || hipMalloc(&ci, (size_t)rows * 4) != hipSuccess ||
+      hipMalloc(&tp.pmax, (size_t)rows * kTopPChunks * 4) != hipSuccess ||
+      hipMalloc(&tp.pbad, (size_t)rows * kTopPChunks * 4) != hipSuccess ||
+      hipMalloc(&tp.hist, (size_t)3 * rows * 256 * 8) != hipSuccess ||
+      hipMalloc(&tp.state, (size_t)2 * rows * sizeof(TopPState)) != hipSuccess) {
+    release();
     set_err("internal: hipMalloc failed");
     return QDEC_INTERNAL;
   }
   SampleArgs a{d_logits, vocab, vocab, rows, temperature, seed, step, pv, pi, nch, d_out, nullptr, nullptr,
                topp ? ck : nullptr, topp ? ci : nullptr};
-  if (topp) {
-    TopPArgs t{d_logits, vocab, vocab, rows, temperature, top_p, ck, ci, nullptr};
-    qlaunch(topp_cut_kernel, rows, 1024, 0, st, t);
-  }
+  if (topp) topp_cut(st, TopPArgs{d_logits, vocab, vocab, rows, temperature, top_p, ck, ci, nullptr, tp.pmax, tp.pbad,
+                                  tp.hist, tp.state, 0});
   qlaunch(sample_stage1_kernel, dim3(nch, rows), 256, 0, st, a);
   qlaunch(sample_stage2_kernel, rows, 64, 0, st, a);
   hipError_t e = hipStreamSynchronize(st);
-  (void)hipFree(pv);
-  (void)hipFree(pi);
-  (void)hipFree(ck);
-  (void)hipFree(ci);
+  release();
   if (e != hipSuccess) { set_err("internal: %s", hipGetErrorString(e)); return QDEC_INTERNAL; }
   return QDEC_OK;
 }
@@ -1826,11 +1852,14 @@ int qdec_sample_noalloc(const float* d_logits, int32_t rows, int32_t vocab, floa
   // (stage 1 writes all rows x chunks, the top-p cut all rows): nothing to clear
   SampleArgs a{d_logits, vocab, vocab, rows, temperature, seed, step, pv, pi, nch, d_out, nullptr, nullptr,
                topp ? ck : nullptr, topp ? ci : nullptr};
+  static_assert(kNoAllocHist % 8 == 0 && kNoAllocState % 8 == 0 && kNoAllocPmax % 8 == 0, "8-byte alignment");
+  TopPArgs t{d_logits, vocab, vocab, rows, temperature, top_p, ck, ci, nullptr,
+             reinterpret_cast<float*>(ptr + kNoAllocPmax),
+             reinterpret_cast<int*>(ptr + kNoAllocPmax + (size_t)kNoAllocRows * kTopPChunks * 4),
+             reinterpret_cast<unsigned long long*>(ptr + kNoAllocHist), reinterpret_cast<TopPState*>(ptr + kNoAllocState),
+             0};
   try {
-    if (topp) {
-      TopPArgs t{d_logits, vocab, vocab, rows, temperature, top_p, ck, ci, nullptr};
-      qlaunch(topp_cut_kernel, rows, 1024, 0, st, t);
-    }
+    if (topp) topp_cut(st, t);
     qlaunch(sample_stage1_kernel, dim3(nch, rows), 256, 0, st, a);
     qlaunch(sample_stage2_kernel, rows, 64, 0, st, a);
     hipck(hipGetLastError(), "sampling launch");
