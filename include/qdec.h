@@ -316,7 +316,7 @@ int qdec_debug_sample(const float* d_logits, int32_t rows, int32_t vocab, float 
  * device memory: code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc.  Same rule and same kernels as qdec_debug_sample; the
  * partial results live in a fixed file-scope device array of the library
- * (131,584 bytes per GPU, held until the process ends), so rows <= 64 and
+ * (563,712 bytes per GPU, held until the process ends), so rows <= 64 and
  * vocab <= 2^20 (refused otherwise, status 1).  Enqueued on `stream` without a
  * host wait (qdec_debug_sample synchronizes).  Calls that overlap on one GPU --
  * on different streams, or from several threads -- share that array and race:
