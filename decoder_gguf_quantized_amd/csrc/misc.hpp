@@ -16,29 +16,40 @@ struct WView {
   const uint32_t* sd;  // K-quant super-block scales
 };
 
-QD_DEV float weight_at(const WView& w, size_t row, int k) {
+template <int QT>
+QD_DEV float weight_at_t(const WView& w, size_t row, int k) {
   const int kp = w.nblk * 32;
-  if (w.type == kQ8_0) {
+  if constexpr (QT == kQ8_0) {
     float d = load_half(w.d + row * w.nblk + (k >> 5));
     return d * (float)reinterpret_cast<const int8_t*>(w.qs)[row * kp + k];
-  }
-  if (w.type == kQ4_0 || w.type == kQ4_K) {
+  } else if constexpr (QT == kQ4_0 || QT == kQ4_K) {
     const int b = k >> 5, j = k & 31;
     uint32_t byte = w.qs[(row * w.nblk + b) * 16 + (j & 15)];
     uint32_t n = j < 16 ? (byte & 15u) : (byte >> 4);
-    if (w.type == kQ4_K) {  // scale * n - min, rounded once
+    if constexpr (QT == kQ4_K) {  // scale * n - min, rounded once
       const uint32_t sm = w.d[row * w.nblk + b], sd = w.sd[row * (w.nblk >> 3) + (b >> 3)];
       return fmaf(q4k_scale(sm, sd), (float)n, -q4k_min(sm, sd));
+    } else {
+      float d = load_half(w.d + row * w.nblk + b);
+      return d * (float)((int)n - 8);
     }
-    float d = load_half(w.d + row * w.nblk + b);
-    return d * (float)((int)n - 8);
-  }
-  if (w.type == kQ6_K) {
+  } else if constexpr (QT == kQ6_K) {
     const uint32_t sc = (uint32_t)(int32_t)reinterpret_cast<const int8_t*>(w.d)[row * 2 * w.nblk + (k >> 4)];
     const float s = q6k_scale(sc, w.sd[row * (w.nblk >> 3) + (k >> 8)]);
     return s * (float)reinterpret_cast<const int8_t*>(w.qs)[row * kp + k];
+  } else {
+    return reinterpret_cast<const float*>(w.qs)[row * kp + k];
   }
-  return reinterpret_cast<const float*>(w.qs)[row * kp + k];
+}
+
+QD_DEV float weight_at(const WView& w, size_t row, int k) {
+  switch (w.type) {
+    case kQ8_0: return weight_at_t<kQ8_0>(w, row, k);
+    case kQ4_0: return weight_at_t<kQ4_0>(w, row, k);
+    case kQ4_K: return weight_at_t<kQ4_K>(w, row, k);
+    case kQ6_K: return weight_at_t<kQ6_K>(w, row, k);
+    default: return weight_at_t<kF32>(w, row, k);
+  }
 }
 
 // ------------------------------------------------------------ embedding
@@ -53,28 +64,30 @@ struct EmbedArgs {
   int* err;
 };
 
+// One workgroup per token, for the table's weight type QT (a type known at
+// compile time keeps the decode free of branches, so all loads of a batch go
+// out together).
+template <int QT>
 __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
   const int t = blockIdx.x;
   int tok = a.tokens[t];
-  if (tok < 0 || tok >= a.vocab) {
-    if (threadIdx.x == 0 && a.err) *a.err = 1;
-    tok = tok < 0 ? 0 : a.vocab - 1;
-  }
-  // eight elements per thread per batch: their loads are all issued before the
-  // first store, so a row costs one memory round trip per 2048 elements
-  for (int k0 = threadIdx.x; k0 < a.hidden; k0 += 256 * 8) {
-    float v[8];
+  const bool bad = tok < 0 || tok >= a.vocab;
+  tok = tok < 0 ? 0 : (tok >= a.vocab ? a.vocab - 1 : tok);
+  // sixteen elements per thread per batch: their loads are all issued before
+  // the first store (loads and stores share one in-order counter, so a load
+  // behind a store waits for it), so a row of up to 4,096 elements costs one
+  // memory round trip; indices past the row read its last element
+  for (int k0 = threadIdx.x; k0 < a.hidden; k0 += 256 * 16) {
+    float v[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int k = k0 + 256 * i;
-      v[i] = k < a.hidden ? weight_at(a.w, (size_t)tok, k) : 0.f;
-    }
+    for (int i = 0; i < 16; ++i) v[i] = weight_at_t<QT>(a.w, (size_t)tok, min(k0 + 256 * i, a.hidden - 1));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 16; ++i) {
       const int k = k0 + 256 * i;
       if (k < a.hidden) a.out[(size_t)t * a.ldo + k] = v[i];
     }
   }
+  if (bad && threadIdx.x == 0 && a.err) *a.err = 1;  // after the loads: ids outside [0, vocab) latch the error
 }
 
 // ------------------------------------------------------------ RMSNorm rows

@@ -515,7 +515,13 @@ void embed(qdec_model* m, hipStream_t st, const int* d_tokens, int n, float* out
   EmbedArgs a{WView{m->embd.qs, m->embd.d, m->embd.type, m->embd.nblk, m->embd.sd}, c.hidden, c.vocab, n, d_tokens, out,
               c.hidden, m->err_dev};
   Timed tm(m, st, "embed", (double)n * (m->embd.gguf_bytes / m->embd.rows + c.hidden * 4), 0);
-  qlaunch(embed_kernel, n, 256, 0, st, a);
+  switch (m->embd.type) {
+    case kQ8_0: qlaunch(embed_kernel<kQ8_0>, n, 256, 0, st, a); break;
+    case kQ4_0: qlaunch(embed_kernel<kQ4_0>, n, 256, 0, st, a); break;
+    case kQ4_K: qlaunch(embed_kernel<kQ4_K>, n, 256, 0, st, a); break;
+    case kQ6_K: qlaunch(embed_kernel<kQ6_K>, n, 256, 0, st, a); break;
+    default: qlaunch(embed_kernel<kF32>, n, 256, 0, st, a); break;
+  }
 }
 
 // The top-p cut of rows x vocab logits: the seven passes of topp_pass_kernel.
