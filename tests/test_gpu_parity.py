@@ -661,6 +661,34 @@ def test_decode_ignores_cache_rows_past_the_length():
         check_row(as_np(dl)[0], om.forward(0, [tok])[0])
 
 
+@pytest.mark.parametrize("key", ["llama_q4_hd64_g4", "qwen3_hd128_g2", "gemma_hd256_g4"])
+def test_prefill_ignores_cache_rows_past_the_prompt(key):
+    """Prefill attention reads the last key tile of a query tile whole: the rows
+    past the prompt's last key (here NaN, written and then truncated away) read
+    as zeros through the tile's buffer descriptor and are masked, so the logits
+    equal those over a clean cache bit for bit (head_dim 64, 128 and 256)."""
+    cfg, t, m = model_for(key)
+    V, nkv, hd, L = cfg["vocab"], cfg["n_head_kv"], cfg["head_dim"], cfg["n_layer"]
+    prompt = synth.prompt(cfg, 70, tag="past-the-prompt")  # last tile: keys 64..95, 26 rows past key 69
+
+    def prefill():
+        pl = torch.empty((len(prompt), V), dtype=torch.float32, device=dev())
+        m.prefill(0, prompt, pl, None, all_logits=True)
+        torch.cuda.synchronize()
+        return as_np(pl)
+
+    m.kv_reset()
+    clean = prefill()
+    nan = torch.full((nkv, 200, hd), float("nan"), dtype=torch.float32, device=dev())
+    m.kv_reset()
+    for layer in range(L):
+        m.kv_write(0, layer, nan, nan)
+    m.kv_truncate(0, 0)
+    dirty = prefill()
+    assert np.isfinite(dirty).all()
+    assert np.array_equal(clean, dirty)
+
+
 def test_refusals_leave_handle_usable():
     cfg, t, m = model_for("c1")
     V = cfg["vocab"]
