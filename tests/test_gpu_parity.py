@@ -689,6 +689,30 @@ def test_prefill_ignores_cache_rows_past_the_prompt(key):
     assert np.array_equal(clean, dirty)
 
 
+@pytest.mark.parametrize("key", ["qwen3_hd128_g2", "gemma_hd256_g4"])
+def test_one_token_prompt_and_a_full_cache(key):
+    """The degenerate lengths: a one-token prompt (one query, one key), then
+    decode up to exactly max_ctx positions, each row against the oracle; one
+    step more is refused before anything is enqueued, and the handle stays
+    usable."""
+    cfg, t, _ = model_for(key)
+    V, max_ctx = cfg["vocab"], 40
+    with qdec.Model(cfg, t, max_seqs=1, max_ctx=max_ctx) as m:
+        prompt = synth.prompt(cfg, 1, tag="one")
+        g_pl, g_dl, g_tok = run_gpu(m, cfg, prompt, max_ctx - 1)
+        o_pl, o_dl = oracle_run(cfg, t, prompt, g_tok, max_ctx - 1)
+        check_row(g_pl[0], o_pl[0])
+        for s in range(max_ctx - 1):
+            check_row(g_dl[s], o_dl[s])
+        assert m.kv_len(0) == max_ctx
+        lg = torch.empty((1, V), dtype=torch.float32, device=dev())
+        with pytest.raises(qdec.QdecError):
+            m.decode_step([1], lg, torch.empty(1, dtype=torch.int32, device=dev()))
+        with pytest.raises(qdec.QdecError):
+            m.prefill(0, [1], lg[0])
+        assert not m.poisoned and m.kv_len(0) == max_ctx
+
+
 def test_refusals_leave_handle_usable():
     cfg, t, m = model_for("c1")
     V = cfg["vocab"]
