@@ -10,10 +10,11 @@
 // one exp2.  Causal rule with a non-empty cache: the query at absolute position
 // p sees keys j <= p; sliding-window layers also need j > p - window.
 //
-// Layout: a lane group of head_dim/8 lanes owns one position (decode) or one
-// query (prefill); each lane holds 8 consecutive dims, so a group reads a K or V
-// row as one contiguous, coalesced segment.  Dot products finish with a DPP
-// tree inside the group.
+// Decode: a lane group of head_dim/8 lanes owns one position; each lane holds
+// 8 of its dims, so a group reads a K or V row as contiguous, coalesced
+// segments, and dot products finish with a DPP tree inside the group.
+// Prefill: 32 queries x 32 keys per tile on the matrix cores (layouts at the
+// kernels below).
 #pragma once
 #include <type_traits>
 
