@@ -52,7 +52,12 @@ struct GemmArgs {
 
 template <int QT, int MODE>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
-  constexpr int BM = 64, BN = 128, BK = 32;
+  // Q4_0 / Q8_0 stage two quant blocks between barriers (their decode is two
+  // instructions per value, so the staging stays cheap beside twice the
+  // products; 48 KB of LDS): half the barriers per product, 0.74-0.80 of the
+  // f32 MFMA peak on the 8B projections.  The other types stage one.
+  constexpr int NBS = (QT == kQ8_0 || QT == kQ4_0) ? 2 : 1;
+  constexpr int BM = 64, BN = 128, BK = 32 * NBS;
   // Columns XOR-swizzled within aligned 32-column blocks so that the staging
   // stores of a half-wave hit 32 distinct banks (X: four tokens x eight k
   // quads per half-wave; W: sixteen rows x the two k halves) while each MFMA
@@ -71,45 +76,63 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
   const int n0 = blockIdx.x * BN, t0 = blockIdx.y * BM;
   const int kp = a.nblk * 32;
 
+  const int nst = (a.nblk + NBS - 1) / NBS;  // stages
+
   // staging registers
-  float4 xa[2];
-  // rows past the matrix never load: their quant bytes and scale stay zero,
-  // which decodes to zeros without a select (Q4_0, Q8_0)
-  uint4 wq = make_uint4(0, 0, 0, 0);  // int8 layouts: 16 int8; F32 uses wf[4]; nibble layouts use the low 8 bytes
+  float4 xa[2 * NBS];
+  uint4 wq = make_uint4(0, 0, 0, 0);  // one-block types. int8 layouts: 16 int8; F32 uses wf[4]; nibble layouts the low 8 bytes
+  // Q4_0 / Q8_0, block j of the stage.  Rows past the matrix never load: their
+  // quant bytes and scale stay zero, which decodes to zeros without a select;
+  // a stage's missing second block (odd block counts) gets scale zero.  The
+  // scales stay raw fp16 bits until the stage is stored: converting them when
+  // they are loaded would make the wave wait for its loads right there.
+  uint4 wq2[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+  uint32_t wh2[2] = {0u, 0u};
+  bool wv2[2] = {false, false};
   float4 wf[4];
   float wd = 0.f, wmin = 0.f;  // block scale (Q6_K: of this thread's 16 values); Q4_K min
   uint32_t wks = 0, wkd = 0;   // K-quants: raw scale words, decoded when stored
   const int brow = tid >> 1, bhalf = tid & 1;
   const bool brow_ok = n0 + brow < a.rows;
 
+  // X of stage kb, register i: block i / 2 of the stage, token row
+  // (tid + 256 (i % 2)) / 8, k quad tid % 8 within the block (a half-wave
+  // stores four tokens x eight quads of one block: the bank-free pattern)
   auto load = [&](int kb) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      int idx = tid + 256 * i, row = idx >> 3, kq = idx & 7;
-      int t = t0 + row;
-      xa[i] = t < a.T ? *reinterpret_cast<const float4*>(a.x + (size_t)t * a.ldx + kb * BK + 4 * kq)
-                      : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = 0; i < 2 * NBS; ++i) {
+      const int idx = tid + 256 * (i & 1), row = idx >> 3, kq = (idx & 7) + 8 * (i >> 1);
+      const int t = t0 + row;
+      const bool ok = t < a.T && kb * NBS + (i >> 1) < a.nblk;
+      xa[i] = ok ? *reinterpret_cast<const float4*>(a.x + (size_t)t * a.ldx + kb * BK + 4 * kq)
+                 : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     if (brow_ok) {
       size_t r = n0 + brow;
-      if constexpr (int8_layout(QT)) {
-        wq = *reinterpret_cast<const uint4*>(a.qs + r * kp + kb * BK + 16 * bhalf);
-        if constexpr (QT == kQ8_0) {
-          wd = load_half(a.d + r * a.nblk + kb);
-        } else {
-          wks = (uint32_t)(int32_t)reinterpret_cast<const int8_t*>(a.d)[r * 2 * a.nblk + 2 * kb + bhalf];
-          wkd = a.sd[r * (a.nblk >> 3) + (kb >> 3)];
+      if constexpr (NBS == 2) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int b = min(2 * kb + j, a.nblk - 1);  // a missing second block reads the last one, scaled by 0
+          wh2[j] = a.d[r * a.nblk + b];
+          wv2[j] = 2 * kb + j < a.nblk;
+          if constexpr (QT == kQ8_0) {
+            wq2[j] = *reinterpret_cast<const uint4*>(a.qs + r * kp + b * 32 + 16 * bhalf);
+          } else {
+            const uint2 v = *reinterpret_cast<const uint2*>(a.qs + (r * a.nblk + b) * 16 + 8 * bhalf);
+            wq2[j].x = v.x;
+            wq2[j].y = v.y;
+          }
         }
-      } else if constexpr (nibble_layout(QT)) {
+      } else if constexpr (int8_layout(QT)) {
+        wq = *reinterpret_cast<const uint4*>(a.qs + r * kp + kb * BK + 16 * bhalf);  // Q6_K
+        wks = (uint32_t)(int32_t)reinterpret_cast<const int8_t*>(a.d)[r * 2 * a.nblk + 2 * kb + bhalf];
+        wkd = a.sd[r * (a.nblk >> 3) + (kb >> 3)];
+      } else if constexpr (nibble_layout(QT)) {  // Q4_K
         uint2 v = *reinterpret_cast<const uint2*>(a.qs + (r * a.nblk + kb) * 16 + 8 * bhalf);
         wq.x = v.x;
         wq.y = v.y;
-        if constexpr (QT == kQ4_0) {
-          wd = load_half(a.d + r * a.nblk + kb);
-        } else {
-          wks = a.d[r * a.nblk + kb];
-          wkd = a.sd[r * (a.nblk >> 3) + (kb >> 3)];
-        }
+        wks = a.d[r * a.nblk + kb];
+        wkd = a.sd[r * (a.nblk >> 3) + (kb >> 3)];
       } else {
         const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.qs) + r * kp + kb * BK + 16 * bhalf);
 #pragma unroll
@@ -120,8 +143,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
 
   auto store = [&]() {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      int idx = tid + 256 * i, row = idx >> 3, kq = idx & 7;
+    for (int i = 0; i < 2 * NBS; ++i) {
+      const int idx = tid + 256 * (i & 1), row = idx >> 3, kq = (idx & 7) + 8 * (i >> 1);
       As[4 * kq + 0][row ^ sa(4 * kq)] = xa[i].x;
       As[4 * kq + 1][row ^ sa(4 * kq + 1)] = xa[i].y;
       As[4 * kq + 2][row ^ sa(4 * kq + 2)] = xa[i].z;
@@ -134,31 +157,39 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
       wd = q6k_scale(wks, wkd);
     }
     if constexpr (QT == kQ8_0) {
-      const uint32_t w4[4] = {wq.x, wq.y, wq.z, wq.w};
-      const float cd = -128.f * wd;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t u = w4[j] ^ 0x80808080u;
-        Bs[16 * bhalf + 4 * j + 0][brow ^ sb(16 * bhalf + 4 * j + 0)] = dq_byte<0>(wd, cd, u);
-        Bs[16 * bhalf + 4 * j + 1][brow ^ sb(16 * bhalf + 4 * j + 1)] = dq_byte<1>(wd, cd, u);
-        Bs[16 * bhalf + 4 * j + 2][brow ^ sb(16 * bhalf + 4 * j + 2)] = dq_byte<2>(wd, cd, u);
-        Bs[16 * bhalf + 4 * j + 3][brow ^ sb(16 * bhalf + 4 * j + 3)] = dq_byte<3>(wd, cd, u);
+      for (int jb = 0; jb < 2; ++jb) {
+        const int k0 = 32 * jb + 16 * bhalf;  // block jb of the stage, this thread's half
+        const uint32_t w4[4] = {wq2[jb].x, wq2[jb].y, wq2[jb].z, wq2[jb].w};
+        const float d = wv2[jb] ? half_bits_to_float((uint16_t)wh2[jb]) : 0.f, cd = -128.f * d;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t u = w4[j] ^ 0x80808080u;
+          Bs[k0 + 4 * j + 0][brow ^ sb(k0 + 4 * j + 0)] = dq_byte<0>(d, cd, u);
+          Bs[k0 + 4 * j + 1][brow ^ sb(k0 + 4 * j + 1)] = dq_byte<1>(d, cd, u);
+          Bs[k0 + 4 * j + 2][brow ^ sb(k0 + 4 * j + 2)] = dq_byte<2>(d, cd, u);
+          Bs[k0 + 4 * j + 3][brow ^ sb(k0 + 4 * j + 3)] = dq_byte<3>(d, cd, u);
+        }
       }
     } else if constexpr (QT == kQ4_0) {
-      const uint32_t w2[2] = {wq.x, wq.y};
-      const float cd = -8.f * wd;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const uint32_t lo = w2[j] & 0x0f0f0f0fu, hi = (w2[j] >> 4) & 0x0f0f0f0fu;
-        const int i = 4 * j;
-        Bs[8 * bhalf + i + 0][brow ^ sb(8 * bhalf + i + 0)] = dq_byte<0>(wd, cd, lo);
-        Bs[8 * bhalf + i + 1][brow ^ sb(8 * bhalf + i + 1)] = dq_byte<1>(wd, cd, lo);
-        Bs[8 * bhalf + i + 2][brow ^ sb(8 * bhalf + i + 2)] = dq_byte<2>(wd, cd, lo);
-        Bs[8 * bhalf + i + 3][brow ^ sb(8 * bhalf + i + 3)] = dq_byte<3>(wd, cd, lo);
-        Bs[16 + 8 * bhalf + i + 0][brow ^ sb(16 + 8 * bhalf + i + 0)] = dq_byte<0>(wd, cd, hi);
-        Bs[16 + 8 * bhalf + i + 1][brow ^ sb(16 + 8 * bhalf + i + 1)] = dq_byte<1>(wd, cd, hi);
-        Bs[16 + 8 * bhalf + i + 2][brow ^ sb(16 + 8 * bhalf + i + 2)] = dq_byte<2>(wd, cd, hi);
-        Bs[16 + 8 * bhalf + i + 3][brow ^ sb(16 + 8 * bhalf + i + 3)] = dq_byte<3>(wd, cd, hi);
+      for (int jb = 0; jb < 2; ++jb) {
+        const int k0 = 32 * jb + 8 * bhalf;  // block jb, this thread's eight bytes (low nibbles k0.., high k0 + 16..)
+        const uint32_t w2[2] = {wq2[jb].x, wq2[jb].y};
+        const float d = wv2[jb] ? half_bits_to_float((uint16_t)wh2[jb]) : 0.f, cd = -8.f * d;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const uint32_t lo = w2[j] & 0x0f0f0f0fu, hi = (w2[j] >> 4) & 0x0f0f0f0fu;
+          const int i = k0 + 4 * j;
+          Bs[i + 0][brow ^ sb(i + 0)] = dq_byte<0>(d, cd, lo);
+          Bs[i + 1][brow ^ sb(i + 1)] = dq_byte<1>(d, cd, lo);
+          Bs[i + 2][brow ^ sb(i + 2)] = dq_byte<2>(d, cd, lo);
+          Bs[i + 3][brow ^ sb(i + 3)] = dq_byte<3>(d, cd, lo);
+          Bs[i + 16][brow ^ sb(i + 16)] = dq_byte<0>(d, cd, hi);
+          Bs[i + 17][brow ^ sb(i + 17)] = dq_byte<1>(d, cd, hi);
+          Bs[i + 18][brow ^ sb(i + 18)] = dq_byte<2>(d, cd, hi);
+          Bs[i + 19][brow ^ sb(i + 19)] = dq_byte<3>(d, cd, hi);
+        }
       }
     } else if constexpr (int8_layout(QT)) {
       uint32_t w4[4] = {wq.x, wq.y, wq.z, wq.w};
@@ -199,8 +230,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
   store();
   __syncthreads();
   const int li = lane & 31, lk = lane >> 5;
-  for (int kb = 0; kb < a.nblk; ++kb) {
-    if (kb + 1 < a.nblk) load(kb + 1);
+  for (int kb = 0; kb < nst; ++kb) {
+    if (kb + 1 < nst) load(kb + 1);
 #pragma unroll
     for (int p = 0; p < BK / 2; ++p) {
       const int k = 2 * p + lk;
@@ -211,7 +242,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
       acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b1, acc1, 0, 0, 0);
     }
     __syncthreads();  // every wave is done reading the stage
-    if (kb + 1 < a.nblk) store();
+    if (kb + 1 < nst) store();
     __syncthreads();
   }
 
@@ -271,7 +302,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_ksplit_kernel(GemmArgs a) {
   uint4 wq[2];
   float4 wf[8];
   float wd = 0.f, wd2 = 0.f, wmin = 0.f;  // scale (Q6_K: of values 0..15, wd2 of 16..31); Q4_K min
-  uint32_t wks = 0, wkd = 0;              // K-quants: raw scale words, decoded when stored
+  uint32_t wks = 0, wkd = 0;              // raw scale words (Q4_0 / Q8_0: the fp16 bits), decoded when stored
   const int brow = tid / NWV, bblk = tid % NWV;
   const bool brow_ok = n0 + brow < a.rows;
 
@@ -291,19 +322,15 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_ksplit_kernel(GemmArgs a) {
         wq[0] = p[0];
         wq[1] = p[1];
         if constexpr (QT == kQ8_0) {
-          wd = wd2 = load_half(a.d + r * a.nblk + kb);
+          wks = a.d[r * a.nblk + kb];
         } else {  // the two int8 scales of the block's 16-value halves
           wks = a.d[r * a.nblk + kb];
           wkd = a.sd[r * (a.nblk >> 3) + (kb >> 3)];
         }
       } else if constexpr (nibble_layout(QT)) {
         wq[0] = *reinterpret_cast<const uint4*>(a.qs + (r * a.nblk + kb) * 16);
-        if constexpr (QT == kQ4_0) {
-          wd = load_half(a.d + r * a.nblk + kb);
-        } else {
-          wks = a.d[r * a.nblk + kb];
-          wkd = a.sd[r * (a.nblk >> 3) + (kb >> 3)];
-        }
+        wks = a.d[r * a.nblk + kb];
+        if constexpr (QT == kQ4_K) wkd = a.sd[r * (a.nblk >> 3) + (kb >> 3)];
       } else {
         const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.qs) + r * kp + kb * 32);
 #pragma unroll
@@ -329,7 +356,9 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_ksplit_kernel(GemmArgs a) {
       As[4 * kq + 3][c] = xa[i].w;
     }
     const int kk = bblk * 32, bc = brow ^ (SW * bblk);
-    if constexpr (QT == kQ4_K) {
+    if constexpr (QT == kQ8_0 || QT == kQ4_0) {
+      wd = half_bits_to_float((uint16_t)wks);  // zero bits (rows or blocks past the matrix): 0
+    } else if constexpr (QT == kQ4_K) {
       wd = q4k_scale(wks, wkd);
       wmin = q4k_min(wks, wkd);
     } else if constexpr (QT == kQ6_K) {
@@ -487,7 +516,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs a) {
   // staging: X row tid / 4, k (tid % 4) * 8 .. +8; W row tid / 2, k (tid % 2) * 16 .. +16
   float4 xa[2];
   uint4 wq;
-  float wd = 0.f;
+  uint32_t wh = 0u;  // the block's fp16 scale bits, converted when stored
   const int xrow = tid >> 2, xk = (tid & 3) * 8;
   const int brow = tid >> 1, bhalf = tid & 1;
   const bool brow_ok = n0 + brow < a.rows;
@@ -505,10 +534,10 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs a) {
       const size_t r = n0 + brow;
       if constexpr (QT == kQ8_0) wq = *reinterpret_cast<const uint4*>(a.qs + r * kp + kb * BK + 16 * bhalf);
       else wq = *reinterpret_cast<const uint4*>(a.qs + (r * a.nblk + kb) * 16);
-      wd = load_half(a.d + r * a.nblk + kb);
+      wh = a.d[r * a.nblk + kb];
     } else {
       wq = make_uint4(0, 0, 0, 0);
-      wd = 0.f;
+      wh = 0u;
     }
   };
 
@@ -541,7 +570,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs a) {
     if (!brow_ok) q0 = q1 = bf16x8{};
     *reinterpret_cast<bf16x8*>(&Bs[buf][brow][16 * bhalf]) = q0;
     *reinterpret_cast<bf16x8*>(&Bs[buf][brow][16 * bhalf + 8]) = q1;
-    if (bhalf == 0) Ds[buf][brow] = wd;
+    if (bhalf == 0) Ds[buf][brow] = half_bits_to_float((uint16_t)wh);
   };
 
   f32x16 acc[2], blk[2];

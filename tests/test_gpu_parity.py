@@ -292,6 +292,9 @@ MATMUL_CASES = [
     # prefill tiles: >= 512 tiles of 64 x 128 (ragged rows and tokens) take the
     # wide tile; fewer take the K-split 32 x 64 tile (partial last K stage)
     (synth.T_Q8_0, 4100, 320, 1030), (synth.T_Q4_0, 4224, 288, 1000),
+    # Q4_0 / Q8_0 wide tiles stage block pairs: an odd block count leaves the
+    # last stage half empty (Q4_0 above: 9 blocks; Q8_0 here: 11)
+    (synth.T_Q8_0, 4100, 352, 1000),
     (synth.T_Q4_0, 200, 720, 40), (synth.T_F32, 96, 300, 33), (synth.T_Q8_0, 1030, 1000, 97),
     # long rows with >= 2048 row groups: eight-wave workgroups (ragged rows)
     (synth.T_Q4_0, 4100, 8192, 1), (synth.T_Q4_0, 4097, 4608, 2), (synth.T_Q8_0, 4100, 2080, 3),
