@@ -519,7 +519,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnPrefillAr
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = key0 + 8 * (r >> 2) + 4 * lk + (r & 3);
-        sacc[r] = (key >= k_lo) & (key <= k_hi) ? sacc[r] : -INFINITY;
+        sacc[r] = ((key >= k_lo) & (key <= k_hi)) ? sacc[r] : -INFINITY;
       }
     }
     float mt = -INFINITY;
@@ -718,7 +718,7 @@ __global__ __launch_bounds__(256) void attn_prefill_dsplit_kernel(AttnPrefillArg
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = key0 + 8 * (r >> 2) + 4 * lk + (r & 3);
-        sc[r] = (key >= k_lo) & (key <= k_hi) ? sc[r] : -INFINITY;
+        sc[r] = ((key >= k_lo) & (key <= k_hi)) ? sc[r] : -INFINITY;
       }
     }
     float mt = -INFINITY;

@@ -86,20 +86,38 @@ void gemv_dispatch_mode(int mode, dim3 grid, size_t lds, hipStream_t st, const G
 //   2: one gate/up pair per wave, four-wave workgroups (pair modes, up to
 //      four input rows);
 //   3: two gate/up pairs per wave, four-wave workgroups (pair modes, eight or
-//      sixteen input rows).
+//      sixteen input rows);
+//   4: one row per wave, sixteen-wave workgroups (one input row, store / add,
+//      4,096 rows or more, rows of 8,192 inputs or more): a CU stages the long
+//      input row once for twice the waves of class 1 (the 8B down projection
+//      10.1 -> 9.4 us).
 // LDS budget of the GEMV's staged input rows (the CU has 160 KB; the rest is
 // left for the kernel's own small arrays).
 constexpr size_t kGemvLdsMax = 128 * 1024;
 
-inline int gemv_tile_class(bool pair, int rows, int m) { return pair ? (m <= 4 ? 2 : 3) : (rows >= 4096 ? 1 : 0); }
-inline int class_rows(int c) { return c == 0 ? 1 : (c == 3 ? 4 : 2); }
-inline int class_waves(int c) { return c == 1 ? 8 : 4; }
+// plain: no residual prologue, no attention-accumulator input, no fused argmax
+inline int gemv_tile_class(bool pair, int rows, int m, int kp, bool plain) {
+  if (!pair && m == 1 && rows >= 4096 && kp >= 8192 && plain) return 4;
+  return pair ? (m <= 4 ? 2 : 3) : (rows >= 4096 ? 1 : 0);
+}
+inline int class_rows(int c) { return (c == 0 || c == 4) ? 1 : (c == 3 ? 4 : 2); }
+inline int class_waves(int c) { return c == 4 ? 16 : (c == 1 ? 8 : 4); }
 
 template <int QT, int M>
 void gemv_dispatch_class(int cls, int mode, dim3 grid, size_t lds, hipStream_t st, const GemvArgs& a) {
   switch (cls) {
     case 0: gemv_dispatch_mode<QT, M, 1, 1, 4, false>(mode, grid, lds, st, a); break;
     case 1: gemv_dispatch_mode<QT, M, 2, 1, 8, false>(mode, grid, lds, st, a); break;
+    case 4:  // plain store / add only (see gemv_tile_class)
+      if constexpr (M == 1) {
+        if (a.res_add || a.xd || a.amax_v) throw HipError{"gemv: tile class 4 takes plain inputs only"};
+        if (mode == kModeAdd) qlaunch(gemv_kernel<QT, 1, kModeAdd, 1, 1, 16, false>, grid, 1024, lds, st, a);
+        else if (mode == kModeStore) qlaunch(gemv_kernel<QT, 1, kModeStore, 1, 1, 16, false>, grid, 1024, lds, st, a);
+        else throw HipError{"gemv: tile class 4 takes the store and add epilogues"};
+      } else {
+        throw HipError{"gemv: tile class 4 takes one input row"};
+      }
+      break;
     case 2:
       if constexpr (M <= 4) gemv_dispatch_mode<QT, M, 2, 1, 4, true>(mode, grid, lds, st, a);
       else throw HipError{"gemv: tile class 2 takes at most four input rows"};

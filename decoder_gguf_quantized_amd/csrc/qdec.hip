@@ -315,7 +315,7 @@ int gemv(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, c
     const int mr = std::min(cap, nrows - r0);
     int M = 1;
     while (M < mr) M *= 2;
-    const int cls = gemv_tile_class(pair, w.rows, M);
+    const int cls = gemv_tile_class(pair, w.rows, M, kp, !res.add && !acc.o && !amax);
     const int R = class_rows(cls), NW = class_waves(cls);
     const int ngroups = pair ? w.rows / R : (w.rows + R - 1) / R;
     // waves stay resident and loop: at most four workgroups per CU, so the

@@ -296,6 +296,9 @@ MATMUL_CASES = [
     # last stage half empty (Q4_0 above: 9 blocks; Q8_0 here: 11)
     (synth.T_Q8_0, 4100, 352, 1000),
     (synth.T_Q4_0, 200, 720, 40), (synth.T_F32, 96, 300, 33), (synth.T_Q8_0, 1030, 1000, 97),
+    # one input row, >= 4,096 rows of >= 8,192 inputs: sixteen-wave workgroups
+    # of one row per wave (ragged rows; Q4_0 in the next group)
+    (synth.T_Q8_0, 4097, 9216, 1), (synth.T_Q4_K, 4100, 8448, 1), (synth.T_Q6_K, 4099, 8192, 1),
     # long rows with >= 2048 row groups: eight-wave workgroups (ragged rows)
     (synth.T_Q4_0, 4100, 8192, 1), (synth.T_Q4_0, 4097, 4608, 2), (synth.T_Q8_0, 4100, 2080, 3),
     (synth.T_F32, 4100, 600, 5),
