@@ -90,7 +90,8 @@ void gemv_dispatch_mode(int mode, dim3 grid, size_t lds, hipStream_t st, const G
 //   4: one row per wave, sixteen-wave workgroups (one input row, store / add,
 //      4,096 rows or more, rows of 8,192 inputs or more): a CU stages the long
 //      input row once for twice the waves of class 1 (the 8B down projection
-//      10.1 -> 9.4 us).
+//      10.1 -> 9.4 us; the same shape for the gate/up pairs, which are bound
+//      by their vector arithmetic, measured 13.5 -> 15.6 us).
 // LDS budget of the GEMV's staged input rows (the CU has 160 KB; the rest is
 // left for the kernel's own small arrays).
 constexpr size_t kGemvLdsMax = 128 * 1024;

@@ -322,7 +322,7 @@ int gemv(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, c
     // input staging of each workgroup is amortised over many row groups;
     // enough waves that none finishes more than 64 outputs (each wave holds
     // its outputs in one register, a lane per output, until it is done)
-    const int grid_cap = 1024;
+    const int grid_cap = NW == 16 ? 256 : 1024;  // sixteen-wave workgroups: one per CU
     const int per_wave = 64 / (pair ? R / 2 : R);  // row groups per wave at most
     const int grid_min = (ngroups + per_wave * NW - 1) / (per_wave * NW);
     dim3 grid(std::max({1, grid_min, std::min((ngroups + NW - 1) / NW, grid_cap)}));
