@@ -47,6 +47,9 @@ struct AttnDecodeArgs {
   int* err;             // host-mapped error word (2: a chunk's scores beyond the merge's range)
   const int* seq;       // [B] sequence slot of each row, or null (row b is sequence b)
   KvMap map;            // cache layout (the paged kernel reads map.table)
+  int gsplit;           // workgroups per KV head (1, or 2: eight query heads per KV head run as
+                        // two groups of four, each streaming the head's cache; a group of eight
+                        // holds more registers than the SIMD has and spills)
 };
 
 // Most position chunks per (sequence, KV head); the launcher sizes chunks so
@@ -151,7 +154,9 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
   __shared__ float sm_o[4][G][HD];
   __shared__ float sm_m[4][G], sm_l[4][G];
 
-  const int c = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  // g: the workgroup's group of G query heads (heads g G .. g G + G - 1), kvh
+  // their KV head
+  const int c = blockIdx.x, g = blockIdx.y, s = blockIdx.z, kvh = g / a.gsplit;
   const int tid = threadIdx.x, gi = tid / LG, li = tid % LG;
   const float* row = a.qkv + (size_t)s * a.ldqkv;
   const int sq = a.seq ? a.seq[s] : s;
@@ -163,12 +168,12 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
   if constexpr (PAGED) {
     const int pi = cb >> a.map.log2p;
     const int pg = a.map.table[sq * a.map.tw + pi];
-    head_base = (((size_t)pg * a.nkv + g) << a.map.log2p) - ((size_t)pi << a.map.log2p);
+    head_base = (((size_t)pg * a.nkv + kvh) << a.map.log2p) - ((size_t)pi << a.map.log2p);
   } else if (a.map.ring) {
-    head_base = ((size_t)sq * a.nkv + g) << a.map.ring;
+    head_base = ((size_t)sq * a.nkv + kvh) << a.map.ring;
     pmask = (1 << a.map.ring) - 1;
   } else {
-    head_base = ((size_t)sq * a.nkv + g) * a.ctx;
+    head_base = ((size_t)sq * a.nkv + kvh) * a.ctx;
   }
   const bool spec = a.window == 0;
 
@@ -195,8 +200,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
   load_lane8(qkn ? a.q_norm : row, HD, li, wq);
   load_lane8(qkn ? a.k_norm : row, HD, li, wk);
   float kn[8], vn[8];
-  load_lane8(row + (size_t)(a.nq + g) * HD, HD, li, kn);
-  load_lane8(row + (size_t)(a.nq + a.nkv + g) * HD, HD, li, vn);
+  load_lane8(row + (size_t)(a.nq + kvh) * HD, HD, li, kn);
+  load_lane8(row + (size_t)(a.nq + a.nkv + kvh) * HD, HD, li, vn);
   // keys/values of positions j0 and j0 + NG (addresses clamped into the cache;
   // positions outside [start, end) are masked when accumulated)
   auto fetch_pair = [&](int j0, float (&k)[2][8], float (&v)[2][8]) {
@@ -339,7 +344,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
   __syncthreads();
   // every load of the kernel has been waited for: now the stores (the new key
   // and value into the cache, for the next steps; the other parity's clear)
-  if (has_new && gi == 0) {
+  if (has_new && gi == 0 && g % a.gsplit == 0) {  // one writer per KV head
     store_lane8(a.kc + (head_base + (p & pmask)) * HD, HD, li, kn);
     store_lane8(a.vc + (head_base + (p & pmask)) * HD, HD, li, vn);
   }

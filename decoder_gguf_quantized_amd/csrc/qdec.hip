@@ -404,9 +404,7 @@ void attn_decode_hd(int G, dim3 grid, hipStream_t st, const AttnDecodeArgs& a) {
     case 1: qlaunch(attn_decode_kernel<HD, 1, PAGED>, grid, 256, 0, st, a); break;
     case 2: qlaunch(attn_decode_kernel<HD, 2, PAGED>, grid, 256, 0, st, a); break;
     case 4: qlaunch(attn_decode_kernel<HD, 4, PAGED>, grid, 256, 0, st, a); break;
-    default:
-      if constexpr (HD == 128) qlaunch(attn_decode_kernel<HD, 8, PAGED>, grid, 256, 0, st, a);
-      break;
+    default: throw HipError{"attention: query heads per KV head per workgroup must be 1, 2 or 4"};
   }
 }
 
@@ -461,7 +459,7 @@ void attention_decode(qdec_model* m, hipStream_t st, int l, int B, bool slotted)
                    m->rope_cur + (L.global ? 0 : (size_t)m->max_seqs * (hd / 2)), scale_log2,
                    m->acc + (size_t)(l % 2) * kAccCopies * m->acc_blk,
                    m->acc + (size_t)((l + 1) % 2) * kAccCopies * m->acc_blk, m->max_seqs, m->err_dev,
-                   slotted ? m->d_seq : nullptr, m->lmap(l)};
+                   slotted ? m->d_seq : nullptr, m->lmap(l), G == 8 ? 2 : 1};
   double kvbytes = 0;
   for (int s = 0; s < B; ++s) {
     int p = m->kvlen[(size_t)s < m->row_seq.size() ? m->row_seq[s] : s];
@@ -470,11 +468,12 @@ void attention_decode(qdec_model* m, hipStream_t st, int l, int B, bool slotted)
   }
   {
     Timed tm(m, st, "attn_decode", kvbytes + (double)B * m->nqkv * 4, 4.0 * kvbytes / 8 * G);
-    dim3 grid(m->nchunk, c.n_head_kv, B);
+    dim3 grid(m->nchunk, c.n_head_kv * a.gsplit, B);
     const bool pg = m->page_size > 0;
-    if (hd == 64) pg ? attn_decode_hd<64, true>(G, grid, st, a) : attn_decode_hd<64, false>(G, grid, st, a);
-    else if (hd == 128) pg ? attn_decode_hd<128, true>(G, grid, st, a) : attn_decode_hd<128, false>(G, grid, st, a);
-    else pg ? attn_decode_hd<256, true>(G, grid, st, a) : attn_decode_hd<256, false>(G, grid, st, a);
+    const int Gw = G / a.gsplit;  // query heads per workgroup
+    if (hd == 64) pg ? attn_decode_hd<64, true>(Gw, grid, st, a) : attn_decode_hd<64, false>(Gw, grid, st, a);
+    else if (hd == 128) pg ? attn_decode_hd<128, true>(Gw, grid, st, a) : attn_decode_hd<128, false>(Gw, grid, st, a);
+    else pg ? attn_decode_hd<256, true>(Gw, grid, st, a) : attn_decode_hd<256, false>(Gw, grid, st, a);
   }
 }
 
