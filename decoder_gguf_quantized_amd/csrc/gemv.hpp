@@ -196,6 +196,7 @@ QD_DEV void gemv_stage_x(const GemvArgs& a, float4* xs4, int kp, float (&scale)[
   // workgroup-uniform test), so short rows issue no extra loads.
   constexpr int JB = RES ? (M >= 2 ? 1 : 2) : (M >= 8 ? 1 : 8 / M);
   const int NU = kp / US, NK4 = kp / 4;
+  [[maybe_unused]] float* xsum = reinterpret_cast<float*>(xs4 + M * NK4);  // nibble layouts: [M][nblk] block sums
   __shared__ float red[NW][M];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool norm = a.norm_w != nullptr;
@@ -287,14 +288,24 @@ QD_DEV void gemv_stage_x(const GemvArgs& a, float4* xs4, int kp, float (&scale)[
     for (int j = 0; j < JB; ++j) {
       if (b0 + NT * j >= NK4) break;
       const int k4 = b0 + NT * j + tid;
-      if (k4 < NK4) {
-        const int slot = (k4 % NV) * NU + k4 / NV;
+      const bool ok = k4 < NK4;
+      const int slot = (k4 % NV) * NU + k4 / NV;
 #pragma unroll
-        for (int mi = 0; mi < M; ++mi) {
-          const float4 v = xv[j][mi], w = wv[j];
+      for (int mi = 0; mi < M; ++mi) {
+        const float4 v = xv[j][mi], w = wv[j];
+        const float4 p = make_float4(v.x * w.x, v.y * w.y, v.z * w.z, v.w * w.w);
+        if (ok) {
           if (write_h && mi < a.m) o4[(size_t)mi * ldx4 + k4] = v;
           ss[mi] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-          xs4[mi * NK4 + slot] = make_float4(v.x * w.x, v.y * w.y, v.z * w.z, v.w * w.w);
+          xs4[mi * NK4 + slot] = p;
+        }
+        if constexpr (nibble_layout(QT)) {
+          // the block sums of the staged values: a block's eight float4 are
+          // the k4 of eight consecutive lanes (NT and b0 are multiples of 64;
+          // lanes past the row hold zeros and whole blocks, kp being a
+          // multiple of 32); all lanes take part in the lane sums
+          const float bsum = group_sum<8>(ok ? (p.x + p.y) + (p.z + p.w) : 0.f);
+          if (ok && k4 % NV == 0) xsum[mi * (NK4 / NV) + k4 / NV] = bsum;
         }
       }
     }
@@ -582,20 +593,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(GemvArgs a) {
     request(std::integral_constant<int, 0>{});
     if constexpr (NS > 2) request(std::integral_constant<int, 1>{});
     if constexpr (NS > 3) request(std::integral_constant<int, 2>{});
-  });  // ends with a barrier
-  if constexpr (nibble_layout(QT)) {
-    for (int i = threadIdx.x; i < M * a.nblk; i += 64 * NW) {
-      const int mi = i / a.nblk, u = i % a.nblk;
-      float s = 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float4 v = xs4[(mi * 8 + j) * a.nblk + u];
-        s += (v.x + v.y) + (v.z + v.w);
-      }
-      xsum[i] = s;
-    }
-    __syncthreads();
-  }
+  });  // ends with a barrier (the staged rows and, for nibble layouts, their block sums)
 
   float acc[R][M];
 #pragma unroll
