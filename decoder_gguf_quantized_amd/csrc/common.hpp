@@ -109,6 +109,25 @@ QD_DEV float wave_sum(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// Two full-wave sums at once: every even lane receives the sum of a0 over the
+// 64 lanes, every odd lane that of a1.  One exchange between lanes l and l ^ 1
+// puts each value's pair sums into one register (even lanes a0's, odd lanes
+// a1's), so the rest of the tree runs once: lanes l ^ 2, the quads of a row
+// (rotations by 4 and 8, which keep the parity), then the rows (gfx950's row
+// swaps, plain VALU instructions).
+QD_DEV float pair_wave_sum(float a0, float a1, int lane) {
+  const bool odd = lane & 1;
+  const float keep = odd ? a1 : a0, send = odd ? a0 : a1;
+  float t = keep + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send), 0xB1, 0xf, 0xf, true));
+  t = dpp_add<0x4E>(t);   // quad_perm [2,3,0,1]: lanes l ^ 2
+  t = dpp_add<0x124>(t);  // row_ror:4: the neighbouring quad
+  t = dpp_add<0x128>(t);  // row_ror:8: the other two quads
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+  t = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 QD_DEV float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;

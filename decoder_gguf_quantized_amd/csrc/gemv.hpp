@@ -492,6 +492,21 @@ QD_DEV void gemv_group_end(const float (&scale)[M], float (&acc)[R][M], float (&
   constexpr bool kPair = MODE == kModePairSilu || MODE == kModePairGelu;
 #pragma unroll
   for (int mi = 0; mi < M; ++mi) {
+    if constexpr (R == 2) {
+      // both rows in one lane tree: lanes of parity i hold row i's sum
+      const float t = pair_wave_sum(acc[0][mi], acc[1][mi], lane) * scale[mi];
+      float v;
+      if constexpr (kPair) {  // (gate, up) = rows (0, 1); lane nslot takes the output
+        const float u = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(t), 0xB1, 0xf, 0xf, true));
+        const float gate = (lane & 1) ? u : t, up = (lane & 1) ? t : u;
+        v = (MODE == kModePairSilu ? act_silu(gate) : act_gelu_tanh(gate)) * up;
+        if (lane == nslot) obuf[mi] = v;
+      } else {  // rows 0 and 1 into lanes nslot and nslot + 1 (nslot is even)
+        if ((lane & ~1) == nslot) obuf[mi] = t;
+      }
+      acc[0][mi] = acc[1][mi] = 0.f;
+      continue;
+    }
     float sv[R];
 #pragma unroll
     for (int i = 0; i < R; ++i) sv[i] = wave_sum(acc[i][mi]) * scale[mi];
