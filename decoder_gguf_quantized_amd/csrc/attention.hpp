@@ -110,10 +110,9 @@ QD_DEV void store_lane8(float* rowp, int hd, int li, const float (&v)[8]) {
 }
 
 // Workgroup = (chunk of positions, KV head, sequence); it serves the KV head's
-// whole group of query heads (eight heads per KV head: two workgroups of four,
-// gsplit).  Prologue: QK-norm + RoPE of the group's queries and of the new
-// key; the chunk that holds the new position also appends the new key and
-// value to the cache.
+// whole group of query heads.  Prologue: QK-norm + RoPE of the group's queries
+// and of the new key; the chunk that holds the new position also appends the
+// new key and value to the cache.
 //
 // Merge without a second round trip.  A split softmax needs a common reference
 // for the chunks' maxima.  Every workgroup can compute the same one without
