@@ -131,6 +131,22 @@ def test_paged_cache_is_bit_identical_to_the_contiguous_one(qwen3_pair):
     run_schedule(paged, cfg, om, pages=True)
 
 
+def test_paged_eight_heads_per_kv_head_matches_the_oracle():
+    """Eight query heads per KV head run decode attention as two workgroups of
+    four per KV head, which both place the KV head's rows (one of them appends
+    the new key and value): the batching schedule on a paged cache, every
+    logits row against the oracle."""
+    cfg = dict(SMALL["gqa8_hd128"])
+    t = synth.generate(cfg)
+    m = qdec.Model(cfg, t, max_seqs=4, max_ctx=256)
+    try:
+        m.kv_paged(64, 12)
+        om = OracleModel(cfg, t, max_ctx=256, n_seqs=4)
+        run_schedule(m, cfg, om, pages=True)
+    finally:
+        m.close()
+
+
 def test_paged_window_model_matches_the_oracle():
     """head_dim 256 (decode chunk 32), window 8, pages of 32: prefill tiles of
     16 keys on window layers start anywhere and straddle pages."""

@@ -299,6 +299,7 @@ MATMUL_CASES = [
     # one input row, >= 4,096 rows of >= 8,192 inputs: sixteen-wave workgroups
     # of one row per wave (ragged rows; Q4_0 in the next group)
     (synth.T_Q8_0, 4097, 9216, 1), (synth.T_Q4_K, 4100, 8448, 1), (synth.T_Q6_K, 4099, 8192, 1),
+    (synth.T_F32, 4096, 8192, 1),
     # long rows with >= 2048 row groups: eight-wave workgroups (ragged rows)
     (synth.T_Q4_0, 4100, 8192, 1), (synth.T_Q4_0, 4097, 4608, 2), (synth.T_Q8_0, 4100, 2080, 3),
     (synth.T_F32, 4100, 600, 5),
