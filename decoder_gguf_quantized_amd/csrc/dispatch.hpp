@@ -96,6 +96,17 @@ void gemv_dispatch_mode(int mode, dim3 grid, size_t lds, hipStream_t st, const G
 // left for the kernel's own small arrays).
 constexpr size_t kGemvLdsMax = 128 * 1024;
 
+// Tile class of the matrix-core decode (gemv_mfma_kernel): 9..16 input rows
+// of Q4_0 / Q8_0 weights with plain inputs and at least 2,048 outputs (128
+// workgroups), launched as M = 16 with one workgroup per 16 outputs and no
+// LDS staging.  Fewer outputs leave most CUs without a workgroup: the
+// 0.6B-shape down projection (1,024 outputs, 64 workgroups) took 17.6 us
+// against 16.8 us for two eight-row launches of the lane-tree kernel.
+constexpr int kGemvMfmaClass = 8;
+inline bool gemv_mfma_fits(int type, int rows_in, int nout, bool plain) {
+  return (type == kQ4_0 || type == kQ8_0) && rows_in >= 9 && rows_in <= 16 && nout >= 2048 && plain;
+}
+
 // plain: no residual prologue, no attention-accumulator input, no fused argmax
 inline int gemv_tile_class(bool pair, int rows, int m, int kp, bool plain) {
   if (!pair && m == 1 && rows >= 4096 && kp >= 8192 && plain) return 4;
@@ -109,6 +120,19 @@ void gemv_dispatch_class(int cls, int mode, dim3 grid, size_t lds, hipStream_t s
   switch (cls) {
     case 0: gemv_dispatch_mode<QT, M, 1, 1, 4, false>(mode, grid, lds, st, a); break;
     case 1: gemv_dispatch_mode<QT, M, 2, 1, 8, false>(mode, grid, lds, st, a); break;
+    case kGemvMfmaClass:  // 9..16 input rows on the matrix cores (Q4_0 / Q8_0, plain inputs)
+      if constexpr (M == 16 && (QT == kQ4_0 || QT == kQ8_0)) {
+        if (a.res_add || a.xd || a.amax_v) throw HipError{"gemv: the matrix-core decode takes plain inputs only"};
+        switch (mode) {
+          case kModeStore: qlaunch(gemv_mfma_kernel<QT, kModeStore>, grid, 256, 0, st, a); break;
+          case kModeAdd: qlaunch(gemv_mfma_kernel<QT, kModeAdd>, grid, 256, 0, st, a); break;
+          case kModePairSilu: qlaunch(gemv_mfma_kernel<QT, kModePairSilu>, grid, 256, 0, st, a); break;
+          default: qlaunch(gemv_mfma_kernel<QT, kModePairGelu>, grid, 256, 0, st, a); break;
+        }
+      } else {
+        throw HipError{"gemv: the matrix-core decode takes Q4_0 / Q8_0 weights and sixteen input rows"};
+      }
+      break;
     case 4:  // plain store / add only (see gemv_tile_class)
       if constexpr (M == 1) {
         if (a.res_add || a.xd || a.amax_v) throw HipError{"gemv: tile class 4 takes plain inputs only"};

@@ -20,23 +20,6 @@
 
 namespace qd {
 
-// Q4_0 / Q8_0 decode from unsigned bytes: with u = q + c (c = 8 for a nibble,
-// 128 for an int8 byte with its sign bit flipped), d q = fma(d, u, -c d).  Both
-// products are exact in f32 (an fp16 scale times an integer below 2^8), and so
-// is their difference, so the fma rounds nothing and the value equals d * q
-// (an exact zero comes out +0).  Byte E of w converts in one instruction
-// (V_CVT_F32_UBYTE0..3, written out: the compiler would otherwise extract a
-// masked nibble with a bit-field instruction first).
-template <int E>
-QD_DEV float dq_byte(float d, float cd, uint32_t w) {
-  float f;
-  if constexpr (E == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(f) : "v"(w));
-  else if constexpr (E == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(f) : "v"(w));
-  else if constexpr (E == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(f) : "v"(w));
-  else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(f) : "v"(w));
-  return fmaf(d, f, cd);
-}
-
 struct GemmArgs {
   const uint8_t* qs;    // weights, same layout as GemvArgs
   const uint16_t* d;

@@ -144,6 +144,23 @@ QD_DEV float act_gelu_tanh(float x) {
 // rows [32b, 32b+32) and [64b+32, 64b+64) the matching up rows.
 QD_DEV int pair_gate_row(int n) { return (n >> 5) * 64 + (n & 31); }
 
+// Q4_0 / Q8_0 decode from unsigned bytes: with u = q + c (c = 8 for a nibble,
+// 128 for an int8 byte with its sign bit flipped), d q = fma(d, u, -c d).  Both
+// products are exact in f32 (an fp16 scale times an integer below 2^8), and so
+// is their difference, so the fma rounds nothing and the value equals d * q
+// (an exact zero comes out +0).  Byte E of w converts in one instruction
+// (V_CVT_F32_UBYTE0..3, written out: the compiler would otherwise extract a
+// masked nibble with a bit-field instruction first).
+template <int E>
+QD_DEV float dq_byte(float d, float cd, uint32_t w) {
+  float f;
+  if constexpr (E == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(f) : "v"(w));
+  else if constexpr (E == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(f) : "v"(w));
+  else if constexpr (E == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(f) : "v"(w));
+  else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(f) : "v"(w));
+  return fmaf(d, f, cd);
+}
+
 QD_DEV float dot16_q8(uint4 w, const float4& a, const float4& b, const float4& c, const float4& e) {
   float s = 0.f;
   s += (float)(int8_t)(w.x) * a.x;
@@ -669,6 +686,190 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(GemvArgs a) {
         a.amax_i[(size_t)mi * nwaves + gwave] = bi[mi];
       }
     }
+  }
+}
+
+// ------------------------------------------------------------ batched decode on the matrix cores
+// Decode projection of 9..16 input rows (a decode batch), Q4_0 / Q8_0
+// weights: y[m][n] = sum_k W[n][k] x[m][k] on V_MFMA_F32_16X16X4F32 (f32
+// operands, f32 accumulation), with the weights decoded exactly in registers
+// (d q, dq_byte) and the inputs read straight from global memory (no LDS
+// staging, so rows of any length take all 16 inputs in one launch).  With the
+// lane-tree GEMV, sixteen inputs cost two wave reductions per row and input
+// and sixteen FMAs per weight on the vector ALU; here the matrix cores do the
+// products and the sums over k.
+//
+// Workgroup = 16 outputs (pair modes: 16 (gate, up) pairs), four waves
+// splitting K in groups of four quant blocks (wave w takes groups w, w + 4,
+// ...).  Lane l = i + 16 q: weight row i and input row i of the tile, block q
+// of the group.  The contraction index of MFMA step s is (block q, element s):
+// lane (i, q) supplies A[i][q] = W[row i][(4g + q) 32 + s] and B[q][i] =
+// x[i][(4g + q) 32 + s], so each lane reads one whole block of its row and 32
+// consecutive inputs.  D[n][m] (output row n, input m) lands in register r of
+// lane m + 16 (n / 4), r = n % 4.  The waves' partial tiles, and for the
+// RMSNorm prologue the partial sums of squares, meet in LDS; wave 0 applies
+// the norm scale (1 / rms, as the lane-tree kernel does: the gains multiply the
+// inputs, the scale the sums) and the epilogue.
+template <int QT, int MODE>
+__global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
+  static_assert(QT == kQ4_0 || QT == kQ8_0, "matrix-core decode: Q4_0 and Q8_0");
+  constexpr bool kPair = MODE == kModePairSilu || MODE == kModePairGelu;
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  __shared__ f32x4 red[4][kPair ? 2 : 1][64];
+  __shared__ float rss[4][64];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i = lane & 15, q = lane >> 4;
+  const int n0 = blockIdx.x * 16;  // first output of the tile
+  const int nout = kPair ? a.rows / 2 : a.rows;
+  const int kp = a.nblk * 32;
+  const int ngrp = (a.nblk + 3) / 4;
+  // weight rows of lane i (clamped into the matrix: rows past it are not stored)
+  int row, row_up = 0;
+  if constexpr (kPair) {
+    row = pair_gate_row(min(n0 + i, nout - 1));
+    row_up = row + 32;
+  } else {
+    row = min(n0 + i, a.rows - 1);
+  }
+  const bool xin = i < a.m;  // input row i exists
+  const float* xrow = a.x + (size_t)min(i, a.m - 1) * a.ldx;
+  const bool norm = a.norm_w != nullptr;
+  const float* grow = norm ? a.norm_w : xrow;  // without a norm the row stands in, unused
+
+  struct Regs {
+    uint4 w[QT == kQ8_0 ? 2 : 1], wu[kPair ? (QT == kQ8_0 ? 2 : 1) : 1];
+    uint32_t d, du;
+    float4 x[8], g[8];
+  };
+  // loads of group g into R (every lane issues the same loads: blocks past
+  // the row are read at the last block and zeroed when used)
+  auto load = [&](int g, Regs& R) {
+    const int kb = min(4 * g + q, a.nblk - 1);
+    if constexpr (QT == kQ8_0) {
+      const uint4* p = reinterpret_cast<const uint4*>(a.qs + (size_t)row * kp + kb * 32);
+      R.w[0] = load_nt(p);
+      R.w[1] = load_nt(p + 1);
+      if constexpr (kPair) {
+        const uint4* pu = reinterpret_cast<const uint4*>(a.qs + (size_t)row_up * kp + kb * 32);
+        R.wu[0] = load_nt(pu);
+        R.wu[1] = load_nt(pu + 1);
+      }
+    } else {
+      R.w[0] = load_nt(reinterpret_cast<const uint4*>(a.qs + ((size_t)row * a.nblk + kb) * 16));
+      if constexpr (kPair) R.wu[0] = load_nt(reinterpret_cast<const uint4*>(a.qs + ((size_t)row_up * a.nblk + kb) * 16));
+    }
+    R.d = load_nt(a.d + (size_t)row * a.nblk + kb);
+    if constexpr (kPair) R.du = load_nt(a.d + (size_t)row_up * a.nblk + kb);
+    const float4* xp = reinterpret_cast<const float4*>(xrow + kb * 32);
+    const float4* gp = reinterpret_cast<const float4*>(grow + kb * 32);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) R.x[e] = xp[e];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) R.g[e] = gp[e];
+  };
+  // element s (0..31) of the lane's block, decoded
+  auto weight = [&](const uint4 (&w)[QT == kQ8_0 ? 2 : 1], float d, int s) -> float {
+    if constexpr (QT == kQ8_0) {
+      const uint32_t words[8] = {w[0].x, w[0].y, w[0].z, w[0].w, w[1].x, w[1].y, w[1].z, w[1].w};
+      const uint32_t u = words[s >> 2] ^ 0x80808080u;
+      const float cd = -128.f * d;
+      switch (s & 3) {
+        case 0: return dq_byte<0>(d, cd, u);
+        case 1: return dq_byte<1>(d, cd, u);
+        case 2: return dq_byte<2>(d, cd, u);
+        default: return dq_byte<3>(d, cd, u);
+      }
+    } else {  // byte b: element b in its low nibble, b + 16 in its high one
+      const uint32_t words[4] = {w[0].x, w[0].y, w[0].z, w[0].w};
+      const uint32_t wd = words[(s & 15) >> 2];
+      const uint32_t u = s < 16 ? wd & 0x0f0f0f0fu : (wd >> 4) & 0x0f0f0f0fu;
+      const float cd = -8.f * d;
+      switch (s & 3) {
+        case 0: return dq_byte<0>(d, cd, u);
+        case 1: return dq_byte<1>(d, cd, u);
+        case 2: return dq_byte<2>(d, cd, u);
+        default: return dq_byte<3>(d, cd, u);
+      }
+    }
+  };
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+  float ss = 0.f;
+  auto compute = [&](int g, const Regs& R) {
+    const bool ok = 4 * g + q < a.nblk;
+    // a block past the row, or an input row past the batch, contributes
+    // exact zeros (selects: its registers may hold anything)
+    const float d = ok ? half_bits_to_float((uint16_t)R.d) : 0.f;
+    const float du = ok ? half_bits_to_float((uint16_t)R.du) : 0.f;
+    const bool use = ok && xin;
+    float xs[32];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float4 v = R.x[e], gg = R.g[e];
+      const float4 gv = norm ? gg : make_float4(1.f, 1.f, 1.f, 1.f);
+      xs[4 * e + 0] = use ? v.x * gv.x : 0.f;
+      xs[4 * e + 1] = use ? v.y * gv.y : 0.f;
+      xs[4 * e + 2] = use ? v.z * gv.z : 0.f;
+      xs[4 * e + 3] = use ? v.w * gv.w : 0.f;
+      ss += use ? (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w) : 0.f;
+    }
+#pragma unroll
+    for (int s = 0; s < 32; ++s) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(weight(R.w, d, s), xs[s], acc, 0, 0, 0);
+      if constexpr (kPair) accu = __builtin_amdgcn_mfma_f32_16x16x4f32(weight(R.wu, du, s), xs[s], accu, 0, 0, 0);
+    }
+  };
+  // two register sets: group g + 4 is requested before group g is computed
+  Regs ra, rb;
+  int g = wave;
+  if (g < ngrp) load(g, ra);
+  while (g < ngrp) {
+    if (g + 4 < ngrp) load(g + 4, rb);
+    compute(g, ra);
+    g += 4;
+    if (g >= ngrp) break;
+    if (g + 4 < ngrp) load(g + 4, ra);
+    compute(g, rb);
+    g += 4;
+  }
+  red[wave][0][lane] = acc;
+  if constexpr (kPair) red[wave][1][lane] = accu;
+  rss[wave][lane] = ss;
+  __syncthreads();
+  if (wave != 0) return;
+  f32x4 dsum = red[0][0][lane], usum = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (kPair) usum = red[0][1][lane];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) {
+    dsum += red[w][0][lane];
+    if constexpr (kPair) usum += red[w][1][lane];
+  }
+  const int m = lane & 15;  // input row of this lane's outputs
+  float scale = 1.f;
+  if (norm) {
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) t += rss[w][m + 16 * qq];
+    scale = 1.0f / sqrtf(t / (float)kp + a.eps);
+  }
+  if (m >= a.m) return;
+  float* const yr = (a.y_ind ? *a.y_ind + a.y_off : a.y) + (size_t)m * a.ldy;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int n = n0 + 4 * q + r;
+    if (n >= nout) continue;
+    float v;
+    if constexpr (kPair) {
+      const float gt = dsum[r] * scale, up = usum[r] * scale;
+      v = (MODE == kModePairSilu ? act_silu(gt) : act_gelu_tanh(gt)) * up;
+    } else {
+      v = dsum[r] * scale;
+    }
+    if constexpr (MODE == kModeAdd) v += yr[n];
+    else if constexpr (MODE == kModeStore) v = a.bias ? v + a.bias[n] : v;
+    yr[n] = v;
   }
 }
 

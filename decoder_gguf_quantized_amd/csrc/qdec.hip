@@ -311,11 +311,25 @@ int gemv(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, c
   if (per_row > kGemvLdsMax) throw HipError{"gemv: input row too long for LDS"};
   const bool pair = mode == kModePairSilu || mode == kModePairGelu;
   int nwaves = 0;
-  for (int r0 = 0; r0 < nrows; r0 += cap) {
-    const int mr = std::min(cap, nrows - r0);
+  const bool plain = !res.add && !acc.o && !amax;
+  for (int r0 = 0, mr = 0; r0 < nrows; r0 += mr) {
+    // 9..16 rows of Q4_0 / Q8_0 with plain inputs: the matrix-core decode
+    // (no LDS staging: up to 16 rows per launch at any row length)
+    const int nout = pair ? w.rows / 2 : w.rows;
+    const bool mf = gemv_mfma_fits(w.type, std::min(16, nrows - r0), nout, plain);
+    mr = std::min(mf ? 16 : cap, nrows - r0);
+    if (mf) {
+      GemvArgs a{w.qs, w.d, w.rows, w.nblk, x + (size_t)r0 * ldx, ldx, norm_w, eps,
+                 y ? y + (size_t)r0 * ldy : nullptr, ldy, mr, y_ind, (long)r0 * ldy,
+                 nullptr, nullptr, nullptr, bias, w.sd};
+      const double bytes = w.gguf_bytes + (double)mr * kp * 4 + (double)mr * nout * 4;
+      Timed tm(m, st, gemv_class(w.type), bytes, 2.0 * mr * w.rows * (double)w.cols);
+      gemv_type(w.type, 16, kGemvMfmaClass, mode, dim3((nout + 15) / 16), 0, st, a);
+      continue;
+    }
     int M = 1;
     while (M < mr) M *= 2;
-    const int cls = gemv_tile_class(pair, w.rows, M, kp, !res.add && !acc.o && !amax);
+    const int cls = gemv_tile_class(pair, w.rows, M, kp, plain);
     const int R = class_rows(cls), NW = class_waves(cls);
     const int ngroups = pair ? w.rows / R : (w.rows + R - 1) / R;
     // waves stay resident and loop: at most four workgroups per CU, so the

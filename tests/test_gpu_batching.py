@@ -179,6 +179,53 @@ def test_paged_window_model_matches_the_oracle():
                 cur[s] = got[r]
 
 
+# One-layer models wide enough (QKV 3,072 rows, 2,112 gate/up pairs, 2,048
+# down outputs, a 2,500-row head) for the matrix-core decode of 9..16 rows.
+WIDE = dict(SMALL["qwen2_bias_hd64_g2"], n_layer=1, hidden=2048, n_head=16, n_head_kv=4, head_dim=128,
+            ffn=2112, vocab=2500, embd_type="f32", tied=False)
+WIDE_CASES = {
+    "wide_q8_0_bias_silu": dict(WIDE, name="wide_q8_0_bias_silu", wtype="q8_0", seed=21),
+    "wide_q4_0_gelu": dict(WIDE, name="wide_q4_0_gelu", wtype="q4_0", qkv_bias=False, act="gelu_tanh", seed=22),
+}
+
+
+@pytest.mark.parametrize("key,n", [("wide_q8_0_bias_silu", 12), ("wide_q4_0_gelu", 16), ("wide_q8_0_bias_silu", 9)])
+def test_decode_batch_of_nine_to_sixteen_matches_the_oracle(key, n):
+    """Nine to sixteen decode rows run the QKV (RMSNorm prologue, bias),
+    gate/up (pair epilogue, SiLU or gelu_tanh), down (residual add) and head
+    projections on the matrix cores (Q8_0 and Q4_0 weights): every logits row
+    of a few greedy steps over a shuffled slot order against the oracle, slots
+    at different lengths."""
+    cfg = dict(WIDE_CASES[key])
+    t = synth.generate(cfg)
+    dev()
+    V = cfg["vocab"]
+    with qdec.Model(cfg, t, max_seqs=n, max_ctx=96) as m:
+        om = OracleModel(cfg, t, max_ctx=96, n_seqs=n)
+        pl = torch.empty((1, V), dtype=torch.float32, device=dev())
+        tok = torch.empty(1, dtype=torch.int32, device=dev())
+        cur = {}
+        for s in range(n):
+            prompt = synth.prompt(cfg, 3 + 5 * s % 37, tag=f"b{s}")
+            m.prefill(s, prompt, pl, tok)
+            torch.cuda.synchronize()
+            cur[s] = int(as_np(tok)[0])
+            om.forward(s, prompt)
+        rng = np.random.default_rng(n)
+        dl = torch.empty((n, V), dtype=torch.float32, device=dev())
+        out = torch.empty(n, dtype=torch.int32, device=dev())
+        for step in range(4):
+            seqs = [int(x) for x in rng.permutation(n)]
+            m.decode_batch(seqs, [cur[s] for s in seqs], dl, out)
+            torch.cuda.synchronize()
+            g, got = as_np(dl), as_np(out).tolist()
+            for r, s in enumerate(seqs):
+                o = om.forward(s, [cur[s]])[0]
+                check_row(g[r], o)
+                assert token_agrees(got[r], o), (step, s)
+                cur[s] = got[r]
+
+
 def test_sampled_slot_uses_its_own_stream(qwen3_pair):
     cfg, t, flat, _ = qwen3_pair
     V = cfg["vocab"]
