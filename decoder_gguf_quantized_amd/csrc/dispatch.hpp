@@ -96,15 +96,26 @@ void gemv_dispatch_mode(int mode, dim3 grid, size_t lds, hipStream_t st, const G
 // left for the kernel's own small arrays).
 constexpr size_t kGemvLdsMax = 128 * 1024;
 
-// Tile class of the matrix-core decode (gemv_mfma_kernel): 9..16 input rows
-// of Q4_0 / Q8_0 weights with plain inputs and at least 2,048 outputs (128
-// workgroups), launched as M = 16 with one workgroup per 16 outputs and no
-// LDS staging.  Fewer outputs leave most CUs without a workgroup: the
-// 0.6B-shape down projection (1,024 outputs, 64 workgroups) took 17.6 us
-// against 16.8 us for two eight-row launches of the lane-tree kernel.
+// Tile class of the matrix-core decode (gemv_mfma_kernel), launched as
+// M = 16 with one workgroup per 16 outputs (times the K split) and no LDS
+// staging.  It takes 9..16 input rows of Q4_0 / Q8_0 weights:
+//   - store and pair modes with plain inputs and at least 2,048 outputs: with
+//     fewer, most CUs get no workgroup (the 0.6B-shape down projection, 1,024
+//     outputs on 64 workgroups, took 17.6 us against 16.8 us for two eight-row
+//     launches of the lane-tree kernel);
+//   - the add mode without a norm prologue, plain or from decode attention's
+//     accumulators, with K split across workgroups until there are about 256.
 constexpr int kGemvMfmaClass = 8;
-inline bool gemv_mfma_fits(int type, int rows_in, int nout, bool plain) {
-  return (type == kQ4_0 || type == kQ8_0) && rows_in >= 9 && rows_in <= 16 && nout >= 2048 && plain;
+// the K split of the matrix-core decode for a projection (0: not taken)
+inline int gemv_mfma_split(int type, int rows_in, int mode, int nout, int nblk, bool norm, bool res, bool acc,
+                           bool amax) {
+  if (!(type == kQ4_0 || type == kQ8_0) || rows_in < 9 || rows_in > 16 || res || amax) return 0;
+  if (mode != kModeAdd) return (!acc && nout >= 2048) ? 1 : 0;
+  if (norm) return 0;
+  const int tiles = (nout + 15) / 16, ngrp = (nblk + 3) / 4;
+  int ks = 1;
+  while (tiles * ks < 256 && 4 * (ks + 1) <= ngrp) ++ks;  // each wave keeps a group at least
+  return ks;
 }
 
 // plain: no residual prologue, no attention-accumulator input, no fused argmax
@@ -122,10 +133,15 @@ void gemv_dispatch_class(int cls, int mode, dim3 grid, size_t lds, hipStream_t s
     case 1: gemv_dispatch_mode<QT, M, 2, 1, 8, false>(mode, grid, lds, st, a); break;
     case kGemvMfmaClass:  // 9..16 input rows on the matrix cores (Q4_0 / Q8_0, plain inputs)
       if constexpr (M == 16 && (QT == kQ4_0 || QT == kQ8_0)) {
-        if (a.res_add || a.xd || a.amax_v) throw HipError{"gemv: the matrix-core decode takes plain inputs only"};
+        if (a.res_add || a.amax_v || (a.xd && mode != kModeAdd) || (mode == kModeAdd && a.norm_w) ||
+            (grid.y > 1 && mode != kModeAdd))
+          throw HipError{"gemv: the matrix-core decode takes plain inputs, or accumulators in add mode"};
         switch (mode) {
           case kModeStore: qlaunch(gemv_mfma_kernel<QT, kModeStore>, grid, 256, 0, st, a); break;
-          case kModeAdd: qlaunch(gemv_mfma_kernel<QT, kModeAdd>, grid, 256, 0, st, a); break;
+          case kModeAdd:
+            if (a.xd) qlaunch(gemv_mfma_kernel<QT, kModeAdd, true>, grid, 256, 0, st, a);
+            else qlaunch(gemv_mfma_kernel<QT, kModeAdd>, grid, 256, 0, st, a);
+            break;
           case kModePairSilu: qlaunch(gemv_mfma_kernel<QT, kModePairSilu>, grid, 256, 0, st, a); break;
           default: qlaunch(gemv_mfma_kernel<QT, kModePairGelu>, grid, 256, 0, st, a); break;
         }

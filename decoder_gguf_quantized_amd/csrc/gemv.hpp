@@ -700,8 +700,14 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(GemvArgs a) {
 // products and the sums over k.
 //
 // Workgroup = 16 outputs (pair modes: 16 (gate, up) pairs), four waves
-// splitting K in groups of four quant blocks (wave w takes groups w, w + 4,
-// ...).  Lane l = i + 16 q: weight row i and input row i of the tile, block q
+// splitting K in groups of four quant blocks; blockIdx.y splits K further
+// across ks = gridDim.y workgroups (wave w of workgroup z takes groups
+// 4 z + w, 4 z + w + 4 ks, ...), for projections with few outputs, which then
+// add their partial sums to y with atomic adds (add mode only: the order of
+// the adds varies, so such outputs agree with themselves to f32 rounding).
+// ACC: the input rows are decode attention's accumulators (the blocks summed
+// and divided by their softmax denominators, as the lane-tree kernel's
+// staging does), add mode only.  The add mode takes no norm prologue.  Lane l = i + 16 q: weight row i and input row i of the tile, block q
 // of the group.  The contraction index of MFMA step s is (block q, element s):
 // lane (i, q) supplies A[i][q] = W[row i][(4g + q) 32 + s] and B[q][i] =
 // x[i][(4g + q) 32 + s], so each lane reads one whole block of its row and 32
@@ -710,10 +716,12 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(GemvArgs a) {
 // RMSNorm prologue the partial sums of squares, meet in LDS; wave 0 applies
 // the norm scale (1 / rms, as the lane-tree kernel does: the gains multiply the
 // inputs, the scale the sums) and the epilogue.
-template <int QT, int MODE>
+template <int QT, int MODE, bool ACC = false>
 __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
   static_assert(QT == kQ4_0 || QT == kQ8_0, "matrix-core decode: Q4_0 and Q8_0");
+  static_assert(!ACC || MODE == kModeAdd, "accumulator input: add mode");
   constexpr bool kPair = MODE == kModePairSilu || MODE == kModePairGelu;
+  constexpr bool kNorm = MODE != kModeAdd;  // the RMSNorm prologue (if norm_w is set)
   typedef float f32x4 __attribute__((ext_vector_type(4)));
   __shared__ f32x4 red[4][kPair ? 2 : 1][64];
   __shared__ float rss[4][64];
@@ -724,6 +732,7 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
   const int nout = kPair ? a.rows / 2 : a.rows;
   const int kp = a.nblk * 32;
   const int ngrp = (a.nblk + 3) / 4;
+  const int ks = gridDim.y, kz = blockIdx.y;
   // weight rows of lane i (clamped into the matrix: rows past it are not stored)
   int row, row_up = 0;
   if constexpr (kPair) {
@@ -733,15 +742,19 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
     row = min(n0 + i, a.rows - 1);
   }
   const bool xin = i < a.m;  // input row i exists
-  const float* xrow = a.x + (size_t)min(i, a.m - 1) * a.ldx;
-  const bool norm = a.norm_w != nullptr;
+  const int mi = min(i, a.m - 1);
+  const float* xrow = ACC ? a.xd + (size_t)mi * a.ldx : a.x + (size_t)mi * a.ldx;
+  const bool norm = kNorm && a.norm_w != nullptr;
   const float* grow = norm ? a.norm_w : xrow;  // without a norm the row stands in, unused
 
+  // ACC: g holds the second accumulator block, l the blocks' denominators
   struct Regs {
     uint4 w[QT == kQ8_0 ? 2 : 1], wu[kPair ? (QT == kQ8_0 ? 2 : 1) : 1];
     uint32_t d, du;
-    float4 x[8], g[8];
+    float4 x[8], g[kNorm || ACC ? 8 : 1];
+    float l[ACC ? kAccCopies : 1];
   };
+  static_assert(kAccCopies == 2, "two accumulator blocks");
   // loads of group g into R (every lane issues the same loads: blocks past
   // the row are read at the last block and zeroed when used)
   auto load = [&](int g, Regs& R) {
@@ -762,11 +775,21 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
     R.d = load_nt(a.d + (size_t)row * a.nblk + kb);
     if constexpr (kPair) R.du = load_nt(a.d + (size_t)row_up * a.nblk + kb);
     const float4* xp = reinterpret_cast<const float4*>(xrow + kb * 32);
-    const float4* gp = reinterpret_cast<const float4*>(grow + kb * 32);
 #pragma unroll
     for (int e = 0; e < 8; ++e) R.x[e] = xp[e];
+    if constexpr (ACC) {
+      const float4* x2 = reinterpret_cast<const float4*>(xrow + a.xcstride + kb * 32);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) R.g[e] = gp[e];
+      for (int e = 0; e < 8; ++e) R.g[e] = x2[e];
+      // the block's 32 inputs lie in one head (head_dim a multiple of 32)
+      const float* lp = a.xl + (size_t)mi * (a.ldx / a.xhd) + (kb * 32) / a.xhd;
+      R.l[0] = lp[0];
+      R.l[1] = lp[a.xcstride];
+    } else if constexpr (kNorm) {
+      const float4* gp = reinterpret_cast<const float4*>(grow + kb * 32);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) R.g[e] = gp[e];
+    }
   };
   // element s (0..31) of the lane's block, decoded
   auto weight = [&](const uint4 (&w)[QT == kQ8_0 ? 2 : 1], float d, int s) -> float {
@@ -803,15 +826,27 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
     const float du = ok ? half_bits_to_float((uint16_t)R.du) : 0.f;
     const bool use = ok && xin;
     float xs[32];
+    if constexpr (ACC) {
+      const float rl = 1.0f / (R.l[0] + R.l[1]);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float4 v = R.x[e], gg = R.g[e];
-      const float4 gv = norm ? gg : make_float4(1.f, 1.f, 1.f, 1.f);
-      xs[4 * e + 0] = use ? v.x * gv.x : 0.f;
-      xs[4 * e + 1] = use ? v.y * gv.y : 0.f;
-      xs[4 * e + 2] = use ? v.z * gv.z : 0.f;
-      xs[4 * e + 3] = use ? v.w * gv.w : 0.f;
-      ss += use ? (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w) : 0.f;
+      for (int e = 0; e < 8; ++e) {
+        const float4 v = R.x[e], v2 = R.g[e];
+        xs[4 * e + 0] = use ? (v.x + v2.x) * rl : 0.f;
+        xs[4 * e + 1] = use ? (v.y + v2.y) * rl : 0.f;
+        xs[4 * e + 2] = use ? (v.z + v2.z) * rl : 0.f;
+        xs[4 * e + 3] = use ? (v.w + v2.w) * rl : 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float4 v = R.x[e], gg = R.g[kNorm ? e : 0];
+        const float4 gv = (kNorm && norm) ? gg : make_float4(1.f, 1.f, 1.f, 1.f);
+        xs[4 * e + 0] = use ? v.x * gv.x : 0.f;
+        xs[4 * e + 1] = use ? v.y * gv.y : 0.f;
+        xs[4 * e + 2] = use ? v.z * gv.z : 0.f;
+        xs[4 * e + 3] = use ? v.w * gv.w : 0.f;
+        if constexpr (kNorm) ss += use ? (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w) : 0.f;
+      }
     }
 #pragma unroll
     for (int s = 0; s < 32; ++s) {
@@ -819,18 +854,20 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
       if constexpr (kPair) accu = __builtin_amdgcn_mfma_f32_16x16x4f32(weight(R.wu, du, s), xs[s], accu, 0, 0, 0);
     }
   };
-  // two register sets: group g + 4 is requested before group g is computed
+  // two register sets: the wave's next group is requested before its
+  // current one is computed
   Regs ra, rb;
-  int g = wave;
+  const int gs = 4 * ks;  // group stride of a wave
+  int g = 4 * kz + wave;
   if (g < ngrp) load(g, ra);
   while (g < ngrp) {
-    if (g + 4 < ngrp) load(g + 4, rb);
+    if (g + gs < ngrp) load(g + gs, rb);
     compute(g, ra);
-    g += 4;
+    g += gs;
     if (g >= ngrp) break;
-    if (g + 4 < ngrp) load(g + 4, ra);
+    if (g + gs < ngrp) load(g + gs, ra);
     compute(g, rb);
-    g += 4;
+    g += gs;
   }
   red[wave][0][lane] = acc;
   if constexpr (kPair) red[wave][1][lane] = accu;
@@ -867,8 +904,15 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
     } else {
       v = dsum[r] * scale;
     }
-    if constexpr (MODE == kModeAdd) v += yr[n];
-    else if constexpr (MODE == kModeStore) v = a.bias ? v + a.bias[n] : v;
+    if constexpr (MODE == kModeAdd) {
+      if (ks > 1) {
+        unsafeAtomicAdd(yr + n, v);  // several workgroups add into this output
+        continue;
+      }
+      v += yr[n];
+    } else if constexpr (MODE == kModeStore) {
+      v = a.bias ? v + a.bias[n] : v;
+    }
     yr[n] = v;
   }
 }

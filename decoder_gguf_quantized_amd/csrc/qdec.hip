@@ -313,18 +313,26 @@ int gemv(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, c
   int nwaves = 0;
   const bool plain = !res.add && !acc.o && !amax;
   for (int r0 = 0, mr = 0; r0 < nrows; r0 += mr) {
-    // 9..16 rows of Q4_0 / Q8_0 with plain inputs: the matrix-core decode
-    // (no LDS staging: up to 16 rows per launch at any row length)
+    // 9..16 rows of Q4_0 / Q8_0: the matrix-core decode where it fits (no LDS
+    // staging: up to 16 rows per launch at any row length)
     const int nout = pair ? w.rows / 2 : w.rows;
-    const bool mf = gemv_mfma_fits(w.type, std::min(16, nrows - r0), nout, plain);
-    mr = std::min(mf ? 16 : cap, nrows - r0);
-    if (mf) {
-      GemvArgs a{w.qs, w.d, w.rows, w.nblk, x + (size_t)r0 * ldx, ldx, norm_w, eps,
+    const int ks = gemv_mfma_split(w.type, std::min(16, nrows - r0), mode, nout, w.nblk, norm_w != nullptr,
+                                   res.add != nullptr, acc.o != nullptr, amax);
+    mr = std::min(ks ? 16 : cap, nrows - r0);
+    if (ks) {
+      GemvArgs a{w.qs, w.d, w.rows, w.nblk, x ? x + (size_t)r0 * ldx : nullptr, ldx, norm_w, eps,
                  y ? y + (size_t)r0 * ldy : nullptr, ldy, mr, y_ind, (long)r0 * ldy,
                  nullptr, nullptr, nullptr, bias, w.sd};
-      const double bytes = w.gguf_bytes + (double)mr * kp * 4 + (double)mr * nout * 4;
+      if (acc.o) {
+        a.xd = acc.o + (size_t)r0 * ldx;
+        a.xl = acc.l + (size_t)r0 * (ldx / acc.hd);
+        a.xhd = acc.hd;
+        a.xcstride = (long)acc.stride;
+      }
+      const double bytes =
+          w.gguf_bytes + (double)mr * kp * (acc.o ? 4 * kAccCopies : 4) + (double)mr * nout * 4;
       Timed tm(m, st, gemv_class(w.type), bytes, 2.0 * mr * w.rows * (double)w.cols);
-      gemv_type(w.type, 16, kGemvMfmaClass, mode, dim3((nout + 15) / 16), 0, st, a);
+      gemv_type(w.type, 16, kGemvMfmaClass, mode, dim3((nout + 15) / 16, ks), 0, st, a);
       continue;
     }
     int M = 1;
