@@ -215,6 +215,10 @@ def bench_batched(cfg, args):
     dev = torch.device("cuda:0")
     if args.decode_steps is not None:
         cfg["decode_steps"] = args.decode_steps
+    if args.batch is not None:  # another number of sequences (the workload's name says it)
+        import re
+        cfg["batch"] = args.batch
+        cfg["name"] = re.sub(r"-b\d+", f"-b{args.batch}", cfg["name"])
     B, P, N, V = cfg["batch"], cfg["preset_kv"], cfg["decode_steps"], cfg["vocab"]
     tensors = synth.generate(cfg)
     model = qdec.Model(cfg, tensors, max_seqs=B, max_ctx=P + N + 1)
@@ -315,6 +319,8 @@ def main():
     ap.add_argument("--weights", default=None, choices=sorted(WEIGHT_MIXES),
                     help="re-type the workload's matrices, e.g. q4_k_m: Q4_K with Q6_K attn_v, ffn_down and head")
     ap.add_argument("--decode-steps", type=int, default=None, help="override the workload's decode steps (profiling runs)")
+    ap.add_argument("--batch", type=int, default=None,
+                    help="batched workload only: number of sequences (default: the workload's 16)")
     ap.add_argument("--prefill-precision", default="f32", choices=sorted(PREFILL_TERMS),
                     help="operand precision of the prefill projections (default f32)")
     ap.add_argument("--top-p", type=float, default=None,

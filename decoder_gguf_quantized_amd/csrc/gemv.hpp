@@ -690,7 +690,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(GemvArgs a) {
 }
 
 // ------------------------------------------------------------ batched decode on the matrix cores
-// Decode projection of 9..16 input rows (a decode batch), Q4_0 / Q8_0
+// Decode projection of 5..16 input rows (a decode batch), Q4_0 / Q8_0
 // weights: y[m][n] = sum_k W[n][k] x[m][k] on V_MFMA_F32_16X16X4F32 (f32
 // operands, f32 accumulation), with the weights decoded exactly in registers
 // (d q, dq_byte) and the inputs read straight from global memory (no LDS

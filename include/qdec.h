@@ -194,7 +194,7 @@ int qdec_prefill(qdec_model* m, int32_t seq, const int32_t* tokens, int32_t n_to
  * (top_p <= 0: the first token).  The running sums use per-token weights
  * floor(2^40 * 2^((l - max l) * log2(e) / temperature)) (f32) summed exactly;
  * a row with a non-finite logit keeps every token.  top_p >= 1: no restriction.
- * Decode attention combines its position chunks with f32 atomic adds, and 9..16
+ * Decode attention combines its position chunks with f32 atomic adds, and 5..16
  * rows run some projections with K split across workgroups the same way, so
  * repeated steps agree with each other to f32 rounding, not bit for bit.
  * With QDEC_TOKENS_ON_DEVICE, tokens is a device pointer; ids outside [0, vocab)

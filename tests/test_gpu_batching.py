@@ -189,9 +189,10 @@ WIDE_CASES = {
 }
 
 
-@pytest.mark.parametrize("key,n", [("wide_q8_0_bias_silu", 12), ("wide_q4_0_gelu", 16), ("wide_q8_0_bias_silu", 9)])
-def test_decode_batch_of_nine_to_sixteen_matches_the_oracle(key, n):
-    """Nine to sixteen decode rows run the QKV (RMSNorm prologue, bias),
+@pytest.mark.parametrize("key,n", [("wide_q8_0_bias_silu", 12), ("wide_q4_0_gelu", 16), ("wide_q8_0_bias_silu", 9),
+                                   ("wide_q4_0_gelu", 5)])
+def test_decode_batch_of_five_to_sixteen_matches_the_oracle(key, n):
+    """Five to sixteen decode rows run the QKV (RMSNorm prologue, bias),
     gate/up (pair epilogue, SiLU or gelu_tanh), down (residual add) and head
     projections on the matrix cores (Q8_0 and Q4_0 weights): every logits row
     of a few greedy steps over a shuffled slot order against the oracle, slots

@@ -300,10 +300,10 @@ MATMUL_CASES = [
     # of one row per wave (ragged rows; Q4_0 in the next group)
     (synth.T_Q8_0, 4097, 9216, 1), (synth.T_Q4_K, 4100, 8448, 1), (synth.T_Q6_K, 4099, 8192, 1),
     (synth.T_F32, 4096, 8192, 1),
-    # 9..16 input rows, >= 2,048 outputs: the matrix-core decode (ragged rows,
+    # 5..16 input rows, >= 2,048 outputs: the matrix-core decode (ragged rows,
     # block counts that are not multiples of four)
     (synth.T_Q8_0, 2100, 1024, 16), (synth.T_Q4_0, 4100, 1120, 9), (synth.T_Q8_0, 2048, 4128, 12),
-    (synth.T_Q4_0, 3000, 2080, 13),
+    (synth.T_Q4_0, 3000, 2080, 13), (synth.T_Q8_0, 2050, 1056, 5), (synth.T_Q4_0, 2060, 1024, 8),
     # long rows with >= 2048 row groups: eight-wave workgroups (ragged rows)
     (synth.T_Q4_0, 4100, 8192, 1), (synth.T_Q4_0, 4097, 4608, 2), (synth.T_Q8_0, 4100, 2080, 3),
     (synth.T_F32, 4100, 600, 5),
