@@ -707,8 +707,10 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(GemvArgs a) {
 // the adds varies, so such outputs agree with themselves to f32 rounding).
 // ACC: the input rows are decode attention's accumulators (the blocks summed
 // and divided by their softmax denominators, as the lane-tree kernel's
-// staging does), add mode only.  The add mode takes no norm prologue.  Lane l = i + 16 q: weight row i and input row i of the tile, block q
-// of the group.  The contraction index of MFMA step s is (block q, element s):
+// staging does), add mode only.  The add mode takes no norm prologue.
+//
+// Lane l = i + 16 q: weight row i and input row i of the tile, block q of the
+// group.  The contraction index of MFMA step s is (block q, element s):
 // lane (i, q) supplies A[i][q] = W[row i][(4g + q) 32 + s] and B[q][i] =
 // x[i][(4g + q) 32 + s], so each lane reads one whole block of its row and 32
 // consecutive inputs.  D[n][m] (output row n, input m) lands in register r of
