@@ -98,7 +98,7 @@ constexpr size_t kGemvLdsMax = 128 * 1024;
 
 // Tile class of the matrix-core decode (gemv_mfma_kernel), launched as
 // M = 16 with one workgroup per 16 outputs (times the K split) and no LDS
-// staging.  It takes 5..16 input rows of Q4_0 / Q8_0 weights (its cost does
+// staging.  It takes 5..16 input rows of block-quantized weights (its cost does
 // not depend on the row count; on the batched 0.6B-shape workload it measured
 // 2,058 against 1,978 tokens/s at 8 sequences and 1,604 against 1,737 at 4):
 //   - store and pair modes with plain inputs and at least 2,048 outputs: with
@@ -112,7 +112,7 @@ constexpr int kGemvMfmaMinRows = 5;
 // the K split of the matrix-core decode for a projection (0: not taken)
 inline int gemv_mfma_split(int type, int rows_in, int mode, int nout, int nblk, bool norm, bool res, bool acc,
                            bool amax) {
-  if (!(type == kQ4_0 || type == kQ8_0) || rows_in < kGemvMfmaMinRows || rows_in > 16 || res || amax) return 0;
+  if (type == kF32 || rows_in < kGemvMfmaMinRows || rows_in > 16 || res || amax) return 0;
   if (mode != kModeAdd) return (!acc && nout >= 2048) ? 1 : 0;
   if (norm) return 0;
   const int tiles = (nout + 15) / 16, ngrp = (nblk + 3) / 4;
@@ -134,8 +134,8 @@ void gemv_dispatch_class(int cls, int mode, dim3 grid, size_t lds, hipStream_t s
   switch (cls) {
     case 0: gemv_dispatch_mode<QT, M, 1, 1, 4, false>(mode, grid, lds, st, a); break;
     case 1: gemv_dispatch_mode<QT, M, 2, 1, 8, false>(mode, grid, lds, st, a); break;
-    case kGemvMfmaClass:  // 5..16 input rows on the matrix cores (Q4_0 / Q8_0, plain inputs)
-      if constexpr (M == 16 && (QT == kQ4_0 || QT == kQ8_0)) {
+    case kGemvMfmaClass:  // 5..16 input rows on the matrix cores (block-quantized weights)
+      if constexpr (M == 16 && QT != kF32) {
         if (a.res_add || a.amax_v || (a.xd && mode != kModeAdd) || (mode == kModeAdd && a.norm_w) ||
             (grid.y > 1 && mode != kModeAdd))
           throw HipError{"gemv: the matrix-core decode takes plain inputs, or accumulators in add mode"};
@@ -149,7 +149,7 @@ void gemv_dispatch_class(int cls, int mode, dim3 grid, size_t lds, hipStream_t s
           default: qlaunch(gemv_mfma_kernel<QT, kModePairGelu>, grid, 256, 0, st, a); break;
         }
       } else {
-        throw HipError{"gemv: the matrix-core decode takes Q4_0 / Q8_0 weights and sixteen input rows"};
+        throw HipError{"gemv: the matrix-core decode takes block-quantized weights and sixteen input rows"};
       }
       break;
     case 4:  // plain store / add only (see gemv_tile_class)

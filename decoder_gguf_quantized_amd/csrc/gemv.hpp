@@ -690,10 +690,11 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(GemvArgs a) {
 }
 
 // ------------------------------------------------------------ batched decode on the matrix cores
-// Decode projection of 5..16 input rows (a decode batch), Q4_0 / Q8_0
-// weights: y[m][n] = sum_k W[n][k] x[m][k] on V_MFMA_F32_16X16X4F32 (f32
+// Decode projection of 5..16 input rows (a decode batch), Q4_0 / Q8_0 / Q4_K /
+// Q6_K weights: y[m][n] = sum_k W[n][k] x[m][k] on V_MFMA_F32_16X16X4F32 (f32
 // operands, f32 accumulation), with the weights decoded exactly in registers
-// (d q, dq_byte) and the inputs read straight from global memory (no LDS
+// (dq_byte: d q for Q4_0 / Q8_0 / Q6_K, scale n - min for Q4_K, each rounded
+// once as in the prefill GEMM) and the inputs read straight from global memory (no LDS
 // staging, so rows of any length take all 16 inputs in one launch).  With the
 // lane-tree GEMV, sixteen inputs cost two wave reductions per row and input
 // and sixteen FMAs per weight on the vector ALU; here the matrix cores do the
@@ -720,7 +721,9 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(GemvArgs a) {
 // inputs, the scale the sums) and the epilogue.
 template <int QT, int MODE, bool ACC = false>
 __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
-  static_assert(QT == kQ4_0 || QT == kQ8_0, "matrix-core decode: Q4_0 and Q8_0");
+  static_assert(QT == kQ4_0 || QT == kQ8_0 || QT == kQ4_K || QT == kQ6_K, "matrix-core decode: block-quantized types");
+  constexpr bool kI8 = int8_layout(QT);  // 32 bytes per block (Q8_0, Q6_K), else 16 nibble bytes
+  constexpr bool kKQ = QT == kQ4_K || QT == kQ6_K;  // scale words plus a super-block word
   static_assert(!ACC || MODE == kModeAdd, "accumulator input: add mode");
   constexpr bool kPair = MODE == kModePairSilu || MODE == kModePairGelu;
   constexpr bool kNorm = MODE != kModeAdd;  // the RMSNorm prologue (if norm_w is set)
@@ -751,8 +754,8 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
 
   // ACC: g holds the second accumulator block, l the blocks' denominators
   struct Regs {
-    uint4 w[QT == kQ8_0 ? 2 : 1], wu[kPair ? (QT == kQ8_0 ? 2 : 1) : 1];
-    uint32_t d, du;
+    uint4 w[kI8 ? 2 : 1], wu[kPair ? (kI8 ? 2 : 1) : 1];
+    uint32_t d, du, sd, sdu;  // raw scale words; K-quants also their super-block words
     float4 x[8], g[kNorm || ACC ? 8 : 1];
     float l[ACC ? kAccCopies : 1];
   };
@@ -761,7 +764,7 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
   // the row are read at the last block and zeroed when used)
   auto load = [&](int g, Regs& R) {
     const int kb = min(4 * g + q, a.nblk - 1);
-    if constexpr (QT == kQ8_0) {
+    if constexpr (kI8) {
       const uint4* p = reinterpret_cast<const uint4*>(a.qs + (size_t)row * kp + kb * 32);
       R.w[0] = load_nt(p);
       R.w[1] = load_nt(p + 1);
@@ -776,6 +779,10 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
     }
     R.d = load_nt(a.d + (size_t)row * a.nblk + kb);
     if constexpr (kPair) R.du = load_nt(a.d + (size_t)row_up * a.nblk + kb);
+    if constexpr (kKQ) {
+      R.sd = load_nt(a.sd + (size_t)row * (a.nblk >> 3) + (kb >> 3));
+      if constexpr (kPair) R.sdu = load_nt(a.sd + (size_t)row_up * (a.nblk >> 3) + (kb >> 3));
+    }
     const float4* xp = reinterpret_cast<const float4*>(xrow + kb * 32);
 #pragma unroll
     for (int e = 0; e < 8; ++e) R.x[e] = xp[e];
@@ -793,11 +800,15 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
       for (int e = 0; e < 8; ++e) R.g[e] = gp[e];
     }
   };
-  // element s (0..31) of the lane's block, decoded
-  auto weight = [&](const uint4 (&w)[QT == kQ8_0 ? 2 : 1], float d, int s) -> float {
-    if constexpr (QT == kQ8_0) {
+  // element s (0..31) of the lane's block, decoded: an int8 layout as
+  // fma(d_s, q + 128, -128 d_s) = d_s q (d_s: the scale of element s's half of
+  // the block, both halves alike but in Q6_K), a nibble layout as
+  // fma(d, n, c) with c = -8 d (Q4_0) or -min (Q4_K); each rounds once
+  auto weight = [&](const uint4 (&w)[kI8 ? 2 : 1], float d, float d2, float c, int s) -> float {
+    if constexpr (kI8) {
       const uint32_t words[8] = {w[0].x, w[0].y, w[0].z, w[0].w, w[1].x, w[1].y, w[1].z, w[1].w};
       const uint32_t u = words[s >> 2] ^ 0x80808080u;
+      if (s >= 16) d = d2;
       const float cd = -128.f * d;
       switch (s & 3) {
         case 0: return dq_byte<0>(d, cd, u);
@@ -809,12 +820,11 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
       const uint32_t words[4] = {w[0].x, w[0].y, w[0].z, w[0].w};
       const uint32_t wd = words[(s & 15) >> 2];
       const uint32_t u = s < 16 ? wd & 0x0f0f0f0fu : (wd >> 4) & 0x0f0f0f0fu;
-      const float cd = -8.f * d;
       switch (s & 3) {
-        case 0: return dq_byte<0>(d, cd, u);
-        case 1: return dq_byte<1>(d, cd, u);
-        case 2: return dq_byte<2>(d, cd, u);
-        default: return dq_byte<3>(d, cd, u);
+        case 0: return dq_byte<0>(d, c, u);
+        case 1: return dq_byte<1>(d, c, u);
+        case 2: return dq_byte<2>(d, c, u);
+        default: return dq_byte<3>(d, c, u);
       }
     }
   };
@@ -824,8 +834,23 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
     const bool ok = 4 * g + q < a.nblk;
     // a block past the row, or an input row past the batch, contributes
     // exact zeros (selects: its registers may hold anything)
-    const float d = ok ? half_bits_to_float((uint16_t)R.d) : 0.f;
-    const float du = ok ? half_bits_to_float((uint16_t)R.du) : 0.f;
+    float d, d2, c, du = 0.f, du2 = 0.f, cu = 0.f;
+    auto scales = [&](uint32_t dw, uint32_t sw, float& s0, float& s1, float& cc) {
+      if constexpr (QT == kQ4_K) {
+        s0 = s1 = q4k_scale(dw, sw);
+        cc = -q4k_min(dw, sw);
+      } else if constexpr (QT == kQ6_K) {
+        s0 = q6k_scale((uint32_t)(int32_t)(int8_t)(dw & 0xffu), sw);
+        s1 = q6k_scale((uint32_t)(int32_t)(int8_t)((dw >> 8) & 0xffu), sw);
+        cc = 0.f;
+      } else {
+        s0 = s1 = half_bits_to_float((uint16_t)dw);
+        cc = QT == kQ4_0 ? -8.f * s0 : 0.f;
+      }
+      if (!ok) s0 = s1 = cc = 0.f;
+    };
+    scales(R.d, kKQ ? R.sd : 0u, d, d2, c);
+    if constexpr (kPair) scales(R.du, kKQ ? R.sdu : 0u, du, du2, cu);
     const bool use = ok && xin;
     float xs[32];
     if constexpr (ACC) {
@@ -852,8 +877,9 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
     }
 #pragma unroll
     for (int s = 0; s < 32; ++s) {
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(weight(R.w, d, s), xs[s], acc, 0, 0, 0);
-      if constexpr (kPair) accu = __builtin_amdgcn_mfma_f32_16x16x4f32(weight(R.wu, du, s), xs[s], accu, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(weight(R.w, d, d2, c, s), xs[s], acc, 0, 0, 0);
+      if constexpr (kPair)
+        accu = __builtin_amdgcn_mfma_f32_16x16x4f32(weight(R.wu, du, du2, cu, s), xs[s], accu, 0, 0, 0);
     }
   };
   // two register sets: the wave's next group is requested before its

@@ -313,7 +313,7 @@ int gemv(qdec_model* m, hipStream_t st, const Mat& w, const float* x, int ldx, c
   int nwaves = 0;
   const bool plain = !res.add && !acc.o && !amax;
   for (int r0 = 0, mr = 0; r0 < nrows; r0 += mr) {
-    // 5..16 rows of Q4_0 / Q8_0: the matrix-core decode where it fits (no LDS
+    // 5..16 rows of block-quantized weights: the matrix-core decode where it fits (no LDS
     // staging: up to 16 rows per launch at any row length)
     const int nout = pair ? w.rows / 2 : w.rows;
     const int ks = gemv_mfma_split(w.type, std::min(16, nrows - r0), mode, nout, w.nblk, norm_w != nullptr,

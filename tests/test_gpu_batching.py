@@ -186,15 +186,19 @@ WIDE = dict(SMALL["qwen2_bias_hd64_g2"], n_layer=1, hidden=2048, n_head=16, n_he
 WIDE_CASES = {
     "wide_q8_0_bias_silu": dict(WIDE, name="wide_q8_0_bias_silu", wtype="q8_0", seed=21),
     "wide_q4_0_gelu": dict(WIDE, name="wide_q4_0_gelu", wtype="q4_0", qkv_bias=False, act="gelu_tanh", seed=22),
+    # a Q4_K_M-like mix (Q4_K, Q6_K for attn_v, ffn_down and the head); FFN
+    # width a multiple of the 256-value super-block
+    "wide_q4km": dict(WIDE, name="wide_q4km", wtype="q4_k", qkv_bias=False, ffn=2304, seed=23,
+                      types={"attn_v": "q6_k", "ffn_down": "q6_k", "output": "q6_k"}),
 }
 
 
 @pytest.mark.parametrize("key,n", [("wide_q8_0_bias_silu", 12), ("wide_q4_0_gelu", 16), ("wide_q8_0_bias_silu", 9),
-                                   ("wide_q4_0_gelu", 5)])
+                                   ("wide_q4_0_gelu", 5), ("wide_q4km", 11)])
 def test_decode_batch_of_five_to_sixteen_matches_the_oracle(key, n):
     """Five to sixteen decode rows run the QKV (RMSNorm prologue, bias),
     gate/up (pair epilogue, SiLU or gelu_tanh), down (residual add) and head
-    projections on the matrix cores (Q8_0 and Q4_0 weights): every logits row
+    projections on the matrix cores (Q8_0, Q4_0 and a Q4_K / Q6_K mix): every logits row
     of a few greedy steps over a shuffled slot order against the oracle, slots
     at different lengths."""
     cfg = dict(WIDE_CASES[key])

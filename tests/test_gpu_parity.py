@@ -304,6 +304,7 @@ MATMUL_CASES = [
     # block counts that are not multiples of four)
     (synth.T_Q8_0, 2100, 1024, 16), (synth.T_Q4_0, 4100, 1120, 9), (synth.T_Q8_0, 2048, 4128, 12),
     (synth.T_Q4_0, 3000, 2080, 13), (synth.T_Q8_0, 2050, 1056, 5), (synth.T_Q4_0, 2060, 1024, 8),
+    (synth.T_Q4_K, 2100, 1280, 12), (synth.T_Q6_K, 2060, 2048, 7), (synth.T_Q6_K, 4097, 768, 16),
     # long rows with >= 2048 row groups: eight-wave workgroups (ragged rows)
     (synth.T_Q4_0, 4100, 8192, 1), (synth.T_Q4_0, 4097, 4608, 2), (synth.T_Q8_0, 4100, 2080, 3),
     (synth.T_F32, 4100, 600, 5),
